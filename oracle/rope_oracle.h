@@ -1,0 +1,115 @@
+/*
+ * rope_oracle.h -- scalar CPU oracle for rotary position embedding apply.
+ *
+ * TEST INFRASTRUCTURE ONLY. This is the plain, slow definition of what the
+ * GPU library computes, evaluated one element at a time in binary64 and
+ * rounded once to the storage type. Only the test suite, the smoke check and
+ * the benchmark's CPU-baseline leg may load it. The product library never
+ * links it and shares no code, header, table or helper with it.
+ *
+ * Sources (web pages, cited by title and section):
+ *  [RE]  "ai.onnx.RotaryEmbedding" WebGPU kernel manifest: `inputs`,
+ *        `attributes`, `attributeDescriptions`, `derive` contracts.
+ *  [MRE] "com.microsoft.MRotaryEmbedding" README: Description, Inputs,
+ *        Attributes, Implementation variants (`pairs4`).
+ *  [PR]  onnxruntime PR #27590 "Add RotaryEmbedding fusion for Qwen3
+ *        on-the-fly RoPE patterns": Motivation (on-the-fly cos/sin), review
+ *        "Modeling Code Alignment Check" (forward, rotate_half,
+ *        apply_rotary_pos_emb), review item 4 (cache = cos(freqs)*scaling).
+ *  [SA]  "com.microsoft.SparseAttention" README: Attributes (`do_rotary`,
+ *        `rotary_interleaved`, `kv_num_heads`).
+ *
+ * Storage types use ONNX TensorProto codes: 1 = float32, 10 = float16.
+ * float16 tensors are passed as arrays of uint16_t bit patterns.
+ * All pointers are host pointers; all arrays are dense row-major.
+ *
+ * Parity status of each function is listed in its comment; "parity unpinned"
+ * marks a reading that nothing on the pages fixes.
+ */
+#ifndef ROPE_ORACLE_H
+#define ROPE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORACLE_F32 1
+#define ORACLE_F16 10
+
+/* IEEE-754 binary16 <-> binary64, round-to-nearest-even, subnormals kept. */
+double   oracle_f16_to_f64(uint16_t h);
+uint16_t oracle_f64_to_f16(double v);
+
+/* Frequency schedule inv_freq[i] = rnd_f32(base^(-2i/R)), i < R/2.
+ * The pages never print the formula ([PR] takes inv_freq from the model's
+ * initializer); this is the standard schedule the workloads name. */
+void oracle_inv_freq(double base, int64_t rotary_dim, float* inv_freq);
+
+/* cos/sin table of [PR] review item 4: for row p and slot i,
+ *   theta = rnd_f32(rnd_f32(p) * inv_freq[i])
+ *   cos[p][i] = rnd_T(rnd_f32(rnd_f32(cos(theta)) * scaling)), sin likewise,
+ * with cos/sin of the exact binary32 theta evaluated in binary64.
+ * Outputs are (rows, half) arrays of storage type `dtype`. */
+void oracle_cos_sin_cache(int dtype, int64_t rows, int64_t half,
+                          const float* inv_freq, float scaling,
+                          void* cos_out, void* sin_out);
+
+/* RotaryEmbedding [RE]. X viewed as x(b,h,s,d):
+ *   rank 4: X[b][h][s][d]; rank 3: X[b][s][h*D + d].
+ * ids == NULL: cos/sin are (B,S,R/2) and token (b,s) uses row b*S+s.
+ * ids != NULL: cos/sin are (M,R/2), token (b,s) uses row ids[b*S+s];
+ *   an id outside [0,M) copies every rotation pair of that token through
+ *   unchanged (reading taken where [RE] leaves such ids outside the contract).
+ * Pairing: interleaved==0 -> (i, i+R/2); interleaved!=0 -> (2i, 2i+1).
+ * Elements R..D-1 are bit-copied. */
+void oracle_rope_apply(int dtype, int rank, int64_t B, int64_t S, int64_t H,
+                       int64_t D, int64_t R, int64_t interleaved,
+                       const void* x, void* y, const void* cos_cache,
+                       const void* sin_cache, const int64_t* ids, int64_t M);
+
+/* M-RoPE slot -> stream map (0 = temporal, 1 = height, 2 = width) for the
+ * half-rotary axis of `half` slots [MRE] Attributes `mrope_section`,
+ * `mrope_layout`. Layout 0: consecutive sections. Layout 1: slots visited in
+ * order, streams taken in turn t, h, w, a stream skipped once it holds its
+ * section count (reading taken where [MRE] names the layout without defining
+ * it; parity unpinned where section_h != section_w or section_t < section_h).
+ * Returns 0, or -1 if the sections are negative or do not sum to `half`. */
+int oracle_mrope_slot_streams(int64_t half, const int64_t section[3],
+                              int64_t layout, int8_t* stream_of_slot);
+
+/* MRotaryEmbedding [MRE]. ids is (3,B,S); cos/sin are (M, R/2). Slot i of
+ * token (b,s) reads row p = ids[k][b][s] with k its stream. If p is outside
+ * [0,M) the pair is bit-copied; otherwise the coefficients are
+ * rnd_T(rnd_f32(c * scale)) ([MRE] `pairs4`: scaled coefficients rounded to
+ * the storage type). Tail bit-copied. */
+void oracle_mrope_apply(int dtype, int rank, int64_t B, int64_t S, int64_t H,
+                        int64_t D, int64_t R, int64_t interleaved,
+                        const void* x, void* y, const void* cos_cache,
+                        const void* sin_cache, const int64_t* ids, int64_t M,
+                        const int64_t section[3], int64_t layout, float scale);
+
+/* Coefficient row of the on-the-fly variant [PR] Motivation: the same
+ * arithmetic as oracle_cos_sin_cache for one position p (any int64). */
+void oracle_onthefly_row(int dtype, int64_t p, const float* inv_freq,
+                         int64_t half, float scaling, void* cos_row,
+                         void* sin_row);
+
+/* Q and K of one attention layer rotated with the same ids and coefficients
+ * ([PR] apply_rotary_pos_emb; [SA] "RoPE on Q and on K"). Q has H heads, K has
+ * Hk heads, same B, S, D, rank. If cos_cache == NULL the coefficients come
+ * from oracle_onthefly_row(ids[b*S+s], inv_freq, R/2, scaling); ids required.
+ * Otherwise exactly oracle_rope_apply on Q and on K. */
+void oracle_rope_apply_qk(int dtype, int rank, int64_t B, int64_t S, int64_t H,
+                          int64_t Hk, int64_t D, int64_t R,
+                          int64_t interleaved, const void* q, const void* k,
+                          void* yq, void* yk, const void* cos_cache,
+                          const void* sin_cache, const int64_t* ids, int64_t M,
+                          const float* inv_freq, float scaling);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPE_ORACLE_H */

@@ -1,0 +1,7 @@
+"""Seeded synthetic inputs for the rotary-embedding library's tests and benchmark.
+
+Shared by the oracle side and the GPU side; contains random-number generators
+and input structure only, never the rotary-embedding arithmetic.
+"""
+from .generators import SplitMix64, normal_tensor, uniform_ints  # noqa: F401
+from .workloads import WORKLOADS, Workload, get, mrope_ids, with_layout  # noqa: F401

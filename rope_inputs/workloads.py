@@ -1,0 +1,220 @@
+"""The five synthetic workloads (shapes, seeds, id structure).
+
+Sizes and structure follow the workloads the rotary-embedding pages imply:
+an fp32 toy case with a per-token (B, S, R/2) cache, an fp16 prefill with a
+gathered (M, R/2) cache, an fp32 partial interleaved rotation, a multimodal
+M-RoPE prefill with text spans and image-patch grids, and an fp16 decode step
+rotating Q and K together. Random values come only from rope_inputs.generators;
+the cos/sin tables are NOT built here (that is the method's arithmetic): each
+workload names the table it needs by (rows, base, rotary_dim, scaling) and the
+caller builds it with its own implementation.
+
+Seeds: 0x5EED0000 + 16 * index + tensor, tensor 0 = X (or Q), 1 = ids,
+2 = K, 3 = out-of-range id selection.
+"""
+from dataclasses import dataclass, field
+from typing import Optional, Tuple
+
+import numpy as np
+
+from .generators import SplitMix64, normal_tensor, sample_without_replacement, uniform_ints
+
+
+def seed(index: int, tensor: int) -> int:
+    return 0x5EED0000 + 16 * index + tensor
+
+
+@dataclass
+class Workload:
+    index: int
+    name: str
+    op: str                      # "rope", "mrope" or "rope_qk"
+    dtype: type
+    x_shape: Tuple[int, ...]     # X, or Q for rope_qk
+    num_heads: int = 0
+    rotary_embedding_dim: int = 0
+    interleaved: int = 0
+    has_ids: bool = True
+    cache_rows: int = 0          # M of the (M, R/2) table; for no-ids the positions 0..S-1
+    cache_base: float = 10000.0
+    scaling: float = 1.0
+    k_shape: Optional[Tuple[int, ...]] = None
+    kv_num_heads: int = 0
+    mrope_section: Optional[Tuple[int, int, int]] = None
+    mrope_layout: int = 0
+    scale: float = 1.0
+    description: str = ""
+    extra: dict = field(default_factory=dict)
+
+    # -- derived sizes -----------------------------------------------------
+    @property
+    def rank(self) -> int:
+        return len(self.x_shape)
+
+    @property
+    def head_size(self) -> int:
+        if self.rank == 4:
+            return self.x_shape[3]
+        return self.x_shape[2] // self.num_heads
+
+    @property
+    def rotary_dim(self) -> int:
+        return self.rotary_embedding_dim or self.head_size
+
+    @property
+    def half(self) -> int:
+        return self.rotary_dim // 2
+
+    @property
+    def batch(self) -> int:
+        return self.x_shape[0]
+
+    @property
+    def seq(self) -> int:
+        return self.x_shape[2] if self.rank == 4 else self.x_shape[1]
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq
+
+    @property
+    def heads(self) -> int:
+        return self.x_shape[1] if self.rank == 4 else self.num_heads
+
+    @property
+    def itemsize(self) -> int:
+        return np.dtype(self.dtype).itemsize
+
+    def algorithmic_bytes(self, onthefly: bool = False) -> int:
+        """X read + Y write + one coefficient row (cos and sin) per token + ids.
+
+        On the fly the coefficient term is the inv_freq vector (4 bytes per
+        slot) read once instead of per-token table rows."""
+        xy = 2 * int(np.prod(self.x_shape)) * self.itemsize
+        if self.k_shape is not None:
+            xy += 2 * int(np.prod(self.k_shape)) * self.itemsize
+        coef = 4 * self.half if onthefly else self.tokens * 2 * self.half * self.itemsize
+        n_id_streams = 3 if self.op == "mrope" else (1 if self.has_ids else 0)
+        return xy + coef + n_id_streams * self.tokens * 8
+
+    def tokens_heads(self) -> int:
+        th = self.tokens * self.heads
+        if self.k_shape is not None:
+            th += self.tokens * self.kv_num_heads
+        return th
+
+    # -- inputs ------------------------------------------------------------
+    def make_x(self) -> np.ndarray:
+        return normal_tensor(seed(self.index, 0), self.x_shape, self.dtype)
+
+    def make_k(self) -> np.ndarray:
+        return normal_tensor(seed(self.index, 2), self.k_shape, self.dtype)
+
+    def make_ids(self) -> Optional[np.ndarray]:
+        if self.op == "mrope":
+            return mrope_ids(self.index, self.batch, self.seq, self.cache_rows,
+                             self.extra.get("oob_fraction", 0.01))
+        if not self.has_ids:
+            return None
+        kind = self.extra.get("ids", "uniform")
+        if kind == "offset_arange":
+            off = uniform_ints(seed(self.index, 1), (self.batch, 1), self.extra["offset_bound"])
+            return off + np.arange(self.seq, dtype=np.int64)[None, :]
+        return uniform_ints(seed(self.index, 1), (self.batch, self.seq), self.extra["id_bound"])
+
+    def cache_positions(self) -> np.ndarray:
+        """Rows the table is built for: 0..M-1 (gathered) or 0..S-1 per batch."""
+        if self.has_ids or self.op == "mrope":
+            return np.arange(self.cache_rows, dtype=np.int64)
+        return np.arange(self.seq, dtype=np.int64)
+
+
+def mrope_ids(index: int, batch: int, seq: int, rows: int, oob_fraction: float) -> np.ndarray:
+    """(3, B, S) temporal/height/width ids: text spans and 32x32 image grids.
+
+    Per batch, a start position p ~ U[0, 8192); segments of 512 text, one
+    1024-token image, 1024 text, one image, 512 text tokens (scaled to S if S
+    differs from 4096). A text token has t = h = w = p and advances p by 1; an
+    image of g x g patches starting at p0 gives the patch in row r, column c
+    the ids (p0, p0 + r, p0 + c) and then sets p = p0 + g. Finally a fraction
+    of all 3*B*S entries, picked without replacement, is moved out of
+    [0, rows): half negative (-1 - U[0, 2^31)), half at or beyond the table
+    (rows + U[0, 2^40), some past 2^31)."""
+    gen = SplitMix64(seed(index, 1))
+    ids = np.zeros((3, batch, seq), np.int64)
+    grid = 32 if seq >= 4096 else max(1, int(np.sqrt(seq // 4)))
+    img = grid * grid
+    text_total = seq - 2 * img
+    t1 = text_total // 4
+    t2 = text_total // 2
+    t3 = text_total - t1 - t2
+    plan = [("text", t1), ("image", img), ("text", t2), ("image", img), ("text", t3)]
+    for b in range(batch):
+        p = int(gen.below(1, 8192)[0])
+        s = 0
+        for kind, n in plan:
+            if kind == "text":
+                ids[:, b, s:s + n] = np.arange(p, p + n, dtype=np.int64)[None, :]
+                p += n
+                s += n
+            else:
+                r = np.repeat(np.arange(grid, dtype=np.int64), grid)
+                c = np.tile(np.arange(grid, dtype=np.int64), grid)
+                ids[0, b, s:s + n] = p
+                ids[1, b, s:s + n] = p + r
+                ids[2, b, s:s + n] = p + c
+                p += grid
+                s += n
+    n_oob = int(round(oob_fraction * ids.size))
+    if n_oob:
+        sel = SplitMix64(seed(index, 3))
+        flat = ids.reshape(-1)
+        picks = sample_without_replacement(sel, flat.size, n_oob)
+        for j, pos in enumerate(picks):
+            if j % 2 == 0:
+                flat[pos] = -1 - sel.below_big(1 << 31)
+            else:
+                flat[pos] = rows + sel.below_big(1 << 40)
+    return ids
+
+
+WORKLOADS = {
+    "c1_rope_f32_tiny": Workload(
+        index=0, name="c1_rope_f32_tiny", op="rope", dtype=np.float32,
+        x_shape=(1, 2, 16, 8), has_ids=False, cache_base=10000.0,
+        description="RotaryEmbedding rank-4 fp32 (1,2,16,8), (1,16,4) per-token table, no ids"),
+    "c2_rope_f16_prefill": Workload(
+        index=1, name="c2_rope_f16_prefill", op="rope", dtype=np.float16,
+        x_shape=(4, 2048, 4096), num_heads=32, cache_rows=8192, cache_base=1e6,
+        extra={"ids": "offset_arange", "offset_bound": 4096},
+        description="RotaryEmbedding rank-3 fp16 (4,2048,4096), 32 heads of 128, "
+                    "ids = per-batch offset + arange, table (8192,64) base 1e6"),
+    "c3_rope_f32_partial_interleaved": Workload(
+        index=2, name="c3_rope_f32_partial_interleaved", op="rope", dtype=np.float32,
+        x_shape=(8, 32, 1024, 96), rotary_embedding_dim=64, interleaved=1,
+        cache_rows=4096, cache_base=10000.0, extra={"ids": "uniform", "id_bound": 4096},
+        description="RotaryEmbedding rank-4 fp32 (8,32,1024,96), R=64 interleaved, "
+                    "tail of 32 passed through, ids U[0,4096), table (4096,32)"),
+    "c4_mrope_f16_prefill": Workload(
+        index=3, name="c4_mrope_f16_prefill", op="mrope", dtype=np.float16,
+        x_shape=(2, 28, 4096, 128), num_heads=28, cache_rows=32768, cache_base=1e6,
+        mrope_section=(16, 24, 24), mrope_layout=0, scale=1.0,
+        extra={"oob_fraction": 0.01},
+        description="MRotaryEmbedding rank-4 fp16 (2,28,4096,128), section [16,24,24], "
+                    "text spans + 32x32 image grids, 1% ids out of range, table (32768,64)"),
+    "c5_rope_qk_f16_decode": Workload(
+        index=4, name="c5_rope_qk_f16_decode", op="rope_qk", dtype=np.float16,
+        x_shape=(256, 1, 4096), num_heads=32, k_shape=(256, 1, 1024), kv_num_heads=8,
+        cache_rows=32768, cache_base=1e6, extra={"ids": "uniform", "id_bound": 32768},
+        description="Decode Q+K fp16: batch 256, seq 1, Q 32 heads + K 8 heads of 128, "
+                    "positions U[0,32768), table (32768,64) or on the fly"),
+}
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def with_layout(w: Workload, layout: int) -> Workload:
+    from dataclasses import replace
+    return replace(w, mrope_layout=layout, name="%s_layout%d" % (w.name.rsplit("_layout", 1)[0], layout))

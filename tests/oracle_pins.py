@@ -1,0 +1,593 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each pin is a function of an `oracle.Oracle` that raises AssertionError when
+the oracle disagrees with something the pages or the mathematics fix: a
+library routine (numpy's binary16 conversion, complex multiplication), an
+arbitrary-precision evaluation (mpmath), a hand-worked fixture, an invariant
+the pages state, or a brute force on tiny inputs. They run against the real
+oracle (test_oracle_pins.py) and against builds with planted mistakes
+(test_oracle_mutants.py), where at least one must fail.
+"""
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+
+from rope_inputs import SplitMix64, normal_tensor, get as get_workload
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+mpmath.mp.prec = 200
+
+
+def bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint16 if a.dtype == np.float16 else np.uint32)
+
+
+def assert_bitwise(a, b, what):
+    ba, bb = bits(a), bits(b)
+    bad = np.flatnonzero(ba.reshape(-1) != bb.reshape(-1))
+    assert bad.size == 0, "%s: %d elements differ bitwise, first at flat %d: %r vs %r" % (
+        what, bad.size, bad[0], a.reshape(-1)[bad[0]], b.reshape(-1)[bad[0]])
+
+
+def assert_value_equal(a, b, what):
+    """Equal as numbers (+0 == -0), NaN == NaN."""
+    a64 = a.astype(np.float64).reshape(-1)
+    b64 = b.astype(np.float64).reshape(-1)
+    ok = (a64 == b64) | (np.isnan(a64) & np.isnan(b64))
+    bad = np.flatnonzero(~ok)
+    assert bad.size == 0, "%s: %d elements differ, first at %d: %r vs %r" % (
+        what, bad.size, bad[0], a64[bad[0]], b64[bad[0]])
+
+
+def angle_table(seed, rows, half, dtype):
+    """cos/sin of random angles, each rounded to dtype (independent of the oracle)."""
+    th = SplitMix64(seed).uniform(rows * half).reshape(rows, half) * (2 * np.pi)
+    return np.cos(th).astype(dtype), np.sin(th).astype(dtype)
+
+
+def ids_in(seed, shape, bound):
+    return SplitMix64(seed).below(int(np.prod(shape)), bound).reshape(shape)
+
+
+def pair_index(interleaved, half):
+    i = np.arange(half)
+    if interleaved:
+        return 2 * i, 2 * i + 1
+    return i, i + half
+
+
+def to_rank4(x, num_heads):
+    """(B,S,H*D) -> (B,H,S,D)"""
+    B, S, hid = x.shape
+    return np.ascontiguousarray(x.reshape(B, S, num_heads, hid // num_heads).transpose(0, 2, 1, 3))
+
+
+def f32_of_mp(v):
+    return np.float32(float(v))
+
+
+# --------------------------------------------------------------------------
+# binary16 conversions against numpy's (a library routine)
+
+def pin_f16_decode_exhaustive(orc):
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = allbits.view(np.float16).astype(np.float64)
+    got = np.array([orc.f16_to_f64(int(b)) for b in allbits])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    same &= np.signbit(got) == np.signbit(ref)
+    assert same.all(), "binary16 decode differs at %s" % np.flatnonzero(~same)[:5]
+
+
+def pin_f16_encode_vs_numpy(orc):
+    g = SplitMix64(7)
+    mags = np.exp2(g.uniform(20000) * 48.0 - 30.0)          # 2^-30 .. 2^18
+    signs = np.where(g.uniform(20000) < 0.5, -1.0, 1.0)
+    vals = list(mags * signs)
+    # every tie point between neighbouring binary16 values, and its neighbours
+    h = np.arange(0, 0x7c00, 97, dtype=np.uint32).astype(np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2
+    vals += list(mid) + list(np.nextafter(mid, 0)) + list(np.nextafter(mid, 1e9))
+    vals += [0.0, -0.0, 65504.0, 65519.99, 65520.0, 1e9, -1e9, 2.0 ** -24, 2.0 ** -25,
+             3 * 2.0 ** -26, 2.0 ** -14 - 2.0 ** -25, float("inf"), -float("inf")]
+    vals = np.array(vals)
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f64_to_f16(float(v)) for v in vals], np.uint16)
+    bad = np.flatnonzero(ref != got)
+    assert bad.size == 0, "binary16 encode differs for %r" % vals[bad[:5]]
+    assert np.isnan(np.uint16(orc.f64_to_f16(float("nan"))).view(np.float16))
+
+
+# --------------------------------------------------------------------------
+# hand-worked cases (tests/golden/hand_rotations.json)
+
+def pin_hand_worked(orc):
+    with open(os.path.join(GOLDEN, "hand_rotations.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        for dt, key in ((np.float32, "f32"), (np.float16, "f16")):
+            x = np.array(case["x"], dt).reshape(1, 1, 1, 4)
+            c = np.array(case["cos"], dt)
+            s = np.array(case["sin"], dt)
+            for il, pk in ((0, "half_split"), (1, "interleaved")):
+                want = np.array(case["expected"][pk][key], dt)
+                # per-token (B,S,R/2) table, no ids
+                y = orc.rope_apply(x, c.reshape(1, 1, 2), s.reshape(1, 1, 2), interleaved=il)
+                assert_value_equal(y.reshape(-1), want, "%s %s %s" % (case["name"], key, pk))
+                # gathered (M,R/2) table, id 2 of 3 rows
+                ct = np.stack([np.zeros(2, dt), np.ones(2, dt), c])
+                st = np.stack([np.ones(2, dt), np.zeros(2, dt), s])
+                y = orc.rope_apply(x, ct, st, np.array([[2]]), interleaved=il)
+                assert_value_equal(y.reshape(-1), want, "%s %s %s ids" % (case["name"], key, pk))
+
+
+# --------------------------------------------------------------------------
+# the rotation against two independent formulations
+
+def pin_complex_multiplication(orc):
+    """Pair (x1, x2) as x1 + i*x2 times c + i*s (numpy complex128), rounded once."""
+    for dt in (np.float32, np.float16):
+        for il in (0, 1):
+            for rank in (3, 4):
+                B, S, H, D, M = 2, 5, 3, 12, 17
+                x = normal_tensor(11, (B, H, S, D), dt)
+                cos, sin = angle_table(12, M, D // 2, dt)
+                ids = ids_in(13, (B, S), M)
+                j1, j2 = pair_index(il, D // 2)
+                z = x[..., j1].astype(np.complex128) + 1j * x[..., j2].astype(np.complex128)
+                w = cos[ids].astype(np.complex128) + 1j * sin[ids].astype(np.complex128)
+                prod = z * w[:, None, :, :]
+                want = np.empty_like(x)
+                want[..., j1] = prod.real.astype(dt)
+                want[..., j2] = prod.imag.astype(dt)
+                if rank == 4:
+                    y = orc.rope_apply(x, cos, sin, ids, interleaved=il)
+                else:
+                    x3 = np.ascontiguousarray(x.transpose(0, 2, 1, 3)).reshape(B, S, H * D)
+                    y = to_rank4(orc.rope_apply(x3, cos, sin, ids, interleaved=il, num_heads=H), H)
+                assert_bitwise(y, want, "complex form dt=%s il=%d rank=%d" % (dt.__name__, il, rank))
+
+
+def pin_rotate_half_form(orc):
+    """q*cat(c,c) + rotate_half(q)*cat(s,s), rotate_half(q) = cat(-q2, q1), on the
+    leading R elements, the rest concatenated back unchanged (partial rotation)."""
+    for dt in (np.float32, np.float16):
+        for D, R in ((16, 16), (16, 8), (10, 4)):
+            B, H, S, M = 2, 2, 7, 9
+            x = normal_tensor(21, (B, H, S, D), dt)
+            cos, sin = angle_table(22, M, R // 2, dt)
+            ids = ids_in(23, (B, S), M)
+            q = x.astype(np.float64)
+            q_rot, q_pass = q[..., :R], q[..., R:]
+            C = np.concatenate([cos[ids], cos[ids]], -1).astype(np.float64)[:, None]
+            Sn = np.concatenate([sin[ids], sin[ids]], -1).astype(np.float64)[:, None]
+            rot_half = np.concatenate([-q_rot[..., R // 2:], q_rot[..., :R // 2]], -1)
+            emb = (q_rot * C + rot_half * Sn).astype(dt)
+            want = np.concatenate([emb, x[..., R:]], -1)
+            y = orc.rope_apply(x, cos, sin, ids, rotary_embedding_dim=R if R != D else 0)
+            assert_bitwise(y, want, "rotate_half form dt=%s D=%d R=%d" % (dt.__name__, D, R))
+            assert_bitwise(y[..., R:], q_pass.astype(dt), "pass-through")
+
+
+# --------------------------------------------------------------------------
+# invariants
+
+def pin_identity(orc):
+    for dt in (np.float32, np.float16):
+        x = normal_tensor(31, (2, 3, 4, 8), dt)
+        ones = np.ones((5, 4), dt)
+        zeros = np.zeros((5, 4), dt)
+        for il in (0, 1):
+            y = orc.rope_apply(x, ones, zeros, ids_in(32, (2, 4), 5), interleaved=il)
+            assert_value_equal(y, x, "identity")
+
+
+def pin_norm_preserved(orc):
+    for dt, rel in ((np.float32, 4 * 2.0 ** -24), (np.float16, 4 * 2.0 ** -11)):
+        for il in (0, 1):
+            x = normal_tensor(41, (2, 4, 6, 16), dt)
+            cos, sin = angle_table(42, 11, 8, dt)
+            # the rounded table has c^2 + s^2 != 1: compare against the exact product
+            ids = ids_in(43, (2, 6), 11)
+            y = orc.rope_apply(x, cos, sin, ids, interleaved=il).astype(np.float64)
+            j1, j2 = pair_index(il, 8)
+            xd = x.astype(np.float64)
+            c = cos[ids].astype(np.float64)[:, None]
+            s = sin[ids].astype(np.float64)[:, None]
+            n_in = (xd[..., j1] ** 2 + xd[..., j2] ** 2) * (c ** 2 + s ** 2)
+            n_out = y[..., j1] ** 2 + y[..., j2] ** 2
+            err = np.abs(n_out - n_in) / np.maximum(n_in, 1e-3)
+            assert err.max() <= rel * 2, "norm not preserved: %g" % err.max()
+
+
+def pin_inverse(orc):
+    x = normal_tensor(51, (2, 3, 5, 8), np.float32)
+    cos, sin = angle_table(52, 7, 4, np.float32)
+    ids = ids_in(53, (2, 5), 7)
+    for il in (0, 1):
+        y = orc.rope_apply(x, cos, sin, ids, interleaved=il)
+        back = orc.rope_apply(y, cos, -sin, ids, interleaved=il)
+        err = np.abs(back.astype(np.float64) - x.astype(np.float64))
+        # two rotations by a rounded unit vector: |c^2+s^2-1| <= 2^-23 plus 2 roundings
+        assert err.max() <= 4 * 2.0 ** -24 * max(1.0, np.abs(x).max()) * 4, err.max()
+
+
+def pin_tail_bitwise(orc):
+    for dt, nan in ((np.float32, np.uint32(0x7fa00123)), (np.float16, np.uint16(0x7e55))):
+        x = normal_tensor(61, (2, 2, 3, 10), dt)
+        raw = bits(x).copy()
+        raw[..., 6] = nan                                  # NaN payload in the tail
+        raw[..., 7] = 0x8000 if dt == np.float16 else 0x80000000   # -0
+        x = raw.view(dt)
+        cos, sin = angle_table(62, 4, 3, dt)
+        for il in (0, 1):
+            y = orc.rope_apply(x, cos, sin, ids_in(63, (2, 3), 4), interleaved=il,
+                               rotary_embedding_dim=6)
+            assert_bitwise(y[..., 6:], x[..., 6:], "tail")
+
+
+def pin_pairing_permutation(orc):
+    """interleaved(P x) == P half_split(x), P: j -> 2j, R/2 + j -> 2j + 1 on [0,R)."""
+    for dt in (np.float32, np.float16):
+        D, R = 12, 8
+        x = normal_tensor(71, (2, 3, 4, D), dt)
+        cos, sin = angle_table(72, 6, R // 2, dt)
+        ids = ids_in(73, (2, 4), 6)
+        perm = np.arange(D)
+        perm[:R] = np.concatenate([np.arange(R // 2), np.arange(R // 2, R)]).reshape(2, -1).T.reshape(-1)
+        # perm[2j] = j, perm[2j+1] = R/2 + j
+        xp = np.ascontiguousarray(x[..., perm])
+        a = orc.rope_apply(xp, cos, sin, ids, interleaved=1, rotary_embedding_dim=R)
+        b = orc.rope_apply(x, cos, sin, ids, interleaved=0, rotary_embedding_dim=R)
+        assert_bitwise(a, np.ascontiguousarray(b[..., perm]), "pairing permutation")
+
+
+def pin_rank_transpose(orc):
+    for dt in (np.float32, np.float16):
+        B, S, H, D = 3, 5, 4, 8
+        x3 = normal_tensor(81, (B, S, H * D), dt)
+        cos, sin = angle_table(82, 9, D // 2, dt)
+        ids = ids_in(83, (B, S), 9)
+        for il in (0, 1):
+            y3 = orc.rope_apply(x3, cos, sin, ids, interleaved=il, num_heads=H)
+            y4 = orc.rope_apply(to_rank4(x3, H), cos, sin, ids, interleaved=il)
+            assert_bitwise(to_rank4(y3, H), y4, "rank 3 vs rank 4")
+
+
+def pin_gather_probe(orc):
+    """Every pair (1, 0) -> the pair becomes (c, s) of the gathered row."""
+    for dt in (np.float32, np.float16):
+        B, H, S, D, M = 2, 3, 6, 8, 13
+        cos, sin = angle_table(91, M, D // 2, dt)
+        ids = ids_in(92, (B, S), M)
+        ids[0, 0] = 0
+        ids[1, 2] = M - 1
+        for il in (0, 1):
+            j1, j2 = pair_index(il, D // 2)
+            x = np.zeros((B, H, S, D), dt)
+            x[..., j1] = 1
+            y = orc.rope_apply(x, cos, sin, ids, interleaved=il)
+            for h in range(H):
+                assert_bitwise(y[:, h][..., j1], cos[ids], "probe cos")
+                assert_bitwise(y[:, h][..., j2], sin[ids], "probe sin")
+
+
+def pin_per_token_table(orc):
+    """No ids with table T3[b][s] = T2[ids[b][s]] equals the gathered call."""
+    for dt in (np.float32, np.float16):
+        for rank in (3, 4):
+            B, S, H, D, M = 3, 4, 2, 8, 7
+            x = normal_tensor(101, (B, H, S, D) if rank == 4 else (B, S, H * D), dt)
+            cos, sin = angle_table(102, M, D // 2, dt)
+            ids = ids_in(103, (B, S), M)
+            ids[0, 0] = 0
+            nh = 0 if rank == 4 else H
+            a = orc.rope_apply(x, cos, sin, ids, num_heads=nh)
+            b = orc.rope_apply(x, np.ascontiguousarray(cos[ids]), np.ascontiguousarray(sin[ids]),
+                               num_heads=nh)
+            assert_bitwise(a, b, "per-token table rank %d" % rank)
+
+
+def pin_out_of_range_ids(orc):
+    """Reading taken: an id outside [0, M) passes the whole row through."""
+    for dt in (np.float32, np.float16):
+        B, H, S, D, M = 2, 2, 6, 8, 5
+        x = normal_tensor(111, (B, H, S, D), dt)
+        cos, sin = angle_table(112, M, D // 2, dt)
+        ids = ids_in(113, (B, S), M)
+        ids[0, 1] = -1
+        ids[1, 3] = M
+        ids[1, 4] = 2 ** 40
+        ids[0, 0] = 0
+        y = orc.rope_apply(x, cos, sin, ids)
+        for b, s in ((0, 1), (1, 3), (1, 4)):
+            assert_bitwise(y[b, :, s], x[b, :, s], "out-of-range row")
+        assert not np.array_equal(bits(y[0, :, 0]), bits(x[0, :, 0]))
+
+
+def pin_empty(orc):
+    for shape in ((0, 2, 3, 8), (2, 2, 0, 8), (2, 0, 3, 8)):
+        x = np.zeros(shape, np.float32)
+        y = orc.rope_apply(x, np.zeros((3, 4), np.float32), np.zeros((3, 4), np.float32),
+                           np.zeros((shape[0], shape[2]), np.int64))
+        assert y.shape == shape
+
+
+# --------------------------------------------------------------------------
+# tables against arbitrary precision (the cache spot check of the ORT review:
+# positions 0, 1, 7, 100, 1000 against cos(pos * inv_freq) * scaling)
+
+def _mp_inv_freq(base, R):
+    return [f32_of_mp(mpmath.power(mpmath.mpf(base), mpmath.mpf(-2 * i) / R)) for i in range(R // 2)]
+
+
+def pin_inv_freq(orc):
+    for base, R in ((1e6, 128), (1e4, 64), (1e4, 8), (5e5, 96), (1e4, 2)):
+        want = np.array(_mp_inv_freq(base, R), np.float32)
+        got = orc.inv_freq(base, R)
+        assert_bitwise(got, want, "inv_freq base=%g R=%d" % (base, R))
+
+
+def pin_cache_spot_rows(orc):
+    rows = (0, 1, 7, 100, 1000)
+    for dt, base, R, scaling in ((np.float16, 1e6, 128, 1.0), (np.float32, 1e6, 128, 1.0),
+                                 (np.float32, 1e4, 64, 1.0), (np.float16, 1e4, 64, 1.25),
+                                 (np.float32, 1e6, 128, 0.7)):
+        inv = np.array(_mp_inv_freq(base, R), np.float32)
+        cos, sin = orc.cos_sin_cache(dt, 1001, inv, scaling)
+        assert cos.shape == (1001, R // 2)
+        sc = np.float32(scaling)
+        for p in rows:
+            for i in range(R // 2):
+                th = np.float32(np.float64(np.float32(p)) * np.float64(inv[i]))
+                c = f32_of_mp(mpmath.cos(mpmath.mpf(float(th))))
+                s = f32_of_mp(mpmath.sin(mpmath.mpf(float(th))))
+                c = np.float32(np.float64(c) * np.float64(sc)).astype(dt)
+                s = np.float32(np.float64(s) * np.float64(sc)).astype(dt)
+                assert bits(np.array([cos[p, i]]))[0] == bits(np.array([c]))[0], (dt, p, i, cos[p, i], c)
+                assert bits(np.array([sin[p, i]]))[0] == bits(np.array([s]))[0], (dt, p, i, sin[p, i], s)
+        if scaling == 1.0:
+            assert (cos[0] == 1).all() and (bits(sin[0]) == 0).all()
+
+
+def pin_c1_against_real_math(orc):
+    """The toy workload: every output against cos/sin(s * 10000^(-2i/8)) evaluated
+    in arbitrary precision, once with the table's binary32 roundings reproduced
+    (bit-exact) and once in exact real arithmetic (1e-5 relative)."""
+    w = get_workload("c1_rope_f32_tiny")
+    x = w.make_x()
+    inv = orc.inv_freq(10000.0, 8)
+    cos, sin = orc.cos_sin_cache(np.float32, 16, inv)
+    y = orc.rope_apply(x, cos.reshape(1, 16, 4), sin.reshape(1, 16, 4))
+    inv_mp = _mp_inv_freq(10000.0, 8)
+    for h in range(2):
+        for s in range(16):
+            for i in range(4):
+                x1 = mpmath.mpf(float(x[0, h, s, i]))
+                x2 = mpmath.mpf(float(x[0, h, s, i + 4]))
+                th = np.float32(np.float64(np.float32(s)) * np.float64(inv_mp[i]))
+                c = mpmath.mpf(float(f32_of_mp(mpmath.cos(mpmath.mpf(float(th))))))
+                sn = mpmath.mpf(float(f32_of_mp(mpmath.sin(mpmath.mpf(float(th))))))
+                assert y[0, h, s, i] == f32_of_mp(x1 * c - x2 * sn), (h, s, i)
+                assert y[0, h, s, i + 4] == f32_of_mp(x2 * c + x1 * sn), (h, s, i)
+                thr = s * mpmath.power(10000, mpmath.mpf(-2 * i) / 8)
+                r1 = x1 * mpmath.cos(thr) - x2 * mpmath.sin(thr)
+                r2 = x2 * mpmath.cos(thr) + x1 * mpmath.sin(thr)
+                assert abs(float(r1) - float(y[0, h, s, i])) <= 1e-5 * max(1.0, abs(float(r1)))
+                assert abs(float(r2) - float(y[0, h, s, i + 4])) <= 1e-5 * max(1.0, abs(float(r2)))
+
+
+# --------------------------------------------------------------------------
+# M-RoPE
+
+def _stride3_rule(half, section):
+    """The stride-3 slot rule of the interleaved multimodal models: slot i -> h if
+    i % 3 == 1 and i < 3*sec_h, -> w if i % 3 == 2 and i < 3*sec_w, else t."""
+    out = []
+    for i in range(half):
+        if i % 3 == 1 and i < 3 * section[1]:
+            out.append(1)
+        elif i % 3 == 2 and i < 3 * section[2]:
+            out.append(2)
+        else:
+            out.append(0)
+    return out
+
+
+def pin_mrope_section_maps(orc):
+    for half in range(1, 41):
+        for t in range(half + 1):
+            for h in range(half + 1 - t):
+                w = half - t - h
+                sec = (t, h, w)
+                m0 = list(orc.mrope_slot_streams(half, sec, 0))
+                assert m0 == [0] * t + [1] * h + [2] * w, (sec, m0)
+                m1 = list(orc.mrope_slot_streams(half, sec, 1))
+                assert [m1.count(k) for k in range(3)] == list(sec), (sec, m1)
+                lo = min(sec)
+                assert m1[:3 * lo] == [0, 1, 2] * lo, (sec, m1)
+                if h == w and h <= t:
+                    assert m1 == _stride3_rule(half, sec), (sec, m1)
+    assert list(orc.mrope_slot_streams(64, (24, 20, 20), 1)) == _stride3_rule(64, (24, 20, 20))
+    for bad in ((1, 1, 1), (-1, 3, 2), (5, 0, 0)):
+        try:
+            orc.mrope_slot_streams(4, bad, 0)
+        except ValueError:
+            continue
+        raise AssertionError("section %s accepted" % (bad,))
+
+
+def pin_mrope_equal_streams(orc):
+    """Text-only tokens (all streams equal) reduce M-RoPE to RotaryEmbedding."""
+    for dt in (np.float32, np.float16):
+        for rank, D, R in ((4, 16, 0), (3, 16, 8), (4, 9, 8), (3, 10, 6)):
+            for il in (0, 1):
+                B, S, H, M = 2, 5, 3, 11
+                Rf = R or D
+                shape = (B, H, S, D) if rank == 4 else (B, S, H * D)
+                x = normal_tensor(121, shape, dt)
+                cos, sin = angle_table(122, M, Rf // 2, dt)
+                ids = ids_in(123, (B, S), M)
+                ids3 = np.stack([ids, ids, ids])
+                sec = (Rf // 2 - 2 * (Rf // 6), Rf // 6, Rf // 6)
+                want = orc.rope_apply(x, cos, sin, ids, interleaved=il, num_heads=H if rank == 3 else 0,
+                                      rotary_embedding_dim=R)
+                for layout in (0, 1):
+                    y = orc.mrope_apply(x, ids3, cos, sin, sec, layout, interleaved=il,
+                                        num_heads=H, rotary_embedding_dim=R)
+                    assert_bitwise(y, want, "equal streams rank=%d D=%d R=%d il=%d layout=%d"
+                                   % (rank, D, R, il, layout))
+
+
+def _mrope_probe(orc, dt, section, layout, expect_map):
+    B, H, S, D, M = 2, 2, 7, 2 * sum(section), 50
+    half = D // 2
+    cos, sin = angle_table(131, M, half, dt)
+    ids = ids_in(132, (3, B, S), M)
+    ids[:, 0, 0] = (0, 1, 2)
+    for il in (0, 1):
+        j1, j2 = pair_index(il, half)
+        x = np.zeros((B, H, S, D), dt)
+        x[..., j1] = 1
+        y = orc.mrope_apply(x, ids, cos, sin, section, layout, interleaved=il, num_heads=H)
+        for b in range(B):
+            for s in range(S):
+                for i in range(half):
+                    p = ids[expect_map[i], b, s]
+                    got = y[b, :, s]
+                    assert (bits(got[:, j1[i]]) == bits(np.array([cos[p, i]]))[0]).all(), (section, layout, b, s, i)
+                    assert (bits(got[:, j2[i]]) == bits(np.array([sin[p, i]]))[0]).all(), (section, layout, b, s, i)
+
+
+def pin_mrope_stream_gather(orc):
+    """Probe X = (1, 0) per pair: slot i of token (b,s) must hold the table row of
+    its own stream. Maps written here independently: sections in order for
+    layout 0, the stride-3 rule for layout 1 (agrees with the reading taken
+    when sec_h == sec_w <= sec_t)."""
+    for dt in (np.float32, np.float16):
+        for sec in ((2, 1, 1), (16, 24, 24), (3, 0, 5), (24, 20, 20), (4, 2, 2)):
+            half = sum(sec)
+            _mrope_probe(orc, dt, sec, 0, [0] * sec[0] + [1] * sec[1] + [2] * sec[2])
+            if sec[1] == sec[2] <= sec[0]:
+                _mrope_probe(orc, dt, sec, 1, _stride3_rule(half, sec))
+
+
+def pin_mrope_out_of_range(orc):
+    for dt in (np.float32, np.float16):
+        for layout in (0, 1):
+            B, H, S, D, M = 2, 3, 9, 16, 20
+            sec = (4, 2, 2)
+            x = normal_tensor(141, (B, H, S, D), dt)
+            cos, sin = angle_table(142, M, D // 2, dt)
+            ids = ids_in(143, (3, B, S), M)
+            bad = ids.copy()
+            bad[0, 0, 1] = -5
+            bad[1, 0, 2] = M
+            bad[2, 1, 3] = 2 ** 33
+            bad[1, 1, 4] = -(2 ** 40)
+            bad[:, 1, 5] = -1
+            oob = (bad < 0) | (bad >= M)
+            y = orc.mrope_apply(x, bad, cos, sin, sec, layout, num_heads=H)
+            ref = orc.mrope_apply(x, ids, cos, sin, sec, layout, num_heads=H)
+            m = list(orc.mrope_slot_streams(D // 2, sec, layout))
+            for b in range(B):
+                for s in range(S):
+                    for i in range(D // 2):
+                        src = x if oob[m[i], b, s] else ref
+                        for j in (i, i + D // 2):
+                            assert bits(y[b, :, s, j:j + 1]).tolist() == bits(src[b, :, s, j:j + 1]).tolist(), \
+                                (layout, b, s, i)
+
+
+def pin_mrope_scale(orc):
+    """scale = 2 (exact) equals scale 1 with a doubled table; scale 0.5 likewise."""
+    for dt in (np.float32, np.float16):
+        B, H, S, D, M = 2, 2, 6, 12, 9
+        sec = (2, 2, 2)
+        x = normal_tensor(151, (B, H, S, D), dt)
+        cos, sin = angle_table(152, M, D // 2, dt)
+        ids = ids_in(153, (3, B, S), M)
+        for layout in (0, 1):
+            for sc in (2.0, 0.5):
+                a = orc.mrope_apply(x, ids, cos, sin, sec, layout, num_heads=H, scale=sc)
+                b = orc.mrope_apply(x, ids, (cos * dt(sc)).astype(dt), (sin * dt(sc)).astype(dt), sec,
+                                    layout, num_heads=H, scale=1.0)
+                assert_bitwise(a, b, "scale %g" % sc)
+
+
+def pin_mrope_tiny_brute_force(orc):
+    """The README's usage example shapes: x [2,2,16] with 2 heads (D=8), ids
+    [3,2,2], cos/sin [2,4], mrope_section [2,1,1]; every output against a
+    complex-multiplication brute force with the slot rows picked by hand."""
+    maps = {0: [0, 0, 1, 2], 1: [0, 1, 2, 0]}
+    for dt in (np.float32, np.float16):
+        x = normal_tensor(161, (2, 2, 16), dt)
+        cos, sin = angle_table(162, 2, 4, dt)
+        ids = ids_in(163, (3, 2, 2), 4) - 1          # values -1..2 with rows 0..1 valid
+        for layout in (0, 1):
+            for il in (0, 1):
+                y = orc.mrope_apply(x, ids, cos, sin, (2, 1, 1), layout, interleaved=il, num_heads=2)
+                j1, j2 = pair_index(il, 4)
+                for b in range(2):
+                    for s in range(2):
+                        for h in range(2):
+                            row = x[b, s, 8 * h:8 * h + 8]
+                            out = y[b, s, 8 * h:8 * h + 8]
+                            for i in range(4):
+                                p = ids[maps[layout][i], b, s]
+                                pair_in = (row[j1[i]], row[j2[i]])
+                                pair_out = (out[j1[i]], out[j2[i]])
+                                if p < 0 or p >= 2:
+                                    assert bits(np.array(pair_out)).tolist() == bits(np.array(pair_in)).tolist()
+                                    continue
+                                z = complex(float(pair_in[0]), float(pair_in[1])) * \
+                                    complex(float(cos[p, i]), float(sin[p, i]))
+                                assert pair_out[0] == dt(z.real) and pair_out[1] == dt(z.imag), \
+                                    (layout, il, b, s, h, i)
+
+
+# --------------------------------------------------------------------------
+# Q+K and on-the-fly
+
+def pin_qk_is_two_applies(orc):
+    for dt in (np.float32, np.float16):
+        for rank in (3, 4):
+            B, S, H, Hk, D, M = 3, 2, 4, 2, 8, 10
+            q = normal_tensor(171, (B, H, S, D) if rank == 4 else (B, S, H * D), dt)
+            k = normal_tensor(172, (B, Hk, S, D) if rank == 4 else (B, S, Hk * D), dt)
+            cos, sin = angle_table(173, M, D // 2, dt)
+            ids = ids_in(174, (B, S), M)
+            yq, yk = orc.rope_apply_qk(q, k, cos, sin, ids, num_heads=H, kv_num_heads=Hk)
+            assert_bitwise(yq, orc.rope_apply(q, cos, sin, ids, num_heads=H if rank == 3 else 0), "Q")
+            assert_bitwise(yk, orc.rope_apply(k, cos, sin, ids, num_heads=Hk if rank == 3 else 0), "K")
+
+
+def pin_onthefly_equals_table(orc):
+    for dt in (np.float32, np.float16):
+        for sc in (1.0, 1.25):
+            B, S, H, Hk, D, M = 4, 3, 4, 2, 16, 40000
+            inv = orc.inv_freq(1e6, D)
+            cos, sin = orc.cos_sin_cache(dt, M, inv, sc)
+            q = normal_tensor(181, (B, S, H * D), dt)
+            k = normal_tensor(182, (B, S, Hk * D), dt)
+            ids = ids_in(183, (B, S), M)
+            ids[0, 0] = 0
+            ids[1, 1] = M - 1
+            a = orc.rope_apply_qk(q, k, None, None, ids, num_heads=H, kv_num_heads=Hk,
+                                  inv_freq=inv, attention_scaling=sc)
+            b = orc.rope_apply_qk(q, k, cos, sin, ids, num_heads=H, kv_num_heads=Hk)
+            assert_bitwise(a[0], b[0], "on-the-fly Q")
+            assert_bitwise(a[1], b[1], "on-the-fly K")
+            for p in (0, 1, 7, 100, 1000, M - 1):
+                c, s = orc.onthefly_row(dt, p, inv, sc)
+                assert_bitwise(c, cos[p], "row %d cos" % p)
+                assert_bitwise(s, sin[p], "row %d sin" % p)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

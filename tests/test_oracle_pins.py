@@ -1,0 +1,11 @@
+"""The oracle against its pins (CPU only). See oracle_pins.py for what each pin
+compares against."""
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    pin(oracle.default())
