@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the rotary-embedding apply on one MI355X.
+
+A step is one rope_apply call of the fp16 prefill workload (X (4, 2048, 4096)
+in 32 heads of 128, int64 position ids gathering an (8192, 64) fp16 table,
+split-half pairing): read the ids, gather one cos/sin row per token, rotate
+every pair of every head in fp32 with one rounding, write Y. Inputs are
+seeded synthetic tensors resident in HBM before the timed region; launches
+rotate over independent (X, Y, ids) sets totalling >= 1 GiB so that the 256 MB
+last-level cache cannot hold them and the rate measured is HBM's.
+
+Prints ONE JSON line on stdout. Also reported (in "also"): the M-RoPE
+prefill in both section layouts, the fp32 partial interleaved case and the
+fp16 decode Q+K step (table and on the fly).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "RoPE apply achieved HBM GB/s and % of MI355X peak (fp16 prefill, M-RoPE)"
+PEAK_GBS = 8000.0            # MI355X HBM3E, published
+ROTATE_BYTES = 1 << 30       # >= 4x the 256 MB last-level cache
+HEADLINE = "c2_rope_f16_prefill"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_rope_f16_prefill.json")
+KERNEL_SOURCE = os.path.join(ROOT, "rotary_position_embedding_amd", "csrc", "rope_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+# ---------------------------------------------------------------------------
+# workload set-up: inputs generated on the host from the seeded generators,
+# tables built on the GPU by the library itself
+
+def setup(w, onthefly=False):
+    import torch
+    import rotary_position_embedding_amd as rpe
+    dev = torch.device("cuda:0")
+    dt = torch.float16 if w.dtype == np.float16 else torch.float32
+    x0 = torch.from_numpy(w.make_x()).to(dev)
+    ids_h = w.make_ids()
+    ids0 = None if ids_h is None else torch.from_numpy(ids_h).to(dev)
+    k0 = torch.from_numpy(w.make_k()).to(dev) if w.op == "rope_qk" else None
+    inv = rpe.rope_inv_freq(w.rotary_dim, w.cache_base, device=dev)
+    if w.op == "rope" and not w.has_ids:
+        cos, sin = rpe.rope_cos_sin_cache(inv, w.seq, dt, w.scaling)
+        cos = cos.unsqueeze(0).expand(w.batch, -1, -1).contiguous()
+        sin = sin.unsqueeze(0).expand(w.batch, -1, -1).contiguous()
+    else:
+        cos, sin = rpe.rope_cos_sin_cache(inv, w.cache_rows, dt, w.scaling)
+    set_bytes = 2 * x0.numel() * x0.element_size()
+    if k0 is not None:
+        set_bytes += 2 * k0.numel() * k0.element_size()
+    nsets = max(2, -(-ROTATE_BYTES // set_bytes))
+    launchers = []
+    for _ in range(nsets):
+        x = x0.clone()
+        ids = None if ids0 is None else ids0.clone()
+        if w.op == "rope":
+            y = torch.empty_like(x)
+            launchers.append(rpe.rope_apply_launcher(
+                x, cos, sin, ids, y, interleaved=w.interleaved,
+                num_heads=w.num_heads if w.rank == 3 else 0,
+                rotary_embedding_dim=w.rotary_embedding_dim))
+        elif w.op == "mrope":
+            y = torch.empty_like(x)
+            launchers.append(rpe.mrope_apply_launcher(
+                x, ids, cos, sin, y, mrope_section=w.mrope_section, mrope_layout=w.mrope_layout,
+                interleaved=w.interleaved, num_heads=w.num_heads,
+                rotary_embedding_dim=w.rotary_embedding_dim, scale=w.scale))
+        else:
+            k = k0.clone()
+            yq, yk = torch.empty_like(x), torch.empty_like(k)
+            if onthefly:
+                launchers.append(rpe.rope_apply_qk_launcher(
+                    x, k, None, None, ids, yq, yk, num_heads=w.num_heads,
+                    kv_num_heads=w.kv_num_heads, inv_freq=inv, attention_scaling=w.scaling))
+            else:
+                launchers.append(rpe.rope_apply_qk_launcher(
+                    x, k, cos, sin, ids, yq, yk, num_heads=w.num_heads,
+                    kv_num_heads=w.kv_num_heads))
+    torch.cuda.synchronize()
+    return launchers, nsets * set_bytes
+
+
+def time_steps(launchers, steps, warmup):
+    """(ms per step over the K-step region, mean kernel ms from per-launch events)."""
+    import torch
+    n = len(launchers)
+    for i in range(warmup):
+        launchers[i % n]()
+    torch.cuda.synchronize()
+    # timed region: K steps between two events, synchronised on both sides
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        launchers[i % n]()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    # per-launch durations: an event pair around each launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        launchers[i % n]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+    return ms_step, float(per.mean()), float(np.median(per))
+
+
+def measure(w, steps, warmup, onthefly=False):
+    launchers, rot = setup(w, onthefly)
+    ms_step, ms_kernel, ms_med = time_steps(launchers, steps, warmup)
+    nbytes = w.algorithmic_bytes(onthefly)
+    return {
+        "workload": w.name + ("_onthefly" if onthefly else ""),
+        "bytes_per_step": nbytes,
+        "ms_per_step": ms_step,
+        "gbs": nbytes / (ms_step * 1e-3) / 1e9,
+        "kernel_ms_mean": ms_kernel,
+        "kernel_ms_median": ms_med,
+        "kernel_gbs": nbytes / (ms_kernel * 1e-3) / 1e9,
+        "frac_of_peak": nbytes / (ms_kernel * 1e-3) / 1e9 / PEAK_GBS,
+        "tokens_heads_per_s": w.tokens_heads() / (ms_step * 1e-3),
+        "rotation_sets_bytes": rot,
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on the host cores of this machine
+
+def cpu_baseline(w, budget_s=10.0):
+    import oracle
+    x = w.make_x()
+    ids = w.make_ids()
+    cos, sin = oracle.table_for(w)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.rope_apply(x, cos, sin, ids, interleaved=w.interleaved,
+                          num_heads=w.num_heads if w.rank == 3 else 0,
+                          rotary_embedding_dim=w.rotary_embedding_dim)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    nbytes = w.algorithmic_bytes() * reps
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "the whole %s input (%d tokens x %d heads), %d repetitions, %.1f s, "
+                      "single-threaded scalar C oracle (binary64)" % (w.name, w.tokens, w.heads, reps, el)}
+
+
+def traffic_for_headline():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it is now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE,
+                    help="workload to time alone (for profiler runs); implies --no-extra")
+    ap.add_argument("--onthefly", action="store_true", help="with the decode Q+K workload")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time plain 128 MiB device copies instead (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the rotary apply has no cross-GPU step and this "
+              "build runs on a single MI355X; --gpus %d is not supported" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rope_inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_calibration:
+        n = 64 << 20
+        a = torch.ones(n, dtype=torch.float16, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(args.warmup):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        log("copy %d bytes x %d: %.1f GB/s" % (2 * n, args.steps, 2 * 2 * n * args.steps / el / 1e9))
+        print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "steps": args.steps}))
+        return
+
+    only = args.workload != HEADLINE or args.no_extra
+    w = rope_inputs.get(args.workload)
+    log("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
+    head = measure(w, args.steps, args.warmup, args.onthefly)
+    log("  %.2f us/step, %.1f GB/s; kernel %.2f us mean, %.1f GB/s (%.1f%% of %g)" % (
+        head["ms_per_step"] * 1e3, head["gbs"], head["kernel_ms_mean"] * 1e3, head["kernel_gbs"],
+        100 * head["frac_of_peak"], PEAK_GBS))
+
+    also = []
+    if not only:
+        extra = [(rope_inputs.with_layout(rope_inputs.get("c4_mrope_f16_prefill"), 0), False),
+                 (rope_inputs.with_layout(rope_inputs.get("c4_mrope_f16_prefill"), 1), False),
+                 (rope_inputs.get("c3_rope_f32_partial_interleaved"), False),
+                 (rope_inputs.get("c5_rope_qk_f16_decode"), False),
+                 (rope_inputs.get("c5_rope_qk_f16_decode"), True)]
+        for ew, otf in extra:
+            log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
+            r = measure(ew, min(args.steps, 100), min(args.warmup, 10), otf)
+            log("  %.2f us/step, %.1f GB/s; kernel %.2f us, %.1f%% of peak" % (
+                r["ms_per_step"] * 1e3, r["gbs"], r["kernel_ms_mean"] * 1e3, 100 * r["frac_of_peak"]))
+            also.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
+
+    cpu = None
+    if not args.no_cpu_baseline and w.op == "rope":
+        log("cpu baseline (oracle) on %s" % w.name)
+        cpu = cpu_baseline(w)
+        log("  %.3f GB/s" % cpu["value"])
+
+    traffic = traffic_for_headline() if w.name == HEADLINE else None
+    result = {
+        "metric": METRIC,
+        "value": round(head["gbs"], 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "description": w.description,
+            "storage_dtype": np.dtype(w.dtype).name,
+            "x_shape": list(w.x_shape),
+            "bytes_per_step": head["bytes_per_step"],
+            "tokens_heads_per_s": round(head["tokens_heads_per_s"], 1),
+            "rotation_sets_bytes": head["rotation_sets_bytes"],
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(head["kernel_gbs"], 3),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["kernel_gbs"] / PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_us_mean": round(head["kernel_ms_mean"] * 1e3, 3),
+            "kernel_us_median": round(head["kernel_ms_median"] * 1e3, 3),
+            "algorithmic_bytes_per_launch": head["bytes_per_step"],
+        },
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * rope_mi355x.h -- C ABI of the rotary position embedding library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operations (the pages are cited by title and section):
+ *   rope_apply         ONNX RotaryEmbedding -- "ai.onnx.RotaryEmbedding"
+ *                      WebGPU kernel manifest: inputs, attributes,
+ *                      attributeDescriptions, derive contracts, variants.
+ *   mrope_apply        com.microsoft.MRotaryEmbedding -- its README:
+ *                      Description, Inputs, Attributes.
+ *   rope_apply_qk      Q and K of one attention layer rotated with the same
+ *                      coefficients, from a table or computed on the fly --
+ *                      onnxruntime PR #27590 (Motivation; review "Modeling
+ *                      Code Alignment Check": Qwen3RotaryEmbedding.forward,
+ *                      apply_rotary_pos_emb, GQA) and the
+ *                      "com.microsoft.SparseAttention" README (Attributes:
+ *                      kv_num_heads, rotary on Q and on K).
+ *   rope_inv_freq,     the frequency vector and the cos/sin table the
+ *   rope_cos_sin_cache gathered ops read -- PR #27590 review item 4
+ *                      (cos_cache = cos(pos * inv_freq) * scaling).
+ *
+ * Conventions for every entry point
+ *   - Tensors are described by rope_tensor: a DEVICE pointer to dense
+ *     row-major data, an ONNX TensorProto element type and a shape.
+ *     Storage types: ROPE_FLOAT (binary32) and ROPE_FLOAT16 (binary16);
+ *     positions are ROPE_INT64.
+ *   - The caller owns every buffer. The library never allocates, frees,
+ *     copies to the host or synchronises: it validates on the host, then
+ *     enqueues its kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns. Results are ready when the stream reaches them.
+ *   - Validation is complete before anything is enqueued: a non-zero return
+ *     means nothing was launched. ROPE_ERR_LAUNCH means a launch was
+ *     attempted and the HIP runtime refused it.
+ *   - A tensor with a zero dimension is valid; an op whose output is empty
+ *     launches nothing and returns ROPE_OK. Data pointers of non-empty
+ *     tensors must not be NULL.
+ *   - Outputs may be the same buffer as their input (y == x, in place);
+ *     any other overlap between an output and an input or another output is
+ *     ROPE_ERR_ALIAS.
+ *   - Arithmetic: products and sums in binary32 with fused multiply-add,
+ *     one rounding to the storage type at the end; subnormals kept.
+ *     Pass-through elements (the tail beyond the rotary dimension, pairs
+ *     with an out-of-range position) are bit copies.
+ *   - Stateless and thread-safe; rope_last_error() is per thread.
+ */
+#ifndef ROPE_MI355X_H
+#define ROPE_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ONNX TensorProto element types. */
+#define ROPE_FLOAT 1
+#define ROPE_INT64 7
+#define ROPE_FLOAT16 10
+
+typedef struct rope_tensor {
+    void* data;       /* device pointer, dense row-major */
+    int32_t dtype;    /* ROPE_FLOAT, ROPE_FLOAT16 or ROPE_INT64 */
+    int32_t rank;     /* 1..4 */
+    int64_t shape[4]; /* entries beyond `rank` are ignored */
+} rope_tensor;
+
+enum rope_status {
+    ROPE_OK = 0,
+    ROPE_ERR_NULL = -1,        /* missing tensor or NULL data of a non-empty tensor */
+    ROPE_ERR_DTYPE = -2,       /* storage type not allowed or inputs disagree */
+    ROPE_ERR_RANK = -3,        /* tensor rank not allowed */
+    ROPE_ERR_SHAPE = -4,       /* a shape clause of the op's contract fails */
+    ROPE_ERR_ATTRIBUTE = -5,   /* attribute value outside its allowed set */
+    ROPE_ERR_UNSUPPORTED = -6, /* defined by the op but not implemented here */
+    ROPE_ERR_ALIAS = -7,       /* an output overlaps an input or another output */
+    ROPE_ERR_LAUNCH = -8       /* the HIP runtime rejected a kernel launch */
+};
+
+/* Name of a status code ("ROPE_OK", ...). Never NULL. */
+const char* rope_status_string(int status);
+
+/* Human-readable reason of the last non-zero status returned on this thread
+ * (which contract clause failed). Empty string if none. */
+const char* rope_last_error(void);
+
+/*
+ * rope_apply -- ONNX RotaryEmbedding ("ai.onnx.RotaryEmbedding" manifest).
+ *
+ * x:            rank 3 (B, S, H*D) with num_heads = H, or rank 4 (B, H, S, D).
+ *               D must be even. Storage type T in {ROPE_FLOAT, ROPE_FLOAT16}.
+ * cos_cache,
+ * sin_cache:    type T, same shape. With position_ids: (M, R/2), row p
+ *               serves position p. Without: (B, S, R/2), row (b, s) serves
+ *               token (b, s). (manifest `inputs`, `derive`.)
+ * position_ids: NULL (absent) or int64 (B, S). An id outside [0, M) passes
+ *               the token's rotary pairs through unchanged and never reads
+ *               the table (the manifest keeps such ids outside its contract;
+ *               this is the behaviour taken).
+ * y:            same shape and type as x; may be x itself.
+ * interleaved:  0 = pairs (i, i + R/2) (split halves), 1 = pairs (2i, 2i+1).
+ * num_heads:    required (>= 1) for rank 3; for rank 4, 0 or dim 1 of x.
+ * rotary_embedding_dim: 0 = R = D, else the even R <= D of leading elements
+ *               rotated; elements R..D-1 are copied.
+ * Per pair with coefficients (c, s) of its slot i:
+ *   y1 = x1*c - x2*s,  y2 = x2*c + x1*s.
+ */
+int rope_apply(const rope_tensor* x, const rope_tensor* cos_cache,
+               const rope_tensor* sin_cache, const rope_tensor* position_ids,
+               const rope_tensor* y, int64_t interleaved, int64_t num_heads,
+               int64_t rotary_embedding_dim, void* stream);
+
+/*
+ * mrope_apply -- com.microsoft.MRotaryEmbedding (its README).
+ *
+ * x:            rank 3 (B, S, H*D) or rank 4 (B, H, S, D), type T.
+ * position_ids: int64 (3, B, S): temporal, height, width streams. Required.
+ * cos_cache,
+ * sin_cache:    type T, (M, R/2), shared by the three streams.
+ * y:            same shape and type as x; may be x itself.
+ * interleaved:  pairing as for rope_apply; independent of mrope_layout.
+ * is_packed_batching: must be 0 (1 is ROPE_ERR_UNSUPPORTED, as on the page).
+ * mrope_layout: 0 = sectioned (slots [0,t) temporal, then h height, then w
+ *               width); 1 = interleaved: slots dealt to t, h, w in turn, a
+ *               stream passed over once it holds its section count (the page
+ *               names this layout without spelling out the slot order; this
+ *               is the reading taken, and it equals the stride-3 rule of the
+ *               models the page names whenever section_h == section_w <=
+ *               section_t).
+ * mrope_section: 3 non-negative int64 summing to R/2.
+ * num_heads:    required (> 0) for rank 3 and whenever rotary_embedding_dim
+ *               != 0; for rank 4 it must then equal dim 1 of x.
+ * rotary_embedding_dim: 0 = R = D (D must be even), else an even R <= D
+ *               (D may then be odd); elements R..D-1 are copied.
+ * scale:        applied to gathered coefficients: c' = rnd_T(rnd_f32(c*scale)).
+ * Slot i of token (b, s) reads row p = position_ids[k][b][s] of its stream
+ * k; p outside [0, M) copies that pair unchanged. Limit: R/2 <= 512.
+ */
+int mrope_apply(const rope_tensor* x, const rope_tensor* position_ids,
+                const rope_tensor* cos_cache, const rope_tensor* sin_cache,
+                const rope_tensor* y, int64_t interleaved,
+                int64_t is_packed_batching, int64_t mrope_layout,
+                const int64_t mrope_section[3], int64_t num_heads,
+                int64_t rotary_embedding_dim, float scale, void* stream);
+
+/*
+ * rope_apply_qk -- Q (num_heads heads) and K (kv_num_heads heads) of one
+ * layer rotated with the same position ids and coefficients, in one launch.
+ *
+ * q, k:         both rank 3 ((B, S, H*D) and (B, S, Hk*D)) or both rank 4
+ *               ((B, H, S, D) and (B, Hk, S, D)); same B, S, D and type T.
+ *               kv_num_heads must divide num_heads.
+ * yq, yk:       outputs shaped like q and k; may be q and k themselves.
+ * Table path:   cos_cache and sin_cache given: exactly rope_apply on q and
+ *               on k (gathered with position_ids, or per-token tables).
+ * On-the-fly:   cos_cache == sin_cache == NULL: inv_freq (float32, (R/2,))
+ *               and position_ids are required, and slot i of a token at
+ *               position p uses theta = rnd_f32(rnd_f32(p) * inv_freq[i]),
+ *               c = rnd_T(rnd_f32(rnd_f32(cos theta) * attention_scaling)),
+ *               s likewise -- the same values rope_cos_sin_cache stores, so
+ *               both paths give bit-identical results. Any int64 p is valid.
+ * num_heads, kv_num_heads: required for rank 3; for rank 4, 0 or dim 1.
+ */
+int rope_apply_qk(const rope_tensor* q, const rope_tensor* k,
+                  const rope_tensor* cos_cache, const rope_tensor* sin_cache,
+                  const rope_tensor* position_ids, const rope_tensor* yq,
+                  const rope_tensor* yk, int64_t interleaved,
+                  int64_t num_heads, int64_t kv_num_heads,
+                  int64_t rotary_embedding_dim, const rope_tensor* inv_freq,
+                  float attention_scaling, void* stream);
+
+/*
+ * rope_inv_freq -- inv_freq[i] = rnd_f32(base^(-2i/R)) for i < R/2 with
+ * R = 2 * dim 0 of inv_freq (float32, rank 1). The pages take inv_freq from
+ * the model; this is the standard schedule. base must be > 0.
+ */
+int rope_inv_freq(const rope_tensor* inv_freq, double base, void* stream);
+
+/*
+ * rope_cos_sin_cache -- the (M, R/2) tables of type T for positions 0..M-1:
+ *   cos_out[p][i] = rnd_T(rnd_f32(rnd_f32(cos theta) * scaling)),
+ *   theta = rnd_f32(rnd_f32(p) * inv_freq[i]), sin likewise
+ * (PR #27590 review item 4: the table equals the on-the-fly values).
+ * inv_freq: float32 (R/2,). cos_out, sin_out: type T, (M, R/2).
+ */
+int rope_cos_sin_cache(const rope_tensor* inv_freq, float scaling,
+                       const rope_tensor* cos_out, const rope_tensor* sin_out,
+                       void* stream);
+
+/*
+ * Validation without launching: the same checks as the op, and the kernel
+ * variant it would run (static string, e.g. "rope/vec16/ids"), written to
+ * *variant when variant != NULL and the status is ROPE_OK. Never touches
+ * the GPU, so it can be called on a machine without one.
+ */
+int rope_apply_check(const rope_tensor* x, const rope_tensor* cos_cache,
+                     const rope_tensor* sin_cache,
+                     const rope_tensor* position_ids, const rope_tensor* y,
+                     int64_t interleaved, int64_t num_heads,
+                     int64_t rotary_embedding_dim, const char** variant);
+
+int mrope_apply_check(const rope_tensor* x, const rope_tensor* position_ids,
+                      const rope_tensor* cos_cache,
+                      const rope_tensor* sin_cache, const rope_tensor* y,
+                      int64_t interleaved, int64_t is_packed_batching,
+                      int64_t mrope_layout, const int64_t mrope_section[3],
+                      int64_t num_heads, int64_t rotary_embedding_dim,
+                      float scale, const char** variant);
+
+int rope_apply_qk_check(const rope_tensor* q, const rope_tensor* k,
+                        const rope_tensor* cos_cache,
+                        const rope_tensor* sin_cache,
+                        const rope_tensor* position_ids, const rope_tensor* yq,
+                        const rope_tensor* yk, int64_t interleaved,
+                        int64_t num_heads, int64_t kv_num_heads,
+                        int64_t rotary_embedding_dim,
+                        const rope_tensor* inv_freq, float attention_scaling,
+                        const char** variant);
+
+/*
+ * Kernel choice for all ops: 0 = automatic (vector kernels where shapes and
+ * alignment allow, the scalar kernel otherwise), 1 = always the scalar
+ * kernel. Process-wide; returns the previous value. Used to test both paths.
+ */
+int rope_set_kernel_policy(int policy);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPE_MI355X_H */

@@ -1,0 +1,535 @@
+// rope_kernels.hip -- rotary position embedding kernels for gfx950 (MI355X).
+//
+// What is computed (pages cited by title and section):
+//   per pair (x1, x2) of a head row with coefficients (c, s) of its slot,
+//   y1 = x1*c - x2*s, y2 = x2*c + x1*s  -- onnxruntime PR #27590 review,
+//   rotate_half / apply_rotary_pos_emb; pairs (i, i+R/2) or (2i, 2i+1) --
+//   "ai.onnx.RotaryEmbedding" manifest, attributeDescriptions.interleaved;
+//   elements R..D-1 copied -- same, rotary_embedding_dim.
+// Coefficient rows: gathered by position id, per-token, M-RoPE (slot i from
+// its stream's row, scaled and rounded to the storage type, out-of-range id
+// copies the pair -- "com.microsoft.MRotaryEmbedding" README), or computed
+// on the fly from inv_freq (PR #27590 Motivation).
+//
+// Per fp16 pair the op moves 8 bytes (read 4, write 4) and does 6 flops:
+// it is HBM-bound and has no contraction, so no MFMA. Design:
+//   * a head row is cut into 16-byte items (global_load/store_dwordx4);
+//   * a wave owns TG consecutive tokens x W items of one row shape, so each
+//     lane's coefficients (one 16-byte slice of cos and of sin) are fetched
+//     once into registers and reused for every head of a head chunk;
+//   * loads for several heads are issued before the first use, so each lane
+//     keeps several 16-byte loads in flight;
+//   * math in fp32 with fma and one rounding to the storage type; copies are
+//     bit moves (no arithmetic on pass-through elements).
+// A scalar kernel (one thread per pair or tail element) covers every shape
+// and alignment the vector kernel does not.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "rope_launch.hpp"
+
+namespace rope {
+
+using half_t = _Float16;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = 64 * kWavesPerBlock;
+
+struct KTask {
+    const char* x;
+    char* y;
+    int64_t sb, sh, ss;  // element strides of (b, h, s)
+    int64_t wave_begin;  // first wave of this task in the launch
+    int32_t heads, hpw, chunks, pad;
+};
+
+struct KArgs {
+    KTask t[2];
+    int64_t ntok, S, M;
+    const char* cos;
+    const char* sin;
+    const int64_t* ids;
+    const float* inv_freq;
+    int32_t ntask, W, NP, TG, P, R, D, interleaved;
+    float scaling, scale;
+    uint32_t sel[kSelWords];
+};
+
+template <typename T> struct Elem;
+template <> struct Elem<float> { using bits = uint32_t; static constexpr int E = 4; };
+template <> struct Elem<half_t> { using bits = uint16_t; static constexpr int E = 8; };
+
+// Materialise a binary32 value in a register. Without it the compiler may
+// merge a binary32 multiply or fma with the following conversion to binary16
+// into one v_fma_mixlo_f16, which rounds the exact result once to binary16
+// and so skips the binary32 rounding the arithmetic here specifies.
+__device__ inline float keep_f32(float v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+__device__ inline float to_f(float v) { return v; }
+__device__ inline float to_f(half_t v) { return (float)v; }
+template <typename T> __device__ inline T from_f(float v);
+template <> __device__ inline float from_f<float>(float v) { return v; }
+template <> __device__ inline half_t from_f<half_t>(float v) {
+    return (half_t)keep_f32(v);  // nearest-even from the binary32 value
+}
+template <typename T> __device__ inline float round_to(float v) { return to_f(from_f<T>(v)); }
+
+// Element e of a 16-byte chunk, as float. The whole chunk is reinterpreted
+// as a vector of T and then indexed (a bit_cast applied to a single vector
+// element is miscompiled to element 0 by this toolchain, so it is avoided).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef half_t f16x8 __attribute__((ext_vector_type(8)));
+template <typename T> struct ChunkVec;
+template <> struct ChunkVec<float> { typedef f32x4 type; };
+template <> struct ChunkVec<half_t> { typedef f16x8 type; };
+
+template <typename T>
+__device__ inline typename ChunkVec<T>::type chunk_values(const u32x4& v) {
+    return __builtin_bit_cast(typename ChunkVec<T>::type, v);
+}
+
+template <typename T>
+__device__ inline u32x4 chunk_pack(const float* f) {
+    typename ChunkVec<T>::type r;
+#pragma unroll
+    for (int i = 0; i < Elem<T>::E; ++i) r[i] = from_f<T>(f[i]);
+    return __builtin_bit_cast(u32x4, r);
+}
+
+// set the bits of element e of a chunk in a mask
+template <typename T> __device__ inline void mask_elem(u32x4& m, int e) {
+    if (sizeof(T) == 4) m[e] = 0xffffffffu;
+    else m[e >> 1] |= 0xffffu << (16 * (e & 1));
+}
+
+__device__ inline u32x4 load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void store16(char* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ inline u32x4 select_bits(const u32x4& keep_mask, const u32x4& keep, const u32x4& other) {
+    return (keep & keep_mask) | (other & ~keep_mask);
+}
+
+// Coefficient of slot i at position p computed on the fly (PR #27590
+// Motivation): theta = rnd_f32(rnd_f32(p) * inv_freq[i]); cos and sin of the
+// exact binary32 theta in binary64, rounded to binary32, times the scaling in
+// binary32, rounded to the storage type. Shared by the table builder so the
+// table and on-the-fly paths agree bit for bit.
+template <typename T>
+__device__ inline void onthefly_coef(float inv, int64_t p, float scaling, float& c, float& s) {
+    const float pf = (float)p;
+    const float theta = keep_f32(pf * inv);
+    double sd, cd;
+    sincos((double)theta, &sd, &cd);
+    const float cf = keep_f32((float)cd);
+    const float sf = keep_f32((float)sd);
+    c = round_to<T>(keep_f32(cf * scaling));
+    s = round_to<T>(keep_f32(sf * scaling));
+}
+
+__device__ inline int mrope_stream(const KArgs& a, int i) {
+    return (a.sel[i >> 4] >> (2 * (i & 15))) & 3;
+}
+
+// Coefficient (c, s) of slot i for token n, or copy = true.
+template <typename T, int COEF>
+__device__ inline void coef_slot(const KArgs& a, int64_t n, int i, float& c, float& s, bool& copy) {
+    const T* cos_t = reinterpret_cast<const T*>(a.cos);
+    const T* sin_t = reinterpret_cast<const T*>(a.sin);
+    copy = false;
+    c = 1.0f;
+    s = 0.0f;
+    if (COEF == kCoefGather) {
+        const int64_t p = a.ids[n];
+        if (p < 0 || p >= a.M) { copy = true; return; }
+        c = to_f(cos_t[p * a.P + i]);
+        s = to_f(sin_t[p * a.P + i]);
+    } else if (COEF == kCoefPerToken) {
+        c = to_f(cos_t[n * a.P + i]);
+        s = to_f(sin_t[n * a.P + i]);
+    } else if (COEF == kCoefMrope) {
+        const int64_t p = a.ids[(int64_t)mrope_stream(a, i) * a.ntok + n];
+        if (p < 0 || p >= a.M) { copy = true; return; }
+        c = round_to<T>(keep_f32(to_f(cos_t[p * a.P + i]) * a.scale));
+        s = round_to<T>(keep_f32(to_f(sin_t[p * a.P + i]) * a.scale));
+    } else {
+        onthefly_coef<T>(a.inv_freq[i], a.ids[n], a.scaling, c, s);
+    }
+}
+
+struct TaskView {
+    const char* x;
+    char* y;
+    int64_t sb, sh, ss, wave_begin;
+    int32_t heads, hpw, chunks;
+};
+
+__device__ inline TaskView task_of(const KArgs& a, bool second) {
+    TaskView v;
+    v.x = second ? a.t[1].x : a.t[0].x;
+    v.y = second ? a.t[1].y : a.t[0].y;
+    v.sb = second ? a.t[1].sb : a.t[0].sb;
+    v.sh = second ? a.t[1].sh : a.t[0].sh;
+    v.ss = second ? a.t[1].ss : a.t[0].ss;
+    v.wave_begin = second ? a.t[1].wave_begin : a.t[0].wave_begin;
+    v.heads = second ? a.t[1].heads : a.t[0].heads;
+    v.hpw = second ? a.t[1].hpw : a.t[0].hpw;
+    v.chunks = second ? a.t[1].chunks : a.t[0].chunks;
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Vector kernel.
+//   wave -> (task, token group g, head chunk hc); hc varies fastest, so the
+//   chunks of one token group sit in one workgroup and share its L1.
+//   lane item q = lane + 64*m (m < IPL) -> token t = q / W, item w = q % W.
+//   item w < NP rotates: split halves -> elements [w*E, w*E+E) with partners
+//   R/2 later; interleaved -> elements [w*E, w*E+E) = E/2 pairs.
+//   item w >= NP copies elements [R + (w-NP)*E, +E).
+template <typename T, int IL, int COEF, int IPL>
+__global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
+    constexpr int E = Elem<T>::E;
+    constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation item
+    constexpr int HU = IPL == 1 ? 4 : 2;  // heads per batch of loads
+    constexpr int ES = (int)sizeof(T);
+
+    const int lane = threadIdx.x & 63;
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const bool second = a.ntask > 1 && gw >= a.t[1].wave_begin;
+    const TaskView tk = task_of(a, second);
+    const int64_t local = gw - tk.wave_begin;
+    const int64_t g = local / tk.chunks;
+    const int hc = (int)(local - g * tk.chunks);
+    const int64_t n0 = g * a.TG;
+    if (n0 >= a.ntok) return;
+    const int h_begin = hc * tk.hpw;
+    const int h_end = min(tk.heads, h_begin + tk.hpw);
+    const int64_t sh_bytes = tk.sh * ES;
+    const int64_t half_bytes = (int64_t)a.P * ES;
+
+    bool act[IPL], rot[IPL];
+    int64_t off[IPL];    // byte offset of the item's first chunk for head 0
+    u32x4 keep[IPL];     // input bits passed through unchanged
+    float cf[IPL][CE], sf[IPL][CE];
+
+#pragma unroll
+    for (int m = 0; m < IPL; ++m) {
+        const int q = lane + 64 * m;
+        const int t = q / a.W;
+        const int w = q - t * a.W;
+        const int64_t n = n0 + t;
+        act[m] = t < a.TG && n < a.ntok;
+        rot[m] = w < a.NP;
+        off[m] = 0;
+        keep[m] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < CE; ++j) { cf[m][j] = 1.0f; sf[m][j] = 0.0f; }
+        if (!act[m]) continue;
+        const int64_t b = n / a.S;
+        const int64_t s = n - b * a.S;
+        const int64_t e0 = rot[m] ? (int64_t)w * E : (int64_t)a.R + (int64_t)(w - a.NP) * E;
+        off[m] = (b * tk.sb + s * tk.ss + e0) * ES;
+        if (!rot[m]) continue;
+        const int slot0 = w * CE;
+        if (COEF == kCoefGather || COEF == kCoefPerToken) {
+            int64_t row = n;
+            bool valid = true;
+            if (COEF == kCoefGather) {
+                row = a.ids[n];
+                valid = row >= 0 && row < a.M;
+            }
+            if (valid) {
+                typedef T cvec __attribute__((ext_vector_type(CE)));
+                const cvec cv = *reinterpret_cast<const cvec*>(a.cos + (row * a.P + slot0) * ES);
+                const cvec sv = *reinterpret_cast<const cvec*>(a.sin + (row * a.P + slot0) * ES);
+#pragma unroll
+                for (int j = 0; j < CE; ++j) { cf[m][j] = to_f(cv[j]); sf[m][j] = to_f(sv[j]); }
+            } else {
+                keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CE; ++j) {
+                bool copy;
+                coef_slot<T, COEF>(a, n, slot0 + j, cf[m][j], sf[m][j], copy);
+                if (copy) {
+                    if (IL) { mask_elem<T>(keep[m], 2 * j); mask_elem<T>(keep[m], 2 * j + 1); }
+                    else mask_elem<T>(keep[m], j);
+                }
+            }
+        }
+    }
+
+    for (int h = h_begin; h < h_end; h += HU) {
+        u32x4 in1[HU][IPL], in2[HU][IPL];
+#pragma unroll
+        for (int u = 0; u < HU; ++u) {
+#pragma unroll
+            for (int m = 0; m < IPL; ++m) {
+                if (act[m] && h + u < h_end) {
+                    const char* px = tk.x + off[m] + (int64_t)(h + u) * sh_bytes;
+                    in1[u][m] = load16(px);
+                    if (!IL && rot[m]) in2[u][m] = load16(px + half_bytes);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < HU; ++u) {
+#pragma unroll
+            for (int m = 0; m < IPL; ++m) {
+                if (!(act[m] && h + u < h_end)) continue;
+                char* py = tk.y + off[m] + (int64_t)(h + u) * sh_bytes;
+                if (!rot[m]) {
+                    store16(py, in1[u][m]);
+                    continue;
+                }
+                if (IL) {
+                    const auto xv = chunk_values<T>(in1[u][m]);
+                    float r[E];
+#pragma unroll
+                    for (int j = 0; j < CE; ++j) {
+                        const float x1 = to_f(xv[2 * j]);
+                        const float x2 = to_f(xv[2 * j + 1]);
+                        r[2 * j] = fmaf(x1, cf[m][j], -(x2 * sf[m][j]));
+                        r[2 * j + 1] = fmaf(x2, cf[m][j], x1 * sf[m][j]);
+                    }
+                    u32x4 o = chunk_pack<T>(r);
+                    if (COEF == kCoefGather || COEF == kCoefMrope) o = select_bits(keep[m], in1[u][m], o);
+                    store16(py, o);
+                } else {
+                    const auto xv1 = chunk_values<T>(in1[u][m]);
+                    const auto xv2 = chunk_values<T>(in2[u][m]);
+                    float r1[E], r2[E];
+#pragma unroll
+                    for (int j = 0; j < E; ++j) {
+                        const float x1 = to_f(xv1[j]);
+                        const float x2 = to_f(xv2[j]);
+                        r1[j] = fmaf(x1, cf[m][j], -(x2 * sf[m][j]));
+                        r2[j] = fmaf(x2, cf[m][j], x1 * sf[m][j]);
+                    }
+                    u32x4 o1 = chunk_pack<T>(r1);
+                    u32x4 o2 = chunk_pack<T>(r2);
+                    if (COEF == kCoefGather || COEF == kCoefMrope) {
+                        o1 = select_bits(keep[m], in1[u][m], o1);
+                        o2 = select_bits(keep[m], in2[u][m], o2);
+                    }
+                    store16(py, o1);
+                    store16(py + half_bytes, o2);
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scalar kernel: one thread per (token, head, k), k < R/2 a pair, k >= R/2 a
+// tail element R + k - R/2. Any head size, rotary dim and alignment.
+template <typename T, int COEF>
+__global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int64_t total0,
+                                                              int64_t total) {
+    using B = typename Elem<T>::bits;
+    const int64_t K = a.P + (a.D - a.R);
+    for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * kBlock) {
+        const bool second = idx >= total0;
+        const TaskView tk = task_of(a, second);
+        const int64_t local = second ? idx - total0 : idx;
+        const int64_t k = local % K;
+        const int64_t rest = local / K;
+        const int64_t h = rest % tk.heads;
+        const int64_t n = rest / tk.heads;
+        const int64_t b = n / a.S;
+        const int64_t s = n - b * a.S;
+        const int64_t base = b * tk.sb + h * tk.sh + s * tk.ss;
+        const B* xb = reinterpret_cast<const B*>(tk.x) + base;
+        B* yb = reinterpret_cast<B*>(tk.y) + base;
+        if (k >= a.P) {
+            const int64_t j = a.R + (k - a.P);
+            yb[j] = xb[j];
+            continue;
+        }
+        const int i = (int)k;
+        const int64_t j1 = a.interleaved ? 2 * (int64_t)i : i;
+        const int64_t j2 = a.interleaved ? 2 * (int64_t)i + 1 : (int64_t)i + a.P;
+        float c, sn;
+        bool copy;
+        coef_slot<T, COEF>(a, n, i, c, sn, copy);
+        if (copy) {
+            yb[j1] = xb[j1];
+            yb[j2] = xb[j2];
+            continue;
+        }
+        const float x1 = to_f(__builtin_bit_cast(T, xb[j1]));
+        const float x2 = to_f(__builtin_bit_cast(T, xb[j2]));
+        yb[j1] = __builtin_bit_cast(B, from_f<T>(fmaf(x1, c, -(x2 * sn))));
+        yb[j2] = __builtin_bit_cast(B, from_f<T>(fmaf(x2, c, x1 * sn)));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Table builders.
+
+__global__ __launch_bounds__(kBlock) void inv_freq_kernel(float* out, int64_t half, double base) {
+    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= half) return;
+    out[i] = (float)pow(base, -2.0 * (double)i / (double)(2 * half));
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void table_kernel(const float* inv_freq, T* cos_out, T* sin_out,
+                                                       int64_t rows, int64_t half, float scaling) {
+    const int64_t total = rows * half;
+    for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * kBlock) {
+        const int64_t p = idx / half;
+        const int64_t i = idx - p * half;
+        float c, s;
+        onthefly_coef<T>(inv_freq[i], p, scaling, c, s);
+        cos_out[idx] = from_f<T>(c);
+        sin_out[idx] = from_f<T>(s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launch.
+
+static int launched(hipError_t e) {
+    if (e != hipSuccess)
+        return fail(ROPE_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
+    return ROPE_OK;
+}
+
+template <typename T, int IL, int COEF>
+static hipError_t launch_vec_ipl(const KArgs& a, int ipl, dim3 grid, hipStream_t st) {
+    void* args[] = {const_cast<KArgs*>(&a)};
+    const void* fn;
+    switch (ipl) {
+        case 1: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1>; break;
+        case 2: fn = (const void*)rope_vec_kernel<T, IL, COEF, 2>; break;
+        case 3: fn = (const void*)rope_vec_kernel<T, IL, COEF, 3>; break;
+        default: fn = (const void*)rope_vec_kernel<T, IL, COEF, 4>; break;
+    }
+    return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
+}
+
+template <typename T, int IL>
+static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, dim3 grid, hipStream_t st) {
+    switch (c) {
+        case kCoefGather: return launch_vec_ipl<T, IL, kCoefGather>(a, ipl, grid, st);
+        case kCoefPerToken: return launch_vec_ipl<T, IL, kCoefPerToken>(a, ipl, grid, st);
+        case kCoefMrope: return launch_vec_ipl<T, IL, kCoefMrope>(a, ipl, grid, st);
+        default: return launch_vec_ipl<T, IL, kCoefOnTheFly>(a, ipl, grid, st);
+    }
+}
+
+template <typename T>
+static hipError_t launch_scalar(const KArgs& a, CoefKind c, int64_t total0, int64_t total,
+                                hipStream_t st) {
+    int64_t blocks = (total + kBlock - 1) / kBlock;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    void* args[] = {const_cast<KArgs*>(&a), &total0, &total};
+    const void* fn;
+    switch (c) {
+        case kCoefGather: fn = (const void*)rope_scalar_kernel<T, kCoefGather>; break;
+        case kCoefPerToken: fn = (const void*)rope_scalar_kernel<T, kCoefPerToken>; break;
+        case kCoefMrope: fn = (const void*)rope_scalar_kernel<T, kCoefMrope>; break;
+        default: fn = (const void*)rope_scalar_kernel<T, kCoefOnTheFly>; break;
+    }
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0, st);
+}
+
+int launch_plan(const Plan& pl, void* stream) {
+    if (pl.empty) return ROPE_OK;
+    const Problem& p = pl.p;
+    const Geometry& g = pl.g;
+    hipStream_t st = (hipStream_t)stream;
+    KArgs a = {};
+    int64_t wave_begin = 0;
+    for (int t = 0; t < p.ntask; ++t) {
+        a.t[t].x = (const char*)p.task[t].x;
+        a.t[t].y = (char*)p.task[t].y;
+        a.t[t].sb = p.task[t].stride_b;
+        a.t[t].sh = p.task[t].stride_h;
+        a.t[t].ss = p.task[t].stride_s;
+        a.t[t].heads = (int32_t)p.task[t].heads;
+        a.t[t].wave_begin = wave_begin;
+        if (g.vector) {
+            a.t[t].hpw = g.heads_per_wave[t];
+            a.t[t].chunks = g.chunks[t] > 0 ? g.chunks[t] : 1;
+            wave_begin += g.waves[t];
+        }
+    }
+    if (p.ntask == 2 && g.vector && g.waves[1] == 0) a.t[1].wave_begin = INT64_MAX;
+    a.ntok = p.B * p.S;
+    a.S = p.S;
+    a.M = p.M;
+    a.cos = (const char*)p.cos;
+    a.sin = (const char*)p.sin;
+    a.ids = p.ids;
+    a.inv_freq = p.inv_freq;
+    a.ntask = p.ntask;
+    a.W = g.W;
+    a.NP = g.NP;
+    a.TG = g.TG;
+    a.P = (int32_t)(p.R / 2);
+    a.R = (int32_t)p.R;
+    a.D = (int32_t)p.D;
+    a.interleaved = p.interleaved;
+    a.scaling = p.scaling;
+    a.scale = p.scale;
+    for (int i = 0; i < kSelWords; ++i) a.sel[i] = p.sel[i];
+
+    hipError_t e;
+    if (g.vector) {
+        const int64_t waves = wave_begin;
+        if (waves == 0) return ROPE_OK;
+        const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+        const int ipl = g.items_per_lane;
+        if (p.dtype == ROPE_FLOAT16)
+            e = p.interleaved ? launch_vec_coef<half_t, 1>(a, p.coef, ipl, grid, st)
+                              : launch_vec_coef<half_t, 0>(a, p.coef, ipl, grid, st);
+        else
+            e = p.interleaved ? launch_vec_coef<float, 1>(a, p.coef, ipl, grid, st)
+                              : launch_vec_coef<float, 0>(a, p.coef, ipl, grid, st);
+    } else {
+        const int64_t K = p.R / 2 + (p.D - p.R);
+        const int64_t total0 = p.B * p.S * p.task[0].heads * K;
+        const int64_t total1 = p.ntask > 1 ? p.B * p.S * p.task[1].heads * K : 0;
+        if (total0 + total1 == 0) return ROPE_OK;
+        e = p.dtype == ROPE_FLOAT16 ? launch_scalar<half_t>(a, p.coef, total0, total0 + total1, st)
+                                    : launch_scalar<float>(a, p.coef, total0, total0 + total1, st);
+    }
+    return launched(e);
+}
+
+int launch_inv_freq(float* inv_freq, int64_t half, double base, void* stream) {
+    if (half == 0) return ROPE_OK;
+    void* args[] = {&inv_freq, &half, &base};
+    const dim3 grid((unsigned)((half + kBlock - 1) / kBlock));
+    return launched(hipLaunchKernel((const void*)inv_freq_kernel, grid, dim3(kBlock), args, 0,
+                                    (hipStream_t)stream));
+}
+
+int launch_cos_sin_cache(const TablePlan& t, void* stream) {
+    const int64_t total = t.rows * t.half;
+    if (total == 0) return ROPE_OK;
+    int64_t blocks = (total + kBlock - 1) / kBlock;
+    if (blocks > 65536) blocks = 65536;
+    const float* inv = t.inv_freq;
+    void* cos = t.cos;
+    void* sin = t.sin;
+    int64_t rows = t.rows, half = t.half;
+    float scaling = t.scaling;
+    void* args[] = {&inv, &cos, &sin, &rows, &half, &scaling};
+    const void* fn = t.dtype == ROPE_FLOAT16 ? (const void*)table_kernel<half_t>
+                                             : (const void*)table_kernel<float>;
+    return launched(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0,
+                                    (hipStream_t)stream));
+}
+
+}  // namespace rope

@@ -1,0 +1,623 @@
+// rope_plan.cpp -- contracts of the ops and the choice of kernel, host only.
+//
+// Contract clauses follow the pages:
+//   RotaryEmbedding: "ai.onnx.RotaryEmbedding" manifest, `derive`
+//     (rank3Contract, rank4Contract, rank3PosContract, rank4PosContract),
+//     `attributeConstraints`, `typeConstraints`.
+//   MRotaryEmbedding: its README, Inputs and Attributes tables.
+//   Q+K: onnxruntime PR #27590 (GQA, shared cos/sin) and the SparseAttention
+//     README Attributes (kv_num_heads divides num_heads).
+// Every failing clause returns its status and records a message.
+#include "rope_plan.hpp"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+namespace rope {
+
+// ---------------------------------------------------------------------------
+// errors
+
+static thread_local char g_error[512];
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_error, sizeof(g_error), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+void clear_error() { g_error[0] = '\0'; }
+const char* last_error() { return g_error; }
+
+static int g_policy = 0;
+int kernel_policy() { return g_policy; }
+int set_kernel_policy(int policy) {
+    int old = g_policy;
+    g_policy = policy;
+    return old;
+}
+
+// ---------------------------------------------------------------------------
+// tensor descriptors
+
+static int elem_size(int32_t dtype) {
+    switch (dtype) {
+        case ROPE_FLOAT: return 4;
+        case ROPE_FLOAT16: return 2;
+        case ROPE_INT64: return 8;
+        default: return 0;
+    }
+}
+
+static bool is_float(int32_t dtype) { return dtype == ROPE_FLOAT || dtype == ROPE_FLOAT16; }
+
+static int64_t numel(const rope_tensor* t) {
+    int64_t n = 1;
+    for (int i = 0; i < t->rank; ++i) n *= t->shape[i];
+    return n;
+}
+
+static int64_t nbytes(const rope_tensor* t) { return numel(t) * elem_size(t->dtype); }
+
+// Rank in [1,4], dims >= 0, element and byte counts fit in int64, known
+// element type, data present when there is data.
+static int check_desc(const rope_tensor* t, const char* name) {
+    if (t->rank < 1 || t->rank > 4)
+        return fail(ROPE_ERR_RANK, "%s: rank %d outside 1..4", name, (int)t->rank);
+    if (elem_size(t->dtype) == 0)
+        return fail(ROPE_ERR_DTYPE, "%s: unknown element type %d", name, (int)t->dtype);
+    int64_t n = 1;
+    for (int i = 0; i < t->rank; ++i) {
+        if (t->shape[i] < 0)
+            return fail(ROPE_ERR_SHAPE, "%s: dimension %d is negative", name, i);
+        if (__builtin_mul_overflow(n, t->shape[i], &n))
+            return fail(ROPE_ERR_SHAPE, "%s: element count overflows", name);
+    }
+    int64_t b;
+    if (__builtin_mul_overflow(n, (int64_t)elem_size(t->dtype), &b))
+        return fail(ROPE_ERR_SHAPE, "%s: byte count overflows", name);
+    if (n > 0 && t->data == nullptr)
+        return fail(ROPE_ERR_NULL, "%s: data is NULL", name);
+    return ROPE_OK;
+}
+
+static bool same_shape(const rope_tensor* a, const rope_tensor* b) {
+    if (a->rank != b->rank) return false;
+    for (int i = 0; i < a->rank; ++i)
+        if (a->shape[i] != b->shape[i]) return false;
+    return true;
+}
+
+static bool overlaps(const rope_tensor* a, const rope_tensor* b) {
+    if (!a || !b) return false;
+    int64_t na = nbytes(a), nb = nbytes(b);
+    if (na == 0 || nb == 0) return false;
+    uintptr_t a0 = (uintptr_t)a->data, b0 = (uintptr_t)b->data;
+    return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+// Output `out` may be exactly `in` (same address, same size); no other overlap.
+static bool in_place(const rope_tensor* out, const rope_tensor* in) {
+    return in && out->data == in->data && nbytes(out) == nbytes(in);
+}
+
+static int check_output(const rope_tensor* out, const char* oname,
+                        const rope_tensor* same_ok, const rope_tensor* const* others,
+                        const char* const* onames, int nothers) {
+    if (overlaps(out, same_ok) && !in_place(out, same_ok))
+        return fail(ROPE_ERR_ALIAS, "%s partially overlaps its input", oname);
+    for (int i = 0; i < nothers; ++i)
+        if (overlaps(out, others[i]))
+            return fail(ROPE_ERR_ALIAS, "%s overlaps %s", oname, onames[i]);
+    return ROPE_OK;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---------------------------------------------------------------------------
+// M-RoPE slot streams ([MRE] Attributes: mrope_section, mrope_layout)
+
+void mrope_streams(int64_t half, const int64_t section[3], int64_t layout,
+                   uint8_t* stream_of_slot) {
+    if (layout == 0) {
+        for (int64_t i = 0; i < half; ++i)
+            stream_of_slot[i] = i < section[0] ? 0 : (i < section[0] + section[1] ? 1 : 2);
+        return;
+    }
+    // Rounds: in round r every stream whose section exceeds r takes one slot,
+    // in the order temporal, height, width.
+    int64_t i = 0;
+    for (int64_t r = 0; i < half; ++r)
+        for (int k = 0; k < 3 && i < half; ++k)
+            if (section[k] > r) stream_of_slot[i++] = (uint8_t)k;
+}
+
+// ---------------------------------------------------------------------------
+// kernel choice
+
+static const char* variant_name(bool vec, CoefKind c) {
+    static const char* names[2][4] = {
+        {"scalar/gather", "scalar/per_token", "scalar/mrope", "scalar/on_the_fly"},
+        {"vec16/gather", "vec16/per_token", "vec16/mrope", "vec16/on_the_fly"}};
+    return names[vec ? 1 : 0][(int)c];
+}
+
+static int heads_per_wave_override() {
+    const char* e = getenv("ROPE_HEADS_PER_WAVE");
+    return e ? atoi(e) : 0;
+}
+
+// Vector kernel: a head row of D elements is cut into 16-byte items; a
+// rotation item holds E = 16/sizeof(T) pairs' first elements (split halves,
+// with its partner item R/2 elements later) or E/2 whole pairs
+// (interleaved); tail items are copied. A wave owns TG consecutive tokens
+// times W items (items_per_lane items per lane) and loops over a chunk of
+// heads, keeping each lane's coefficients in registers.
+static void choose_geometry(Plan* pl) {
+    Problem& p = pl->p;
+    Geometry& g = pl->g;
+    const int es = p.dtype == ROPE_FLOAT16 ? 2 : 4;
+    const int E = 16 / es;
+    const int64_t half = p.R / 2;
+    bool ok = kernel_policy() == 0;
+    ok = ok && p.D % E == 0 && p.R % E == 0 && (p.interleaved || half % E == 0);
+    for (int t = 0; t < p.ntask; ++t)
+        ok = ok && aligned16(p.task[t].x) && aligned16(p.task[t].y);
+    if (p.coef == kCoefGather || p.coef == kCoefPerToken)
+        ok = ok && aligned16(p.cos) && aligned16(p.sin);
+    const int64_t NP = p.interleaved ? p.R / E : half / E;
+    const int64_t NT = (p.D - p.R) / E;
+    const int64_t W = NP + NT;
+    ok = ok && W >= 1 && W <= 256;
+    g.vector = ok;
+    g.variant = variant_name(ok, p.coef);
+    if (!ok) return;
+
+    int best = 0;
+    double best_util = 0.0;
+    for (int ipl = 1; ipl <= 4; ++ipl) {
+        int64_t tg = 64 * ipl / W;
+        if (tg < 1) continue;
+        double util = (double)(tg * W) / (64.0 * ipl);
+        if (util > best_util + 1e-9) {
+            best_util = util;
+            best = ipl;
+        }
+    }
+    g.items_per_lane = best;
+    g.W = (int32_t)W;
+    g.NP = (int32_t)NP;
+    g.TG = (int32_t)(64 * best / W);
+    const int64_t ntok = p.B * p.S;
+    const int64_t groups = (ntok + g.TG - 1) / g.TG;
+    const int over = heads_per_wave_override();
+    // Head chunks: split heads until the launch has enough waves to cover
+    // the chip (256 CUs) several times over.
+    const int64_t target = 4096;
+    for (int t = 0; t < p.ntask; ++t) {
+        int64_t H = p.task[t].heads;
+        int64_t hpw = H > 0 ? H : 1;
+        if (over > 0) {
+            hpw = over < hpw ? over : hpw;
+        } else {
+            while (hpw > 1 && groups * ((H + hpw - 1) / hpw) < target)
+                hpw = (hpw + 1) / 2;
+        }
+        g.heads_per_wave[t] = (int32_t)hpw;
+        g.chunks[t] = (int32_t)((H + hpw - 1) / hpw);
+        g.waves[t] = H > 0 ? groups * g.chunks[t] : 0;
+    }
+}
+
+static void fill_strides(Task* t, int rank, int64_t S, int64_t H, int64_t D) {
+    t->heads = H;
+    if (rank == 4) {
+        t->stride_b = H * S * D;
+        t->stride_h = S * D;
+        t->stride_s = D;
+    } else {
+        t->stride_b = S * H * D;
+        t->stride_s = H * D;
+        t->stride_h = D;
+    }
+}
+
+// (B, S, H, D) of a rank-3 or rank-4 activation.
+static int activation_dims(const rope_tensor* x, const char* name, int64_t heads_attr,
+                           bool heads_required, int64_t* B, int64_t* S, int64_t* H,
+                           int64_t* D) {
+    if (x->rank == 3) {
+        if (heads_attr < 1)
+            return fail(ROPE_ERR_ATTRIBUTE, "%s: the head count attribute is required (>= 1) for rank 3",
+                        name);
+        if (x->shape[2] % heads_attr != 0)
+            return fail(ROPE_ERR_SHAPE, "%s: hidden size %lld is not divisible by %lld heads", name,
+                        (long long)x->shape[2], (long long)heads_attr);
+        *B = x->shape[0];
+        *S = x->shape[1];
+        *H = heads_attr;
+        *D = x->shape[2] / heads_attr;
+        return ROPE_OK;
+    }
+    if (x->rank == 4) {
+        if (heads_required && heads_attr < 1)
+            return fail(ROPE_ERR_ATTRIBUTE, "%s: num_heads must be positive here", name);
+        if (heads_attr != 0 && heads_attr != x->shape[1])
+            return fail(ROPE_ERR_SHAPE, "%s: head count attribute %lld disagrees with dim 1 = %lld",
+                        name, (long long)heads_attr, (long long)x->shape[1]);
+        *B = x->shape[0];
+        *H = x->shape[1];
+        *S = x->shape[2];
+        *D = x->shape[3];
+        return ROPE_OK;
+    }
+    return fail(ROPE_ERR_RANK, "%s must be rank 3 or 4, got %d", name, (int)x->rank);
+}
+
+#define TRY(expr)                          \
+    do {                                   \
+        int rc_ = (expr);                  \
+        if (rc_ != ROPE_OK) return rc_;    \
+    } while (0)
+
+// cos/sin tables of a gathered (ids) or per-token (no ids) RotaryEmbedding:
+// manifest derive rank*PosContract / rank*Contract.
+static int check_tables(const rope_tensor* cos, const rope_tensor* sin, const rope_tensor* ids,
+                        int64_t B, int64_t S, int64_t R, int64_t* M) {
+    if (!same_shape(cos, sin))
+        return fail(ROPE_ERR_SHAPE, "sin_cache must have the shape of cos_cache");
+    if (ids) {
+        if (cos->rank != 2)
+            return fail(ROPE_ERR_RANK, "cos_cache must be rank 2 (max_sequence_length, rotary_dim/2) with position_ids");
+        if (cos->shape[1] * 2 != R)
+            return fail(ROPE_ERR_SHAPE, "cos_cache width %lld * 2 != rotary dim %lld",
+                        (long long)cos->shape[1], (long long)R);
+        if (ids->rank != 2)
+            return fail(ROPE_ERR_RANK, "position_ids must be rank 2 (batch, sequence)");
+        if (ids->shape[0] != B || ids->shape[1] != S)
+            return fail(ROPE_ERR_SHAPE, "position_ids shape (%lld, %lld) != (batch %lld, sequence %lld)",
+                        (long long)ids->shape[0], (long long)ids->shape[1], (long long)B, (long long)S);
+        *M = cos->shape[0];
+        return ROPE_OK;
+    }
+    if (cos->rank != 3)
+        return fail(ROPE_ERR_RANK, "cos_cache must be rank 3 (batch, sequence, rotary_dim/2) without position_ids");
+    if (cos->shape[0] != B || cos->shape[1] != S)
+        return fail(ROPE_ERR_SHAPE, "cos_cache leading dims (%lld, %lld) != (batch %lld, sequence %lld)",
+                    (long long)cos->shape[0], (long long)cos->shape[1], (long long)B, (long long)S);
+    if (cos->shape[2] * 2 != R)
+        return fail(ROPE_ERR_SHAPE, "cos_cache width %lld * 2 != rotary dim %lld",
+                    (long long)cos->shape[2], (long long)R);
+    *M = 0;
+    return ROPE_OK;
+}
+
+static int check_rotary_dim(int64_t D, int64_t rotary_embedding_dim, int64_t* R) {
+    if (rotary_embedding_dim < 0)
+        return fail(ROPE_ERR_ATTRIBUTE, "rotary_embedding_dim must be >= 0");
+    if (rotary_embedding_dim % 2 != 0)
+        return fail(ROPE_ERR_ATTRIBUTE, "rotary_embedding_dim must be even");
+    if (rotary_embedding_dim > D)
+        return fail(ROPE_ERR_SHAPE, "rotary_embedding_dim %lld exceeds head_size %lld",
+                    (long long)rotary_embedding_dim, (long long)D);
+    *R = rotary_embedding_dim ? rotary_embedding_dim : D;
+    return ROPE_OK;
+}
+
+// ---------------------------------------------------------------------------
+
+int plan_rope(const rope_tensor* x, const rope_tensor* cos_cache, const rope_tensor* sin_cache,
+              const rope_tensor* position_ids, const rope_tensor* y, int64_t interleaved,
+              int64_t num_heads, int64_t rotary_embedding_dim, Plan* out) {
+    clear_error();
+    memset(out, 0, sizeof(*out));
+    if (!x) return fail(ROPE_ERR_NULL, "x is missing");
+    if (!cos_cache) return fail(ROPE_ERR_NULL, "cos_cache is missing");
+    if (!sin_cache) return fail(ROPE_ERR_NULL, "sin_cache is missing");
+    if (!y) return fail(ROPE_ERR_NULL, "y is missing");
+    TRY(check_desc(x, "x"));
+    TRY(check_desc(cos_cache, "cos_cache"));
+    TRY(check_desc(sin_cache, "sin_cache"));
+    TRY(check_desc(y, "y"));
+    if (position_ids) TRY(check_desc(position_ids, "position_ids"));
+
+    if (!is_float(x->dtype))
+        return fail(ROPE_ERR_DTYPE, "x must be float32 or float16");
+    if (cos_cache->dtype != x->dtype || sin_cache->dtype != x->dtype || y->dtype != x->dtype)
+        return fail(ROPE_ERR_DTYPE, "cos_cache, sin_cache and y must have the type of x");
+    if (position_ids && position_ids->dtype != ROPE_INT64)
+        return fail(ROPE_ERR_DTYPE, "position_ids must be int64");
+    if (interleaved != 0 && interleaved != 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "interleaved must be 0 or 1");
+    if (num_heads < 0) return fail(ROPE_ERR_ATTRIBUTE, "num_heads must be >= 0");
+
+    if (x->rank != 3 && x->rank != 4)
+        return fail(ROPE_ERR_RANK, "x must be rank 3 or 4, got %d", (int)x->rank);
+    if (!same_shape(x, y)) return fail(ROPE_ERR_SHAPE, "y must have the shape of x");
+    int64_t B, S, H, D, R, M;
+    TRY(activation_dims(x, "x", num_heads, false, &B, &S, &H, &D));
+    if (D % 2 != 0) return fail(ROPE_ERR_SHAPE, "head_size %lld must be even", (long long)D);
+    TRY(check_rotary_dim(D, rotary_embedding_dim, &R));
+    TRY(check_tables(cos_cache, sin_cache, position_ids, B, S, R, &M));
+
+    const rope_tensor* others[3] = {cos_cache, sin_cache, position_ids};
+    const char* names[3] = {"cos_cache", "sin_cache", "position_ids"};
+    TRY(check_output(y, "y", x, others, names, 3));
+
+    Problem& p = out->p;
+    p.dtype = x->dtype;
+    p.interleaved = (int32_t)interleaved;
+    p.B = B; p.S = S; p.D = D; p.R = R;
+    p.ntask = 1;
+    p.task[0].x = x->data;
+    p.task[0].y = y->data;
+    fill_strides(&p.task[0], x->rank, S, H, D);
+    p.coef = position_ids ? kCoefGather : kCoefPerToken;
+    p.cos = cos_cache->data;
+    p.sin = sin_cache->data;
+    p.ids = position_ids ? (const int64_t*)position_ids->data : nullptr;
+    p.M = M;
+    p.scale = 1.0f;
+    p.scaling = 1.0f;
+    out->empty = numel(x) == 0;
+    choose_geometry(out);
+    return ROPE_OK;
+}
+
+int plan_mrope(const rope_tensor* x, const rope_tensor* position_ids, const rope_tensor* cos_cache,
+               const rope_tensor* sin_cache, const rope_tensor* y, int64_t interleaved,
+               int64_t is_packed_batching, int64_t mrope_layout, const int64_t mrope_section[3],
+               int64_t num_heads, int64_t rotary_embedding_dim, float scale, Plan* out) {
+    clear_error();
+    memset(out, 0, sizeof(*out));
+    if (!x) return fail(ROPE_ERR_NULL, "x is missing");
+    if (!position_ids) return fail(ROPE_ERR_NULL, "position_ids is required");
+    if (!cos_cache) return fail(ROPE_ERR_NULL, "cos_cache is missing");
+    if (!sin_cache) return fail(ROPE_ERR_NULL, "sin_cache is missing");
+    if (!y) return fail(ROPE_ERR_NULL, "y is missing");
+    if (!mrope_section) return fail(ROPE_ERR_NULL, "mrope_section is required");
+    TRY(check_desc(x, "x"));
+    TRY(check_desc(position_ids, "position_ids"));
+    TRY(check_desc(cos_cache, "cos_cache"));
+    TRY(check_desc(sin_cache, "sin_cache"));
+    TRY(check_desc(y, "y"));
+
+    if (!is_float(x->dtype))
+        return fail(ROPE_ERR_DTYPE, "x must be float32 or float16");
+    if (cos_cache->dtype != x->dtype || sin_cache->dtype != x->dtype || y->dtype != x->dtype)
+        return fail(ROPE_ERR_DTYPE, "cos_cache, sin_cache and y must have the type of x");
+    if (position_ids->dtype != ROPE_INT64)
+        return fail(ROPE_ERR_DTYPE, "position_ids must be int64");
+    if (is_packed_batching != 0 && is_packed_batching != 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "is_packed_batching must be 0 or 1");
+    if (is_packed_batching == 1)
+        return fail(ROPE_ERR_UNSUPPORTED, "packed batching (is_packed_batching=1) is not implemented");
+    if (mrope_layout != 0 && mrope_layout != 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "mrope_layout must be 0 or 1");
+    if (interleaved != 0 && interleaved != 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "interleaved must be 0 or 1");
+    for (int k = 0; k < 3; ++k)
+        if (mrope_section[k] < 0)
+            return fail(ROPE_ERR_ATTRIBUTE, "mrope_section entries must be non-negative");
+    if (num_heads < 0) return fail(ROPE_ERR_ATTRIBUTE, "num_heads must be >= 0");
+    if (rotary_embedding_dim < 0 || rotary_embedding_dim % 2 != 0)
+        return fail(ROPE_ERR_ATTRIBUTE, "rotary_embedding_dim must be 0 or a positive even number");
+
+    if (x->rank != 3 && x->rank != 4)
+        return fail(ROPE_ERR_RANK, "x must be rank 3 or 4, got %d", (int)x->rank);
+    if (!same_shape(x, y)) return fail(ROPE_ERR_SHAPE, "y must have the shape of x");
+    int64_t B, S, H, D, R;
+    TRY(activation_dims(x, "x", num_heads, rotary_embedding_dim != 0, &B, &S, &H, &D));
+    if (rotary_embedding_dim == 0) {
+        if (D % 2 != 0)
+            return fail(ROPE_ERR_SHAPE, "head_size %lld must be even when rotary_embedding_dim is 0",
+                        (long long)D);
+        R = D;
+    } else {
+        if (rotary_embedding_dim > D)
+            return fail(ROPE_ERR_SHAPE, "rotary_embedding_dim %lld exceeds head_size %lld",
+                        (long long)rotary_embedding_dim, (long long)D);
+        R = rotary_embedding_dim;
+    }
+    const int64_t half = R / 2;
+    if (half > kMaxMropeHalf)
+        return fail(ROPE_ERR_UNSUPPORTED, "rotary dim / 2 = %lld exceeds %d", (long long)half,
+                    kMaxMropeHalf);
+    if (mrope_section[0] + mrope_section[1] + mrope_section[2] != half)
+        return fail(ROPE_ERR_ATTRIBUTE, "mrope_section sums to %lld, must be rotary dim / 2 = %lld",
+                    (long long)(mrope_section[0] + mrope_section[1] + mrope_section[2]),
+                    (long long)half);
+    if (cos_cache->rank != 2)
+        return fail(ROPE_ERR_RANK, "cos_cache must be rank 2 (max_sequence_length, rotary_dim/2)");
+    if (!same_shape(cos_cache, sin_cache))
+        return fail(ROPE_ERR_SHAPE, "sin_cache must have the shape of cos_cache");
+    if (cos_cache->shape[1] != half)
+        return fail(ROPE_ERR_SHAPE, "cos_cache width %lld != rotary dim / 2 = %lld",
+                    (long long)cos_cache->shape[1], (long long)half);
+    if (position_ids->rank != 3)
+        return fail(ROPE_ERR_RANK, "position_ids must be rank 3 (3, batch, sequence)");
+    if (position_ids->shape[0] != 3 || position_ids->shape[1] != B || position_ids->shape[2] != S)
+        return fail(ROPE_ERR_SHAPE, "position_ids must be (3, %lld, %lld)", (long long)B, (long long)S);
+
+    const rope_tensor* others[3] = {cos_cache, sin_cache, position_ids};
+    const char* names[3] = {"cos_cache", "sin_cache", "position_ids"};
+    TRY(check_output(y, "y", x, others, names, 3));
+
+    Problem& p = out->p;
+    p.dtype = x->dtype;
+    p.interleaved = (int32_t)interleaved;
+    p.B = B; p.S = S; p.D = D; p.R = R;
+    p.ntask = 1;
+    p.task[0].x = x->data;
+    p.task[0].y = y->data;
+    fill_strides(&p.task[0], x->rank, S, H, D);
+    p.coef = kCoefMrope;
+    p.cos = cos_cache->data;
+    p.sin = sin_cache->data;
+    p.ids = (const int64_t*)position_ids->data;
+    p.M = cos_cache->shape[0];
+    p.scale = scale;
+    p.scaling = 1.0f;
+    uint8_t streams[kMaxMropeHalf];
+    mrope_streams(half, mrope_section, mrope_layout, streams);
+    for (int64_t i = 0; i < half; ++i)
+        p.sel[i / 16] |= (uint32_t)streams[i] << (2 * (i % 16));
+    out->empty = numel(x) == 0;
+    choose_geometry(out);
+    return ROPE_OK;
+}
+
+int plan_rope_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor* cos_cache,
+                 const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                 const rope_tensor* yq, const rope_tensor* yk, int64_t interleaved,
+                 int64_t num_heads, int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                 const rope_tensor* inv_freq, float attention_scaling, Plan* out) {
+    clear_error();
+    memset(out, 0, sizeof(*out));
+    if (!q) return fail(ROPE_ERR_NULL, "q is missing");
+    if (!k) return fail(ROPE_ERR_NULL, "k is missing");
+    if (!yq) return fail(ROPE_ERR_NULL, "yq is missing");
+    if (!yk) return fail(ROPE_ERR_NULL, "yk is missing");
+    if ((cos_cache == nullptr) != (sin_cache == nullptr))
+        return fail(ROPE_ERR_NULL, "cos_cache and sin_cache must both be given or both be NULL");
+    const bool onthefly = cos_cache == nullptr;
+    if (onthefly && !inv_freq)
+        return fail(ROPE_ERR_NULL, "inv_freq is required when cos/sin tables are absent");
+    if (onthefly && !position_ids)
+        return fail(ROPE_ERR_NULL, "position_ids are required when cos/sin tables are absent");
+    TRY(check_desc(q, "q"));
+    TRY(check_desc(k, "k"));
+    TRY(check_desc(yq, "yq"));
+    TRY(check_desc(yk, "yk"));
+    if (cos_cache) TRY(check_desc(cos_cache, "cos_cache"));
+    if (sin_cache) TRY(check_desc(sin_cache, "sin_cache"));
+    if (position_ids) TRY(check_desc(position_ids, "position_ids"));
+    if (onthefly) TRY(check_desc(inv_freq, "inv_freq"));
+
+    if (!is_float(q->dtype)) return fail(ROPE_ERR_DTYPE, "q must be float32 or float16");
+    if (k->dtype != q->dtype || yq->dtype != q->dtype || yk->dtype != q->dtype)
+        return fail(ROPE_ERR_DTYPE, "k, yq and yk must have the type of q");
+    if (cos_cache && (cos_cache->dtype != q->dtype || sin_cache->dtype != q->dtype))
+        return fail(ROPE_ERR_DTYPE, "cos_cache and sin_cache must have the type of q");
+    if (position_ids && position_ids->dtype != ROPE_INT64)
+        return fail(ROPE_ERR_DTYPE, "position_ids must be int64");
+    if (onthefly && inv_freq->dtype != ROPE_FLOAT)
+        return fail(ROPE_ERR_DTYPE, "inv_freq must be float32");
+    if (interleaved != 0 && interleaved != 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "interleaved must be 0 or 1");
+    if (num_heads < 0 || kv_num_heads < 0)
+        return fail(ROPE_ERR_ATTRIBUTE, "num_heads and kv_num_heads must be >= 0");
+
+    if (q->rank != 3 && q->rank != 4)
+        return fail(ROPE_ERR_RANK, "q must be rank 3 or 4, got %d", (int)q->rank);
+    if (k->rank != q->rank) return fail(ROPE_ERR_RANK, "k must have the rank of q");
+    if (!same_shape(q, yq)) return fail(ROPE_ERR_SHAPE, "yq must have the shape of q");
+    if (!same_shape(k, yk)) return fail(ROPE_ERR_SHAPE, "yk must have the shape of k");
+    int64_t B, S, H, D, Bk, Sk, Hk, Dk, R, M = 0;
+    TRY(activation_dims(q, "q", num_heads, false, &B, &S, &H, &D));
+    TRY(activation_dims(k, "k", kv_num_heads, false, &Bk, &Sk, &Hk, &Dk));
+    if (Bk != B || Sk != S)
+        return fail(ROPE_ERR_SHAPE, "q and k disagree on batch or sequence length");
+    if (Dk != D) return fail(ROPE_ERR_SHAPE, "q and k disagree on head_size");
+    if (Hk > 0 && H % Hk != 0)
+        return fail(ROPE_ERR_SHAPE, "kv_num_heads %lld must divide num_heads %lld", (long long)Hk,
+                    (long long)H);
+    if (D % 2 != 0) return fail(ROPE_ERR_SHAPE, "head_size %lld must be even", (long long)D);
+    TRY(check_rotary_dim(D, rotary_embedding_dim, &R));
+    if (!onthefly) {
+        TRY(check_tables(cos_cache, sin_cache, position_ids, B, S, R, &M));
+    } else {
+        if (inv_freq->rank != 1 || inv_freq->shape[0] * 2 != R)
+            return fail(ROPE_ERR_SHAPE, "inv_freq must be (rotary_dim/2,) = (%lld,)", (long long)(R / 2));
+        if (position_ids->rank != 2)
+            return fail(ROPE_ERR_RANK, "position_ids must be rank 2 (batch, sequence)");
+        if (position_ids->shape[0] != B || position_ids->shape[1] != S)
+            return fail(ROPE_ERR_SHAPE, "position_ids must be (%lld, %lld)", (long long)B, (long long)S);
+    }
+
+    const rope_tensor* in_q[5] = {k, cos_cache, sin_cache, position_ids, onthefly ? inv_freq : nullptr};
+    const char* nm_q[5] = {"k", "cos_cache", "sin_cache", "position_ids", "inv_freq"};
+    TRY(check_output(yq, "yq", q, in_q, nm_q, 5));
+    const rope_tensor* in_k[6] = {q, cos_cache, sin_cache, position_ids,
+                                  onthefly ? inv_freq : nullptr, yq};
+    const char* nm_k[6] = {"q", "cos_cache", "sin_cache", "position_ids", "inv_freq", "yq"};
+    TRY(check_output(yk, "yk", k, in_k, nm_k, 6));
+
+    Problem& p = out->p;
+    p.dtype = q->dtype;
+    p.interleaved = (int32_t)interleaved;
+    p.B = B; p.S = S; p.D = D; p.R = R;
+    p.ntask = 2;
+    p.task[0].x = q->data;
+    p.task[0].y = yq->data;
+    fill_strides(&p.task[0], q->rank, S, H, D);
+    p.task[1].x = k->data;
+    p.task[1].y = yk->data;
+    fill_strides(&p.task[1], k->rank, S, Hk, D);
+    p.ids = position_ids ? (const int64_t*)position_ids->data : nullptr;
+    p.M = M;
+    p.scale = 1.0f;
+    p.scaling = attention_scaling;
+    if (onthefly) {
+        p.coef = kCoefOnTheFly;
+        p.inv_freq = (const float*)inv_freq->data;
+    } else {
+        p.coef = position_ids ? kCoefGather : kCoefPerToken;
+        p.cos = cos_cache->data;
+        p.sin = sin_cache->data;
+    }
+    out->empty = numel(q) == 0 && numel(k) == 0;
+    choose_geometry(out);
+    return ROPE_OK;
+}
+
+int plan_inv_freq(const rope_tensor* inv_freq, double base, float** out, int64_t* half) {
+    clear_error();
+    if (!inv_freq) return fail(ROPE_ERR_NULL, "inv_freq is missing");
+    TRY(check_desc(inv_freq, "inv_freq"));
+    if (inv_freq->dtype != ROPE_FLOAT) return fail(ROPE_ERR_DTYPE, "inv_freq must be float32");
+    if (inv_freq->rank != 1) return fail(ROPE_ERR_RANK, "inv_freq must be rank 1");
+    if (!(base > 0.0) || !std::isfinite(base))
+        return fail(ROPE_ERR_ATTRIBUTE, "base must be positive and finite");
+    *out = (float*)inv_freq->data;
+    *half = inv_freq->shape[0];
+    return ROPE_OK;
+}
+
+int plan_cos_sin_cache(const rope_tensor* inv_freq, float scaling, const rope_tensor* cos_out,
+                       const rope_tensor* sin_out, TablePlan* out) {
+    clear_error();
+    memset(out, 0, sizeof(*out));
+    if (!inv_freq) return fail(ROPE_ERR_NULL, "inv_freq is missing");
+    if (!cos_out) return fail(ROPE_ERR_NULL, "cos_out is missing");
+    if (!sin_out) return fail(ROPE_ERR_NULL, "sin_out is missing");
+    TRY(check_desc(inv_freq, "inv_freq"));
+    TRY(check_desc(cos_out, "cos_out"));
+    TRY(check_desc(sin_out, "sin_out"));
+    if (inv_freq->dtype != ROPE_FLOAT) return fail(ROPE_ERR_DTYPE, "inv_freq must be float32");
+    if (!is_float(cos_out->dtype) || sin_out->dtype != cos_out->dtype)
+        return fail(ROPE_ERR_DTYPE, "cos_out and sin_out must both be float32 or both float16");
+    if (inv_freq->rank != 1) return fail(ROPE_ERR_RANK, "inv_freq must be rank 1");
+    if (cos_out->rank != 2) return fail(ROPE_ERR_RANK, "cos_out must be rank 2 (rows, rotary_dim/2)");
+    if (!same_shape(cos_out, sin_out)) return fail(ROPE_ERR_SHAPE, "sin_out must have the shape of cos_out");
+    if (cos_out->shape[1] != inv_freq->shape[0])
+        return fail(ROPE_ERR_SHAPE, "table width %lld != inv_freq length %lld",
+                    (long long)cos_out->shape[1], (long long)inv_freq->shape[0]);
+    if (overlaps(cos_out, inv_freq) || overlaps(sin_out, inv_freq) || overlaps(cos_out, sin_out))
+        return fail(ROPE_ERR_ALIAS, "outputs overlap each other or inv_freq");
+    out->inv_freq = (const float*)inv_freq->data;
+    out->cos = cos_out->data;
+    out->sin = sin_out->data;
+    out->dtype = cos_out->dtype;
+    out->rows = cos_out->shape[0];
+    out->half = cos_out->shape[1];
+    out->scaling = scaling;
+    return ROPE_OK;
+}
+
+}  // namespace rope

@@ -1,0 +1,116 @@
+// rope_plan.hpp -- host-side description of one rotary-embedding launch.
+//
+// Validation (the ops' contracts) and kernel choice are plain C++ with no HIP
+// dependency (rope_plan.cpp); rope_kernels.hip turns a Plan into launches.
+#pragma once
+
+#include <cstdint>
+
+#include "rope_mi355x.h"
+
+namespace rope {
+
+// How a token's coefficient row is obtained.
+enum CoefKind : int32_t {
+    kCoefGather = 0,   // row ids[b,s] of an (M, R/2) table, id outside [0,M) -> copy
+    kCoefPerToken = 1, // row b*S+s of a (B, S, R/2) table
+    kCoefMrope = 2,    // slot i from row ids[stream(i), b, s], scaled, per-pair copy
+    kCoefOnTheFly = 3  // computed from inv_freq and the position
+};
+
+constexpr int kMaxMropeHalf = 512;             // slots the stream table can hold
+constexpr int kSelWords = kMaxMropeHalf / 16;  // 2 bits per slot
+
+// One input/output pair rotated with the shared coefficients.
+struct Task {
+    const void* x;
+    void* y;
+    int64_t heads;
+    int64_t stride_b, stride_h, stride_s;  // element strides of x(b, h, s, 0)
+};
+
+struct Problem {
+    int32_t dtype;        // ROPE_FLOAT or ROPE_FLOAT16
+    int32_t interleaved;  // 0 or 1
+    int64_t B, S, D, R;   // batch, sequence, head size, rotary dim
+    Task task[2];
+    int32_t ntask;
+    CoefKind coef;
+    const void* cos;
+    const void* sin;
+    const int64_t* ids;
+    int64_t M;            // table rows (gathered kinds)
+    const float* inv_freq;
+    float scaling;        // on-the-fly attention scaling
+    float scale;          // M-RoPE coefficient scale
+    uint32_t sel[kSelWords];  // M-RoPE stream of slot i in bits 2*(i%16) of word i/16
+};
+
+// Launch geometry of the vector kernel (see rope_kernels.hip for the mapping).
+struct Geometry {
+    bool vector;          // false: scalar kernel
+    int32_t items_per_lane;
+    int32_t W;            // 16-byte work items per head row
+    int32_t NP;           // of which rotation items
+    int32_t TG;           // tokens per wave
+    int32_t heads_per_wave[2];
+    int32_t chunks[2];    // head chunks per token group
+    int64_t waves[2];
+    const char* variant;
+};
+
+struct Plan {
+    Problem p;
+    Geometry g;
+    bool empty;           // nothing to launch
+};
+
+int plan_rope(const rope_tensor* x, const rope_tensor* cos_cache,
+              const rope_tensor* sin_cache, const rope_tensor* position_ids,
+              const rope_tensor* y, int64_t interleaved, int64_t num_heads,
+              int64_t rotary_embedding_dim, Plan* out);
+
+int plan_mrope(const rope_tensor* x, const rope_tensor* position_ids,
+               const rope_tensor* cos_cache, const rope_tensor* sin_cache,
+               const rope_tensor* y, int64_t interleaved,
+               int64_t is_packed_batching, int64_t mrope_layout,
+               const int64_t mrope_section[3], int64_t num_heads,
+               int64_t rotary_embedding_dim, float scale, Plan* out);
+
+int plan_rope_qk(const rope_tensor* q, const rope_tensor* k,
+                 const rope_tensor* cos_cache, const rope_tensor* sin_cache,
+                 const rope_tensor* position_ids, const rope_tensor* yq,
+                 const rope_tensor* yk, int64_t interleaved, int64_t num_heads,
+                 int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                 const rope_tensor* inv_freq, float attention_scaling,
+                 Plan* out);
+
+struct TablePlan {
+    const float* inv_freq;
+    void* cos;
+    void* sin;
+    int32_t dtype;
+    int64_t rows, half;
+    float scaling;
+};
+
+int plan_inv_freq(const rope_tensor* inv_freq, double base, float** out,
+                  int64_t* half);
+int plan_cos_sin_cache(const rope_tensor* inv_freq, float scaling,
+                       const rope_tensor* cos_out, const rope_tensor* sin_out,
+                       TablePlan* out);
+
+// Stream of each M-RoPE slot (0 t, 1 h, 2 w) for layout 0 or 1; the caller
+// has checked that the sections are non-negative and sum to `half`.
+void mrope_streams(int64_t half, const int64_t section[3], int64_t layout,
+                   uint8_t* stream_of_slot);
+
+// Error reporting: sets the thread's message and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+const char* last_error();
+
+int kernel_policy();
+int set_kernel_policy(int policy);
+
+}  // namespace rope

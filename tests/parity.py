@@ -1,0 +1,66 @@
+"""Element-by-element comparison of GPU results with the oracle.
+
+Tolerances (stated for the rotary-embedding apply, arithmetic in binary32 with
+fma and one rounding to the storage type):
+  float16: |gpu - oracle| <= 1 ulp of the oracle value, where the ulp of a
+           binary16 value v is 2^(floor(log2|v|) - 10) for |v| >= 2^-14 and
+           2^-24 below (the binary32 result is correctly rounded, so only the
+           second rounding to binary16 can differ from the oracle's single
+           rounding, by at most one unit).
+  float32: |gpu - oracle| <= 2e-6 * max(1, |oracle|).
+Pass-through elements (tail, out-of-range pairs) and gathered coefficient
+probes are compared bit for bit.
+"""
+import numpy as np
+
+
+def bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view({2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize])
+
+
+def ulp_f16(v):
+    a = np.abs(v.astype(np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
+    return np.exp2(e - 10)
+
+
+def compare(got, want):
+    assert got.shape == want.shape and got.dtype == want.dtype, (got.shape, want.shape, got.dtype, want.dtype)
+    g = got.astype(np.float64).reshape(-1)
+    w = want.astype(np.float64).reshape(-1)
+    nan_w = np.isnan(w)
+    nan_bad = int(np.count_nonzero(nan_w != np.isnan(g)))
+    finite = ~nan_w & ~np.isnan(g)
+    diff = np.zeros_like(w)
+    diff[finite] = np.abs(g[finite] - w[finite])
+    diff[~np.isfinite(diff)] = np.inf
+    same_inf = np.isinf(w) & (g == w)
+    diff[same_inf] = 0.0
+    if got.dtype == np.float16:
+        tol = ulp_f16(w)
+        ulps = np.where(finite, diff / tol, 0.0)
+    else:
+        tol = 2e-6 * np.maximum(1.0, np.abs(w))
+        ulps = np.zeros_like(w)
+    over = finite & (diff > tol)
+    return {
+        "n": int(w.size),
+        "max_abs": float(diff[finite].max()) if finite.any() else 0.0,
+        "max_ulp": float(ulps.max()) if ulps.size else 0.0,
+        "n_over_tol": int(np.count_nonzero(over)) + nan_bad,
+        "n_bit_diff": int(np.count_nonzero(bits(got).reshape(-1) != bits(want).reshape(-1))),
+    }
+
+
+def assert_parity(got, want, what=""):
+    r = compare(got, want)
+    assert r["n_over_tol"] == 0, "%s: %s" % (what, r)
+    return r
+
+
+def assert_bitwise(got, want, what=""):
+    bg, bw = bits(got).reshape(-1), bits(want).reshape(-1)
+    bad = np.flatnonzero(bg != bw)
+    assert bad.size == 0, "%s: %d of %d differ bitwise; first at %d: %r vs %r" % (
+        what, bad.size, bg.size, bad[0], got.reshape(-1)[bad[0]], want.reshape(-1)[bad[0]])

@@ -1,0 +1,400 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and its validation (the *_check entry points, which never touch the
+GPU) enforces each clause of the ops' contracts."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rotary_position_embedding_amd as rpe
+from rotary_position_embedding_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rope_mi355x.h")
+
+F32, F16, I64 = 1, 10, 7
+OK, NULL, DTYPE, RANK, SHAPE, ATTR, UNSUP, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_parses():
+    fns = header_functions()
+    for name in ("rope_apply", "mrope_apply", "rope_apply_qk", "rope_inv_freq",
+                 "rope_cos_sin_cache", "rope_status_string", "rope_last_error"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+        assert name in _lib.SIGNATURES, "binding lacks %s" % name
+
+
+def test_status_strings():
+    lib = _lib.load()
+    for code, name in _lib.STATUS.items():
+        assert lib.rope_status_string(code).decode() == name
+    assert lib.rope_status_string(-99).decode() == "ROPE_ERR_UNKNOWN"
+
+
+# ---------------------------------------------------------------------------
+# descriptors over fake, aligned, non-overlapping device addresses: validation
+# never dereferences them.
+
+class Alloc:
+    def __init__(self):
+        self.next = 1 << 32
+
+    def __call__(self, dtype, shape, align=256):
+        nbytes = {F32: 4, F16: 2, I64: 8}.get(dtype, 4)
+        for d in shape:
+            nbytes *= d
+        addr = self.next
+        self.next += (nbytes + 2 * align) // align * align
+        return rpe.tensor_spec(addr, dtype, shape)
+
+
+def rope_case(rank=3, dt=F16, B=2, S=5, H=4, D=16, R=0, ids=True, M=16, interleaved=0,
+              num_heads=None, **over):
+    a = Alloc()
+    Rf = R or D
+    x = a(dt, (B, S, H * D) if rank == 3 else (B, H, S, D))
+    y = a(dt, tuple(x.shape[:rank]))
+    if ids:
+        cos = a(dt, (M, Rf // 2))
+        sin = a(dt, (M, Rf // 2))
+        pid = a(I64, (B, S))
+    else:
+        cos = a(dt, (B, S, Rf // 2))
+        sin = a(dt, (B, S, Rf // 2))
+        pid = None
+    kw = dict(x=x, cos_cache=cos, sin_cache=sin, position_ids=pid, y=y, interleaved=interleaved,
+              num_heads=(H if rank == 3 else 0) if num_heads is None else num_heads,
+              rotary_embedding_dim=R)
+    kw.update(over)
+    return kw
+
+
+def check_rope(kw):
+    return rpe.rope_apply_check(kw["x"], kw["cos_cache"], kw["sin_cache"], kw["position_ids"],
+                                kw["y"], interleaved=kw["interleaved"], num_heads=kw["num_heads"],
+                                rotary_embedding_dim=kw["rotary_embedding_dim"])
+
+
+def reshape(t, shape, dtype=None):
+    return rpe.tensor_spec(t.data, dtype if dtype is not None else t.dtype, shape)
+
+
+@pytest.mark.parametrize("rank,ids", [(3, True), (4, True), (3, False), (4, False)])
+@pytest.mark.parametrize("dt", [F16, F32])
+def test_rope_variants_accepted(rank, ids, dt):
+    """One positive case per manifest variant (rank3/rank4 x cache2+ids / cache3)."""
+    rc, variant = check_rope(rope_case(rank=rank, ids=ids, dt=dt))
+    assert rc == OK, _lib.load().rope_last_error()
+    assert variant == ("vec16/gather" if ids else "vec16/per_token")
+
+
+def test_rope_partial_interleaved_accepted():
+    for il in (0, 1):
+        rc, v = check_rope(rope_case(rank=4, dt=F32, D=96, R=64, interleaved=il))
+        assert rc == OK and v == "vec16/gather"
+
+
+def test_rope_scalar_path_for_unaligned_shapes():
+    rc, v = check_rope(rope_case(D=6))       # 6 halves: no 16-byte items
+    assert rc == OK and v == "scalar/gather"
+    kw = rope_case()
+    kw["x"] = reshape(kw["x"], tuple(kw["x"].shape[:3]))
+    kw["x"].data += 2                      # misaligned x
+    rc, v = check_rope(kw)
+    assert rc == OK and v == "scalar/gather"
+
+
+def test_kernel_policy_forces_scalar():
+    old = rpe.set_kernel_policy(1)
+    try:
+        rc, v = check_rope(rope_case())
+        assert rc == OK and v == "scalar/gather"
+    finally:
+        rpe.set_kernel_policy(old)
+    rc, v = check_rope(rope_case())
+    assert v == "vec16/gather"
+
+
+# Each clause of the manifest's contracts, negated -> its status.
+def _neg_cases():
+    cases = []
+
+    def add(name, code, **kw):
+        cases.append((name, code, kw))
+
+    add("x_missing", NULL, x=None)
+    add("cos_missing", NULL, cos_cache=None)
+    add("sin_missing", NULL, sin_cache=None)
+    add("y_missing", NULL, y=None)
+    add("interleaved_2", ATTR, interleaved=2)
+    add("interleaved_neg", ATTR, interleaved=-1)
+    add("num_heads_negative", ATTR, num_heads=-1)
+    add("rank3_without_num_heads", ATTR, num_heads=0)
+    add("rotary_dim_negative", ATTR, rotary_embedding_dim=-2)
+    add("rotary_dim_odd", ATTR, rotary_embedding_dim=3)
+    return cases
+
+
+@pytest.mark.parametrize("name,code,over", _neg_cases(), ids=[c[0] for c in _neg_cases()])
+def test_rope_attribute_clauses(name, code, over):
+    kw = rope_case()
+    kw.update(over)
+    rc, _ = check_rope(kw)
+    assert rc == code, (name, rc, _lib.load().rope_last_error())
+
+
+def test_rope_shape_clauses():
+    lib = _lib.load()
+
+    def expect(kw, code, what):
+        rc, _ = check_rope(kw)
+        assert rc == code, (what, rc, lib.rope_last_error())
+
+    # dtype clauses
+    kw = rope_case(); kw["x"] = reshape(kw["x"], tuple(kw["x"].shape[:3]), 16)      # bf16
+    expect(kw, DTYPE, "x bf16")
+    kw = rope_case(); kw["cos_cache"] = reshape(kw["cos_cache"], (16, 8), F32)
+    expect(kw, DTYPE, "cos dtype")
+    kw = rope_case(); kw["y"] = reshape(kw["y"], (2, 5, 64), F32)
+    expect(kw, DTYPE, "y dtype")
+    kw = rope_case(); kw["position_ids"] = reshape(kw["position_ids"], (2, 5), F32)
+    expect(kw, DTYPE, "ids dtype")
+    # rank clauses
+    kw = rope_case(); kw["x"] = reshape(kw["x"], (10, 64))
+    expect(kw, RANK, "x rank 2")
+    kw = rope_case(); kw["cos_cache"] = reshape(kw["cos_cache"], (1, 16, 8)); kw["sin_cache"] = reshape(kw["sin_cache"], (1, 16, 8))
+    expect(kw, RANK, "3-D cache with ids")
+    kw = rope_case(ids=False); kw["cos_cache"] = reshape(kw["cos_cache"], (10, 8)); kw["sin_cache"] = reshape(kw["sin_cache"], (10, 8))
+    expect(kw, RANK, "2-D cache without ids")
+    kw = rope_case(); kw["position_ids"] = reshape(kw["position_ids"], (10,))
+    expect(kw, RANK, "ids rank 1")
+    # shape clauses
+    kw = rope_case(); kw["y"] = reshape(kw["y"], (2, 5, 32))
+    expect(kw, SHAPE, "y shape")
+    expect(rope_case(num_heads=3), SHAPE, "hidden % num_heads")
+    expect(rope_case(D=6, H=4, num_heads=8), SHAPE, "odd head size via num_heads")       # 24/8 = 3
+    expect(rope_case(rank=4, num_heads=3), SHAPE, "rank-4 num_heads disagrees")
+    expect(rope_case(rotary_embedding_dim=18), SHAPE, "rotary dim > head size")
+    kw = rope_case(); kw["cos_cache"] = reshape(kw["cos_cache"], (16, 7)); kw["sin_cache"] = reshape(kw["sin_cache"], (16, 7))
+    expect(kw, SHAPE, "cache width")
+    kw = rope_case(); kw["sin_cache"] = reshape(kw["sin_cache"], (15, 8))
+    expect(kw, SHAPE, "sin shape != cos shape")
+    kw = rope_case(); kw["position_ids"] = reshape(kw["position_ids"], (2, 4))
+    expect(kw, SHAPE, "ids (B,S)")
+    kw = rope_case(ids=False); kw["cos_cache"] = reshape(kw["cos_cache"], (2, 4, 8)); kw["sin_cache"] = reshape(kw["sin_cache"], (2, 4, 8))
+    expect(kw, SHAPE, "3-D cache (B,S)")
+    kw = rope_case(rank=4, D=7); expect(kw, SHAPE, "rank-4 odd head size")
+    # NULL data of a non-empty tensor
+    kw = rope_case(); kw["x"] = reshape(kw["x"], (2, 5, 64)); kw["x"].data = None
+    expect(kw, NULL, "x data NULL")
+    # negative dimension
+    kw = rope_case(); kw["x"] = reshape(kw["x"], (2, -5, 64))
+    expect(kw, SHAPE, "negative dim")
+
+
+def test_rope_alias_clauses():
+    kw = rope_case()
+    kw["y"] = reshape(kw["x"], (2, 5, 64))          # exactly x: in place, allowed
+    assert check_rope(kw)[0] == OK
+    kw = rope_case()
+    y = reshape(kw["x"], (2, 5, 64)); y.data += 16   # shifted: partial overlap
+    kw["y"] = y
+    assert check_rope(kw)[0] == ALIAS
+    kw = rope_case()
+    kw["y"] = reshape(kw["y"], (2, 5, 64)); kw["y"].data = kw["cos_cache"].data
+    assert check_rope(kw)[0] == ALIAS
+    kw = rope_case()
+    kw["y"] = reshape(kw["y"], (2, 5, 64)); kw["y"].data = kw["position_ids"].data
+    assert check_rope(kw)[0] == ALIAS
+
+
+def test_rope_empty_tensors_accepted():
+    for B, S in ((0, 5), (2, 0)):
+        kw = rope_case(B=B, S=S)
+        assert check_rope(kw)[0] == OK
+    kw = rope_case(rank=4, H=0, num_heads=0)
+    assert check_rope(kw)[0] == OK
+    kw = rope_case(M=0)          # empty table: every id out of range, still valid
+    kw["cos_cache"].data = None
+    kw["sin_cache"].data = None
+    assert check_rope(kw)[0] == OK
+
+
+# ---------------------------------------------------------------------------
+# MRotaryEmbedding README: Inputs and Attributes
+
+def mrope_case(rank=4, dt=F16, B=2, S=5, H=3, D=16, R=0, M=20, section=(4, 2, 2), **over):
+    a = Alloc()
+    Rf = R or D
+    x = a(dt, (B, S, H * D) if rank == 3 else (B, H, S, D))
+    kw = dict(x=x, position_ids=a(I64, (3, B, S)), cos_cache=a(dt, (M, Rf // 2)),
+              sin_cache=a(dt, (M, Rf // 2)), y=a(dt, tuple(x.shape[:rank])),
+              mrope_section=section, interleaved=0, is_packed_batching=0, mrope_layout=0,
+              num_heads=H if (rank == 3 or R) else 0, rotary_embedding_dim=R, scale=1.0)
+    kw.update(over)
+    return kw
+
+
+def check_mrope(kw):
+    kw = dict(kw)
+    args = [kw.pop(k) for k in ("x", "position_ids", "cos_cache", "sin_cache", "y")]
+    return rpe.mrope_apply_check(*args, **kw)
+
+
+def test_mrope_accepted():
+    for rank in (3, 4):
+        for layout in (0, 1):
+            for dt in (F16, F32):
+                rc, v = check_mrope(mrope_case(rank=rank, mrope_layout=layout, dt=dt))
+                assert rc == OK and v == "vec16/mrope", _lib.load().rope_last_error()
+    # odd head size with a smaller even rotary dim: allowed, scalar kernel
+    rc, v = check_mrope(mrope_case(D=9, R=8, section=(2, 1, 1)))
+    assert rc == OK and v == "scalar/mrope"
+
+
+def test_mrope_clauses():
+    lib = _lib.load()
+    cases = [
+        ("ids missing", NULL, dict(position_ids=None)),
+        ("section missing", NULL, dict(mrope_section=None)),
+        ("packed batching", UNSUP, dict(is_packed_batching=1)),
+        ("packed batching 2", ATTR, dict(is_packed_batching=2)),
+        ("layout 2", ATTR, dict(mrope_layout=2)),
+        ("interleaved 2", ATTR, dict(interleaved=2)),
+        ("negative section", ATTR, dict(mrope_section=(5, -1, 4))),
+        ("section sum", ATTR, dict(mrope_section=(4, 2, 1))),
+        ("rotary odd", ATTR, dict(rotary_embedding_dim=7)),
+        ("rotary negative", ATTR, dict(rotary_embedding_dim=-2)),
+        ("num_heads negative", ATTR, dict(num_heads=-1)),
+        ("rank-4 rotary dim without num_heads", ATTR, dict(rotary_embedding_dim=8, num_heads=0,
+                                                           mrope_section=(2, 1, 1))),
+        ("rank-4 num_heads disagrees", SHAPE, dict(num_heads=2)),
+    ]
+    for name, code, over in cases:
+        kw = mrope_case()
+        kw.update(over)
+        rc, _ = check_mrope(kw)
+        assert rc == code, (name, rc, lib.rope_last_error())
+    kw = mrope_case(rank=3, num_heads=0)
+    assert check_mrope(kw)[0] == ATTR
+    kw = mrope_case(rank=3); kw["num_heads"] = 5
+    assert check_mrope(kw)[0] == SHAPE
+    kw = mrope_case(D=9, R=0, section=(2, 1, 1))
+    assert check_mrope(kw)[0] == SHAPE                  # odd head size needs a rotary dim
+    kw = mrope_case(R=18, section=(5, 2, 2))
+    assert check_mrope(kw)[0] == SHAPE                  # rotary dim > head size
+    kw = mrope_case(); kw["position_ids"] = reshape(kw["position_ids"], (2, 5))
+    assert check_mrope(kw)[0] == RANK
+    kw = mrope_case(); kw["position_ids"] = reshape(kw["position_ids"], (2, 2, 5))
+    assert check_mrope(kw)[0] == SHAPE
+    kw = mrope_case(); kw["cos_cache"] = reshape(kw["cos_cache"], (20, 7)); kw["sin_cache"] = reshape(kw["sin_cache"], (20, 7))
+    assert check_mrope(kw)[0] == SHAPE
+    kw = mrope_case(); kw["cos_cache"] = reshape(kw["cos_cache"], (2, 10, 8))
+    assert check_mrope(kw)[0] == RANK
+    kw = mrope_case(); kw["sin_cache"] = reshape(kw["sin_cache"], (19, 8))
+    assert check_mrope(kw)[0] == SHAPE
+    kw = mrope_case(); kw["position_ids"] = reshape(kw["position_ids"], (3, 2, 5), F32)
+    assert check_mrope(kw)[0] == DTYPE
+    kw = mrope_case(D=2048, section=(1024, 0, 0))
+    assert check_mrope(kw)[0] == UNSUP                  # beyond the stream table
+
+
+# ---------------------------------------------------------------------------
+# Q + K
+
+def qk_case(rank=3, dt=F16, B=4, S=1, H=8, Hk=2, D=16, M=64, table=True, ids=True, **over):
+    a = Alloc()
+    q = a(dt, (B, S, H * D) if rank == 3 else (B, H, S, D))
+    k = a(dt, (B, S, Hk * D) if rank == 3 else (B, Hk, S, D))
+    kw = dict(q=q, k=k,
+              cos_cache=a(dt, (M, D // 2) if ids else (B, S, D // 2)) if table else None,
+              sin_cache=a(dt, (M, D // 2) if ids else (B, S, D // 2)) if table else None,
+              position_ids=a(I64, (B, S)) if ids else None,
+              yq=a(dt, tuple(q.shape[:rank])), yk=a(dt, tuple(k.shape[:rank])),
+              interleaved=0, num_heads=H if rank == 3 else 0, kv_num_heads=Hk if rank == 3 else 0,
+              rotary_embedding_dim=0, inv_freq=None if table else a(F32, (D // 2,)),
+              attention_scaling=1.0)
+    kw.update(over)
+    return kw
+
+
+def check_qk(kw):
+    kw = dict(kw)
+    args = [kw.pop(k) for k in ("q", "k", "cos_cache", "sin_cache", "position_ids", "yq", "yk")]
+    return rpe.rope_apply_qk_check(*args, **kw)
+
+
+def test_qk_accepted():
+    for rank in (3, 4):
+        assert check_qk(qk_case(rank=rank)) == (OK, "vec16/gather")
+        assert check_qk(qk_case(rank=rank, table=False)) == (OK, "vec16/on_the_fly")
+        assert check_qk(qk_case(rank=rank, ids=False)) == (OK, "vec16/per_token")
+
+
+def test_qk_clauses():
+    lib = _lib.load()
+    cases = [
+        ("only cos", NULL, dict(sin_cache=None)),
+        ("on the fly without inv_freq", NULL, dict(cos_cache=None, sin_cache=None)),
+        ("kv heads do not divide", SHAPE, dict(kv_num_heads=3)),
+        ("num_heads missing", ATTR, dict(num_heads=0)),
+    ]
+    for name, code, over in cases:
+        kw = qk_case()
+        kw.update(over)
+        rc, _ = check_qk(kw)
+        assert rc == code, (name, rc, lib.rope_last_error())
+    kw = qk_case(table=False, ids=False)
+    assert check_qk(kw)[0] == NULL                     # on the fly needs positions
+    kw = qk_case(table=False); kw["inv_freq"] = reshape(kw["inv_freq"], (7,))
+    assert check_qk(kw)[0] == SHAPE
+    kw = qk_case(table=False); kw["inv_freq"] = reshape(kw["inv_freq"], (8,), F16)
+    assert check_qk(kw)[0] == DTYPE
+    kw = qk_case(); kw["k"] = reshape(kw["k"], (4, 2, 32))
+    assert check_qk(kw)[0] == SHAPE                    # sequence differs
+    kw = qk_case(); kw["k"] = reshape(kw["k"], (4, 1, 2, 16))
+    assert check_qk(kw)[0] == RANK
+    kw = qk_case(); kw["yk"] = reshape(kw["yk"], (4, 1, 32)); kw["yk"].data = kw["yq"].data
+    assert check_qk(kw)[0] == ALIAS                    # outputs overlap
+    kw = qk_case(); kw["yq"] = reshape(kw["q"], (4, 1, 128))
+    kw["yk"] = reshape(kw["k"], (4, 1, 32))
+    assert check_qk(kw)[0] == OK                       # both in place
+
+
+# ---------------------------------------------------------------------------
+# host copies of the slot-to-stream reading agree (product vs oracle, both
+# written independently from the same reading) -- exercised via the check
+# path is not possible, so compare on the only shared observable: counts.
+
+def test_inv_freq_and_table_validation():
+    lib = _lib.load()
+    a = Alloc()
+    inv = a(F32, (64,))
+    assert lib.rope_inv_freq(ctypes.byref(reshape(inv, (64,), F16)), 1e4, None) == DTYPE
+    assert lib.rope_inv_freq(ctypes.byref(reshape(inv, (8, 8))), 1e4, None) == RANK
+    assert lib.rope_inv_freq(ctypes.byref(inv), -1.0, None) == ATTR
+    assert lib.rope_inv_freq(None, 1e4, None) == NULL
+    cos, sin = a(F16, (128, 64)), a(F16, (128, 64))
+    f = lib.rope_cos_sin_cache
+    assert f(ctypes.byref(inv), 1.0, ctypes.byref(reshape(cos, (128, 32))), ctypes.byref(reshape(sin, (128, 32))), None) == SHAPE
+    assert f(ctypes.byref(inv), 1.0, ctypes.byref(cos), ctypes.byref(reshape(sin, (128, 64), F32)), None) == DTYPE
+    assert f(ctypes.byref(inv), 1.0, ctypes.byref(cos), ctypes.byref(cos), None) == ALIAS
+    assert f(ctypes.byref(inv), 1.0, ctypes.byref(reshape(cos, (8192,))), ctypes.byref(reshape(sin, (8192,))), None) == RANK

@@ -1,0 +1,387 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs, element by element. Tolerances are in parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotary_position_embedding_amd as rpe
+from oracle_pins import angle_table, ids_in, pair_index
+from parity import assert_bitwise, assert_parity, bits, compare
+from rope_inputs import WORKLOADS, normal_tensor, with_layout
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@pytest.fixture(autouse=True)
+def _policy():
+    old = rpe.set_kernel_policy(0)
+    yield
+    rpe.set_kernel_policy(old)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at their full sizes, in the default launch configuration
+
+def run_workload(w, onthefly=False):
+    """(gpu output(s), oracle output(s), inputs) for a workload."""
+    x = w.make_x()
+    ids = w.make_ids()
+    cos, sin = oracle.table_for(w)
+    if w.op == "rope":
+        want = oracle.rope_apply(x, cos, sin, ids, interleaved=w.interleaved,
+                                 num_heads=w.num_heads if w.rank == 3 else 0,
+                                 rotary_embedding_dim=w.rotary_embedding_dim)
+        got = rpe.rope_apply(cuda(x), cuda(cos), cuda(sin), None if ids is None else cuda(ids),
+                             interleaved=w.interleaved, num_heads=w.num_heads if w.rank == 3 else 0,
+                             rotary_embedding_dim=w.rotary_embedding_dim)
+        return host(got), want, (x, ids, cos, sin)
+    if w.op == "mrope":
+        want = oracle.mrope_apply(x, ids, cos, sin, w.mrope_section, w.mrope_layout,
+                                  interleaved=w.interleaved, num_heads=w.num_heads,
+                                  rotary_embedding_dim=w.rotary_embedding_dim, scale=w.scale)
+        got = rpe.mrope_apply(cuda(x), cuda(ids), cuda(cos), cuda(sin), mrope_section=w.mrope_section,
+                              mrope_layout=w.mrope_layout, interleaved=w.interleaved,
+                              num_heads=w.num_heads, rotary_embedding_dim=w.rotary_embedding_dim,
+                              scale=w.scale)
+        return host(got), want, (x, ids, cos, sin)
+    k = w.make_k()
+    inv = oracle.inv_freq(w.cache_base, w.rotary_dim)
+    if onthefly:
+        want = oracle.rope_apply_qk(x, k, None, None, ids, num_heads=w.num_heads,
+                                    kv_num_heads=w.kv_num_heads, inv_freq=inv,
+                                    attention_scaling=w.scaling)
+        got = rpe.rope_apply_qk(cuda(x), cuda(k), None, None, cuda(ids), num_heads=w.num_heads,
+                                kv_num_heads=w.kv_num_heads, inv_freq=cuda(inv),
+                                attention_scaling=w.scaling)
+    else:
+        want = oracle.rope_apply_qk(x, k, cos, sin, ids, num_heads=w.num_heads,
+                                    kv_num_heads=w.kv_num_heads)
+        got = rpe.rope_apply_qk(cuda(x), cuda(k), cuda(cos), cuda(sin), cuda(ids),
+                                num_heads=w.num_heads, kv_num_heads=w.kv_num_heads)
+    return (host(got[0]), host(got[1])), want, (x, k, ids)
+
+
+def test_c1_rope_f32_tiny():
+    w = WORKLOADS["c1_rope_f32_tiny"]
+    got, want, _ = run_workload(w)
+    r = assert_parity(got, want, w.name)
+    log("%s %s" % (w.name, r))
+
+
+def test_c2_rope_f16_prefill():
+    w = WORKLOADS["c2_rope_f16_prefill"]
+    got, want, _ = run_workload(w)
+    r = assert_parity(got, want, w.name)
+    log("%s %s" % (w.name, r))
+
+
+def test_c3_rope_f32_partial_interleaved():
+    w = WORKLOADS["c3_rope_f32_partial_interleaved"]
+    got, want, (x, *_rest) = run_workload(w)
+    r = assert_parity(got, want, w.name)
+    assert_bitwise(got[..., 64:], x[..., 64:], "tail")
+    log("%s %s" % (w.name, r))
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_c4_mrope_f16_prefill(layout):
+    w = with_layout(WORKLOADS["c4_mrope_f16_prefill"], layout)
+    got, want, (x, ids, _c, _s) = run_workload(w)
+    r = assert_parity(got, want, w.name)
+    # pairs whose stream id is out of range: bit copies of x
+    streams = oracle.mrope_slot_streams(w.half, w.mrope_section, layout)
+    sid = ids[streams]                              # (P, B, S)
+    oob = (sid < 0) | (sid >= w.cache_rows)
+    i, b, s = np.nonzero(oob)
+    assert i.size > 0
+    for j in (i, i + w.half):
+        assert_bitwise(got[b, :, s, j], x[b, :, s, j], "out-of-range pairs")
+    log("%s %s oob_pairs=%d" % (w.name, r, i.size))
+
+
+@pytest.mark.parametrize("onthefly", [False, True])
+def test_c5_rope_qk_f16_decode(onthefly):
+    w = WORKLOADS["c5_rope_qk_f16_decode"]
+    (gq, gk), (wq, wk), _ = run_workload(w, onthefly)
+    rq = assert_parity(gq, wq, w.name + " Q")
+    rk = assert_parity(gk, wk, w.name + " K")
+    log("%s onthefly=%s Q %s K %s" % (w.name, onthefly, rq, rk))
+
+
+def test_c5_onthefly_equals_table_on_gpu():
+    w = WORKLOADS["c5_rope_qk_f16_decode"]
+    q, k, ids = cuda(w.make_x()), cuda(w.make_k()), cuda(w.make_ids())
+    inv = rpe.rope_inv_freq(w.rotary_dim, w.cache_base, device=DEV)
+    cos, sin = rpe.rope_cos_sin_cache(inv, w.cache_rows, torch.float16)
+    a = rpe.rope_apply_qk(q, k, cos, sin, ids, num_heads=32, kv_num_heads=8)
+    b = rpe.rope_apply_qk(q, k, None, None, ids, num_heads=32, kv_num_heads=8, inv_freq=inv)
+    assert_bitwise(host(a[0]), host(b[0]), "Q")
+    assert_bitwise(host(a[1]), host(b[1]), "K")
+
+
+# ---------------------------------------------------------------------------
+# table builders
+
+@pytest.mark.parametrize("dt,base,R,rows,scaling", [
+    (np.float16, 1e6, 128, 32768, 1.0), (np.float32, 1e4, 64, 4096, 1.0),
+    (np.float16, 1e4, 8, 16, 1.0), (np.float32, 1e6, 128, 4096, 0.7), (np.float16, 5e5, 96, 1000, 1.25)])
+def test_tables_match_oracle(dt, base, R, rows, scaling):
+    inv_o = oracle.inv_freq(base, R)
+    inv_g = host(rpe.rope_inv_freq(R, base, device=DEV))
+    assert_bitwise(inv_g, inv_o, "inv_freq")
+    cos_o, sin_o = oracle.cos_sin_cache(dt, rows, inv_o, scaling)
+    cos_g, sin_g = rpe.rope_cos_sin_cache(cuda(inv_o), rows, torch.float16 if dt == np.float16 else torch.float32,
+                                          scaling)
+    rc = compare(host(cos_g), cos_o)
+    rs = compare(host(sin_g), sin_o)
+    # cos/sin of a binary32 angle rounded to binary32 by two libraries: equal
+    # unless the value sits within a binary64 ulp of a rounding boundary
+    assert rc["n_over_tol"] == 0 and rs["n_over_tol"] == 0
+    assert rc["n_bit_diff"] + rs["n_bit_diff"] <= 2, (rc, rs)
+    log("table %s base=%g R=%d rows=%d bitdiff=%d/%d" % (np.dtype(dt), base, R, rows,
+                                                           rc["n_bit_diff"], rs["n_bit_diff"]))
+
+
+# ---------------------------------------------------------------------------
+# sweeps over shapes, both kernels, ragged tails
+
+SHAPES = [
+    # rank, dt, B, S, H, D, R, interleaved, ids, M
+    (3, np.float16, 3, 37, 5, 128, 0, 0, True, 300),
+    (4, np.float16, 2, 41, 3, 64, 0, 1, True, 100),
+    (4, np.float32, 2, 19, 7, 96, 64, 1, True, 64),
+    (4, np.float32, 3, 23, 2, 96, 64, 0, True, 64),
+    (3, np.float32, 2, 33, 4, 80, 32, 0, False, 0),
+    (3, np.float16, 1, 70, 3, 256, 128, 0, True, 500),
+    (4, np.float16, 2, 9, 9, 80, 0, 0, False, 0),
+    (3, np.float16, 5, 1, 33, 128, 0, 0, True, 1000),   # decode-like
+    (4, np.float32, 1, 130, 1, 32, 0, 1, True, 140),
+    (3, np.float16, 2, 13, 4, 6, 0, 0, True, 20),        # not 16-byte items
+    (4, np.float16, 2, 13, 4, 18, 10, 1, True, 20),
+    (3, np.float32, 2, 7, 3, 2, 0, 0, False, 0),
+    (4, np.float16, 1, 17, 2, 1024, 0, 0, True, 40),     # long rows
+]
+
+
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("case", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
+def test_rope_sweep(case, policy):
+    rank, dt, B, S, H, D, R, il, has_ids, M = case
+    rpe.set_kernel_policy(policy)
+    Rf = R or D
+    shape = (B, S, H * D) if rank == 3 else (B, H, S, D)
+    x = normal_tensor(1000 + B * S * H + D, shape, dt)
+    if has_ids:
+        cos, sin = angle_table(2000 + D, M, Rf // 2, dt)
+        ids = ids_in(3000 + S, (B, S), M + 3) - 1        # some -1 and some >= M
+        ids[0, 0] = 0
+    else:
+        cos, sin = angle_table(2001 + D, B * S, Rf // 2, dt)
+        cos, sin = cos.reshape(B, S, -1), sin.reshape(B, S, -1)
+        ids = None
+    nh = H if rank == 3 else 0
+    want = oracle.rope_apply(x, cos, sin, ids, interleaved=il, num_heads=nh, rotary_embedding_dim=R)
+    got = host(rpe.rope_apply(cuda(x), cuda(cos), cuda(sin), None if ids is None else cuda(ids),
+                              interleaved=il, num_heads=nh, rotary_embedding_dim=R))
+    assert_parity(got, want, str(case))
+    xd = x if rank == 4 else x.reshape(B, S, H, D)
+    gd = got if rank == 4 else got.reshape(B, S, H, D)
+    assert_bitwise(gd[..., Rf:], xd[..., Rf:], "tail")
+    if ids is not None:
+        bad = (ids < 0) | (ids >= M)
+        b, s = np.nonzero(bad)
+        if rank == 4:
+            assert_bitwise(got[b, :, s], x[b, :, s], "out-of-range rows")
+        else:
+            assert_bitwise(got[b, s], x[b, s], "out-of-range rows")
+
+
+@pytest.mark.parametrize("dt", [np.float16, np.float32])
+@pytest.mark.parametrize("il", [0, 1])
+def test_gather_probe_bitexact(dt, il):
+    B, H, S, D, M = 3, 4, 29, 128, 777
+    cos, sin = angle_table(4000, M, D // 2, dt)
+    ids = ids_in(4001, (B, S), M)
+    j1, j2 = pair_index(il, D // 2)
+    x = np.zeros((B, H, S, D), dt)
+    x[..., j1] = 1
+    y = host(rpe.rope_apply(cuda(x), cuda(cos), cuda(sin), cuda(ids), interleaved=il))
+    for h in range(H):
+        assert_bitwise(y[:, h][..., j1], cos[ids], "probe cos")
+        assert_bitwise(y[:, h][..., j2], sin[ids], "probe sin")
+
+
+def test_in_place_and_canaries():
+    B, S, H, D, M = 2, 300, 8, 128, 1024
+    x = normal_tensor(5000, (B, S, H * D), np.float16)
+    cos, sin = angle_table(5001, M, D // 2, np.float16)
+    ids = ids_in(5002, (B, S), M)
+    want = oracle.rope_apply(x, cos, sin, ids, num_heads=H)
+    # in place
+    xt = cuda(x)
+    out = rpe.rope_apply(xt, cuda(cos), cuda(sin), cuda(ids), num_heads=H, out=xt)
+    assert out.data_ptr() == xt.data_ptr()
+    assert_parity(host(xt), want, "in place")
+    # y inside a poisoned buffer: every element overwritten, canaries untouched
+    n = x.size
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=torch.float16, device=DEV)
+    buf.view(torch.int16)[:] = 0x7e11                      # NaN with a payload
+    y = buf[pad:pad + n].view(B, S, H * D)
+    rpe.rope_apply(cuda(x), cuda(cos), cuda(sin), cuda(ids), num_heads=H, out=y)
+    whole = bits(host(buf))
+    assert (whole[:pad] == 0x7e11).all() and (whole[pad + n:] == 0x7e11).all(), "canary overwritten"
+    assert_parity(host(y), want, "poisoned output")
+
+
+def test_empty_inputs_launch_nothing():
+    for shape, ids_shape in (((0, 4, 64), (0, 4)), ((2, 0, 64), (2, 0))):
+        x = torch.empty(shape, dtype=torch.float16, device=DEV)
+        cos = torch.zeros(8, 16, dtype=torch.float16, device=DEV)
+        ids = torch.zeros(ids_shape, dtype=torch.int64, device=DEV)
+        y = rpe.rope_apply(x, cos, cos, ids, num_heads=2)
+        assert y.shape == shape
+
+
+def test_errors_raise():
+    x = torch.zeros(2, 3, 64, dtype=torch.float16, device=DEV)
+    cos = torch.zeros(8, 16, dtype=torch.float16, device=DEV)
+    ids = torch.zeros(2, 3, dtype=torch.int64, device=DEV)
+    with pytest.raises(rpe.RopeError) as e:
+        rpe.rope_apply(x, cos, cos, ids, num_heads=3)
+    assert e.value.status_name == "ROPE_ERR_SHAPE"
+    with pytest.raises(rpe.RopeError):
+        rpe.rope_apply(x, cos.float(), cos.float(), ids, num_heads=2)
+
+
+# ---------------------------------------------------------------------------
+# M-RoPE
+
+MROPE = [
+    # rank, dt, B, S, H, D, R, section, interleaved, scale
+    (4, np.float16, 2, 45, 3, 128, 0, (16, 24, 24), 0, 1.0),
+    (3, np.float16, 2, 33, 4, 128, 0, (24, 20, 20), 1, 1.0),
+    (4, np.float32, 1, 50, 2, 64, 0, (10, 11, 11), 0, 2.0),
+    (3, np.float32, 3, 17, 3, 96, 64, (8, 12, 12), 1, 0.5),
+    (4, np.float16, 2, 20, 2, 9, 8, (2, 1, 1), 0, 1.0),      # odd head size, scalar kernel
+    (4, np.float16, 2, 21, 5, 80, 48, (0, 12, 12), 0, 1.25),
+    (3, np.float16, 1, 40, 2, 256, 0, (40, 44, 44), 1, 1.0),
+]
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("case", MROPE, ids=[str(i) for i in range(len(MROPE))])
+def test_mrope_sweep(case, policy, layout):
+    rank, dt, B, S, H, D, R, sec, il, scale = case
+    rpe.set_kernel_policy(policy)
+    Rf = R or D
+    M = 97
+    shape = (B, S, H * D) if rank == 3 else (B, H, S, D)
+    x = normal_tensor(6000 + D + S, shape, dt)
+    cos, sin = angle_table(6001 + D, M, Rf // 2, dt)
+    ids = ids_in(6002 + S, (3, B, S), M + 4) - 2
+    ids[:, 0, 0] = (0, 1, 2)
+    ids[1, -1, -1] = 2 ** 40
+    ids[2, -1, -2] = -(2 ** 40)
+    want = oracle.mrope_apply(x, ids, cos, sin, sec, layout, interleaved=il, num_heads=H,
+                              rotary_embedding_dim=R, scale=scale)
+    got = host(rpe.mrope_apply(cuda(x), cuda(ids), cuda(cos), cuda(sin), mrope_section=sec,
+                               mrope_layout=layout, interleaved=il, num_heads=H,
+                               rotary_embedding_dim=R, scale=scale))
+    assert_parity(got, want, str(case))
+    # copies are bit-exact
+    xd = x if rank == 4 else x.reshape(B, S, H, D).transpose(0, 2, 1, 3)
+    gd = got if rank == 4 else got.reshape(B, S, H, D).transpose(0, 2, 1, 3)
+    assert_bitwise(np.ascontiguousarray(gd[..., Rf:]), np.ascontiguousarray(xd[..., Rf:]), "tail")
+    streams = oracle.mrope_slot_streams(Rf // 2, sec, layout)
+    sid = ids[streams]
+    oob = (sid < 0) | (sid >= M)
+    i, b, s = np.nonzero(oob)
+    j1, j2 = pair_index(il, Rf // 2)
+    for j in (j1[i], j2[i]):
+        assert_bitwise(gd[b, :, s, j], xd[b, :, s, j], "out-of-range pairs")
+
+
+def test_mrope_equal_streams_equal_rope_on_gpu():
+    B, H, S, D, M = 2, 6, 77, 128, 500
+    x = cuda(normal_tensor(7000, (B, H, S, D), np.float16))
+    cos, sin = (cuda(a) for a in angle_table(7001, M, D // 2, np.float16))
+    ids = ids_in(7002, (B, S), M)
+    ids3 = cuda(np.stack([ids, ids, ids]))
+    a = host(rpe.rope_apply(x, cos, sin, cuda(ids)))
+    for layout in (0, 1):
+        b = host(rpe.mrope_apply(x, ids3, cos, sin, mrope_section=(16, 24, 24), mrope_layout=layout))
+        assert_bitwise(b, a, "equal streams layout %d" % layout)
+
+
+# ---------------------------------------------------------------------------
+# Q + K
+
+QK = [
+    # rank, dt, B, S, H, Hk, D, R, il
+    (3, np.float16, 7, 1, 8, 2, 128, 0, 0),
+    (4, np.float16, 3, 17, 4, 4, 64, 0, 1),
+    (3, np.float32, 2, 9, 6, 2, 96, 64, 1),
+    (4, np.float32, 2, 5, 4, 1, 128, 0, 0),
+    (3, np.float16, 3, 4, 4, 2, 10, 0, 0),   # scalar kernel
+]
+
+
+@pytest.mark.parametrize("onthefly", [False, True])
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("case", QK, ids=[str(i) for i in range(len(QK))])
+def test_qk_sweep(case, policy, onthefly):
+    rank, dt, B, S, H, Hk, D, R, il = case
+    rpe.set_kernel_policy(policy)
+    Rf = R or D
+    M = 40000
+    q = normal_tensor(8000 + D, (B, S, H * D) if rank == 3 else (B, H, S, D), dt)
+    k = normal_tensor(8001 + D, (B, S, Hk * D) if rank == 3 else (B, Hk, S, D), dt)
+    ids = ids_in(8002, (B, S), M)
+    inv = oracle.inv_freq(1e6, Rf)
+    cos, sin = oracle.cos_sin_cache(dt, M, inv, 1.0)
+    nh, nk = (H, Hk) if rank == 3 else (0, 0)
+    if onthefly:
+        want = oracle.rope_apply_qk(q, k, None, None, ids, interleaved=il, num_heads=nh, kv_num_heads=nk,
+                                    rotary_embedding_dim=R, inv_freq=inv, attention_scaling=1.0)
+        got = rpe.rope_apply_qk(cuda(q), cuda(k), None, None, cuda(ids), interleaved=il, num_heads=nh,
+                                kv_num_heads=nk, rotary_embedding_dim=R, inv_freq=cuda(inv))
+    else:
+        want = oracle.rope_apply_qk(q, k, cos, sin, ids, interleaved=il, num_heads=nh, kv_num_heads=nk,
+                                    rotary_embedding_dim=R)
+        got = rpe.rope_apply_qk(cuda(q), cuda(k), cuda(cos), cuda(sin), cuda(ids), interleaved=il,
+                                num_heads=nh, kv_num_heads=nk, rotary_embedding_dim=R)
+    assert_parity(host(got[0]), want[0], "Q " + str(case))
+    assert_parity(host(got[1]), want[1], "K " + str(case))
+
+
+def test_qk_in_place():
+    B, S, H, Hk, D = 16, 1, 8, 2, 128
+    q = normal_tensor(9000, (B, S, H * D), np.float16)
+    k = normal_tensor(9001, (B, S, Hk * D), np.float16)
+    ids = ids_in(9002, (B, S), 4096)
+    inv = oracle.inv_freq(1e6, D)
+    cos, sin = oracle.cos_sin_cache(np.float16, 4096, inv)
+    want = oracle.rope_apply_qk(q, k, cos, sin, ids, num_heads=H, kv_num_heads=Hk)
+    qt, kt = cuda(q), cuda(k)
+    rpe.rope_apply_qk(qt, kt, cuda(cos), cuda(sin), cuda(ids), num_heads=H, kv_num_heads=Hk,
+                      out_q=qt, out_k=kt)
+    assert_parity(host(qt), want[0], "Q in place")
+    assert_parity(host(kt), want[1], "K in place")
