@@ -190,12 +190,35 @@ __device__ inline TaskView task_of(const KArgs& a, bool second) {
 //   item w < NP rotates: split halves -> elements [w*E, w*E+E) with partners
 //   R/2 later; interleaved -> elements [w*E, w*E+E) = E/2 pairs.
 //   item w >= NP copies elements [R + (w-NP)*E, +E).
-template <typename T, int IL, int COEF, int IPL>
+// Memory order per wave: position ids first, then the X chunks of the first
+// head batch, then the table gather that depends on the ids; vector loads
+// complete in issue order, so the gather's latency hides under the X loads.
+// X and Y are touched once: nontemporal loads and stores.
+
+template <typename T, int IL, int IPL, int HU>
+__device__ inline void load_batch(const char* x, const int64_t* off, const bool* act, const bool* rot,
+                                  int h, int h_end, int64_t sh_bytes, int64_t half_bytes,
+                                  u32x4 (*in1)[IPL], u32x4 (*in2)[IPL]) {
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+#pragma unroll
+        for (int m = 0; m < IPL; ++m) {
+            if (act[m] && h + u < h_end) {
+                const u32x4* px = reinterpret_cast<const u32x4*>(x + off[m] + (int64_t)(h + u) * sh_bytes);
+                in1[u][m] = __builtin_nontemporal_load(px);
+                if (!IL && rot[m])
+                    in2[u][m] = __builtin_nontemporal_load(px + half_bytes / 16);
+            }
+        }
+    }
+}
+
+template <typename T, int IL, int COEF, int IPL, int HU>
 __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation item
-    constexpr int HU = IPL == 1 ? 4 : 2;  // heads per batch of loads
     constexpr int ES = (int)sizeof(T);
+    typedef T cvec __attribute__((ext_vector_type(CE)));
 
     const int lane = threadIdx.x & 63;
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
@@ -211,11 +234,11 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     const int64_t sh_bytes = tk.sh * ES;
     const int64_t half_bytes = (int64_t)a.P * ES;
 
+    // -- items of this lane (no memory traffic) -----------------------------
     bool act[IPL], rot[IPL];
     int64_t off[IPL];    // byte offset of the item's first chunk for head 0
-    u32x4 keep[IPL];     // input bits passed through unchanged
-    float cf[IPL][CE], sf[IPL][CE];
-
+    int64_t tok[IPL];
+    int slot0[IPL];
 #pragma unroll
     for (int m = 0; m < IPL; ++m) {
         const int q = lane + 64 * m;
@@ -223,68 +246,104 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         const int w = q - t * a.W;
         const int64_t n = n0 + t;
         act[m] = t < a.TG && n < a.ntok;
-        rot[m] = w < a.NP;
-        off[m] = 0;
+        rot[m] = act[m] && w < a.NP;
+        tok[m] = act[m] ? n : 0;
+        const int64_t b = tok[m] / a.S;
+        const int64_t s = tok[m] - b * a.S;
+        const int64_t e0 = w < a.NP ? (int64_t)w * E : (int64_t)a.R + (int64_t)(w - a.NP) * E;
+        off[m] = act[m] ? (b * tk.sb + s * tk.ss + e0) * ES : 0;
+        slot0[m] = w * CE;
+    }
+
+    // -- position ids, then X, then the dependent table reads --------------
+    int64_t pos[IPL][COEF == kCoefMrope ? 3 : 1];
+    if (COEF == kCoefGather || COEF == kCoefOnTheFly) {
+#pragma unroll
+        for (int m = 0; m < IPL; ++m) pos[m][0] = rot[m] ? a.ids[tok[m]] : 0;
+    } else if (COEF == kCoefMrope) {
+#pragma unroll
+        for (int m = 0; m < IPL; ++m)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) pos[m][k] = rot[m] ? a.ids[k * a.ntok + tok[m]] : 0;
+    }
+
+    u32x4 in1[HU][IPL], in2[HU][IPL];
+    load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h_begin, h_end, sh_bytes, half_bytes, in1, in2);
+
+    T cf[IPL][CE], sf[IPL][CE];
+    u32x4 keep[IPL];  // input bits passed through unchanged
+#pragma unroll
+    for (int m = 0; m < IPL; ++m) {
         keep[m] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int j = 0; j < CE; ++j) { cf[m][j] = 1.0f; sf[m][j] = 0.0f; }
-        if (!act[m]) continue;
-        const int64_t b = n / a.S;
-        const int64_t s = n - b * a.S;
-        const int64_t e0 = rot[m] ? (int64_t)w * E : (int64_t)a.R + (int64_t)(w - a.NP) * E;
-        off[m] = (b * tk.sb + s * tk.ss + e0) * ES;
+        for (int j = 0; j < CE; ++j) { cf[m][j] = (T)1.0f; sf[m][j] = (T)0.0f; }
         if (!rot[m]) continue;
-        const int slot0 = w * CE;
         if (COEF == kCoefGather || COEF == kCoefPerToken) {
-            int64_t row = n;
-            bool valid = true;
-            if (COEF == kCoefGather) {
-                row = a.ids[n];
-                valid = row >= 0 && row < a.M;
-            }
+            const int64_t row = COEF == kCoefGather ? pos[m][0] : tok[m];
+            const bool valid = COEF == kCoefPerToken || (row >= 0 && row < a.M);
             if (valid) {
-                typedef T cvec __attribute__((ext_vector_type(CE)));
-                const cvec cv = *reinterpret_cast<const cvec*>(a.cos + (row * a.P + slot0) * ES);
-                const cvec sv = *reinterpret_cast<const cvec*>(a.sin + (row * a.P + slot0) * ES);
+                const int64_t e = (row * a.P + slot0[m]) * ES;
+                const cvec cv = *reinterpret_cast<const cvec*>(a.cos + e);
+                const cvec sv = *reinterpret_cast<const cvec*>(a.sin + e);
 #pragma unroll
-                for (int j = 0; j < CE; ++j) { cf[m][j] = to_f(cv[j]); sf[m][j] = to_f(sv[j]); }
+                for (int j = 0; j < CE; ++j) { cf[m][j] = cv[j]; sf[m][j] = sv[j]; }
             } else {
                 keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
             }
-        } else {
+        } else if (COEF == kCoefMrope) {
+            // the slice [slot0, slot0 + CE) of each stream's row; slot i takes
+            // the slice of its stream (2-bit codes, CE <= 16 slots in a word)
+            const uint32_t codes = a.sel[slot0[m] >> 4] >> (2 * (slot0[m] & 15));
+            cvec cs3[3], ss3[3];
+            bool ok3[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int64_t p = pos[m][k];
+                ok3[k] = p >= 0 && p < a.M;
+                cs3[k] = cvec{};
+                ss3[k] = cvec{};
+                if (ok3[k]) {
+                    const int64_t e = (p * a.P + slot0[m]) * ES;
+                    cs3[k] = *reinterpret_cast<const cvec*>(a.cos + e);
+                    ss3[k] = *reinterpret_cast<const cvec*>(a.sin + e);
+                }
+            }
+            const bool unit = a.scale == 1.0f;
 #pragma unroll
             for (int j = 0; j < CE; ++j) {
-                bool copy;
-                coef_slot<T, COEF>(a, n, slot0 + j, cf[m][j], sf[m][j], copy);
-                if (copy) {
+                const uint32_t k = (codes >> (2 * j)) & 3u;
+                const T c = k == 0 ? cs3[0][j] : (k == 1 ? cs3[1][j] : cs3[2][j]);
+                const T sn = k == 0 ? ss3[0][j] : (k == 1 ? ss3[1][j] : ss3[2][j]);
+                const bool ok = k == 0 ? ok3[0] : (k == 1 ? ok3[1] : ok3[2]);
+                // scaled coefficient: binary32 product rounded to T
+                cf[m][j] = unit ? c : from_f<T>(keep_f32(to_f(c) * a.scale));
+                sf[m][j] = unit ? sn : from_f<T>(keep_f32(to_f(sn) * a.scale));
+                if (!ok) {
                     if (IL) { mask_elem<T>(keep[m], 2 * j); mask_elem<T>(keep[m], 2 * j + 1); }
                     else mask_elem<T>(keep[m], j);
                 }
             }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CE; ++j) {
+                float c, s;
+                onthefly_coef<T>(a.inv_freq[slot0[m] + j], pos[m][0], a.scaling, c, s);
+                cf[m][j] = from_f<T>(c);
+                sf[m][j] = from_f<T>(s);
+            }
         }
     }
 
+    // -- rotate and store, one head batch at a time --------------------------
     for (int h = h_begin; h < h_end; h += HU) {
-        u32x4 in1[HU][IPL], in2[HU][IPL];
-#pragma unroll
-        for (int u = 0; u < HU; ++u) {
-#pragma unroll
-            for (int m = 0; m < IPL; ++m) {
-                if (act[m] && h + u < h_end) {
-                    const char* px = tk.x + off[m] + (int64_t)(h + u) * sh_bytes;
-                    in1[u][m] = load16(px);
-                    if (!IL && rot[m]) in2[u][m] = load16(px + half_bytes);
-                }
-            }
-        }
 #pragma unroll
         for (int u = 0; u < HU; ++u) {
 #pragma unroll
             for (int m = 0; m < IPL; ++m) {
                 if (!(act[m] && h + u < h_end)) continue;
-                char* py = tk.y + off[m] + (int64_t)(h + u) * sh_bytes;
+                u32x4* py = reinterpret_cast<u32x4*>(tk.y + off[m] + (int64_t)(h + u) * sh_bytes);
                 if (!rot[m]) {
-                    store16(py, in1[u][m]);
+                    __builtin_nontemporal_store(in1[u][m], py);
                     continue;
                 }
                 if (IL) {
@@ -294,12 +353,13 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     for (int j = 0; j < CE; ++j) {
                         const float x1 = to_f(xv[2 * j]);
                         const float x2 = to_f(xv[2 * j + 1]);
-                        r[2 * j] = fmaf(x1, cf[m][j], -(x2 * sf[m][j]));
-                        r[2 * j + 1] = fmaf(x2, cf[m][j], x1 * sf[m][j]);
+                        const float c = to_f(cf[m][j]), s = to_f(sf[m][j]);
+                        r[2 * j] = fmaf(x1, c, -(x2 * s));
+                        r[2 * j + 1] = fmaf(x2, c, x1 * s);
                     }
                     u32x4 o = chunk_pack<T>(r);
                     if (COEF == kCoefGather || COEF == kCoefMrope) o = select_bits(keep[m], in1[u][m], o);
-                    store16(py, o);
+                    __builtin_nontemporal_store(o, py);
                 } else {
                     const auto xv1 = chunk_values<T>(in1[u][m]);
                     const auto xv2 = chunk_values<T>(in2[u][m]);
@@ -308,8 +368,9 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     for (int j = 0; j < E; ++j) {
                         const float x1 = to_f(xv1[j]);
                         const float x2 = to_f(xv2[j]);
-                        r1[j] = fmaf(x1, cf[m][j], -(x2 * sf[m][j]));
-                        r2[j] = fmaf(x2, cf[m][j], x1 * sf[m][j]);
+                        const float c = to_f(cf[m][j]), s = to_f(sf[m][j]);
+                        r1[j] = fmaf(x1, c, -(x2 * s));
+                        r2[j] = fmaf(x2, c, x1 * s);
                     }
                     u32x4 o1 = chunk_pack<T>(r1);
                     u32x4 o2 = chunk_pack<T>(r2);
@@ -317,11 +378,13 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         o1 = select_bits(keep[m], in1[u][m], o1);
                         o2 = select_bits(keep[m], in2[u][m], o2);
                     }
-                    store16(py, o1);
-                    store16(py + half_bytes, o2);
+                    __builtin_nontemporal_store(o1, py);
+                    __builtin_nontemporal_store(o2, py + half_bytes / 16);
                 }
             }
         }
+        if (h + HU < h_end)
+            load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h + HU, h_end, sh_bytes, half_bytes, in1, in2);
     }
 }
 
@@ -403,26 +466,37 @@ static int launched(hipError_t e) {
     return ROPE_OK;
 }
 
+// Instantiated (items per lane, head batch) pairs; the planner picks one.
 template <typename T, int IL, int COEF>
-static hipError_t launch_vec_ipl(const KArgs& a, int ipl, dim3 grid, hipStream_t st) {
+static hipError_t launch_vec_ipl(const KArgs& a, int ipl, int hu, dim3 grid, hipStream_t st) {
     void* args[] = {const_cast<KArgs*>(&a)};
     const void* fn;
-    switch (ipl) {
-        case 1: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1>; break;
-        case 2: fn = (const void*)rope_vec_kernel<T, IL, COEF, 2>; break;
-        case 3: fn = (const void*)rope_vec_kernel<T, IL, COEF, 3>; break;
-        default: fn = (const void*)rope_vec_kernel<T, IL, COEF, 4>; break;
+#define ROPE_VEC(I, H) (const void*)rope_vec_kernel<T, IL, COEF, I, H>
+    switch (ipl * 16 + hu) {
+        case 1 * 16 + 2: fn = ROPE_VEC(1, 2); break;
+        case 1 * 16 + 4: fn = ROPE_VEC(1, 4); break;
+        case 1 * 16 + 8: fn = ROPE_VEC(1, 8); break;
+        case 2 * 16 + 2: fn = ROPE_VEC(2, 2); break;
+        case 2 * 16 + 4: fn = ROPE_VEC(2, 4); break;
+        case 2 * 16 + 8: fn = ROPE_VEC(2, 8); break;
+        case 3 * 16 + 2: fn = ROPE_VEC(3, 2); break;
+        case 3 * 16 + 4: fn = ROPE_VEC(3, 4); break;
+        case 4 * 16 + 2: fn = ROPE_VEC(4, 2); break;
+        case 4 * 16 + 4: fn = ROPE_VEC(4, 4); break;
+        default: return hipErrorInvalidValue;
     }
+#undef ROPE_VEC
     return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
 }
 
 template <typename T, int IL>
-static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, dim3 grid, hipStream_t st) {
+static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, dim3 grid,
+                                  hipStream_t st) {
     switch (c) {
-        case kCoefGather: return launch_vec_ipl<T, IL, kCoefGather>(a, ipl, grid, st);
-        case kCoefPerToken: return launch_vec_ipl<T, IL, kCoefPerToken>(a, ipl, grid, st);
-        case kCoefMrope: return launch_vec_ipl<T, IL, kCoefMrope>(a, ipl, grid, st);
-        default: return launch_vec_ipl<T, IL, kCoefOnTheFly>(a, ipl, grid, st);
+        case kCoefGather: return launch_vec_ipl<T, IL, kCoefGather>(a, ipl, hu, grid, st);
+        case kCoefPerToken: return launch_vec_ipl<T, IL, kCoefPerToken>(a, ipl, hu, grid, st);
+        case kCoefMrope: return launch_vec_ipl<T, IL, kCoefMrope>(a, ipl, hu, grid, st);
+        default: return launch_vec_ipl<T, IL, kCoefOnTheFly>(a, ipl, hu, grid, st);
     }
 }
 
@@ -490,12 +564,13 @@ int launch_plan(const Plan& pl, void* stream) {
         if (waves == 0) return ROPE_OK;
         const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
         const int ipl = g.items_per_lane;
+        const int hu = g.head_batch;
         if (p.dtype == ROPE_FLOAT16)
-            e = p.interleaved ? launch_vec_coef<half_t, 1>(a, p.coef, ipl, grid, st)
-                              : launch_vec_coef<half_t, 0>(a, p.coef, ipl, grid, st);
+            e = p.interleaved ? launch_vec_coef<half_t, 1>(a, p.coef, ipl, hu, grid, st)
+                              : launch_vec_coef<half_t, 0>(a, p.coef, ipl, hu, grid, st);
         else
-            e = p.interleaved ? launch_vec_coef<float, 1>(a, p.coef, ipl, grid, st)
-                              : launch_vec_coef<float, 0>(a, p.coef, ipl, grid, st);
+            e = p.interleaved ? launch_vec_coef<float, 1>(a, p.coef, ipl, hu, grid, st)
+                              : launch_vec_coef<float, 0>(a, p.coef, ipl, hu, grid, st);
     } else {
         const int64_t K = p.R / 2 + (p.D - p.R);
         const int64_t total0 = p.B * p.S * p.task[0].heads * K;

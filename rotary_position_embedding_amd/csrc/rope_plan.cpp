@@ -147,10 +147,13 @@ static const char* variant_name(bool vec, CoefKind c) {
     return names[vec ? 1 : 0][(int)c];
 }
 
-static int heads_per_wave_override() {
-    const char* e = getenv("ROPE_HEADS_PER_WAVE");
+static int env_int(const char* name) {
+    const char* e = getenv(name);
     return e ? atoi(e) : 0;
 }
+
+// Tuning overrides (for measurement sweeps): heads per wave, head batch.
+static int heads_per_wave_override() { return env_int("ROPE_HEADS_PER_WAVE"); }
 
 // Vector kernel: a head row of D elements is cut into 16-byte items; a
 // rotation item holds E = 16/sizeof(T) pairs' first elements (split halves,
@@ -168,7 +171,7 @@ static void choose_geometry(Plan* pl) {
     ok = ok && p.D % E == 0 && p.R % E == 0 && (p.interleaved || half % E == 0);
     for (int t = 0; t < p.ntask; ++t)
         ok = ok && aligned16(p.task[t].x) && aligned16(p.task[t].y);
-    if (p.coef == kCoefGather || p.coef == kCoefPerToken)
+    if (p.coef == kCoefGather || p.coef == kCoefPerToken || p.coef == kCoefMrope)
         ok = ok && aligned16(p.cos) && aligned16(p.sin);
     const int64_t NP = p.interleaved ? p.R / E : half / E;
     const int64_t NT = (p.D - p.R) / E;
@@ -196,21 +199,32 @@ static void choose_geometry(Plan* pl) {
     const int64_t ntok = p.B * p.S;
     const int64_t groups = (ntok + g.TG - 1) / g.TG;
     const int over = heads_per_wave_override();
-    // Head chunks: split heads until the launch has enough waves to cover
-    // the chip (256 CUs) several times over.
-    const int64_t target = 4096;
+    const int over_batch = env_int("ROPE_HEAD_BATCH");
+    // Head batch: heads whose X loads a lane issues together. Aim for about
+    // 16 16-byte loads in flight per lane (a rotation item of split halves
+    // loads two chunks), within the instantiated (items, batch) pairs.
+    const int per_item = p.interleaved ? 1 : 2;
+    const int max_batch = best <= 2 ? 8 : 4;
+    int hb = 2;
+    while (hb * 2 <= max_batch && best * hb * 2 * per_item <= 16) hb *= 2;
+    if (over_batch == 2 || over_batch == 4 || over_batch == 8)
+        hb = over_batch <= max_batch ? over_batch : max_batch;
+    g.head_batch = hb;
+    // Heads per wave: one batch, split evenly over the head count (28 heads
+    // with batch 8 -> 4 waves of 7); halved for small launches so that they
+    // still spread over the chip.
+    int64_t total_heads = 0;
+    for (int t = 0; t < p.ntask; ++t) total_heads += p.task[t].heads;
+    int64_t hpw_cap = hb;
+    while (hpw_cap > 2 && groups * ((total_heads + hpw_cap - 1) / hpw_cap) < 1024) hpw_cap /= 2;
+    if (over > 0) hpw_cap = over;
     for (int t = 0; t < p.ntask; ++t) {
-        int64_t H = p.task[t].heads;
-        int64_t hpw = H > 0 ? H : 1;
-        if (over > 0) {
-            hpw = over < hpw ? over : hpw;
-        } else {
-            while (hpw > 1 && groups * ((H + hpw - 1) / hpw) < target)
-                hpw = (hpw + 1) / 2;
-        }
+        const int64_t H = p.task[t].heads;
+        int64_t chunks = H > 0 ? (H + hpw_cap - 1) / hpw_cap : 1;
+        int64_t hpw = H > 0 ? (H + chunks - 1) / chunks : 1;
         g.heads_per_wave[t] = (int32_t)hpw;
-        g.chunks[t] = (int32_t)((H + hpw - 1) / hpw);
-        g.waves[t] = H > 0 ? groups * g.chunks[t] : 0;
+        g.chunks[t] = (int32_t)chunks;
+        g.waves[t] = H > 0 ? groups * chunks : 0;
     }
 }
 

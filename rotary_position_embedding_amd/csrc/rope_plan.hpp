@@ -50,6 +50,7 @@ struct Problem {
 struct Geometry {
     bool vector;          // false: scalar kernel
     int32_t items_per_lane;
+    int32_t head_batch;   // heads whose loads are issued together (kernel template)
     int32_t W;            // 16-byte work items per head row
     int32_t NP;           // of which rotation items
     int32_t TG;           // tokens per wave
