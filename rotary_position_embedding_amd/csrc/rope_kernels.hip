@@ -42,7 +42,7 @@ struct KTask {
     char* y;
     int64_t sb, sh, ss;  // element strides of (b, h, s)
     int64_t wave_begin;  // first wave of this task in the launch
-    int32_t heads, hpw, chunks, pad;
+    int32_t heads, hpw, chunks, tile;  // tile: token groups per head chunk in a wave tile
 };
 
 struct KArgs {
@@ -53,6 +53,7 @@ struct KArgs {
     const int64_t* ids;
     const float* inv_freq;
     int32_t ntask, W, NP, TG, P, R, D, interleaved;
+    int32_t xcd_remap, pad2;
     float scaling, scale;
     uint32_t sel[kSelWords];
 };
@@ -165,7 +166,7 @@ struct TaskView {
     const char* x;
     char* y;
     int64_t sb, sh, ss, wave_begin;
-    int32_t heads, hpw, chunks;
+    int32_t heads, hpw, chunks, tile;
 };
 
 __device__ inline TaskView task_of(const KArgs& a, bool second) {
@@ -179,13 +180,17 @@ __device__ inline TaskView task_of(const KArgs& a, bool second) {
     v.heads = second ? a.t[1].heads : a.t[0].heads;
     v.hpw = second ? a.t[1].hpw : a.t[0].hpw;
     v.chunks = second ? a.t[1].chunks : a.t[0].chunks;
+    v.tile = second ? a.t[1].tile : a.t[0].tile;
     return v;
 }
 
 // ---------------------------------------------------------------------------
 // Vector kernel.
-//   wave -> (task, token group g, head chunk hc); hc varies fastest, so the
-//   chunks of one token group sit in one workgroup and share its L1.
+//   wave -> (task, token group g, head chunk hc) in tiles of `tile` token
+//   groups x all chunks: g varies fastest inside a tile. tile = 1 (rank 3:
+//   a token's heads are contiguous) puts the chunks of one token group in one
+//   workgroup; tile = 4 (rank 4: a head's tokens are contiguous) gives each
+//   head chunk a run of 4 consecutive token groups per workgroup.
 //   lane item q = lane + 64*m (m < IPL) -> token t = q / W, item w = q % W.
 //   item w < NP rotates: split halves -> elements [w*E, w*E+E) with partners
 //   R/2 later; interleaved -> elements [w*E, w*E+E) = E/2 pairs.
@@ -194,6 +199,18 @@ __device__ inline TaskView task_of(const KArgs& a, bool second) {
 // head batch, then the table gather that depends on the ids; vector loads
 // complete in issue order, so the gather's latency hides under the X loads.
 // X and Y are touched once: nontemporal loads and stores.
+
+// Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i % 8),
+// each XCD with its own L2. With remapping, consecutive logical workgroups
+// run on the same XCD, so the waves that share a token group's ids and
+// coefficient rows fill one L2 instead of several. A bijection on
+// [0, gridDim.x) for any grid size.
+__device__ inline uint32_t logical_block(int remap) {
+    const uint32_t p = blockIdx.x;
+    if (!remap) return p;
+    const uint32_t n = gridDim.x, q = n / 8, r = n % 8, x = p % 8;
+    return x * q + min(x, r) + p / 8;
+}
 
 template <typename T, int IL, int IPL, int HU>
 __device__ inline void load_batch(const char* x, const int64_t* off, const bool* act, const bool* rot,
@@ -221,12 +238,15 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     typedef T cvec __attribute__((ext_vector_type(CE)));
 
     const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + (threadIdx.x >> 6);
     const bool second = a.ntask > 1 && gw >= a.t[1].wave_begin;
     const TaskView tk = task_of(a, second);
     const int64_t local = gw - tk.wave_begin;
-    const int64_t g = local / tk.chunks;
-    const int hc = (int)(local - g * tk.chunks);
+    const int64_t per_tile = (int64_t)tk.tile * tk.chunks;
+    const int64_t tile = local / per_tile;
+    const int r = (int)(local - tile * per_tile);
+    const int hc = r / tk.tile;
+    const int64_t g = tile * tk.tile + (r - hc * tk.tile);
     const int64_t n0 = g * a.TG;
     if (n0 >= a.ntok) return;
     const int h_begin = hc * tk.hpw;
@@ -291,36 +311,60 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                 keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
             }
         } else if (COEF == kCoefMrope) {
-            // the slice [slot0, slot0 + CE) of each stream's row; slot i takes
-            // the slice of its stream (2-bit codes, CE <= 16 slots in a word)
+            // Slots [slot0, slot0 + CE) of the three stream rows; slot i takes
+            // its stream's value. Per-stream element masks over the slice are
+            // built once, then the slice is assembled with bitwise and/or on
+            // whole dwords; a stream whose id is out of range contributes its
+            // slots to the copy mask instead.
+            constexpr int CW = CE * ES / 4;  // dwords in a coefficient slice
+            typedef uint32_t cbits __attribute__((ext_vector_type(CW)));
             const uint32_t codes = a.sel[slot0[m] >> 4] >> (2 * (slot0[m] & 15));
-            cvec cs3[3], ss3[3];
-            bool ok3[3];
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const int64_t p = pos[m][k];
-                ok3[k] = p >= 0 && p < a.M;
-                cs3[k] = cvec{};
-                ss3[k] = cvec{};
-                if (ok3[k]) {
-                    const int64_t e = (p * a.P + slot0[m]) * ES;
-                    cs3[k] = *reinterpret_cast<const cvec*>(a.cos + e);
-                    ss3[k] = *reinterpret_cast<const cvec*>(a.sin + e);
-                }
-            }
-            const bool unit = a.scale == 1.0f;
+            cbits msk0 = {}, msk1 = {}, msk2 = {};
 #pragma unroll
             for (int j = 0; j < CE; ++j) {
                 const uint32_t k = (codes >> (2 * j)) & 3u;
-                const T c = k == 0 ? cs3[0][j] : (k == 1 ? cs3[1][j] : cs3[2][j]);
-                const T sn = k == 0 ? ss3[0][j] : (k == 1 ? ss3[1][j] : ss3[2][j]);
-                const bool ok = k == 0 ? ok3[0] : (k == 1 ? ok3[1] : ok3[2]);
+                const int dw = (j * ES) / 4;
+                const uint32_t bitsj = ES == 4 ? 0xffffffffu : 0xffffu << (16 * (j & 1));
+                msk0[dw] |= k == 0 ? bitsj : 0u;
+                msk1[dw] |= k == 1 ? bitsj : 0u;
+                msk2[dw] |= k == 2 ? bitsj : 0u;
+            }
+            cbits cs = {}, ss = {}, copy = {};
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int64_t p = pos[m][k];
+                const cbits mk = k == 0 ? msk0 : (k == 1 ? msk1 : msk2);
+                if (p >= 0 && p < a.M) {
+                    const int64_t e = (p * a.P + slot0[m]) * ES;
+                    cs |= *reinterpret_cast<const cbits*>(a.cos + e) & mk;
+                    ss |= *reinterpret_cast<const cbits*>(a.sin + e) & mk;
+                } else {
+                    copy |= mk;
+                }
+            }
+            const cvec cv = __builtin_bit_cast(cvec, cs);
+            const cvec sv = __builtin_bit_cast(cvec, ss);
+            if (a.scale == 1.0f) {
+#pragma unroll
+                for (int j = 0; j < CE; ++j) { cf[m][j] = cv[j]; sf[m][j] = sv[j]; }
+            } else {
                 // scaled coefficient: binary32 product rounded to T
-                cf[m][j] = unit ? c : from_f<T>(keep_f32(to_f(c) * a.scale));
-                sf[m][j] = unit ? sn : from_f<T>(keep_f32(to_f(sn) * a.scale));
-                if (!ok) {
-                    if (IL) { mask_elem<T>(keep[m], 2 * j); mask_elem<T>(keep[m], 2 * j + 1); }
-                    else mask_elem<T>(keep[m], j);
+#pragma unroll
+                for (int j = 0; j < CE; ++j) {
+                    cf[m][j] = from_f<T>(keep_f32(to_f(cv[j]) * a.scale));
+                    sf[m][j] = from_f<T>(keep_f32(to_f(sv[j]) * a.scale));
+                }
+            }
+            // copy mask over the X chunk: split halves share the slice layout;
+            // interleaved slot j covers chunk elements 2j and 2j+1
+            if (!IL) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) keep[m][d] = copy[d % CW];
+            } else {
+#pragma unroll
+                for (int j = 0; j < CE; ++j) {
+                    const uint32_t cj = ES == 4 ? copy[j] : (copy[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+                    if (cj) { mask_elem<T>(keep[m], 2 * j); mask_elem<T>(keep[m], 2 * j + 1); }
                 }
             }
         } else {
@@ -535,6 +579,7 @@ int launch_plan(const Plan& pl, void* stream) {
         if (g.vector) {
             a.t[t].hpw = g.heads_per_wave[t];
             a.t[t].chunks = g.chunks[t] > 0 ? g.chunks[t] : 1;
+            a.t[t].tile = g.tile > 0 ? g.tile : 1;
             wave_begin += g.waves[t];
         }
     }
@@ -554,6 +599,7 @@ int launch_plan(const Plan& pl, void* stream) {
     a.R = (int32_t)p.R;
     a.D = (int32_t)p.D;
     a.interleaved = p.interleaved;
+    a.xcd_remap = g.xcd_remap;
     a.scaling = p.scaling;
     a.scale = p.scale;
     for (int i = 0; i < kSelWords; ++i) a.sel[i] = p.sel[i];

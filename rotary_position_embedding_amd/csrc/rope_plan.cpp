@@ -183,14 +183,20 @@ static void choose_geometry(Plan* pl) {
 
     int best = 0;
     double best_util = 0.0;
+    const int over_ipl = env_int("ROPE_ITEMS_PER_LANE");
     for (int ipl = 1; ipl <= 4; ++ipl) {
         int64_t tg = 64 * ipl / W;
         if (tg < 1) continue;
+        if (over_ipl > 0 && ipl != over_ipl) continue;
         double util = (double)(tg * W) / (64.0 * ipl);
         if (util > best_util + 1e-9) {
             best_util = util;
             best = ipl;
         }
+    }
+    if (best == 0) {  // the override fits no row: ignore it
+        for (int ipl = 1; ipl <= 4 && best == 0; ++ipl)
+            if (64 * ipl / W >= 1) best = ipl;
     }
     g.items_per_lane = best;
     g.W = (int32_t)W;
@@ -218,13 +224,20 @@ static void choose_geometry(Plan* pl) {
     int64_t hpw_cap = hb;
     while (hpw_cap > 2 && groups * ((total_heads + hpw_cap - 1) / hpw_cap) < 1024) hpw_cap /= 2;
     if (over > 0) hpw_cap = over;
+    // Wave order: rank 4 keeps a head's tokens contiguous, so a tile of 4
+    // token groups per head chunk gives each workgroup longer runs per head.
+    const char* remap = getenv("ROPE_XCD_REMAP");
+    g.xcd_remap = remap ? atoi(remap) : 0;
+    const int over_tile = env_int("ROPE_WAVE_TILE");
+    g.tile = over_tile > 0 ? over_tile : (g.rank == 4 ? 4 : 1);
+    const int64_t tiles = (groups + g.tile - 1) / g.tile;
     for (int t = 0; t < p.ntask; ++t) {
         const int64_t H = p.task[t].heads;
         int64_t chunks = H > 0 ? (H + hpw_cap - 1) / hpw_cap : 1;
         int64_t hpw = H > 0 ? (H + chunks - 1) / chunks : 1;
         g.heads_per_wave[t] = (int32_t)hpw;
         g.chunks[t] = (int32_t)chunks;
-        g.waves[t] = H > 0 ? groups * chunks : 0;
+        g.waves[t] = H > 0 ? tiles * g.tile * chunks : 0;
     }
 }
 
@@ -379,6 +392,7 @@ int plan_rope(const rope_tensor* x, const rope_tensor* cos_cache, const rope_ten
     p.scale = 1.0f;
     p.scaling = 1.0f;
     out->empty = numel(x) == 0;
+    out->g.rank = x->rank;
     choose_geometry(out);
     return ROPE_OK;
 }
@@ -482,6 +496,7 @@ int plan_mrope(const rope_tensor* x, const rope_tensor* position_ids, const rope
     for (int64_t i = 0; i < half; ++i)
         p.sel[i / 16] |= (uint32_t)streams[i] << (2 * (i % 16));
     out->empty = numel(x) == 0;
+    out->g.rank = x->rank;
     choose_geometry(out);
     return ROPE_OK;
 }
@@ -586,6 +601,7 @@ int plan_rope_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor* 
         p.sin = sin_cache->data;
     }
     out->empty = numel(q) == 0 && numel(k) == 0;
+    out->g.rank = q->rank;
     choose_geometry(out);
     return ROPE_OK;
 }

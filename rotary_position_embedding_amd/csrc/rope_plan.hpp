@@ -49,11 +49,14 @@ struct Problem {
 // Launch geometry of the vector kernel (see rope_kernels.hip for the mapping).
 struct Geometry {
     bool vector;          // false: scalar kernel
+    int32_t rank;         // of the activations
     int32_t items_per_lane;
     int32_t head_batch;   // heads whose loads are issued together (kernel template)
     int32_t W;            // 16-byte work items per head row
     int32_t NP;           // of which rotation items
     int32_t TG;           // tokens per wave
+    int32_t tile;         // token groups per head chunk in a tile of waves
+    int32_t xcd_remap;    // 1: consecutive workgroups on one XCD
     int32_t heads_per_wave[2];
     int32_t chunks[2];    // head chunks per token group
     int64_t waves[2];
