@@ -15,6 +15,8 @@
  *                      apply_rotary_pos_emb, GQA) and the
  *                      "com.microsoft.SparseAttention" README (Attributes:
  *                      kv_num_heads, rotary on Q and on K).
+ *   rope_apply_qkv_packed  the same on a packed [Q|K|V] activation --
+ *                      "com.microsoft.SparseAttention" README (Inputs).
  *   rope_inv_freq,     the frequency vector and the cos/sin table the
  *   rope_cos_sin_cache gathered ops read -- PR #27590 review item 4
  *                      (cos_cache = cos(pos * inv_freq) * scaling).
@@ -169,6 +171,30 @@ int rope_apply_qk(const rope_tensor* q, const rope_tensor* k,
                   float attention_scaling, void* stream);
 
 /*
+ * rope_apply_qkv_packed -- the Q and K parts of a packed [Q|K|V] activation
+ * ("com.microsoft.SparseAttention" README, Inputs: a packed query holds the
+ * query, key and value heads of each token when key and value are omitted)
+ * rotated with shared coefficients, in one launch.
+ *
+ * qkv:          rank 3 (B, S, (H + 2*Hk)*D): per token H query heads, then
+ *               Hk key heads, then Hk value heads; or rank 4
+ *               (B, H + 2*Hk, S, D) with the head groups in that order.
+ * y:            same shape and type. Query and key heads rotated exactly as
+ *               rope_apply_qk would; value heads copied bit for bit. y may be
+ *               qkv itself (in place); then the value heads are not touched.
+ * num_heads, kv_num_heads: required (>= 1); kv_num_heads divides num_heads.
+ * Tables, position_ids, inv_freq (on the fly when both tables are NULL),
+ * interleaved, rotary_embedding_dim, attention_scaling: as rope_apply_qk.
+ */
+int rope_apply_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
+                          const rope_tensor* sin_cache,
+                          const rope_tensor* position_ids, const rope_tensor* y,
+                          int64_t interleaved, int64_t num_heads,
+                          int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                          const rope_tensor* inv_freq, float attention_scaling,
+                          void* stream);
+
+/*
  * rope_inv_freq -- inv_freq[i] = rnd_f32(base^(-2i/R)) for i < R/2 with
  * R = 2 * dim 0 of inv_freq (float32, rank 1). The pages take inv_freq from
  * the model; this is the standard schedule. base must be > 0.
@@ -215,6 +241,16 @@ int rope_apply_qk_check(const rope_tensor* q, const rope_tensor* k,
                         int64_t rotary_embedding_dim,
                         const rope_tensor* inv_freq, float attention_scaling,
                         const char** variant);
+
+int rope_apply_qkv_packed_check(const rope_tensor* qkv,
+                                const rope_tensor* cos_cache,
+                                const rope_tensor* sin_cache,
+                                const rope_tensor* position_ids,
+                                const rope_tensor* y, int64_t interleaved,
+                                int64_t num_heads, int64_t kv_num_heads,
+                                int64_t rotary_embedding_dim,
+                                const rope_tensor* inv_freq,
+                                float attention_scaling, const char** variant);
 
 /*
  * Kernel choice for all ops: 0 = automatic (vector kernels where shapes and

@@ -8,6 +8,7 @@ in the library's HIP kernels; nothing falls back to torch or the CPU.
     rope_apply      ONNX RotaryEmbedding
     mrope_apply     com.microsoft.MRotaryEmbedding
     rope_apply_qk   Q and K rotated with shared coefficients (table or on the fly)
+    rope_apply_qkv_packed  the same on a packed [Q|K|V] activation
     rope_inv_freq   frequency vector base^(-2i/R)
     rope_cos_sin_cache  cos/sin tables from inv_freq
 """
@@ -21,7 +22,8 @@ from ._lib import ROPE_FLOAT, ROPE_FLOAT16, ROPE_INT64
 __all__ = ["RopeError", "rope_apply", "mrope_apply", "rope_apply_qk", "rope_inv_freq",
            "rope_cos_sin_cache", "rope_apply_check", "mrope_apply_check",
            "rope_apply_qk_check", "set_kernel_policy", "library_path", "Launcher",
-           "rope_apply_launcher", "mrope_apply_launcher", "rope_apply_qk_launcher"]
+           "rope_apply_launcher", "mrope_apply_launcher", "rope_apply_qk_launcher",
+           "rope_apply_qkv_packed", "rope_apply_qkv_packed_check", "rope_apply_qkv_packed_launcher"]
 
 _DTYPE = {torch.float32: ROPE_FLOAT, torch.float16: ROPE_FLOAT16, torch.int64: ROPE_INT64,
           torch.bfloat16: 16}
@@ -127,6 +129,49 @@ def rope_apply_qk(q, k, cos_cache=None, sin_cache=None, position_ids=None, *, in
                                          kv_num_heads, rotary_embedding_dim, _lib.ref(ds[7]),
                                          attention_scaling, _stream(dev)))
     return yq, yk
+
+
+def rope_apply_qkv_packed(qkv, cos_cache=None, sin_cache=None, position_ids=None, *,
+                          interleaved=0, num_heads=0, kv_num_heads=0, rotary_embedding_dim=0,
+                          inv_freq=None, attention_scaling=1.0, out=None):
+    """Packed [Q|K|V] (rank 3 (B, S, (H+2Hk)*D) or rank 4 (B, H+2Hk, S, D)):
+    query and key heads rotated, value heads copied; out may be qkv (in place)."""
+    dev = _device_of(qkv)
+    y = torch.empty_like(qkv) if out is None else out
+    ds = [_desc(t, dev) for t in (qkv, cos_cache, sin_cache, position_ids, y, inv_freq)]
+    with _on_device(dev):
+        _check(_lib.load().rope_apply_qkv_packed(*[_lib.ref(d) for d in ds[:5]], interleaved,
+                                                 num_heads, kv_num_heads, rotary_embedding_dim,
+                                                 _lib.ref(ds[5]), attention_scaling, _stream(dev)))
+    return y
+
+
+def rope_apply_qkv_packed_check(qkv, cos_cache, sin_cache, position_ids, y, *, interleaved=0,
+                                num_heads=0, kv_num_heads=0, rotary_embedding_dim=0,
+                                inv_freq=None, attention_scaling=1.0):
+    v = _variant_out()
+    rc = _lib.load().rope_apply_qkv_packed_check(_lib.ref(qkv), _lib.ref(cos_cache),
+                                                 _lib.ref(sin_cache), _lib.ref(position_ids),
+                                                 _lib.ref(y), interleaved, num_heads, kv_num_heads,
+                                                 rotary_embedding_dim, _lib.ref(inv_freq),
+                                                 attention_scaling, ctypes.byref(v))
+    return rc, (v.value.decode() if rc == 0 and v.value else None)
+
+
+def rope_apply_qkv_packed_launcher(qkv, cos_cache, sin_cache, position_ids, out, *, interleaved=0,
+                                   num_heads=0, kv_num_heads=0, rotary_embedding_dim=0,
+                                   inv_freq=None, attention_scaling=1.0):
+    dev = _device_of(qkv)
+    ds = [_desc(t, dev) for t in (qkv, cos_cache, sin_cache, position_ids, out, inv_freq)]
+    rc, _ = rope_apply_qkv_packed_check(*ds[:5], interleaved=interleaved, num_heads=num_heads,
+                                        kv_num_heads=kv_num_heads,
+                                        rotary_embedding_dim=rotary_embedding_dim,
+                                        inv_freq=ds[5], attention_scaling=attention_scaling)
+    _check(rc)
+    args = [_lib.ref(d) for d in ds[:5]] + [interleaved, num_heads, kv_num_heads, rotary_embedding_dim,
+                                            _lib.ref(ds[5]), attention_scaling, _stream(dev)]
+    return Launcher(_lib.load().rope_apply_qkv_packed, args,
+                    (ds, qkv, cos_cache, sin_cache, position_ids, out, inv_freq))
 
 
 def rope_inv_freq(rotary_dim, base, device="cuda", out=None):

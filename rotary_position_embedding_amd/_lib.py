@@ -43,6 +43,8 @@ SIGNATURES = {
     "mrope_apply_check": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _i64, _i64, _f32, _ccp], _int),
     "rope_apply_qk_check": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _ccp], _int),
     "rope_set_kernel_policy": ([_int], _int),
+    "rope_apply_qkv_packed": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _vp], _int),
+    "rope_apply_qkv_packed_check": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _ccp], _int),
 }
 
 _lib = None

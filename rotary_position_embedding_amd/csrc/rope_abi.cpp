@@ -102,6 +102,33 @@ int rope_apply_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor*
     return rope::launch_plan(pl, stream);
 }
 
+int rope_apply_qkv_packed_check(const rope_tensor* qkv, const rope_tensor* cos_cache,
+                                const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                                const rope_tensor* y, int64_t interleaved, int64_t num_heads,
+                                int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                                const rope_tensor* inv_freq, float attention_scaling,
+                                const char** variant) {
+    Plan pl;
+    int rc = rope::plan_rope_qkv_packed(qkv, cos_cache, sin_cache, position_ids, y, interleaved,
+                                        num_heads, kv_num_heads, rotary_embedding_dim, inv_freq,
+                                        attention_scaling, &pl);
+    if (rc == ROPE_OK && variant) *variant = pl.g.variant;
+    return rc;
+}
+
+int rope_apply_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
+                          const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                          const rope_tensor* y, int64_t interleaved, int64_t num_heads,
+                          int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                          const rope_tensor* inv_freq, float attention_scaling, void* stream) {
+    Plan pl;
+    int rc = rope::plan_rope_qkv_packed(qkv, cos_cache, sin_cache, position_ids, y, interleaved,
+                                        num_heads, kv_num_heads, rotary_embedding_dim, inv_freq,
+                                        attention_scaling, &pl);
+    if (rc != ROPE_OK) return rc;
+    return rope::launch_plan(pl, stream);
+}
+
 int rope_inv_freq(const rope_tensor* inv_freq, double base, void* stream) {
     float* out;
     int64_t half;

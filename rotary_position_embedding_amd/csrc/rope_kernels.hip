@@ -37,16 +37,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
 
+constexpr int kMaxTasks = 3;
+
 struct KTask {
     const char* x;
     char* y;
-    int64_t sb, sh, ss;  // element strides of (b, h, s)
-    int64_t wave_begin;  // first wave of this task in the launch
+    int64_t sb, sh, ss;    // element strides of (b, h, s)
+    int64_t wave_begin;    // first wave of this task (vector kernel)
+    int64_t item_begin;    // first thread item of this task (scalar kernel)
     int32_t heads, hpw, chunks, tile;  // tile: token groups per head chunk in a wave tile
+    int32_t copy, pad;     // copy: pass every element through (no rotation)
 };
 
 struct KArgs {
-    KTask t[2];
+    KTask t[kMaxTasks];
     int64_t ntok, S, M;
     const char* cos;
     const char* sin;
@@ -165,23 +169,51 @@ __device__ inline void coef_slot(const KArgs& a, int64_t n, int i, float& c, flo
 struct TaskView {
     const char* x;
     char* y;
-    int64_t sb, sh, ss, wave_begin;
-    int32_t heads, hpw, chunks, tile;
+    int64_t sb, sh, ss, wave_begin, item_begin;
+    int32_t heads, hpw, chunks, tile, copy;
 };
 
-__device__ inline TaskView task_of(const KArgs& a, bool second) {
-    TaskView v;
-    v.x = second ? a.t[1].x : a.t[0].x;
-    v.y = second ? a.t[1].y : a.t[0].y;
-    v.sb = second ? a.t[1].sb : a.t[0].sb;
-    v.sh = second ? a.t[1].sh : a.t[0].sh;
-    v.ss = second ? a.t[1].ss : a.t[0].ss;
-    v.wave_begin = second ? a.t[1].wave_begin : a.t[0].wave_begin;
-    v.heads = second ? a.t[1].heads : a.t[0].heads;
-    v.hpw = second ? a.t[1].hpw : a.t[0].hpw;
-    v.chunks = second ? a.t[1].chunks : a.t[0].chunks;
-    v.tile = second ? a.t[1].tile : a.t[0].tile;
+// An SGPR value the compiler must treat as opaque: keeps a select of two
+// kernel-argument loads from being folded into one load from a selected
+// address (that costs the wave a second, dependent round of scalar loads).
+template <typename V>
+__device__ inline V opaque_s(V v) {
+    asm volatile("" : "+s"(v));
     return v;
+}
+
+// Task i (0..2) of the launch: every task's fields are read in the first
+// batch of scalar loads and the values are selected.
+__device__ inline TaskView task_of(const KArgs& a, int i) {
+#define ROPE_PICK(f)                                                                      \
+    do {                                                                                  \
+        const auto f0 = opaque_s(a.t[0].f), f1 = opaque_s(a.t[1].f), f2 = opaque_s(a.t[2].f); \
+        v.f = i == 2 ? f2 : (i == 1 ? f1 : f0);                                           \
+    } while (0)
+    TaskView v;
+    ROPE_PICK(x);
+    ROPE_PICK(y);
+    ROPE_PICK(sb);
+    ROPE_PICK(sh);
+    ROPE_PICK(ss);
+    ROPE_PICK(wave_begin);
+    ROPE_PICK(item_begin);
+    ROPE_PICK(heads);
+    ROPE_PICK(hpw);
+    ROPE_PICK(chunks);
+    ROPE_PICK(tile);
+    ROPE_PICK(copy);
+#undef ROPE_PICK
+    return v;
+}
+
+// Tasks occupy consecutive ranges; unused ones start at INT64_MAX.
+__device__ inline int task_index(const KArgs& a, int64_t wave) {
+    return wave >= a.t[2].wave_begin ? 2 : (wave >= a.t[1].wave_begin ? 1 : 0);
+}
+
+__device__ inline int task_index_items(const KArgs& a, int64_t item) {
+    return item >= a.t[2].item_begin ? 2 : (item >= a.t[1].item_begin ? 1 : 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -195,10 +227,14 @@ __device__ inline TaskView task_of(const KArgs& a, bool second) {
 //   item w < NP rotates: split halves -> elements [w*E, w*E+E) with partners
 //   R/2 later; interleaved -> elements [w*E, w*E+E) = E/2 pairs.
 //   item w >= NP copies elements [R + (w-NP)*E, +E).
-// Memory order per wave: position ids first, then the X chunks of the first
-// head batch, then the table gather that depends on the ids; vector loads
-// complete in issue order, so the gather's latency hides under the X loads.
-// X and Y are touched once: nontemporal loads and stores.
+// Memory order per wave: the position ids, the X chunks of the head batch
+// (predicated per item and head), then the table gather, then per head the
+// rotation and its stores. The compiler places a full wait before each head's
+// stores, so a lane has at most two 16-byte stores in flight; measured on
+// MI355X this metering is faster than letting a wave's stores pile up (a
+// batch of 16 unmetered stores per lane doubled the kernel time), and so are
+// the predicated loads (versus clamped unconditional ones). X and Y are
+// touched once: nontemporal loads and stores.
 
 // Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i % 8),
 // each XCD with its own L2. With remapping, consecutive logical workgroups
@@ -212,6 +248,7 @@ __device__ inline uint32_t logical_block(int remap) {
     return x * q + min(x, r) + p / 8;
 }
 
+// X chunks of one head batch (one or two 16-byte chunks per item and head).
 template <typename T, int IL, int IPL, int HU>
 __device__ inline void load_batch(const char* x, const int64_t* off, const bool* act, const bool* rot,
                                   int h, int h_end, int64_t sh_bytes, int64_t half_bytes,
@@ -238,9 +275,11 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     typedef T cvec __attribute__((ext_vector_type(CE)));
 
     const int lane = threadIdx.x & 63;
-    const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + (threadIdx.x >> 6);
-    const bool second = a.ntask > 1 && gw >= a.t[1].wave_begin;
-    const TaskView tk = task_of(a, second);
+    // wave-uniform by construction; readfirstlane lets the compiler keep the
+    // task selection and its fields in scalar registers
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + wave_in_block;
+    const TaskView tk = task_of(a, task_index(a, gw));
     const int64_t local = gw - tk.wave_begin;
     const int64_t per_tile = (int64_t)tk.tile * tk.chunks;
     const int64_t tile = local / per_tile;
@@ -272,19 +311,27 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         const int64_t s = tok[m] - b * a.S;
         const int64_t e0 = w < a.NP ? (int64_t)w * E : (int64_t)a.R + (int64_t)(w - a.NP) * E;
         off[m] = act[m] ? (b * tk.sb + s * tk.ss + e0) * ES : 0;
-        slot0[m] = w * CE;
+        slot0[m] = rot[m] ? w * CE : 0;  // non-rotation items read slot 0 (unused)
     }
 
     // -- position ids, then X, then the dependent table reads --------------
     int64_t pos[IPL][COEF == kCoefMrope ? 3 : 1];
+    const bool need = !tk.copy;
+    // ids are read for every item (index 0 for inactive ones): unconditional
     if (COEF == kCoefGather || COEF == kCoefOnTheFly) {
 #pragma unroll
-        for (int m = 0; m < IPL; ++m) pos[m][0] = rot[m] ? a.ids[tok[m]] : 0;
+        for (int m = 0; m < IPL; ++m) pos[m][0] = a.ids[tok[m]];
     } else if (COEF == kCoefMrope) {
 #pragma unroll
         for (int m = 0; m < IPL; ++m)
 #pragma unroll
-            for (int k = 0; k < 3; ++k) pos[m][k] = rot[m] ? a.ids[k * a.ntok + tok[m]] : 0;
+            for (int k = 0; k < 3; ++k) pos[m][k] = a.ids[k * a.ntok + tok[m]];
+    }
+
+    uint32_t codes[IPL];  // M-RoPE: 2-bit stream of each slot of the item
+    if (COEF == kCoefMrope) {
+#pragma unroll
+        for (int m = 0; m < IPL; ++m) codes[m] = a.sel[slot0[m] >> 4] >> (2 * (slot0[m] & 15));
     }
 
     u32x4 in1[HU][IPL], in2[HU][IPL];
@@ -297,19 +344,22 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         keep[m] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < CE; ++j) { cf[m][j] = (T)1.0f; sf[m][j] = (T)0.0f; }
-        if (!rot[m]) continue;
+        if (!need) {  // a pass-through task: every element copied
+            keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+            continue;
+        }
         if (COEF == kCoefGather || COEF == kCoefPerToken) {
+            // the row is read unconditionally: an out-of-range id reads row 0
+            // (with an empty table the host points the table at valid memory)
+            // and the pair is then copied
             const int64_t row = COEF == kCoefGather ? pos[m][0] : tok[m];
             const bool valid = COEF == kCoefPerToken || (row >= 0 && row < a.M);
-            if (valid) {
-                const int64_t e = (row * a.P + slot0[m]) * ES;
-                const cvec cv = *reinterpret_cast<const cvec*>(a.cos + e);
-                const cvec sv = *reinterpret_cast<const cvec*>(a.sin + e);
+            const int64_t e = ((valid ? row : 0) * a.P + slot0[m]) * ES;
+            const cvec cv = *reinterpret_cast<const cvec*>(a.cos + e);
+            const cvec sv = *reinterpret_cast<const cvec*>(a.sin + e);
 #pragma unroll
-                for (int j = 0; j < CE; ++j) { cf[m][j] = cv[j]; sf[m][j] = sv[j]; }
-            } else {
-                keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-            }
+            for (int j = 0; j < CE; ++j) { cf[m][j] = cv[j]; sf[m][j] = sv[j]; }
+            if (!valid) keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
         } else if (COEF == kCoefMrope) {
             // Slots [slot0, slot0 + CE) of the three stream rows; slot i takes
             // its stream's value. Per-stream element masks over the slice are
@@ -318,11 +368,10 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
             // slots to the copy mask instead.
             constexpr int CW = CE * ES / 4;  // dwords in a coefficient slice
             typedef uint32_t cbits __attribute__((ext_vector_type(CW)));
-            const uint32_t codes = a.sel[slot0[m] >> 4] >> (2 * (slot0[m] & 15));
             cbits msk0 = {}, msk1 = {}, msk2 = {};
 #pragma unroll
             for (int j = 0; j < CE; ++j) {
-                const uint32_t k = (codes >> (2 * j)) & 3u;
+                const uint32_t k = (codes[m] >> (2 * j)) & 3u;
                 const int dw = (j * ES) / 4;
                 const uint32_t bitsj = ES == 4 ? 0xffffffffu : 0xffffu << (16 * (j & 1));
                 msk0[dw] |= k == 0 ? bitsj : 0u;
@@ -334,13 +383,14 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
             for (int k = 0; k < 3; ++k) {
                 const int64_t p = pos[m][k];
                 const cbits mk = k == 0 ? msk0 : (k == 1 ? msk1 : msk2);
-                if (p >= 0 && p < a.M) {
-                    const int64_t e = (p * a.P + slot0[m]) * ES;
-                    cs |= *reinterpret_cast<const cbits*>(a.cos + e) & mk;
-                    ss |= *reinterpret_cast<const cbits*>(a.sin + e) & mk;
-                } else {
-                    copy |= mk;
-                }
+                const bool ok = p >= 0 && p < a.M;
+                const int64_t e = ((ok ? p : 0) * a.P + slot0[m]) * ES;  // row 0 if out of range
+                const cbits cl = *reinterpret_cast<const cbits*>(a.cos + e);
+                const cbits sl = *reinterpret_cast<const cbits*>(a.sin + e);
+                const cbits use = ok ? mk : cbits{};
+                cs |= cl & use;
+                ss |= sl & use;
+                copy |= ok ? cbits{} : mk;
             }
             const cvec cv = __builtin_bit_cast(cvec, cs);
             const cvec sv = __builtin_bit_cast(cvec, ss);
@@ -402,7 +452,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         r[2 * j + 1] = fmaf(x2, c, x1 * s);
                     }
                     u32x4 o = chunk_pack<T>(r);
-                    if (COEF == kCoefGather || COEF == kCoefMrope) o = select_bits(keep[m], in1[u][m], o);
+                    if (COEF == kCoefGather || COEF == kCoefMrope || tk.copy)
+                        o = select_bits(keep[m], in1[u][m], o);
                     __builtin_nontemporal_store(o, py);
                 } else {
                     const auto xv1 = chunk_values<T>(in1[u][m]);
@@ -418,7 +469,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     }
                     u32x4 o1 = chunk_pack<T>(r1);
                     u32x4 o2 = chunk_pack<T>(r2);
-                    if (COEF == kCoefGather || COEF == kCoefMrope) {
+                    if (COEF == kCoefGather || COEF == kCoefMrope || tk.copy) {
                         o1 = select_bits(keep[m], in1[u][m], o1);
                         o2 = select_bits(keep[m], in2[u][m], o2);
                     }
@@ -436,15 +487,13 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 // Scalar kernel: one thread per (token, head, k), k < R/2 a pair, k >= R/2 a
 // tail element R + k - R/2. Any head size, rotary dim and alignment.
 template <typename T, int COEF>
-__global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int64_t total0,
-                                                              int64_t total) {
+__global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int64_t total) {
     using B = typename Elem<T>::bits;
     const int64_t K = a.P + (a.D - a.R);
     for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * kBlock) {
-        const bool second = idx >= total0;
-        const TaskView tk = task_of(a, second);
-        const int64_t local = second ? idx - total0 : idx;
+        const TaskView tk = task_of(a, task_index_items(a, idx));
+        const int64_t local = idx - tk.item_begin;
         const int64_t k = local % K;
         const int64_t rest = local / K;
         const int64_t h = rest % tk.heads;
@@ -462,9 +511,9 @@ __global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int6
         const int i = (int)k;
         const int64_t j1 = a.interleaved ? 2 * (int64_t)i : i;
         const int64_t j2 = a.interleaved ? 2 * (int64_t)i + 1 : (int64_t)i + a.P;
-        float c, sn;
-        bool copy;
-        coef_slot<T, COEF>(a, n, i, c, sn, copy);
+        float c = 1.0f, sn = 0.0f;
+        bool copy = tk.copy != 0;
+        if (!copy) coef_slot<T, COEF>(a, n, i, c, sn, copy);
         if (copy) {
             yb[j1] = xb[j1];
             yb[j2] = xb[j2];
@@ -545,12 +594,11 @@ static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, d
 }
 
 template <typename T>
-static hipError_t launch_scalar(const KArgs& a, CoefKind c, int64_t total0, int64_t total,
-                                hipStream_t st) {
+static hipError_t launch_scalar(const KArgs& a, CoefKind c, int64_t total, hipStream_t st) {
     int64_t blocks = (total + kBlock - 1) / kBlock;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
-    void* args[] = {const_cast<KArgs*>(&a), &total0, &total};
+    void* args[] = {const_cast<KArgs*>(&a), &total};
     const void* fn;
     switch (c) {
         case kCoefGather: fn = (const void*)rope_scalar_kernel<T, kCoefGather>; break;
@@ -567,7 +615,15 @@ int launch_plan(const Plan& pl, void* stream) {
     const Geometry& g = pl.g;
     hipStream_t st = (hipStream_t)stream;
     KArgs a = {};
-    int64_t wave_begin = 0;
+    const int64_t K = p.R / 2 + (p.D - p.R);
+    int64_t wave_begin = 0, item_begin = 0;
+    for (int t = 0; t < kMaxTasks; ++t) {
+        a.t[t].wave_begin = INT64_MAX;
+        a.t[t].item_begin = INT64_MAX;
+        a.t[t].chunks = 1;
+        a.t[t].tile = 1;
+        a.t[t].hpw = 1;
+    }
     for (int t = 0; t < p.ntask; ++t) {
         a.t[t].x = (const char*)p.task[t].x;
         a.t[t].y = (char*)p.task[t].y;
@@ -575,20 +631,34 @@ int launch_plan(const Plan& pl, void* stream) {
         a.t[t].sh = p.task[t].stride_h;
         a.t[t].ss = p.task[t].stride_s;
         a.t[t].heads = (int32_t)p.task[t].heads;
-        a.t[t].wave_begin = wave_begin;
+        a.t[t].copy = p.task[t].copy;
+        const int64_t items = p.B * p.S * p.task[t].heads * K;
+        if (items > 0) {  // an empty task keeps INT64_MAX and is never selected
+            a.t[t].item_begin = item_begin;
+            item_begin += items;
+        }
         if (g.vector) {
             a.t[t].hpw = g.heads_per_wave[t];
             a.t[t].chunks = g.chunks[t] > 0 ? g.chunks[t] : 1;
             a.t[t].tile = g.tile > 0 ? g.tile : 1;
-            wave_begin += g.waves[t];
+            if (g.waves[t] > 0) {
+                a.t[t].wave_begin = wave_begin;
+                wave_begin += g.waves[t];
+            }
         }
     }
-    if (p.ntask == 2 && g.vector && g.waves[1] == 0) a.t[1].wave_begin = INT64_MAX;
     a.ntok = p.B * p.S;
     a.S = p.S;
     a.M = p.M;
     a.cos = (const char*)p.cos;
     a.sin = (const char*)p.sin;
+    if (g.vector && p.M == 0 && (p.coef == kCoefGather || p.coef == kCoefMrope)) {
+        // empty table: every id is out of range and every pair is copied, but
+        // the vector kernel reads a row unconditionally; point it at the
+        // first non-empty input (16-byte aligned, at least one row long)
+        for (int t = p.ntask - 1; t >= 0; --t)
+            if (p.task[t].heads > 0) a.cos = a.sin = (const char*)p.task[t].x;
+    }
     a.ids = p.ids;
     a.inv_freq = p.inv_freq;
     a.ntask = p.ntask;
@@ -618,12 +688,9 @@ int launch_plan(const Plan& pl, void* stream) {
             e = p.interleaved ? launch_vec_coef<float, 1>(a, p.coef, ipl, hu, grid, st)
                               : launch_vec_coef<float, 0>(a, p.coef, ipl, hu, grid, st);
     } else {
-        const int64_t K = p.R / 2 + (p.D - p.R);
-        const int64_t total0 = p.B * p.S * p.task[0].heads * K;
-        const int64_t total1 = p.ntask > 1 ? p.B * p.S * p.task[1].heads * K : 0;
-        if (total0 + total1 == 0) return ROPE_OK;
-        e = p.dtype == ROPE_FLOAT16 ? launch_scalar<half_t>(a, p.coef, total0, total0 + total1, st)
-                                    : launch_scalar<float>(a, p.coef, total0, total0 + total1, st);
+        if (item_begin == 0) return ROPE_OK;
+        e = p.dtype == ROPE_FLOAT16 ? launch_scalar<half_t>(a, p.coef, item_begin, st)
+                                    : launch_scalar<float>(a, p.coef, item_begin, st);
     }
     return launched(e);
 }

@@ -223,7 +223,7 @@ static void choose_geometry(Plan* pl) {
     for (int t = 0; t < p.ntask; ++t) total_heads += p.task[t].heads;
     int64_t hpw_cap = hb;
     while (hpw_cap > 2 && groups * ((total_heads + hpw_cap - 1) / hpw_cap) < 1024) hpw_cap /= 2;
-    if (over > 0) hpw_cap = over;
+    if (over > 0 && over < hpw_cap) hpw_cap = over;  // a wave holds at most one batch
     // Wave order: rank 4 keeps a head's tokens contiguous, so a tile of 4
     // token groups per head chunk gives each workgroup longer runs per head.
     const char* remap = getenv("ROPE_XCD_REMAP");
@@ -602,6 +602,122 @@ int plan_rope_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor* 
     }
     out->empty = numel(q) == 0 && numel(k) == 0;
     out->g.rank = q->rank;
+    choose_geometry(out);
+    return ROPE_OK;
+}
+
+// Packed [Q|K|V]: the SparseAttention README's packed query input holds,
+// per token, num_heads query heads, then kv_num_heads key heads, then
+// kv_num_heads value heads. Q and K are rotated; V is copied to y unless y is
+// the input itself (in place), where it is left alone.
+int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
+                         const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                         const rope_tensor* y, int64_t interleaved, int64_t num_heads,
+                         int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                         const rope_tensor* inv_freq, float attention_scaling, Plan* out) {
+    clear_error();
+    memset(out, 0, sizeof(*out));
+    if (!qkv) return fail(ROPE_ERR_NULL, "qkv is missing");
+    if (!y) return fail(ROPE_ERR_NULL, "y is missing");
+    if ((cos_cache == nullptr) != (sin_cache == nullptr))
+        return fail(ROPE_ERR_NULL, "cos_cache and sin_cache must both be given or both be NULL");
+    const bool onthefly = cos_cache == nullptr;
+    if (onthefly && !inv_freq)
+        return fail(ROPE_ERR_NULL, "inv_freq is required when cos/sin tables are absent");
+    if (onthefly && !position_ids)
+        return fail(ROPE_ERR_NULL, "position_ids are required when cos/sin tables are absent");
+    TRY(check_desc(qkv, "qkv"));
+    TRY(check_desc(y, "y"));
+    if (cos_cache) TRY(check_desc(cos_cache, "cos_cache"));
+    if (sin_cache) TRY(check_desc(sin_cache, "sin_cache"));
+    if (position_ids) TRY(check_desc(position_ids, "position_ids"));
+    if (onthefly) TRY(check_desc(inv_freq, "inv_freq"));
+    if (!is_float(qkv->dtype)) return fail(ROPE_ERR_DTYPE, "qkv must be float32 or float16");
+    if (y->dtype != qkv->dtype) return fail(ROPE_ERR_DTYPE, "y must have the type of qkv");
+    if (cos_cache && (cos_cache->dtype != qkv->dtype || sin_cache->dtype != qkv->dtype))
+        return fail(ROPE_ERR_DTYPE, "cos_cache and sin_cache must have the type of qkv");
+    if (position_ids && position_ids->dtype != ROPE_INT64)
+        return fail(ROPE_ERR_DTYPE, "position_ids must be int64");
+    if (onthefly && inv_freq->dtype != ROPE_FLOAT)
+        return fail(ROPE_ERR_DTYPE, "inv_freq must be float32");
+    if (interleaved != 0 && interleaved != 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "interleaved must be 0 or 1");
+    if (num_heads < 1 || kv_num_heads < 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "num_heads and kv_num_heads are required (>= 1) for packed QKV");
+    if (num_heads % kv_num_heads != 0)
+        return fail(ROPE_ERR_SHAPE, "kv_num_heads %lld must divide num_heads %lld",
+                    (long long)kv_num_heads, (long long)num_heads);
+    if (qkv->rank != 3 && qkv->rank != 4)
+        return fail(ROPE_ERR_RANK, "qkv must be rank 3 or 4, got %d", (int)qkv->rank);
+    if (!same_shape(qkv, y)) return fail(ROPE_ERR_SHAPE, "y must have the shape of qkv");
+    const int64_t Hall = num_heads + 2 * kv_num_heads;
+    int64_t B, S, D, R, M = 0;
+    if (qkv->rank == 3) {
+        if (qkv->shape[2] % Hall != 0)
+            return fail(ROPE_ERR_SHAPE, "packed width %lld is not (num_heads + 2*kv_num_heads) * head_size",
+                        (long long)qkv->shape[2]);
+        B = qkv->shape[0];
+        S = qkv->shape[1];
+        D = qkv->shape[2] / Hall;
+    } else {
+        if (qkv->shape[1] != Hall)
+            return fail(ROPE_ERR_SHAPE, "packed dim 1 = %lld != num_heads + 2*kv_num_heads = %lld",
+                        (long long)qkv->shape[1], (long long)Hall);
+        B = qkv->shape[0];
+        S = qkv->shape[2];
+        D = qkv->shape[3];
+    }
+    if (D % 2 != 0) return fail(ROPE_ERR_SHAPE, "head_size %lld must be even", (long long)D);
+    TRY(check_rotary_dim(D, rotary_embedding_dim, &R));
+    if (!onthefly) {
+        TRY(check_tables(cos_cache, sin_cache, position_ids, B, S, R, &M));
+    } else {
+        if (inv_freq->rank != 1 || inv_freq->shape[0] * 2 != R)
+            return fail(ROPE_ERR_SHAPE, "inv_freq must be (rotary_dim/2,) = (%lld,)", (long long)(R / 2));
+        if (position_ids->rank != 2)
+            return fail(ROPE_ERR_RANK, "position_ids must be rank 2 (batch, sequence)");
+        if (position_ids->shape[0] != B || position_ids->shape[1] != S)
+            return fail(ROPE_ERR_SHAPE, "position_ids must be (%lld, %lld)", (long long)B, (long long)S);
+    }
+    const rope_tensor* others[4] = {cos_cache, sin_cache, position_ids, onthefly ? inv_freq : nullptr};
+    const char* names[4] = {"cos_cache", "sin_cache", "position_ids", "inv_freq"};
+    TRY(check_output(y, "y", qkv, others, names, 4));
+
+    Problem& p = out->p;
+    p.dtype = qkv->dtype;
+    p.interleaved = (int32_t)interleaved;
+    p.B = B; p.S = S; p.D = D; p.R = R;
+    const int es = elem_size(qkv->dtype);
+    // the three head groups share the packed strides; they start H*D (rank 3)
+    // or H*S*D (rank 4) elements apart
+    Task base = {};
+    fill_strides(&base, qkv->rank, S, Hall, D);
+    const int64_t group_step = qkv->rank == 3 ? D : S * D;  // elements per head step
+    const int64_t first[3] = {0, num_heads, num_heads + kv_num_heads};
+    const int64_t heads[3] = {num_heads, kv_num_heads, kv_num_heads};
+    const bool inplace = y->data == qkv->data;
+    p.ntask = inplace ? 2 : 3;
+    for (int t = 0; t < p.ntask; ++t) {
+        p.task[t] = base;
+        p.task[t].heads = heads[t];
+        p.task[t].x = (const char*)qkv->data + first[t] * group_step * es;
+        p.task[t].y = (char*)y->data + first[t] * group_step * es;
+        p.task[t].copy = t == 2;
+    }
+    p.ids = position_ids ? (const int64_t*)position_ids->data : nullptr;
+    p.M = M;
+    p.scale = 1.0f;
+    p.scaling = attention_scaling;
+    if (onthefly) {
+        p.coef = kCoefOnTheFly;
+        p.inv_freq = (const float*)inv_freq->data;
+    } else {
+        p.coef = position_ids ? kCoefGather : kCoefPerToken;
+        p.cos = cos_cache->data;
+        p.sin = sin_cache->data;
+    }
+    out->empty = numel(qkv) == 0;
+    out->g.rank = qkv->rank;
     choose_geometry(out);
     return ROPE_OK;
 }

@@ -21,19 +21,23 @@ enum CoefKind : int32_t {
 constexpr int kMaxMropeHalf = 512;             // slots the stream table can hold
 constexpr int kSelWords = kMaxMropeHalf / 16;  // 2 bits per slot
 
-// One input/output pair rotated with the shared coefficients.
+// One input/output pair rotated with the shared coefficients (or, with
+// copy set, passed through unchanged).
 struct Task {
     const void* x;
     void* y;
     int64_t heads;
     int64_t stride_b, stride_h, stride_s;  // element strides of x(b, h, s, 0)
+    int32_t copy;
 };
+
+constexpr int kMaxPlanTasks = 3;
 
 struct Problem {
     int32_t dtype;        // ROPE_FLOAT or ROPE_FLOAT16
     int32_t interleaved;  // 0 or 1
     int64_t B, S, D, R;   // batch, sequence, head size, rotary dim
-    Task task[2];
+    Task task[kMaxPlanTasks];
     int32_t ntask;
     CoefKind coef;
     const void* cos;
@@ -57,9 +61,9 @@ struct Geometry {
     int32_t TG;           // tokens per wave
     int32_t tile;         // token groups per head chunk in a tile of waves
     int32_t xcd_remap;    // 1: consecutive workgroups on one XCD
-    int32_t heads_per_wave[2];
-    int32_t chunks[2];    // head chunks per token group
-    int64_t waves[2];
+    int32_t heads_per_wave[kMaxPlanTasks];
+    int32_t chunks[kMaxPlanTasks];  // head chunks per token group
+    int64_t waves[kMaxPlanTasks];
     const char* variant;
 };
 
@@ -88,6 +92,12 @@ int plan_rope_qk(const rope_tensor* q, const rope_tensor* k,
                  int64_t kv_num_heads, int64_t rotary_embedding_dim,
                  const rope_tensor* inv_freq, float attention_scaling,
                  Plan* out);
+
+int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
+                         const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                         const rope_tensor* y, int64_t interleaved, int64_t num_heads,
+                         int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                         const rope_tensor* inv_freq, float attention_scaling, Plan* out);
 
 struct TablePlan {
     const float* inv_freq;

@@ -398,3 +398,66 @@ def test_inv_freq_and_table_validation():
     assert f(ctypes.byref(inv), 1.0, ctypes.byref(cos), ctypes.byref(reshape(sin, (128, 64), F32)), None) == DTYPE
     assert f(ctypes.byref(inv), 1.0, ctypes.byref(cos), ctypes.byref(cos), None) == ALIAS
     assert f(ctypes.byref(inv), 1.0, ctypes.byref(reshape(cos, (8192,))), ctypes.byref(reshape(sin, (8192,))), None) == RANK
+
+
+# ---------------------------------------------------------------------------
+# packed [Q|K|V] (SparseAttention README, Inputs)
+
+def packed_case(rank=3, dt=F16, B=2, S=3, H=8, Hk=2, D=16, M=64, table=True, inplace=False, **over):
+    a = Alloc()
+    shape = (B, S, (H + 2 * Hk) * D) if rank == 3 else (B, H + 2 * Hk, S, D)
+    qkv = a(dt, shape)
+    kw = dict(qkv=qkv,
+              cos_cache=a(dt, (M, D // 2)) if table else None,
+              sin_cache=a(dt, (M, D // 2)) if table else None,
+              position_ids=a(I64, (B, S)),
+              y=reshape(qkv, shape) if inplace else a(dt, shape),
+              interleaved=0, num_heads=H, kv_num_heads=Hk, rotary_embedding_dim=0,
+              inv_freq=None if table else a(F32, (D // 2,)), attention_scaling=1.0)
+    kw.update(over)
+    return kw
+
+
+def check_packed(kw):
+    kw = dict(kw)
+    args = [kw.pop(k) for k in ("qkv", "cos_cache", "sin_cache", "position_ids", "y")]
+    return rpe.rope_apply_qkv_packed_check(*args, **kw)
+
+
+def test_packed_accepted():
+    for rank in (3, 4):
+        for table in (True, False):
+            for inplace in (False, True):
+                rc, v = check_packed(packed_case(rank=rank, table=table, inplace=inplace))
+                assert rc == OK, _lib.load().rope_last_error()
+                assert v == ("vec16/gather" if table else "vec16/on_the_fly")
+    rc, v = check_packed(packed_case(D=6))
+    assert rc == OK and v == "scalar/gather"
+
+
+def test_packed_clauses():
+    lib = _lib.load()
+    cases = [
+        ("num_heads missing", ATTR, dict(num_heads=0)),
+        ("kv heads missing", ATTR, dict(kv_num_heads=0)),
+        ("kv does not divide", SHAPE, dict(kv_num_heads=3)),
+        ("interleaved 3", ATTR, dict(interleaved=3)),
+        ("qkv missing", NULL, dict(qkv=None)),
+        ("y missing", NULL, dict(y=None)),
+        ("only sin", NULL, dict(cos_cache=None)),
+    ]
+    for name, code, over in cases:
+        kw = packed_case()
+        kw.update(over)
+        rc, _ = check_packed(kw)
+        assert rc == code, (name, rc, lib.rope_last_error())
+    kw = packed_case(); kw["qkv"] = reshape(kw["qkv"], (2, 3, 190)); kw["y"] = reshape(kw["y"], (2, 3, 190))
+    assert check_packed(kw)[0] == SHAPE            # width not (H + 2Hk) * D
+    kw = packed_case(rank=4); kw["qkv"] = reshape(kw["qkv"], (2, 11, 3, 16)); kw["y"] = reshape(kw["y"], (2, 11, 3, 16))
+    assert check_packed(kw)[0] == SHAPE            # dim 1 != H + 2Hk
+    kw = packed_case(); kw["y"] = reshape(kw["y"], (2, 3, 96))
+    assert check_packed(kw)[0] == SHAPE
+    kw = packed_case(); y = reshape(kw["qkv"], (2, 3, 192)); y.data += 32; kw["y"] = y
+    assert check_packed(kw)[0] == ALIAS            # shifted output
+    kw = packed_case(table=False, position_ids=None)
+    assert check_packed(kw)[0] == NULL

@@ -385,3 +385,76 @@ def test_qk_in_place():
                       out_q=qt, out_k=kt)
     assert_parity(host(qt), want[0], "Q in place")
     assert_parity(host(kt), want[1], "K in place")
+
+
+# ---------------------------------------------------------------------------
+# packed [Q|K|V]
+
+PACKED = [
+    # rank, dt, B, S, H, Hk, D, R, il
+    (3, np.float16, 256, 1, 32, 8, 128, 0, 0),
+    (3, np.float16, 3, 37, 8, 2, 128, 0, 1),
+    (4, np.float16, 2, 29, 4, 2, 64, 0, 0),
+    (3, np.float32, 2, 11, 6, 3, 96, 64, 1),
+    (4, np.float32, 2, 13, 2, 1, 128, 0, 0),
+    (3, np.float16, 2, 7, 4, 2, 10, 0, 0),     # scalar kernel
+]
+
+
+def split_packed(qkv, rank, H, Hk):
+    if rank == 3:
+        B, S, W = qkv.shape
+        D = W // (H + 2 * Hk)
+        return (np.ascontiguousarray(qkv[..., :H * D]), np.ascontiguousarray(qkv[..., H * D:(H + Hk) * D]),
+                np.ascontiguousarray(qkv[..., (H + Hk) * D:]))
+    return (np.ascontiguousarray(qkv[:, :H]), np.ascontiguousarray(qkv[:, H:H + Hk]),
+            np.ascontiguousarray(qkv[:, H + Hk:]))
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("onthefly", [False, True])
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("case", PACKED, ids=[str(i) for i in range(len(PACKED))])
+def test_qkv_packed(case, policy, onthefly, inplace):
+    rank, dt, B, S, H, Hk, D, R, il = case
+    rpe.set_kernel_policy(policy)
+    Rf = R or D
+    M = 40000
+    shape = (B, S, (H + 2 * Hk) * D) if rank == 3 else (B, H + 2 * Hk, S, D)
+    qkv = normal_tensor(9100 + D + S, shape, dt)
+    ids = ids_in(9101, (B, S), M)
+    inv = oracle.inv_freq(1e6, Rf)
+    q, k, v = split_packed(qkv, rank, H, Hk)
+    nh, nk = (H, Hk) if rank == 3 else (0, 0)
+    if onthefly:
+        wq, wk = oracle.rope_apply_qk(q, k, None, None, ids, interleaved=il, num_heads=nh, kv_num_heads=nk,
+                                      rotary_embedding_dim=R, inv_freq=inv)
+        tabs = dict(cos_cache=None, sin_cache=None, inv_freq=cuda(inv))
+    else:
+        cos, sin = oracle.cos_sin_cache(dt, M, inv)
+        wq, wk = oracle.rope_apply_qk(q, k, cos, sin, ids, interleaved=il, num_heads=nh, kv_num_heads=nk,
+                                      rotary_embedding_dim=R)
+        tabs = dict(cos_cache=cuda(cos), sin_cache=cuda(sin))
+    xt = cuda(qkv)
+    y = rpe.rope_apply_qkv_packed(xt, position_ids=cuda(ids), interleaved=il, num_heads=H, kv_num_heads=Hk,
+                                  rotary_embedding_dim=R, out=xt if inplace else None, **tabs)
+    gq, gk, gv = split_packed(host(y), rank, H, Hk)
+    assert_parity(gq, wq, "Q " + str(case))
+    assert_parity(gk, wk, "K " + str(case))
+    assert_bitwise(gv, v, "V")
+
+
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+def test_empty_table_copies_everything(policy):
+    """M = 0 rows: every id is out of range, so Y == X bit for bit (the vector
+    kernel reads a substitute row and discards it)."""
+    rpe.set_kernel_policy(policy)
+    x = normal_tensor(9300, (2, 9, 4 * 128), np.float16)
+    ids = ids_in(9301, (2, 9), 5)
+    cos = torch.empty(0, 64, dtype=torch.float16, device=DEV)
+    y = host(rpe.rope_apply(cuda(x), cos, cos.clone(), cuda(ids), num_heads=4))
+    assert_bitwise(y, x, "empty table")
+    x4 = normal_tensor(9302, (2, 4, 9, 128), np.float16)
+    ids3 = ids_in(9303, (3, 2, 9), 5)
+    y4 = host(rpe.mrope_apply(cuda(x4), cuda(ids3), cos, cos.clone(), mrope_section=(16, 24, 24)))
+    assert_bitwise(y4, x4, "empty table, M-RoPE")
