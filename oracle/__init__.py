@@ -5,7 +5,8 @@ import this package. The product library (rotary_position_embedding_amd)
 never imports it, and this package never imports the product.
 
 Thin numpy wrappers around liboracle_rope.so (rope_oracle.c). float16 arrays
-travel as numpy float16 (bit patterns pass through untouched). The functions
+travel as numpy float16 and bfloat16 arrays as numpy uint16 bit patterns
+(bit patterns pass through untouched). The functions
 and their parity status are documented in rope_oracle.h.
 
 `Oracle(path)` binds the wrappers to one build of the C file; the module-level
@@ -23,7 +24,9 @@ SOURCE_PATH = os.path.join(_HERE, "rope_oracle.c")
 
 F32 = 1
 F16 = 10
-_DTYPE_CODE = {np.dtype(np.float32): F32, np.dtype(np.float16): F16}
+BF16 = 16
+# bfloat16 arrays travel as numpy uint16 bit patterns
+_DTYPE_CODE = {np.dtype(np.float32): F32, np.dtype(np.float16): F16, np.dtype(np.uint16): BF16}
 
 
 def _ptr(a):
@@ -34,7 +37,7 @@ def _code(dtype):
     try:
         return _DTYPE_CODE[np.dtype(dtype)]
     except KeyError:
-        raise TypeError("oracle supports float32 and float16, got %s" % dtype)
+        raise TypeError("oracle supports float32, float16 and bfloat16 (uint16 bits), got %s" % dtype)
 
 
 def _dense(a, dtype=None):
@@ -68,6 +71,8 @@ class Oracle:
         sig = {
             "oracle_f16_to_f64": ([ctypes.c_uint16], ctypes.c_double),
             "oracle_f64_to_f16": ([ctypes.c_double], ctypes.c_uint16),
+            "oracle_bf16_to_f64": ([ctypes.c_uint16], ctypes.c_double),
+            "oracle_f64_to_bf16": ([ctypes.c_double], ctypes.c_uint16),
             "oracle_inv_freq": ([ctypes.c_double, i64, vp], None),
             "oracle_cos_sin_cache": ([i32, i64, i64, vp, f32, vp, vp], None),
             "oracle_rope_apply": ([i32, i32, i64, i64, i64, i64, i64, i64,
@@ -92,6 +97,12 @@ class Oracle:
 
     def f64_to_f16(self, v: float) -> int:
         return self.lib.oracle_f64_to_f16(v)
+
+    def bf16_to_f64(self, bits: int) -> float:
+        return self.lib.oracle_bf16_to_f64(bits)
+
+    def f64_to_bf16(self, v: float) -> int:
+        return self.lib.oracle_f64_to_bf16(v)
 
     # -- coefficient tables --------------------------------------------------
     def inv_freq(self, base: float, rotary_dim: int) -> np.ndarray:
@@ -207,6 +218,14 @@ def f16_to_f64(bits):
 
 def f64_to_f16(v):
     return default().f64_to_f16(v)
+
+
+def bf16_to_f64(bits):
+    return default().bf16_to_f64(bits)
+
+
+def f64_to_bf16(v):
+    return default().f64_to_bf16(v)
 
 
 def inv_freq(base, rotary_dim):

@@ -64,6 +64,52 @@ uint16_t oracle_f64_to_f16(double v)
     return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | frac);
 }
 
+/* bfloat16: the upper 16 bits of a binary32 -- 8 exponent bits (bias 127),
+ * 7 fraction bits. Same rounding rule as above with the binary32 exponent
+ * range: binades from 2^-126, quantum 2^(E-7), below 2^-126 a fixed 2^-133. */
+
+double oracle_bf16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int m = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -133);            /* zero or subnormal: m * 2^-133 */
+    else if (e == 255)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(128 + m), e - 134); /* (1 + m/128) * 2^(e-127) */
+    return sign ? -v : v;
+}
+
+uint16_t oracle_f64_to_bf16(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7fc0);
+    if (a == 0.0)
+        return sign;
+    /* halfway between the largest finite value (2 - 2^-7) * 2^127 and 2^128 */
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127))
+        return (uint16_t)(sign | 0x7f80);
+    int ex;
+    frexp(a, &ex);
+    int E = ex - 1;
+    if (E < -126)
+        E = -126;
+    double quantum = ldexp(1.0, E - 7);
+    double n = nearbyint(a / quantum);
+    double r = n * quantum;
+    if (r < ldexp(1.0, -126))
+        return (uint16_t)(sign | (uint16_t)n); /* subnormal: fraction = r/2^-133 */
+    frexp(r, &ex);
+    E = ex - 1;
+    uint16_t frac = (uint16_t)(ldexp(r, 7 - E) - 128.0);
+    return (uint16_t)(sign | (uint16_t)((E + 127) << 7) | frac);
+}
+
 /* ------------------------------------------------------------------------ */
 /* element access in the storage type */
 
@@ -71,6 +117,8 @@ static double load_elem(int dtype, const void* p, int64_t idx)
 {
     if (dtype == ORACLE_F32)
         return (double)((const float*)p)[idx];
+    if (dtype == ORACLE_BF16)
+        return oracle_bf16_to_f64(((const uint16_t*)p)[idx]);
     return oracle_f16_to_f64(((const uint16_t*)p)[idx]);
 }
 
@@ -78,6 +126,8 @@ static void store_elem(int dtype, void* p, int64_t idx, double v)
 {
     if (dtype == ORACLE_F32)
         ((float*)p)[idx] = (float)v; /* one rounding, nearest-even */
+    else if (dtype == ORACLE_BF16)
+        ((uint16_t*)p)[idx] = oracle_f64_to_bf16(v);
     else
         ((uint16_t*)p)[idx] = oracle_f64_to_f16(v);
 }
@@ -95,6 +145,8 @@ static double round_to_storage(int dtype, double v)
 {
     if (dtype == ORACLE_F32)
         return (double)(float)v;
+    if (dtype == ORACLE_BF16)
+        return oracle_bf16_to_f64(oracle_f64_to_bf16(v));
     return oracle_f16_to_f64(oracle_f64_to_f16(v));
 }
 
@@ -117,8 +169,9 @@ static int64_t row_offset(int rank, int64_t S, int64_t H, int64_t D,
  * Both products are exact in binary64 for binary16/binary32 operands; the
  * sum is rounded to binary64 and then once to the storage type.
  * A pair flagged `copy` and every element at or beyond R are bit copies
- * ([RE] `rotary_embedding_dim`: "the rest are passed through unchanged";
- * [MRE] Description: out-of-range id copies its pair unchanged). */
+ * ([RE] `rotary_embedding_dim`: only the leading R elements rotate, the
+ * others are kept; [MRE] Description: a pair whose id is out of range is
+ * kept as it was). */
 static void rotate_row(int dtype, const void* x, void* y, int64_t off,
                        int64_t D, int64_t R, int64_t interleaved,
                        const double* c, const double* s,

@@ -19,8 +19,9 @@
  *  [SA]  "com.microsoft.SparseAttention" README: Attributes (`do_rotary`,
  *        `rotary_interleaved`, `kv_num_heads`).
  *
- * Storage types use ONNX TensorProto codes: 1 = float32, 10 = float16.
- * float16 tensors are passed as arrays of uint16_t bit patterns.
+ * Storage types use ONNX TensorProto codes: 1 = float32, 10 = float16,
+ * 16 = bfloat16. float16 and bfloat16 tensors are passed as arrays of
+ * uint16_t bit patterns.
  * All pointers are host pointers; all arrays are dense row-major.
  *
  * Parity status of each function is listed in its comment; "parity unpinned"
@@ -37,10 +38,16 @@ extern "C" {
 
 #define ORACLE_F32 1
 #define ORACLE_F16 10
+#define ORACLE_BF16 16
 
 /* IEEE-754 binary16 <-> binary64, round-to-nearest-even, subnormals kept. */
 double   oracle_f16_to_f64(uint16_t h);
 uint16_t oracle_f64_to_f16(double v);
+
+/* bfloat16 (1 sign, 8 exponent bits with bias 127, 7 fraction bits: the
+ * upper half of a binary32) <-> binary64, nearest-even, subnormals kept. */
+double   oracle_bf16_to_f64(uint16_t h);
+uint16_t oracle_f64_to_bf16(double v);
 
 /* Frequency schedule inv_freq[i] = rnd_f32(base^(-2i/R)), i < R/2.
  * The pages never print the formula ([PR] takes inv_freq from the model's

@@ -22,9 +22,32 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 mpmath.mp.prec = 200
 
 
+BF16 = np.uint16   # bfloat16 arrays travel as uint16 bit patterns
+
+
 def bits(a):
     a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return a
     return a.view(np.uint16 if a.dtype == np.float16 else np.uint32)
+
+
+def to_f64(a):
+    """Values of a float32/float16/bfloat16(uint16 bits) array as float64."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def from_f64(v, dt):
+    """Round float64 values to dt (bfloat16 through torch, which rounds to
+    nearest-even from binary32: exact for every value used with it here)."""
+    v = np.asarray(v, np.float64)
+    if dt is BF16:
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(v)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return v.astype(dt)
 
 
 def assert_bitwise(a, b, what):
@@ -36,8 +59,8 @@ def assert_bitwise(a, b, what):
 
 def assert_value_equal(a, b, what):
     """Equal as numbers (+0 == -0), NaN == NaN."""
-    a64 = a.astype(np.float64).reshape(-1)
-    b64 = b.astype(np.float64).reshape(-1)
+    a64 = to_f64(a).reshape(-1)
+    b64 = to_f64(b).reshape(-1)
     ok = (a64 == b64) | (np.isnan(a64) & np.isnan(b64))
     bad = np.flatnonzero(~ok)
     assert bad.size == 0, "%s: %d elements differ, first at %d: %r vs %r" % (
@@ -47,7 +70,15 @@ def assert_value_equal(a, b, what):
 def angle_table(seed, rows, half, dtype):
     """cos/sin of random angles, each rounded to dtype (independent of the oracle)."""
     th = SplitMix64(seed).uniform(rows * half).reshape(rows, half) * (2 * np.pi)
+    if dtype is BF16:
+        return from_f64(np.cos(th).astype(np.float32), BF16), from_f64(np.sin(th).astype(np.float32), BF16)
     return np.cos(th).astype(dtype), np.sin(th).astype(dtype)
+
+
+def normal_any(seed, shape, dt):
+    if dt is BF16:
+        return from_f64(normal_tensor(seed, shape, np.float32), BF16)
+    return normal_tensor(seed, shape, dt)
 
 
 def ids_in(seed, shape, bound):
@@ -104,6 +135,77 @@ def pin_f16_encode_vs_numpy(orc):
     assert np.isnan(np.uint16(orc.f64_to_f16(float("nan"))).view(np.float16))
 
 
+def pin_bf16_decode_exhaustive(orc):
+    import torch
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(allbits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([orc.bf16_to_f64(int(b)) for b in allbits])
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    same &= np.signbit(got) == np.signbit(ref)
+    assert same.all(), "bfloat16 decode differs at %s" % np.flatnonzero(~same)[:5]
+
+
+def _bf16_exact_rne(v):
+    """bfloat16 bits of v by exact rational arithmetic (independent check)."""
+    from fractions import Fraction
+    import math
+    if v == 0:
+        return 0x8000 if math.copysign(1.0, v) < 0 else 0
+    sign = 0x8000 if v < 0 else 0
+    a = Fraction(abs(v))
+    if a >= Fraction(2 ** 128) - Fraction(2 ** 119):
+        return sign | 0x7f80
+    E = max(-126, math.floor(math.log2(abs(v))))
+    while E > -126 and Fraction(2) ** E > a:   # guard the float log2
+        E -= 1
+    while E > -126 and Fraction(2) ** (E + 1) <= a:
+        E += 1
+    q = Fraction(2) ** (E - 7)
+    n, rem = divmod(a, q)
+    n = int(n)
+    if rem > q / 2 or (rem == q / 2 and n % 2 == 1):
+        n += 1
+    r = n * q
+    if r < Fraction(2) ** -126:
+        return sign | n
+    E2 = E + 1 if r >= Fraction(2) ** (E + 1) else E
+    frac = int(r / Fraction(2) ** (E2 - 7)) - 128
+    return sign | ((E2 + 127) << 7) | frac
+
+
+def rne_bf16(v):
+    """bfloat16 bits of each float64 value by the exact rational rule."""
+    v = np.asarray(v, np.float64)
+    return np.vectorize(_bf16_exact_rne, otypes=[np.uint16])(v).reshape(v.shape)
+
+
+def round_to(v, dt):
+    """float64 values rounded once to dt (nearest-even)."""
+    return rne_bf16(v) if dt is BF16 else np.asarray(v, np.float64).astype(dt)
+
+
+def pin_bf16_encode(orc):
+    import torch
+    # every tie point between neighbouring bfloat16 values (exact in binary32)
+    # and its binary32 neighbours, against torch's nearest-even conversion
+    h = np.arange(0, 0x7f80, 61, dtype=np.uint32)
+    lo = ((h << 16).view(np.float32)).astype(np.float64)
+    hi = (((h + 1) << 16).view(np.float32)).astype(np.float64)
+    mid32 = ((lo + hi) / 2).astype(np.float32)
+    vals32 = np.concatenate([mid32, np.nextafter(mid32, np.float32(0)), np.nextafter(mid32, np.float32(1e30)),
+                             -mid32, np.float32([0.0, 1e-40, 3.3e38, 3.4e38, 1.17e-38])])
+    ref = torch.from_numpy(vals32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.f64_to_bf16(float(v)) for v in vals32], np.uint16)
+    bad = np.flatnonzero(ref != got)
+    assert bad.size == 0, "bfloat16 encode differs for %r" % vals32[bad[:5]]
+    # binary64 values (not binary32) against exact rational rounding
+    g = SplitMix64(17)
+    mags = np.exp2(g.uniform(3000) * 280.0 - 140.0)
+    signs = np.where(g.uniform(3000) < 0.5, -1.0, 1.0)
+    for v in mags * signs:
+        assert orc.f64_to_bf16(float(v)) == _bf16_exact_rne(float(v)), v
+
+
 # --------------------------------------------------------------------------
 # hand-worked cases (tests/golden/hand_rotations.json)
 
@@ -111,18 +213,18 @@ def pin_hand_worked(orc):
     with open(os.path.join(GOLDEN, "hand_rotations.json")) as f:
         cases = json.load(f)["cases"]
     for case in cases:
-        for dt, key in ((np.float32, "f32"), (np.float16, "f16")):
-            x = np.array(case["x"], dt).reshape(1, 1, 1, 4)
-            c = np.array(case["cos"], dt)
-            s = np.array(case["sin"], dt)
+        for dt, key in ((np.float32, "f32"), (np.float16, "f16"), (BF16, "bf16")):
+            x = from_f64(case["x"], dt).reshape(1, 1, 1, 4)
+            c = from_f64(case["cos"], dt)
+            s = from_f64(case["sin"], dt)
             for il, pk in ((0, "half_split"), (1, "interleaved")):
-                want = np.array(case["expected"][pk][key], dt)
+                want = from_f64(case["expected"][pk][key], dt)
                 # per-token (B,S,R/2) table, no ids
                 y = orc.rope_apply(x, c.reshape(1, 1, 2), s.reshape(1, 1, 2), interleaved=il)
                 assert_value_equal(y.reshape(-1), want, "%s %s %s" % (case["name"], key, pk))
                 # gathered (M,R/2) table, id 2 of 3 rows
-                ct = np.stack([np.zeros(2, dt), np.ones(2, dt), c])
-                st = np.stack([np.ones(2, dt), np.zeros(2, dt), s])
+                ct = np.stack([from_f64(np.zeros(2), dt), from_f64(np.ones(2), dt), c])
+                st = np.stack([from_f64(np.ones(2), dt), from_f64(np.zeros(2), dt), s])
                 y = orc.rope_apply(x, ct, st, np.array([[2]]), interleaved=il)
                 assert_value_equal(y.reshape(-1), want, "%s %s %s ids" % (case["name"], key, pk))
 
@@ -131,75 +233,76 @@ def pin_hand_worked(orc):
 # the rotation against two independent formulations
 
 def pin_complex_multiplication(orc):
-    """Pair (x1, x2) as x1 + i*x2 times c + i*s (numpy complex128), rounded once."""
-    for dt in (np.float32, np.float16):
+    """Pair (x1, x2) as x1 + i*x2 times c + i*s (numpy complex128), rounded once
+    (bfloat16: rounded by the exact rational rule)."""
+    for dt in (np.float32, np.float16, BF16):
         for il in (0, 1):
             for rank in (3, 4):
                 B, S, H, D, M = 2, 5, 3, 12, 17
-                x = normal_tensor(11, (B, H, S, D), dt)
+                x = normal_any(11, (B, H, S, D), dt)
                 cos, sin = angle_table(12, M, D // 2, dt)
                 ids = ids_in(13, (B, S), M)
                 j1, j2 = pair_index(il, D // 2)
-                z = x[..., j1].astype(np.complex128) + 1j * x[..., j2].astype(np.complex128)
-                w = cos[ids].astype(np.complex128) + 1j * sin[ids].astype(np.complex128)
+                z = to_f64(x[..., j1]) + 1j * to_f64(x[..., j2])
+                w = to_f64(cos[ids]) + 1j * to_f64(sin[ids])
                 prod = z * w[:, None, :, :]
                 want = np.empty_like(x)
-                want[..., j1] = prod.real.astype(dt)
-                want[..., j2] = prod.imag.astype(dt)
+                want[..., j1] = round_to(prod.real, dt)
+                want[..., j2] = round_to(prod.imag, dt)
                 if rank == 4:
                     y = orc.rope_apply(x, cos, sin, ids, interleaved=il)
                 else:
                     x3 = np.ascontiguousarray(x.transpose(0, 2, 1, 3)).reshape(B, S, H * D)
                     y = to_rank4(orc.rope_apply(x3, cos, sin, ids, interleaved=il, num_heads=H), H)
-                assert_bitwise(y, want, "complex form dt=%s il=%d rank=%d" % (dt.__name__, il, rank))
+                assert_bitwise(y, want, "complex form dt=%s il=%d rank=%d" % (np.dtype(dt).name, il, rank))
 
 
 def pin_rotate_half_form(orc):
     """q*cat(c,c) + rotate_half(q)*cat(s,s), rotate_half(q) = cat(-q2, q1), on the
     leading R elements, the rest concatenated back unchanged (partial rotation)."""
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         for D, R in ((16, 16), (16, 8), (10, 4)):
             B, H, S, M = 2, 2, 7, 9
-            x = normal_tensor(21, (B, H, S, D), dt)
+            x = normal_any(21, (B, H, S, D), dt)
             cos, sin = angle_table(22, M, R // 2, dt)
             ids = ids_in(23, (B, S), M)
-            q = x.astype(np.float64)
-            q_rot, q_pass = q[..., :R], q[..., R:]
-            C = np.concatenate([cos[ids], cos[ids]], -1).astype(np.float64)[:, None]
-            Sn = np.concatenate([sin[ids], sin[ids]], -1).astype(np.float64)[:, None]
+            q = to_f64(x)
+            q_rot = q[..., :R]
+            C = to_f64(np.concatenate([cos[ids], cos[ids]], -1))[:, None]
+            Sn = to_f64(np.concatenate([sin[ids], sin[ids]], -1))[:, None]
             rot_half = np.concatenate([-q_rot[..., R // 2:], q_rot[..., :R // 2]], -1)
-            emb = (q_rot * C + rot_half * Sn).astype(dt)
+            emb = round_to(q_rot * C + rot_half * Sn, dt)
             want = np.concatenate([emb, x[..., R:]], -1)
             y = orc.rope_apply(x, cos, sin, ids, rotary_embedding_dim=R if R != D else 0)
-            assert_bitwise(y, want, "rotate_half form dt=%s D=%d R=%d" % (dt.__name__, D, R))
-            assert_bitwise(y[..., R:], q_pass.astype(dt), "pass-through")
+            assert_bitwise(y, want, "rotate_half form dt=%s D=%d R=%d" % (np.dtype(dt).name, D, R))
+            assert_bitwise(y[..., R:], x[..., R:], "pass-through")
 
 
 # --------------------------------------------------------------------------
 # invariants
 
 def pin_identity(orc):
-    for dt in (np.float32, np.float16):
-        x = normal_tensor(31, (2, 3, 4, 8), dt)
-        ones = np.ones((5, 4), dt)
-        zeros = np.zeros((5, 4), dt)
+    for dt in (np.float32, np.float16, BF16):
+        x = normal_any(31, (2, 3, 4, 8), dt)
+        ones = from_f64(np.ones((5, 4)), dt)
+        zeros = from_f64(np.zeros((5, 4)), dt)
         for il in (0, 1):
             y = orc.rope_apply(x, ones, zeros, ids_in(32, (2, 4), 5), interleaved=il)
             assert_value_equal(y, x, "identity")
 
 
 def pin_norm_preserved(orc):
-    for dt, rel in ((np.float32, 4 * 2.0 ** -24), (np.float16, 4 * 2.0 ** -11)):
+    for dt, rel in ((np.float32, 4 * 2.0 ** -24), (np.float16, 4 * 2.0 ** -11), (BF16, 4 * 2.0 ** -8)):
         for il in (0, 1):
-            x = normal_tensor(41, (2, 4, 6, 16), dt)
+            x = normal_any(41, (2, 4, 6, 16), dt)
             cos, sin = angle_table(42, 11, 8, dt)
             # the rounded table has c^2 + s^2 != 1: compare against the exact product
             ids = ids_in(43, (2, 6), 11)
-            y = orc.rope_apply(x, cos, sin, ids, interleaved=il).astype(np.float64)
+            y = to_f64(orc.rope_apply(x, cos, sin, ids, interleaved=il))
             j1, j2 = pair_index(il, 8)
-            xd = x.astype(np.float64)
-            c = cos[ids].astype(np.float64)[:, None]
-            s = sin[ids].astype(np.float64)[:, None]
+            xd = to_f64(x)
+            c = to_f64(cos[ids])[:, None]
+            s = to_f64(sin[ids])[:, None]
             n_in = (xd[..., j1] ** 2 + xd[..., j2] ** 2) * (c ** 2 + s ** 2)
             n_out = y[..., j1] ** 2 + y[..., j2] ** 2
             err = np.abs(n_out - n_in) / np.maximum(n_in, 1e-3)
@@ -219,11 +322,12 @@ def pin_inverse(orc):
 
 
 def pin_tail_bitwise(orc):
-    for dt, nan in ((np.float32, np.uint32(0x7fa00123)), (np.float16, np.uint16(0x7e55))):
-        x = normal_tensor(61, (2, 2, 3, 10), dt)
+    for dt, nan in ((np.float32, np.uint32(0x7fa00123)), (np.float16, np.uint16(0x7e55)),
+                    (BF16, np.uint16(0x7fa1))):
+        x = normal_any(61, (2, 2, 3, 10), dt)
         raw = bits(x).copy()
         raw[..., 6] = nan                                  # NaN payload in the tail
-        raw[..., 7] = 0x8000 if dt == np.float16 else 0x80000000   # -0
+        raw[..., 7] = 0x80000000 if dt == np.float32 else 0x8000   # -0
         x = raw.view(dt)
         cos, sin = angle_table(62, 4, 3, dt)
         for il in (0, 1):
@@ -234,9 +338,9 @@ def pin_tail_bitwise(orc):
 
 def pin_pairing_permutation(orc):
     """interleaved(P x) == P half_split(x), P: j -> 2j, R/2 + j -> 2j + 1 on [0,R)."""
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         D, R = 12, 8
-        x = normal_tensor(71, (2, 3, 4, D), dt)
+        x = normal_any(71, (2, 3, 4, D), dt)
         cos, sin = angle_table(72, 6, R // 2, dt)
         ids = ids_in(73, (2, 4), 6)
         perm = np.arange(D)
@@ -249,9 +353,9 @@ def pin_pairing_permutation(orc):
 
 
 def pin_rank_transpose(orc):
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         B, S, H, D = 3, 5, 4, 8
-        x3 = normal_tensor(81, (B, S, H * D), dt)
+        x3 = normal_any(81, (B, S, H * D), dt)
         cos, sin = angle_table(82, 9, D // 2, dt)
         ids = ids_in(83, (B, S), 9)
         for il in (0, 1):
@@ -262,7 +366,7 @@ def pin_rank_transpose(orc):
 
 def pin_gather_probe(orc):
     """Every pair (1, 0) -> the pair becomes (c, s) of the gathered row."""
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         B, H, S, D, M = 2, 3, 6, 8, 13
         cos, sin = angle_table(91, M, D // 2, dt)
         ids = ids_in(92, (B, S), M)
@@ -271,7 +375,7 @@ def pin_gather_probe(orc):
         for il in (0, 1):
             j1, j2 = pair_index(il, D // 2)
             x = np.zeros((B, H, S, D), dt)
-            x[..., j1] = 1
+            x[..., j1] = from_f64(1.0, dt)
             y = orc.rope_apply(x, cos, sin, ids, interleaved=il)
             for h in range(H):
                 assert_bitwise(y[:, h][..., j1], cos[ids], "probe cos")
@@ -280,10 +384,10 @@ def pin_gather_probe(orc):
 
 def pin_per_token_table(orc):
     """No ids with table T3[b][s] = T2[ids[b][s]] equals the gathered call."""
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         for rank in (3, 4):
             B, S, H, D, M = 3, 4, 2, 8, 7
-            x = normal_tensor(101, (B, H, S, D) if rank == 4 else (B, S, H * D), dt)
+            x = normal_any(101, (B, H, S, D) if rank == 4 else (B, S, H * D), dt)
             cos, sin = angle_table(102, M, D // 2, dt)
             ids = ids_in(103, (B, S), M)
             ids[0, 0] = 0
@@ -296,9 +400,9 @@ def pin_per_token_table(orc):
 
 def pin_out_of_range_ids(orc):
     """Reading taken: an id outside [0, M) passes the whole row through."""
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         B, H, S, D, M = 2, 2, 6, 8, 5
-        x = normal_tensor(111, (B, H, S, D), dt)
+        x = normal_any(111, (B, H, S, D), dt)
         cos, sin = angle_table(112, M, D // 2, dt)
         ids = ids_in(113, (B, S), M)
         ids[0, 1] = -1
@@ -338,7 +442,7 @@ def pin_cache_spot_rows(orc):
     rows = (0, 1, 7, 100, 1000)
     for dt, base, R, scaling in ((np.float16, 1e6, 128, 1.0), (np.float32, 1e6, 128, 1.0),
                                  (np.float32, 1e4, 64, 1.0), (np.float16, 1e4, 64, 1.25),
-                                 (np.float32, 1e6, 128, 0.7)):
+                                 (np.float32, 1e6, 128, 0.7), (BF16, 1e6, 128, 1.0), (BF16, 1e4, 64, 1.25)):
         inv = np.array(_mp_inv_freq(base, R), np.float32)
         cos, sin = orc.cos_sin_cache(dt, 1001, inv, scaling)
         assert cos.shape == (1001, R // 2)
@@ -348,12 +452,12 @@ def pin_cache_spot_rows(orc):
                 th = np.float32(np.float64(np.float32(p)) * np.float64(inv[i]))
                 c = f32_of_mp(mpmath.cos(mpmath.mpf(float(th))))
                 s = f32_of_mp(mpmath.sin(mpmath.mpf(float(th))))
-                c = np.float32(np.float64(c) * np.float64(sc)).astype(dt)
-                s = np.float32(np.float64(s) * np.float64(sc)).astype(dt)
+                c = from_f64(np.float32(np.float64(c) * np.float64(sc)), dt)
+                s = from_f64(np.float32(np.float64(s) * np.float64(sc)), dt)
                 assert bits(np.array([cos[p, i]]))[0] == bits(np.array([c]))[0], (dt, p, i, cos[p, i], c)
                 assert bits(np.array([sin[p, i]]))[0] == bits(np.array([s]))[0], (dt, p, i, sin[p, i], s)
         if scaling == 1.0:
-            assert (cos[0] == 1).all() and (bits(sin[0]) == 0).all()
+            assert (to_f64(cos[0]) == 1).all() and (bits(sin[0]) == 0).all()
 
 
 def pin_c1_against_real_math(orc):
@@ -425,13 +529,13 @@ def pin_mrope_section_maps(orc):
 
 def pin_mrope_equal_streams(orc):
     """Text-only tokens (all streams equal) reduce M-RoPE to RotaryEmbedding."""
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         for rank, D, R in ((4, 16, 0), (3, 16, 8), (4, 9, 8), (3, 10, 6)):
             for il in (0, 1):
                 B, S, H, M = 2, 5, 3, 11
                 Rf = R or D
                 shape = (B, H, S, D) if rank == 4 else (B, S, H * D)
-                x = normal_tensor(121, shape, dt)
+                x = normal_any(121, shape, dt)
                 cos, sin = angle_table(122, M, Rf // 2, dt)
                 ids = ids_in(123, (B, S), M)
                 ids3 = np.stack([ids, ids, ids])
@@ -454,7 +558,7 @@ def _mrope_probe(orc, dt, section, layout, expect_map):
     for il in (0, 1):
         j1, j2 = pair_index(il, half)
         x = np.zeros((B, H, S, D), dt)
-        x[..., j1] = 1
+        x[..., j1] = from_f64(1.0, dt)
         y = orc.mrope_apply(x, ids, cos, sin, section, layout, interleaved=il, num_heads=H)
         for b in range(B):
             for s in range(S):
@@ -470,7 +574,7 @@ def pin_mrope_stream_gather(orc):
     its own stream. Maps written here independently: sections in order for
     layout 0, the stride-3 rule for layout 1 (agrees with the reading taken
     when sec_h == sec_w <= sec_t)."""
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         for sec in ((2, 1, 1), (16, 24, 24), (3, 0, 5), (24, 20, 20), (4, 2, 2)):
             half = sum(sec)
             _mrope_probe(orc, dt, sec, 0, [0] * sec[0] + [1] * sec[1] + [2] * sec[2])
@@ -479,11 +583,11 @@ def pin_mrope_stream_gather(orc):
 
 
 def pin_mrope_out_of_range(orc):
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         for layout in (0, 1):
             B, H, S, D, M = 2, 3, 9, 16, 20
             sec = (4, 2, 2)
-            x = normal_tensor(141, (B, H, S, D), dt)
+            x = normal_any(141, (B, H, S, D), dt)
             cos, sin = angle_table(142, M, D // 2, dt)
             ids = ids_in(143, (3, B, S), M)
             bad = ids.copy()
@@ -507,16 +611,16 @@ def pin_mrope_out_of_range(orc):
 
 def pin_mrope_scale(orc):
     """scale = 2 (exact) equals scale 1 with a doubled table; scale 0.5 likewise."""
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         B, H, S, D, M = 2, 2, 6, 12, 9
         sec = (2, 2, 2)
-        x = normal_tensor(151, (B, H, S, D), dt)
+        x = normal_any(151, (B, H, S, D), dt)
         cos, sin = angle_table(152, M, D // 2, dt)
         ids = ids_in(153, (3, B, S), M)
         for layout in (0, 1):
             for sc in (2.0, 0.5):
                 a = orc.mrope_apply(x, ids, cos, sin, sec, layout, num_heads=H, scale=sc)
-                b = orc.mrope_apply(x, ids, (cos * dt(sc)).astype(dt), (sin * dt(sc)).astype(dt), sec,
+                b = orc.mrope_apply(x, ids, round_to(to_f64(cos) * sc, dt), round_to(to_f64(sin) * sc, dt), sec,
                                     layout, num_heads=H, scale=1.0)
                 assert_bitwise(a, b, "scale %g" % sc)
 
@@ -526,8 +630,8 @@ def pin_mrope_tiny_brute_force(orc):
     [3,2,2], cos/sin [2,4], mrope_section [2,1,1]; every output against a
     complex-multiplication brute force with the slot rows picked by hand."""
     maps = {0: [0, 0, 1, 2], 1: [0, 1, 2, 0]}
-    for dt in (np.float32, np.float16):
-        x = normal_tensor(161, (2, 2, 16), dt)
+    for dt in (np.float32, np.float16, BF16):
+        x = normal_any(161, (2, 2, 16), dt)
         cos, sin = angle_table(162, 2, 4, dt)
         ids = ids_in(163, (3, 2, 2), 4) - 1          # values -1..2 with rows 0..1 valid
         for layout in (0, 1):
@@ -546,9 +650,10 @@ def pin_mrope_tiny_brute_force(orc):
                                 if p < 0 or p >= 2:
                                     assert bits(np.array(pair_out)).tolist() == bits(np.array(pair_in)).tolist()
                                     continue
-                                z = complex(float(pair_in[0]), float(pair_in[1])) * \
-                                    complex(float(cos[p, i]), float(sin[p, i]))
-                                assert pair_out[0] == dt(z.real) and pair_out[1] == dt(z.imag), \
+                                z = complex(*to_f64(np.array(pair_in))) * \
+                                    complex(*to_f64(np.array([cos[p, i], sin[p, i]])))
+                                want = round_to(np.array([z.real, z.imag]), dt)
+                                assert bits(np.array(pair_out)).tolist() == bits(want).tolist(), \
                                     (layout, il, b, s, h, i)
 
 
@@ -556,11 +661,11 @@ def pin_mrope_tiny_brute_force(orc):
 # Q+K and on-the-fly
 
 def pin_qk_is_two_applies(orc):
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         for rank in (3, 4):
             B, S, H, Hk, D, M = 3, 2, 4, 2, 8, 10
-            q = normal_tensor(171, (B, H, S, D) if rank == 4 else (B, S, H * D), dt)
-            k = normal_tensor(172, (B, Hk, S, D) if rank == 4 else (B, S, Hk * D), dt)
+            q = normal_any(171, (B, H, S, D) if rank == 4 else (B, S, H * D), dt)
+            k = normal_any(172, (B, Hk, S, D) if rank == 4 else (B, S, Hk * D), dt)
             cos, sin = angle_table(173, M, D // 2, dt)
             ids = ids_in(174, (B, S), M)
             yq, yk = orc.rope_apply_qk(q, k, cos, sin, ids, num_heads=H, kv_num_heads=Hk)
@@ -569,13 +674,13 @@ def pin_qk_is_two_applies(orc):
 
 
 def pin_onthefly_equals_table(orc):
-    for dt in (np.float32, np.float16):
+    for dt in (np.float32, np.float16, BF16):
         for sc in (1.0, 1.25):
             B, S, H, Hk, D, M = 4, 3, 4, 2, 16, 40000
             inv = orc.inv_freq(1e6, D)
             cos, sin = orc.cos_sin_cache(dt, M, inv, sc)
-            q = normal_tensor(181, (B, S, H * D), dt)
-            k = normal_tensor(182, (B, S, Hk * D), dt)
+            q = normal_any(181, (B, S, H * D), dt)
+            k = normal_any(182, (B, S, Hk * D), dt)
             ids = ids_in(183, (B, S), M)
             ids[0, 0] = 0
             ids[1, 1] = M - 1

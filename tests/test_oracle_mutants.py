@@ -37,6 +37,11 @@ MUTANTS = {
     "cache_scaling_ignored": [("float cs = (float)((double)cf * (double)scaling);", "float cs = cf;")],
     "f16_round_down": [("nearbyint(a / quantum)", "floor(a / quantum)")],
     "f16_subnormal_scale": [("v = ldexp((double)m, -24);", "v = ldexp((double)m, -25);")],
+    "bf16_decode_exponent": [("v = ldexp((double)(128 + m), e - 134);", "v = ldexp((double)(128 + m), e - 133);")],
+    "bf16_subnormal_bound": [("if (r < ldexp(1.0, -126))", "if (r < ldexp(1.0, -127))")],
+    "bf16_fraction_bits": [("ldexp(r, 7 - E) - 128.0", "ldexp(r, 7 - E) - 127.0")],
+    "bf16_stored_as_f16": [("((uint16_t*)p)[idx] = oracle_f64_to_bf16(v);",
+                            "((uint16_t*)p)[idx] = oracle_f64_to_f16(v);")],
     "inv_freq_exponent": [("-2.0 * (double)i / (double)rotary_dim", "-1.0 * (double)i / (double)rotary_dim")],
     "onthefly_uses_position_zero": [("coefficient(dtype, p, inv_freq[i], scaling, &cr.c[i], &cr.s[i]);",
                                      "coefficient(dtype, 0, inv_freq[i], scaling, &cr.c[i], &cr.s[i]);")],
