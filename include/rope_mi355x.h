@@ -24,8 +24,11 @@
  * Conventions for every entry point
  *   - Tensors are described by rope_tensor: a DEVICE pointer to dense
  *     row-major data, an ONNX TensorProto element type and a shape.
- *     Storage types: ROPE_FLOAT (binary32) and ROPE_FLOAT16 (binary16);
- *     positions are ROPE_INT64.
+ *     Storage types: ROPE_FLOAT (binary32), ROPE_FLOAT16 (binary16) and
+ *     ROPE_BFLOAT16 (bfloat16: the upper half of a binary32). The
+ *     MRotaryEmbedding README (Description) lists bfloat16 as not implemented
+ *     in its package; here it is the same arithmetic with another storage
+ *     type. Positions are ROPE_INT64.
  *   - The caller owns every buffer. The library never allocates, frees,
  *     copies to the host or synchronises: it validates on the host, then
  *     enqueues its kernels on `stream` (a hipStream_t; NULL = the null
@@ -58,10 +61,11 @@ extern "C" {
 #define ROPE_FLOAT 1
 #define ROPE_INT64 7
 #define ROPE_FLOAT16 10
+#define ROPE_BFLOAT16 16
 
 typedef struct rope_tensor {
     void* data;       /* device pointer, dense row-major */
-    int32_t dtype;    /* ROPE_FLOAT, ROPE_FLOAT16 or ROPE_INT64 */
+    int32_t dtype;    /* ROPE_FLOAT, ROPE_FLOAT16, ROPE_BFLOAT16 or ROPE_INT64 */
     int32_t rank;     /* 1..4 */
     int64_t shape[4]; /* entries beyond `rank` are ignored */
 } rope_tensor;
@@ -89,7 +93,7 @@ const char* rope_last_error(void);
  * rope_apply -- ONNX RotaryEmbedding ("ai.onnx.RotaryEmbedding" manifest).
  *
  * x:            rank 3 (B, S, H*D) with num_heads = H, or rank 4 (B, H, S, D).
- *               D must be even. Storage type T in {ROPE_FLOAT, ROPE_FLOAT16}.
+ *               D must be even. Storage type T in {ROPE_FLOAT, ROPE_FLOAT16, ROPE_BFLOAT16}.
  * cos_cache,
  * sin_cache:    type T, same shape. With position_ids: (M, R/2), row p
  *               serves position p. Without: (B, S, R/2), row (b, s) serves

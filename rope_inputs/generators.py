@@ -80,10 +80,25 @@ class SplitMix64:
         return (z * bound) >> 64
 
 
+BFLOAT16 = np.uint16
+"""bfloat16 tensors are carried as uint16 arrays of their bit patterns."""
+
+
+def bfloat16_bits(v) -> np.ndarray:
+    """bfloat16 bit patterns of binary32 values, nearest-even (finite inputs):
+    add 0x7fff plus the lowest kept bit, then keep the upper 16 bits."""
+    u = np.ascontiguousarray(np.asarray(v, np.float32)).view(np.uint32).astype(np.uint64)
+    return ((u + np.uint64(0x7fff) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)).astype(np.uint16)
+
+
 def normal_tensor(seed: int, shape, dtype) -> np.ndarray:
-    """N(0,1) values rounded to `dtype` (numpy's round-to-nearest-even)."""
+    """N(0,1) values rounded to `dtype` (numpy's round-to-nearest-even; for
+    bfloat16 through binary32, then nearest-even to 8 significant bits)."""
     n = int(np.prod(shape))
-    return SplitMix64(seed).normal(n).astype(dtype).reshape(shape)
+    v = SplitMix64(seed).normal(n)
+    if np.dtype(dtype) == BFLOAT16:
+        return bfloat16_bits(v.astype(np.float32)).reshape(shape)
+    return v.astype(dtype).reshape(shape)
 
 
 def uniform_ints(seed: int, shape, bound: int) -> np.ndarray:

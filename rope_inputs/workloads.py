@@ -215,6 +215,12 @@ def get(name: str) -> Workload:
     return WORKLOADS[name]
 
 
+def with_dtype(w: Workload, dtype, tag: str) -> Workload:
+    """The same workload stored in another type (same seeds and structure)."""
+    from dataclasses import replace
+    return replace(w, dtype=dtype, name="%s_%s" % (w.name, tag))
+
+
 def with_layout(w: Workload, layout: int) -> Workload:
     from dataclasses import replace
     return replace(w, mrope_layout=layout, name="%s_layout%d" % (w.name.rsplit("_layout", 1)[0], layout))

@@ -17,7 +17,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import ROPE_FLOAT, ROPE_FLOAT16, ROPE_INT64
+from ._lib import ROPE_BFLOAT16, ROPE_FLOAT, ROPE_FLOAT16, ROPE_INT64
 
 __all__ = ["RopeError", "rope_apply", "mrope_apply", "rope_apply_qk", "rope_inv_freq",
            "rope_cos_sin_cache", "rope_apply_check", "mrope_apply_check",
@@ -26,7 +26,7 @@ __all__ = ["RopeError", "rope_apply", "mrope_apply", "rope_apply_qk", "rope_inv_
            "rope_apply_qkv_packed", "rope_apply_qkv_packed_check", "rope_apply_qkv_packed_launcher"]
 
 _DTYPE = {torch.float32: ROPE_FLOAT, torch.float16: ROPE_FLOAT16, torch.int64: ROPE_INT64,
-          torch.bfloat16: 16}
+          torch.bfloat16: ROPE_BFLOAT16}
 
 library_path = _lib.LIB_PATH
 

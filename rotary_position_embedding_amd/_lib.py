@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(HERE, "librope_mi355x.so")
 ROPE_FLOAT = 1
 ROPE_INT64 = 7
 ROPE_FLOAT16 = 10
+ROPE_BFLOAT16 = 16
 
 STATUS = {
     0: "ROPE_OK", -1: "ROPE_ERR_NULL", -2: "ROPE_ERR_DTYPE", -3: "ROPE_ERR_RANK",

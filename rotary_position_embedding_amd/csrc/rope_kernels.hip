@@ -32,6 +32,7 @@
 namespace rope {
 
 using half_t = _Float16;
+using bf16_t = __bf16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWavesPerBlock = 4;
@@ -65,6 +66,7 @@ struct KArgs {
 template <typename T> struct Elem;
 template <> struct Elem<float> { using bits = uint32_t; static constexpr int E = 4; };
 template <> struct Elem<half_t> { using bits = uint16_t; static constexpr int E = 8; };
+template <> struct Elem<bf16_t> { using bits = uint16_t; static constexpr int E = 8; };
 
 // Materialise a binary32 value in a register. Without it the compiler may
 // merge a binary32 multiply or fma with the following conversion to binary16
@@ -77,10 +79,14 @@ __device__ inline float keep_f32(float v) {
 
 __device__ inline float to_f(float v) { return v; }
 __device__ inline float to_f(half_t v) { return (float)v; }
+__device__ inline float to_f(bf16_t v) { return (float)v; }  // exact: the upper half of a binary32
 template <typename T> __device__ inline T from_f(float v);
 template <> __device__ inline float from_f<float>(float v) { return v; }
 template <> __device__ inline half_t from_f<half_t>(float v) {
     return (half_t)keep_f32(v);  // nearest-even from the binary32 value
+}
+template <> __device__ inline bf16_t from_f<bf16_t>(float v) {
+    return (bf16_t)keep_f32(v);  // nearest-even from the binary32 value
 }
 template <typename T> __device__ inline float round_to(float v) { return to_f(from_f<T>(v)); }
 
@@ -89,9 +95,11 @@ template <typename T> __device__ inline float round_to(float v) { return to_f(fr
 // element is miscompiled to element 0 by this toolchain, so it is avoided).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef half_t f16x8 __attribute__((ext_vector_type(8)));
+typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
 template <typename T> struct ChunkVec;
 template <> struct ChunkVec<float> { typedef f32x4 type; };
 template <> struct ChunkVec<half_t> { typedef f16x8 type; };
+template <> struct ChunkVec<bf16_t> { typedef bf16x8 type; };
 
 template <typename T>
 __device__ inline typename ChunkVec<T>::type chunk_values(const u32x4& v) {
@@ -338,7 +346,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h_begin, h_end, sh_bytes, half_bytes, in1, in2);
 
     T cf[IPL][CE], sf[IPL][CE];
-    u32x4 keep[IPL];  // input bits passed through unchanged
+    u32x4 keep[IPL];  // input bits copied to the output as they are
 #pragma unroll
     for (int m = 0; m < IPL; ++m) {
         keep[m] = u32x4{0u, 0u, 0u, 0u};
@@ -684,13 +692,17 @@ int launch_plan(const Plan& pl, void* stream) {
         if (p.dtype == ROPE_FLOAT16)
             e = p.interleaved ? launch_vec_coef<half_t, 1>(a, p.coef, ipl, hu, grid, st)
                               : launch_vec_coef<half_t, 0>(a, p.coef, ipl, hu, grid, st);
+        else if (p.dtype == ROPE_BFLOAT16)
+            e = p.interleaved ? launch_vec_coef<bf16_t, 1>(a, p.coef, ipl, hu, grid, st)
+                              : launch_vec_coef<bf16_t, 0>(a, p.coef, ipl, hu, grid, st);
         else
             e = p.interleaved ? launch_vec_coef<float, 1>(a, p.coef, ipl, hu, grid, st)
                               : launch_vec_coef<float, 0>(a, p.coef, ipl, hu, grid, st);
     } else {
         if (item_begin == 0) return ROPE_OK;
-        e = p.dtype == ROPE_FLOAT16 ? launch_scalar<half_t>(a, p.coef, item_begin, st)
-                                    : launch_scalar<float>(a, p.coef, item_begin, st);
+        e = p.dtype == ROPE_FLOAT16    ? launch_scalar<half_t>(a, p.coef, item_begin, st)
+            : p.dtype == ROPE_BFLOAT16 ? launch_scalar<bf16_t>(a, p.coef, item_begin, st)
+                                       : launch_scalar<float>(a, p.coef, item_begin, st);
     }
     return launched(e);
 }
@@ -714,8 +726,9 @@ int launch_cos_sin_cache(const TablePlan& t, void* stream) {
     int64_t rows = t.rows, half = t.half;
     float scaling = t.scaling;
     void* args[] = {&inv, &cos, &sin, &rows, &half, &scaling};
-    const void* fn = t.dtype == ROPE_FLOAT16 ? (const void*)table_kernel<half_t>
-                                             : (const void*)table_kernel<float>;
+    const void* fn = t.dtype == ROPE_FLOAT16    ? (const void*)table_kernel<half_t>
+                     : t.dtype == ROPE_BFLOAT16 ? (const void*)table_kernel<bf16_t>
+                                                : (const void*)table_kernel<float>;
     return launched(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0,
                                     (hipStream_t)stream));
 }

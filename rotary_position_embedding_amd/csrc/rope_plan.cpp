@@ -49,12 +49,15 @@ static int elem_size(int32_t dtype) {
     switch (dtype) {
         case ROPE_FLOAT: return 4;
         case ROPE_FLOAT16: return 2;
+        case ROPE_BFLOAT16: return 2;
         case ROPE_INT64: return 8;
         default: return 0;
     }
 }
 
-static bool is_float(int32_t dtype) { return dtype == ROPE_FLOAT || dtype == ROPE_FLOAT16; }
+static bool is_float(int32_t dtype) {
+    return dtype == ROPE_FLOAT || dtype == ROPE_FLOAT16 || dtype == ROPE_BFLOAT16;
+}
 
 static int64_t numel(const rope_tensor* t) {
     int64_t n = 1;
@@ -164,7 +167,7 @@ static int heads_per_wave_override() { return env_int("ROPE_HEADS_PER_WAVE"); }
 static void choose_geometry(Plan* pl) {
     Problem& p = pl->p;
     Geometry& g = pl->g;
-    const int es = p.dtype == ROPE_FLOAT16 ? 2 : 4;
+    const int es = elem_size(p.dtype);
     const int E = 16 / es;
     const int64_t half = p.R / 2;
     bool ok = kernel_policy() == 0;
@@ -354,7 +357,7 @@ int plan_rope(const rope_tensor* x, const rope_tensor* cos_cache, const rope_ten
     if (position_ids) TRY(check_desc(position_ids, "position_ids"));
 
     if (!is_float(x->dtype))
-        return fail(ROPE_ERR_DTYPE, "x must be float32 or float16");
+        return fail(ROPE_ERR_DTYPE, "x must be float32, float16 or bfloat16");
     if (cos_cache->dtype != x->dtype || sin_cache->dtype != x->dtype || y->dtype != x->dtype)
         return fail(ROPE_ERR_DTYPE, "cos_cache, sin_cache and y must have the type of x");
     if (position_ids && position_ids->dtype != ROPE_INT64)
@@ -416,7 +419,7 @@ int plan_mrope(const rope_tensor* x, const rope_tensor* position_ids, const rope
     TRY(check_desc(y, "y"));
 
     if (!is_float(x->dtype))
-        return fail(ROPE_ERR_DTYPE, "x must be float32 or float16");
+        return fail(ROPE_ERR_DTYPE, "x must be float32, float16 or bfloat16");
     if (cos_cache->dtype != x->dtype || sin_cache->dtype != x->dtype || y->dtype != x->dtype)
         return fail(ROPE_ERR_DTYPE, "cos_cache, sin_cache and y must have the type of x");
     if (position_ids->dtype != ROPE_INT64)
@@ -528,7 +531,7 @@ int plan_rope_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor* 
     if (position_ids) TRY(check_desc(position_ids, "position_ids"));
     if (onthefly) TRY(check_desc(inv_freq, "inv_freq"));
 
-    if (!is_float(q->dtype)) return fail(ROPE_ERR_DTYPE, "q must be float32 or float16");
+    if (!is_float(q->dtype)) return fail(ROPE_ERR_DTYPE, "q must be float32, float16 or bfloat16");
     if (k->dtype != q->dtype || yq->dtype != q->dtype || yk->dtype != q->dtype)
         return fail(ROPE_ERR_DTYPE, "k, yq and yk must have the type of q");
     if (cos_cache && (cos_cache->dtype != q->dtype || sin_cache->dtype != q->dtype))
@@ -632,7 +635,7 @@ int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
     if (sin_cache) TRY(check_desc(sin_cache, "sin_cache"));
     if (position_ids) TRY(check_desc(position_ids, "position_ids"));
     if (onthefly) TRY(check_desc(inv_freq, "inv_freq"));
-    if (!is_float(qkv->dtype)) return fail(ROPE_ERR_DTYPE, "qkv must be float32 or float16");
+    if (!is_float(qkv->dtype)) return fail(ROPE_ERR_DTYPE, "qkv must be float32, float16 or bfloat16");
     if (y->dtype != qkv->dtype) return fail(ROPE_ERR_DTYPE, "y must have the type of qkv");
     if (cos_cache && (cos_cache->dtype != qkv->dtype || sin_cache->dtype != qkv->dtype))
         return fail(ROPE_ERR_DTYPE, "cos_cache and sin_cache must have the type of qkv");

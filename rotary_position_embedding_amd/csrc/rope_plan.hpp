@@ -22,7 +22,7 @@ constexpr int kMaxMropeHalf = 512;             // slots the stream table can hol
 constexpr int kSelWords = kMaxMropeHalf / 16;  // 2 bits per slot
 
 // One input/output pair rotated with the shared coefficients (or, with
-// copy set, passed through unchanged).
+// copy set, copied to the output as it is).
 struct Task {
     const void* x;
     void* y;
@@ -34,7 +34,7 @@ struct Task {
 constexpr int kMaxPlanTasks = 3;
 
 struct Problem {
-    int32_t dtype;        // ROPE_FLOAT or ROPE_FLOAT16
+    int32_t dtype;        // ROPE_FLOAT, ROPE_FLOAT16 or ROPE_BFLOAT16
     int32_t interleaved;  // 0 or 1
     int64_t B, S, D, R;   // batch, sequence, head size, rotary dim
     Task task[kMaxPlanTasks];

@@ -7,6 +7,9 @@ fma and one rounding to the storage type):
            2^-24 below (the binary32 result is correctly rounded, so only the
            second rounding to binary16 can differ from the oracle's single
            rounding, by at most one unit).
+  bfloat16 (uint16 bit patterns): |gpu - oracle| <= 1 ulp of the oracle value,
+           2^(floor(log2|v|) - 7) for |v| >= 2^-126 and 2^-133 below (same
+           argument: 8 significant bits instead of 11).
   float32: |gpu - oracle| <= 2e-6 * max(1, |oracle|).
 Pass-through elements (tail, out-of-range pairs) and gathered coefficient
 probes are compared bit for bit.
@@ -19,6 +22,20 @@ def bits(a):
     return a.view({2: np.uint16, 4: np.uint32, 8: np.uint64}[a.dtype.itemsize])
 
 
+def values(a):
+    """float64 values; uint16 arrays are bfloat16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def ulp_bf16(v):
+    a = np.abs(v)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
 def ulp_f16(v):
     a = np.abs(v.astype(np.float64))
     e = np.floor(np.log2(np.maximum(a, 2.0 ** -14)))
@@ -27,8 +44,8 @@ def ulp_f16(v):
 
 def compare(got, want):
     assert got.shape == want.shape and got.dtype == want.dtype, (got.shape, want.shape, got.dtype, want.dtype)
-    g = got.astype(np.float64).reshape(-1)
-    w = want.astype(np.float64).reshape(-1)
+    g = values(got).reshape(-1)
+    w = values(want).reshape(-1)
     nan_w = np.isnan(w)
     nan_bad = int(np.count_nonzero(nan_w != np.isnan(g)))
     finite = ~nan_w & ~np.isnan(g)
@@ -39,6 +56,9 @@ def compare(got, want):
     diff[same_inf] = 0.0
     if got.dtype == np.float16:
         tol = ulp_f16(w)
+        ulps = np.where(finite, diff / tol, 0.0)
+    elif got.dtype == np.uint16:
+        tol = ulp_bf16(w)
         ulps = np.where(finite, diff / tol, 0.0)
     else:
         tol = 2e-6 * np.maximum(1.0, np.abs(w))

@@ -14,7 +14,7 @@ from rotary_position_embedding_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rope_mi355x.h")
 
-F32, F16, I64 = 1, 10, 7
+F32, F16, BF16, I64 = 1, 10, 16, 7
 OK, NULL, DTYPE, RANK, SHAPE, ATTR, UNSUP, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
 
 
@@ -58,7 +58,7 @@ class Alloc:
         self.next = 1 << 32
 
     def __call__(self, dtype, shape, align=256):
-        nbytes = {F32: 4, F16: 2, I64: 8}.get(dtype, 4)
+        nbytes = {F32: 4, F16: 2, BF16: 2, I64: 8}.get(dtype, 4)
         for d in shape:
             nbytes *= d
         addr = self.next
@@ -98,7 +98,7 @@ def reshape(t, shape, dtype=None):
 
 
 @pytest.mark.parametrize("rank,ids", [(3, True), (4, True), (3, False), (4, False)])
-@pytest.mark.parametrize("dt", [F16, F32])
+@pytest.mark.parametrize("dt", [F16, F32, BF16])
 def test_rope_variants_accepted(rank, ids, dt):
     """One positive case per manifest variant (rank3/rank4 x cache2+ids / cache3)."""
     rc, variant = check_rope(rope_case(rank=rank, ids=ids, dt=dt))
@@ -169,8 +169,11 @@ def test_rope_shape_clauses():
         assert rc == code, (what, rc, lib.rope_last_error())
 
     # dtype clauses
-    kw = rope_case(); kw["x"] = reshape(kw["x"], tuple(kw["x"].shape[:3]), 16)      # bf16
-    expect(kw, DTYPE, "x bf16")
+    kw = rope_case(); kw["x"] = reshape(kw["x"], tuple(kw["x"].shape[:3]), BF16)
+    expect(kw, DTYPE, "x bf16 with f16 tables")
+    kw = rope_case(dt=BF16); kw["x"] = reshape(kw["x"], tuple(kw["x"].shape[:3]), 11)  # double
+    kw["y"] = reshape(kw["y"], tuple(kw["y"].shape[:3]), 11)
+    expect(kw, DTYPE, "binary64 storage")
     kw = rope_case(); kw["cos_cache"] = reshape(kw["cos_cache"], (16, 8), F32)
     expect(kw, DTYPE, "cos dtype")
     kw = rope_case(); kw["y"] = reshape(kw["y"], (2, 5, 64), F32)

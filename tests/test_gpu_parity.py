@@ -8,7 +8,7 @@ import oracle
 import rotary_position_embedding_amd as rpe
 from oracle_pins import angle_table, ids_in, pair_index
 from parity import assert_bitwise, assert_parity, bits, compare
-from rope_inputs import WORKLOADS, normal_tensor, with_layout
+from rope_inputs import BFLOAT16, WORKLOADS, bfloat16_bits, normal_tensor, with_dtype, with_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -16,12 +16,27 @@ DEV = "cuda:0"
 
 
 def cuda(a):
-    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    """numpy -> device tensor; uint16 arrays are bfloat16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == BFLOAT16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
 
 
 def host(t):
     torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
+
+
+def torch_dtype(dt):
+    return {np.dtype(np.float16): torch.float16, np.dtype(np.float32): torch.float32,
+            np.dtype(BFLOAT16): torch.bfloat16}[np.dtype(dt)]
+
+
+def one(dt):
+    return bfloat16_bits(1.0) if np.dtype(dt) == BFLOAT16 else 1
 
 
 @pytest.fixture(autouse=True)
@@ -135,19 +150,43 @@ def test_c5_onthefly_equals_table_on_gpu():
     assert_bitwise(host(a[1]), host(b[1]), "K")
 
 
+# the same workloads stored in bfloat16 (same seeds and shapes)
+
+@pytest.mark.parametrize("name,variant", [
+    ("c1_rope_f32_tiny", None), ("c2_rope_f16_prefill", None), ("c3_rope_f32_partial_interleaved", None),
+    ("c4_mrope_f16_prefill", 0), ("c4_mrope_f16_prefill", 1), ("c5_rope_qk_f16_decode", False),
+    ("c5_rope_qk_f16_decode", True)])
+def test_workloads_bf16(name, variant):
+    w = with_dtype(WORKLOADS[name], BFLOAT16, "bf16")
+    if w.op == "mrope":
+        w = with_layout(w, variant)
+    log("bf16 workload %s variant=%s" % (w.name, variant))
+    got, want, inputs = run_workload(w, onthefly=bool(variant) if w.op == "rope_qk" else False)
+    if w.op == "rope_qk":
+        rq = assert_parity(got[0], want[0], w.name + " Q")
+        rk = assert_parity(got[1], want[1], w.name + " K")
+        log("%s Q %s K %s" % (w.name, rq, rk))
+        return
+    r = assert_parity(got, want, w.name)
+    if w.rotary_embedding_dim:
+        R = w.rotary_embedding_dim
+        assert_bitwise(got[..., R:], inputs[0][..., R:], "tail")
+    log("%s %s" % (w.name, r))
+
+
 # ---------------------------------------------------------------------------
 # table builders
 
 @pytest.mark.parametrize("dt,base,R,rows,scaling", [
     (np.float16, 1e6, 128, 32768, 1.0), (np.float32, 1e4, 64, 4096, 1.0),
-    (np.float16, 1e4, 8, 16, 1.0), (np.float32, 1e6, 128, 4096, 0.7), (np.float16, 5e5, 96, 1000, 1.25)])
+    (np.float16, 1e4, 8, 16, 1.0), (np.float32, 1e6, 128, 4096, 0.7), (np.float16, 5e5, 96, 1000, 1.25),
+    (BFLOAT16, 1e6, 128, 32768, 1.0), (BFLOAT16, 1e4, 64, 1000, 1.25)])
 def test_tables_match_oracle(dt, base, R, rows, scaling):
     inv_o = oracle.inv_freq(base, R)
     inv_g = host(rpe.rope_inv_freq(R, base, device=DEV))
     assert_bitwise(inv_g, inv_o, "inv_freq")
     cos_o, sin_o = oracle.cos_sin_cache(dt, rows, inv_o, scaling)
-    cos_g, sin_g = rpe.rope_cos_sin_cache(cuda(inv_o), rows, torch.float16 if dt == np.float16 else torch.float32,
-                                          scaling)
+    cos_g, sin_g = rpe.rope_cos_sin_cache(cuda(inv_o), rows, torch_dtype(dt), scaling)
     rc = compare(host(cos_g), cos_o)
     rs = compare(host(sin_g), sin_o)
     # cos/sin of a binary32 angle rounded to binary32 by two libraries: equal
@@ -176,6 +215,11 @@ SHAPES = [
     (4, np.float16, 2, 13, 4, 18, 10, 1, True, 20),
     (3, np.float32, 2, 7, 3, 2, 0, 0, False, 0),
     (4, np.float16, 1, 17, 2, 1024, 0, 0, True, 40),     # long rows
+    (3, BFLOAT16, 3, 37, 5, 128, 0, 0, True, 300),
+    (4, BFLOAT16, 2, 41, 3, 64, 0, 1, True, 100),
+    (4, BFLOAT16, 2, 19, 7, 96, 64, 1, True, 64),
+    (3, BFLOAT16, 2, 33, 4, 80, 32, 0, False, 0),
+    (3, BFLOAT16, 2, 13, 4, 6, 0, 0, True, 20),          # not 16-byte items
 ]
 
 
@@ -212,7 +256,7 @@ def test_rope_sweep(case, policy):
             assert_bitwise(got[b, s], x[b, s], "out-of-range rows")
 
 
-@pytest.mark.parametrize("dt", [np.float16, np.float32])
+@pytest.mark.parametrize("dt", [np.float16, np.float32, BFLOAT16])
 @pytest.mark.parametrize("il", [0, 1])
 def test_gather_probe_bitexact(dt, il):
     B, H, S, D, M = 3, 4, 29, 128, 777
@@ -220,7 +264,7 @@ def test_gather_probe_bitexact(dt, il):
     ids = ids_in(4001, (B, S), M)
     j1, j2 = pair_index(il, D // 2)
     x = np.zeros((B, H, S, D), dt)
-    x[..., j1] = 1
+    x[..., j1] = one(dt)
     y = host(rpe.rope_apply(cuda(x), cuda(cos), cuda(sin), cuda(ids), interleaved=il))
     for h in range(H):
         assert_bitwise(y[:, h][..., j1], cos[ids], "probe cos")
@@ -282,6 +326,9 @@ MROPE = [
     (4, np.float16, 2, 20, 2, 9, 8, (2, 1, 1), 0, 1.0),      # odd head size, scalar kernel
     (4, np.float16, 2, 21, 5, 80, 48, (0, 12, 12), 0, 1.25),
     (3, np.float16, 1, 40, 2, 256, 0, (40, 44, 44), 1, 1.0),
+    (4, BFLOAT16, 2, 45, 3, 128, 0, (16, 24, 24), 0, 1.0),
+    (3, BFLOAT16, 2, 33, 4, 128, 0, (24, 20, 20), 1, 1.25),
+    (4, BFLOAT16, 2, 20, 2, 9, 8, (2, 1, 1), 0, 1.0),
 ]
 
 
@@ -341,6 +388,8 @@ QK = [
     (3, np.float32, 2, 9, 6, 2, 96, 64, 1),
     (4, np.float32, 2, 5, 4, 1, 128, 0, 0),
     (3, np.float16, 3, 4, 4, 2, 10, 0, 0),   # scalar kernel
+    (3, BFLOAT16, 7, 1, 8, 2, 128, 0, 0),
+    (4, BFLOAT16, 3, 17, 4, 4, 64, 0, 1),
 ]
 
 
@@ -398,6 +447,8 @@ PACKED = [
     (3, np.float32, 2, 11, 6, 3, 96, 64, 1),
     (4, np.float32, 2, 13, 2, 1, 128, 0, 0),
     (3, np.float16, 2, 7, 4, 2, 10, 0, 0),     # scalar kernel
+    (3, BFLOAT16, 256, 1, 32, 8, 128, 0, 0),
+    (3, BFLOAT16, 3, 37, 8, 2, 128, 0, 1),
 ]
 
 
