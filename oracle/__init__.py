@@ -83,6 +83,8 @@ class Oracle:
             "oracle_onthefly_row": ([i32, i64, vp, i64, f32, vp, vp], None),
             "oracle_rope_apply_qk": ([i32, i32, i64, i64, i64, i64, i64, i64, i64,
                                       vp, vp, vp, vp, vp, vp, vp, i64, vp, f32], None),
+            "oracle_rope_kv_append": ([i32, i64, i64, i64, i64, i64, i64, i64,
+                                       vp, vp, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -201,6 +203,37 @@ class Oracle:
                                       _ptr(sin), _ptr(ids), M, _ptr(inv), attention_scaling)
         return yq, yk
 
+    def rope_kv_append(self, query, key, value, past_key, past_value, key_total_sequence_lengths,
+                       total_sequence_length, cos, sin, num_heads, kv_num_heads, interleaved=0):
+        """RoPE on Q and K and the key/value cache append. query (B,S,H*D), or
+        packed [Q|K|V] when key and value are None; past_key/past_value
+        (B,Hk,Smax,D) are copied and the updated copies returned with q_out:
+        (q_out, present_key, present_value)."""
+        query = _dense(query)
+        packed = key is None
+        if packed != (value is None):
+            raise ValueError("key and value are both given or both None")
+        key = _dense(key, query.dtype)
+        value = _dense(value, query.dtype)
+        lens = _dense(key_total_sequence_lengths, np.int32)
+        cos = _dense(cos, query.dtype)
+        sin = _dense(sin, query.dtype)
+        pk = np.array(past_key, copy=True, order="C")
+        pv = np.array(past_value, copy=True, order="C")
+        B, S, W = query.shape
+        Hall = num_heads + (2 * kv_num_heads if packed else 0)
+        D = W // Hall
+        Bc, Hk, Smax, Dc = pk.shape
+        if (Bc, Hk, Dc) != (B, kv_num_heads, D) or pv.shape != pk.shape:
+            raise ValueError("cache shape disagrees with the inputs")
+        R = 2 * cos.shape[1]
+        q_out = np.zeros((B, S, num_heads * D), query.dtype)
+        self.lib.oracle_rope_kv_append(_code(query.dtype), B, S, num_heads, kv_num_heads, D, R, interleaved,
+                                       _ptr(query), _ptr(key), _ptr(value), _ptr(lens),
+                                       int(total_sequence_length), _ptr(cos), _ptr(sin), cos.shape[0],
+                                       _ptr(pk), _ptr(pv), Smax, _ptr(q_out))
+        return q_out, pk, pv
+
 
 _default = None
 
@@ -254,6 +287,10 @@ def mrope_apply(*a, **kw):
 
 def rope_apply_qk(*a, **kw):
     return default().rope_apply_qk(*a, **kw)
+
+
+def rope_kv_append(*a, **kw):
+    return default().rope_kv_append(*a, **kw)
 
 
 def table_for(workload, dtype=None):

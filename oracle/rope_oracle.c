@@ -132,12 +132,12 @@ static void store_elem(int dtype, void* p, int64_t idx, double v)
         ((uint16_t*)p)[idx] = oracle_f64_to_f16(v);
 }
 
-static void copy_elem(int dtype, const void* src, void* dst, int64_t idx)
+/* bit copy of element sidx of src to element didx of dst */
+static void copy_elem_to(int dtype, const void* src, int64_t sidx, void* dst,
+                         int64_t didx)
 {
-    if (dtype == ORACLE_F32)
-        memcpy((char*)dst + 4 * idx, (const char*)src + 4 * idx, 4);
-    else
-        memcpy((char*)dst + 2 * idx, (const char*)src + 2 * idx, 2);
+    size_t w = dtype == ORACLE_F32 ? 4 : 2;
+    memcpy((char*)dst + w * (size_t)didx, (const char*)src + w * (size_t)sidx, w);
 }
 
 /* rnd_T(v) as a double */
@@ -172,27 +172,36 @@ static int64_t row_offset(int rank, int64_t S, int64_t H, int64_t D,
  * ([RE] `rotary_embedding_dim`: only the leading R elements rotate, the
  * others are kept; [MRE] Description: a pair whose id is out of range is
  * kept as it was). */
-static void rotate_row(int dtype, const void* x, void* y, int64_t off,
-                       int64_t D, int64_t R, int64_t interleaved,
-                       const double* c, const double* s,
-                       const unsigned char* copy)
+static void rotate_row_to(int dtype, const void* x, int64_t xoff, void* y,
+                          int64_t yoff, int64_t D, int64_t R,
+                          int64_t interleaved, const double* c,
+                          const double* s, const unsigned char* copy)
 {
     int64_t half = R / 2;
     for (int64_t i = 0; i < half; ++i) {
         int64_t j1 = interleaved ? 2 * i : i;
         int64_t j2 = interleaved ? 2 * i + 1 : i + half;
         if (copy[i]) {
-            copy_elem(dtype, x, y, off + j1);
-            copy_elem(dtype, x, y, off + j2);
+            copy_elem_to(dtype, x, xoff + j1, y, yoff + j1);
+            copy_elem_to(dtype, x, xoff + j2, y, yoff + j2);
             continue;
         }
-        double x1 = load_elem(dtype, x, off + j1);
-        double x2 = load_elem(dtype, x, off + j2);
-        store_elem(dtype, y, off + j1, x1 * c[i] - x2 * s[i]);
-        store_elem(dtype, y, off + j2, x2 * c[i] + x1 * s[i]);
+        double x1 = load_elem(dtype, x, xoff + j1);
+        double x2 = load_elem(dtype, x, xoff + j2);
+        store_elem(dtype, y, yoff + j1, x1 * c[i] - x2 * s[i]);
+        store_elem(dtype, y, yoff + j2, x2 * c[i] + x1 * s[i]);
     }
     for (int64_t j = R; j < D; ++j)
-        copy_elem(dtype, x, y, off + j);
+        copy_elem_to(dtype, x, xoff + j, y, yoff + j);
+}
+
+/* The same row of x and y (y may be x). */
+static void rotate_row(int dtype, const void* x, void* y, int64_t off,
+                       int64_t D, int64_t R, int64_t interleaved,
+                       const double* c, const double* s,
+                       const unsigned char* copy)
+{
+    rotate_row_to(dtype, x, off, y, off, D, R, interleaved, c, s, copy);
 }
 
 typedef struct {
@@ -403,5 +412,78 @@ void oracle_rope_apply_qk(int dtype, int rank, int64_t B, int64_t S, int64_t H,
                 rotate_row(dtype, k, yk, row_offset(rank, S, Hk, D, b, h, s),
                            D, R, interleaved, cr.c, cr.s, cr.copy);
         }
+    coef_free(&cr);
+}
+
+/* ------------------------------------------------------------------------ */
+/* RoPE on Q and K and the key/value cache append: [SA] Description (the
+ * past/present caches share storage and are updated in place), Inputs
+ * (`query` plain or packed [Q|K|V], `past_key`/`past_value` of shape
+ * (B, Hk, Smax, D), `total_sequence_length`, `key_total_sequence_lengths`,
+ * `cos_cache`/`sin_cache` of width R/2), Attributes (`do_rotary`: Q and K are
+ * rotated before K enters the cache; `rotary_interleaved`; `kv_num_heads`).
+ *
+ * The page decides the past length from total_sequence_length alone: equal
+ * to S is the prompt, where every sequence starts at 0. Otherwise the
+ * per-batch total key length L[b] counts the past plus the S new tokens, so
+ * the past is L[b] - S (reading taken: new tokens follow the past directly).
+ * Token s of sequence b has position p = past + s: its pairs use table row p
+ * (an id outside [0, M) keeps the pair, as elsewhere in this file), its
+ * rotated Q row goes to q_out, its rotated K row and its V row go to row p of
+ * the caches (a row outside [0, Smax) is not written -- outside the contract,
+ * which bounds L[b] by total_sequence_length and that by the cache).
+ * key == NULL: query is packed, per token H query heads, then Hk key heads,
+ * then Hk value heads. */
+void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
+                           int64_t Hk, int64_t D, int64_t R,
+                           int64_t interleaved, const void* query,
+                           const void* key, const void* value,
+                           const int32_t* key_total_sequence_lengths,
+                           int64_t total_sequence_length,
+                           const void* cos_cache, const void* sin_cache,
+                           int64_t M, void* past_key, void* past_value,
+                           int64_t Smax, void* q_out)
+{
+    int64_t half = R / 2;
+    int packed = key == NULL;
+    int64_t qw = packed ? (H + 2 * Hk) * D : H * D; /* query row width */
+    int64_t kw = packed ? qw : Hk * D;
+    const void* ksrc = packed ? query : key;
+    const void* vsrc = packed ? query : value;
+    int64_t k0 = packed ? H * D : 0;            /* first key element of a token */
+    int64_t v0 = packed ? (H + Hk) * D : 0;
+    int prompt = total_sequence_length == S;
+    coef_row cr;
+    if (!coef_alloc(&cr, half))
+        abort();
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t past = prompt ? 0 : (int64_t)key_total_sequence_lengths[b] - S;
+        for (int64_t s = 0; s < S; ++s) {
+            int64_t p = past + s;
+            int in_range = p >= 0 && p < M;
+            for (int64_t i = 0; i < half; ++i) {
+                cr.copy[i] = (unsigned char)!in_range;
+                if (in_range) {
+                    cr.c[i] = load_elem(dtype, cos_cache, p * half + i);
+                    cr.s[i] = load_elem(dtype, sin_cache, p * half + i);
+                }
+            }
+            int64_t tok = b * S + s;
+            for (int64_t h = 0; h < H; ++h)
+                rotate_row_to(dtype, query, tok * qw + h * D, q_out,
+                              (tok * H + h) * D, D, R, interleaved, cr.c, cr.s,
+                              cr.copy);
+            if (p < 0 || p >= Smax)
+                continue;
+            for (int64_t h = 0; h < Hk; ++h) {
+                int64_t dst = ((b * Hk + h) * Smax + p) * D;
+                rotate_row_to(dtype, ksrc, tok * kw + k0 + h * D, past_key, dst,
+                              D, R, interleaved, cr.c, cr.s, cr.copy);
+                for (int64_t j = 0; j < D; ++j)
+                    copy_elem_to(dtype, vsrc, tok * kw + v0 + h * D + j,
+                                 past_value, dst + j);
+            }
+        }
+    }
     coef_free(&cr);
 }

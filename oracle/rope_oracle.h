@@ -115,6 +115,26 @@ void oracle_rope_apply_qk(int dtype, int rank, int64_t B, int64_t S, int64_t H,
                           const void* sin_cache, const int64_t* ids, int64_t M,
                           const float* inv_freq, float scaling);
 
+/* RoPE on Q and K plus the in-place key/value cache append of [SA]
+ * (Description, Inputs, Attributes). query is (B, S, H*D), or packed
+ * (B, S, (H + 2*Hk)*D) when key == value == NULL; key/value (B, S, Hk*D);
+ * past_key/past_value (B, Hk, Smax, D), updated in place; cos/sin (M, R/2);
+ * key_total_sequence_lengths (B,) int32; q_out (B, S, H*D).
+ * Prompt (total_sequence_length == S): past = 0; otherwise past =
+ * key_total_sequence_lengths[b] - S (reading taken). Token s has position
+ * p = past + s: Q and K rows rotated with table row p (p outside [0, M)
+ * keeps the pairs), Q to q_out, K and V (bit copy) to cache row p when
+ * 0 <= p < Smax (rows outside are not written). */
+void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
+                           int64_t Hk, int64_t D, int64_t R,
+                           int64_t interleaved, const void* query,
+                           const void* key, const void* value,
+                           const int32_t* key_total_sequence_lengths,
+                           int64_t total_sequence_length,
+                           const void* cos_cache, const void* sin_cache,
+                           int64_t M, void* past_key, void* past_value,
+                           int64_t Smax, void* q_out);
+
 #ifdef __cplusplus
 }
 #endif

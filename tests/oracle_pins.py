@@ -695,4 +695,123 @@ def pin_onthefly_equals_table(orc):
                 assert_bitwise(s, sin[p], "row %d sin" % p)
 
 
+# --------------------------------------------------------------------------
+# RoPE on Q and K with the key/value cache append (SparseAttention README)
+
+def _kv_positions(B, S, lens, total):
+    """past + s per token: 0-based in the prompt (total == S), else L[b] - S."""
+    past = np.zeros(B, np.int64) if total == S else lens.astype(np.int64) - S
+    return past[:, None] + np.arange(S, dtype=np.int64)[None, :]
+
+
+def _kv_expected(orc, q, k, v, pk, pv, lens, total, cos, sin, H, Hk, il):
+    """Expected outputs assembled with numpy scatters around the pinned
+    RotaryEmbedding oracle (rank 3, gathered rows = the token positions)."""
+    B, S, _ = q.shape
+    D = pk.shape[3]
+    Smax = pk.shape[2]
+    pos = _kv_positions(B, S, lens, total)
+    R = 2 * cos.shape[1]
+    q_out = orc.rope_apply(q, cos, sin, pos, interleaved=il, num_heads=H, rotary_embedding_dim=R if R != D else 0)
+    k_rot = orc.rope_apply(k, cos, sin, pos, interleaved=il, num_heads=Hk, rotary_embedding_dim=R if R != D else 0)
+    ek, ev = pk.copy(), pv.copy()
+    for b in range(B):
+        for s in range(S):
+            r = pos[b, s]
+            if 0 <= r < Smax:
+                ek[b, :, r, :] = k_rot[b, s].reshape(Hk, D)
+                ev[b, :, r, :] = v[b, s].reshape(Hk, D)
+    return q_out, ek, ev
+
+
+def pin_kv_append_probe(orc):
+    """Hand-checkable: every Q and K pair (1, 0) becomes (c, s) of table row
+    past + s, V lands unchanged in the same cache row, every other row keeps
+    its old value. Decode (total > S) and prompt (total == S)."""
+    for dt in (np.float32, np.float16, BF16):
+        B, S, H, Hk, D, Smax, M = 2, 2, 2, 1, 8, 7, 9
+        cos, sin = angle_table(201, M, D // 2, dt)
+        j1, j2 = pair_index(0, D // 2)
+        q = np.zeros((B, S, H, D), dt)
+        q[..., j1] = from_f64(1.0, dt)
+        k = np.zeros((B, S, Hk, D), dt)
+        k[..., j1] = from_f64(1.0, dt)
+        v = normal_any(202, (B, S, Hk * D), dt)
+        old = normal_any(203, (B, Hk, Smax, D), dt)
+        for lens, total, rows in (((3, 6), 6, ((1, 2), (4, 5))), ((2, 2), 2, ((0, 1), (0, 1)))):
+            qo, ko, vo = orc.rope_kv_append(q.reshape(B, S, -1), k.reshape(B, S, -1), v, old, old,
+                                            np.array(lens, np.int32), total, cos, sin, H, Hk)
+            for b in range(B):
+                for s in range(S):
+                    r = rows[b][s]
+                    for h in range(H):
+                        assert_bitwise(qo[b, s, h * D:(h + 1) * D][j1], cos[r], "q cos")
+                        assert_bitwise(qo[b, s, h * D:(h + 1) * D][j2], sin[r], "q sin")
+                    assert_bitwise(ko[b, 0, r][j1], cos[r], "k cos")
+                    assert_bitwise(ko[b, 0, r][j2], sin[r], "k sin")
+                    assert_bitwise(vo[b, 0, r], v[b, s], "v row")
+                untouched = [i for i in range(Smax) if i not in rows[b]]
+                assert_bitwise(ko[b, :, untouched], old[b, :, untouched], "k other rows")
+                assert_bitwise(vo[b, :, untouched], old[b, :, untouched], "v other rows")
+
+
+def pin_kv_append_equals_rope_and_scatter(orc):
+    for dt in (np.float32, np.float16, BF16):
+        for il in (0, 1):
+            for D, half in ((16, 8), (16, 4), (12, 2)):
+                B, S, H, Hk, Smax, M = 3, 4, 4, 2, 13, 20
+                q = normal_any(211, (B, S, H * D), dt)
+                k = normal_any(212, (B, S, Hk * D), dt)
+                v = normal_any(213, (B, S, Hk * D), dt)
+                pk = normal_any(214, (B, Hk, Smax, D), dt)
+                pv = normal_any(215, (B, Hk, Smax, D), dt)
+                cos, sin = angle_table(216, M, half, dt)
+                for lens, total in (((4, 9, 13), 13), ((4, 4, 4), 4), ((1, 3, 4), 4), ((5, 6, 7), 9)):
+                    lens = np.array(lens, np.int32)
+                    got = orc.rope_kv_append(q, k, v, pk, pv, lens, total, cos, sin, H, Hk, interleaved=il)
+                    want = _kv_expected(orc, q, k, v, pk, pv, lens, total, cos, sin, H, Hk, il)
+                    for g, w, what in zip(got, want, ("q_out", "present_key", "present_value")):
+                        assert_bitwise(g, w, "%s dt=%s il=%d D=%d lens=%s" % (what, np.dtype(dt).name, il, D,
+                                                                           lens.tolist()))
+
+
+def pin_kv_append_packed_equals_split(orc):
+    for dt in (np.float16, BF16):
+        B, S, H, Hk, D, Smax, M = 2, 3, 4, 2, 16, 9, 12
+        qkv = normal_any(221, (B, S, (H + 2 * Hk) * D), dt)
+        q = np.ascontiguousarray(qkv[..., :H * D])
+        k = np.ascontiguousarray(qkv[..., H * D:(H + Hk) * D])
+        v = np.ascontiguousarray(qkv[..., (H + Hk) * D:])
+        pk = normal_any(222, (B, Hk, Smax, D), dt)
+        cos, sin = angle_table(223, M, D // 2, dt)
+        lens = np.array([5, 9], np.int32)
+        a = orc.rope_kv_append(qkv, None, None, pk, pk, lens, 9, cos, sin, H, Hk)
+        b = orc.rope_kv_append(q, k, v, pk, pk, lens, 9, cos, sin, H, Hk)
+        for x, y in zip(a, b):
+            assert_bitwise(x, y, "packed vs split")
+
+
+def pin_kv_append_out_of_contract(orc):
+    """Rows outside the cache are not written; positions outside the table
+    keep their pairs (Q and K) -- the rule used for every gathered id."""
+    dt = np.float32
+    B, S, H, Hk, D, Smax, M = 3, 2, 2, 1, 8, 6, 5
+    q = normal_any(231, (B, S, H * D), dt)
+    k = normal_any(232, (B, S, Hk * D), dt)
+    v = normal_any(233, (B, S, Hk * D), dt)
+    pk = normal_any(234, (B, Hk, Smax, D), dt)
+    cos, sin = angle_table(235, M, D // 2, dt)
+    lens = np.array([7, 1, 6], np.int32)      # past 5 (rows 5, 6), past -1 (rows -1, 0), past 4 (rows 4, 5)
+    qo, ko, vo = orc.rope_kv_append(q, k, v, pk, pk, lens, 6, cos, sin, H, Hk)
+    assert_bitwise(qo[0, 0], q[0, 0], "position 5 >= M keeps Q")
+    assert_bitwise(qo[1, 0], q[1, 0], "position -1 keeps Q")
+    assert_bitwise(ko[0, 0, 5], k[0, 0], "row 5 holds K unrotated (position >= M)")
+    assert_bitwise(vo[0, 0, 5], v[0, 0], "row 5 holds V")
+    assert_bitwise(ko[1, 0, 0], orc.rope_apply(k, cos, sin, np.zeros((B, S), np.int64), num_heads=1)[1, 1],
+                   "row 0 of batch 1 holds K at position 0")
+    rest = [r for r in range(Smax) if r != 0]
+    assert_bitwise(ko[1, 0, rest], pk[1, 0, rest], "batch 1: row -1 not written")
+    assert_bitwise(ko[2, 0, :4], pk[2, 0, :4], "batch 2: rows below the past untouched")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

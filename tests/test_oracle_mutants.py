@@ -42,6 +42,15 @@ MUTANTS = {
     "bf16_fraction_bits": [("ldexp(r, 7 - E) - 128.0", "ldexp(r, 7 - E) - 127.0")],
     "bf16_stored_as_f16": [("((uint16_t*)p)[idx] = oracle_f64_to_bf16(v);",
                             "((uint16_t*)p)[idx] = oracle_f64_to_f16(v);")],
+    "kv_past_without_minus_s": [("(int64_t)key_total_sequence_lengths[b] - S;", "(int64_t)key_total_sequence_lengths[b];")],
+    "kv_prompt_ignored": [("int prompt = total_sequence_length == S;", "int prompt = 0;")],
+    "kv_cache_head_major_swapped": [("int64_t dst = ((b * Hk + h) * Smax + p) * D;",
+                                     "int64_t dst = ((h * B + b) * Smax + p) * D;")],
+    "kv_packed_key_value_swapped": [("int64_t k0 = packed ? H * D : 0;", "int64_t k0 = packed ? (H + Hk) * D : 0;"),
+                                    ("int64_t v0 = packed ? (H + Hk) * D : 0;", "int64_t v0 = packed ? H * D : 0;")],
+    "kv_row_bound_off_by_one": [("if (p < 0 || p >= Smax)", "if (p < 0 || p > Smax - 2)")],
+    "kv_value_not_written": [("                    copy_elem_to(dtype, vsrc, tok * kw + v0 + h * D + j,\n                                 past_value, dst + j);",
+                              "                    ;")],
     "inv_freq_exponent": [("-2.0 * (double)i / (double)rotary_dim", "-1.0 * (double)i / (double)rotary_dim")],
     "onthefly_uses_position_zero": [("coefficient(dtype, p, inv_freq[i], scaling, &cr.c[i], &cr.s[i]);",
                                      "coefficient(dtype, 0, inv_freq[i], scaling, &cr.c[i], &cr.s[i]);")],
