@@ -17,6 +17,10 @@
  *                      kv_num_heads, rotary on Q and on K).
  *   rope_apply_qkv_packed  the same on a packed [Q|K|V] activation --
  *                      "com.microsoft.SparseAttention" README (Inputs).
+ *   rope_kv_append     RoPE on Q and K with K and V appended to the key and
+ *                      value caches in place, one launch --
+ *                      "com.microsoft.SparseAttention" README (Description,
+ *                      Inputs, Outputs, Attributes).
  *   rope_inv_freq,     the frequency vector and the cos/sin table the
  *   rope_cos_sin_cache gathered ops read -- PR #27590 review item 4
  *                      (cos_cache = cos(pos * inv_freq) * scaling).
@@ -59,13 +63,14 @@ extern "C" {
 
 /* ONNX TensorProto element types. */
 #define ROPE_FLOAT 1
+#define ROPE_INT32 6
 #define ROPE_INT64 7
 #define ROPE_FLOAT16 10
 #define ROPE_BFLOAT16 16
 
 typedef struct rope_tensor {
     void* data;       /* device pointer, dense row-major */
-    int32_t dtype;    /* ROPE_FLOAT, ROPE_FLOAT16, ROPE_BFLOAT16 or ROPE_INT64 */
+    int32_t dtype;    /* ROPE_FLOAT, ROPE_FLOAT16, ROPE_BFLOAT16, ROPE_INT32, ROPE_INT64 */
     int32_t rank;     /* 1..4 */
     int64_t shape[4]; /* entries beyond `rank` are ignored */
 } rope_tensor;
@@ -199,6 +204,48 @@ int rope_apply_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
                           void* stream);
 
 /*
+ * rope_kv_append -- the rotary part of "com.microsoft.SparseAttention"
+ * (README Description: past and present key/value caches share storage and
+ * are updated in place; Attributes: do_rotary rotates Q and K before K enters
+ * the cache, rotary_interleaved, kv_num_heads): Q rotated to q_out, K rotated
+ * and V copied into the caches at each token's row, in one launch.
+ *
+ * query:        (B, S, H*D) of type T (float32, float16, bfloat16); or the
+ *               packed (B, S, (H + 2*Hk)*D) -- per token H query, Hk key,
+ *               Hk value heads -- when key and value are both NULL.
+ * key, value:   (B, S, Hk*D), type T, or both NULL (packed query).
+ * past_key, past_value: (B, Hk, Smax, D), type T; rows are written in place
+ *               (Outputs: present_key/present_value are these tensors).
+ * key_total_sequence_lengths: int32 (B,): per sequence, the total key length
+ *               after this call (past + new tokens, padding excluded).
+ * total_sequence_length: host value; S <= it <= Smax and <= M required.
+ *               Equal to S: the prompt, every sequence starts at position 0.
+ *               Otherwise token s of sequence b has position
+ *               key_total_sequence_lengths[b] - S + s (the README decides the
+ *               past length this way; new tokens follow the past directly).
+ * cos_cache, sin_cache: (M, R/2) of type T, R/2 >= 1, R <= D. Rotation as
+ *               rope_apply with these tables and those positions (R from the
+ *               table width, as the README's cos_cache shape states).
+ * q_out:        (B, S, H*D), type T; may be `query` itself when it is not
+ *               packed (in place). The caches may not overlap any input,
+ *               q_out or each other.
+ * rotary_interleaved: 0 half-split pairs, 1 adjacent pairs.
+ * num_heads, kv_num_heads: >= 1, kv_num_heads divides num_heads.
+ * Device data outside the README's bounds (a per-sequence length above
+ * total_sequence_length or below S): a row outside [0, Smax) is not written
+ * and a position outside [0, M) keeps its pairs; nothing is read or written
+ * out of bounds.
+ */
+int rope_kv_append(const rope_tensor* query, const rope_tensor* key,
+                   const rope_tensor* value, const rope_tensor* past_key,
+                   const rope_tensor* past_value,
+                   const rope_tensor* key_total_sequence_lengths,
+                   int64_t total_sequence_length, const rope_tensor* cos_cache,
+                   const rope_tensor* sin_cache, const rope_tensor* q_out,
+                   int64_t rotary_interleaved, int64_t num_heads,
+                   int64_t kv_num_heads, void* stream);
+
+/*
  * rope_inv_freq -- inv_freq[i] = rnd_f32(base^(-2i/R)) for i < R/2 with
  * R = 2 * dim 0 of inv_freq (float32, rank 1). The pages take inv_freq from
  * the model; this is the standard schedule. base must be > 0.
@@ -255,6 +302,17 @@ int rope_apply_qkv_packed_check(const rope_tensor* qkv,
                                 int64_t rotary_embedding_dim,
                                 const rope_tensor* inv_freq,
                                 float attention_scaling, const char** variant);
+
+int rope_kv_append_check(const rope_tensor* query, const rope_tensor* key,
+                         const rope_tensor* value, const rope_tensor* past_key,
+                         const rope_tensor* past_value,
+                         const rope_tensor* key_total_sequence_lengths,
+                         int64_t total_sequence_length,
+                         const rope_tensor* cos_cache,
+                         const rope_tensor* sin_cache,
+                         const rope_tensor* q_out, int64_t rotary_interleaved,
+                         int64_t num_heads, int64_t kv_num_heads,
+                         const char** variant);
 
 /*
  * Kernel choice for all ops: 0 = automatic (vector kernels where shapes and

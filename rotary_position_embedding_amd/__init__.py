@@ -17,16 +17,17 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import ROPE_BFLOAT16, ROPE_FLOAT, ROPE_FLOAT16, ROPE_INT64
+from ._lib import ROPE_BFLOAT16, ROPE_FLOAT, ROPE_FLOAT16, ROPE_INT32, ROPE_INT64
 
 __all__ = ["RopeError", "rope_apply", "mrope_apply", "rope_apply_qk", "rope_inv_freq",
            "rope_cos_sin_cache", "rope_apply_check", "mrope_apply_check",
            "rope_apply_qk_check", "set_kernel_policy", "library_path", "Launcher",
            "rope_apply_launcher", "mrope_apply_launcher", "rope_apply_qk_launcher",
-           "rope_apply_qkv_packed", "rope_apply_qkv_packed_check", "rope_apply_qkv_packed_launcher"]
+           "rope_apply_qkv_packed", "rope_apply_qkv_packed_check", "rope_apply_qkv_packed_launcher",
+           "rope_kv_append", "rope_kv_append_check", "rope_kv_append_launcher"]
 
 _DTYPE = {torch.float32: ROPE_FLOAT, torch.float16: ROPE_FLOAT16, torch.int64: ROPE_INT64,
-          torch.bfloat16: ROPE_BFLOAT16}
+          torch.bfloat16: ROPE_BFLOAT16, torch.int32: ROPE_INT32}
 
 library_path = _lib.LIB_PATH
 
@@ -172,6 +173,55 @@ def rope_apply_qkv_packed_launcher(qkv, cos_cache, sin_cache, position_ids, out,
                                             _lib.ref(ds[5]), attention_scaling, _stream(dev)]
     return Launcher(_lib.load().rope_apply_qkv_packed, args,
                     (ds, qkv, cos_cache, sin_cache, position_ids, out, inv_freq))
+
+
+def rope_kv_append(query, key, value, past_key, past_value, key_total_sequence_lengths,
+                   total_sequence_length, cos_cache, sin_cache, *, num_heads, kv_num_heads,
+                   rotary_interleaved=0, out=None):
+    """RoPE on Q and K with K and V appended to the caches in place (the
+    SparseAttention rotary inputs). key = value = None: query is packed
+    [Q|K|V]. Returns q_out ((B, S, H*D): a new tensor, or `out`, which may be
+    an unpacked query); past_key and past_value are updated in place."""
+    dev = _device_of(query)
+    if out is None:
+        B, S = query.shape[0], query.shape[1]
+        width = query.shape[2]
+        groups = num_heads + (2 * kv_num_heads if key is None else 0)
+        out = torch.empty(B, S, width // groups * num_heads if groups else 0, dtype=query.dtype, device=dev)
+    ds = [_desc(t, dev) for t in (query, key, value, past_key, past_value, key_total_sequence_lengths,
+                                  cos_cache, sin_cache, out)]
+    with _on_device(dev):
+        _check(_lib.load().rope_kv_append(*[_lib.ref(d) for d in ds[:6]], int(total_sequence_length),
+                                          *[_lib.ref(d) for d in ds[6:]], rotary_interleaved, num_heads,
+                                          kv_num_heads, _stream(dev)))
+    return out
+
+
+def rope_kv_append_check(query, key, value, past_key, past_value, key_total_sequence_lengths,
+                         total_sequence_length, cos_cache, sin_cache, q_out, *, num_heads,
+                         kv_num_heads, rotary_interleaved=0):
+    v = _variant_out()
+    refs = [_lib.ref(d) for d in (query, key, value, past_key, past_value, key_total_sequence_lengths)]
+    rc = _lib.load().rope_kv_append_check(*refs, int(total_sequence_length), _lib.ref(cos_cache),
+                                          _lib.ref(sin_cache), _lib.ref(q_out), rotary_interleaved,
+                                          num_heads, kv_num_heads, ctypes.byref(v))
+    return rc, (v.value.decode() if rc == 0 and v.value else None)
+
+
+def rope_kv_append_launcher(query, key, value, past_key, past_value, key_total_sequence_lengths,
+                            total_sequence_length, cos_cache, sin_cache, out, *, num_heads,
+                            kv_num_heads, rotary_interleaved=0):
+    dev = _device_of(query)
+    ds = [_desc(t, dev) for t in (query, key, value, past_key, past_value, key_total_sequence_lengths,
+                                  cos_cache, sin_cache, out)]
+    rc, _ = rope_kv_append_check(*ds[:6], total_sequence_length, *ds[6:], num_heads=num_heads,
+                                 kv_num_heads=kv_num_heads, rotary_interleaved=rotary_interleaved)
+    _check(rc)
+    args = [_lib.ref(d) for d in ds[:6]] + [int(total_sequence_length)] + [_lib.ref(d) for d in ds[6:]] + \
+        [rotary_interleaved, num_heads, kv_num_heads, _stream(dev)]
+    return Launcher(_lib.load().rope_kv_append, args,
+                    (ds, query, key, value, past_key, past_value, key_total_sequence_lengths, cos_cache,
+                     sin_cache, out))
 
 
 def rope_inv_freq(rotary_dim, base, device="cuda", out=None):

@@ -10,6 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librope_mi355x.so")
 
 ROPE_FLOAT = 1
+ROPE_INT32 = 6
 ROPE_INT64 = 7
 ROPE_FLOAT16 = 10
 ROPE_BFLOAT16 = 16
@@ -46,6 +47,8 @@ SIGNATURES = {
     "rope_set_kernel_policy": ([_int], _int),
     "rope_apply_qkv_packed": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _vp], _int),
     "rope_apply_qkv_packed_check": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _ccp], _int),
+    "rope_kv_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp], _int),
+    "rope_kv_append_check": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _ccp], _int),
 }
 
 _lib = None

@@ -47,7 +47,9 @@ struct KTask {
     int64_t wave_begin;    // first wave of this task (vector kernel)
     int64_t item_begin;    // first thread item of this task (scalar kernel)
     int32_t heads, hpw, chunks, tile;  // tile: token groups per head chunk in a wave tile
-    int32_t copy, pad;     // copy: pass every element through (no rotation)
+    int32_t copy;          // copy: pass every element through (no rotation)
+    int32_t yrow;          // append kind: y row is the token's position
+    int64_t ysb, ysh, yss; // append kind: element strides of y (b, h, row)
 };
 
 struct KArgs {
@@ -58,8 +60,10 @@ struct KArgs {
     const int64_t* ids;
     const float* inv_freq;
     int32_t ntask, W, NP, TG, P, R, D, interleaved;
-    int32_t xcd_remap, pad2;
+    int32_t xcd_remap, prompt;  // prompt: append kind, every sequence starts at 0
     float scaling, scale;
+    const int32_t* seqlens;     // append kind: total key length per sequence
+    int64_t rows_out;           // append kind: cache rows
     uint32_t sel[kSelWords];
 };
 
@@ -148,6 +152,15 @@ __device__ inline int mrope_stream(const KArgs& a, int i) {
     return (a.sel[i >> 4] >> (2 * (i & 15))) & 3;
 }
 
+// Cache append: token n = b*S + s has position past(b) + s, past = 0 in the
+// prompt and the sequence's total key length minus S otherwise.
+__device__ inline int64_t append_position(const KArgs& a, int64_t n) {
+    const int64_t b = n / a.S;
+    const int64_t s = n - b * a.S;
+    const int64_t past = a.prompt ? 0 : (int64_t)a.seqlens[b] - a.S;
+    return past + s;
+}
+
 // Coefficient (c, s) of slot i for token n, or copy = true.
 template <typename T, int COEF>
 __device__ inline void coef_slot(const KArgs& a, int64_t n, int i, float& c, float& s, bool& copy) {
@@ -164,6 +177,11 @@ __device__ inline void coef_slot(const KArgs& a, int64_t n, int i, float& c, flo
     } else if (COEF == kCoefPerToken) {
         c = to_f(cos_t[n * a.P + i]);
         s = to_f(sin_t[n * a.P + i]);
+    } else if (COEF == kCoefAppend) {
+        const int64_t p = append_position(a, n);
+        if (p < 0 || p >= a.M) { copy = true; return; }
+        c = to_f(cos_t[p * a.P + i]);
+        s = to_f(sin_t[p * a.P + i]);
     } else if (COEF == kCoefMrope) {
         const int64_t p = a.ids[(int64_t)mrope_stream(a, i) * a.ntok + n];
         if (p < 0 || p >= a.M) { copy = true; return; }
@@ -178,7 +196,8 @@ struct TaskView {
     const char* x;
     char* y;
     int64_t sb, sh, ss, wave_begin, item_begin;
-    int32_t heads, hpw, chunks, tile, copy;
+    int32_t heads, hpw, chunks, tile, copy, yrow;
+    int64_t ysb, ysh, yss;
 };
 
 // An SGPR value the compiler must treat as opaque: keeps a select of two
@@ -191,7 +210,9 @@ __device__ inline V opaque_s(V v) {
 }
 
 // Task i (0..2) of the launch: every task's fields are read in the first
-// batch of scalar loads and the values are selected.
+// batch of scalar loads and the values are selected. The output geometry is
+// the input's except for the append kind.
+template <int COEF>
 __device__ inline TaskView task_of(const KArgs& a, int i) {
 #define ROPE_PICK(f)                                                                      \
     do {                                                                                  \
@@ -211,6 +232,17 @@ __device__ inline TaskView task_of(const KArgs& a, int i) {
     ROPE_PICK(chunks);
     ROPE_PICK(tile);
     ROPE_PICK(copy);
+    if (COEF == kCoefAppend) {
+        ROPE_PICK(yrow);
+        ROPE_PICK(ysb);
+        ROPE_PICK(ysh);
+        ROPE_PICK(yss);
+    } else {
+        v.yrow = 0;
+        v.ysb = v.sb;
+        v.ysh = v.sh;
+        v.yss = v.ss;
+    }
 #undef ROPE_PICK
     return v;
 }
@@ -287,7 +319,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     // task selection and its fields in scalar registers
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + wave_in_block;
-    const TaskView tk = task_of(a, task_index(a, gw));
+    const TaskView tk = task_of<COEF>(a, task_index(a, gw));
     const int64_t local = gw - tk.wave_begin;
     const int64_t per_tile = (int64_t)tk.tile * tk.chunks;
     const int64_t tile = local / per_tile;
@@ -299,12 +331,16 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     const int h_begin = hc * tk.hpw;
     const int h_end = min(tk.heads, h_begin + tk.hpw);
     const int64_t sh_bytes = tk.sh * ES;
+    const int64_t ysh_bytes = tk.ysh * ES;
     const int64_t half_bytes = (int64_t)a.P * ES;
 
-    // -- items of this lane (no memory traffic) -----------------------------
+    // -- items of this lane (no memory traffic but the append kind's lengths)
     bool act[IPL], rot[IPL];
     int64_t off[IPL];    // byte offset of the item's first chunk for head 0
+    int64_t yoff[IPL];   // the same in y
+    bool wr[IPL];        // the item's output row exists
     int64_t tok[IPL];
+    int64_t apos[IPL];   // append kind: the token's position
     int slot0[IPL];
 #pragma unroll
     for (int m = 0; m < IPL; ++m) {
@@ -320,6 +356,18 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         const int64_t e0 = w < a.NP ? (int64_t)w * E : (int64_t)a.R + (int64_t)(w - a.NP) * E;
         off[m] = act[m] ? (b * tk.sb + s * tk.ss + e0) * ES : 0;
         slot0[m] = rot[m] ? w * CE : 0;  // non-rotation items read slot 0 (unused)
+        if (COEF == kCoefAppend) {
+            // the lengths are read for every item (sequence 0 for inactive ones)
+            const int64_t past = a.prompt ? 0 : (int64_t)a.seqlens[b] - a.S;
+            apos[m] = past + s;
+            const int64_t row = tk.yrow ? apos[m] : s;
+            wr[m] = act[m] && (!tk.yrow || (row >= 0 && row < a.rows_out));
+            yoff[m] = wr[m] ? (b * tk.ysb + row * tk.yss + e0) * ES : 0;
+        } else {
+            apos[m] = 0;
+            wr[m] = act[m];
+            yoff[m] = off[m];
+        }
     }
 
     // -- position ids, then X, then the dependent table reads --------------
@@ -329,6 +377,9 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     if (COEF == kCoefGather || COEF == kCoefOnTheFly) {
 #pragma unroll
         for (int m = 0; m < IPL; ++m) pos[m][0] = a.ids[tok[m]];
+    } else if (COEF == kCoefAppend) {
+#pragma unroll
+        for (int m = 0; m < IPL; ++m) pos[m][0] = apos[m];
     } else if (COEF == kCoefMrope) {
 #pragma unroll
         for (int m = 0; m < IPL; ++m)
@@ -356,11 +407,11 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
             keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
             continue;
         }
-        if (COEF == kCoefGather || COEF == kCoefPerToken) {
+        if (COEF == kCoefGather || COEF == kCoefPerToken || COEF == kCoefAppend) {
             // the row is read unconditionally: an out-of-range id reads row 0
             // (with an empty table the host points the table at valid memory)
             // and the pair is then copied
-            const int64_t row = COEF == kCoefGather ? pos[m][0] : tok[m];
+            const int64_t row = COEF == kCoefPerToken ? tok[m] : pos[m][0];
             const bool valid = COEF == kCoefPerToken || (row >= 0 && row < a.M);
             const int64_t e = ((valid ? row : 0) * a.P + slot0[m]) * ES;
             const cvec cv = *reinterpret_cast<const cvec*>(a.cos + e);
@@ -442,8 +493,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         for (int u = 0; u < HU; ++u) {
 #pragma unroll
             for (int m = 0; m < IPL; ++m) {
-                if (!(act[m] && h + u < h_end)) continue;
-                u32x4* py = reinterpret_cast<u32x4*>(tk.y + off[m] + (int64_t)(h + u) * sh_bytes);
+                if (!(wr[m] && h + u < h_end)) continue;
+                u32x4* py = reinterpret_cast<u32x4*>(tk.y + yoff[m] + (int64_t)(h + u) * ysh_bytes);
                 if (!rot[m]) {
                     __builtin_nontemporal_store(in1[u][m], py);
                     continue;
@@ -460,7 +511,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         r[2 * j + 1] = fmaf(x2, c, x1 * s);
                     }
                     u32x4 o = chunk_pack<T>(r);
-                    if (COEF == kCoefGather || COEF == kCoefMrope || tk.copy)
+                    if (COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy)
                         o = select_bits(keep[m], in1[u][m], o);
                     __builtin_nontemporal_store(o, py);
                 } else {
@@ -477,7 +528,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     }
                     u32x4 o1 = chunk_pack<T>(r1);
                     u32x4 o2 = chunk_pack<T>(r2);
-                    if (COEF == kCoefGather || COEF == kCoefMrope || tk.copy) {
+                    if (COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy) {
                         o1 = select_bits(keep[m], in1[u][m], o1);
                         o2 = select_bits(keep[m], in2[u][m], o2);
                     }
@@ -500,7 +551,7 @@ __global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int6
     const int64_t K = a.P + (a.D - a.R);
     for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * kBlock) {
-        const TaskView tk = task_of(a, task_index_items(a, idx));
+        const TaskView tk = task_of<COEF>(a, task_index_items(a, idx));
         const int64_t local = idx - tk.item_begin;
         const int64_t k = local % K;
         const int64_t rest = local / K;
@@ -509,8 +560,14 @@ __global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int6
         const int64_t b = n / a.S;
         const int64_t s = n - b * a.S;
         const int64_t base = b * tk.sb + h * tk.sh + s * tk.ss;
+        int64_t ybase = base;
+        if (COEF == kCoefAppend) {
+            const int64_t row = tk.yrow ? append_position(a, n) : s;
+            if (tk.yrow && (row < 0 || row >= a.rows_out)) continue;  // no such cache row
+            ybase = b * tk.ysb + h * tk.ysh + row * tk.yss;
+        }
         const B* xb = reinterpret_cast<const B*>(tk.x) + base;
-        B* yb = reinterpret_cast<B*>(tk.y) + base;
+        B* yb = reinterpret_cast<B*>(tk.y) + ybase;
         if (k >= a.P) {
             const int64_t j = a.R + (k - a.P);
             yb[j] = xb[j];
@@ -597,6 +654,7 @@ static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, d
         case kCoefGather: return launch_vec_ipl<T, IL, kCoefGather>(a, ipl, hu, grid, st);
         case kCoefPerToken: return launch_vec_ipl<T, IL, kCoefPerToken>(a, ipl, hu, grid, st);
         case kCoefMrope: return launch_vec_ipl<T, IL, kCoefMrope>(a, ipl, hu, grid, st);
+        case kCoefAppend: return launch_vec_ipl<T, IL, kCoefAppend>(a, ipl, hu, grid, st);
         default: return launch_vec_ipl<T, IL, kCoefOnTheFly>(a, ipl, hu, grid, st);
     }
 }
@@ -612,6 +670,7 @@ static hipError_t launch_scalar(const KArgs& a, CoefKind c, int64_t total, hipSt
         case kCoefGather: fn = (const void*)rope_scalar_kernel<T, kCoefGather>; break;
         case kCoefPerToken: fn = (const void*)rope_scalar_kernel<T, kCoefPerToken>; break;
         case kCoefMrope: fn = (const void*)rope_scalar_kernel<T, kCoefMrope>; break;
+        case kCoefAppend: fn = (const void*)rope_scalar_kernel<T, kCoefAppend>; break;
         default: fn = (const void*)rope_scalar_kernel<T, kCoefOnTheFly>; break;
     }
     return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0, st);
@@ -640,6 +699,10 @@ int launch_plan(const Plan& pl, void* stream) {
         a.t[t].ss = p.task[t].stride_s;
         a.t[t].heads = (int32_t)p.task[t].heads;
         a.t[t].copy = p.task[t].copy;
+        a.t[t].yrow = p.task[t].yrow;
+        a.t[t].ysb = p.task[t].ystride_b;
+        a.t[t].ysh = p.task[t].ystride_h;
+        a.t[t].yss = p.task[t].ystride_s;
         const int64_t items = p.B * p.S * p.task[t].heads * K;
         if (items > 0) {  // an empty task keeps INT64_MAX and is never selected
             a.t[t].item_begin = item_begin;
@@ -680,6 +743,9 @@ int launch_plan(const Plan& pl, void* stream) {
     a.xcd_remap = g.xcd_remap;
     a.scaling = p.scaling;
     a.scale = p.scale;
+    a.seqlens = p.seqlens;
+    a.prompt = p.prompt;
+    a.rows_out = p.rows_out;
     for (int i = 0; i < kSelWords; ++i) a.sel[i] = p.sel[i];
 
     hipError_t e;

@@ -50,6 +50,7 @@ static int elem_size(int32_t dtype) {
         case ROPE_FLOAT: return 4;
         case ROPE_FLOAT16: return 2;
         case ROPE_BFLOAT16: return 2;
+        case ROPE_INT32: return 4;
         case ROPE_INT64: return 8;
         default: return 0;
     }
@@ -144,9 +145,9 @@ void mrope_streams(int64_t half, const int64_t section[3], int64_t layout,
 // kernel choice
 
 static const char* variant_name(bool vec, CoefKind c) {
-    static const char* names[2][4] = {
-        {"scalar/gather", "scalar/per_token", "scalar/mrope", "scalar/on_the_fly"},
-        {"vec16/gather", "vec16/per_token", "vec16/mrope", "vec16/on_the_fly"}};
+    static const char* names[2][5] = {
+        {"scalar/gather", "scalar/per_token", "scalar/mrope", "scalar/on_the_fly", "scalar/append"},
+        {"vec16/gather", "vec16/per_token", "vec16/mrope", "vec16/on_the_fly", "vec16/append"}};
     return names[vec ? 1 : 0][(int)c];
 }
 
@@ -174,7 +175,7 @@ static void choose_geometry(Plan* pl) {
     ok = ok && p.D % E == 0 && p.R % E == 0 && (p.interleaved || half % E == 0);
     for (int t = 0; t < p.ntask; ++t)
         ok = ok && aligned16(p.task[t].x) && aligned16(p.task[t].y);
-    if (p.coef == kCoefGather || p.coef == kCoefPerToken || p.coef == kCoefMrope)
+    if (p.coef != kCoefOnTheFly)
         ok = ok && aligned16(p.cos) && aligned16(p.sin);
     const int64_t NP = p.interleaved ? p.R / E : half / E;
     const int64_t NT = (p.D - p.R) / E;
@@ -255,6 +256,9 @@ static void fill_strides(Task* t, int rank, int64_t S, int64_t H, int64_t D) {
         t->stride_s = H * D;
         t->stride_h = D;
     }
+    t->ystride_b = t->stride_b;
+    t->ystride_h = t->stride_h;
+    t->ystride_s = t->stride_s;
 }
 
 // (B, S, H, D) of a rank-3 or rank-4 activation.
@@ -721,6 +725,156 @@ int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
     }
     out->empty = numel(qkv) == 0;
     out->g.rank = qkv->rank;
+    choose_geometry(out);
+    return ROPE_OK;
+}
+
+// RoPE on Q and K with the key/value cache append: the SparseAttention
+// README's inputs (query plain or packed, past_key/past_value updated in
+// place, total_sequence_length, key_total_sequence_lengths, cos/sin caches)
+// and attributes (rotary_interleaved, num_heads, kv_num_heads).
+int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
+                        const rope_tensor* value, const rope_tensor* past_key,
+                        const rope_tensor* past_value,
+                        const rope_tensor* key_total_sequence_lengths,
+                        int64_t total_sequence_length, const rope_tensor* cos_cache,
+                        const rope_tensor* sin_cache, const rope_tensor* q_out,
+                        int64_t interleaved, int64_t num_heads, int64_t kv_num_heads,
+                        Plan* out) {
+    clear_error();
+    memset(out, 0, sizeof(*out));
+    if (!query) return fail(ROPE_ERR_NULL, "query is missing");
+    if ((key == nullptr) != (value == nullptr))
+        return fail(ROPE_ERR_NULL, "key and value must both be given or both be NULL (packed query)");
+    if (!past_key) return fail(ROPE_ERR_NULL, "past_key is missing");
+    if (!past_value) return fail(ROPE_ERR_NULL, "past_value is missing");
+    if (!key_total_sequence_lengths) return fail(ROPE_ERR_NULL, "key_total_sequence_lengths is missing");
+    if (!cos_cache) return fail(ROPE_ERR_NULL, "cos_cache is missing");
+    if (!sin_cache) return fail(ROPE_ERR_NULL, "sin_cache is missing");
+    if (!q_out) return fail(ROPE_ERR_NULL, "q_out is missing");
+    const bool packed = key == nullptr;
+    TRY(check_desc(query, "query"));
+    if (!packed) {
+        TRY(check_desc(key, "key"));
+        TRY(check_desc(value, "value"));
+    }
+    TRY(check_desc(past_key, "past_key"));
+    TRY(check_desc(past_value, "past_value"));
+    TRY(check_desc(key_total_sequence_lengths, "key_total_sequence_lengths"));
+    TRY(check_desc(cos_cache, "cos_cache"));
+    TRY(check_desc(sin_cache, "sin_cache"));
+    TRY(check_desc(q_out, "q_out"));
+
+    const int32_t T = query->dtype;
+    if (!is_float(T)) return fail(ROPE_ERR_DTYPE, "query must be float32, float16 or bfloat16");
+    if ((!packed && (key->dtype != T || value->dtype != T)) || past_key->dtype != T ||
+        past_value->dtype != T || cos_cache->dtype != T || sin_cache->dtype != T || q_out->dtype != T)
+        return fail(ROPE_ERR_DTYPE, "key, value, caches, tables and q_out must have the type of query");
+    if (key_total_sequence_lengths->dtype != ROPE_INT32)
+        return fail(ROPE_ERR_DTYPE, "key_total_sequence_lengths must be int32");
+    if (interleaved != 0 && interleaved != 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "rotary_interleaved must be 0 or 1");
+    if (num_heads < 1 || kv_num_heads < 1)
+        return fail(ROPE_ERR_ATTRIBUTE, "num_heads and kv_num_heads are required (>= 1)");
+    if (num_heads % kv_num_heads != 0)
+        return fail(ROPE_ERR_SHAPE, "kv_num_heads %lld must divide num_heads %lld",
+                    (long long)kv_num_heads, (long long)num_heads);
+
+    if (query->rank != 3) return fail(ROPE_ERR_RANK, "query must be rank 3 (batch, sequence, hidden)");
+    const int64_t B = query->shape[0], S = query->shape[1];
+    const int64_t groups = packed ? num_heads + 2 * kv_num_heads : num_heads;
+    if (query->shape[2] % groups != 0)
+        return fail(ROPE_ERR_SHAPE, "query width %lld is not %s * head_size", (long long)query->shape[2],
+                    packed ? "(num_heads + 2*kv_num_heads)" : "num_heads");
+    const int64_t D = query->shape[2] / groups;
+    if (D % 2 != 0) return fail(ROPE_ERR_SHAPE, "head_size %lld must be even", (long long)D);
+    if (!packed) {
+        if (key->rank != 3 || value->rank != 3) return fail(ROPE_ERR_RANK, "key and value must be rank 3");
+        if (key->shape[0] != B || key->shape[1] != S || key->shape[2] != kv_num_heads * D)
+            return fail(ROPE_ERR_SHAPE, "key must be (%lld, %lld, %lld)", (long long)B, (long long)S,
+                        (long long)(kv_num_heads * D));
+        if (!same_shape(key, value)) return fail(ROPE_ERR_SHAPE, "value must have the shape of key");
+    }
+    if (past_key->rank != 4) return fail(ROPE_ERR_RANK, "past_key must be rank 4 (batch, kv_num_heads, max_sequence, head_size)");
+    if (past_key->shape[0] != B || past_key->shape[1] != kv_num_heads || past_key->shape[3] != D)
+        return fail(ROPE_ERR_SHAPE, "past_key must be (%lld, %lld, max_sequence, %lld)", (long long)B,
+                    (long long)kv_num_heads, (long long)D);
+    if (!same_shape(past_key, past_value)) return fail(ROPE_ERR_SHAPE, "past_value must have the shape of past_key");
+    const int64_t Smax = past_key->shape[2];
+    if (key_total_sequence_lengths->rank != 1 || key_total_sequence_lengths->shape[0] != B)
+        return fail(ROPE_ERR_SHAPE, "key_total_sequence_lengths must be (batch,) = (%lld,)", (long long)B);
+    if (cos_cache->rank != 2) return fail(ROPE_ERR_RANK, "cos_cache must be rank 2 (rows, rotary_dim/2)");
+    if (!same_shape(cos_cache, sin_cache)) return fail(ROPE_ERR_SHAPE, "sin_cache must have the shape of cos_cache");
+    const int64_t R = 2 * cos_cache->shape[1];
+    const int64_t M = cos_cache->shape[0];
+    if (R < 2 || R > D)
+        return fail(ROPE_ERR_SHAPE, "cos_cache width %lld must be in [1, head_size/2 = %lld]",
+                    (long long)cos_cache->shape[1], (long long)(D / 2));
+    if (q_out->rank != 3 || q_out->shape[0] != B || q_out->shape[1] != S || q_out->shape[2] != num_heads * D)
+        return fail(ROPE_ERR_SHAPE, "q_out must be (%lld, %lld, %lld)", (long long)B, (long long)S,
+                    (long long)(num_heads * D));
+    if (total_sequence_length < S || total_sequence_length > Smax || total_sequence_length > M)
+        return fail(ROPE_ERR_SHAPE,
+                    "total_sequence_length %lld must lie in [sequence %lld, min(cache rows %lld, table rows %lld)]",
+                    (long long)total_sequence_length, (long long)S, (long long)Smax, (long long)M);
+
+    // aliasing: q_out may be the (unpacked) query itself; the caches are
+    // written in place and overlap nothing else
+    const rope_tensor* ins[6] = {key, value, cos_cache, sin_cache, key_total_sequence_lengths,
+                                 packed ? query : nullptr};
+    const char* in_names[6] = {"key", "value", "cos_cache", "sin_cache", "key_total_sequence_lengths", "query"};
+    TRY(check_output(q_out, "q_out", packed ? nullptr : query, ins, in_names, 6));
+    const rope_tensor* all[8] = {query, key, value, cos_cache, sin_cache, key_total_sequence_lengths, q_out,
+                                 past_value};
+    const char* all_names[8] = {"query", "key", "value", "cos_cache", "sin_cache",
+                                "key_total_sequence_lengths", "q_out", "past_value"};
+    TRY(check_output(past_key, "past_key", nullptr, all, all_names, 8));
+    TRY(check_output(past_value, "past_value", nullptr, all, all_names, 7));
+
+    Problem& p = out->p;
+    p.dtype = T;
+    p.interleaved = (int32_t)interleaved;
+    p.B = B; p.S = S; p.D = D; p.R = R;
+    const int es = elem_size(T);
+    const int64_t Hall = packed ? num_heads + 2 * kv_num_heads : num_heads;
+    p.ntask = 3;
+    // Q: rows of the query (packed or not) to the dense q_out
+    fill_strides(&p.task[0], 3, S, Hall, D);
+    p.task[0].heads = num_heads;
+    p.task[0].x = query->data;
+    p.task[0].y = q_out->data;
+    p.task[0].ystride_b = S * num_heads * D;
+    p.task[0].ystride_s = num_heads * D;
+    p.task[0].ystride_h = D;
+    // K (rotated) and V (copied) to row `position` of the caches
+    for (int t = 1; t < 3; ++t) {
+        Task& k = p.task[t];
+        if (packed) {
+            fill_strides(&k, 3, S, Hall, D);
+            k.x = (const char*)query->data + (t == 1 ? num_heads : num_heads + kv_num_heads) * D * es;
+        } else {
+            fill_strides(&k, 3, S, kv_num_heads, D);
+            k.x = t == 1 ? key->data : value->data;
+        }
+        k.heads = kv_num_heads;
+        k.y = t == 1 ? past_key->data : past_value->data;
+        k.ystride_b = kv_num_heads * Smax * D;
+        k.ystride_h = Smax * D;
+        k.ystride_s = D;
+        k.yrow = 1;
+        k.copy = t == 2;
+    }
+    p.coef = kCoefAppend;
+    p.cos = cos_cache->data;
+    p.sin = sin_cache->data;
+    p.M = M;
+    p.seqlens = (const int32_t*)key_total_sequence_lengths->data;
+    p.prompt = total_sequence_length == S;
+    p.rows_out = Smax;
+    p.scale = 1.0f;
+    p.scaling = 1.0f;
+    out->empty = B * S == 0;
+    out->g.rank = 3;
     choose_geometry(out);
     return ROPE_OK;
 }

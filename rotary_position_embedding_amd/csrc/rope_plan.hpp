@@ -15,7 +15,9 @@ enum CoefKind : int32_t {
     kCoefGather = 0,   // row ids[b,s] of an (M, R/2) table, id outside [0,M) -> copy
     kCoefPerToken = 1, // row b*S+s of a (B, S, R/2) table
     kCoefMrope = 2,    // slot i from row ids[stream(i), b, s], scaled, per-pair copy
-    kCoefOnTheFly = 3  // computed from inv_freq and the position
+    kCoefOnTheFly = 3, // computed from inv_freq and the position
+    kCoefAppend = 4    // row past(b) + s of an (M, R/2) table; outputs may go to
+                       // cache row past(b) + s (key/value cache append)
 };
 
 constexpr int kMaxMropeHalf = 512;             // slots the stream table can hold
@@ -28,7 +30,11 @@ struct Task {
     void* y;
     int64_t heads;
     int64_t stride_b, stride_h, stride_s;  // element strides of x(b, h, s, 0)
+    // element strides of y(b, h, row, 0); row = s, or with yrow set (append
+    // kind only) the token's position. Equal to the x strides unless set.
+    int64_t ystride_b, ystride_h, ystride_s;
     int32_t copy;
+    int32_t yrow;
 };
 
 constexpr int kMaxPlanTasks = 3;
@@ -48,6 +54,10 @@ struct Problem {
     float scaling;        // on-the-fly attention scaling
     float scale;          // M-RoPE coefficient scale
     uint32_t sel[kSelWords];  // M-RoPE stream of slot i in bits 2*(i%16) of word i/16
+    // cache append: per-sequence total lengths, prompt flag, cache rows
+    const int32_t* seqlens;
+    int32_t prompt;
+    int64_t rows_out;
 };
 
 // Launch geometry of the vector kernel (see rope_kernels.hip for the mapping).
@@ -98,6 +108,15 @@ int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
                          const rope_tensor* y, int64_t interleaved, int64_t num_heads,
                          int64_t kv_num_heads, int64_t rotary_embedding_dim,
                          const rope_tensor* inv_freq, float attention_scaling, Plan* out);
+
+int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
+                        const rope_tensor* value, const rope_tensor* past_key,
+                        const rope_tensor* past_value,
+                        const rope_tensor* key_total_sequence_lengths,
+                        int64_t total_sequence_length, const rope_tensor* cos_cache,
+                        const rope_tensor* sin_cache, const rope_tensor* q_out,
+                        int64_t interleaved, int64_t num_heads, int64_t kv_num_heads,
+                        Plan* out);
 
 struct TablePlan {
     const float* inv_freq;

@@ -1,0 +1,31 @@
+"""numpy <-> device tensors for the GPU tests (uint16 arrays are bfloat16 bits)."""
+import numpy as np
+import torch
+
+from rope_inputs import BFLOAT16, bfloat16_bits
+
+DEV = "cuda:0"
+
+
+def cuda(a):
+    """numpy -> device tensor; uint16 arrays are bfloat16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == BFLOAT16:
+        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def torch_dtype(dt):
+    return {np.dtype(np.float16): torch.float16, np.dtype(np.float32): torch.float32,
+            np.dtype(BFLOAT16): torch.bfloat16}[np.dtype(dt)]
+
+
+def one(dt):
+    return bfloat16_bits(1.0) if np.dtype(dt) == BFLOAT16 else 1

@@ -464,3 +464,108 @@ def test_packed_clauses():
     assert check_packed(kw)[0] == ALIAS            # shifted output
     kw = packed_case(table=False, position_ids=None)
     assert check_packed(kw)[0] == NULL
+
+
+# ---------------------------------------------------------------------------
+# RoPE on Q and K with the key/value cache append
+
+I32 = 6
+
+
+def kv_case(dt=F16, B=2, S=3, H=8, Hk=2, D=16, Smax=40, M=64, width=None, packed=False,
+            inplace=False, total=20, **over):
+    a = Alloc()
+    width = D // 2 if width is None else width
+    if packed:
+        query = a(dt, (B, S, (H + 2 * Hk) * D))
+        key = value = None
+    else:
+        query = a(dt, (B, S, H * D))
+        key = a(dt, (B, S, Hk * D))
+        value = a(dt, (B, S, Hk * D))
+    kw = dict(query=query, key=key, value=value,
+              past_key=a(dt, (B, Hk, Smax, D)), past_value=a(dt, (B, Hk, Smax, D)),
+              key_total_sequence_lengths=a(I32, (B,)), total_sequence_length=total,
+              cos_cache=a(dt, (M, width)), sin_cache=a(dt, (M, width)),
+              q_out=reshape(query, (B, S, H * D)) if inplace else a(dt, (B, S, H * D)),
+              rotary_interleaved=0, num_heads=H, kv_num_heads=Hk)
+    kw.update(over)
+    return kw
+
+
+def check_kv(kw):
+    kw = dict(kw)
+    args = [kw.pop(k) for k in ("query", "key", "value", "past_key", "past_value",
+                                "key_total_sequence_lengths", "total_sequence_length",
+                                "cos_cache", "sin_cache", "q_out")]
+    return rpe.rope_kv_append_check(*args, **kw)
+
+
+def test_kv_append_accepted():
+    for dt in (F16, F32, BF16):
+        for packed in (False, True):
+            rc, v = check_kv(kv_case(dt=dt, packed=packed))
+            assert rc == OK, _lib.load().rope_last_error()
+            assert v == "vec16/append"
+    for total in (3, 40):                                 # prompt; full cache
+        assert check_kv(kv_case(total=total))[0] == OK
+    rc, v = check_kv(kv_case(inplace=True))
+    assert rc == OK and v == "vec16/append"
+    rc, v = check_kv(kv_case(D=6, width=3))                # 6 halves: no 16-byte items
+    assert rc == OK and v == "scalar/append"
+    rc, v = check_kv(kv_case(D=32, width=8))               # partial rotation
+    assert rc == OK and v == "vec16/append"
+    rc, v = check_kv(kv_case(B=0))
+    assert rc == OK
+
+
+def test_kv_append_clauses():
+    lib = _lib.load()
+    base = kv_case()
+    cases = [
+        ("query missing", NULL, dict(query=None)),
+        ("only key", NULL, dict(value=None)),
+        ("past_key missing", NULL, dict(past_key=None)),
+        ("lengths missing", NULL, dict(key_total_sequence_lengths=None)),
+        ("q_out missing", NULL, dict(q_out=None)),
+        ("lengths int64", DTYPE, dict(key_total_sequence_lengths=reshape(base["key_total_sequence_lengths"], (2,), I64))),
+        ("cache float32", DTYPE, dict(past_key=reshape(base["past_key"], (2, 2, 40, 16), F32))),
+        ("query int64", DTYPE, dict(query=reshape(base["query"], (2, 3, 128), I64))),
+        ("interleaved 2", ATTR, dict(rotary_interleaved=2)),
+        ("no heads", ATTR, dict(num_heads=0)),
+        ("kv does not divide", SHAPE, dict(kv_num_heads=3)),
+        ("query rank 4", RANK, dict(query=reshape(base["query"], (2, 3, 8, 16)))),
+        ("key shape", SHAPE, dict(key=reshape(base["key"], (2, 3, 16)), value=reshape(base["value"], (2, 3, 16)))),
+        ("value shape", SHAPE, dict(value=reshape(base["value"], (2, 1, 96)))),
+        ("cache rank 3", RANK, dict(past_key=reshape(base["past_key"], (2, 80, 16)))),
+        ("cache heads", SHAPE, dict(past_key=reshape(base["past_key"], (2, 1, 80, 16)),
+                                    past_value=reshape(base["past_value"], (2, 1, 80, 16)))),
+        ("value cache shape", SHAPE, dict(past_value=reshape(base["past_value"], (2, 2, 39, 16)))),
+        ("lengths shape", SHAPE, dict(key_total_sequence_lengths=reshape(base["key_total_sequence_lengths"], (1,)))),
+        ("table too wide", SHAPE, dict(cos_cache=reshape(base["cos_cache"], (32, 16)),
+                                       sin_cache=reshape(base["sin_cache"], (32, 16)))),
+        ("table rank 3", RANK, dict(cos_cache=reshape(base["cos_cache"], (1, 64, 8)))),
+        ("sin shape", SHAPE, dict(sin_cache=reshape(base["sin_cache"], (32, 8)))),
+        ("q_out shape", SHAPE, dict(q_out=reshape(base["q_out"], (2, 3, 64)))),
+        ("total below S", SHAPE, dict(total_sequence_length=2)),
+        ("total above cache", SHAPE, dict(total_sequence_length=41)),
+        ("total above table", SHAPE, dict(cos_cache=reshape(base["cos_cache"], (10, 8)),
+                                          sin_cache=reshape(base["sin_cache"], (10, 8)))),
+        ("caches alias", ALIAS, dict(past_value=base["past_key"])),
+        ("q_out in the cache", ALIAS, dict(q_out=reshape(base["past_key"], (2, 3, 128)))),
+        ("cache over the key", ALIAS, dict(past_key=reshape(base["key"], (2, 2, 3, 16)),
+                                           past_value=reshape(base["value"], (2, 2, 3, 16)),
+                                           total_sequence_length=3)),
+    ]
+    for name, code, over in cases:
+        kw = kv_case()
+        kw.update(over)
+        rc, _ = check_kv(kw)
+        assert rc == code, (name, rc, lib.rope_last_error())
+    # packed: q_out may not be the packed query
+    kw = kv_case(packed=True)
+    kw["q_out"] = reshape(kw["query"], (2, 3, 128))
+    assert check_kv(kw)[0] == ALIAS
+    kw = kv_case(packed=True)
+    kw["query"] = reshape(kw["query"], (2, 3, 190))       # not (H + 2Hk) * D
+    assert check_kv(kw)[0] == SHAPE

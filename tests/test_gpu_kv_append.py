@@ -1,0 +1,145 @@
+"""GPU parity for RoPE on Q and K with the key/value cache append (through the
+C ABI) against the oracle: q_out within the rotation tolerance (parity.py),
+the caches element by element (rotated K rows within it, V rows and every
+row not written bit for bit), and guard regions around the caches untouched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rotary_position_embedding_amd as rpe
+from gpu_io import DEV, cuda, host, torch_dtype
+from oracle_pins import angle_table, ids_in
+from parity import assert_bitwise, assert_parity, bits
+from rope_inputs import BFLOAT16, normal_tensor
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 4096  # elements of poison on each side of a cache
+
+
+@pytest.fixture(autouse=True)
+def _policy():
+    old = rpe.set_kernel_policy(0)
+    yield
+    rpe.set_kernel_policy(old)
+
+
+def guarded(arr):
+    """A device copy of `arr` inside a buffer with poisoned guard regions;
+    returns (view, whole buffer)."""
+    dt = torch_dtype(arr.dtype)
+    buf = torch.empty(arr.size + 2 * GUARD, dtype=dt, device=DEV)
+    buf.view(torch.int16 if buf.element_size() == 2 else torch.int32).fill_(0x7e11)
+    view = buf[GUARD:GUARD + arr.size].view(arr.shape)
+    view.copy_(cuda(arr))
+    return view, buf
+
+
+def check_guards(buf, what):
+    whole = bits(host(buf))
+    assert (whole[:GUARD] == 0x7e11).all() and (whole[-GUARD:] == 0x7e11).all(), what + ": guard overwritten"
+
+
+def run_case(dt, B, S, H, Hk, D, width, Smax, M, lens, total, il=0, packed=False, inplace=False, seed=0):
+    if packed:
+        query = normal_tensor(12000 + seed, (B, S, (H + 2 * Hk) * D), dt)
+        key = value = None
+    else:
+        query = normal_tensor(12000 + seed, (B, S, H * D), dt)
+        key = normal_tensor(12001 + seed, (B, S, Hk * D), dt)
+        value = normal_tensor(12002 + seed, (B, S, Hk * D), dt)
+    pk = normal_tensor(12003 + seed, (B, Hk, Smax, D), dt)
+    pv = normal_tensor(12004 + seed, (B, Hk, Smax, D), dt)
+    cos, sin = angle_table(12005 + seed, M, width, dt)
+    lens = np.asarray(lens, np.int32)
+    wq, wk, wv = oracle.rope_kv_append(query, key, value, pk, pv, lens, total, cos, sin, H, Hk,
+                                       interleaved=il)
+    gk, bk = guarded(pk)
+    gv, bv = guarded(pv)
+    q_t = cuda(query)
+    out = q_t if inplace else None
+    got_q = rpe.rope_kv_append(q_t, None if packed else cuda(key), None if packed else cuda(value), gk, gv,
+                               cuda(lens), total, cuda(cos), cuda(sin), num_heads=H, kv_num_heads=Hk,
+                               rotary_interleaved=il, out=out)
+    what = "dt=%s B=%d S=%d H=%d Hk=%d D=%d w=%d lens=%s total=%d il=%d packed=%s" % (
+        np.dtype(dt).name, B, S, H, Hk, D, width, lens.tolist()[:4], total, il, packed)
+    assert_parity(host(got_q), wq, "q_out " + what)
+    assert_parity(host(gk), wk, "present_key " + what)
+    assert_bitwise(host(gv), wv, "present_value " + what)
+    # rows that were not written hold their old bits
+    written = np.zeros((B, Smax), bool)
+    past = np.zeros(B, np.int64) if total == S else lens.astype(np.int64) - S
+    for b in range(B):
+        for s in range(S):
+            r = past[b] + s
+            if 0 <= r < Smax:
+                written[b, r] = True
+    keep = ~written
+    hk = host(gk)
+    for b in range(B):
+        assert_bitwise(hk[b][:, keep[b]], pk[b][:, keep[b]], "untouched key rows " + what)
+    check_guards(bk, "past_key " + what)
+    check_guards(bv, "past_value " + what)
+    return what
+
+
+KV = [
+    # dt, B, S, H, Hk, D, width, Smax, M, lens, total, il, packed
+    (np.float16, 64, 1, 32, 8, 128, 64, 512, 1024, "decode", None, 0, False),
+    (BFLOAT16, 3, 37, 8, 2, 128, 64, 160, 200, (37, 100, 64), 100, 0, False),
+    (np.float32, 2, 45, 4, 4, 64, 32, 64, 64, (45, 20), 45, 0, False),      # prompt with padding
+    (np.float16, 4, 5, 8, 2, 128, 64, 40, 40, (5, 9, 33, 40), 40, 0, True),  # packed
+    (np.float16, 2, 7, 4, 2, 128, 16, 30, 50, (7, 30), 30, 1, False),       # interleaved, partial
+    (BFLOAT16, 2, 3, 4, 1, 10, 5, 12, 12, (3, 11), 11, 0, False),           # scalar kernel
+    (np.float32, 2, 3, 2, 2, 96, 32, 24, 30, (3, 24), 24, 1, True),
+]
+
+
+@pytest.mark.parametrize("inplace", [False, True])
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("case", KV, ids=[str(i) for i in range(len(KV))])
+def test_kv_append_sweep(case, policy, inplace):
+    dt, B, S, H, Hk, D, width, Smax, M, lens, total, il, packed = case
+    if inplace and packed:
+        pytest.skip("q_out cannot be a packed query")
+    rpe.set_kernel_policy(policy)
+    if lens == "decode":
+        lens = ids_in(12100, (B,), Smax) + 1                 # 1..Smax, past = L - 1
+        total = int(lens.max())
+    print(run_case(dt, B, S, H, Hk, D, width, Smax, M, lens, total, il, packed, inplace, seed=B + S + D),
+          flush=True)
+
+
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+def test_kv_append_out_of_contract_lengths(policy):
+    """Lengths above total_sequence_length or below S: rows outside the cache
+    are skipped, positions outside the table keep their pairs, nothing
+    outside the caches is written."""
+    rpe.set_kernel_policy(policy)
+    print(run_case(np.float16, 4, 3, 8, 2, 128, 64, 20, 20, (2, 21, 25, -7), 20, seed=77), flush=True)
+
+
+def test_kv_append_decode_full_size():
+    """The decode step at serving size: 256 sequences, 32 query and 8 key heads
+    of 128, f16, a 512-row cache, lengths U[1, 512]; the old cache contents
+    are a cheap deterministic bit pattern (values in [0, 1))."""
+    B, H, Hk, D, Smax, M = 256, 32, 8, 128, 512, 32768
+    lens = (ids_in(12200, (B,), Smax) + 1).astype(np.int32)
+    inv = oracle.inv_freq(1e6, D)
+    cos, sin = oracle.cos_sin_cache(np.float16, M, inv)
+    q = normal_tensor(12201, (B, 1, H * D), np.float16)
+    k = normal_tensor(12202, (B, 1, Hk * D), np.float16)
+    v = normal_tensor(12203, (B, 1, Hk * D), np.float16)
+    n = B * Hk * Smax * D
+    pk = ((np.arange(n, dtype=np.uint64) * np.uint64(2654435761)) >> np.uint64(7) & np.uint64(0x3bff)) \
+        .astype(np.uint16).view(np.float16).reshape(B, Hk, Smax, D)
+    total = int(lens.max())
+    wq, wk, wv = oracle.rope_kv_append(q, k, v, pk, pk, lens, total, cos, sin, H, Hk)
+    gk, gv = cuda(pk), cuda(pk)
+    gq = rpe.rope_kv_append(cuda(q), cuda(k), cuda(v), gk, gv, cuda(lens), total,
+                            cuda(cos), cuda(sin), num_heads=H, kv_num_heads=Hk)
+    r = assert_parity(host(gq), wq, "q_out")
+    assert_parity(host(gk), wk, "present_key")
+    assert_bitwise(host(gv), wv, "present_value")
+    print("decode full size", r, flush=True)

@@ -8,35 +8,10 @@ import oracle
 import rotary_position_embedding_amd as rpe
 from oracle_pins import angle_table, ids_in, pair_index
 from parity import assert_bitwise, assert_parity, bits, compare
-from rope_inputs import BFLOAT16, WORKLOADS, bfloat16_bits, normal_tensor, with_dtype, with_layout
+from gpu_io import DEV, cuda, host, one, torch_dtype
+from rope_inputs import BFLOAT16, WORKLOADS, normal_tensor, with_dtype, with_layout
 
 pytestmark = pytest.mark.gpu
-
-DEV = "cuda:0"
-
-
-def cuda(a):
-    """numpy -> device tensor; uint16 arrays are bfloat16 bit patterns."""
-    a = np.ascontiguousarray(a)
-    if a.dtype == BFLOAT16:
-        return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
-    return torch.from_numpy(a).to(DEV)
-
-
-def host(t):
-    torch.cuda.synchronize()
-    if t.dtype == torch.bfloat16:
-        return t.view(torch.int16).cpu().numpy().view(np.uint16)
-    return t.cpu().numpy()
-
-
-def torch_dtype(dt):
-    return {np.dtype(np.float16): torch.float16, np.dtype(np.float32): torch.float32,
-            np.dtype(BFLOAT16): torch.bfloat16}[np.dtype(dt)]
-
-
-def one(dt):
-    return bfloat16_bits(1.0) if np.dtype(dt) == BFLOAT16 else 1
 
 
 @pytest.fixture(autouse=True)
