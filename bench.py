@@ -10,8 +10,10 @@ rotate over independent (X, Y, ids) sets totalling >= 1 GiB so that the 256 MB
 last-level cache cannot hold them and the rate measured is HBM's.
 
 Prints ONE JSON line on stdout. Also reported (in "also"): the M-RoPE
-prefill in both section layouts, the fp32 partial interleaved case and the
-fp16 decode Q+K step (table and on the fly).
+prefill in both section layouts, the fp32 partial interleaved case, the fp16
+decode Q+K step (table and on the fly), the prefill and M-RoPE stored in
+bfloat16, the packed [Q|K|V] decode step and the decode step with the
+key/value cache append.
 """
 import argparse
 import hashlib
@@ -47,15 +49,27 @@ def kernel_source_sha():
 # workload set-up: inputs generated on the host from the seeded generators,
 # tables built on the GPU by the library itself
 
+def to_device(a, dev):
+    """numpy -> device tensor (uint16 arrays are bfloat16 bit patterns)."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(a).to(dev)
+
+
 def setup(w, onthefly=False):
     import torch
     import rotary_position_embedding_amd as rpe
     dev = torch.device("cuda:0")
-    dt = torch.float16 if w.dtype == np.float16 else torch.float32
-    x0 = torch.from_numpy(w.make_x()).to(dev)
+    dt = {np.dtype(np.float16): torch.float16, np.dtype(np.float32): torch.float32,
+          np.dtype(np.uint16): torch.bfloat16}[np.dtype(w.dtype)]
+    x0 = to_device(w.make_x(), dev)
+    if w.op == "kv_append":
+        return setup_kv_append(w, x0, dt, dev)
     ids_h = w.make_ids()
     ids0 = None if ids_h is None else torch.from_numpy(ids_h).to(dev)
-    k0 = torch.from_numpy(w.make_k()).to(dev) if w.op == "rope_qk" else None
+    k0 = to_device(w.make_k(), dev) if w.op == "rope_qk" else None
     inv = rpe.rope_inv_freq(w.rotary_dim, w.cache_base, device=dev)
     if w.op == "rope" and not w.has_ids:
         cos, sin = rpe.rope_cos_sin_cache(inv, w.seq, dt, w.scaling)
@@ -77,6 +91,10 @@ def setup(w, onthefly=False):
                 x, cos, sin, ids, y, interleaved=w.interleaved,
                 num_heads=w.num_heads if w.rank == 3 else 0,
                 rotary_embedding_dim=w.rotary_embedding_dim))
+        elif w.op == "qkv_packed":
+            y = torch.empty_like(x)
+            launchers.append(rpe.rope_apply_qkv_packed_launcher(
+                x, cos, sin, ids, y, num_heads=w.num_heads, kv_num_heads=w.kv_num_heads))
         elif w.op == "mrope":
             y = torch.empty_like(x)
             launchers.append(rpe.mrope_apply_launcher(
@@ -94,6 +112,36 @@ def setup(w, onthefly=False):
                 launchers.append(rpe.rope_apply_qk_launcher(
                     x, k, cos, sin, ids, yq, yk, num_heads=w.num_heads,
                     kv_num_heads=w.kv_num_heads))
+    torch.cuda.synchronize()
+    return launchers, nsets * set_bytes
+
+
+def setup_kv_append(w, q0, dt, dev):
+    """Decode with cache append: sets of (Q, K, V, q_out, lengths) rotate;
+    the two caches are shared, and each set's lengths are the base lengths
+    shifted by a set-dependent offset (mod the cache length) so that the
+    rows written differ from set to set."""
+    import torch
+    import rotary_position_embedding_amd as rpe
+    smax = w.extra["cache_seq"]
+    B, Hk, D = w.batch, w.kv_num_heads, w.head_size
+    k0 = to_device(w.make_k(), dev)
+    v0 = to_device(w.make_v(), dev)
+    lens0 = w.make_lengths()
+    inv = rpe.rope_inv_freq(w.rotary_dim, w.cache_base, device=dev)
+    cos, sin = rpe.rope_cos_sin_cache(inv, w.cache_rows, dt, w.scaling)
+    pk = torch.zeros(B, Hk, smax, D, dtype=dt, device=dev)
+    pv = torch.zeros_like(pk)
+    set_bytes = 2 * (q0.numel() + 2 * k0.numel()) * q0.element_size()
+    nsets = max(2, -(-ROTATE_BYTES // set_bytes))
+    launchers = []
+    for i in range(nsets):
+        lens_h = ((lens0.astype(np.int64) - 1 + 997 * i) % smax + 1).astype(np.int32)
+        q, k, v = q0.clone(), k0.clone(), v0.clone()
+        lens = torch.from_numpy(lens_h).to(dev)
+        launchers.append(rpe.rope_kv_append_launcher(
+            q, k, v, pk, pv, lens, int(lens_h.max()), cos, sin, torch.empty_like(q),
+            num_heads=w.num_heads, kv_num_heads=Hk))
     torch.cuda.synchronize()
     return launchers, nsets * set_bytes
 
@@ -182,6 +230,7 @@ def main():
     ap.add_argument("--workload", default=HEADLINE,
                     help="workload to time alone (for profiler runs); implies --no-extra")
     ap.add_argument("--onthefly", action="store_true", help="with the decode Q+K workload")
+    ap.add_argument("--bf16", action="store_true", help="time the workload stored in bfloat16")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -219,6 +268,8 @@ def main():
 
     only = args.workload != HEADLINE or args.no_extra
     w = rope_inputs.get(args.workload)
+    if args.bf16:
+        w = rope_inputs.with_dtype(w, rope_inputs.BFLOAT16, "bf16")
     log("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
     head = measure(w, args.steps, args.warmup, args.onthefly)
     log("  %.2f us/step, %.1f GB/s (%.1f%% of %g)" % (
@@ -230,7 +281,12 @@ def main():
                  (rope_inputs.with_layout(rope_inputs.get("c4_mrope_f16_prefill"), 1), False),
                  (rope_inputs.get("c3_rope_f32_partial_interleaved"), False),
                  (rope_inputs.get("c5_rope_qk_f16_decode"), False),
-                 (rope_inputs.get("c5_rope_qk_f16_decode"), True)]
+                 (rope_inputs.get("c5_rope_qk_f16_decode"), True),
+                 (rope_inputs.with_dtype(rope_inputs.get(HEADLINE), rope_inputs.BFLOAT16, "bf16"), False),
+                 (rope_inputs.with_dtype(rope_inputs.with_layout(rope_inputs.get("c4_mrope_f16_prefill"), 0),
+                                         rope_inputs.BFLOAT16, "bf16"), False),
+                 (rope_inputs.get("qkv_packed_f16_decode"), False),
+                 (rope_inputs.get("kv_append_f16_decode"), False)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
             r = measure(ew, min(args.steps, 100), min(args.warmup, 10), otf)
@@ -261,7 +317,7 @@ def main():
         "config": {
             "workload": w.name,
             "description": w.description,
-            "storage_dtype": np.dtype(w.dtype).name,
+            "storage_dtype": "bfloat16" if np.dtype(w.dtype) == np.uint16 else np.dtype(w.dtype).name,
             "x_shape": list(w.x_shape),
             "bytes_per_step": head["bytes_per_step"],
             "tokens_heads_per_s": round(head["tokens_heads_per_s"], 1),

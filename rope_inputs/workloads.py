@@ -28,7 +28,7 @@ def seed(index: int, tensor: int) -> int:
 class Workload:
     index: int
     name: str
-    op: str                      # "rope", "mrope" or "rope_qk"
+    op: str                      # "rope", "mrope", "rope_qk", "qkv_packed" or "kv_append"
     dtype: type
     x_shape: Tuple[int, ...]     # X, or Q for rope_qk
     num_heads: int = 0
@@ -55,6 +55,8 @@ class Workload:
     def head_size(self) -> int:
         if self.rank == 4:
             return self.x_shape[3]
+        if self.op == "qkv_packed":
+            return self.x_shape[2] // (self.num_heads + 2 * self.kv_num_heads)
         return self.x_shape[2] // self.num_heads
 
     @property
@@ -93,13 +95,19 @@ class Workload:
         xy = 2 * int(np.prod(self.x_shape)) * self.itemsize
         if self.k_shape is not None:
             xy += 2 * int(np.prod(self.k_shape)) * self.itemsize
+        if self.op == "kv_append":
+            # Q read + written, K and V read and written to one cache row each,
+            # the per-sequence lengths (int32) instead of ids
+            xy += 2 * int(np.prod(self.k_shape)) * self.itemsize
+            return xy + self.tokens * 2 * self.half * self.itemsize + self.batch * 4
         coef = 4 * self.half if onthefly else self.tokens * 2 * self.half * self.itemsize
         n_id_streams = 3 if self.op == "mrope" else (1 if self.has_ids else 0)
         return xy + coef + n_id_streams * self.tokens * 8
 
     def tokens_heads(self) -> int:
+        """(token, head) rows rotated."""
         th = self.tokens * self.heads
-        if self.k_shape is not None:
+        if self.k_shape is not None or self.op == "qkv_packed":
             th += self.tokens * self.kv_num_heads
         return th
 
@@ -109,6 +117,14 @@ class Workload:
 
     def make_k(self) -> np.ndarray:
         return normal_tensor(seed(self.index, 2), self.k_shape, self.dtype)
+
+    def make_v(self) -> np.ndarray:
+        return normal_tensor(seed(self.index, 4), self.k_shape, self.dtype)
+
+    def make_lengths(self) -> np.ndarray:
+        """kv_append: per-sequence total key lengths U[1, cache_seq] (int32)."""
+        cap = self.extra["cache_seq"]
+        return (uniform_ints(seed(self.index, 1), (self.batch,), cap) + 1).astype(np.int32)
 
     def make_ids(self) -> Optional[np.ndarray]:
         if self.op == "mrope":
@@ -211,8 +227,25 @@ WORKLOADS = {
 }
 
 
+# Workloads of the fused variants (same seeding scheme, indices after the five).
+EXTRA_WORKLOADS = {
+    "qkv_packed_f16_decode": Workload(
+        index=5, name="qkv_packed_f16_decode", op="qkv_packed", dtype=np.float16,
+        x_shape=(256, 1, 48 * 128), num_heads=32, kv_num_heads=8, cache_rows=32768, cache_base=1e6,
+        extra={"ids": "uniform", "id_bound": 32768},
+        description="Packed [Q|K|V] decode fp16: batch 256, seq 1, 32 query + 8 key + 8 value heads "
+                    "of 128 in one (256, 1, 6144) tensor; Q and K rotated, V copied; table (32768, 64)"),
+    "kv_append_f16_decode": Workload(
+        index=6, name="kv_append_f16_decode", op="kv_append", dtype=np.float16,
+        x_shape=(256, 1, 4096), num_heads=32, k_shape=(256, 1, 1024), kv_num_heads=8,
+        cache_rows=32768, cache_base=1e6, extra={"cache_seq": 4096},
+        description="Decode fp16 with cache append: batch 256, seq 1, Q 32 heads + K, V 8 heads of 128, "
+                    "caches (256, 8, 4096, 128), lengths U[1, 4096], table (32768, 64)"),
+}
+
+
 def get(name: str) -> Workload:
-    return WORKLOADS[name]
+    return WORKLOADS[name] if name in WORKLOADS else EXTRA_WORKLOADS[name]
 
 
 def with_dtype(w: Workload, dtype, tag: str) -> Workload:
