@@ -85,6 +85,8 @@ class Oracle:
                                       vp, vp, vp, vp, vp, vp, vp, i64, vp, f32], None),
             "oracle_rope_kv_append": ([i32, i64, i64, i64, i64, i64, i64, i64,
                                        vp, vp, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp], None),
+            "oracle_rope_apply_qk_norm": ([i32, i32, i64, i64, i64, i64, i64, i64, i64,
+                                           vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i64, vp, f32], None),
         }
         for name, (args, res) in sig.items():
             fn = getattr(lib, name)
@@ -203,6 +205,39 @@ class Oracle:
                                       _ptr(sin), _ptr(ids), M, _ptr(inv), attention_scaling)
         return yq, yk
 
+    def rope_apply_qk_norm(self, q, k, q_weight, k_weight, epsilon, cos=None, sin=None,
+                           position_ids=None, interleaved=0, num_heads=0, kv_num_heads=0,
+                           rotary_embedding_dim=0, inv_freq=None, attention_scaling=1.0):
+        """RMSNorm of every Q and K head row (weights (D,), epsilon), then the
+        rotation of rope_apply_qk; cos=None selects on-the-fly."""
+        q = _dense(q)
+        k = _dense(k, q.dtype)
+        qw = _dense(q_weight, q.dtype)
+        kw = _dense(k_weight, q.dtype)
+        ids = _dense(position_ids, np.int64)
+        rank, B, S, H, D = _dims(q, num_heads)
+        rk, Bk, Sk, Hk, Dk = _dims(k, kv_num_heads)
+        if (rk, Bk, Sk, Dk) != (rank, B, S, D) or qw.shape != (D,) or kw.shape != (D,):
+            raise ValueError("Q, K and the weights disagree")
+        R = rotary_embedding_dim or D
+        inv = None
+        if cos is None:
+            inv = _dense(inv_freq, np.float32)
+            if ids is None or inv is None:
+                raise ValueError("on-the-fly needs position_ids and inv_freq")
+            M = 0
+        else:
+            cos = _dense(cos, q.dtype)
+            sin = _dense(sin, q.dtype)
+            M = cos.shape[0] if ids is not None else 0
+        yq = np.zeros_like(q)
+        yk = np.zeros_like(k)
+        self.lib.oracle_rope_apply_qk_norm(_code(q.dtype), rank, B, S, H, Hk, D, R, interleaved,
+                                           _ptr(q), _ptr(k), _ptr(qw), _ptr(kw), float(epsilon),
+                                           _ptr(yq), _ptr(yk), _ptr(cos), _ptr(sin), _ptr(ids), M,
+                                           _ptr(inv), attention_scaling)
+        return yq, yk
+
     def rope_kv_append(self, query, key, value, past_key, past_value, key_total_sequence_lengths,
                        total_sequence_length, cos, sin, num_heads, kv_num_heads, interleaved=0):
         """RoPE on Q and K and the key/value cache append. query (B,S,H*D), or
@@ -291,6 +326,10 @@ def rope_apply_qk(*a, **kw):
 
 def rope_kv_append(*a, **kw):
     return default().rope_kv_append(*a, **kw)
+
+
+def rope_apply_qk_norm(*a, **kw):
+    return default().rope_apply_qk_norm(*a, **kw)
 
 
 def table_for(workload, dtype=None):

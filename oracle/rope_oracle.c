@@ -487,3 +487,98 @@ void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
     }
     coef_free(&cr);
 }
+
+/* ------------------------------------------------------------------------ */
+/* QK-norm then RoPE: [PR] review, Qwen3 architecture (RMSNorm is applied to Q
+ * and K after the projection and reshape, before RoPE; the fused graph holds
+ * SimplifiedLayerNormalization nodes for it). RMSNorm of a head row x of D
+ * elements with weight g (D values) and epsilon e:
+ *     z_j = x_j * g_j / sqrt(mean_k(x_k^2) + e)
+ * (reading taken: the standard RMSNorm over the head dimension; the pages
+ * name it without writing it out). The rotation then acts on z exactly as
+ * oracle_rope_apply_qk acts on x; a kept pair and the tail hold z. All in
+ * binary64, one rounding to the storage type (the fused op never stores z).
+ * q_weight and k_weight are (D,) arrays of the storage type. */
+static void norm_row(int dtype, const void* x, int64_t off, const void* w,
+                     int64_t D, double eps, double* z)
+{
+    double ss = 0.0;
+    for (int64_t j = 0; j < D; ++j) {
+        double v = load_elem(dtype, x, off + j);
+        ss += v * v;
+    }
+    double inv_rms = 1.0 / sqrt(ss / (double)D + eps);
+    for (int64_t j = 0; j < D; ++j)
+        z[j] = load_elem(dtype, x, off + j) * inv_rms * load_elem(dtype, w, j);
+}
+
+static void rotate_values(int dtype, const double* z, void* y, int64_t off,
+                          int64_t D, int64_t R, int64_t interleaved,
+                          const double* c, const double* s,
+                          const unsigned char* copy)
+{
+    int64_t half = R / 2;
+    for (int64_t i = 0; i < half; ++i) {
+        int64_t j1 = interleaved ? 2 * i : i;
+        int64_t j2 = interleaved ? 2 * i + 1 : i + half;
+        if (copy[i]) {
+            store_elem(dtype, y, off + j1, z[j1]);
+            store_elem(dtype, y, off + j2, z[j2]);
+            continue;
+        }
+        store_elem(dtype, y, off + j1, z[j1] * c[i] - z[j2] * s[i]);
+        store_elem(dtype, y, off + j2, z[j2] * c[i] + z[j1] * s[i]);
+    }
+    for (int64_t j = R; j < D; ++j)
+        store_elem(dtype, y, off + j, z[j]);
+}
+
+void oracle_rope_apply_qk_norm(int dtype, int rank, int64_t B, int64_t S,
+                               int64_t H, int64_t Hk, int64_t D, int64_t R,
+                               int64_t interleaved, const void* q,
+                               const void* k, const void* q_weight,
+                               const void* k_weight, float epsilon, void* yq,
+                               void* yk, const void* cos_cache,
+                               const void* sin_cache, const int64_t* ids,
+                               int64_t M, const float* inv_freq,
+                               float scaling)
+{
+    int64_t half = R / 2;
+    coef_row cr;
+    double* z = (double*)calloc((size_t)(D > 0 ? D : 1), sizeof(double));
+    if (!z || !coef_alloc(&cr, half))
+        abort();
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t s = 0; s < S; ++s) {
+            /* the coefficient row of the token: table row (gathered or per
+             * token), or on the fly from inv_freq */
+            int64_t row = ids ? ids[b * S + s] : b * S + s;
+            int in_range = cos_cache == NULL || !ids || (row >= 0 && row < M);
+            for (int64_t i = 0; i < half; ++i) {
+                cr.copy[i] = (unsigned char)!in_range;
+                if (!in_range)
+                    continue;
+                if (cos_cache) {
+                    cr.c[i] = load_elem(dtype, cos_cache, row * half + i);
+                    cr.s[i] = load_elem(dtype, sin_cache, row * half + i);
+                } else {
+                    coefficient(dtype, row, inv_freq[i], scaling, &cr.c[i],
+                                &cr.s[i]);
+                }
+            }
+            for (int64_t h = 0; h < H; ++h) {
+                int64_t off = row_offset(rank, S, H, D, b, h, s);
+                norm_row(dtype, q, off, q_weight, D, (double)epsilon, z);
+                rotate_values(dtype, z, yq, off, D, R, interleaved, cr.c, cr.s,
+                              cr.copy);
+            }
+            for (int64_t h = 0; h < Hk; ++h) {
+                int64_t off = row_offset(rank, S, Hk, D, b, h, s);
+                norm_row(dtype, k, off, k_weight, D, (double)epsilon, z);
+                rotate_values(dtype, z, yk, off, D, R, interleaved, cr.c, cr.s,
+                              cr.copy);
+            }
+        }
+    coef_free(&cr);
+    free(z);
+}

@@ -135,6 +135,25 @@ void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
                            int64_t M, void* past_key, void* past_value,
                            int64_t Smax, void* q_out);
 
+/* QK-norm then RoPE ([PR] review, Qwen3 architecture: RMSNorm on Q and K
+ * before RoPE). Each head row x of Q (K) becomes
+ *     z_j = x_j * w_j / sqrt(mean_k(x_k^2) + epsilon)
+ * with w = q_weight (k_weight), (D,) of the storage type (reading taken: the
+ * standard RMSNorm over the head dimension). z is then rotated as
+ * oracle_rope_apply_qk rotates x (same tables, ids, on-the-fly rule); kept
+ * pairs and the tail hold z. Binary64 throughout, one rounding to the storage
+ * type. Parity pinned by closed forms and invariants (mean of squares,
+ * epsilon, weights, scale invariance). */
+void oracle_rope_apply_qk_norm(int dtype, int rank, int64_t B, int64_t S,
+                               int64_t H, int64_t Hk, int64_t D, int64_t R,
+                               int64_t interleaved, const void* q,
+                               const void* k, const void* q_weight,
+                               const void* k_weight, float epsilon, void* yq,
+                               void* yk, const void* cos_cache,
+                               const void* sin_cache, const int64_t* ids,
+                               int64_t M, const float* inv_freq,
+                               float scaling);
+
 #ifdef __cplusplus
 }
 #endif

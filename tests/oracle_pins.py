@@ -814,4 +814,126 @@ def pin_kv_append_out_of_contract(orc):
     assert_bitwise(ko[2, 0, :4], pk[2, 0, :4], "batch 2: rows below the past untouched")
 
 
+# --------------------------------------------------------------------------
+# QK-norm (RMSNorm over the head row) then RoPE
+
+def pin_qk_norm_hand_worked(orc):
+    """D = 4, x = (2, 2, 2, 2): mean of squares 4. epsilon 0: 1/rms = 1/2, so
+    with weights w = (1, 4, 0.5, 2), z_j = 2 * w_j / 2 = w_j.
+    Quarter turn (c, s) = (0, 1) on both slots:
+    half-split pairs (z0, z2) = (1, 0.5) -> (-0.5, 1), (z1, z3) = (4, 2) -> (-2, 4),
+    so y = (-0.5, -2, 1, 4); interleaved (z0, z1) = (1, 4) -> (-4, 1),
+    (z2, z3) = (0.5, 2) -> (-2, 0.5), so y = (-4, 1, -2, 0.5).
+    epsilon 12: 1/sqrt(4 + 12) = 1/4, z = w/2, y halves. Exact in every type."""
+    for dt in (np.float32, np.float16, BF16):
+        x = from_f64([2.0, 2.0, 2.0, 2.0], dt).reshape(1, 1, 1, 4)
+        w = from_f64([1.0, 4.0, 0.5, 2.0], dt)
+        c = from_f64([[0.0, 0.0]], dt)
+        sn = from_f64([[1.0, 1.0]], dt)
+        ids = np.zeros((1, 1), np.int64)
+        for eps, f in ((0.0, 1.0), (12.0, 0.5)):
+            for il, want in ((0, [-0.5, -2.0, 1.0, 4.0]), (1, [-4.0, 1.0, -2.0, 0.5])):
+                yq, yk = orc.rope_apply_qk_norm(x, x, w, w, eps, c, sn, ids, interleaved=il)
+                assert_bitwise(yq.reshape(-1), from_f64(np.array(want) * f, dt), "qk-norm eps=%g il=%d" % (eps, il))
+                assert_bitwise(yk.reshape(-1), from_f64(np.array(want) * f, dt), "qk-norm K")
+
+
+def pin_qk_norm_constant_magnitude_rows(orc):
+    """Rows with |x_j| = a for all j, unit weights, epsilon 0: z = sign(x), so
+    the result is RotaryEmbedding of the +-1 row (the mean, not the sum, of
+    the squares; the square root)."""
+    for dt in (np.float32, np.float16, BF16):
+        for D, R in ((16, 16), (12, 8)):
+            B, S, H, M = 2, 3, 2, 7
+            sign = np.where(SplitMix64(241).uniform(B * S * H * D) < 0.5, -1.0, 1.0).reshape(B, H, S, D)
+            a = np.exp2(np.floor(SplitMix64(242).uniform(B * H * S) * 10 - 5)).reshape(B, H, S, 1)
+            x = from_f64(sign * a, dt)
+            ones = from_f64(np.ones(D), dt)
+            cos, sin = angle_table(243, M, R // 2, dt)
+            ids = ids_in(244, (B, S), M)
+            rd = R if R != D else 0
+            yq, _ = orc.rope_apply_qk_norm(x, x, ones, ones, 0.0, cos, sin, ids, rotary_embedding_dim=rd)
+            want = orc.rope_apply(from_f64(sign, dt), cos, sin, ids, rotary_embedding_dim=rd)
+            assert_bitwise(yq, want, "constant-magnitude rows dt=%s D=%d" % (np.dtype(dt).name, D))
+
+
+def pin_qk_norm_scale_invariant(orc):
+    """epsilon 0: scaling a row by 2^k changes nothing, bit for bit."""
+    for dt in (np.float32, np.float16, BF16):
+        x = normal_any(251, (2, 3, 4, 16), dt)
+        w = normal_any(252, (16,), dt)
+        cos, sin = angle_table(253, 9, 8, dt)
+        ids = ids_in(254, (2, 4), 9)
+        a, _ = orc.rope_apply_qk_norm(x, x, w, w, 0.0, cos, sin, ids)
+        for k in (-3, 2):
+            xs = from_f64(to_f64(x) * 2.0 ** k, dt)
+            b, _ = orc.rope_apply_qk_norm(xs, xs, w, w, 0.0, cos, sin, ids)
+            assert_bitwise(a, b, "scale 2^%d" % k)
+
+
+def pin_qk_norm_unit_rows(orc):
+    """Unit weights, epsilon 0, a table of rotations: every output row has
+    sum of squares D (the normalised row has mean square 1 and the rotation
+    keeps the pair norms), within the roundings."""
+    for dt, rel in ((np.float32, 2.0 ** -20), (np.float16, 2.0 ** -8), (BF16, 2.0 ** -5)):
+        B, S, H, D, M = 2, 5, 3, 32, 11
+        x = normal_any(261, (B, H, S, D), dt)
+        ones = from_f64(np.ones(D), dt)
+        th = SplitMix64(262).uniform(M * D // 2).reshape(M, D // 2) * 2 * np.pi
+        cos, sin = from_f64(np.cos(th).astype(np.float32), dt), from_f64(np.sin(th).astype(np.float32), dt)
+        ids = ids_in(263, (B, S), M)
+        for il in (0, 1):
+            y, _ = orc.rope_apply_qk_norm(x, x, ones, ones, 0.0, cos, sin, ids, interleaved=il)
+            ssq = (to_f64(y) ** 2).sum(-1)
+            assert np.abs(ssq / D - 1).max() < rel, np.abs(ssq / D - 1).max()
+
+
+def pin_qk_norm_kept_pairs_and_tail(orc):
+    """An out-of-range id keeps the pairs: the row is normalised and not
+    rotated, which equals a table row (1, 0); the tail is normalised too."""
+    for dt in (np.float32, np.float16, BF16):
+        B, S, H, D, R, M = 2, 4, 2, 16, 8, 6
+        x = normal_any(271, (B, S, H * D), dt)
+        w = normal_any(272, (D,), dt)
+        cos, sin = angle_table(273, M, R // 2, dt)
+        ids = ids_in(274, (B, S), M)
+        ids[0, 1] = -1
+        ids[1, 2] = M
+        ident_c = np.concatenate([cos, from_f64(np.ones((1, R // 2)), dt)])
+        ident_s = np.concatenate([sin, from_f64(np.zeros((1, R // 2)), dt)])
+        ids_ident = ids.copy()
+        ids_ident[0, 1] = M
+        ids_ident[1, 2] = M
+        a, _ = orc.rope_apply_qk_norm(x, x, w, w, 1e-6, cos, sin, ids, num_heads=H, kv_num_heads=H,
+                                      rotary_embedding_dim=R)
+        b, _ = orc.rope_apply_qk_norm(x, x, w, w, 1e-6, ident_c, ident_s, ids_ident, num_heads=H,
+                                      kv_num_heads=H, rotary_embedding_dim=R)
+        assert_bitwise(a, b, "kept pairs = identity row")
+        # tail: same as the tail of a full-width identity rotation
+        c_full = from_f64(np.ones((M, D // 2)), dt)
+        s_full = from_f64(np.zeros((M, D // 2)), dt)
+        full, _ = orc.rope_apply_qk_norm(x, x, w, w, 1e-6, c_full, s_full, ids_in(275, (B, S), M),
+                                         num_heads=H, kv_num_heads=H)
+        assert_bitwise(a.reshape(B, S, H, D)[..., R:], full.reshape(B, S, H, D)[..., R:], "normalised tail")
+
+
+def pin_qk_norm_weights_per_projection(orc):
+    """Q uses q_weight and K uses k_weight: K's result equals the Q result of
+    a call whose Q is K and whose q_weight is k_weight."""
+    dt = np.float16
+    q = normal_any(281, (2, 3, 4 * 16), dt)
+    k = normal_any(282, (2, 3, 2 * 16), dt)
+    wq = normal_any(283, (16,), dt)
+    wk = normal_any(284, (16,), dt)
+    inv = orc.inv_freq(1e4, 16)
+    ids = ids_in(285, (2, 3), 100)
+    for tables in (True, False):
+        cos, sin = orc.cos_sin_cache(dt, 100, inv) if tables else (None, None)
+        _, yk = orc.rope_apply_qk_norm(q, k, wq, wk, 1e-6, cos, sin, ids, num_heads=4, kv_num_heads=2,
+                                       inv_freq=inv)
+        yq2, _ = orc.rope_apply_qk_norm(k, k, wk, wq, 1e-6, cos, sin, ids, num_heads=2, kv_num_heads=2,
+                                        inv_freq=inv)
+        assert_bitwise(yk, yq2, "k_weight routing")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

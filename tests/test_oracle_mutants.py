@@ -51,6 +51,15 @@ MUTANTS = {
     "kv_row_bound_off_by_one": [("if (p < 0 || p >= Smax)", "if (p < 0 || p > Smax - 2)")],
     "kv_value_not_written": [("                    copy_elem_to(dtype, vsrc, tok * kw + v0 + h * D + j,\n                                 past_value, dst + j);",
                               "                    ;")],
+    "norm_sum_not_mean": [("1.0 / sqrt(ss / (double)D + eps)", "1.0 / sqrt(ss + eps)")],
+    "norm_epsilon_ignored": [("1.0 / sqrt(ss / (double)D + eps)", "1.0 / sqrt(ss / (double)D)")],
+    "norm_no_square_root": [("1.0 / sqrt(ss / (double)D + eps)", "1.0 / (ss / (double)D + eps)")],
+    "norm_weight_ignored": [("z[j] = load_elem(dtype, x, off + j) * inv_rms * load_elem(dtype, w, j);",
+                             "z[j] = load_elem(dtype, x, off + j) * inv_rms;")],
+    "norm_k_uses_q_weight": [("norm_row(dtype, k, off, k_weight, D, (double)epsilon, z);",
+                              "norm_row(dtype, k, off, q_weight, D, (double)epsilon, z);")],
+    "norm_tail_not_normalised": [("        store_elem(dtype, y, off + j, z[j]);\n}",
+                                  "        store_elem(dtype, y, off + j, z[j] / z[j] * 0.0 + 1.0);\n}")],
     "inv_freq_exponent": [("-2.0 * (double)i / (double)rotary_dim", "-1.0 * (double)i / (double)rotary_dim")],
     "onthefly_uses_position_zero": [("coefficient(dtype, p, inv_freq[i], scaling, &cr.c[i], &cr.s[i]);",
                                      "coefficient(dtype, 0, inv_freq[i], scaling, &cr.c[i], &cr.s[i]);")],
