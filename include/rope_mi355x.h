@@ -17,6 +17,9 @@
  *                      kv_num_heads, rotary on Q and on K).
  *   rope_apply_qkv_packed  the same on a packed [Q|K|V] activation --
  *                      "com.microsoft.SparseAttention" README (Inputs).
+ *   rope_apply_qk_norm RMSNorm of every Q and K head row, then the rotation of
+ *                      rope_apply_qk, in one pass -- PR #27590 review, Qwen3
+ *                      architecture (QK-Norm before RoPE).
  *   rope_kv_append     RoPE on Q and K with K and V appended to the key and
  *                      value caches in place, one launch --
  *                      "com.microsoft.SparseAttention" README (Description,
@@ -204,6 +207,32 @@ int rope_apply_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
                           void* stream);
 
 /*
+ * rope_apply_qk_norm -- QK-norm then RoPE in one pass (PR #27590 review,
+ * Qwen3 architecture: RMSNorm is applied to Q and K after the projection and
+ * reshape, before RoPE). Each head row x (D elements) of Q, resp. K, becomes
+ *     z_j = x_j * w_j / sqrt(mean_k(x_k^2) + epsilon)
+ * with w = q_weight, resp. k_weight (type T, shape (D,)), and z is rotated
+ * exactly as rope_apply_qk rotates x: same tables or on-the-fly rule, ids,
+ * interleaved, rotary_embedding_dim, attention_scaling. Pairs kept by an
+ * out-of-range id and the tail beyond the rotary dimension hold z. z is not
+ * stored: the sum of squares, the scale and the rotation are binary32, with
+ * one rounding to T at the end.
+ * epsilon: finite, >= 0 (the model's RMSNorm epsilon).
+ * Other arguments, shapes, aliasing rules: as rope_apply_qk; the outputs may
+ * not overlap the weights.
+ */
+int rope_apply_qk_norm(const rope_tensor* q, const rope_tensor* k,
+                       const rope_tensor* q_weight, const rope_tensor* k_weight,
+                       float epsilon, const rope_tensor* cos_cache,
+                       const rope_tensor* sin_cache,
+                       const rope_tensor* position_ids, const rope_tensor* yq,
+                       const rope_tensor* yk, int64_t interleaved,
+                       int64_t num_heads, int64_t kv_num_heads,
+                       int64_t rotary_embedding_dim,
+                       const rope_tensor* inv_freq, float attention_scaling,
+                       void* stream);
+
+/*
  * rope_kv_append -- the rotary part of "com.microsoft.SparseAttention"
  * (README Description: past and present key/value caches share storage and
  * are updated in place; Attributes: do_rotary rotates Q and K before K enters
@@ -302,6 +331,19 @@ int rope_apply_qkv_packed_check(const rope_tensor* qkv,
                                 int64_t rotary_embedding_dim,
                                 const rope_tensor* inv_freq,
                                 float attention_scaling, const char** variant);
+
+int rope_apply_qk_norm_check(const rope_tensor* q, const rope_tensor* k,
+                             const rope_tensor* q_weight,
+                             const rope_tensor* k_weight, float epsilon,
+                             const rope_tensor* cos_cache,
+                             const rope_tensor* sin_cache,
+                             const rope_tensor* position_ids,
+                             const rope_tensor* yq, const rope_tensor* yk,
+                             int64_t interleaved, int64_t num_heads,
+                             int64_t kv_num_heads,
+                             int64_t rotary_embedding_dim,
+                             const rope_tensor* inv_freq,
+                             float attention_scaling, const char** variant);
 
 int rope_kv_append_check(const rope_tensor* query, const rope_tensor* key,
                          const rope_tensor* value, const rope_tensor* past_key,

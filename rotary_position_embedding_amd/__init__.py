@@ -24,7 +24,8 @@ __all__ = ["RopeError", "rope_apply", "mrope_apply", "rope_apply_qk", "rope_inv_
            "rope_apply_qk_check", "set_kernel_policy", "library_path", "Launcher",
            "rope_apply_launcher", "mrope_apply_launcher", "rope_apply_qk_launcher",
            "rope_apply_qkv_packed", "rope_apply_qkv_packed_check", "rope_apply_qkv_packed_launcher",
-           "rope_kv_append", "rope_kv_append_check", "rope_kv_append_launcher"]
+           "rope_kv_append", "rope_kv_append_check", "rope_kv_append_launcher",
+           "rope_apply_qk_norm", "rope_apply_qk_norm_check", "rope_apply_qk_norm_launcher"]
 
 _DTYPE = {torch.float32: ROPE_FLOAT, torch.float16: ROPE_FLOAT16, torch.int64: ROPE_INT64,
           torch.bfloat16: ROPE_BFLOAT16, torch.int32: ROPE_INT32}
@@ -173,6 +174,53 @@ def rope_apply_qkv_packed_launcher(qkv, cos_cache, sin_cache, position_ids, out,
                                             _lib.ref(ds[5]), attention_scaling, _stream(dev)]
     return Launcher(_lib.load().rope_apply_qkv_packed, args,
                     (ds, qkv, cos_cache, sin_cache, position_ids, out, inv_freq))
+
+
+def rope_apply_qk_norm(q, k, q_weight, k_weight, cos_cache=None, sin_cache=None, position_ids=None, *,
+                       epsilon, interleaved=0, num_heads=0, kv_num_heads=0, rotary_embedding_dim=0,
+                       inv_freq=None, attention_scaling=1.0, out_q=None, out_k=None):
+    """RMSNorm of every Q and K head row (weights (D,), epsilon) then the
+    rotation of rope_apply_qk, in one pass. Returns (yq, yk)."""
+    dev = _device_of(q)
+    yq = torch.empty_like(q) if out_q is None else out_q
+    yk = torch.empty_like(k) if out_k is None else out_k
+    ds = [_desc(t, dev) for t in (q, k, q_weight, k_weight, cos_cache, sin_cache, position_ids, yq, yk,
+                                  inv_freq)]
+    with _on_device(dev):
+        _check(_lib.load().rope_apply_qk_norm(
+            _lib.ref(ds[0]), _lib.ref(ds[1]), _lib.ref(ds[2]), _lib.ref(ds[3]), float(epsilon),
+            *[_lib.ref(d) for d in ds[4:9]], interleaved, num_heads, kv_num_heads, rotary_embedding_dim,
+            _lib.ref(ds[9]), attention_scaling, _stream(dev)))
+    return yq, yk
+
+
+def rope_apply_qk_norm_check(q, k, q_weight, k_weight, cos_cache, sin_cache, position_ids, yq, yk, *,
+                             epsilon, interleaved=0, num_heads=0, kv_num_heads=0, rotary_embedding_dim=0,
+                             inv_freq=None, attention_scaling=1.0):
+    v = _variant_out()
+    rc = _lib.load().rope_apply_qk_norm_check(
+        _lib.ref(q), _lib.ref(k), _lib.ref(q_weight), _lib.ref(k_weight), float(epsilon),
+        _lib.ref(cos_cache), _lib.ref(sin_cache), _lib.ref(position_ids), _lib.ref(yq), _lib.ref(yk),
+        interleaved, num_heads, kv_num_heads, rotary_embedding_dim, _lib.ref(inv_freq), attention_scaling,
+        ctypes.byref(v))
+    return rc, (v.value.decode() if rc == 0 and v.value else None)
+
+
+def rope_apply_qk_norm_launcher(q, k, q_weight, k_weight, cos_cache, sin_cache, position_ids, out_q, out_k,
+                                *, epsilon, interleaved=0, num_heads=0, kv_num_heads=0,
+                                rotary_embedding_dim=0, inv_freq=None, attention_scaling=1.0):
+    dev = _device_of(q)
+    ds = [_desc(t, dev) for t in (q, k, q_weight, k_weight, cos_cache, sin_cache, position_ids, out_q, out_k,
+                                  inv_freq)]
+    rc, _ = rope_apply_qk_norm_check(*ds[:9], epsilon=epsilon, interleaved=interleaved, num_heads=num_heads,
+                                     kv_num_heads=kv_num_heads, rotary_embedding_dim=rotary_embedding_dim,
+                                     inv_freq=ds[9], attention_scaling=attention_scaling)
+    _check(rc)
+    args = [_lib.ref(ds[0]), _lib.ref(ds[1]), _lib.ref(ds[2]), _lib.ref(ds[3]), float(epsilon)] + \
+        [_lib.ref(d) for d in ds[4:9]] + [interleaved, num_heads, kv_num_heads, rotary_embedding_dim,
+                                          _lib.ref(ds[9]), attention_scaling, _stream(dev)]
+    return Launcher(_lib.load().rope_apply_qk_norm, args,
+                    (ds, q, k, q_weight, k_weight, cos_cache, sin_cache, position_ids, out_q, out_k, inv_freq))
 
 
 def rope_kv_append(query, key, value, past_key, past_value, key_total_sequence_lengths,

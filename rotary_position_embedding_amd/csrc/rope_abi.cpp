@@ -129,6 +129,34 @@ int rope_apply_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
     return rope::launch_plan(pl, stream);
 }
 
+int rope_apply_qk_norm_check(const rope_tensor* q, const rope_tensor* k, const rope_tensor* q_weight,
+                             const rope_tensor* k_weight, float epsilon, const rope_tensor* cos_cache,
+                             const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                             const rope_tensor* yq, const rope_tensor* yk, int64_t interleaved,
+                             int64_t num_heads, int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                             const rope_tensor* inv_freq, float attention_scaling, const char** variant) {
+    Plan pl;
+    int rc = rope::plan_rope_qk_norm(q, k, q_weight, k_weight, epsilon, cos_cache, sin_cache,
+                                     position_ids, yq, yk, interleaved, num_heads, kv_num_heads,
+                                     rotary_embedding_dim, inv_freq, attention_scaling, &pl);
+    if (rc == ROPE_OK && variant) *variant = pl.g.variant;
+    return rc;
+}
+
+int rope_apply_qk_norm(const rope_tensor* q, const rope_tensor* k, const rope_tensor* q_weight,
+                       const rope_tensor* k_weight, float epsilon, const rope_tensor* cos_cache,
+                       const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                       const rope_tensor* yq, const rope_tensor* yk, int64_t interleaved,
+                       int64_t num_heads, int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                       const rope_tensor* inv_freq, float attention_scaling, void* stream) {
+    Plan pl;
+    int rc = rope::plan_rope_qk_norm(q, k, q_weight, k_weight, epsilon, cos_cache, sin_cache,
+                                     position_ids, yq, yk, interleaved, num_heads, kv_num_heads,
+                                     rotary_embedding_dim, inv_freq, attention_scaling, &pl);
+    if (rc != ROPE_OK) return rc;
+    return rope::launch_plan(pl, stream);
+}
+
 int rope_kv_append_check(const rope_tensor* query, const rope_tensor* key, const rope_tensor* value,
                          const rope_tensor* past_key, const rope_tensor* past_value,
                          const rope_tensor* key_total_sequence_lengths, int64_t total_sequence_length,

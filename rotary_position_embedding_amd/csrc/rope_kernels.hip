@@ -50,6 +50,7 @@ struct KTask {
     int32_t copy;          // copy: pass every element through (no rotation)
     int32_t yrow;          // append kind: y row is the token's position
     int64_t ysb, ysh, yss; // append kind: element strides of y (b, h, row)
+    const char* wgt;       // QK-norm: (D,) weight of this projection
 };
 
 struct KArgs {
@@ -62,6 +63,8 @@ struct KArgs {
     int32_t ntask, W, NP, TG, P, R, D, interleaved;
     int32_t xcd_remap, prompt;  // prompt: append kind, every sequence starts at 0
     float scaling, scale;
+    float eps;                  // QK-norm epsilon
+    int32_t pad3;
     const int32_t* seqlens;     // append kind: total key length per sequence
     int64_t rows_out;           // append kind: cache rows
     uint32_t sel[kSelWords];
@@ -198,6 +201,7 @@ struct TaskView {
     int64_t sb, sh, ss, wave_begin, item_begin;
     int32_t heads, hpw, chunks, tile, copy, yrow;
     int64_t ysb, ysh, yss;
+    const char* wgt;
 };
 
 // An SGPR value the compiler must treat as opaque: keeps a select of two
@@ -212,7 +216,7 @@ __device__ inline V opaque_s(V v) {
 // Task i (0..2) of the launch: every task's fields are read in the first
 // batch of scalar loads and the values are selected. The output geometry is
 // the input's except for the append kind.
-template <int COEF>
+template <int COEF, bool NORM = false>
 __device__ inline TaskView task_of(const KArgs& a, int i) {
 #define ROPE_PICK(f)                                                                      \
     do {                                                                                  \
@@ -243,6 +247,8 @@ __device__ inline TaskView task_of(const KArgs& a, int i) {
         v.ysh = v.sh;
         v.yss = v.ss;
     }
+    if (NORM) ROPE_PICK(wgt);
+    else v.wgt = nullptr;
 #undef ROPE_PICK
     return v;
 }
@@ -307,7 +313,7 @@ __device__ inline void load_batch(const char* x, const int64_t* off, const bool*
     }
 }
 
-template <typename T, int IL, int COEF, int IPL, int HU>
+template <typename T, int IL, int COEF, int IPL, int HU, bool NORM = false>
 __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation item
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     // task selection and its fields in scalar registers
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + wave_in_block;
-    const TaskView tk = task_of<COEF>(a, task_index(a, gw));
+    const TaskView tk = task_of<COEF, NORM>(a, task_index(a, gw));
     const int64_t local = gw - tk.wave_begin;
     const int64_t per_tile = (int64_t)tk.tile * tk.chunks;
     const int64_t tile = local / per_tile;
@@ -342,6 +348,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     int64_t tok[IPL];
     int64_t apos[IPL];   // append kind: the token's position
     int slot0[IPL];
+    int64_t elem0[IPL];  // first element of the item in its head row
 #pragma unroll
     for (int m = 0; m < IPL; ++m) {
         const int q = lane + 64 * m;
@@ -356,6 +363,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         const int64_t e0 = w < a.NP ? (int64_t)w * E : (int64_t)a.R + (int64_t)(w - a.NP) * E;
         off[m] = act[m] ? (b * tk.sb + s * tk.ss + e0) * ES : 0;
         slot0[m] = rot[m] ? w * CE : 0;  // non-rotation items read slot 0 (unused)
+        elem0[m] = e0;
         if (COEF == kCoefAppend) {
             // the lengths are read for every item (sequence 0 for inactive ones)
             const int64_t past = a.prompt ? 0 : (int64_t)a.seqlens[b] - a.S;
@@ -487,8 +495,87 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         }
     }
 
+    // QK-norm (one item per lane): the weights of the item's elements
+    float gw1[NORM ? E : 1], gw2[NORM ? E : 1];
+    if (NORM) {
+        const auto w1 = chunk_values<T>(load16(tk.wgt + elem0[0] * ES));
+        const auto w2 = chunk_values<T>(load16(tk.wgt + (elem0[0] + (rot[0] && !IL ? a.P : 0)) * ES));
+#pragma unroll
+        for (int e = 0; e < E; ++e) { gw1[e] = to_f(w1[e]); gw2[e] = to_f(w2[e]); }
+    }
+
     // -- rotate and store, one head batch at a time --------------------------
     for (int h = h_begin; h < h_end; h += HU) {
+        if (NORM) {
+            // RMSNorm of each head row first: the lane's sum of squares, summed
+            // over the row's W lanes (an aligned group: W divides 64), then
+            // z = (x / rms) * weight, rotated like x; kept pairs and tail
+            // items store z
+            float rn[HU];
+#pragma unroll
+            for (int u = 0; u < HU; ++u) {
+                float ss = 0.0f;
+                if (act[0] && h + u < h_end) {
+                    const auto v1 = chunk_values<T>(in1[u][0]);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) ss = fmaf(to_f(v1[e]), to_f(v1[e]), ss);
+                    if (!IL && rot[0]) {
+                        const auto v2 = chunk_values<T>(in2[u][0]);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) ss = fmaf(to_f(v2[e]), to_f(v2[e]), ss);
+                    }
+                }
+                for (int o = 1; o < a.W; o <<= 1) ss += __shfl_xor(ss, o);
+                rn[u] = 1.0f / sqrtf(ss / (float)a.D + a.eps);
+            }
+#pragma unroll
+            for (int u = 0; u < HU; ++u) {
+                if (!(wr[0] && h + u < h_end)) continue;
+                u32x4* py = reinterpret_cast<u32x4*>(tk.y + yoff[0] + (int64_t)(h + u) * ysh_bytes);
+                const auto xv1 = chunk_values<T>(in1[u][0]);
+                float z1[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) z1[e] = (to_f(xv1[e]) * rn[u]) * gw1[e];
+                if (!rot[0]) {
+                    __builtin_nontemporal_store(chunk_pack<T>(z1), py);
+                    continue;
+                }
+                if (IL) {
+                    float r[E];
+#pragma unroll
+                    for (int j = 0; j < CE; ++j) {
+                        const float c = to_f(cf[0][j]), s = to_f(sf[0][j]);
+                        r[2 * j] = fmaf(z1[2 * j], c, -(z1[2 * j + 1] * s));
+                        r[2 * j + 1] = fmaf(z1[2 * j + 1], c, z1[2 * j] * s);
+                    }
+                    u32x4 o = chunk_pack<T>(r);
+                    if (COEF == kCoefGather) o = select_bits(keep[0], chunk_pack<T>(z1), o);
+                    __builtin_nontemporal_store(o, py);
+                } else {
+                    const auto xv2 = chunk_values<T>(in2[u][0]);
+                    float z2[E], r1[E], r2[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) z2[e] = (to_f(xv2[e]) * rn[u]) * gw2[e];
+#pragma unroll
+                    for (int j = 0; j < E; ++j) {
+                        const float c = to_f(cf[0][j]), s = to_f(sf[0][j]);
+                        r1[j] = fmaf(z1[j], c, -(z2[j] * s));
+                        r2[j] = fmaf(z2[j], c, z1[j] * s);
+                    }
+                    u32x4 o1 = chunk_pack<T>(r1);
+                    u32x4 o2 = chunk_pack<T>(r2);
+                    if (COEF == kCoefGather) {
+                        o1 = select_bits(keep[0], chunk_pack<T>(z1), o1);
+                        o2 = select_bits(keep[0], chunk_pack<T>(z2), o2);
+                    }
+                    __builtin_nontemporal_store(o1, py);
+                    __builtin_nontemporal_store(o2, py + half_bytes / 16);
+                }
+            }
+            if (h + HU < h_end)
+                load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h + HU, h_end, sh_bytes, half_bytes, in1, in2);
+            continue;
+        }
 #pragma unroll
         for (int u = 0; u < HU; ++u) {
 #pragma unroll
@@ -591,6 +678,54 @@ __global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int6
     }
 }
 
+// Scalar QK-norm kernel: one thread per (task, token, head) row -- the sum
+// of squares over the row, then every pair rotated from z = (x / rms) * w
+// and every tail element stored as z. Any head size and alignment.
+template <typename T, int COEF>
+__global__ __launch_bounds__(kBlock) void rope_norm_row_kernel(const KArgs a, int64_t total) {
+    using B = typename Elem<T>::bits;
+    for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * kBlock) {
+        const TaskView tk = task_of<COEF, true>(a, task_index_items(a, idx));
+        const int64_t local = idx - tk.item_begin;
+        const int64_t h = local % tk.heads;
+        const int64_t n = local / tk.heads;
+        const int64_t b = n / a.S;
+        const int64_t s = n - b * a.S;
+        const int64_t base = b * tk.sb + h * tk.sh + s * tk.ss;
+        const B* xb = reinterpret_cast<const B*>(tk.x) + base;
+        B* yb = reinterpret_cast<B*>(tk.y) + base;
+        const B* wb = reinterpret_cast<const B*>(tk.wgt);
+        // the sum of squares in binary64 (one long sequential sum here)
+        double ss = 0.0;
+        for (int j = 0; j < a.D; ++j) {
+            const double v = to_f(__builtin_bit_cast(T, xb[j]));
+            ss = fma(v, v, ss);
+        }
+        const float rn = 1.0f / sqrtf((float)(ss / (double)a.D) + a.eps);
+        for (int i = 0; i < a.P; ++i) {
+            const int j1 = a.interleaved ? 2 * i : i;
+            const int j2 = a.interleaved ? 2 * i + 1 : i + a.P;
+            const float z1 = (to_f(__builtin_bit_cast(T, xb[j1])) * rn) * to_f(__builtin_bit_cast(T, wb[j1]));
+            const float z2 = (to_f(__builtin_bit_cast(T, xb[j2])) * rn) * to_f(__builtin_bit_cast(T, wb[j2]));
+            float c = 1.0f, sn = 0.0f;
+            bool copy = false;
+            coef_slot<T, COEF>(a, n, i, c, sn, copy);
+            if (copy) {
+                yb[j1] = __builtin_bit_cast(B, from_f<T>(z1));
+                yb[j2] = __builtin_bit_cast(B, from_f<T>(z2));
+                continue;
+            }
+            yb[j1] = __builtin_bit_cast(B, from_f<T>(fmaf(z1, c, -(z2 * sn))));
+            yb[j2] = __builtin_bit_cast(B, from_f<T>(fmaf(z2, c, z1 * sn)));
+        }
+        for (int j = a.R; j < a.D; ++j) {
+            const float z = (to_f(__builtin_bit_cast(T, xb[j])) * rn) * to_f(__builtin_bit_cast(T, wb[j]));
+            yb[j] = __builtin_bit_cast(B, from_f<T>(z));
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Table builders.
 
@@ -647,9 +782,32 @@ static hipError_t launch_vec_ipl(const KArgs& a, int ipl, int hu, dim3 grid, hip
     return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
 }
 
+// QK-norm: one item per lane, any instantiated head batch.
+template <typename T, int IL, int COEF>
+static hipError_t launch_vec_norm(const KArgs& a, int hu, dim3 grid, hipStream_t st) {
+    void* args[] = {const_cast<KArgs*>(&a)};
+    const void* fn;
+    switch (hu) {
+        case 2: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 2, true>; break;
+        case 4: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 4, true>; break;
+        case 8: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 8, true>; break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
+}
+
 template <typename T, int IL>
 static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, dim3 grid,
-                                  hipStream_t st) {
+                                  hipStream_t st, bool norm) {
+    if (norm) {
+        if (ipl != 1) return hipErrorInvalidValue;
+        switch (c) {
+            case kCoefGather: return launch_vec_norm<T, IL, kCoefGather>(a, hu, grid, st);
+            case kCoefPerToken: return launch_vec_norm<T, IL, kCoefPerToken>(a, hu, grid, st);
+            case kCoefOnTheFly: return launch_vec_norm<T, IL, kCoefOnTheFly>(a, hu, grid, st);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (c) {
         case kCoefGather: return launch_vec_ipl<T, IL, kCoefGather>(a, ipl, hu, grid, st);
         case kCoefPerToken: return launch_vec_ipl<T, IL, kCoefPerToken>(a, ipl, hu, grid, st);
@@ -660,12 +818,21 @@ static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, d
 }
 
 template <typename T>
-static hipError_t launch_scalar(const KArgs& a, CoefKind c, int64_t total, hipStream_t st) {
+static hipError_t launch_scalar(const KArgs& a, CoefKind c, int64_t total, hipStream_t st, bool norm) {
     int64_t blocks = (total + kBlock - 1) / kBlock;
     if (blocks > 65536) blocks = 65536;
     if (blocks < 1) blocks = 1;
     void* args[] = {const_cast<KArgs*>(&a), &total};
     const void* fn;
+    if (norm) {
+        switch (c) {
+            case kCoefGather: fn = (const void*)rope_norm_row_kernel<T, kCoefGather>; break;
+            case kCoefPerToken: fn = (const void*)rope_norm_row_kernel<T, kCoefPerToken>; break;
+            case kCoefOnTheFly: fn = (const void*)rope_norm_row_kernel<T, kCoefOnTheFly>; break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0, st);
+    }
     switch (c) {
         case kCoefGather: fn = (const void*)rope_scalar_kernel<T, kCoefGather>; break;
         case kCoefPerToken: fn = (const void*)rope_scalar_kernel<T, kCoefPerToken>; break;
@@ -682,7 +849,9 @@ int launch_plan(const Plan& pl, void* stream) {
     const Geometry& g = pl.g;
     hipStream_t st = (hipStream_t)stream;
     KArgs a = {};
-    const int64_t K = p.R / 2 + (p.D - p.R);
+    // scalar work items per (token, head): pairs plus tail elements, or the
+    // whole row for the QK-norm kernel
+    const int64_t K = p.norm ? 1 : p.R / 2 + (p.D - p.R);
     int64_t wave_begin = 0, item_begin = 0;
     for (int t = 0; t < kMaxTasks; ++t) {
         a.t[t].wave_begin = INT64_MAX;
@@ -703,6 +872,7 @@ int launch_plan(const Plan& pl, void* stream) {
         a.t[t].ysb = p.task[t].ystride_b;
         a.t[t].ysh = p.task[t].ystride_h;
         a.t[t].yss = p.task[t].ystride_s;
+        a.t[t].wgt = (const char*)p.task[t].weight;
         const int64_t items = p.B * p.S * p.task[t].heads * K;
         if (items > 0) {  // an empty task keeps INT64_MAX and is never selected
             a.t[t].item_begin = item_begin;
@@ -743,6 +913,7 @@ int launch_plan(const Plan& pl, void* stream) {
     a.xcd_remap = g.xcd_remap;
     a.scaling = p.scaling;
     a.scale = p.scale;
+    a.eps = p.eps;
     a.seqlens = p.seqlens;
     a.prompt = p.prompt;
     a.rows_out = p.rows_out;
@@ -756,19 +927,19 @@ int launch_plan(const Plan& pl, void* stream) {
         const int ipl = g.items_per_lane;
         const int hu = g.head_batch;
         if (p.dtype == ROPE_FLOAT16)
-            e = p.interleaved ? launch_vec_coef<half_t, 1>(a, p.coef, ipl, hu, grid, st)
-                              : launch_vec_coef<half_t, 0>(a, p.coef, ipl, hu, grid, st);
+            e = p.interleaved ? launch_vec_coef<half_t, 1>(a, p.coef, ipl, hu, grid, st, p.norm)
+                              : launch_vec_coef<half_t, 0>(a, p.coef, ipl, hu, grid, st, p.norm);
         else if (p.dtype == ROPE_BFLOAT16)
-            e = p.interleaved ? launch_vec_coef<bf16_t, 1>(a, p.coef, ipl, hu, grid, st)
-                              : launch_vec_coef<bf16_t, 0>(a, p.coef, ipl, hu, grid, st);
+            e = p.interleaved ? launch_vec_coef<bf16_t, 1>(a, p.coef, ipl, hu, grid, st, p.norm)
+                              : launch_vec_coef<bf16_t, 0>(a, p.coef, ipl, hu, grid, st, p.norm);
         else
-            e = p.interleaved ? launch_vec_coef<float, 1>(a, p.coef, ipl, hu, grid, st)
-                              : launch_vec_coef<float, 0>(a, p.coef, ipl, hu, grid, st);
+            e = p.interleaved ? launch_vec_coef<float, 1>(a, p.coef, ipl, hu, grid, st, p.norm)
+                              : launch_vec_coef<float, 0>(a, p.coef, ipl, hu, grid, st, p.norm);
     } else {
         if (item_begin == 0) return ROPE_OK;
-        e = p.dtype == ROPE_FLOAT16    ? launch_scalar<half_t>(a, p.coef, item_begin, st)
-            : p.dtype == ROPE_BFLOAT16 ? launch_scalar<bf16_t>(a, p.coef, item_begin, st)
-                                       : launch_scalar<float>(a, p.coef, item_begin, st);
+        e = p.dtype == ROPE_FLOAT16    ? launch_scalar<half_t>(a, p.coef, item_begin, st, p.norm)
+            : p.dtype == ROPE_BFLOAT16 ? launch_scalar<bf16_t>(a, p.coef, item_begin, st, p.norm)
+                                       : launch_scalar<float>(a, p.coef, item_begin, st, p.norm);
     }
     return launched(e);
 }

@@ -144,11 +144,14 @@ void mrope_streams(int64_t half, const int64_t section[3], int64_t layout,
 // ---------------------------------------------------------------------------
 // kernel choice
 
-static const char* variant_name(bool vec, CoefKind c) {
+static const char* variant_name(bool vec, CoefKind c, bool norm) {
     static const char* names[2][5] = {
         {"scalar/gather", "scalar/per_token", "scalar/mrope", "scalar/on_the_fly", "scalar/append"},
         {"vec16/gather", "vec16/per_token", "vec16/mrope", "vec16/on_the_fly", "vec16/append"}};
-    return names[vec ? 1 : 0][(int)c];
+    static const char* norm_names[2][5] = {
+        {"scalar/norm/gather", "scalar/norm/per_token", "", "scalar/norm/on_the_fly", ""},
+        {"vec16/norm/gather", "vec16/norm/per_token", "", "vec16/norm/on_the_fly", ""}};
+    return (norm ? norm_names : names)[vec ? 1 : 0][(int)c];
 }
 
 static int env_int(const char* name) {
@@ -175,14 +178,19 @@ static void choose_geometry(Plan* pl) {
     ok = ok && p.D % E == 0 && p.R % E == 0 && (p.interleaved || half % E == 0);
     for (int t = 0; t < p.ntask; ++t)
         ok = ok && aligned16(p.task[t].x) && aligned16(p.task[t].y);
+    if (p.norm)
+        for (int t = 0; t < p.ntask; ++t) ok = ok && aligned16(p.task[t].weight);
     if (p.coef != kCoefOnTheFly)
         ok = ok && aligned16(p.cos) && aligned16(p.sin);
     const int64_t NP = p.interleaved ? p.R / E : half / E;
     const int64_t NT = (p.D - p.R) / E;
     const int64_t W = NP + NT;
     ok = ok && W >= 1 && W <= 256;
+    // QK-norm: a row's items must sit in one aligned group of W lanes (W a
+    // power of two dividing the wave) for the in-wave sum of squares
+    if (p.norm) ok = ok && W <= 64 && (W & (W - 1)) == 0;
     g.vector = ok;
-    g.variant = variant_name(ok, p.coef);
+    g.variant = variant_name(ok, p.coef, p.norm != 0);
     if (!ok) return;
 
     int best = 0;
@@ -202,6 +210,7 @@ static void choose_geometry(Plan* pl) {
         for (int ipl = 1; ipl <= 4 && best == 0; ++ipl)
             if (64 * ipl / W >= 1) best = ipl;
     }
+    if (p.norm) best = 1;  // the only instantiation with the norm
     g.items_per_lane = best;
     g.W = (int32_t)W;
     g.NP = (int32_t)NP;
@@ -609,6 +618,42 @@ int plan_rope_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor* 
     }
     out->empty = numel(q) == 0 && numel(k) == 0;
     out->g.rank = q->rank;
+    choose_geometry(out);
+    return ROPE_OK;
+}
+
+// QK-norm then RoPE: onnxruntime PR #27590 review, Qwen3 architecture (RMSNorm
+// on Q and K after the projection, before RoPE). The Q+K contract plus the
+// two (D,) weights of the storage type and a finite epsilon >= 0.
+int plan_rope_qk_norm(const rope_tensor* q, const rope_tensor* k, const rope_tensor* q_weight,
+                      const rope_tensor* k_weight, float epsilon, const rope_tensor* cos_cache,
+                      const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                      const rope_tensor* yq, const rope_tensor* yk, int64_t interleaved,
+                      int64_t num_heads, int64_t kv_num_heads, int64_t rotary_embedding_dim,
+                      const rope_tensor* inv_freq, float attention_scaling, Plan* out) {
+    TRY(plan_rope_qk(q, k, cos_cache, sin_cache, position_ids, yq, yk, interleaved, num_heads,
+                     kv_num_heads, rotary_embedding_dim, inv_freq, attention_scaling, out));
+    if (!q_weight) return fail(ROPE_ERR_NULL, "q_weight is missing");
+    if (!k_weight) return fail(ROPE_ERR_NULL, "k_weight is missing");
+    TRY(check_desc(q_weight, "q_weight"));
+    TRY(check_desc(k_weight, "k_weight"));
+    Problem& p = out->p;
+    if (q_weight->dtype != p.dtype || k_weight->dtype != p.dtype)
+        return fail(ROPE_ERR_DTYPE, "q_weight and k_weight must have the type of q");
+    if (q_weight->rank != 1 || k_weight->rank != 1)
+        return fail(ROPE_ERR_RANK, "q_weight and k_weight must be rank 1 (head_size,)");
+    if (q_weight->shape[0] != p.D || k_weight->shape[0] != p.D)
+        return fail(ROPE_ERR_SHAPE, "q_weight and k_weight must be (%lld,)", (long long)p.D);
+    if (!(epsilon >= 0.0f) || !std::isfinite(epsilon))
+        return fail(ROPE_ERR_ATTRIBUTE, "epsilon must be finite and >= 0");
+    const rope_tensor* w[2] = {q_weight, k_weight};
+    const char* wn[2] = {"q_weight", "k_weight"};
+    TRY(check_output(yq, "yq", nullptr, w, wn, 2));
+    TRY(check_output(yk, "yk", nullptr, w, wn, 2));
+    p.norm = 1;
+    p.eps = epsilon;
+    p.task[0].weight = q_weight->data;
+    p.task[1].weight = k_weight->data;
     choose_geometry(out);
     return ROPE_OK;
 }

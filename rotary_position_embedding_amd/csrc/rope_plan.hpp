@@ -35,6 +35,7 @@ struct Task {
     int64_t ystride_b, ystride_h, ystride_s;
     int32_t copy;
     int32_t yrow;
+    const void* weight;   // QK-norm: (D,) RMSNorm weight of this projection
 };
 
 constexpr int kMaxPlanTasks = 3;
@@ -58,6 +59,9 @@ struct Problem {
     const int32_t* seqlens;
     int32_t prompt;
     int64_t rows_out;
+    // QK-norm: every head row RMS-normalised (weights per task) before rotation
+    int32_t norm;
+    float eps;
 };
 
 // Launch geometry of the vector kernel (see rope_kernels.hip for the mapping).
@@ -108,6 +112,15 @@ int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
                          const rope_tensor* y, int64_t interleaved, int64_t num_heads,
                          int64_t kv_num_heads, int64_t rotary_embedding_dim,
                          const rope_tensor* inv_freq, float attention_scaling, Plan* out);
+
+int plan_rope_qk_norm(const rope_tensor* q, const rope_tensor* k,
+                      const rope_tensor* q_weight, const rope_tensor* k_weight,
+                      float epsilon, const rope_tensor* cos_cache,
+                      const rope_tensor* sin_cache, const rope_tensor* position_ids,
+                      const rope_tensor* yq, const rope_tensor* yk, int64_t interleaved,
+                      int64_t num_heads, int64_t kv_num_heads,
+                      int64_t rotary_embedding_dim, const rope_tensor* inv_freq,
+                      float attention_scaling, Plan* out);
 
 int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
                         const rope_tensor* value, const rope_tensor* past_key,

@@ -84,3 +84,35 @@ def assert_bitwise(got, want, what=""):
     bad = np.flatnonzero(bg != bw)
     assert bad.size == 0, "%s: %d of %d differ bitwise; first at %d: %r vs %r" % (
         what, bad.size, bg.size, bad[0], got.reshape(-1)[bad[0]], want.reshape(-1)[bad[0]])
+
+
+def ulp_of(want):
+    """One unit in the last place of each oracle value in its storage type."""
+    v = np.abs(values(want))
+    if want.dtype == np.float16:
+        return np.exp2(np.floor(np.log2(np.maximum(v, 2.0 ** -14))) - 10)
+    if want.dtype == np.uint16:
+        return np.exp2(np.floor(np.log2(np.maximum(v, 2.0 ** -126))) - 7)
+    return np.exp2(np.floor(np.log2(np.maximum(v, 2.0 ** -126))) - 23)
+
+
+def assert_parity_norm(got, want, zmax, what=""):
+    """QK-norm + RoPE tolerance: |gpu - oracle| <= 1 ulp of the oracle value
+    + 2^-18 * zmax, zmax the largest |z_j| = |x_j w_j| / rms of the element's
+    head row (broadcast to the output's shape). Bound: the binary32 sum of
+    squares (at most ~20 roundings of positive terms), mean, epsilon, square
+    root and reciprocal leave 1/rms within ~13 * 2^-24 relative; z = (x/rms)*w
+    adds 2 roundings; the fma rotation of z adds ~2 more on |z1 c| + |z2 s|
+    <= 2 * zmax * max|c, s|. That is <= ~34 * 2^-24 * zmax * max|c, s| ~ 2^-19
+    * zmax for coefficients up to 1.25; 2^-18 leaves a factor of two. The
+    final rounding to the storage type adds one unit."""
+    g = values(got).reshape(-1)
+    w = values(want).reshape(-1)
+    tol = ulp_of(want).reshape(-1) + 2.0 ** -18 * np.broadcast_to(zmax, got.shape).reshape(-1)
+    bad_nan = np.isnan(g) != np.isnan(w)
+    diff = np.abs(g - w)
+    over = (diff > tol) & ~np.isnan(w)
+    n = int(np.count_nonzero(over)) + int(np.count_nonzero(bad_nan))
+    assert n == 0, "%s: %d of %d outside tolerance; max diff/tol %.3g" % (
+        what, n, w.size, float(np.nanmax(diff / tol)))
+    return {"n": int(w.size), "max_abs": float(np.nanmax(diff)), "max_over_tol": float(np.nanmax(diff / tol))}

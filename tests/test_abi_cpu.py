@@ -569,3 +569,60 @@ def test_kv_append_clauses():
     kw = kv_case(packed=True)
     kw["query"] = reshape(kw["query"], (2, 3, 190))       # not (H + 2Hk) * D
     assert check_kv(kw)[0] == SHAPE
+
+
+# ---------------------------------------------------------------------------
+# QK-norm then RoPE
+
+def norm_case(dt=F16, rank=3, D=128, table=True, **over):
+    kw = qk_case(dt=dt, rank=rank, D=D, table=table)
+    a = Alloc()
+    a.next = 1 << 40
+    kw["q_weight"] = a(dt, (D,))
+    kw["k_weight"] = a(dt, (D,))
+    kw["epsilon"] = 1e-6
+    kw.update(over)
+    return kw
+
+
+def check_norm(kw):
+    kw = dict(kw)
+    args = [kw.pop(k) for k in ("q", "k", "q_weight", "k_weight", "cos_cache", "sin_cache", "position_ids",
+                                "yq", "yk")]
+    return rpe.rope_apply_qk_norm_check(*args, **kw)
+
+
+def test_qk_norm_accepted():
+    for dt in (F16, BF16, F32):
+        for table in (True, False):
+            rc, v = check_norm(norm_case(dt=dt, table=table))
+            assert rc == OK, _lib.load().rope_last_error()
+            assert v == ("vec16/norm/gather" if table else "vec16/norm/on_the_fly")
+    rc, v = check_norm(norm_case(dt=F32, D=96))      # 12 items per row: not a power of two
+    assert rc == OK and v == "scalar/norm/gather"
+    rc, v = check_norm(norm_case(rank=4))
+    assert rc == OK and v == "vec16/norm/gather"
+    rc, v = check_norm(norm_case(epsilon=0.0))
+    assert rc == OK
+
+
+def test_qk_norm_clauses():
+    lib = _lib.load()
+    base = norm_case()
+    cases = [
+        ("q_weight missing", NULL, dict(q_weight=None)),
+        ("k_weight missing", NULL, dict(k_weight=None)),
+        ("weight dtype", DTYPE, dict(q_weight=reshape(base["q_weight"], (64,), F32))),
+        ("weight rank", RANK, dict(k_weight=reshape(base["k_weight"], (2, 64)))),
+        ("weight length", SHAPE, dict(q_weight=reshape(base["q_weight"], (64,)))),
+        ("epsilon negative", ATTR, dict(epsilon=-1e-6)),
+        ("epsilon nan", ATTR, dict(epsilon=float("nan"))),
+        ("epsilon inf", ATTR, dict(epsilon=float("inf"))),
+        ("yq over the weight", ALIAS, dict(yq=reshape(base["q_weight"], tuple(base["yq"].shape[:3])))),
+        ("q contract still applies", ATTR, dict(interleaved=2)),
+    ]
+    for name, code, over in cases:
+        kw = norm_case()
+        kw.update(over)
+        rc, _ = check_norm(kw)
+        assert rc == code, (name, rc, lib.rope_last_error())
