@@ -12,8 +12,9 @@ last-level cache cannot hold them and the rate measured is HBM's.
 Prints ONE JSON line on stdout. Also reported (in "also"): the M-RoPE
 prefill in both section layouts, the fp32 partial interleaved case, the fp16
 decode Q+K step (table and on the fly), the prefill and M-RoPE stored in
-bfloat16, the packed [Q|K|V] decode step and the decode step with the
-key/value cache append.
+bfloat16, the packed [Q|K|V] decode step, the decode step with the
+key/value cache append, and QK-norm + RoPE (prefill with a table, decode on
+the fly).
 """
 import argparse
 import hashlib
@@ -69,7 +70,8 @@ def setup(w, onthefly=False):
         return setup_kv_append(w, x0, dt, dev)
     ids_h = w.make_ids()
     ids0 = None if ids_h is None else torch.from_numpy(ids_h).to(dev)
-    k0 = to_device(w.make_k(), dev) if w.op == "rope_qk" else None
+    k0 = to_device(w.make_k(), dev) if w.op in ("rope_qk", "qk_norm") else None
+    wts = [to_device(a, dev) for a in w.make_norm_weights()] if w.op == "qk_norm" else None
     inv = rpe.rope_inv_freq(w.rotary_dim, w.cache_base, device=dev)
     if w.op == "rope" and not w.has_ids:
         cos, sin = rpe.rope_cos_sin_cache(inv, w.seq, dt, w.scaling)
@@ -91,6 +93,13 @@ def setup(w, onthefly=False):
                 x, cos, sin, ids, y, interleaved=w.interleaved,
                 num_heads=w.num_heads if w.rank == 3 else 0,
                 rotary_embedding_dim=w.rotary_embedding_dim))
+        elif w.op == "qk_norm":
+            k = k0.clone()
+            yq, yk = torch.empty_like(x), torch.empty_like(k)
+            tabs = dict(inv_freq=inv, attention_scaling=w.scaling) if onthefly else {}
+            launchers.append(rpe.rope_apply_qk_norm_launcher(
+                x, k, wts[0], wts[1], None if onthefly else cos, None if onthefly else sin, ids, yq, yk,
+                epsilon=1e-6, num_heads=w.num_heads, kv_num_heads=w.kv_num_heads, **tabs))
         elif w.op == "qkv_packed":
             y = torch.empty_like(x)
             launchers.append(rpe.rope_apply_qkv_packed_launcher(
@@ -286,7 +295,9 @@ def main():
                  (rope_inputs.with_dtype(rope_inputs.with_layout(rope_inputs.get("c4_mrope_f16_prefill"), 0),
                                          rope_inputs.BFLOAT16, "bf16"), False),
                  (rope_inputs.get("qkv_packed_f16_decode"), False),
-                 (rope_inputs.get("kv_append_f16_decode"), False)]
+                 (rope_inputs.get("kv_append_f16_decode"), False),
+                 (rope_inputs.get("qk_norm_f16_prefill"), False),
+                 (rope_inputs.get("qk_norm_f16_decode"), True)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
             r = measure(ew, min(args.steps, 100), min(args.warmup, 10), otf)

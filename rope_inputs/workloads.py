@@ -28,7 +28,7 @@ def seed(index: int, tensor: int) -> int:
 class Workload:
     index: int
     name: str
-    op: str                      # "rope", "mrope", "rope_qk", "qkv_packed" or "kv_append"
+    op: str                      # "rope", "mrope", "rope_qk", "qkv_packed", "kv_append", "qk_norm"
     dtype: type
     x_shape: Tuple[int, ...]     # X, or Q for rope_qk
     num_heads: int = 0
@@ -102,7 +102,8 @@ class Workload:
             return xy + self.tokens * 2 * self.half * self.itemsize + self.batch * 4
         coef = 4 * self.half if onthefly else self.tokens * 2 * self.half * self.itemsize
         n_id_streams = 3 if self.op == "mrope" else (1 if self.has_ids else 0)
-        return xy + coef + n_id_streams * self.tokens * 8
+        weights = 2 * self.head_size * self.itemsize if self.op == "qk_norm" else 0
+        return xy + coef + n_id_streams * self.tokens * 8 + weights
 
     def tokens_heads(self) -> int:
         """(token, head) rows rotated."""
@@ -117,6 +118,14 @@ class Workload:
 
     def make_k(self) -> np.ndarray:
         return normal_tensor(seed(self.index, 2), self.k_shape, self.dtype)
+
+    def make_norm_weights(self):
+        """qk_norm: (q_weight, k_weight), values 1 + N(0, 1/16) rounded to the type."""
+        out = []
+        for t in (5, 6):
+            v = 1.0 + 0.25 * normal_tensor(seed(self.index, t), (self.head_size,), np.float32)
+            out.append(normal_like_type(v, self.dtype))
+        return tuple(out)
 
     def make_v(self) -> np.ndarray:
         return normal_tensor(seed(self.index, 4), self.k_shape, self.dtype)
@@ -244,8 +253,32 @@ EXTRA_WORKLOADS = {
 }
 
 
+EXTRA_WORKLOADS.update({
+    "qk_norm_f16_prefill": Workload(
+        index=7, name="qk_norm_f16_prefill", op="qk_norm", dtype=np.float16,
+        x_shape=(4, 2048, 4096), num_heads=32, k_shape=(4, 2048, 1024), kv_num_heads=8,
+        cache_rows=8192, cache_base=1e6, extra={"ids": "offset_arange", "offset_bound": 4096},
+        description="QK-norm + RoPE prefill fp16 (Qwen3 layout): Q (4, 2048, 32x128), K (4, 2048, 8x128), "
+                    "RMSNorm weights (128,), ids = per-batch offset + arange, table (8192, 64) base 1e6"),
+    "qk_norm_f16_decode": Workload(
+        index=8, name="qk_norm_f16_decode", op="qk_norm", dtype=np.float16,
+        x_shape=(256, 1, 4096), num_heads=32, k_shape=(256, 1, 1024), kv_num_heads=8,
+        cache_rows=32768, cache_base=1e6, extra={"ids": "uniform", "id_bound": 32768},
+        description="QK-norm + RoPE decode fp16: batch 256, Q 32 + K 8 heads of 128, positions "
+                    "U[0, 32768), coefficients on the fly"),
+})
+
+
 def get(name: str) -> Workload:
     return WORKLOADS[name] if name in WORKLOADS else EXTRA_WORKLOADS[name]
+
+
+def normal_like_type(v: np.ndarray, dtype) -> np.ndarray:
+    """binary32 values rounded to `dtype` (bfloat16 as uint16 bits)."""
+    from .generators import BFLOAT16, bfloat16_bits
+    if np.dtype(dtype) == BFLOAT16:
+        return bfloat16_bits(v)
+    return v.astype(dtype)
 
 
 def with_dtype(w: Workload, dtype, tag: str) -> Workload:
