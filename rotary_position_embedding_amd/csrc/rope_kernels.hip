@@ -64,7 +64,7 @@ struct KArgs {
     int32_t xcd_remap, prompt;  // prompt: append kind, every sequence starts at 0
     float scaling, scale;
     float eps;                  // QK-norm epsilon
-    int32_t pad3;
+    float inv_d;                // QK-norm: 1/D rounded to binary32
     const int32_t* seqlens;     // append kind: total key length per sequence
     int64_t rows_out;           // append kind: cache rows
     uint32_t sel[kSelWords];
@@ -128,10 +128,40 @@ template <typename T> __device__ inline void mask_elem(u32x4& m, int e) {
 }
 
 __device__ inline u32x4 load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Activations are reached through pointers the compiler cannot trace back to
+// kernel arguments (the task selection hides them), so without a cast it
+// emits flat instructions; these go through global (address space 1) ones.
+#define ROPE_GLOBAL __attribute__((address_space(1)))
+__device__ inline u32x4 load16_global(const char* p) { return *(const ROPE_GLOBAL u32x4*)p; }
+__device__ inline u32x4 load_nt(const char* p) { return __builtin_nontemporal_load((const ROPE_GLOBAL u32x4*)p); }
+__device__ inline void store_nt(char* p, const u32x4& v) { __builtin_nontemporal_store(v, (ROPE_GLOBAL u32x4*)p); }
 __device__ inline void store16(char* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ inline u32x4 select_bits(const u32x4& keep_mask, const u32x4& keep, const u32x4& other) {
     return (keep & keep_mask) | (other & ~keep_mask);
+}
+
+// v from another lane of the same row of 16 lanes (DPP control word CTRL).
+template <int CTRL>
+__device__ inline float dpp_move(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum of v over aligned groups of W lanes (W a power of two <= 64, uniform);
+// every lane of a group receives the same total (pairs are combined
+// symmetrically, and a + b == b + a). Lanes 1 and 2 apart: quad permutes
+// [1,0,3,2] and [2,3,0,1]; the other quad of an 8-lane half: half-row mirror
+// (lane i <-> 7 - i); the other half of a 16-lane row: row mirror
+// (i <-> 15 - i); rows 16 and 32 apart: xor shuffles.
+__device__ inline float group_sum(float v, int W) {
+    if (W >= 2) v += dpp_move<0xb1>(v);
+    if (W >= 4) v += dpp_move<0x4e>(v);
+    if (W >= 8) v += dpp_move<0x141>(v);
+    if (W >= 16) v += dpp_move<0x140>(v);
+    if (W >= 32) v += __shfl_xor(v, 16);
+    if (W >= 64) v += __shfl_xor(v, 32);
+    return v;
 }
 
 // Coefficient of slot i at position p computed on the fly (PR #27590
@@ -304,10 +334,10 @@ __device__ inline void load_batch(const char* x, const int64_t* off, const bool*
 #pragma unroll
         for (int m = 0; m < IPL; ++m) {
             if (act[m] && h + u < h_end) {
-                const u32x4* px = reinterpret_cast<const u32x4*>(x + off[m] + (int64_t)(h + u) * sh_bytes);
-                in1[u][m] = __builtin_nontemporal_load(px);
+                const char* px = x + off[m] + (int64_t)(h + u) * sh_bytes;
+                in1[u][m] = load_nt(px);
                 if (!IL && rot[m])
-                    in2[u][m] = __builtin_nontemporal_load(px + half_bytes / 16);
+                    in2[u][m] = load_nt(px + half_bytes);
             }
         }
     }
@@ -495,13 +525,31 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         }
     }
 
-    // QK-norm (one item per lane): the weights of the item's elements
+    // QK-norm (one item per lane): the weights of the item's elements, and
+    // per slot the weights folded into the coefficients, so that per head
+    // y1 = (1/rms) * (x1*(w1*c) - x2*(w2*s)), y2 = (1/rms) * (x2*(w2*c) + x1*(w1*s))
     float gw1[NORM ? E : 1], gw2[NORM ? E : 1];
+    float fa1[NORM ? E : 1], fb1[NORM ? E : 1], fa2[NORM ? E : 1], fb2[NORM ? E : 1];
+    bool kany = false;  // some lane of the wave keeps pairs (gathered kind)
     if (NORM) {
-        const auto w1 = chunk_values<T>(load16(tk.wgt + elem0[0] * ES));
-        const auto w2 = chunk_values<T>(load16(tk.wgt + (elem0[0] + (rot[0] && !IL ? a.P : 0)) * ES));
+        const auto w1 = chunk_values<T>(load16_global(tk.wgt + elem0[0] * ES));
+        const auto w2 = chunk_values<T>(load16_global(tk.wgt + (elem0[0] + (rot[0] && !IL ? a.P : 0)) * ES));
 #pragma unroll
         for (int e = 0; e < E; ++e) { gw1[e] = to_f(w1[e]); gw2[e] = to_f(w2[e]); }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = IL ? e / 2 : e;
+            const float c = to_f(cf[0][j]), s = to_f(sf[0][j]);
+            // split halves: element e pairs with its partner chunk's element e;
+            // interleaved: elements 2j and 2j+1 of this chunk
+            const float wa = IL ? gw1[2 * j] : gw1[e];
+            const float wb = IL ? gw1[2 * j + 1] : gw2[e];
+            fa1[e] = wa * c;
+            fb1[e] = wb * s;
+            fa2[e] = wb * c;
+            fb2[e] = wa * s;
+        }
+        if (COEF == kCoefGather) kany = __ballot(keep[0][0] != 0u) != 0;
     }
 
     // -- rotate and store, one head batch at a time --------------------------
@@ -525,51 +573,61 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         for (int e = 0; e < E; ++e) ss = fmaf(to_f(v2[e]), to_f(v2[e]), ss);
                     }
                 }
-                for (int o = 1; o < a.W; o <<= 1) ss += __shfl_xor(ss, o);
-                rn[u] = 1.0f / sqrtf(ss / (float)a.D + a.eps);
+                ss = group_sum(ss, a.W);
+                rn[u] = rsqrtf(ss * a.inv_d + a.eps);  // v_rsq_f32: about 1 ulp
             }
 #pragma unroll
             for (int u = 0; u < HU; ++u) {
                 if (!(wr[0] && h + u < h_end)) continue;
-                u32x4* py = reinterpret_cast<u32x4*>(tk.y + yoff[0] + (int64_t)(h + u) * ysh_bytes);
+                char* py = tk.y + yoff[0] + (int64_t)(h + u) * ysh_bytes;
+                const float r = rn[u];
                 const auto xv1 = chunk_values<T>(in1[u][0]);
-                float z1[E];
-#pragma unroll
-                for (int e = 0; e < E; ++e) z1[e] = (to_f(xv1[e]) * rn[u]) * gw1[e];
                 if (!rot[0]) {
-                    __builtin_nontemporal_store(chunk_pack<T>(z1), py);
+                    float z[E];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) z[e] = (to_f(xv1[e]) * r) * gw1[e];
+                    store_nt(py, chunk_pack<T>(z));
                     continue;
                 }
                 if (IL) {
-                    float r[E];
+                    float o[E];
 #pragma unroll
                     for (int j = 0; j < CE; ++j) {
-                        const float c = to_f(cf[0][j]), s = to_f(sf[0][j]);
-                        r[2 * j] = fmaf(z1[2 * j], c, -(z1[2 * j + 1] * s));
-                        r[2 * j + 1] = fmaf(z1[2 * j + 1], c, z1[2 * j] * s);
+                        const float x1 = to_f(xv1[2 * j]), x2 = to_f(xv1[2 * j + 1]);
+                        o[2 * j] = r * fmaf(x1, fa1[2 * j], -(x2 * fb1[2 * j]));
+                        o[2 * j + 1] = r * fmaf(x2, fa2[2 * j], x1 * fb2[2 * j]);
                     }
-                    u32x4 o = chunk_pack<T>(r);
-                    if (COEF == kCoefGather) o = select_bits(keep[0], chunk_pack<T>(z1), o);
-                    __builtin_nontemporal_store(o, py);
+                    u32x4 ov = chunk_pack<T>(o);
+                    if (COEF == kCoefGather && kany) {
+                        float z[E];
+#pragma unroll
+                        for (int e = 0; e < E; ++e) z[e] = (to_f(xv1[e]) * r) * gw1[e];
+                        ov = select_bits(keep[0], chunk_pack<T>(z), ov);
+                    }
+                    store_nt(py, ov);
                 } else {
                     const auto xv2 = chunk_values<T>(in2[u][0]);
-                    float z2[E], r1[E], r2[E];
+                    float o1[E], o2[E];
 #pragma unroll
-                    for (int e = 0; e < E; ++e) z2[e] = (to_f(xv2[e]) * rn[u]) * gw2[e];
+                    for (int e = 0; e < E; ++e) {
+                        const float x1 = to_f(xv1[e]), x2 = to_f(xv2[e]);
+                        o1[e] = r * fmaf(x1, fa1[e], -(x2 * fb1[e]));
+                        o2[e] = r * fmaf(x2, fa2[e], x1 * fb2[e]);
+                    }
+                    u32x4 ov1 = chunk_pack<T>(o1);
+                    u32x4 ov2 = chunk_pack<T>(o2);
+                    if (COEF == kCoefGather && kany) {
+                        float z1[E], z2[E];
 #pragma unroll
-                    for (int j = 0; j < E; ++j) {
-                        const float c = to_f(cf[0][j]), s = to_f(sf[0][j]);
-                        r1[j] = fmaf(z1[j], c, -(z2[j] * s));
-                        r2[j] = fmaf(z2[j], c, z1[j] * s);
+                        for (int e = 0; e < E; ++e) {
+                            z1[e] = (to_f(xv1[e]) * r) * gw1[e];
+                            z2[e] = (to_f(xv2[e]) * r) * gw2[e];
+                        }
+                        ov1 = select_bits(keep[0], chunk_pack<T>(z1), ov1);
+                        ov2 = select_bits(keep[0], chunk_pack<T>(z2), ov2);
                     }
-                    u32x4 o1 = chunk_pack<T>(r1);
-                    u32x4 o2 = chunk_pack<T>(r2);
-                    if (COEF == kCoefGather) {
-                        o1 = select_bits(keep[0], chunk_pack<T>(z1), o1);
-                        o2 = select_bits(keep[0], chunk_pack<T>(z2), o2);
-                    }
-                    __builtin_nontemporal_store(o1, py);
-                    __builtin_nontemporal_store(o2, py + half_bytes / 16);
+                    store_nt(py, ov1);
+                    store_nt(py + half_bytes, ov2);
                 }
             }
             if (h + HU < h_end)
@@ -581,9 +639,9 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 #pragma unroll
             for (int m = 0; m < IPL; ++m) {
                 if (!(wr[m] && h + u < h_end)) continue;
-                u32x4* py = reinterpret_cast<u32x4*>(tk.y + yoff[m] + (int64_t)(h + u) * ysh_bytes);
+                char* py = tk.y + yoff[m] + (int64_t)(h + u) * ysh_bytes;
                 if (!rot[m]) {
-                    __builtin_nontemporal_store(in1[u][m], py);
+                    store_nt(py, in1[u][m]);
                     continue;
                 }
                 if (IL) {
@@ -600,7 +658,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     u32x4 o = chunk_pack<T>(r);
                     if (COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy)
                         o = select_bits(keep[m], in1[u][m], o);
-                    __builtin_nontemporal_store(o, py);
+                    store_nt(py, o);
                 } else {
                     const auto xv1 = chunk_values<T>(in1[u][m]);
                     const auto xv2 = chunk_values<T>(in2[u][m]);
@@ -619,8 +677,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         o1 = select_bits(keep[m], in1[u][m], o1);
                         o2 = select_bits(keep[m], in2[u][m], o2);
                     }
-                    __builtin_nontemporal_store(o1, py);
-                    __builtin_nontemporal_store(o2, py + half_bytes / 16);
+                    store_nt(py, o1);
+                    store_nt(py + half_bytes, o2);
                 }
             }
         }
@@ -914,6 +972,7 @@ int launch_plan(const Plan& pl, void* stream) {
     a.scaling = p.scaling;
     a.scale = p.scale;
     a.eps = p.eps;
+    a.inv_d = 1.0f / (float)p.D;
     a.seqlens = p.seqlens;
     a.prompt = p.prompt;
     a.rows_out = p.rows_out;

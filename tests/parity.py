@@ -99,13 +99,15 @@ def ulp_of(want):
 def assert_parity_norm(got, want, zmax, what=""):
     """QK-norm + RoPE tolerance: |gpu - oracle| <= 1 ulp of the oracle value
     + 2^-18 * zmax, zmax the largest |z_j| = |x_j w_j| / rms of the element's
-    head row (broadcast to the output's shape). Bound: the binary32 sum of
-    squares (at most ~20 roundings of positive terms), mean, epsilon, square
-    root and reciprocal leave 1/rms within ~13 * 2^-24 relative; z = (x/rms)*w
-    adds 2 roundings; the fma rotation of z adds ~2 more on |z1 c| + |z2 s|
-    <= 2 * zmax * max|c, s|. That is <= ~34 * 2^-24 * zmax * max|c, s| ~ 2^-19
-    * zmax for coefficients up to 1.25; 2^-18 leaves a factor of two. The
-    final rounding to the storage type adds one unit."""
+    head row (broadcast to the output's shape). Worst-case first-order bound
+    for the binary32 path, u = 2^-24: the sum of squares has at most ~22
+    roundings of positive terms (16 in a lane, log2 W across lanes); the
+    mean and epsilon add ~2.5, so the reciprocal square root (v_rsq_f32,
+    taken as 2u) is within ~14.3u relative; each rotated term x*(w*c)
+    carries 3 more roundings and the scale by 1/rms one, so before the final
+    rounding |error| <= ~18.3u * (|z1 c| + |z2 s|) <= ~18.3u * 2 * zmax * 1.25
+    ~ 2^-18.5 * zmax for coefficients up to 1.25. The final rounding to the
+    storage type adds one unit."""
     g = values(got).reshape(-1)
     w = values(want).reshape(-1)
     tol = ulp_of(want).reshape(-1) + 2.0 ** -18 * np.broadcast_to(zmax, got.shape).reshape(-1)
