@@ -42,7 +42,9 @@
  *     stream) and returns. Results are ready when the stream reaches them.
  *   - Validation is complete before anything is enqueued: a non-zero return
  *     means nothing was launched. ROPE_ERR_LAUNCH means a launch was
- *     attempted and the HIP runtime refused it.
+ *     attempted and the HIP runtime refused it. ROPE_ERR_UNSUPPORTED is also
+ *     returned, before any launch, for a problem whose grid would exceed
+ *     2^31 - 1 workgroups (inputs of about 2^39 elements).
  *   - A tensor with a zero dimension is valid; an op whose output is empty
  *     launches nothing and returns ROPE_OK. Data pointers of non-empty
  *     tensors must not be NULL.

@@ -982,7 +982,10 @@ int launch_plan(const Plan& pl, void* stream) {
     if (g.vector) {
         const int64_t waves = wave_begin;
         if (waves == 0) return ROPE_OK;
-        const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+        const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+        if (blocks > INT32_MAX)  // beyond the grid limit (about 2^39 elements): refuse, never wrap
+            return fail(ROPE_ERR_UNSUPPORTED, "launch of %lld workgroups exceeds the grid limit", (long long)blocks);
+        const dim3 grid((unsigned)blocks);
         const int ipl = g.items_per_lane;
         const int hu = g.head_batch;
         if (p.dtype == ROPE_FLOAT16)

@@ -484,3 +484,34 @@ def test_empty_table_copies_everything(policy):
     ids3 = ids_in(9303, (3, 2, 9), 5)
     y4 = host(rpe.mrope_apply(cuda(x4), cuda(ids3), cos, cos.clone(), mrope_section=(16, 24, 24)))
     assert_bitwise(y4, x4, "empty table, M-RoPE")
+
+
+# ---------------------------------------------------------------------------
+# 64-bit addressing: more than 2^31 elements (4 GiB of float16 in and out)
+
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+def test_more_than_2_31_elements(policy):
+    """X (1, 524291, 4096) float16 = 2^31 + 12288 elements, made on the GPU by
+    torch's seeded generator (not by this library); sampled token rows, among
+    them the ones past the 2^31-element and 4 GiB marks, against the oracle."""
+    rpe.set_kernel_policy(policy)
+    S, H, D, M = 524291, 32, 128, 8192
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(0x5EED)
+    x = torch.randn((1, S, H * D), generator=gen, dtype=torch.float16, device=DEV)
+    ids_h = ((np.arange(S, dtype=np.int64) * 7 + 3) % M).reshape(1, S)
+    inv = oracle.inv_freq(1e6, D)
+    cos, sin = oracle.cos_sin_cache(np.float16, M, inv)
+    y = rpe.rope_apply(x, cuda(cos), cuda(sin), cuda(ids_h), num_heads=H)
+    torch.cuda.synchronize()
+    picks = np.unique(np.concatenate([
+        [0, 1, S // 2, 524287, 524288, 524289, S - 2, S - 1],
+        ids_in(0x5EEE, (64,), S)]))
+    sel = torch.from_numpy(picks).to(DEV)
+    xs = host(x[0].index_select(0, sel))[None]                 # (1, k, H*D)
+    ys = host(y[0].index_select(0, sel))[None]
+    want = oracle.rope_apply(xs, cos, sin, ids_h[:, picks], num_heads=H)
+    r = assert_parity(ys, want, "rows %s" % picks[:8].tolist())
+    print("2^31+ elements policy=%d rows=%d %s" % (policy, picks.size, r), flush=True)
+    del x, y
+    torch.cuda.empty_cache()
