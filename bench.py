@@ -239,7 +239,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE,
                     help="workload to time alone (for profiler runs); implies --no-extra")
     ap.add_argument("--onthefly", action="store_true", help="with the decode Q+K workload")
-    ap.add_argument("--bf16", action="store_true", help="time the workload stored in bfloat16")
+    ap.add_argument("--dtype", choices=["bf16", "f32", "f16"], default=None,
+                    help="time the workload stored in this type instead of its own")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -277,8 +278,9 @@ def main():
 
     only = args.workload != HEADLINE or args.no_extra
     w = rope_inputs.get(args.workload)
-    if args.bf16:
-        w = rope_inputs.with_dtype(w, rope_inputs.BFLOAT16, "bf16")
+    if args.dtype:
+        dt = {"bf16": rope_inputs.BFLOAT16, "f32": np.float32, "f16": np.float16}[args.dtype]
+        w = rope_inputs.with_dtype(w, dt, args.dtype)
     log("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
     head = measure(w, args.steps, args.warmup, args.onthefly)
     log("  %.2f us/step, %.1f GB/s (%.1f%% of %g)" % (
