@@ -243,7 +243,7 @@ static void choose_geometry(Plan* pl) {
     for (int t = 0; t < p.ntask; ++t) total_heads += p.task[t].heads;
     int64_t hpw_cap = hb;
     while (hpw_cap > 2 && groups * ((total_heads + hpw_cap - 1) / hpw_cap) < 1024) hpw_cap /= 2;
-    if (over > 0 && over < hpw_cap) hpw_cap = over;  // a wave holds at most one batch
+    if (over > 0) hpw_cap = over;  // tuning override (a wave loops over its batches)
     // Wave order: rank 4 keeps a head's tokens contiguous, so a tile of 4
     // token groups per head chunk gives each workgroup longer runs per head.
     const char* remap = getenv("ROPE_XCD_REMAP");
