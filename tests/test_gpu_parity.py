@@ -7,7 +7,7 @@ import torch
 import oracle
 import rotary_position_embedding_amd as rpe
 from oracle_pins import angle_table, ids_in, pair_index
-from parity import assert_bitwise, assert_parity, bits, compare
+from parity import assert_bitwise, assert_parity, assert_parity_binary32_range, bits, compare
 from gpu_io import DEV, cuda, host, one, torch_dtype
 from rope_inputs import BFLOAT16, WORKLOADS, normal_tensor, with_dtype, with_layout
 
@@ -515,3 +515,62 @@ def test_more_than_2_31_elements(policy):
     print("2^31+ elements policy=%d rows=%d %s" % (policy, picks.size, r), flush=True)
     del x, y
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# degenerate values: signed zeros, infinities, NaN, subnormals, the largest
+# finite values (rotations by unit-bounded coefficients cannot overflow a
+# binary32 product, so the binary32 path and the oracle meet the same
+# overflows)
+
+def _special_values(dt):
+    if np.dtype(dt) == np.float16:
+        v = [0.0, -0.0, np.inf, -np.inf, np.nan, 6.0e-8, -6.0e-8, 6.1e-5, 65504.0, -65504.0, 1.0, -3.5]
+        return np.array(v, np.float16)
+    if np.dtype(dt) == np.float32:
+        v = [0.0, -0.0, np.inf, -np.inf, np.nan, 1.4e-45, -1.4e-45, 1.2e-38, 3.4e38, -3.4e38, 1.0, -3.5]
+        return np.array(v, np.float32)
+    from rope_inputs import bfloat16_bits
+    f = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 9.2e-41, -9.2e-41, 1.2e-38, 3.38e38, -3.38e38, 1.0, -3.5],
+                 np.float32)
+    bits_ = bfloat16_bits(np.where(np.isfinite(f), f, 0.0))
+    bits_[2], bits_[3], bits_[4] = 0x7f80, 0xff80, 0x7fc1
+    return bits_
+
+
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("dt", [np.float16, np.float32, BFLOAT16])
+@pytest.mark.parametrize("il", [0, 1])
+def test_special_values(dt, il, policy):
+    rpe.set_kernel_policy(policy)
+    B, S, H, D, M = 2, 24, 3, 64, 6
+    sv = _special_values(dt)
+    pick = ids_in(14000 + il, (B, S, H, D), sv.size)
+    x = sv[pick]
+    x = np.ascontiguousarray(x.reshape(B, S, H * D))
+    th = np.array([0.0, np.pi / 2, np.pi, np.pi / 4, 1.0, 2.5])
+    c = np.cos(th)[:, None] * np.ones((1, D // 2))
+    s = np.sin(th)[:, None] * np.ones((1, D // 2))
+    if np.dtype(dt) == BFLOAT16:
+        from rope_inputs import bfloat16_bits
+        cos, sin = bfloat16_bits(c.astype(np.float32)), bfloat16_bits(s.astype(np.float32))
+    else:
+        cos, sin = c.astype(dt), s.astype(dt)
+    ids = ids_in(14002, (B, S), M)
+    want = oracle.rope_apply(x, cos, sin, ids, interleaved=il, num_heads=H)
+    got = host(rpe.rope_apply(cuda(x), cuda(cos), cuda(sin), cuda(ids), interleaved=il, num_heads=H))
+    what = "special values dt=%s il=%d" % (np.dtype(dt).name, il)
+    if np.dtype(dt) == np.float32:
+        # magnitudes of each element's two products, for the binary32-range bound
+        xr = x.reshape(B, S, H, D).astype(np.float64)
+        j1, j2 = pair_index(il, D // 2)
+        c64 = cos[ids][:, :, None, :].astype(np.float64)
+        s64 = sin[ids][:, :, None, :].astype(np.float64)
+        with np.errstate(invalid="ignore"):
+            mag = np.zeros_like(xr)
+            mag[..., j1] = np.abs(xr[..., j1] * c64) + np.abs(xr[..., j2] * s64)
+            mag[..., j2] = np.abs(xr[..., j2] * c64) + np.abs(xr[..., j1] * s64)
+        r = assert_parity_binary32_range(got, want, mag.reshape(B, S, H * D), what)
+    else:
+        r = assert_parity(got, want, what)
+    log("special values %s il=%d policy=%d %s" % (np.dtype(dt).name, il, policy, r))
