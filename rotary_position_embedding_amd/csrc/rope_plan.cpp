@@ -10,6 +10,7 @@
 // Every failing clause returns its status and records a message.
 #include "rope_plan.hpp"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -34,13 +35,10 @@ int fail(int code, const char* fmt, ...) {
 void clear_error() { g_error[0] = '\0'; }
 const char* last_error() { return g_error; }
 
-static int g_policy = 0;
-int kernel_policy() { return g_policy; }
-int set_kernel_policy(int policy) {
-    int old = g_policy;
-    g_policy = policy;
-    return old;
-}
+// process-wide; atomic so that concurrent calls see one value or the other
+static std::atomic<int> g_policy{0};
+int kernel_policy() { return g_policy.load(std::memory_order_relaxed); }
+int set_kernel_policy(int policy) { return g_policy.exchange(policy, std::memory_order_relaxed); }
 
 // ---------------------------------------------------------------------------
 // tensor descriptors
