@@ -574,3 +574,31 @@ def test_special_values(dt, il, policy):
     else:
         r = assert_parity(got, want, what)
     log("special values %s il=%d policy=%d %s" % (np.dtype(dt).name, il, policy, r))
+
+
+def test_side_streams():
+    """Calls are enqueued on the caller's current stream: two side streams run
+    independent problems concurrently, and each result equals the oracle once
+    its own stream is synchronised."""
+    B, S, H, D, M = 2, 300, 8, 128, 1024
+    inv = oracle.inv_freq(1e6, D)
+    cos, sin = oracle.cos_sin_cache(np.float16, M, inv)
+    cos_t, sin_t = cuda(cos), cuda(sin)
+    cases = []
+    for i in range(2):
+        x = normal_tensor(15000 + i, (B, S, H * D), np.float16)
+        ids = ids_in(15010 + i, (B, S), M)
+        cases.append((x, ids, cuda(x), cuda(ids)))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for (x, ids, xt, it), st in zip(cases, streams):
+        with torch.cuda.stream(st):
+            y = torch.empty_like(xt)
+            for _ in range(20):
+                rpe.rope_apply(xt, cos_t, sin_t, it, num_heads=H, out=y)
+            outs.append(y)
+    for (x, ids, _xt, _it), st, y in zip(cases, streams, outs):
+        st.synchronize()
+        want = oracle.rope_apply(x, cos, sin, ids, num_heads=H)
+        assert_parity(y.cpu().numpy(), want, "side stream")
