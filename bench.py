@@ -9,6 +9,10 @@ seeded synthetic tensors resident in HBM before the timed region; launches
 rotate over independent (X, Y, ids) sets totalling >= 1 GiB so that the 256 MB
 last-level cache cannot hold them and the rate measured is HBM's.
 
+Decode-sized workloads (a few MB per step) are bound by the host's per-call
+cost when launched one by one; for them the rates come from the same launches
+captured in one HIP graph and replayed (the eager time is reported too).
+
 Prints ONE JSON line on stdout. Also reported (in "also"): the M-RoPE
 prefill in both section layouts, the fp32 partial interleaved case, the fp16
 decode Q+K step (table and on the fly), the prefill and M-RoPE stored in
@@ -176,20 +180,57 @@ def time_steps(launchers, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
-def measure(w, steps, warmup, onthefly=False):
-    launchers, rot = setup(w, onthefly)
-    ms = time_steps(launchers, steps, warmup)
+def time_steps_graph(launchers, steps, warmup):
+    """Mean ms per launch with the K launches captured in one HIP graph and
+    replayed: what the GPU takes per step once the host's per-call cost is
+    out of the way (decode steps are that small). The launchers were bound
+    to the capture stream when they were made."""
+    import torch
+    n = len(launchers)
+    for i in range(warmup):
+        launchers[i % n]()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=torch.cuda.current_stream()):
+        for i in range(steps):
+            launchers[i % n]()
+    g.replay()                       # first replay uploads the graph
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def measure(w, steps, warmup, onthefly=False, graph=False):
+    """Eager timing; with graph=True also the HIP-graph replay timing, which
+    then gives the rates (the launch-bound decode steps)."""
+    import torch
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):    # launchers bind the stream they are made on
+        launchers, rot = setup(w, onthefly)
+        ms = time_steps(launchers, steps, warmup)
+        ms_graph = time_steps_graph(launchers, steps, warmup) if graph else None
+    torch.cuda.synchronize()
     nbytes = w.algorithmic_bytes(onthefly)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    return {
+    ms_rate = ms_graph if graph else ms
+    gbs = nbytes / (ms_rate * 1e-3) / 1e9
+    r = {
         "workload": w.name + ("_onthefly" if onthefly else ""),
         "bytes_per_step": nbytes,
-        "ms_per_step": ms,
+        "ms_per_step": ms_rate,
         "gbs": gbs,
         "frac_of_peak": gbs / PEAK_GBS,
-        "tokens_heads_per_s": w.tokens_heads() / (ms * 1e-3),
+        "tokens_heads_per_s": w.tokens_heads() / (ms_rate * 1e-3),
         "rotation_sets_bytes": rot,
     }
+    if graph:
+        r["ms_per_step_eager"] = ms
+        r["rates_from"] = "hip_graph"
+    return r
 
 
 # ---------------------------------------------------------------------------
@@ -282,7 +323,7 @@ def main():
         dt = {"bf16": rope_inputs.BFLOAT16, "f32": np.float32, "f16": np.float16}[args.dtype]
         w = rope_inputs.with_dtype(w, dt, args.dtype)
     log("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
-    head = measure(w, args.steps, args.warmup, args.onthefly)
+    head = measure(w, args.steps, args.warmup, args.onthefly, graph=w.tokens <= 4096)
     log("  %.2f us/step, %.1f GB/s (%.1f%% of %g)" % (
         head["ms_per_step"] * 1e3, head["gbs"], 100 * head["frac_of_peak"], PEAK_GBS))
 
@@ -302,9 +343,14 @@ def main():
                  (rope_inputs.get("qk_norm_f16_decode"), True)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
-            r = measure(ew, min(args.steps, 100), min(args.warmup, 10), otf)
-            log("  %.2f us/step, %.1f GB/s (%.1f%% of peak)" % (
-                r["ms_per_step"] * 1e3, r["gbs"], 100 * r["frac_of_peak"]))
+            decode = ew.tokens <= 4096
+            r = measure(ew, min(args.steps, 100), min(args.warmup, 10), otf, graph=decode)
+            if decode:
+                log("  %.2f us/step in a HIP graph (%.2f eager): %.1f GB/s (%.1f%% of peak)" % (
+                    r["ms_per_step"] * 1e3, r["ms_per_step_eager"] * 1e3, r["gbs"], 100 * r["frac_of_peak"]))
+            else:
+                log("  %.2f us/step, %.1f GB/s (%.1f%% of peak)" % (
+                    r["ms_per_step"] * 1e3, r["gbs"], 100 * r["frac_of_peak"]))
             also.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
 
     cpu = None
