@@ -8,8 +8,14 @@
 //   elements R..D-1 copied -- same, rotary_embedding_dim.
 // Coefficient rows: gathered by position id, per-token, M-RoPE (slot i from
 // its stream's row, scaled and rounded to the storage type, out-of-range id
-// copies the pair -- "com.microsoft.MRotaryEmbedding" README), or computed
-// on the fly from inv_freq (PR #27590 Motivation).
+// copies the pair -- "com.microsoft.MRotaryEmbedding" README), computed
+// on the fly from inv_freq (PR #27590 Motivation), or gathered at the
+// position past + s of a key/value cache append, whose K and V rows are
+// written to that cache row ("com.microsoft.SparseAttention" README).
+// With the QK-norm, each head row is first RMS-normalised and weighted (PR
+// #27590 review, Qwen3 architecture) and the rotation acts on the result.
+// A launch holds up to three tasks (Q, K, V or a packed [Q|K|V]); storage is
+// float32, float16 or bfloat16.
 //
 // Per fp16 pair the op moves 8 bytes (read 4, write 4) and does 6 flops:
 // it is HBM-bound and has no contraction, so no MFMA. Design:
