@@ -536,7 +536,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     // y1 = (1/rms) * (x1*(w1*c) - x2*(w2*s)), y2 = (1/rms) * (x2*(w2*c) + x1*(w1*s))
     float gw1[NORM ? E : 1], gw2[NORM ? E : 1];
     float fa1[NORM ? E : 1], fb1[NORM ? E : 1], fa2[NORM ? E : 1], fb2[NORM ? E : 1];
-    bool kany = false;  // some lane of the wave keeps pairs (gathered kind)
+    bool kany = false;  // some lane of the wave keeps input bits (pairs or a copied task)
     if (NORM) {
         const auto w1 = chunk_values<T>(load16_global(tk.wgt + elem0[0] * ES));
         const auto w2 = chunk_values<T>(load16_global(tk.wgt + (elem0[0] + (rot[0] && !IL ? a.P : 0)) * ES));
@@ -556,6 +556,12 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
             fb2[e] = wa * s;
         }
         if (COEF == kCoefGather) kany = __ballot(keep[0][0] != 0u) != 0;
+    } else if (COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend) {
+        // some lane of the wave keeps an element: only then merge input bits
+        bool k = tk.copy != 0;
+#pragma unroll
+        for (int m = 0; m < IPL; ++m) k = k || (keep[m][0] | keep[m][1] | keep[m][2] | keep[m][3]) != 0u;
+        kany = __ballot(k) != 0;
     }
 
     // -- rotate and store, one head batch at a time --------------------------
@@ -662,7 +668,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         r[2 * j + 1] = fmaf(x2, c, x1 * s);
                     }
                     u32x4 o = chunk_pack<T>(r);
-                    if (COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy)
+                    if ((COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy) && kany)
                         o = select_bits(keep[m], in1[u][m], o);
                     store_nt(py, o);
                 } else {
@@ -679,7 +685,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     }
                     u32x4 o1 = chunk_pack<T>(r1);
                     u32x4 o2 = chunk_pack<T>(r2);
-                    if (COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy) {
+                    if ((COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy) && kany) {
                         o1 = select_bits(keep[m], in1[u][m], o1);
                         o2 = select_bits(keep[m], in2[u][m], o2);
                     }
