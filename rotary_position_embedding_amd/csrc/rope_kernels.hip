@@ -71,6 +71,8 @@ struct KArgs {
     float scaling, scale;
     float eps;                  // QK-norm epsilon
     float inv_d;                // QK-norm: 1/D rounded to binary32
+    int32_t share_coef;         // on the fly: the waves of a workgroup split the slots
+    int32_t pad4;
     const int32_t* seqlens;     // append kind: total key length per sequence
     int64_t rows_out;           // append kind: cache rows
     uint32_t sel[kSelWords];
@@ -520,6 +522,26 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     if (cj) { mask_elem<T>(keep[m], 2 * j); mask_elem<T>(keep[m], 2 * j + 1); }
                 }
             }
+        } else if (a.share_coef) {
+            // The four waves of this workgroup hold the same token group and
+            // lane mapping (the host guarantees it): each computes every
+            // fourth slot, and the values are exchanged through LDS.
+            __shared__ float lds_c[CE * 64], lds_s[CE * 64];
+#pragma unroll
+            for (int j = 0; j < CE; ++j) {
+                if (j % kWavesPerBlock != wave_in_block) continue;
+                float c, s;
+                onthefly_coef<T>(a.inv_freq[slot0[m] + j], pos[m][0], a.scaling, c, s);
+                lds_c[j * 64 + lane] = c;
+                lds_s[j * 64 + lane] = s;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < CE; ++j) {
+                cf[m][j] = from_f<T>(lds_c[j * 64 + lane]);
+                sf[m][j] = from_f<T>(lds_s[j * 64 + lane]);
+            }
+            __syncthreads();  // the next item reuses the buffers
         } else {
 #pragma unroll
             for (int j = 0; j < CE; ++j) {
@@ -984,6 +1006,7 @@ int launch_plan(const Plan& pl, void* stream) {
     a.scaling = p.scaling;
     a.scale = p.scale;
     a.eps = p.eps;
+    a.share_coef = g.vector && g.share_coef;
     a.inv_d = 1.0f / (float)p.D;
     a.seqlens = p.seqlens;
     a.prompt = p.prompt;

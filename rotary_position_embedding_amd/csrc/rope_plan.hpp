@@ -75,6 +75,7 @@ struct Geometry {
     int32_t TG;           // tokens per wave
     int32_t tile;         // token groups per head chunk in a tile of waves
     int32_t xcd_remap;    // 1: consecutive workgroups on one XCD
+    int32_t share_coef;   // on the fly: the 4 waves of a workgroup share one token group
     int32_t heads_per_wave[kMaxPlanTasks];
     int32_t chunks[kMaxPlanTasks];  // head chunks per token group
     int64_t waves[kMaxPlanTasks];
