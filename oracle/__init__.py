@@ -84,7 +84,8 @@ class Oracle:
             "oracle_rope_apply_qk": ([i32, i32, i64, i64, i64, i64, i64, i64, i64,
                                       vp, vp, vp, vp, vp, vp, vp, i64, vp, f32], None),
             "oracle_rope_kv_append": ([i32, i64, i64, i64, i64, i64, i64, i64,
-                                       vp, vp, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp], None),
+                                       vp, vp, vp, vp, i64, vp, vp, i64, vp, vp, i64, vp,
+                                       vp, vp, f32], None),
             "oracle_rope_apply_qk_norm": ([i32, i32, i64, i64, i64, i64, i64, i64, i64,
                                            vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, i64, vp, f32], None),
         }
@@ -239,11 +240,13 @@ class Oracle:
         return yq, yk
 
     def rope_kv_append(self, query, key, value, past_key, past_value, key_total_sequence_lengths,
-                       total_sequence_length, cos, sin, num_heads, kv_num_heads, interleaved=0):
+                       total_sequence_length, cos, sin, num_heads, kv_num_heads, interleaved=0,
+                       q_weight=None, k_weight=None, epsilon=0.0):
         """RoPE on Q and K and the key/value cache append. query (B,S,H*D), or
         packed [Q|K|V] when key and value are None; past_key/past_value
         (B,Hk,Smax,D) are copied and the updated copies returned with q_out:
-        (q_out, present_key, present_value)."""
+        (q_out, present_key, present_value). With q_weight and k_weight ((D,)),
+        Q and K are RMS-normalised first (QK-norm)."""
         query = _dense(query)
         packed = key is None
         if packed != (value is None):
@@ -262,11 +265,16 @@ class Oracle:
         if (Bc, Hk, Dc) != (B, kv_num_heads, D) or pv.shape != pk.shape:
             raise ValueError("cache shape disagrees with the inputs")
         R = 2 * cos.shape[1]
+        qwt = _dense(q_weight, query.dtype)
+        kwt = _dense(k_weight, query.dtype)
+        if (qwt is None) != (kwt is None):
+            raise ValueError("q_weight and k_weight are both given or both None")
         q_out = np.zeros((B, S, num_heads * D), query.dtype)
         self.lib.oracle_rope_kv_append(_code(query.dtype), B, S, num_heads, kv_num_heads, D, R, interleaved,
                                        _ptr(query), _ptr(key), _ptr(value), _ptr(lens),
                                        int(total_sequence_length), _ptr(cos), _ptr(sin), cos.shape[0],
-                                       _ptr(pk), _ptr(pv), Smax, _ptr(q_out))
+                                       _ptr(pk), _ptr(pv), Smax, _ptr(q_out), _ptr(qwt), _ptr(kwt),
+                                       float(epsilon))
         return q_out, pk, pv
 
 

@@ -434,6 +434,13 @@ void oracle_rope_apply_qk(int dtype, int rank, int64_t B, int64_t S, int64_t H,
  * which bounds L[b] by total_sequence_length and that by the cache).
  * key == NULL: query is packed, per token H query heads, then Hk key heads,
  * then Hk value heads. */
+static void norm_row(int dtype, const void* x, int64_t off, const void* w,
+                     int64_t D, double eps, double* z);
+static void rotate_values(int dtype, const double* z, void* y, int64_t off,
+                          int64_t D, int64_t R, int64_t interleaved,
+                          const double* c, const double* s,
+                          const unsigned char* copy);
+
 void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
                            int64_t Hk, int64_t D, int64_t R,
                            int64_t interleaved, const void* query,
@@ -442,7 +449,8 @@ void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
                            int64_t total_sequence_length,
                            const void* cos_cache, const void* sin_cache,
                            int64_t M, void* past_key, void* past_value,
-                           int64_t Smax, void* q_out)
+                           int64_t Smax, void* q_out, const void* q_weight,
+                           const void* k_weight, float epsilon)
 {
     int64_t half = R / 2;
     int packed = key == NULL;
@@ -454,7 +462,8 @@ void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
     int64_t v0 = packed ? (H + Hk) * D : 0;
     int prompt = total_sequence_length == S;
     coef_row cr;
-    if (!coef_alloc(&cr, half))
+    double* z = (double*)calloc((size_t)(D > 0 ? D : 1), sizeof(double));
+    if (!z || !coef_alloc(&cr, half))
         abort();
     for (int64_t b = 0; b < B; ++b) {
         int64_t past = prompt ? 0 : (int64_t)key_total_sequence_lengths[b] - S;
@@ -469,16 +478,31 @@ void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
                 }
             }
             int64_t tok = b * S + s;
-            for (int64_t h = 0; h < H; ++h)
-                rotate_row_to(dtype, query, tok * qw + h * D, q_out,
-                              (tok * H + h) * D, D, R, interleaved, cr.c, cr.s,
-                              cr.copy);
+            for (int64_t h = 0; h < H; ++h) {
+                if (q_weight) { /* QK-norm first (oracle_rope_apply_qk_norm) */
+                    norm_row(dtype, query, tok * qw + h * D, q_weight, D,
+                             (double)epsilon, z);
+                    rotate_values(dtype, z, q_out, (tok * H + h) * D, D, R,
+                                  interleaved, cr.c, cr.s, cr.copy);
+                } else {
+                    rotate_row_to(dtype, query, tok * qw + h * D, q_out,
+                                  (tok * H + h) * D, D, R, interleaved, cr.c,
+                                  cr.s, cr.copy);
+                }
+            }
             if (p < 0 || p >= Smax)
                 continue;
             for (int64_t h = 0; h < Hk; ++h) {
                 int64_t dst = ((b * Hk + h) * Smax + p) * D;
-                rotate_row_to(dtype, ksrc, tok * kw + k0 + h * D, past_key, dst,
-                              D, R, interleaved, cr.c, cr.s, cr.copy);
+                if (k_weight) {
+                    norm_row(dtype, ksrc, tok * kw + k0 + h * D, k_weight, D,
+                             (double)epsilon, z);
+                    rotate_values(dtype, z, past_key, dst, D, R, interleaved,
+                                  cr.c, cr.s, cr.copy);
+                } else {
+                    rotate_row_to(dtype, ksrc, tok * kw + k0 + h * D, past_key,
+                                  dst, D, R, interleaved, cr.c, cr.s, cr.copy);
+                }
                 for (int64_t j = 0; j < D; ++j)
                     copy_elem_to(dtype, vsrc, tok * kw + v0 + h * D + j,
                                  past_value, dst + j);
@@ -486,6 +510,7 @@ void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
         }
     }
     coef_free(&cr);
+    free(z);
 }
 
 /* ------------------------------------------------------------------------ */

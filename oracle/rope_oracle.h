@@ -124,7 +124,10 @@ void oracle_rope_apply_qk(int dtype, int rank, int64_t B, int64_t S, int64_t H,
  * key_total_sequence_lengths[b] - S (reading taken). Token s has position
  * p = past + s: Q and K rows rotated with table row p (p outside [0, M)
  * keeps the pairs), Q to q_out, K and V (bit copy) to cache row p when
- * 0 <= p < Smax (rows outside are not written). */
+ * 0 <= p < Smax (rows outside are not written).
+ * q_weight/k_weight non-NULL: the Q, resp. K, rows are first RMS-normalised
+ * exactly as in oracle_rope_apply_qk_norm (epsilon; V is never normalised):
+ * the decode step of a model with QK-norm, in one call. */
 void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
                            int64_t Hk, int64_t D, int64_t R,
                            int64_t interleaved, const void* query,
@@ -133,7 +136,8 @@ void oracle_rope_kv_append(int dtype, int64_t B, int64_t S, int64_t H,
                            int64_t total_sequence_length,
                            const void* cos_cache, const void* sin_cache,
                            int64_t M, void* past_key, void* past_value,
-                           int64_t Smax, void* q_out);
+                           int64_t Smax, void* q_out, const void* q_weight,
+                           const void* k_weight, float epsilon);
 
 /* QK-norm then RoPE ([PR] review, Qwen3 architecture: RMSNorm on Q and K
  * before RoPE). Each head row x of Q (K) becomes

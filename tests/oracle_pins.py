@@ -814,6 +814,44 @@ def pin_kv_append_out_of_contract(orc):
     assert_bitwise(ko[2, 0, :4], pk[2, 0, :4], "batch 2: rows below the past untouched")
 
 
+def pin_kv_append_with_qk_norm(orc):
+    """With QK-norm weights the append equals QK-norm + RoPE of Q and K at the
+    positions past + s (oracle_rope_apply_qk_norm, pinned below), K scattered
+    into the key cache, V copied unnormalised; packed input alike."""
+    for dt in (np.float16, BF16, np.float32):
+        for il in (0, 1):
+            B, S, H, Hk, D, Smax, M = 3, 2, 4, 2, 16, 11, 14
+            q = normal_any(291, (B, S, H * D), dt)
+            k = normal_any(292, (B, S, Hk * D), dt)
+            v = normal_any(293, (B, S, Hk * D), dt)
+            pk = normal_any(294, (B, Hk, Smax, D), dt)
+            wq = normal_any(295, (D,), dt)
+            wk = normal_any(296, (D,), dt)
+            cos, sin = angle_table(297, M, 6, dt)           # R = 12 < D: a normalised tail
+            lens = np.array([2, 9, 11], np.int32)
+            for total in (11, 2):
+                got = orc.rope_kv_append(q, k, v, pk, pk, lens, total, cos, sin, H, Hk, interleaved=il,
+                                         q_weight=wq, k_weight=wk, epsilon=1e-6)
+                pos = _kv_positions(B, S, lens, total)
+                eq, ek_rot = orc.rope_apply_qk_norm(q, k, wq, wk, 1e-6, cos, sin, pos, interleaved=il,
+                                                    num_heads=H, kv_num_heads=Hk, rotary_embedding_dim=12)
+                ek, ev = pk.copy(), pk.copy()
+                for b in range(B):
+                    for s_ in range(S):
+                        ek[b, :, pos[b, s_], :] = ek_rot[b, s_].reshape(Hk, D)
+                        ev[b, :, pos[b, s_], :] = v[b, s_].reshape(Hk, D)
+                for g, w, what in zip(got, (eq, ek, ev), ("q_out", "key cache", "value cache")):
+                    assert_bitwise(g, w, "norm append %s dt=%s il=%d total=%d" % (what, np.dtype(dt).name,
+                                                                                  il, total))
+            qkv = np.concatenate([q, k, v], -1)
+            a = orc.rope_kv_append(qkv, None, None, pk, pk, lens, 11, cos, sin, H, Hk, interleaved=il,
+                                   q_weight=wq, k_weight=wk, epsilon=1e-6)
+            b_ = orc.rope_kv_append(q, k, v, pk, pk, lens, 11, cos, sin, H, Hk, interleaved=il,
+                                    q_weight=wq, k_weight=wk, epsilon=1e-6)
+            for x, y in zip(a, b_):
+                assert_bitwise(x, y, "packed norm append")
+
+
 # --------------------------------------------------------------------------
 # QK-norm (RMSNorm over the head row) then RoPE
 

@@ -60,6 +60,10 @@ MUTANTS = {
                               "norm_row(dtype, k, off, q_weight, D, (double)epsilon, z);")],
     "norm_tail_not_normalised": [("        store_elem(dtype, y, off + j, z[j]);\n}",
                                   "        store_elem(dtype, y, off + j, z[j] / z[j] * 0.0 + 1.0);\n}")],
+    "kv_norm_value_normalised": [("                    copy_elem_to(dtype, vsrc, tok * kw + v0 + h * D + j,\n                                 past_value, dst + j);",
+                                  "                    store_elem(dtype, past_value, dst + j, z[j]);")],
+    "kv_norm_k_uses_q_weight": [("norm_row(dtype, ksrc, tok * kw + k0 + h * D, k_weight, D,",
+                                 "norm_row(dtype, ksrc, tok * kw + k0 + h * D, q_weight, D,")],
     "inv_freq_exponent": [("-2.0 * (double)i / (double)rotary_dim", "-1.0 * (double)i / (double)rotary_dim")],
     "onthefly_uses_position_zero": [("coefficient(dtype, p, inv_freq[i], scaling, &cr.c[i], &cr.s[i]);",
                                      "coefficient(dtype, 0, inv_freq[i], scaling, &cr.c[i], &cr.s[i]);")],
