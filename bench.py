@@ -17,8 +17,8 @@ Prints ONE JSON line on stdout. Also reported (in "also"): the M-RoPE
 prefill in both section layouts, the fp32 partial interleaved case, the fp16
 decode Q+K step (table and on the fly), the prefill and M-RoPE stored in
 bfloat16, the packed [Q|K|V] decode step, the decode step with the
-key/value cache append, and QK-norm + RoPE (prefill with a table, decode on
-the fly).
+key/value cache append, QK-norm + RoPE (prefill with a table, decode on the
+fly), and the QK-norm decode step with the cache append.
 """
 import argparse
 import hashlib
@@ -70,7 +70,7 @@ def setup(w, onthefly=False):
     dt = {np.dtype(np.float16): torch.float16, np.dtype(np.float32): torch.float32,
           np.dtype(np.uint16): torch.bfloat16}[np.dtype(w.dtype)]
     x0 = to_device(w.make_x(), dev)
-    if w.op == "kv_append":
+    if w.op in ("kv_append", "kv_append_norm"):
         return setup_kv_append(w, x0, dt, dev)
     ids_h = w.make_ids()
     ids0 = None if ids_h is None else torch.from_numpy(ids_h).to(dev)
@@ -148,13 +148,19 @@ def setup_kv_append(w, q0, dt, dev):
     set_bytes = 2 * (q0.numel() + 2 * k0.numel()) * q0.element_size()
     nsets = max(2, -(-ROTATE_BYTES // set_bytes))
     launchers = []
+    wts = [to_device(a, dev) for a in w.make_norm_weights()] if w.op == "kv_append_norm" else None
     for i in range(nsets):
         lens_h = ((lens0.astype(np.int64) - 1 + 997 * i) % smax + 1).astype(np.int32)
         q, k, v = q0.clone(), k0.clone(), v0.clone()
         lens = torch.from_numpy(lens_h).to(dev)
-        launchers.append(rpe.rope_kv_append_launcher(
-            q, k, v, pk, pv, lens, int(lens_h.max()), cos, sin, torch.empty_like(q),
-            num_heads=w.num_heads, kv_num_heads=Hk))
+        if wts is None:
+            launchers.append(rpe.rope_kv_append_launcher(
+                q, k, v, pk, pv, lens, int(lens_h.max()), cos, sin, torch.empty_like(q),
+                num_heads=w.num_heads, kv_num_heads=Hk))
+        else:
+            launchers.append(rpe.rope_kv_append_qk_norm_launcher(
+                q, k, v, pk, pv, lens, int(lens_h.max()), cos, sin, torch.empty_like(q), wts[0], wts[1],
+                epsilon=1e-6, num_heads=w.num_heads, kv_num_heads=Hk))
     torch.cuda.synchronize()
     return launchers, nsets * set_bytes
 
@@ -340,7 +346,8 @@ def main():
                  (rope_inputs.get("qkv_packed_f16_decode"), False),
                  (rope_inputs.get("kv_append_f16_decode"), False),
                  (rope_inputs.get("qk_norm_f16_prefill"), False),
-                 (rope_inputs.get("qk_norm_f16_decode"), True)]
+                 (rope_inputs.get("qk_norm_f16_decode"), True),
+                 (rope_inputs.get("qk_norm_kv_append_f16_decode"), False)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
             decode = ew.tokens <= 4096

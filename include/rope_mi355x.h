@@ -24,6 +24,8 @@
  *                      value caches in place, one launch --
  *                      "com.microsoft.SparseAttention" README (Description,
  *                      Inputs, Outputs, Attributes).
+ *   rope_kv_append_qk_norm  the same with Q and K RMS-normalised first
+ *                      (QK-norm before RoPE, as rope_apply_qk_norm).
  *   rope_inv_freq,     the frequency vector and the cos/sin table the
  *   rope_cos_sin_cache gathered ops read -- PR #27590 review item 4
  *                      (cos_cache = cos(pos * inv_freq) * scaling).
@@ -277,6 +279,27 @@ int rope_kv_append(const rope_tensor* query, const rope_tensor* key,
                    int64_t kv_num_heads, void* stream);
 
 /*
+ * rope_kv_append_qk_norm -- rope_kv_append with each Q and K head row first
+ * RMS-normalised exactly as rope_apply_qk_norm does (weights q_weight and
+ * k_weight, type T, shape (D,); epsilon finite and >= 0): the decode step of
+ * a model with QK-norm (PR #27590 review, Qwen3 architecture) before
+ * attention, in one launch. V is copied into the value cache unnormalised.
+ * Arguments, layouts and bounds otherwise as rope_kv_append; the outputs and
+ * caches may not overlap the weights.
+ */
+int rope_kv_append_qk_norm(const rope_tensor* query, const rope_tensor* key,
+                           const rope_tensor* value, const rope_tensor* past_key,
+                           const rope_tensor* past_value,
+                           const rope_tensor* key_total_sequence_lengths,
+                           int64_t total_sequence_length,
+                           const rope_tensor* cos_cache,
+                           const rope_tensor* sin_cache,
+                           const rope_tensor* q_out, const rope_tensor* q_weight,
+                           const rope_tensor* k_weight, float epsilon,
+                           int64_t rotary_interleaved, int64_t num_heads,
+                           int64_t kv_num_heads, void* stream);
+
+/*
  * rope_inv_freq -- inv_freq[i] = rnd_f32(base^(-2i/R)) for i < R/2 with
  * R = 2 * dim 0 of inv_freq (float32, rank 1). The pages take inv_freq from
  * the model; this is the standard schedule. base must be > 0.
@@ -357,6 +380,21 @@ int rope_kv_append_check(const rope_tensor* query, const rope_tensor* key,
                          const rope_tensor* q_out, int64_t rotary_interleaved,
                          int64_t num_heads, int64_t kv_num_heads,
                          const char** variant);
+
+int rope_kv_append_qk_norm_check(const rope_tensor* query,
+                                 const rope_tensor* key,
+                                 const rope_tensor* value,
+                                 const rope_tensor* past_key,
+                                 const rope_tensor* past_value,
+                                 const rope_tensor* key_total_sequence_lengths,
+                                 int64_t total_sequence_length,
+                                 const rope_tensor* cos_cache,
+                                 const rope_tensor* sin_cache,
+                                 const rope_tensor* q_out,
+                                 const rope_tensor* q_weight,
+                                 const rope_tensor* k_weight, float epsilon,
+                                 int64_t rotary_interleaved, int64_t num_heads,
+                                 int64_t kv_num_heads, const char** variant);
 
 /*
  * Kernel choice for all ops: 0 = automatic (vector kernels where shapes and

@@ -95,14 +95,15 @@ class Workload:
         xy = 2 * int(np.prod(self.x_shape)) * self.itemsize
         if self.k_shape is not None:
             xy += 2 * int(np.prod(self.k_shape)) * self.itemsize
-        if self.op == "kv_append":
+        if self.op in ("kv_append", "kv_append_norm"):
             # Q read + written, K and V read and written to one cache row each,
             # the per-sequence lengths (int32) instead of ids
             xy += 2 * int(np.prod(self.k_shape)) * self.itemsize
-            return xy + self.tokens * 2 * self.half * self.itemsize + self.batch * 4
+            w = 2 * self.head_size * self.itemsize if self.op == "kv_append_norm" else 0
+            return xy + self.tokens * 2 * self.half * self.itemsize + self.batch * 4 + w
         coef = 4 * self.half if onthefly else self.tokens * 2 * self.half * self.itemsize
         n_id_streams = 3 if self.op == "mrope" else (1 if self.has_ids else 0)
-        weights = 2 * self.head_size * self.itemsize if self.op == "qk_norm" else 0
+        weights = 2 * self.head_size * self.itemsize if self.op in ("qk_norm", "kv_append_norm") else 0
         return xy + coef + n_id_streams * self.tokens * 8 + weights
 
     def tokens_heads(self) -> int:
@@ -260,6 +261,12 @@ EXTRA_WORKLOADS.update({
         cache_rows=8192, cache_base=1e6, extra={"ids": "offset_arange", "offset_bound": 4096},
         description="QK-norm + RoPE prefill fp16 (Qwen3 layout): Q (4, 2048, 32x128), K (4, 2048, 8x128), "
                     "RMSNorm weights (128,), ids = per-batch offset + arange, table (8192, 64) base 1e6"),
+    "qk_norm_kv_append_f16_decode": Workload(
+        index=9, name="qk_norm_kv_append_f16_decode", op="kv_append_norm", dtype=np.float16,
+        x_shape=(256, 1, 4096), num_heads=32, k_shape=(256, 1, 1024), kv_num_heads=8,
+        cache_rows=32768, cache_base=1e6, extra={"cache_seq": 4096},
+        description="QK-norm model decode step: Q 32 + K, V 8 heads of 128 (batch 256), RMSNorm of Q and "
+                    "K, RoPE, K and V appended to (256, 8, 4096, 128) caches, lengths U[1, 4096]"),
     "qk_norm_f16_decode": Workload(
         index=8, name="qk_norm_f16_decode", op="qk_norm", dtype=np.float16,
         x_shape=(256, 1, 4096), num_heads=32, k_shape=(256, 1, 1024), kv_num_heads=8,

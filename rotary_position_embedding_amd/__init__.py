@@ -25,7 +25,8 @@ __all__ = ["RopeError", "rope_apply", "mrope_apply", "rope_apply_qk", "rope_inv_
            "rope_apply_launcher", "mrope_apply_launcher", "rope_apply_qk_launcher",
            "rope_apply_qkv_packed", "rope_apply_qkv_packed_check", "rope_apply_qkv_packed_launcher",
            "rope_kv_append", "rope_kv_append_check", "rope_kv_append_launcher",
-           "rope_apply_qk_norm", "rope_apply_qk_norm_check", "rope_apply_qk_norm_launcher"]
+           "rope_apply_qk_norm", "rope_apply_qk_norm_check", "rope_apply_qk_norm_launcher",
+           "rope_kv_append_qk_norm", "rope_kv_append_qk_norm_check", "rope_kv_append_qk_norm_launcher"]
 
 _DTYPE = {torch.float32: ROPE_FLOAT, torch.float16: ROPE_FLOAT16, torch.int64: ROPE_INT64,
           torch.bfloat16: ROPE_BFLOAT16, torch.int32: ROPE_INT32}
@@ -270,6 +271,58 @@ def rope_kv_append_launcher(query, key, value, past_key, past_value, key_total_s
     return Launcher(_lib.load().rope_kv_append, args,
                     (ds, query, key, value, past_key, past_value, key_total_sequence_lengths, cos_cache,
                      sin_cache, out))
+
+
+def _q_out_for(query, key, num_heads, kv_num_heads):
+    B, S, width = query.shape
+    groups = num_heads + (2 * kv_num_heads if key is None else 0)
+    return torch.empty(B, S, width // groups * num_heads if groups else 0, dtype=query.dtype,
+                       device=query.device)
+
+
+def rope_kv_append_qk_norm(query, key, value, past_key, past_value, key_total_sequence_lengths,
+                           total_sequence_length, cos_cache, sin_cache, q_weight, k_weight, *, epsilon,
+                           num_heads, kv_num_heads, rotary_interleaved=0, out=None):
+    """rope_kv_append with Q and K RMS-normalised first (QK-norm weights (D,),
+    epsilon); V copied as it is. Returns q_out; the caches are updated in place."""
+    dev = _device_of(query)
+    out = _q_out_for(query, key, num_heads, kv_num_heads) if out is None else out
+    ds = [_desc(t, dev) for t in (query, key, value, past_key, past_value, key_total_sequence_lengths,
+                                  cos_cache, sin_cache, out, q_weight, k_weight)]
+    with _on_device(dev):
+        _check(_lib.load().rope_kv_append_qk_norm(
+            *[_lib.ref(d) for d in ds[:6]], int(total_sequence_length), *[_lib.ref(d) for d in ds[6:11]],
+            float(epsilon), rotary_interleaved, num_heads, kv_num_heads, _stream(dev)))
+    return out
+
+
+def rope_kv_append_qk_norm_check(query, key, value, past_key, past_value, key_total_sequence_lengths,
+                                 total_sequence_length, cos_cache, sin_cache, q_out, q_weight, k_weight, *,
+                                 epsilon, num_heads, kv_num_heads, rotary_interleaved=0):
+    v = _variant_out()
+    refs = [_lib.ref(d) for d in (query, key, value, past_key, past_value, key_total_sequence_lengths)]
+    rc = _lib.load().rope_kv_append_qk_norm_check(
+        *refs, int(total_sequence_length), _lib.ref(cos_cache), _lib.ref(sin_cache), _lib.ref(q_out),
+        _lib.ref(q_weight), _lib.ref(k_weight), float(epsilon), rotary_interleaved, num_heads, kv_num_heads,
+        ctypes.byref(v))
+    return rc, (v.value.decode() if rc == 0 and v.value else None)
+
+
+def rope_kv_append_qk_norm_launcher(query, key, value, past_key, past_value, key_total_sequence_lengths,
+                                    total_sequence_length, cos_cache, sin_cache, out, q_weight, k_weight, *,
+                                    epsilon, num_heads, kv_num_heads, rotary_interleaved=0):
+    dev = _device_of(query)
+    ds = [_desc(t, dev) for t in (query, key, value, past_key, past_value, key_total_sequence_lengths,
+                                  cos_cache, sin_cache, out, q_weight, k_weight)]
+    rc, _ = rope_kv_append_qk_norm_check(*ds[:6], total_sequence_length, *ds[6:], epsilon=epsilon,
+                                         num_heads=num_heads, kv_num_heads=kv_num_heads,
+                                         rotary_interleaved=rotary_interleaved)
+    _check(rc)
+    args = [_lib.ref(d) for d in ds[:6]] + [int(total_sequence_length)] + [_lib.ref(d) for d in ds[6:11]] + \
+        [float(epsilon), rotary_interleaved, num_heads, kv_num_heads, _stream(dev)]
+    return Launcher(_lib.load().rope_kv_append_qk_norm, args,
+                    (ds, query, key, value, past_key, past_value, key_total_sequence_lengths, cos_cache,
+                     sin_cache, out, q_weight, k_weight))
 
 
 def rope_inv_freq(rotary_dim, base, device="cuda", out=None):

@@ -49,6 +49,10 @@ SIGNATURES = {
     "rope_apply_qkv_packed_check": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _ccp], _int),
     "rope_apply_qk_norm": ([_vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _vp], _int),
     "rope_apply_qk_norm_check": ([_vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _f32, _ccp], _int),
+    "rope_kv_append_qk_norm": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _f32,
+                                _i64, _i64, _i64, _vp], _int),
+    "rope_kv_append_qk_norm_check": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _f32,
+                                      _i64, _i64, _i64, _ccp], _int),
     "rope_kv_append": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _vp], _int),
     "rope_kv_append_check": ([_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _ccp], _int),
 }

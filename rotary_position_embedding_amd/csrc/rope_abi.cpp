@@ -187,6 +187,44 @@ int rope_kv_append(const rope_tensor* query, const rope_tensor* key, const rope_
     return rope::launch_plan(pl, stream);
 }
 
+int rope_kv_append_qk_norm_check(const rope_tensor* query, const rope_tensor* key,
+                                 const rope_tensor* value, const rope_tensor* past_key,
+                                 const rope_tensor* past_value,
+                                 const rope_tensor* key_total_sequence_lengths,
+                                 int64_t total_sequence_length, const rope_tensor* cos_cache,
+                                 const rope_tensor* sin_cache, const rope_tensor* q_out,
+                                 const rope_tensor* q_weight, const rope_tensor* k_weight,
+                                 float epsilon, int64_t rotary_interleaved, int64_t num_heads,
+                                 int64_t kv_num_heads, const char** variant) {
+    Plan pl;
+    int rc = rope::plan_rope_kv_append_qk_norm(query, key, value, past_key, past_value,
+                                               key_total_sequence_lengths, total_sequence_length,
+                                               cos_cache, sin_cache, q_out, q_weight, k_weight,
+                                               epsilon, rotary_interleaved, num_heads, kv_num_heads,
+                                               &pl);
+    if (rc == ROPE_OK && variant) *variant = pl.g.variant;
+    return rc;
+}
+
+int rope_kv_append_qk_norm(const rope_tensor* query, const rope_tensor* key,
+                           const rope_tensor* value, const rope_tensor* past_key,
+                           const rope_tensor* past_value,
+                           const rope_tensor* key_total_sequence_lengths,
+                           int64_t total_sequence_length, const rope_tensor* cos_cache,
+                           const rope_tensor* sin_cache, const rope_tensor* q_out,
+                           const rope_tensor* q_weight, const rope_tensor* k_weight, float epsilon,
+                           int64_t rotary_interleaved, int64_t num_heads, int64_t kv_num_heads,
+                           void* stream) {
+    Plan pl;
+    int rc = rope::plan_rope_kv_append_qk_norm(query, key, value, past_key, past_value,
+                                               key_total_sequence_lengths, total_sequence_length,
+                                               cos_cache, sin_cache, q_out, q_weight, k_weight,
+                                               epsilon, rotary_interleaved, num_heads, kv_num_heads,
+                                               &pl);
+    if (rc != ROPE_OK) return rc;
+    return rope::launch_plan(pl, stream);
+}
+
 int rope_inv_freq(const rope_tensor* inv_freq, double base, void* stream) {
     float* out;
     int64_t half;

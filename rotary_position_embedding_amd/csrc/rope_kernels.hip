@@ -559,7 +559,9 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     float gw1[NORM ? E : 1], gw2[NORM ? E : 1];
     float fa1[NORM ? E : 1], fb1[NORM ? E : 1], fa2[NORM ? E : 1], fb2[NORM ? E : 1];
     bool kany = false;  // some lane of the wave keeps input bits (pairs or a copied task)
-    if (NORM) {
+    // a copied task (V of the cache append) is never normalised
+    const bool norm = NORM && !tk.copy;
+    if (norm) {
         const auto w1 = chunk_values<T>(load16_global(tk.wgt + elem0[0] * ES));
         const auto w2 = chunk_values<T>(load16_global(tk.wgt + (elem0[0] + (rot[0] && !IL ? a.P : 0)) * ES));
 #pragma unroll
@@ -577,7 +579,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
             fa2[e] = wb * c;
             fb2[e] = wa * s;
         }
-        if (COEF == kCoefGather) kany = __ballot(keep[0][0] != 0u) != 0;
+        if (COEF == kCoefGather || COEF == kCoefAppend) kany = __ballot(keep[0][0] != 0u) != 0;
     } else if (COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend) {
         // some lane of the wave keeps an element: only then merge input bits
         bool k = tk.copy != 0;
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 
     // -- rotate and store, one head batch at a time --------------------------
     for (int h = h_begin; h < h_end; h += HU) {
-        if (NORM) {
+        if (norm) {
             // RMSNorm of each head row first: the lane's sum of squares, summed
             // over the row's W lanes (an aligned group: W divides 64), then
             // z = (x / rms) * weight, rotated like x; kept pairs and tail
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         o[2 * j + 1] = r * fmaf(x2, fa2[2 * j], x1 * fb2[2 * j]);
                     }
                     u32x4 ov = chunk_pack<T>(o);
-                    if (COEF == kCoefGather && kany) {
+                    if ((COEF == kCoefGather || COEF == kCoefAppend) && kany) {
                         float z[E];
 #pragma unroll
                         for (int e = 0; e < E; ++e) z[e] = (to_f(xv1[e]) * r) * gw1[e];
@@ -650,7 +652,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     }
                     u32x4 ov1 = chunk_pack<T>(o1);
                     u32x4 ov2 = chunk_pack<T>(o2);
-                    if (COEF == kCoefGather && kany) {
+                    if ((COEF == kCoefGather || COEF == kCoefAppend) && kany) {
                         float z1[E], z2[E];
 #pragma unroll
                         for (int e = 0; e < E; ++e) {
@@ -785,8 +787,18 @@ __global__ __launch_bounds__(kBlock) void rope_norm_row_kernel(const KArgs a, in
         const int64_t b = n / a.S;
         const int64_t s = n - b * a.S;
         const int64_t base = b * tk.sb + h * tk.sh + s * tk.ss;
+        int64_t ybase = base;
+        if (COEF == kCoefAppend) {
+            const int64_t row = tk.yrow ? append_position(a, n) : s;
+            if (tk.yrow && (row < 0 || row >= a.rows_out)) continue;  // no such cache row
+            ybase = b * tk.ysb + h * tk.ysh + row * tk.yss;
+        }
         const B* xb = reinterpret_cast<const B*>(tk.x) + base;
-        B* yb = reinterpret_cast<B*>(tk.y) + base;
+        B* yb = reinterpret_cast<B*>(tk.y) + ybase;
+        if (tk.copy) {  // a copied task (V of the cache append): bits as they are
+            for (int j = 0; j < a.D; ++j) yb[j] = xb[j];
+            continue;
+        }
         const B* wb = reinterpret_cast<const B*>(tk.wgt);
         // the sum of squares in binary64 (one long sequential sum here)
         double ss = 0.0;
@@ -897,6 +909,7 @@ static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, d
             case kCoefGather: return launch_vec_norm<T, IL, kCoefGather>(a, hu, grid, st);
             case kCoefPerToken: return launch_vec_norm<T, IL, kCoefPerToken>(a, hu, grid, st);
             case kCoefOnTheFly: return launch_vec_norm<T, IL, kCoefOnTheFly>(a, hu, grid, st);
+            case kCoefAppend: return launch_vec_norm<T, IL, kCoefAppend>(a, hu, grid, st);
             default: return hipErrorInvalidValue;
         }
     }
@@ -921,6 +934,7 @@ static hipError_t launch_scalar(const KArgs& a, CoefKind c, int64_t total, hipSt
             case kCoefGather: fn = (const void*)rope_norm_row_kernel<T, kCoefGather>; break;
             case kCoefPerToken: fn = (const void*)rope_norm_row_kernel<T, kCoefPerToken>; break;
             case kCoefOnTheFly: fn = (const void*)rope_norm_row_kernel<T, kCoefOnTheFly>; break;
+            case kCoefAppend: fn = (const void*)rope_norm_row_kernel<T, kCoefAppend>; break;
             default: return hipErrorInvalidValue;
         }
         return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0, st);

@@ -147,8 +147,8 @@ static const char* variant_name(bool vec, CoefKind c, bool norm) {
         {"scalar/gather", "scalar/per_token", "scalar/mrope", "scalar/on_the_fly", "scalar/append"},
         {"vec16/gather", "vec16/per_token", "vec16/mrope", "vec16/on_the_fly", "vec16/append"}};
     static const char* norm_names[2][5] = {
-        {"scalar/norm/gather", "scalar/norm/per_token", "", "scalar/norm/on_the_fly", ""},
-        {"vec16/norm/gather", "vec16/norm/per_token", "", "vec16/norm/on_the_fly", ""}};
+        {"scalar/norm/gather", "scalar/norm/per_token", "", "scalar/norm/on_the_fly", "scalar/norm/append"},
+        {"vec16/norm/gather", "vec16/norm/per_token", "", "vec16/norm/on_the_fly", "vec16/norm/append"}};
     return (norm ? norm_names : names)[vec ? 1 : 0][(int)c];
 }
 
@@ -936,6 +936,48 @@ int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
     p.scaling = 1.0f;
     out->empty = B * S == 0;
     out->g.rank = 3;
+    choose_geometry(out);
+    return ROPE_OK;
+}
+
+// The cache append with QK-norm: Q and K RMS-normalised before the rotation
+// (PR #27590 review, Qwen3 architecture), V copied as it is: a QK-norm
+// model's decode step before attention, in one launch.
+int plan_rope_kv_append_qk_norm(const rope_tensor* query, const rope_tensor* key,
+                                const rope_tensor* value, const rope_tensor* past_key,
+                                const rope_tensor* past_value,
+                                const rope_tensor* key_total_sequence_lengths,
+                                int64_t total_sequence_length, const rope_tensor* cos_cache,
+                                const rope_tensor* sin_cache, const rope_tensor* q_out,
+                                const rope_tensor* q_weight, const rope_tensor* k_weight,
+                                float epsilon, int64_t interleaved, int64_t num_heads,
+                                int64_t kv_num_heads, Plan* out) {
+    TRY(plan_rope_kv_append(query, key, value, past_key, past_value, key_total_sequence_lengths,
+                            total_sequence_length, cos_cache, sin_cache, q_out, interleaved, num_heads,
+                            kv_num_heads, out));
+    if (!q_weight) return fail(ROPE_ERR_NULL, "q_weight is missing");
+    if (!k_weight) return fail(ROPE_ERR_NULL, "k_weight is missing");
+    TRY(check_desc(q_weight, "q_weight"));
+    TRY(check_desc(k_weight, "k_weight"));
+    Problem& p = out->p;
+    if (q_weight->dtype != p.dtype || k_weight->dtype != p.dtype)
+        return fail(ROPE_ERR_DTYPE, "q_weight and k_weight must have the type of query");
+    if (q_weight->rank != 1 || k_weight->rank != 1)
+        return fail(ROPE_ERR_RANK, "q_weight and k_weight must be rank 1 (head_size,)");
+    if (q_weight->shape[0] != p.D || k_weight->shape[0] != p.D)
+        return fail(ROPE_ERR_SHAPE, "q_weight and k_weight must be (%lld,)", (long long)p.D);
+    if (!(epsilon >= 0.0f) || !std::isfinite(epsilon))
+        return fail(ROPE_ERR_ATTRIBUTE, "epsilon must be finite and >= 0");
+    const rope_tensor* w[2] = {q_weight, k_weight};
+    const char* wn[2] = {"q_weight", "k_weight"};
+    TRY(check_output(q_out, "q_out", nullptr, w, wn, 2));
+    TRY(check_output(past_key, "past_key", nullptr, w, wn, 2));
+    TRY(check_output(past_value, "past_value", nullptr, w, wn, 2));
+    p.norm = 1;
+    p.eps = epsilon;
+    p.task[0].weight = q_weight->data;
+    p.task[1].weight = k_weight->data;
+    p.task[2].weight = nullptr;  // V: copied, never normalised
     choose_geometry(out);
     return ROPE_OK;
 }

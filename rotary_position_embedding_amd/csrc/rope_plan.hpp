@@ -132,6 +132,16 @@ int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
                         int64_t interleaved, int64_t num_heads, int64_t kv_num_heads,
                         Plan* out);
 
+int plan_rope_kv_append_qk_norm(const rope_tensor* query, const rope_tensor* key,
+                                const rope_tensor* value, const rope_tensor* past_key,
+                                const rope_tensor* past_value,
+                                const rope_tensor* key_total_sequence_lengths,
+                                int64_t total_sequence_length, const rope_tensor* cos_cache,
+                                const rope_tensor* sin_cache, const rope_tensor* q_out,
+                                const rope_tensor* q_weight, const rope_tensor* k_weight,
+                                float epsilon, int64_t interleaved, int64_t num_heads,
+                                int64_t kv_num_heads, Plan* out);
+
 struct TablePlan {
     const float* inv_freq;
     void* cos;

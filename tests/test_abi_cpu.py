@@ -626,3 +626,44 @@ def test_qk_norm_clauses():
         kw.update(over)
         rc, _ = check_norm(kw)
         assert rc == code, (name, rc, lib.rope_last_error())
+
+
+def kv_norm_case(dt=F16, **over):
+    kw = kv_case(dt=dt, D=128, **over)
+    a = Alloc()
+    a.next = 1 << 41
+    kw["q_weight"] = a(dt, (128,))
+    kw["k_weight"] = a(dt, (128,))
+    kw["epsilon"] = 1e-6
+    return kw
+
+
+def check_kv_norm(kw):
+    kw = dict(kw)
+    args = [kw.pop(k) for k in ("query", "key", "value", "past_key", "past_value",
+                                "key_total_sequence_lengths", "total_sequence_length",
+                                "cos_cache", "sin_cache", "q_out", "q_weight", "k_weight")]
+    return rpe.rope_kv_append_qk_norm_check(*args, **kw)
+
+
+def test_kv_append_qk_norm_accepted_and_clauses():
+    lib = _lib.load()
+    for dt in (F16, BF16, F32):
+        for packed in (False, True):
+            rc, v = check_kv_norm(kv_norm_case(dt=dt, packed=packed))
+            assert rc == OK, lib.rope_last_error()
+            assert v == "vec16/norm/append"
+    base = kv_norm_case()
+    cases = [
+        ("q_weight missing", NULL, dict(q_weight=None)),
+        ("weight dtype", DTYPE, dict(k_weight=reshape(base["k_weight"], (64,), F32))),
+        ("weight length", SHAPE, dict(q_weight=reshape(base["q_weight"], (64,)))),
+        ("epsilon negative", ATTR, dict(epsilon=-1.0)),
+        ("cache over a weight", ALIAS, dict(q_weight=reshape(base["past_key"], (128,)))),
+        ("append contract still applies", SHAPE, dict(total_sequence_length=2)),
+    ]
+    for name, code, over in cases:
+        kw = kv_norm_case()
+        kw.update(over)
+        rc, _ = check_kv_norm(kw)
+        assert rc == code, (name, rc, lib.rope_last_error())

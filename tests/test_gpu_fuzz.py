@@ -32,7 +32,7 @@ def pick(g, options):
 
 def config(i):
     g = SplitMix64(0xF022 + i)
-    op = pick(g, ["rope", "mrope", "qk", "packed", "qk_norm", "kv_append"])
+    op = pick(g, ["rope", "mrope", "qk", "packed", "qk_norm", "kv_append", "kv_append_norm"])
     dt = pick(g, [np.float16, np.float32, BFLOAT16])
     E = 4 if np.dtype(dt) == np.float32 else 8
     D = pick(g, [2, 6, 8, 10, 16, 24, 32, 48, 64, 96, 128, 160, 256, 2 * E * 3])
@@ -155,7 +155,7 @@ def test_fuzz(i):
         assert_parity(np.ascontiguousarray(gq), wq, "packed Q")
         assert_parity(np.ascontiguousarray(gk), wk, "packed K")
         assert_bitwise(np.ascontiguousarray(gv), v, "packed V")
-    else:  # kv_append (rank 3 only, table width R/2 with R <= D)
+    else:  # kv_append[_norm] (rank 3 only, table width R/2 with R <= D)
         Smax = S + int(SplitMix64(seed + 9).below(1, 20)[0])
         q = x_like(seed, (B, S, H * D), dt)
         k = x_like(seed + 5, (B, S, Hk * D), dt)
@@ -167,12 +167,25 @@ def test_fuzz(i):
         prompt = i % 3 == 0
         total = S if prompt else Smax
         lens = (ids_in(seed + 11, (B,), Smax - S + 1) + S).astype(np.int32)
-        eq, ek, ev = oracle.rope_kv_append(q, k, v, pk, pv, lens, total, ct, st, H, Hk, interleaved=il)
         gk_, gv_ = cuda(pk), cuda(pv)
         qt = cuda(q)
-        gq = rpe.rope_kv_append(qt, cuda(k), cuda(v), gk_, gv_, cuda(lens), total, cuda(ct), cuda(st),
-                                num_heads=H, kv_num_heads=Hk, rotary_interleaved=il,
-                                out=qt if c["inplace"] else None)
-        assert_parity(host(gq), eq, "q_out")
-        assert_parity(host(gk_), ek, "key cache")
+        if op == "kv_append":
+            eq, ek, ev = oracle.rope_kv_append(q, k, v, pk, pv, lens, total, ct, st, H, Hk, interleaved=il)
+            gq = rpe.rope_kv_append(qt, cuda(k), cuda(v), gk_, gv_, cuda(lens), total, cuda(ct), cuda(st),
+                                    num_heads=H, kv_num_heads=Hk, rotary_interleaved=il,
+                                    out=qt if c["inplace"] else None)
+            assert_parity(host(gq), eq, "q_out")
+            assert_parity(host(gk_), ek, "key cache")
+        else:
+            w1, w2 = weights(seed + 12, D, dt), weights(seed + 13, D, dt)
+            eq, ek, ev = oracle.rope_kv_append(q, k, v, pk, pv, lens, total, ct, st, H, Hk, interleaved=il,
+                                               q_weight=w1, k_weight=w2, epsilon=1e-6)
+            gq = rpe.rope_kv_append_qk_norm(qt, cuda(k), cuda(v), gk_, gv_, cuda(lens), total, cuda(ct),
+                                            cuda(st), cuda(w1), cuda(w2), epsilon=1e-6, num_heads=H,
+                                            kv_num_heads=Hk, rotary_interleaved=il,
+                                            out=qt if c["inplace"] else None)
+            assert_parity_norm(host(gq), eq, zmax_rows(q, w1, 1e-6, 3, H), "q_out")
+            # every cache element against the largest normalised K value of the batch
+            zk = np.max(zmax_rows(k, w2, 1e-6, 3, Hk)) if k.size else 0.0
+            assert_parity_norm(host(gk_), ek, np.full(ek.shape, zk), "key cache")
         assert_bitwise(host(gv_), ev, "value cache")

@@ -10,7 +10,7 @@ import oracle
 import rotary_position_embedding_amd as rpe
 from gpu_io import DEV, cuda, host, torch_dtype
 from oracle_pins import angle_table, ids_in
-from parity import assert_bitwise, assert_parity, bits
+from parity import assert_bitwise, assert_parity, assert_parity_norm, bits
 from rope_inputs import BFLOAT16, normal_tensor
 
 pytestmark = pytest.mark.gpu
@@ -143,3 +143,78 @@ def test_kv_append_decode_full_size():
     assert_parity(host(gk), wk, "present_key")
     assert_bitwise(host(gv), wv, "present_value")
     print("decode full size", r, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# with QK-norm first (the decode step of a QK-norm model)
+
+def norm_weights(seed, D, dt):
+    v = 1.0 + 0.25 * normal_tensor(seed, (D,), np.float32)
+    if np.dtype(dt) == BFLOAT16:
+        from rope_inputs import bfloat16_bits
+        return bfloat16_bits(v)
+    return v.astype(dt)
+
+
+def zmax(x, w, eps, heads):
+    def f64(a):
+        a = np.ascontiguousarray(a)
+        return ((a.astype(np.uint32) << 16).view(np.float32) if a.dtype == np.uint16 else a).astype(np.float64)
+    xd = f64(x)
+    B, S, _ = xd.shape
+    xd = xd.reshape(B, S, heads, -1)
+    z = np.abs(xd * f64(w)) / np.sqrt((xd ** 2).mean(-1, keepdims=True) + float(np.float32(eps)))
+    return z
+
+
+@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("case", [
+    # dt, B, S, H, Hk, D, width, Smax, M, total, il, packed
+    (np.float16, 64, 1, 32, 8, 128, 64, 256, 512, None, 0, False),
+    (BFLOAT16, 3, 9, 8, 2, 128, 32, 40, 64, 40, 1, False),
+    (np.float32, 2, 5, 4, 2, 64, 32, 16, 20, 5, 0, True),
+    (np.float16, 2, 3, 4, 1, 10, 3, 12, 12, 11, 0, False),    # scalar kernel
+], ids=["decode_f16", "chunk_bf16", "prompt_f32_packed", "odd_rows"])
+def test_kv_append_qk_norm(case, policy):
+    dt, B, S, H, Hk, D, width, Smax, M, total, il, packed = case
+    rpe.set_kernel_policy(policy)
+    eps = 1e-6
+    seed = 17000 + D + S
+    if total is None:
+        lens = (ids_in(seed, (B,), Smax) + 1).astype(np.int32)
+        total = int(lens.max())
+    else:
+        lens = (ids_in(seed, (B,), total - S + 1) + S).astype(np.int32)
+    q = normal_tensor(seed + 1, (B, S, H * D), dt)
+    k = normal_tensor(seed + 2, (B, S, Hk * D), dt)
+    v = normal_tensor(seed + 3, (B, S, Hk * D), dt)
+    pk = normal_tensor(seed + 4, (B, Hk, Smax, D), dt)
+    pv = normal_tensor(seed + 5, (B, Hk, Smax, D), dt)
+    wq, wk = norm_weights(seed + 6, D, dt), norm_weights(seed + 7, D, dt)
+    cos, sin = angle_table(seed + 8, M, width, dt)
+    if packed:
+        qkv = np.concatenate([q, k, v], -1)
+        eq, ek, ev = oracle.rope_kv_append(qkv, None, None, pk, pv, lens, total, cos, sin, H, Hk, interleaved=il,
+                                           q_weight=wq, k_weight=wk, epsilon=eps)
+        args = (cuda(qkv), None, None)
+    else:
+        eq, ek, ev = oracle.rope_kv_append(q, k, v, pk, pv, lens, total, cos, sin, H, Hk, interleaved=il,
+                                           q_weight=wq, k_weight=wk, epsilon=eps)
+        args = (cuda(q), cuda(k), cuda(v))
+    gk, gv = cuda(pk), cuda(pv)
+    gq = rpe.rope_kv_append_qk_norm(*args, gk, gv, cuda(lens), total, cuda(cos), cuda(sin), cuda(wq), cuda(wk),
+                                    epsilon=eps, num_heads=H, kv_num_heads=Hk, rotary_interleaved=il)
+    zq = zmax(q, wq, eps, H).max(-1, keepdims=True)
+    zq = np.broadcast_to(zq, (B, S, H, D)).reshape(B, S, H * D)
+    assert_parity_norm(host(gq), eq, zq, "q_out")
+    # key cache: rows written get the K bound, the others must be bit-identical
+    zk = zmax(k, wk, eps, Hk).max(-1)                    # (B, S, Hk)
+    zmax_cache = np.zeros((B, Hk, Smax, D))
+    past = np.zeros(B, np.int64) if total == S else lens.astype(np.int64) - S
+    for b in range(B):
+        for s in range(S):
+            r = past[b] + s
+            if 0 <= r < Smax:
+                zmax_cache[b, :, r, :] = zk[b, s][:, None]
+    assert_parity_norm(host(gk), ek, zmax_cache, "key cache")
+    assert_bitwise(host(gv), ev, "value cache")
