@@ -41,7 +41,6 @@ using half_t = _Float16;
 using bf16_t = __bf16;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWavesPerBlock = 4;
 constexpr int kBlock = 64 * kWavesPerBlock;
 
 constexpr int kMaxTasks = 3;
@@ -559,8 +558,9 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     float gw1[NORM ? E : 1], gw2[NORM ? E : 1];
     float fa1[NORM ? E : 1], fb1[NORM ? E : 1], fa2[NORM ? E : 1], fb2[NORM ? E : 1];
     bool kany = false;  // some lane of the wave keeps input bits (pairs or a copied task)
-    // a copied task (V of the cache append) is never normalised
-    const bool norm = NORM && !tk.copy;
+    // a copied task (V of the cache append, the only norm launch that has
+    // one) is never normalised; elsewhere the decision is compile-time
+    const bool norm = NORM && (COEF != kCoefAppend || !tk.copy);
     if (norm) {
         const auto w1 = chunk_values<T>(load16_global(tk.wgt + elem0[0] * ES));
         const auto w2 = chunk_values<T>(load16_global(tk.wgt + (elem0[0] + (rot[0] && !IL ? a.P : 0)) * ES));

@@ -258,14 +258,14 @@ static void choose_geometry(Plan* pl) {
         g.waves[t] = H > 0 ? tiles * g.tile * chunks : 0;
     }
     // On the fly, every head chunk of a token group computes the same
-    // coefficients. When each workgroup's four waves are four chunks of one
-    // token group of one task (a tile of one group, chunk counts divisible by
-    // four), they split that work and exchange it through LDS.
+    // coefficients. When each workgroup's waves are chunks of one token group
+    // of one task (a tile of one group, chunk counts divisible by the waves
+    // per workgroup), they split that work and exchange it through LDS.
     g.share_coef = 0;
     if (p.coef == kCoefOnTheFly && g.tile == 1 && env_int("ROPE_NO_SHARE") == 0) {
         bool ok_share = true;
         for (int t = 0; t < p.ntask; ++t)
-            if (p.task[t].heads > 0 && g.chunks[t] % 4 != 0) ok_share = false;
+            if (p.task[t].heads > 0 && g.chunks[t] % kWavesPerBlock != 0) ok_share = false;
         g.share_coef = ok_share ? 1 : 0;
     }
 }

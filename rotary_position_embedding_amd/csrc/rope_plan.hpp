@@ -40,6 +40,10 @@ struct Task {
 
 constexpr int kMaxPlanTasks = 3;
 
+// Waves per workgroup of the vector kernel (the planner's grouping rules
+// depend on it).
+constexpr int kWavesPerBlock = 4;
+
 struct Problem {
     int32_t dtype;        // ROPE_FLOAT, ROPE_FLOAT16 or ROPE_BFLOAT16
     int32_t interleaved;  // 0 or 1
