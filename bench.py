@@ -288,6 +288,10 @@ def main():
     ap.add_argument("--onthefly", action="store_true", help="with the decode Q+K workload")
     ap.add_argument("--dtype", choices=["bf16", "f32", "f16"], default=None,
                     help="time the workload stored in this type instead of its own")
+    ap.add_argument("--interleaved", type=int, choices=[0, 1], default=None,
+                    help="time the workload with this pairing instead of its own")
+    ap.add_argument("--rotary-dim", type=int, default=None,
+                    help="time the workload with this rotary_embedding_dim instead of its own")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -328,6 +332,11 @@ def main():
     if args.dtype:
         dt = {"bf16": rope_inputs.BFLOAT16, "f32": np.float32, "f16": np.float16}[args.dtype]
         w = rope_inputs.with_dtype(w, dt, args.dtype)
+    if args.interleaved is not None or args.rotary_dim is not None:
+        from dataclasses import replace
+        w = replace(w, interleaved=w.interleaved if args.interleaved is None else args.interleaved,
+                    rotary_embedding_dim=w.rotary_embedding_dim if args.rotary_dim is None else args.rotary_dim,
+                    name="%s_il%s_r%s" % (w.name, args.interleaved, args.rotary_dim))
     log("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
     head = measure(w, args.steps, args.warmup, args.onthefly, graph=w.tokens <= 4096)
     log("  %.2f us/step, %.1f GB/s (%.1f%% of %g)" % (

@@ -191,29 +191,71 @@ static void choose_geometry(Plan* pl) {
     g.variant = variant_name(ok, p.coef, p.norm != 0);
     if (!ok) return;
 
-    // Items per lane: the smallest count that keeps at least 3/4 of the lanes
-    // busy, else the best-filled. Measured on MI355X: more, smaller waves beat
-    // fuller lanes (the fp32 partial interleaved case, 24 items per row: one
-    // item per lane and 48 busy lanes is 5% faster than three and 64).
-    int best = 0;
-    double best_util = 0.0;
+    // Items per lane (ipl) and head batch (hb: heads whose X loads a lane
+    // issues together), among the instantiated pairs. Chosen from sweeps on
+    // MI355X over all pairs:
+    //  * 2-byte types: lanes all busy if some ipl allows it, then the most
+    //    16-byte loads in flight per lane up to 16, then the fewer items per
+    //    lane (split fp16 rows of 128: (1, 8); interleaved: (2, 8), 24.2 vs
+    //    27.1 us for (1, 8); 12 items per row: (3, 4), 19.3 vs 20.8 us);
+    //  * 4-byte types: the smallest ipl keeping 3/4 of the lanes busy and at
+    //    most 4 heads per batch (fp32 prefill 44.2 vs 51.1 us with 8 heads;
+    //    the partial interleaved fp32 case, 24 items per row, 37.3 us with
+    //    one item per lane vs 39.8 with three);
+    //  * QK-norm: one item per lane (its only instantiation).
+    static const int kPairs[][2] = {{1, 2}, {1, 4}, {1, 8}, {2, 2}, {2, 4}, {2, 8},
+                                    {3, 2}, {3, 4}, {4, 2}, {4, 4}};
+    const int per_item = p.interleaved ? 1 : 2;
+    const double loads_per_item = (double)(NP * per_item + NT) / (double)W;
     const int over_ipl = env_int("ROPE_ITEMS_PER_LANE");
-    for (int ipl = 1; ipl <= 4; ++ipl) {
-        int64_t tg = 64 * ipl / W;
-        if (tg < 1) continue;
-        if (over_ipl > 0 && ipl != over_ipl) continue;
-        double util = (double)(tg * W) / (64.0 * ipl);
-        if (util > best_util + 1e-9) {
-            best_util = util;
-            best = ipl;
+    const int over_batch = env_int("ROPE_HEAD_BATCH");
+    int best = 0, hb = 2;
+    if (es == 2 && !p.norm) {
+        double best_key[4] = {-1, -1, -1, -1};
+        for (const auto& pr : kPairs) {
+            const int ipl = pr[0], h = pr[1];
+            const int64_t tg = 64 * ipl / W;
+            if (tg < 1) continue;
+            const double util = (double)(tg * W) / (64.0 * ipl);
+            const double loads = ipl * h * loads_per_item;
+            if (loads > 16.0 + 1e-9) continue;
+            const bool full = util >= 0.99;
+            const double key[4] = {full ? 1.0 : 0.0, full ? 0.0 : util, loads, -(double)ipl};
+            bool better = false;
+            for (int k = 0; k < 4; ++k) {
+                if (key[k] > best_key[k] + 1e-9) { better = true; break; }
+                if (key[k] < best_key[k] - 1e-9) break;
+            }
+            if (better) {
+                for (int k = 0; k < 4; ++k) best_key[k] = key[k];
+                best = ipl;
+                hb = h;
+            }
         }
-        if (over_ipl == 0 && util >= 0.75) break;
+    } else {
+        double best_util = 0.0;
+        for (int ipl = 1; ipl <= (p.norm ? 1 : 4); ++ipl) {
+            int64_t tg = 64 * ipl / W;
+            if (tg < 1) continue;
+            double util = (double)(tg * W) / (64.0 * ipl);
+            if (util > best_util + 1e-9) {
+                best_util = util;
+                best = ipl;
+            }
+            if (util >= 0.75) break;
+        }
+        const int max_batch = es == 4 ? 4 : 8;
+        hb = 2;
+        while (hb * 2 <= max_batch && best * hb * 2 * per_item <= 16) hb *= 2;
     }
-    if (best == 0) {  // the override fits no row: ignore it
-        for (int ipl = 1; ipl <= 4 && best == 0; ++ipl)
-            if (64 * ipl / W >= 1) best = ipl;
-    }
-    if (p.norm) best = 1;  // the only instantiation with the norm
+    // tuning overrides (sweeps): items per lane, then head batch
+    if (over_ipl > 0 && over_ipl <= 4 && !p.norm && 64 * over_ipl / W >= 1) best = over_ipl;
+    for (int ipl = 1; best == 0 && ipl <= 4; ++ipl)  // nothing chosen: the first that fits
+        if (64 * ipl / W >= 1) { best = ipl; hb = 2; }
+    const int max_batch = best <= 2 ? 8 : 4;
+    if (hb > max_batch) hb = max_batch;
+    if (over_batch == 2 || over_batch == 4 || over_batch == 8)
+        hb = over_batch <= max_batch ? over_batch : max_batch;
     g.items_per_lane = best;
     g.W = (int32_t)W;
     g.NP = (int32_t)NP;
@@ -221,18 +263,6 @@ static void choose_geometry(Plan* pl) {
     const int64_t ntok = p.B * p.S;
     const int64_t groups = (ntok + g.TG - 1) / g.TG;
     const int over = heads_per_wave_override();
-    const int over_batch = env_int("ROPE_HEAD_BATCH");
-    // Head batch: heads whose X loads a lane issues together. Aim for about
-    // 16 16-byte loads in flight per lane (a rotation item of split halves
-    // loads two chunks), within the instantiated (items, batch) pairs.
-    // 4-byte types: at most 4 heads per batch (measured: the fp32 prefill runs
-    // 14% faster with 4 than with 8, the partial interleaved case 4% faster).
-    const int per_item = p.interleaved ? 1 : 2;
-    const int max_batch = es == 4 ? 4 : (best <= 2 ? 8 : 4);
-    int hb = 2;
-    while (hb * 2 <= max_batch && best * hb * 2 * per_item <= 16) hb *= 2;
-    if (over_batch == 2 || over_batch == 4 || over_batch == 8)
-        hb = over_batch <= max_batch ? over_batch : max_batch;
     g.head_batch = hb;
     // Heads per wave: one batch, split evenly over the head count (28 heads
     // with batch 8 -> 4 waves of 7); halved for small launches so that they
