@@ -157,8 +157,17 @@ static int env_int(const char* name) {
     return e ? atoi(e) : 0;
 }
 
-// Tuning overrides (for measurement sweeps): heads per wave, head batch.
-static int heads_per_wave_override() { return env_int("ROPE_HEADS_PER_WAVE"); }
+// Tuning overrides for measurement sweeps, read once per process (getenv
+// scans the environment: too slow for every call).
+struct TuningOverrides {
+    int heads_per_wave, items_per_lane, head_batch, xcd_remap, wave_tile, no_share;
+};
+static const TuningOverrides& overrides() {
+    static const TuningOverrides o = {env_int("ROPE_HEADS_PER_WAVE"), env_int("ROPE_ITEMS_PER_LANE"),
+                                      env_int("ROPE_HEAD_BATCH"),     env_int("ROPE_XCD_REMAP"),
+                                      env_int("ROPE_WAVE_TILE"),      env_int("ROPE_NO_SHARE")};
+    return o;
+}
 
 // Vector kernel: a head row of D elements is cut into 16-byte items; a
 // rotation item holds E = 16/sizeof(T) pairs' first elements (split halves,
@@ -207,8 +216,8 @@ static void choose_geometry(Plan* pl) {
                                     {3, 2}, {3, 4}, {4, 2}, {4, 4}};
     const int per_item = p.interleaved ? 1 : 2;
     const double loads_per_item = (double)(NP * per_item + NT) / (double)W;
-    const int over_ipl = env_int("ROPE_ITEMS_PER_LANE");
-    const int over_batch = env_int("ROPE_HEAD_BATCH");
+    const int over_ipl = overrides().items_per_lane;
+    const int over_batch = overrides().head_batch;
     int best = 0, hb = 2;
     if (es == 2 && !p.norm) {
         double best_key[4] = {-1, -1, -1, -1};
@@ -262,7 +271,7 @@ static void choose_geometry(Plan* pl) {
     g.TG = (int32_t)(64 * best / W);
     const int64_t ntok = p.B * p.S;
     const int64_t groups = (ntok + g.TG - 1) / g.TG;
-    const int over = heads_per_wave_override();
+    const int over = overrides().heads_per_wave;
     g.head_batch = hb;
     // Heads per wave: one batch, split evenly over the head count (28 heads
     // with batch 8 -> 4 waves of 7); halved for small launches so that they
@@ -274,9 +283,8 @@ static void choose_geometry(Plan* pl) {
     if (over > 0) hpw_cap = over;  // tuning override (a wave loops over its batches)
     // Wave order: rank 4 keeps a head's tokens contiguous, so a tile of 4
     // token groups per head chunk gives each workgroup longer runs per head.
-    const char* remap = getenv("ROPE_XCD_REMAP");
-    g.xcd_remap = remap ? atoi(remap) : 0;
-    const int over_tile = env_int("ROPE_WAVE_TILE");
+    g.xcd_remap = overrides().xcd_remap;
+    const int over_tile = overrides().wave_tile;
     g.tile = over_tile > 0 ? over_tile : (g.rank == 4 ? 4 : 1);
     const int64_t tiles = (groups + g.tile - 1) / g.tile;
     for (int t = 0; t < p.ntask; ++t) {
@@ -292,7 +300,7 @@ static void choose_geometry(Plan* pl) {
     // of one task (a tile of one group, chunk counts divisible by the waves
     // per workgroup), they split that work and exchange it through LDS.
     g.share_coef = 0;
-    if (p.coef == kCoefOnTheFly && g.tile == 1 && env_int("ROPE_NO_SHARE") == 0) {
+    if (p.coef == kCoefOnTheFly && g.tile == 1 && overrides().no_share == 0) {
         bool ok_share = true;
         for (int t = 0; t < p.ntask; ++t)
             if (p.task[t].heads > 0 && g.chunks[t] % kWavesPerBlock != 0) ok_share = false;
