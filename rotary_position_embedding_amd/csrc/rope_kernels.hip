@@ -134,8 +134,6 @@ template <typename T> __device__ inline void mask_elem(u32x4& m, int e) {
     else m[e >> 1] |= 0xffffu << (16 * (e & 1));
 }
 
-__device__ inline u32x4 load16(const char* p) { return *reinterpret_cast<const u32x4*>(p); }
-
 // Activations are reached through pointers the compiler cannot trace back to
 // kernel arguments (the task selection hides them), so without a cast it
 // emits flat instructions; these go through global (address space 1) ones.
@@ -143,7 +141,6 @@ __device__ inline u32x4 load16(const char* p) { return *reinterpret_cast<const u
 __device__ inline u32x4 load16_global(const char* p) { return *(const ROPE_GLOBAL u32x4*)p; }
 __device__ inline u32x4 load_nt(const char* p) { return __builtin_nontemporal_load((const ROPE_GLOBAL u32x4*)p); }
 __device__ inline void store_nt(char* p, const u32x4& v) { __builtin_nontemporal_store(v, (ROPE_GLOBAL u32x4*)p); }
-__device__ inline void store16(char* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 __device__ inline u32x4 select_bits(const u32x4& keep_mask, const u32x4& keep, const u32x4& other) {
     return (keep & keep_mask) | (other & ~keep_mask);
