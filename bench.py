@@ -38,7 +38,10 @@ PEAK_GBS = 8000.0            # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30       # >= 4x the 256 MB last-level cache
 HEADLINE = "c2_rope_f16_prefill"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_rope_f16_prefill.json")
-KERNEL_SOURCE = os.path.join(ROOT, "rotary_position_embedding_amd", "csrc", "rope_kernels.hip")
+# the kernel source files (device code and its per-type instantiations)
+KERNEL_SOURCES = [os.path.join(ROOT, "rotary_position_embedding_amd", "csrc", f)
+                  for f in ("rope_device.hpp", "rope_kernels.hip", "rope_kernels_f32.hip",
+                            "rope_kernels_f16.hip", "rope_kernels_bf16.hip")]
 
 
 def log(*a):
@@ -46,8 +49,11 @@ def log(*a):
 
 
 def kernel_source_sha():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 # ---------------------------------------------------------------------------

@@ -7,6 +7,7 @@ denormals kept), packed-fp32 instruction selection disabled; hipcc links.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -18,7 +19,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["rope_plan.cpp", "rope_abi.cpp"]
-HIP_SOURCES = ["rope_kernels.hip"]
+# the kernels of each storage type in a translation unit of their own, so that
+# they compile in parallel
+HIP_SOURCES = ["rope_kernels.hip", "rope_kernels_f32.hip", "rope_kernels_f16.hip", "rope_kernels_bf16.hip"]
 
 
 def _run(cmd, verbose):
@@ -35,13 +38,18 @@ def build(verbose: bool = False) -> str:
         _run(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE,
               "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
-    for src in HIP_SOURCES:
+
+    def hip_obj(src):
         obj = os.path.join(BUILD, src + ".o")
         _run([HIPCC, "--offload-arch=" + ARCH, "-std=c++17", "-O3", "-fPIC", "-Wall", "-ffp-contract=off",
               "-fno-gpu-flush-denormals-to-zero",
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        return obj
+
+    jobs = max(1, min(len(HIP_SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        objs += list(pool.map(hip_obj, HIP_SOURCES))
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)

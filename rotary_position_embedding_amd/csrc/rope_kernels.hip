@@ -1,831 +1,9 @@
-// rope_kernels.hip -- rotary position embedding kernels for gfx950 (MI355X).
-//
-// What is computed (pages cited by title and section):
-//   per pair (x1, x2) of a head row with coefficients (c, s) of its slot,
-//   y1 = x1*c - x2*s, y2 = x2*c + x1*s  -- onnxruntime PR #27590 review,
-//   rotate_half / apply_rotary_pos_emb; pairs (i, i+R/2) or (2i, 2i+1) --
-//   "ai.onnx.RotaryEmbedding" manifest, attributeDescriptions.interleaved;
-//   elements R..D-1 copied -- same, rotary_embedding_dim.
-// Coefficient rows: gathered by position id, per-token, M-RoPE (slot i from
-// its stream's row, scaled and rounded to the storage type, out-of-range id
-// copies the pair -- "com.microsoft.MRotaryEmbedding" README), computed
-// on the fly from inv_freq (PR #27590 Motivation), or gathered at the
-// position past + s of a key/value cache append, whose K and V rows are
-// written to that cache row ("com.microsoft.SparseAttention" README).
-// With the QK-norm, each head row is first RMS-normalised and weighted (PR
-// #27590 review, Qwen3 architecture) and the rotation acts on the result.
-// A launch holds up to three tasks (Q, K, V or a packed [Q|K|V]); storage is
-// float32, float16 or bfloat16.
-//
-// Per fp16 pair the op moves 8 bytes (read 4, write 4) and does 6 flops:
-// it is HBM-bound and has no contraction, so no MFMA. Design:
-//   * a head row is cut into 16-byte items (global_load/store_dwordx4);
-//   * a wave owns TG consecutive tokens x W items of one row shape, so each
-//     lane's coefficients (one 16-byte slice of cos and of sin) are fetched
-//     once into registers and reused for every head of a head chunk;
-//   * loads for several heads are issued before the first use, so each lane
-//     keeps several 16-byte loads in flight;
-//   * math in fp32 with fma and one rounding to the storage type; copies are
-//     bit moves (no arithmetic on pass-through elements).
-// A scalar kernel (one thread per pair or tail element) covers every shape
-// and alignment the vector kernel does not.
-#include <hip/hip_runtime.h>
-
-#include <cstdint>
-
+// rope_kernels.hip -- launch of a validated plan (the kernels themselves are
+// in rope_device.hpp, instantiated per storage type in rope_kernels_<type>.hip).
+#include "rope_device.hpp"
 #include "rope_launch.hpp"
 
 namespace rope {
-
-using half_t = _Float16;
-using bf16_t = __bf16;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kBlock = 64 * kWavesPerBlock;
-
-constexpr int kMaxTasks = 3;
-
-struct KTask {
-    const char* x;
-    char* y;
-    int64_t sb, sh, ss;    // element strides of (b, h, s)
-    int64_t wave_begin;    // first wave of this task (vector kernel)
-    int64_t item_begin;    // first thread item of this task (scalar kernel)
-    int32_t heads, hpw, chunks, tile;  // tile: token groups per head chunk in a wave tile
-    int32_t copy;          // copy: pass every element through (no rotation)
-    int32_t yrow;          // append kind: y row is the token's position
-    int64_t ysb, ysh, yss; // append kind: element strides of y (b, h, row)
-    const char* wgt;       // QK-norm: (D,) weight of this projection
-};
-
-struct KArgs {
-    KTask t[kMaxTasks];
-    int64_t ntok, S, M;
-    const char* cos;
-    const char* sin;
-    const int64_t* ids;
-    const float* inv_freq;
-    int32_t ntask, W, NP, TG, P, R, D, interleaved;
-    int32_t xcd_remap, prompt;  // prompt: append kind, every sequence starts at 0
-    float scaling, scale;
-    float eps;                  // QK-norm epsilon
-    float inv_d;                // QK-norm: 1/D rounded to binary32
-    int32_t share_coef;         // on the fly: the waves of a workgroup split the slots
-    int32_t pad4;
-    const int32_t* seqlens;     // append kind: total key length per sequence
-    int64_t rows_out;           // append kind: cache rows
-    uint32_t sel[kSelWords];
-};
-
-template <typename T> struct Elem;
-template <> struct Elem<float> { using bits = uint32_t; static constexpr int E = 4; };
-template <> struct Elem<half_t> { using bits = uint16_t; static constexpr int E = 8; };
-template <> struct Elem<bf16_t> { using bits = uint16_t; static constexpr int E = 8; };
-
-// Materialise a binary32 value in a register. Without it the compiler may
-// merge a binary32 multiply or fma with the following conversion to binary16
-// into one v_fma_mixlo_f16, which rounds the exact result once to binary16
-// and so skips the binary32 rounding the arithmetic here specifies.
-__device__ inline float keep_f32(float v) {
-    asm volatile("" : "+v"(v));
-    return v;
-}
-
-__device__ inline float to_f(float v) { return v; }
-__device__ inline float to_f(half_t v) { return (float)v; }
-__device__ inline float to_f(bf16_t v) { return (float)v; }  // exact: the upper half of a binary32
-template <typename T> __device__ inline T from_f(float v);
-template <> __device__ inline float from_f<float>(float v) { return v; }
-template <> __device__ inline half_t from_f<half_t>(float v) {
-    return (half_t)keep_f32(v);  // nearest-even from the binary32 value
-}
-template <> __device__ inline bf16_t from_f<bf16_t>(float v) {
-    return (bf16_t)keep_f32(v);  // nearest-even from the binary32 value
-}
-template <typename T> __device__ inline float round_to(float v) { return to_f(from_f<T>(v)); }
-
-// Element e of a 16-byte chunk, as float. The whole chunk is reinterpreted
-// as a vector of T and then indexed (a bit_cast applied to a single vector
-// element is miscompiled to element 0 by this toolchain, so it is avoided).
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef half_t f16x8 __attribute__((ext_vector_type(8)));
-typedef bf16_t bf16x8 __attribute__((ext_vector_type(8)));
-template <typename T> struct ChunkVec;
-template <> struct ChunkVec<float> { typedef f32x4 type; };
-template <> struct ChunkVec<half_t> { typedef f16x8 type; };
-template <> struct ChunkVec<bf16_t> { typedef bf16x8 type; };
-
-template <typename T>
-__device__ inline typename ChunkVec<T>::type chunk_values(const u32x4& v) {
-    return __builtin_bit_cast(typename ChunkVec<T>::type, v);
-}
-
-template <typename T>
-__device__ inline u32x4 chunk_pack(const float* f) {
-    typename ChunkVec<T>::type r;
-#pragma unroll
-    for (int i = 0; i < Elem<T>::E; ++i) r[i] = from_f<T>(f[i]);
-    return __builtin_bit_cast(u32x4, r);
-}
-
-// set the bits of element e of a chunk in a mask
-template <typename T> __device__ inline void mask_elem(u32x4& m, int e) {
-    if (sizeof(T) == 4) m[e] = 0xffffffffu;
-    else m[e >> 1] |= 0xffffu << (16 * (e & 1));
-}
-
-// Activations are reached through pointers the compiler cannot trace back to
-// kernel arguments (the task selection hides them), so without a cast it
-// emits flat instructions; these go through global (address space 1) ones.
-#define ROPE_GLOBAL __attribute__((address_space(1)))
-__device__ inline u32x4 load16_global(const char* p) { return *(const ROPE_GLOBAL u32x4*)p; }
-__device__ inline u32x4 load_nt(const char* p) { return __builtin_nontemporal_load((const ROPE_GLOBAL u32x4*)p); }
-__device__ inline void store_nt(char* p, const u32x4& v) { __builtin_nontemporal_store(v, (ROPE_GLOBAL u32x4*)p); }
-
-__device__ inline u32x4 select_bits(const u32x4& keep_mask, const u32x4& keep, const u32x4& other) {
-    return (keep & keep_mask) | (other & ~keep_mask);
-}
-
-// v from another lane of the same row of 16 lanes (DPP control word CTRL).
-template <int CTRL>
-__device__ inline float dpp_move(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-
-// Sum of v over aligned groups of W lanes (W a power of two <= 64, uniform);
-// every lane of a group receives the same total (pairs are combined
-// symmetrically, and a + b == b + a). Lanes 1 and 2 apart: quad permutes
-// [1,0,3,2] and [2,3,0,1]; the other quad of an 8-lane half: half-row mirror
-// (lane i <-> 7 - i); the other half of a 16-lane row: row mirror
-// (i <-> 15 - i); rows 16 and 32 apart: xor shuffles.
-__device__ inline float group_sum(float v, int W) {
-    if (W >= 2) v += dpp_move<0xb1>(v);
-    if (W >= 4) v += dpp_move<0x4e>(v);
-    if (W >= 8) v += dpp_move<0x141>(v);
-    if (W >= 16) v += dpp_move<0x140>(v);
-    if (W >= 32) v += __shfl_xor(v, 16);
-    if (W >= 64) v += __shfl_xor(v, 32);
-    return v;
-}
-
-// Coefficient of slot i at position p computed on the fly (PR #27590
-// Motivation): theta = rnd_f32(rnd_f32(p) * inv_freq[i]); cos and sin of the
-// exact binary32 theta in binary64, rounded to binary32, times the scaling in
-// binary32, rounded to the storage type. Shared by the table builder so the
-// table and on-the-fly paths agree bit for bit.
-template <typename T>
-__device__ inline void onthefly_coef(float inv, int64_t p, float scaling, float& c, float& s) {
-    const float pf = (float)p;
-    const float theta = keep_f32(pf * inv);
-    double sd, cd;
-    sincos((double)theta, &sd, &cd);
-    const float cf = keep_f32((float)cd);
-    const float sf = keep_f32((float)sd);
-    c = round_to<T>(keep_f32(cf * scaling));
-    s = round_to<T>(keep_f32(sf * scaling));
-}
-
-__device__ inline int mrope_stream(const KArgs& a, int i) {
-    return (a.sel[i >> 4] >> (2 * (i & 15))) & 3;
-}
-
-// Cache append: token n = b*S + s has position past(b) + s, past = 0 in the
-// prompt and the sequence's total key length minus S otherwise.
-__device__ inline int64_t append_position(const KArgs& a, int64_t n) {
-    const int64_t b = n / a.S;
-    const int64_t s = n - b * a.S;
-    const int64_t past = a.prompt ? 0 : (int64_t)a.seqlens[b] - a.S;
-    return past + s;
-}
-
-// Coefficient (c, s) of slot i for token n, or copy = true.
-template <typename T, int COEF>
-__device__ inline void coef_slot(const KArgs& a, int64_t n, int i, float& c, float& s, bool& copy) {
-    const T* cos_t = reinterpret_cast<const T*>(a.cos);
-    const T* sin_t = reinterpret_cast<const T*>(a.sin);
-    copy = false;
-    c = 1.0f;
-    s = 0.0f;
-    if (COEF == kCoefGather) {
-        const int64_t p = a.ids[n];
-        if (p < 0 || p >= a.M) { copy = true; return; }
-        c = to_f(cos_t[p * a.P + i]);
-        s = to_f(sin_t[p * a.P + i]);
-    } else if (COEF == kCoefPerToken) {
-        c = to_f(cos_t[n * a.P + i]);
-        s = to_f(sin_t[n * a.P + i]);
-    } else if (COEF == kCoefAppend) {
-        const int64_t p = append_position(a, n);
-        if (p < 0 || p >= a.M) { copy = true; return; }
-        c = to_f(cos_t[p * a.P + i]);
-        s = to_f(sin_t[p * a.P + i]);
-    } else if (COEF == kCoefMrope) {
-        const int64_t p = a.ids[(int64_t)mrope_stream(a, i) * a.ntok + n];
-        if (p < 0 || p >= a.M) { copy = true; return; }
-        c = round_to<T>(keep_f32(to_f(cos_t[p * a.P + i]) * a.scale));
-        s = round_to<T>(keep_f32(to_f(sin_t[p * a.P + i]) * a.scale));
-    } else {
-        onthefly_coef<T>(a.inv_freq[i], a.ids[n], a.scaling, c, s);
-    }
-}
-
-struct TaskView {
-    const char* x;
-    char* y;
-    int64_t sb, sh, ss, wave_begin, item_begin;
-    int32_t heads, hpw, chunks, tile, copy, yrow;
-    int64_t ysb, ysh, yss;
-    const char* wgt;
-};
-
-// An SGPR value the compiler must treat as opaque: keeps a select of two
-// kernel-argument loads from being folded into one load from a selected
-// address (that costs the wave a second, dependent round of scalar loads).
-template <typename V>
-__device__ inline V opaque_s(V v) {
-    asm volatile("" : "+s"(v));
-    return v;
-}
-
-// Task i (0..2) of the launch: every task's fields are read in the first
-// batch of scalar loads and the values are selected. The output geometry is
-// the input's except for the append kind.
-template <int COEF, bool NORM = false>
-__device__ inline TaskView task_of(const KArgs& a, int i) {
-#define ROPE_PICK(f)                                                                      \
-    do {                                                                                  \
-        const auto f0 = opaque_s(a.t[0].f), f1 = opaque_s(a.t[1].f), f2 = opaque_s(a.t[2].f); \
-        v.f = i == 2 ? f2 : (i == 1 ? f1 : f0);                                           \
-    } while (0)
-    TaskView v;
-    ROPE_PICK(x);
-    ROPE_PICK(y);
-    ROPE_PICK(sb);
-    ROPE_PICK(sh);
-    ROPE_PICK(ss);
-    ROPE_PICK(wave_begin);
-    ROPE_PICK(item_begin);
-    ROPE_PICK(heads);
-    ROPE_PICK(hpw);
-    ROPE_PICK(chunks);
-    ROPE_PICK(tile);
-    ROPE_PICK(copy);
-    if (COEF == kCoefAppend) {
-        ROPE_PICK(yrow);
-        ROPE_PICK(ysb);
-        ROPE_PICK(ysh);
-        ROPE_PICK(yss);
-    } else {
-        v.yrow = 0;
-        v.ysb = v.sb;
-        v.ysh = v.sh;
-        v.yss = v.ss;
-    }
-    if (NORM) ROPE_PICK(wgt);
-    else v.wgt = nullptr;
-#undef ROPE_PICK
-    return v;
-}
-
-// Tasks occupy consecutive ranges; unused ones start at INT64_MAX.
-__device__ inline int task_index(const KArgs& a, int64_t wave) {
-    return wave >= a.t[2].wave_begin ? 2 : (wave >= a.t[1].wave_begin ? 1 : 0);
-}
-
-__device__ inline int task_index_items(const KArgs& a, int64_t item) {
-    return item >= a.t[2].item_begin ? 2 : (item >= a.t[1].item_begin ? 1 : 0);
-}
-
-// ---------------------------------------------------------------------------
-// Vector kernel.
-//   wave -> (task, token group g, head chunk hc) in tiles of `tile` token
-//   groups x all chunks: g varies fastest inside a tile. tile = 1 (rank 3:
-//   a token's heads are contiguous) puts the chunks of one token group in one
-//   workgroup; tile = 4 (rank 4: a head's tokens are contiguous) gives each
-//   head chunk a run of 4 consecutive token groups per workgroup.
-//   lane item q = lane + 64*m (m < IPL) -> token t = q / W, item w = q % W.
-//   item w < NP rotates: split halves -> elements [w*E, w*E+E) with partners
-//   R/2 later; interleaved -> elements [w*E, w*E+E) = E/2 pairs.
-//   item w >= NP copies elements [R + (w-NP)*E, +E).
-// Memory order per wave: the position ids, the X chunks of the head batch
-// (predicated per item and head), then the table gather, then per head the
-// rotation and its stores. The compiler places a full wait before each head's
-// stores, so a lane has at most two 16-byte stores in flight; measured on
-// MI355X this metering is faster than letting a wave's stores pile up (a
-// batch of 16 unmetered stores per lane doubled the kernel time), and so are
-// the predicated loads (versus clamped unconditional ones). X and Y are
-// touched once: nontemporal loads and stores.
-
-// Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i % 8),
-// each XCD with its own L2. With remapping, consecutive logical workgroups
-// run on the same XCD, so the waves that share a token group's ids and
-// coefficient rows fill one L2 instead of several. A bijection on
-// [0, gridDim.x) for any grid size.
-__device__ inline uint32_t logical_block(int remap) {
-    const uint32_t p = blockIdx.x;
-    if (!remap) return p;
-    const uint32_t n = gridDim.x, q = n / 8, r = n % 8, x = p % 8;
-    return x * q + min(x, r) + p / 8;
-}
-
-// X chunks of one head batch (one or two 16-byte chunks per item and head).
-template <typename T, int IL, int IPL, int HU>
-__device__ inline void load_batch(const char* x, const int64_t* off, const bool* act, const bool* rot,
-                                  int h, int h_end, int64_t sh_bytes, int64_t half_bytes,
-                                  u32x4 (*in1)[IPL], u32x4 (*in2)[IPL]) {
-#pragma unroll
-    for (int u = 0; u < HU; ++u) {
-#pragma unroll
-        for (int m = 0; m < IPL; ++m) {
-            if (act[m] && h + u < h_end) {
-                const char* px = x + off[m] + (int64_t)(h + u) * sh_bytes;
-                in1[u][m] = load_nt(px);
-                if (!IL && rot[m])
-                    in2[u][m] = load_nt(px + half_bytes);
-            }
-        }
-    }
-}
-
-template <typename T, int IL, int COEF, int IPL, int HU, bool NORM = false>
-__global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
-    constexpr int E = Elem<T>::E;
-    constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation item
-    constexpr int ES = (int)sizeof(T);
-    typedef T cvec __attribute__((ext_vector_type(CE)));
-
-    const int lane = threadIdx.x & 63;
-    // wave-uniform by construction; readfirstlane lets the compiler keep the
-    // task selection and its fields in scalar registers
-    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + wave_in_block;
-    const TaskView tk = task_of<COEF, NORM>(a, task_index(a, gw));
-    const int64_t local = gw - tk.wave_begin;
-    const int64_t per_tile = (int64_t)tk.tile * tk.chunks;
-    const int64_t tile = local / per_tile;
-    const int r = (int)(local - tile * per_tile);
-    const int hc = r / tk.tile;
-    const int64_t g = tile * tk.tile + (r - hc * tk.tile);
-    const int64_t n0 = g * a.TG;
-    if (n0 >= a.ntok) return;
-    const int h_begin = hc * tk.hpw;
-    const int h_end = min(tk.heads, h_begin + tk.hpw);
-    const int64_t sh_bytes = tk.sh * ES;
-    const int64_t ysh_bytes = tk.ysh * ES;
-    const int64_t half_bytes = (int64_t)a.P * ES;
-
-    // -- items of this lane (no memory traffic but the append kind's lengths)
-    bool act[IPL], rot[IPL];
-    int64_t off[IPL];    // byte offset of the item's first chunk for head 0
-    int64_t yoff[IPL];   // the same in y
-    bool wr[IPL];        // the item's output row exists
-    int64_t tok[IPL];
-    int64_t apos[IPL];   // append kind: the token's position
-    int slot0[IPL];
-    int64_t elem0[IPL];  // first element of the item in its head row
-#pragma unroll
-    for (int m = 0; m < IPL; ++m) {
-        const int q = lane + 64 * m;
-        const int t = q / a.W;
-        const int w = q - t * a.W;
-        const int64_t n = n0 + t;
-        act[m] = t < a.TG && n < a.ntok;
-        rot[m] = act[m] && w < a.NP;
-        tok[m] = act[m] ? n : 0;
-        const int64_t b = tok[m] / a.S;
-        const int64_t s = tok[m] - b * a.S;
-        const int64_t e0 = w < a.NP ? (int64_t)w * E : (int64_t)a.R + (int64_t)(w - a.NP) * E;
-        off[m] = act[m] ? (b * tk.sb + s * tk.ss + e0) * ES : 0;
-        slot0[m] = rot[m] ? w * CE : 0;  // non-rotation items read slot 0 (unused)
-        elem0[m] = e0;
-        if (COEF == kCoefAppend) {
-            // the lengths are read for every item (sequence 0 for inactive ones)
-            const int64_t past = a.prompt ? 0 : (int64_t)a.seqlens[b] - a.S;
-            apos[m] = past + s;
-            const int64_t row = tk.yrow ? apos[m] : s;
-            wr[m] = act[m] && (!tk.yrow || (row >= 0 && row < a.rows_out));
-            yoff[m] = wr[m] ? (b * tk.ysb + row * tk.yss + e0) * ES : 0;
-        } else {
-            apos[m] = 0;
-            wr[m] = act[m];
-            yoff[m] = off[m];
-        }
-    }
-
-    // -- position ids, then X, then the dependent table reads --------------
-    int64_t pos[IPL][COEF == kCoefMrope ? 3 : 1];
-    const bool need = !tk.copy;
-    // ids are read for every item (index 0 for inactive ones): unconditional
-    if (COEF == kCoefGather || COEF == kCoefOnTheFly) {
-#pragma unroll
-        for (int m = 0; m < IPL; ++m) pos[m][0] = a.ids[tok[m]];
-    } else if (COEF == kCoefAppend) {
-#pragma unroll
-        for (int m = 0; m < IPL; ++m) pos[m][0] = apos[m];
-    } else if (COEF == kCoefMrope) {
-#pragma unroll
-        for (int m = 0; m < IPL; ++m)
-#pragma unroll
-            for (int k = 0; k < 3; ++k) pos[m][k] = a.ids[k * a.ntok + tok[m]];
-    }
-
-    uint32_t codes[IPL];  // M-RoPE: 2-bit stream of each slot of the item
-    if (COEF == kCoefMrope) {
-#pragma unroll
-        for (int m = 0; m < IPL; ++m) codes[m] = a.sel[slot0[m] >> 4] >> (2 * (slot0[m] & 15));
-    }
-
-    u32x4 in1[HU][IPL], in2[HU][IPL];
-    load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h_begin, h_end, sh_bytes, half_bytes, in1, in2);
-
-    T cf[IPL][CE], sf[IPL][CE];
-    u32x4 keep[IPL];  // input bits copied to the output as they are
-#pragma unroll
-    for (int m = 0; m < IPL; ++m) {
-        keep[m] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < CE; ++j) { cf[m][j] = (T)1.0f; sf[m][j] = (T)0.0f; }
-        if (!need) {  // a pass-through task: every element copied
-            keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-            continue;
-        }
-        if (COEF == kCoefGather || COEF == kCoefPerToken || COEF == kCoefAppend) {
-            // the row is read unconditionally: an out-of-range id reads row 0
-            // (with an empty table the host points the table at valid memory)
-            // and the pair is then copied
-            const int64_t row = COEF == kCoefPerToken ? tok[m] : pos[m][0];
-            const bool valid = COEF == kCoefPerToken || (row >= 0 && row < a.M);
-            const int64_t e = ((valid ? row : 0) * a.P + slot0[m]) * ES;
-            const cvec cv = *reinterpret_cast<const cvec*>(a.cos + e);
-            const cvec sv = *reinterpret_cast<const cvec*>(a.sin + e);
-#pragma unroll
-            for (int j = 0; j < CE; ++j) { cf[m][j] = cv[j]; sf[m][j] = sv[j]; }
-            if (!valid) keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
-        } else if (COEF == kCoefMrope) {
-            // Slots [slot0, slot0 + CE) of the three stream rows; slot i takes
-            // its stream's value. Per-stream element masks over the slice are
-            // built once, then the slice is assembled with bitwise and/or on
-            // whole dwords; a stream whose id is out of range contributes its
-            // slots to the copy mask instead.
-            constexpr int CW = CE * ES / 4;  // dwords in a coefficient slice
-            typedef uint32_t cbits __attribute__((ext_vector_type(CW)));
-            cbits msk0 = {}, msk1 = {}, msk2 = {};
-#pragma unroll
-            for (int j = 0; j < CE; ++j) {
-                const uint32_t k = (codes[m] >> (2 * j)) & 3u;
-                const int dw = (j * ES) / 4;
-                const uint32_t bitsj = ES == 4 ? 0xffffffffu : 0xffffu << (16 * (j & 1));
-                msk0[dw] |= k == 0 ? bitsj : 0u;
-                msk1[dw] |= k == 1 ? bitsj : 0u;
-                msk2[dw] |= k == 2 ? bitsj : 0u;
-            }
-            cbits cs = {}, ss = {}, copy = {};
-#pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const int64_t p = pos[m][k];
-                const cbits mk = k == 0 ? msk0 : (k == 1 ? msk1 : msk2);
-                const bool ok = p >= 0 && p < a.M;
-                const int64_t e = ((ok ? p : 0) * a.P + slot0[m]) * ES;  // row 0 if out of range
-                const cbits cl = *reinterpret_cast<const cbits*>(a.cos + e);
-                const cbits sl = *reinterpret_cast<const cbits*>(a.sin + e);
-                const cbits use = ok ? mk : cbits{};
-                cs |= cl & use;
-                ss |= sl & use;
-                copy |= ok ? cbits{} : mk;
-            }
-            const cvec cv = __builtin_bit_cast(cvec, cs);
-            const cvec sv = __builtin_bit_cast(cvec, ss);
-            if (a.scale == 1.0f) {
-#pragma unroll
-                for (int j = 0; j < CE; ++j) { cf[m][j] = cv[j]; sf[m][j] = sv[j]; }
-            } else {
-                // scaled coefficient: binary32 product rounded to T
-#pragma unroll
-                for (int j = 0; j < CE; ++j) {
-                    cf[m][j] = from_f<T>(keep_f32(to_f(cv[j]) * a.scale));
-                    sf[m][j] = from_f<T>(keep_f32(to_f(sv[j]) * a.scale));
-                }
-            }
-            // copy mask over the X chunk: split halves share the slice layout;
-            // interleaved slot j covers chunk elements 2j and 2j+1
-            if (!IL) {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) keep[m][d] = copy[d % CW];
-            } else {
-#pragma unroll
-                for (int j = 0; j < CE; ++j) {
-                    const uint32_t cj = ES == 4 ? copy[j] : (copy[j >> 1] >> (16 * (j & 1))) & 0xffffu;
-                    if (cj) { mask_elem<T>(keep[m], 2 * j); mask_elem<T>(keep[m], 2 * j + 1); }
-                }
-            }
-        } else if (a.share_coef) {
-            // The four waves of this workgroup hold the same token group and
-            // lane mapping (the host guarantees it): each computes every
-            // fourth slot, and the values are exchanged through LDS.
-            __shared__ float lds_c[CE * 64], lds_s[CE * 64];
-#pragma unroll
-            for (int j = 0; j < CE; ++j) {
-                if (j % kWavesPerBlock != wave_in_block) continue;
-                float c, s;
-                onthefly_coef<T>(a.inv_freq[slot0[m] + j], pos[m][0], a.scaling, c, s);
-                lds_c[j * 64 + lane] = c;
-                lds_s[j * 64 + lane] = s;
-            }
-            __syncthreads();
-#pragma unroll
-            for (int j = 0; j < CE; ++j) {
-                cf[m][j] = from_f<T>(lds_c[j * 64 + lane]);
-                sf[m][j] = from_f<T>(lds_s[j * 64 + lane]);
-            }
-            __syncthreads();  // the next item reuses the buffers
-        } else {
-#pragma unroll
-            for (int j = 0; j < CE; ++j) {
-                float c, s;
-                onthefly_coef<T>(a.inv_freq[slot0[m] + j], pos[m][0], a.scaling, c, s);
-                cf[m][j] = from_f<T>(c);
-                sf[m][j] = from_f<T>(s);
-            }
-        }
-    }
-
-    // QK-norm (one item per lane): the weights of the item's elements, and
-    // per slot the weights folded into the coefficients, so that per head
-    // y1 = (1/rms) * (x1*(w1*c) - x2*(w2*s)), y2 = (1/rms) * (x2*(w2*c) + x1*(w1*s))
-    float gw1[NORM ? E : 1], gw2[NORM ? E : 1];
-    float fa1[NORM ? E : 1], fb1[NORM ? E : 1], fa2[NORM ? E : 1], fb2[NORM ? E : 1];
-    bool kany = false;  // some lane of the wave keeps input bits (pairs or a copied task)
-    // a copied task (V of the cache append, the only norm launch that has
-    // one) is never normalised; elsewhere the decision is compile-time
-    const bool norm = NORM && (COEF != kCoefAppend || !tk.copy);
-    if (norm) {
-        const auto w1 = chunk_values<T>(load16_global(tk.wgt + elem0[0] * ES));
-        const auto w2 = chunk_values<T>(load16_global(tk.wgt + (elem0[0] + (rot[0] && !IL ? a.P : 0)) * ES));
-#pragma unroll
-        for (int e = 0; e < E; ++e) { gw1[e] = to_f(w1[e]); gw2[e] = to_f(w2[e]); }
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int j = IL ? e / 2 : e;
-            const float c = to_f(cf[0][j]), s = to_f(sf[0][j]);
-            // split halves: element e pairs with its partner chunk's element e;
-            // interleaved: elements 2j and 2j+1 of this chunk
-            const float wa = IL ? gw1[2 * j] : gw1[e];
-            const float wb = IL ? gw1[2 * j + 1] : gw2[e];
-            fa1[e] = wa * c;
-            fb1[e] = wb * s;
-            fa2[e] = wb * c;
-            fb2[e] = wa * s;
-        }
-        if (COEF == kCoefGather || COEF == kCoefAppend) kany = __ballot(keep[0][0] != 0u) != 0;
-    } else if (COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend) {
-        // some lane of the wave keeps an element: only then merge input bits
-        bool k = tk.copy != 0;
-#pragma unroll
-        for (int m = 0; m < IPL; ++m) k = k || (keep[m][0] | keep[m][1] | keep[m][2] | keep[m][3]) != 0u;
-        kany = __ballot(k) != 0;
-    }
-
-    // -- rotate and store, one head batch at a time --------------------------
-    for (int h = h_begin; h < h_end; h += HU) {
-        if (norm) {
-            // RMSNorm of each head row first: the lane's sum of squares, summed
-            // over the row's W lanes (an aligned group: W divides 64), then
-            // z = (x / rms) * weight, rotated like x; kept pairs and tail
-            // items store z
-            float rn[HU];
-#pragma unroll
-            for (int u = 0; u < HU; ++u) {
-                float ss = 0.0f;
-                if (act[0] && h + u < h_end) {
-                    const auto v1 = chunk_values<T>(in1[u][0]);
-#pragma unroll
-                    for (int e = 0; e < E; ++e) ss = fmaf(to_f(v1[e]), to_f(v1[e]), ss);
-                    if (!IL && rot[0]) {
-                        const auto v2 = chunk_values<T>(in2[u][0]);
-#pragma unroll
-                        for (int e = 0; e < E; ++e) ss = fmaf(to_f(v2[e]), to_f(v2[e]), ss);
-                    }
-                }
-                ss = group_sum(ss, a.W);
-                rn[u] = rsqrtf(ss * a.inv_d + a.eps);  // v_rsq_f32: about 1 ulp
-            }
-#pragma unroll
-            for (int u = 0; u < HU; ++u) {
-                if (!(wr[0] && h + u < h_end)) continue;
-                char* py = tk.y + yoff[0] + (int64_t)(h + u) * ysh_bytes;
-                const float r = rn[u];
-                const auto xv1 = chunk_values<T>(in1[u][0]);
-                if (!rot[0]) {
-                    float z[E];
-#pragma unroll
-                    for (int e = 0; e < E; ++e) z[e] = (to_f(xv1[e]) * r) * gw1[e];
-                    store_nt(py, chunk_pack<T>(z));
-                    continue;
-                }
-                if (IL) {
-                    float o[E];
-#pragma unroll
-                    for (int j = 0; j < CE; ++j) {
-                        const float x1 = to_f(xv1[2 * j]), x2 = to_f(xv1[2 * j + 1]);
-                        o[2 * j] = r * fmaf(x1, fa1[2 * j], -(x2 * fb1[2 * j]));
-                        o[2 * j + 1] = r * fmaf(x2, fa2[2 * j], x1 * fb2[2 * j]);
-                    }
-                    u32x4 ov = chunk_pack<T>(o);
-                    if ((COEF == kCoefGather || COEF == kCoefAppend) && kany) {
-                        float z[E];
-#pragma unroll
-                        for (int e = 0; e < E; ++e) z[e] = (to_f(xv1[e]) * r) * gw1[e];
-                        ov = select_bits(keep[0], chunk_pack<T>(z), ov);
-                    }
-                    store_nt(py, ov);
-                } else {
-                    const auto xv2 = chunk_values<T>(in2[u][0]);
-                    float o1[E], o2[E];
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        const float x1 = to_f(xv1[e]), x2 = to_f(xv2[e]);
-                        o1[e] = r * fmaf(x1, fa1[e], -(x2 * fb1[e]));
-                        o2[e] = r * fmaf(x2, fa2[e], x1 * fb2[e]);
-                    }
-                    u32x4 ov1 = chunk_pack<T>(o1);
-                    u32x4 ov2 = chunk_pack<T>(o2);
-                    if ((COEF == kCoefGather || COEF == kCoefAppend) && kany) {
-                        float z1[E], z2[E];
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            z1[e] = (to_f(xv1[e]) * r) * gw1[e];
-                            z2[e] = (to_f(xv2[e]) * r) * gw2[e];
-                        }
-                        ov1 = select_bits(keep[0], chunk_pack<T>(z1), ov1);
-                        ov2 = select_bits(keep[0], chunk_pack<T>(z2), ov2);
-                    }
-                    store_nt(py, ov1);
-                    store_nt(py + half_bytes, ov2);
-                }
-            }
-            if (h + HU < h_end)
-                load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h + HU, h_end, sh_bytes, half_bytes, in1, in2);
-            continue;
-        }
-#pragma unroll
-        for (int u = 0; u < HU; ++u) {
-#pragma unroll
-            for (int m = 0; m < IPL; ++m) {
-                if (!(wr[m] && h + u < h_end)) continue;
-                char* py = tk.y + yoff[m] + (int64_t)(h + u) * ysh_bytes;
-                if (!rot[m]) {
-                    store_nt(py, in1[u][m]);
-                    continue;
-                }
-                if (IL) {
-                    const auto xv = chunk_values<T>(in1[u][m]);
-                    float r[E];
-#pragma unroll
-                    for (int j = 0; j < CE; ++j) {
-                        const float x1 = to_f(xv[2 * j]);
-                        const float x2 = to_f(xv[2 * j + 1]);
-                        const float c = to_f(cf[m][j]), s = to_f(sf[m][j]);
-                        r[2 * j] = fmaf(x1, c, -(x2 * s));
-                        r[2 * j + 1] = fmaf(x2, c, x1 * s);
-                    }
-                    u32x4 o = chunk_pack<T>(r);
-                    if ((COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy) && kany)
-                        o = select_bits(keep[m], in1[u][m], o);
-                    store_nt(py, o);
-                } else {
-                    const auto xv1 = chunk_values<T>(in1[u][m]);
-                    const auto xv2 = chunk_values<T>(in2[u][m]);
-                    float r1[E], r2[E];
-#pragma unroll
-                    for (int j = 0; j < E; ++j) {
-                        const float x1 = to_f(xv1[j]);
-                        const float x2 = to_f(xv2[j]);
-                        const float c = to_f(cf[m][j]), s = to_f(sf[m][j]);
-                        r1[j] = fmaf(x1, c, -(x2 * s));
-                        r2[j] = fmaf(x2, c, x1 * s);
-                    }
-                    u32x4 o1 = chunk_pack<T>(r1);
-                    u32x4 o2 = chunk_pack<T>(r2);
-                    if ((COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy) && kany) {
-                        o1 = select_bits(keep[m], in1[u][m], o1);
-                        o2 = select_bits(keep[m], in2[u][m], o2);
-                    }
-                    store_nt(py, o1);
-                    store_nt(py + half_bytes, o2);
-                }
-            }
-        }
-        if (h + HU < h_end)
-            load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h + HU, h_end, sh_bytes, half_bytes, in1, in2);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Scalar kernel: one thread per (token, head, k), k < R/2 a pair, k >= R/2 a
-// tail element R + k - R/2. Any head size, rotary dim and alignment.
-template <typename T, int COEF>
-__global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int64_t total) {
-    using B = typename Elem<T>::bits;
-    const int64_t K = a.P + (a.D - a.R);
-    for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * kBlock) {
-        const TaskView tk = task_of<COEF>(a, task_index_items(a, idx));
-        const int64_t local = idx - tk.item_begin;
-        const int64_t k = local % K;
-        const int64_t rest = local / K;
-        const int64_t h = rest % tk.heads;
-        const int64_t n = rest / tk.heads;
-        const int64_t b = n / a.S;
-        const int64_t s = n - b * a.S;
-        const int64_t base = b * tk.sb + h * tk.sh + s * tk.ss;
-        int64_t ybase = base;
-        if (COEF == kCoefAppend) {
-            const int64_t row = tk.yrow ? append_position(a, n) : s;
-            if (tk.yrow && (row < 0 || row >= a.rows_out)) continue;  // no such cache row
-            ybase = b * tk.ysb + h * tk.ysh + row * tk.yss;
-        }
-        const B* xb = reinterpret_cast<const B*>(tk.x) + base;
-        B* yb = reinterpret_cast<B*>(tk.y) + ybase;
-        if (k >= a.P) {
-            const int64_t j = a.R + (k - a.P);
-            yb[j] = xb[j];
-            continue;
-        }
-        const int i = (int)k;
-        const int64_t j1 = a.interleaved ? 2 * (int64_t)i : i;
-        const int64_t j2 = a.interleaved ? 2 * (int64_t)i + 1 : (int64_t)i + a.P;
-        float c = 1.0f, sn = 0.0f;
-        bool copy = tk.copy != 0;
-        if (!copy) coef_slot<T, COEF>(a, n, i, c, sn, copy);
-        if (copy) {
-            yb[j1] = xb[j1];
-            yb[j2] = xb[j2];
-            continue;
-        }
-        const float x1 = to_f(__builtin_bit_cast(T, xb[j1]));
-        const float x2 = to_f(__builtin_bit_cast(T, xb[j2]));
-        yb[j1] = __builtin_bit_cast(B, from_f<T>(fmaf(x1, c, -(x2 * sn))));
-        yb[j2] = __builtin_bit_cast(B, from_f<T>(fmaf(x2, c, x1 * sn)));
-    }
-}
-
-// Scalar QK-norm kernel: one thread per (task, token, head) row -- the sum
-// of squares over the row, then every pair rotated from z = (x / rms) * w
-// and every tail element stored as z. Any head size and alignment.
-template <typename T, int COEF>
-__global__ __launch_bounds__(kBlock) void rope_norm_row_kernel(const KArgs a, int64_t total) {
-    using B = typename Elem<T>::bits;
-    for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * kBlock) {
-        const TaskView tk = task_of<COEF, true>(a, task_index_items(a, idx));
-        const int64_t local = idx - tk.item_begin;
-        const int64_t h = local % tk.heads;
-        const int64_t n = local / tk.heads;
-        const int64_t b = n / a.S;
-        const int64_t s = n - b * a.S;
-        const int64_t base = b * tk.sb + h * tk.sh + s * tk.ss;
-        int64_t ybase = base;
-        if (COEF == kCoefAppend) {
-            const int64_t row = tk.yrow ? append_position(a, n) : s;
-            if (tk.yrow && (row < 0 || row >= a.rows_out)) continue;  // no such cache row
-            ybase = b * tk.ysb + h * tk.ysh + row * tk.yss;
-        }
-        const B* xb = reinterpret_cast<const B*>(tk.x) + base;
-        B* yb = reinterpret_cast<B*>(tk.y) + ybase;
-        if (tk.copy) {  // a copied task (V of the cache append): bits as they are
-            for (int j = 0; j < a.D; ++j) yb[j] = xb[j];
-            continue;
-        }
-        const B* wb = reinterpret_cast<const B*>(tk.wgt);
-        // the sum of squares in binary64 (one long sequential sum here)
-        double ss = 0.0;
-        for (int j = 0; j < a.D; ++j) {
-            const double v = to_f(__builtin_bit_cast(T, xb[j]));
-            ss = fma(v, v, ss);
-        }
-        const float rn = 1.0f / sqrtf((float)(ss / (double)a.D) + a.eps);
-        for (int i = 0; i < a.P; ++i) {
-            const int j1 = a.interleaved ? 2 * i : i;
-            const int j2 = a.interleaved ? 2 * i + 1 : i + a.P;
-            const float z1 = (to_f(__builtin_bit_cast(T, xb[j1])) * rn) * to_f(__builtin_bit_cast(T, wb[j1]));
-            const float z2 = (to_f(__builtin_bit_cast(T, xb[j2])) * rn) * to_f(__builtin_bit_cast(T, wb[j2]));
-            float c = 1.0f, sn = 0.0f;
-            bool copy = false;
-            coef_slot<T, COEF>(a, n, i, c, sn, copy);
-            if (copy) {
-                yb[j1] = __builtin_bit_cast(B, from_f<T>(z1));
-                yb[j2] = __builtin_bit_cast(B, from_f<T>(z2));
-                continue;
-            }
-            yb[j1] = __builtin_bit_cast(B, from_f<T>(fmaf(z1, c, -(z2 * sn))));
-            yb[j2] = __builtin_bit_cast(B, from_f<T>(fmaf(z2, c, z1 * sn)));
-        }
-        for (int j = a.R; j < a.D; ++j) {
-            const float z = (to_f(__builtin_bit_cast(T, xb[j])) * rn) * to_f(__builtin_bit_cast(T, wb[j]));
-            yb[j] = __builtin_bit_cast(B, from_f<T>(z));
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Table builders.
@@ -834,116 +12,6 @@ __global__ __launch_bounds__(kBlock) void inv_freq_kernel(float* out, int64_t ha
     const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (i >= half) return;
     out[i] = (float)pow(base, -2.0 * (double)i / (double)(2 * half));
-}
-
-template <typename T>
-__global__ __launch_bounds__(kBlock) void table_kernel(const float* inv_freq, T* cos_out, T* sin_out,
-                                                       int64_t rows, int64_t half, float scaling) {
-    const int64_t total = rows * half;
-    for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * kBlock) {
-        const int64_t p = idx / half;
-        const int64_t i = idx - p * half;
-        float c, s;
-        onthefly_coef<T>(inv_freq[i], p, scaling, c, s);
-        cos_out[idx] = from_f<T>(c);
-        sin_out[idx] = from_f<T>(s);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Launch.
-
-static int launched(hipError_t e) {
-    if (e != hipSuccess)
-        return fail(ROPE_ERR_LAUNCH, "kernel launch failed: %s", hipGetErrorString(e));
-    return ROPE_OK;
-}
-
-// Instantiated (items per lane, head batch) pairs; the planner picks one.
-template <typename T, int IL, int COEF>
-static hipError_t launch_vec_ipl(const KArgs& a, int ipl, int hu, dim3 grid, hipStream_t st) {
-    void* args[] = {const_cast<KArgs*>(&a)};
-    const void* fn;
-#define ROPE_VEC(I, H) (const void*)rope_vec_kernel<T, IL, COEF, I, H>
-    switch (ipl * 16 + hu) {
-        case 1 * 16 + 2: fn = ROPE_VEC(1, 2); break;
-        case 1 * 16 + 4: fn = ROPE_VEC(1, 4); break;
-        case 1 * 16 + 8: fn = ROPE_VEC(1, 8); break;
-        case 2 * 16 + 2: fn = ROPE_VEC(2, 2); break;
-        case 2 * 16 + 4: fn = ROPE_VEC(2, 4); break;
-        case 2 * 16 + 8: fn = ROPE_VEC(2, 8); break;
-        case 3 * 16 + 2: fn = ROPE_VEC(3, 2); break;
-        case 3 * 16 + 4: fn = ROPE_VEC(3, 4); break;
-        case 4 * 16 + 2: fn = ROPE_VEC(4, 2); break;
-        case 4 * 16 + 4: fn = ROPE_VEC(4, 4); break;
-        default: return hipErrorInvalidValue;
-    }
-#undef ROPE_VEC
-    return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
-}
-
-// QK-norm: one item per lane, any instantiated head batch.
-template <typename T, int IL, int COEF>
-static hipError_t launch_vec_norm(const KArgs& a, int hu, dim3 grid, hipStream_t st) {
-    void* args[] = {const_cast<KArgs*>(&a)};
-    const void* fn;
-    switch (hu) {
-        case 2: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 2, true>; break;
-        case 4: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 4, true>; break;
-        case 8: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 8, true>; break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
-}
-
-template <typename T, int IL>
-static hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, dim3 grid,
-                                  hipStream_t st, bool norm) {
-    if (norm) {
-        if (ipl != 1) return hipErrorInvalidValue;
-        switch (c) {
-            case kCoefGather: return launch_vec_norm<T, IL, kCoefGather>(a, hu, grid, st);
-            case kCoefPerToken: return launch_vec_norm<T, IL, kCoefPerToken>(a, hu, grid, st);
-            case kCoefOnTheFly: return launch_vec_norm<T, IL, kCoefOnTheFly>(a, hu, grid, st);
-            case kCoefAppend: return launch_vec_norm<T, IL, kCoefAppend>(a, hu, grid, st);
-            default: return hipErrorInvalidValue;
-        }
-    }
-    switch (c) {
-        case kCoefGather: return launch_vec_ipl<T, IL, kCoefGather>(a, ipl, hu, grid, st);
-        case kCoefPerToken: return launch_vec_ipl<T, IL, kCoefPerToken>(a, ipl, hu, grid, st);
-        case kCoefMrope: return launch_vec_ipl<T, IL, kCoefMrope>(a, ipl, hu, grid, st);
-        case kCoefAppend: return launch_vec_ipl<T, IL, kCoefAppend>(a, ipl, hu, grid, st);
-        default: return launch_vec_ipl<T, IL, kCoefOnTheFly>(a, ipl, hu, grid, st);
-    }
-}
-
-template <typename T>
-static hipError_t launch_scalar(const KArgs& a, CoefKind c, int64_t total, hipStream_t st, bool norm) {
-    int64_t blocks = (total + kBlock - 1) / kBlock;
-    if (blocks > 65536) blocks = 65536;
-    if (blocks < 1) blocks = 1;
-    void* args[] = {const_cast<KArgs*>(&a), &total};
-    const void* fn;
-    if (norm) {
-        switch (c) {
-            case kCoefGather: fn = (const void*)rope_norm_row_kernel<T, kCoefGather>; break;
-            case kCoefPerToken: fn = (const void*)rope_norm_row_kernel<T, kCoefPerToken>; break;
-            case kCoefOnTheFly: fn = (const void*)rope_norm_row_kernel<T, kCoefOnTheFly>; break;
-            case kCoefAppend: fn = (const void*)rope_norm_row_kernel<T, kCoefAppend>; break;
-            default: return hipErrorInvalidValue;
-        }
-        return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0, st);
-    }
-    switch (c) {
-        case kCoefGather: fn = (const void*)rope_scalar_kernel<T, kCoefGather>; break;
-        case kCoefPerToken: fn = (const void*)rope_scalar_kernel<T, kCoefPerToken>; break;
-        case kCoefMrope: fn = (const void*)rope_scalar_kernel<T, kCoefMrope>; break;
-        case kCoefAppend: fn = (const void*)rope_scalar_kernel<T, kCoefAppend>; break;
-        default: fn = (const void*)rope_scalar_kernel<T, kCoefOnTheFly>; break;
-    }
-    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0, st);
 }
 
 int launch_plan(const Plan& pl, void* stream) {
@@ -1035,19 +103,16 @@ int launch_plan(const Plan& pl, void* stream) {
         const int ipl = g.items_per_lane;
         const int hu = g.head_batch;
         if (p.dtype == ROPE_FLOAT16)
-            e = p.interleaved ? launch_vec_coef<half_t, 1>(a, p.coef, ipl, hu, grid, st, p.norm)
-                              : launch_vec_coef<half_t, 0>(a, p.coef, ipl, hu, grid, st, p.norm);
+            e = launch_vector_for<half_t>(a, p.coef, p.interleaved, ipl, hu, grid, st, p.norm);
         else if (p.dtype == ROPE_BFLOAT16)
-            e = p.interleaved ? launch_vec_coef<bf16_t, 1>(a, p.coef, ipl, hu, grid, st, p.norm)
-                              : launch_vec_coef<bf16_t, 0>(a, p.coef, ipl, hu, grid, st, p.norm);
+            e = launch_vector_for<bf16_t>(a, p.coef, p.interleaved, ipl, hu, grid, st, p.norm);
         else
-            e = p.interleaved ? launch_vec_coef<float, 1>(a, p.coef, ipl, hu, grid, st, p.norm)
-                              : launch_vec_coef<float, 0>(a, p.coef, ipl, hu, grid, st, p.norm);
+            e = launch_vector_for<float>(a, p.coef, p.interleaved, ipl, hu, grid, st, p.norm);
     } else {
         if (item_begin == 0) return ROPE_OK;
-        e = p.dtype == ROPE_FLOAT16    ? launch_scalar<half_t>(a, p.coef, item_begin, st, p.norm)
-            : p.dtype == ROPE_BFLOAT16 ? launch_scalar<bf16_t>(a, p.coef, item_begin, st, p.norm)
-                                       : launch_scalar<float>(a, p.coef, item_begin, st, p.norm);
+        e = p.dtype == ROPE_FLOAT16    ? launch_scalar_for<half_t>(a, p.coef, item_begin, st, p.norm)
+            : p.dtype == ROPE_BFLOAT16 ? launch_scalar_for<bf16_t>(a, p.coef, item_begin, st, p.norm)
+                                       : launch_scalar_for<float>(a, p.coef, item_begin, st, p.norm);
     }
     return launched(e);
 }
@@ -1065,17 +130,13 @@ int launch_cos_sin_cache(const TablePlan& t, void* stream) {
     if (total == 0) return ROPE_OK;
     int64_t blocks = (total + kBlock - 1) / kBlock;
     if (blocks > 65536) blocks = 65536;
-    const float* inv = t.inv_freq;
-    void* cos = t.cos;
-    void* sin = t.sin;
-    int64_t rows = t.rows, half = t.half;
-    float scaling = t.scaling;
-    void* args[] = {&inv, &cos, &sin, &rows, &half, &scaling};
-    const void* fn = t.dtype == ROPE_FLOAT16    ? (const void*)table_kernel<half_t>
-                     : t.dtype == ROPE_BFLOAT16 ? (const void*)table_kernel<bf16_t>
-                                                : (const void*)table_kernel<float>;
-    return launched(hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kBlock), args, 0,
-                                    (hipStream_t)stream));
+    const dim3 grid((unsigned)blocks);
+    hipStream_t st = (hipStream_t)stream;
+    const hipError_t e =
+        t.dtype == ROPE_FLOAT16    ? launch_table_for<half_t>(t.inv_freq, t.cos, t.sin, t.rows, t.half, t.scaling, grid, st)
+        : t.dtype == ROPE_BFLOAT16 ? launch_table_for<bf16_t>(t.inv_freq, t.cos, t.sin, t.rows, t.half, t.scaling, grid, st)
+                                   : launch_table_for<float>(t.inv_freq, t.cos, t.sin, t.rows, t.half, t.scaling, grid, st);
+    return launched(e);
 }
 
 }  // namespace rope

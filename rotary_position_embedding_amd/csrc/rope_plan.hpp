@@ -1,7 +1,8 @@
 // rope_plan.hpp -- host-side description of one rotary-embedding launch.
 //
 // Validation (the ops' contracts) and kernel choice are plain C++ with no HIP
-// dependency (rope_plan.cpp); rope_kernels.hip turns a Plan into launches.
+// dependency (rope_plan.cpp); rope_kernels.hip turns a Plan into launches of
+// the kernels in rope_device.hpp.
 #pragma once
 
 #include <cstdint>
@@ -68,7 +69,7 @@ struct Problem {
     float eps;
 };
 
-// Launch geometry of the vector kernel (see rope_kernels.hip for the mapping).
+// Launch geometry of the vector kernel (see rope_device.hpp for the mapping).
 struct Geometry {
     bool vector;          // false: scalar kernel
     int32_t rank;         // of the activations
