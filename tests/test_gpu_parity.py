@@ -278,6 +278,37 @@ def test_empty_inputs_launch_nothing():
         assert y.shape == shape
 
 
+def test_empty_inputs_every_op():
+    """Zero tokens: every op returns at once and touches nothing (a cache
+    guard value stays)."""
+    f16 = dict(dtype=torch.float16, device=DEV)
+    cos = torch.zeros(8, 16, **f16)
+    w = torch.ones(32, **f16)
+    for B, S in ((0, 3), (2, 0)):
+        q = torch.empty(B, S, 4 * 32, **f16)
+        k = torch.empty(B, S, 2 * 32, **f16)
+        ids = torch.zeros(B, S, dtype=torch.int64, device=DEV)
+        ids3 = torch.zeros(3, B, S, dtype=torch.int64, device=DEV)
+        assert rpe.mrope_apply(q, ids3, cos, cos, mrope_section=(8, 4, 4), num_heads=4).shape == q.shape
+        yq, yk = rpe.rope_apply_qk(q, k, cos, cos, ids, num_heads=4, kv_num_heads=2)
+        assert yq.shape == q.shape and yk.shape == k.shape
+        yq, yk = rpe.rope_apply_qk_norm(q, k, w, w, cos, cos, ids, epsilon=1e-6, num_heads=4, kv_num_heads=2)
+        assert yq.shape == q.shape and yk.shape == k.shape
+        qkv = torch.empty(B, S, 8 * 32, **f16)
+        assert rpe.rope_apply_qkv_packed(qkv, cos, cos, ids, num_heads=4, kv_num_heads=2).shape == qkv.shape
+        pk = torch.full((max(B, 1), 2, 8, 32), 7.0, **f16)[:B]
+        pv = pk.clone()
+        lens = torch.full((B,), max(S, 1), dtype=torch.int32, device=DEV)
+        out = rpe.rope_kv_append(q, k, k, pk, pv, lens, max(S, 1) if B else S, cos, cos,
+                                 num_heads=4, kv_num_heads=2)
+        assert out.shape == q.shape
+        out = rpe.rope_kv_append_qk_norm(q, k, k, pk, pv, lens, max(S, 1) if B else S, cos, cos, w, w,
+                                         epsilon=1e-6, num_heads=4, kv_num_heads=2)
+        assert out.shape == q.shape
+        torch.cuda.synchronize()
+        assert bool((pk == 7.0).all()) and bool((pv == 7.0).all())
+
+
 def test_errors_raise():
     x = torch.zeros(2, 3, 64, dtype=torch.float16, device=DEV)
     cos = torch.zeros(8, 16, dtype=torch.float16, device=DEV)
