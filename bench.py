@@ -300,6 +300,9 @@ def main():
                     help="time the workload with this rotary_embedding_dim instead of its own")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-policy", type=int, default=0, choices=[0, 1, 2, 3],
+                    help="rope_set_kernel_policy: 0 automatic, 1 scalar, 2 vector kernel only, "
+                         "3 row kernel wherever its shape rules allow (kernel comparisons)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time plain 128 MiB device copies instead (counter calibration)")
     args = ap.parse_args()
@@ -316,6 +319,10 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if args.kernel_policy:
+        import rotary_position_embedding_amd as rpe
+        rpe.set_kernel_policy(args.kernel_policy)
 
     if args.copy_calibration:
         n = 64 << 20

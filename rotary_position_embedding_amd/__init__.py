@@ -404,7 +404,9 @@ def describe(t):
 
 
 def set_kernel_policy(policy):
-    """0: vector kernels where possible, 1: scalar kernel always. Returns the old policy."""
+    """0: automatic, 1: the scalar kernel always, 2: the vector kernel wherever
+    it applies (never the row kernel), 3: the row kernel wherever its shape
+    rules allow, at any size. Returns the old policy."""
     return _lib.load().rope_set_kernel_policy(int(policy))
 
 

@@ -26,7 +26,7 @@ const char* rope_status_string(int status) {
 const char* rope_last_error(void) { return rope::last_error(); }
 
 int rope_set_kernel_policy(int policy) {
-    return rope::set_kernel_policy(policy == 1 ? 1 : 0);
+    return rope::set_kernel_policy(policy >= 1 && policy <= 3 ? policy : 0);
 }
 
 int rope_apply_check(const rope_tensor* x, const rope_tensor* cos_cache,

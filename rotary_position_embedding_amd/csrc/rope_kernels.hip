@@ -86,6 +86,10 @@ int launch_plan(const Plan& pl, void* stream) {
     a.scale = p.scale;
     a.eps = p.eps;
     a.share_coef = g.vector && g.share_coef;
+    a.row_lanes = g.row_kernel ? g.row_lanes : 1;
+    a.row_shift = 0;
+    while ((1 << a.row_shift) < a.row_lanes) ++a.row_shift;
+    a.half_lanes = g.row_kernel ? g.half_lanes : 0;
     a.inv_d = 1.0f / (float)p.D;
     a.seqlens = p.seqlens;
     a.prompt = p.prompt;
@@ -102,7 +106,11 @@ int launch_plan(const Plan& pl, void* stream) {
         const dim3 grid((unsigned)blocks);
         const int ipl = g.items_per_lane;
         const int hu = g.head_batch;
-        if (p.dtype == ROPE_FLOAT16)
+        if (g.row_kernel)
+            e = p.dtype == ROPE_FLOAT16    ? launch_row_for<half_t>(a, p.coef, p.interleaved, grid, st, p.norm)
+                : p.dtype == ROPE_BFLOAT16 ? launch_row_for<bf16_t>(a, p.coef, p.interleaved, grid, st, p.norm)
+                                           : launch_row_for<float>(a, p.coef, p.interleaved, grid, st, p.norm);
+        else if (p.dtype == ROPE_FLOAT16)
             e = launch_vector_for<half_t>(a, p.coef, p.interleaved, ipl, hu, grid, st, p.norm);
         else if (p.dtype == ROPE_BFLOAT16)
             e = launch_vector_for<bf16_t>(a, p.coef, p.interleaved, ipl, hu, grid, st, p.norm);

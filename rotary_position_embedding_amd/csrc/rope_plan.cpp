@@ -10,6 +10,7 @@
 // Every failing clause returns its status and records a message.
 #include "rope_plan.hpp"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -152,6 +153,13 @@ static const char* variant_name(bool vec, CoefKind c, bool norm) {
     return (norm ? norm_names : names)[vec ? 1 : 0][(int)c];
 }
 
+static const char* row_variant_name(CoefKind c, bool norm) {
+    static const char* names[5] = {"row16/gather", "row16/per_token", "", "row16/on_the_fly", "row16/append"};
+    static const char* norm_names[5] = {"row16/norm/gather", "row16/norm/per_token", "", "row16/norm/on_the_fly",
+                                        "row16/norm/append"};
+    return (norm ? norm_names : names)[(int)c];
+}
+
 static int env_int(const char* name) {
     const char* e = getenv(name);
     return e ? atoi(e) : 0;
@@ -169,6 +177,73 @@ static const TuningOverrides& overrides() {
     return o;
 }
 
+static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Row kernel (rope_device.hpp): lanes along the head rows of one token, for
+// head rows of a power-of-two byte size from 32 bytes to 1 KiB, split-half
+// partners a power of two of lanes apart, coefficients gathered, per token,
+// on the fly or at the cache-append position. Used for launches that read at
+// most kRowMaxBytes of activations (decode steps): there its short per-wave
+// dependence chain (one wave-uniform position, at most kRowLoads loads per
+// lane) makes the launch 0.5-0.7 us shorter than the vector kernel's
+// (fp16, 32 heads of 128: 2.7 vs 3.4 us at 64 tokens, 3.2 vs 3.7 at 256);
+// for large launches the vector kernel streams faster (23.6 vs 25.6 us at
+// 8192 tokens), both measured on MI355X in HIP-graph replay.
+// A wave takes up to kRowLoads instructions of one token; launches of fewer
+// than ~1024 waves take fewer per wave so that they still spread over the chip.
+static constexpr int64_t kRowMaxBytes = 4 << 20;
+
+static bool choose_row_geometry(Plan* pl) {
+    Problem& p = pl->p;
+    Geometry& g = pl->g;
+    const int policy = kernel_policy();
+    if (policy == 2) return false;
+    if (p.coef == kCoefMrope) return false;
+    if (p.coef == kCoefOnTheFly && p.R / 2 > kRowMaxSlots) return false;
+    const int es = elem_size(p.dtype);
+    const int64_t row_bytes = p.D * es;
+    if (!pow2(row_bytes) || row_bytes < 32 || row_bytes > 1024) return false;
+    const int64_t dl = p.interleaved ? 0 : (p.R / 2) * es / 16;
+    if (!p.interleaved && !pow2(dl)) return false;
+    int64_t xbytes = 0;
+    for (int t = 0; t < p.ntask; ++t) xbytes += p.B * p.S * p.task[t].heads * row_bytes;
+    if (xbytes > kRowMaxBytes && policy != 3) return false;
+    const int RL = (int)(row_bytes / 16);
+    const int rpi = 64 / RL;
+    const int64_t ntok = p.B * p.S;
+    int loads = kRowLoads;
+    for (;;) {
+        int64_t waves = 0;
+        for (int t = 0; t < p.ntask; ++t) {
+            const int64_t H = p.task[t].heads;
+            const int64_t hpw = std::min<int64_t>(H, (int64_t)loads * rpi);
+            waves += H > 0 ? ntok * ((H + hpw - 1) / hpw) : 0;
+        }
+        if (waves >= 1024 || loads == 1) break;
+        loads /= 2;
+    }
+    for (int t = 0; t < p.ntask; ++t) {
+        const int64_t H = p.task[t].heads;
+        const int64_t hpw = H > 0 ? std::min<int64_t>(H, (int64_t)loads * rpi) : 1;
+        const int64_t chunks = H > 0 ? (H + hpw - 1) / hpw : 1;
+        g.heads_per_wave[t] = (int32_t)hpw;
+        g.chunks[t] = (int32_t)chunks;
+        g.waves[t] = H > 0 ? ntok * chunks : 0;
+    }
+    g.row_kernel = 1;
+    g.row_lanes = RL;
+    g.half_lanes = (int32_t)dl;
+    g.NP = (int32_t)(p.R * es / 16);  // chunks of the rotated prefix
+    g.W = RL;
+    g.TG = 1;
+    g.tile = 1;
+    g.items_per_lane = 1;
+    g.head_batch = loads;
+    g.share_coef = 0;
+    g.xcd_remap = 0;
+    return true;
+}
+
 // Vector kernel: a head row of D elements is cut into 16-byte items; a
 // rotation item holds E = 16/sizeof(T) pairs' first elements (split halves,
 // with its partner item R/2 elements later) or E/2 whole pairs
@@ -181,7 +256,7 @@ static void choose_geometry(Plan* pl) {
     const int es = elem_size(p.dtype);
     const int E = 16 / es;
     const int64_t half = p.R / 2;
-    bool ok = kernel_policy() == 0;
+    bool ok = kernel_policy() != 1;
     ok = ok && p.D % E == 0 && p.R % E == 0 && (p.interleaved || half % E == 0);
     for (int t = 0; t < p.ntask; ++t)
         ok = ok && aligned16(p.task[t].x) && aligned16(p.task[t].y);
@@ -198,7 +273,12 @@ static void choose_geometry(Plan* pl) {
     if (p.norm) ok = ok && W <= 64 && (W & (W - 1)) == 0;
     g.vector = ok;
     g.variant = variant_name(ok, p.coef, p.norm != 0);
+    g.row_kernel = 0;
     if (!ok) return;
+    if (choose_row_geometry(pl)) {
+        g.variant = row_variant_name(p.coef, p.norm != 0);
+        return;
+    }
 
     // Items per lane (ipl) and head batch (hb: heads whose X loads a lane
     // issues together), among the instantiated pairs. Chosen from sweeps on

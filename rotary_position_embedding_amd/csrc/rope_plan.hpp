@@ -44,6 +44,10 @@ constexpr int kMaxPlanTasks = 3;
 // Waves per workgroup of the vector kernel (the planner's grouping rules
 // depend on it).
 constexpr int kWavesPerBlock = 4;
+// row kernel: 16-byte load instructions per wave (each covering 64 / row_lanes head rows)
+constexpr int kRowLoads = 8;
+// row kernel, on the fly: slots per token computed once per wave (LDS rows)
+constexpr int kRowMaxSlots = 256;
 
 struct Problem {
     int32_t dtype;        // ROPE_FLOAT, ROPE_FLOAT16 or ROPE_BFLOAT16
@@ -81,6 +85,9 @@ struct Geometry {
     int32_t tile;         // token groups per head chunk in a tile of waves
     int32_t xcd_remap;    // 1: consecutive workgroups on one XCD
     int32_t share_coef;   // on the fly: the 4 waves of a workgroup share one token group
+    int32_t row_kernel;   // 1: the row kernel (lanes along head rows of one token)
+    int32_t row_lanes;    // row kernel: lanes per head row
+    int32_t half_lanes;   // row kernel, split halves: lanes between partner chunks
     int32_t heads_per_wave[kMaxPlanTasks];
     int32_t chunks[kMaxPlanTasks];  // head chunks per token group
     int64_t waves[kMaxPlanTasks];

@@ -6,6 +6,11 @@ from rope_inputs import BFLOAT16, bfloat16_bits
 
 DEV = "cuda:0"
 
+# kernel policies of rope_set_kernel_policy: automatic, the scalar kernel, the
+# vector kernel only, the row kernel wherever its shape rules allow
+POLICIES = [0, 1, 2, 3]
+POLICY_IDS = ["auto", "scalar", "vector", "row"]
+
 
 def cuda(a):
     """numpy -> device tensor; uint16 arrays are bfloat16 bit patterns."""

@@ -87,6 +87,14 @@ def rope_case(rank=3, dt=F16, B=2, S=5, H=4, D=16, R=0, ids=True, M=16, interlea
     return kw
 
 
+def with_policy(policy, fn, *args):
+    old = rpe.set_kernel_policy(policy)
+    try:
+        return fn(*args)
+    finally:
+        rpe.set_kernel_policy(old)
+
+
 def check_rope(kw):
     return rpe.rope_apply_check(kw["x"], kw["cos_cache"], kw["sin_cache"], kw["position_ids"],
                                 kw["y"], interleaved=kw["interleaved"], num_heads=kw["num_heads"],
@@ -103,7 +111,10 @@ def test_rope_variants_accepted(rank, ids, dt):
     """One positive case per manifest variant (rank3/rank4 x cache2+ids / cache3)."""
     rc, variant = check_rope(rope_case(rank=rank, ids=ids, dt=dt))
     assert rc == OK, _lib.load().rope_last_error()
-    assert variant == ("vec16/gather" if ids else "vec16/per_token")
+    # a decode-sized launch: the row kernel; with policy 2 the vector kernel
+    kind = "/gather" if ids else "/per_token"
+    assert variant == "row16" + kind
+    assert with_policy(2, check_rope, rope_case(rank=rank, ids=ids, dt=dt)) == (OK, "vec16" + kind)
 
 
 def test_rope_partial_interleaved_accepted():
@@ -130,7 +141,28 @@ def test_kernel_policy_forces_scalar():
     finally:
         rpe.set_kernel_policy(old)
     rc, v = check_rope(rope_case())
-    assert v == "vec16/gather"
+    assert v == "row16/gather"
+    assert with_policy(2, check_rope, rope_case()) == (OK, "vec16/gather")
+    assert with_policy(3, check_rope, rope_case()) == (OK, "row16/gather")
+    assert rpe.set_kernel_policy(7) == 0 and rpe.set_kernel_policy(0) == 0  # out of range: automatic
+
+
+def test_row_kernel_selection_rules():
+    """The row kernel: decode-sized launches (<= 4 MiB of activations read), head
+    rows of a power-of-two size from 32 B to 1 KiB, split-half partners a power
+    of two of lanes apart; never M-RoPE. Policy 3 lifts the size rule."""
+    big = dict(B=1, S=8192, H=32, D=128)                        # 64 MiB of fp16 X
+    assert check_rope(rope_case(**big)) == (OK, "vec16/gather")
+    assert with_policy(3, check_rope, rope_case(**big)) == (OK, "row16/gather")
+    assert check_rope(rope_case(B=1, S=512, H=32, D=128)) == (OK, "row16/gather")    # 4 MiB
+    assert check_rope(rope_case(B=1, S=513, H=32, D=128)) == (OK, "vec16/gather")
+    assert check_rope(rope_case(D=96)) == (OK, "vec16/gather")            # 192-byte rows
+    assert check_rope(rope_case(D=128, R=96)) == (OK, "vec16/gather")     # partners 6 lanes apart
+    assert check_rope(rope_case(D=128, R=96, interleaved=1)) == (OK, "row16/gather")
+    assert check_rope(rope_case(D=1024)) == (OK, "vec16/gather")          # 2 KiB rows
+    assert check_rope(rope_case(D=8, dt=F16, interleaved=1)) == (OK, "vec16/gather")  # 16-byte rows
+    assert check_rope(rope_case(D=8, dt=F32)) == (OK, "row16/gather")     # 32-byte rows
+    assert check_rope(rope_case(D=64, dt=F32, R=32)) == (OK, "row16/gather")  # partial, 4 lanes apart
 
 
 # Each clause of the manifest's contracts, negated -> its status.
@@ -347,9 +379,10 @@ def check_qk(kw):
 
 def test_qk_accepted():
     for rank in (3, 4):
-        assert check_qk(qk_case(rank=rank)) == (OK, "vec16/gather")
-        assert check_qk(qk_case(rank=rank, table=False)) == (OK, "vec16/on_the_fly")
-        assert check_qk(qk_case(rank=rank, ids=False)) == (OK, "vec16/per_token")
+        for fam, pol in (("row16", 0), ("vec16", 2)):
+            assert with_policy(pol, check_qk, qk_case(rank=rank)) == (OK, fam + "/gather")
+            assert with_policy(pol, check_qk, qk_case(rank=rank, table=False)) == (OK, fam + "/on_the_fly")
+            assert with_policy(pol, check_qk, qk_case(rank=rank, ids=False)) == (OK, fam + "/per_token")
 
 
 def test_qk_clauses():
@@ -433,6 +466,8 @@ def test_packed_accepted():
             for inplace in (False, True):
                 rc, v = check_packed(packed_case(rank=rank, table=table, inplace=inplace))
                 assert rc == OK, _lib.load().rope_last_error()
+                assert v == ("row16/gather" if table else "row16/on_the_fly")
+                rc, v = with_policy(2, check_packed, packed_case(rank=rank, table=table, inplace=inplace))
                 assert v == ("vec16/gather" if table else "vec16/on_the_fly")
     rc, v = check_packed(packed_case(D=6))
     assert rc == OK and v == "scalar/gather"
@@ -506,15 +541,16 @@ def test_kv_append_accepted():
         for packed in (False, True):
             rc, v = check_kv(kv_case(dt=dt, packed=packed))
             assert rc == OK, _lib.load().rope_last_error()
-            assert v == "vec16/append"
+            assert v == "row16/append"
+            assert with_policy(2, check_kv, kv_case(dt=dt, packed=packed)) == (OK, "vec16/append")
     for total in (3, 40):                                 # prompt; full cache
         assert check_kv(kv_case(total=total))[0] == OK
     rc, v = check_kv(kv_case(inplace=True))
-    assert rc == OK and v == "vec16/append"
+    assert rc == OK and v == "row16/append"
     rc, v = check_kv(kv_case(D=6, width=3))                # 6 halves: no 16-byte items
     assert rc == OK and v == "scalar/append"
     rc, v = check_kv(kv_case(D=32, width=8))               # partial rotation
-    assert rc == OK and v == "vec16/append"
+    assert rc == OK and v == "row16/append"
     rc, v = check_kv(kv_case(B=0))
     assert rc == OK
 
@@ -597,11 +633,14 @@ def test_qk_norm_accepted():
         for table in (True, False):
             rc, v = check_norm(norm_case(dt=dt, table=table))
             assert rc == OK, _lib.load().rope_last_error()
+            assert v == ("row16/norm/gather" if table else "row16/norm/on_the_fly")
+            rc, v = with_policy(2, check_norm, norm_case(dt=dt, table=table))
             assert v == ("vec16/norm/gather" if table else "vec16/norm/on_the_fly")
     rc, v = check_norm(norm_case(dt=F32, D=96))      # 12 items per row: not a power of two
     assert rc == OK and v == "scalar/norm/gather"
     rc, v = check_norm(norm_case(rank=4))
-    assert rc == OK and v == "vec16/norm/gather"
+    assert rc == OK and v == "row16/norm/gather"
+    assert with_policy(2, check_norm, norm_case(rank=4)) == (OK, "vec16/norm/gather")
     rc, v = check_norm(norm_case(epsilon=0.0))
     assert rc == OK
 
@@ -652,7 +691,8 @@ def test_kv_append_qk_norm_accepted_and_clauses():
         for packed in (False, True):
             rc, v = check_kv_norm(kv_norm_case(dt=dt, packed=packed))
             assert rc == OK, lib.rope_last_error()
-            assert v == "vec16/norm/append"
+            assert v == "row16/norm/append"
+            assert with_policy(2, check_kv_norm, kv_norm_case(dt=dt, packed=packed)) == (OK, "vec16/norm/append")
     base = kv_norm_case()
     cases = [
         ("q_weight missing", NULL, dict(q_weight=None)),

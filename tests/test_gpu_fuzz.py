@@ -43,7 +43,7 @@ def config(i):
                 rank=pick(g, [3, 4]), B=int(g.below(1, 4)[0]) + 1, S=int(g.below(1, 40)[0]) + 1,
                 H=int(g.below(1, 9)[0]) + 1, kv_div=pick(g, [1, 2, 4]),
                 il=pick(g, [0, 1]), onthefly=pick(g, [False, True]), inplace=pick(g, [False, True]),
-                policy=pick(g, [0, 0, 1]), seed=i)
+                policy=pick(g, [0, 0, 1, 2, 3]), seed=i)
 
 
 def x_like(seed, shape, dt):

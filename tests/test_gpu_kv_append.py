@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import rotary_position_embedding_amd as rpe
-from gpu_io import DEV, cuda, host, torch_dtype
+from gpu_io import DEV, cuda, host, torch_dtype, POLICIES, POLICY_IDS
 from oracle_pins import angle_table, ids_in
 from parity import assert_bitwise, assert_parity, assert_parity_norm, bits
 from rope_inputs import BFLOAT16, normal_tensor
@@ -97,7 +97,7 @@ KV = [
 
 
 @pytest.mark.parametrize("inplace", [False, True])
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 @pytest.mark.parametrize("case", KV, ids=[str(i) for i in range(len(KV))])
 def test_kv_append_sweep(case, policy, inplace):
     dt, B, S, H, Hk, D, width, Smax, M, lens, total, il, packed = case
@@ -111,7 +111,7 @@ def test_kv_append_sweep(case, policy, inplace):
           flush=True)
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 def test_kv_append_out_of_contract_lengths(policy):
     """Lengths above total_sequence_length or below S: rows outside the cache
     are skipped, positions outside the table keep their pairs, nothing
@@ -167,7 +167,7 @@ def zmax(x, w, eps, heads):
     return z
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 @pytest.mark.parametrize("case", [
     # dt, B, S, H, Hk, D, width, Smax, M, total, il, packed
     (np.float16, 64, 1, 32, 8, 128, 64, 256, 512, None, 0, False),

@@ -8,7 +8,7 @@ import oracle
 import rotary_position_embedding_amd as rpe
 from oracle_pins import angle_table, ids_in, pair_index
 from parity import assert_bitwise, assert_parity, assert_parity_binary32_range, bits, compare
-from gpu_io import DEV, cuda, host, one, torch_dtype
+from gpu_io import DEV, cuda, host, one, torch_dtype, POLICIES, POLICY_IDS
 from rope_inputs import BFLOAT16, WORKLOADS, normal_tensor, with_dtype, with_layout
 
 pytestmark = pytest.mark.gpu
@@ -198,7 +198,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 @pytest.mark.parametrize("case", SHAPES, ids=[str(i) for i in range(len(SHAPES))])
 def test_rope_sweep(case, policy):
     rank, dt, B, S, H, D, R, il, has_ids, M = case
@@ -400,7 +400,7 @@ QK = [
 
 
 @pytest.mark.parametrize("onthefly", [False, True])
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 @pytest.mark.parametrize("case", QK, ids=[str(i) for i in range(len(QK))])
 def test_qk_sweep(case, policy, onthefly):
     rank, dt, B, S, H, Hk, D, R, il = case
@@ -470,7 +470,7 @@ def split_packed(qkv, rank, H, Hk):
 
 @pytest.mark.parametrize("inplace", [False, True])
 @pytest.mark.parametrize("onthefly", [False, True])
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 @pytest.mark.parametrize("case", PACKED, ids=[str(i) for i in range(len(PACKED))])
 def test_qkv_packed(case, policy, onthefly, inplace):
     rank, dt, B, S, H, Hk, D, R, il = case
@@ -501,7 +501,7 @@ def test_qkv_packed(case, policy, onthefly, inplace):
     assert_bitwise(gv, v, "V")
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 def test_empty_table_copies_everything(policy):
     """M = 0 rows: every id is out of range, so Y == X bit for bit (the vector
     kernel reads a substitute row and discards it)."""
@@ -520,7 +520,7 @@ def test_empty_table_copies_everything(policy):
 # ---------------------------------------------------------------------------
 # 64-bit addressing: more than 2^31 elements (4 GiB of float16 in and out)
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 def test_more_than_2_31_elements(policy):
     """X (1, 524291, 4096) float16 = 2^31 + 12288 elements, made on the GPU by
     torch's seeded generator (not by this library); sampled token rows, among
@@ -569,7 +569,7 @@ def _special_values(dt):
     return bits_
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 @pytest.mark.parametrize("dt", [np.float16, np.float32, BFLOAT16])
 @pytest.mark.parametrize("il", [0, 1])
 def test_special_values(dt, il, policy):

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import rotary_position_embedding_amd as rpe
-from gpu_io import cuda, host
+from gpu_io import cuda, host, POLICIES, POLICY_IDS
 from oracle_pins import angle_table, ids_in
 from parity import assert_parity_norm
 from rope_inputs import BFLOAT16, normal_tensor
@@ -64,7 +64,7 @@ NORM = [
 ]
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 @pytest.mark.parametrize("case", NORM, ids=[str(i) for i in range(len(NORM))])
 def test_qk_norm_sweep(case, policy):
     rank, dt, B, S, H, Hk, D, R, il, kind = case
