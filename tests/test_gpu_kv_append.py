@@ -93,6 +93,8 @@ KV = [
     (np.float16, 2, 7, 4, 2, 128, 16, 30, 50, (7, 30), 30, 1, False),       # interleaved, partial
     (BFLOAT16, 2, 3, 4, 1, 10, 5, 12, 12, (3, 11), 11, 0, False),           # scalar kernel
     (np.float32, 2, 3, 2, 2, 96, 32, 24, 30, (3, 24), 24, 1, True),
+    (np.float16, 2, 3, 4, 2, 64, 16, 20, 30, (3, 11), 11, 0, False),       # partners 2 lanes apart, tail
+    (np.float32, 1, 2, 2, 1, 256, 128, 8, 10, (2,), 2, 0, False),          # 1 KiB rows, prompt
 ]
 
 

@@ -195,6 +195,14 @@ SHAPES = [
     (4, BFLOAT16, 2, 19, 7, 96, 64, 1, True, 64),
     (3, BFLOAT16, 2, 33, 4, 80, 32, 0, False, 0),
     (3, BFLOAT16, 2, 13, 4, 6, 0, 0, True, 20),          # not 16-byte items
+    # row-kernel partner distances and row sizes (policy "row" runs them there)
+    (3, np.float16, 2, 11, 6, 16, 0, 0, True, 50),       # 32-byte rows: partners 1 lane apart
+    (4, np.float32, 2, 9, 3, 16, 0, 0, True, 50),        # partners 2 lanes apart
+    (3, np.float16, 1, 5, 3, 512, 0, 0, True, 50),       # 1 KiB rows: partners 32 lanes apart
+    (3, np.float32, 1, 6, 2, 256, 128, 0, True, 50),     # 1 KiB rows, partial: 16 lanes apart
+    (3, np.float16, 2, 7, 3, 128, 64, 0, True, 50),      # partial: 4 lanes apart, tail chunks
+    (3, np.float16, 2, 7, 3, 128, 96, 1, True, 50),      # interleaved partial, 12 rotated chunks
+    (3, BFLOAT16, 2, 11, 6, 32, 0, 0, False, 0),         # 64-byte rows, per-token table
 ]
 
 

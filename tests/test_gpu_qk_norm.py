@@ -61,6 +61,9 @@ NORM = [
     (3, np.float32, 2, 7, 4, 2, 96, 0, 0, "gather"),       # scalar kernel (12 items per row)
     (3, np.float16, 2, 5, 2, 1, 10, 6, 0, "onthefly"),     # scalar kernel
     (3, np.float16, 64, 1, 32, 8, 128, 0, 0, "onthefly"),  # decode
+    (3, np.float32, 2, 5, 2, 1, 256, 0, 0, "gather"),      # 1 KiB rows: the sum over 64 lanes
+    (3, np.float16, 2, 9, 4, 2, 16, 0, 0, "onthefly"),     # 32-byte rows
+    (3, BFLOAT16, 2, 6, 2, 2, 32, 0, 0, "per_token"),      # partners 2 lanes apart
 ]
 
 
