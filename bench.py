@@ -44,6 +44,10 @@ KERNEL_SOURCES = [os.path.join(ROOT, "rotary_position_embedding_amd", "csrc", f)
                             "rope_kernels_f16.hip", "rope_kernels_bf16.hip")]
 
 
+# kernel variant prefix (as the *_check functions report it) -> kernel function
+KERNEL_FUNCTIONS = {"vec16": "rope_vec_kernel", "row16": "rope_row_kernel", "scalar": "rope_scalar_kernel"}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -217,6 +221,24 @@ def time_steps_graph(launchers, steps, warmup):
     return t0.elapsed_time(t1) / steps
 
 
+def copy_reference(nbytes, steps, warmup):
+    """A plain device copy (torch copy_) of `nbytes` read and the same written,
+    N(0,1) fp16 data, rotating over >= 1 GiB like the kernels: the rate a pure
+    stream of this size reaches on this GPU, for context (GB/s, ms)."""
+    import torch
+    n = nbytes // 2
+    nsets = max(2, -(-ROTATE_BYTES // (2 * nbytes)))
+    pairs = []
+    for _ in range(nsets):
+        a = torch.empty(n, dtype=torch.float16, device="cuda:0").normal_()
+        pairs.append((a, torch.empty_like(a)))
+    launchers = [lambda a=a, b=b: b.copy_(a) for a, b in pairs]
+    ms = time_steps(launchers, steps, warmup)
+    del pairs, launchers
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9, ms
+
+
 def measure(w, steps, warmup, onthefly=False, graph=False):
     """Eager timing; with graph=True also the HIP-graph replay timing, which
     then gives the rates (the launch-bound decode steps)."""
@@ -238,6 +260,7 @@ def measure(w, steps, warmup, onthefly=False, graph=False):
         "frac_of_peak": gbs / PEAK_GBS,
         "tokens_heads_per_s": w.tokens_heads() / (ms_rate * 1e-3),
         "rotation_sets_bytes": rot,
+        "kernel_variant": launchers[0].variant,
     }
     if graph:
         r["ms_per_step_eager"] = ms
@@ -389,6 +412,17 @@ def main():
         log("  %.3f GB/s" % cpu["value"])
 
     traffic = traffic_for_headline() if w.name == HEADLINE else None
+    copy_ref = None
+    if not only and w.op == "rope":
+        # the activation bytes of the step (X read, Y written) as a plain copy
+        nx = int(np.prod(w.x_shape)) * np.dtype(w.dtype).itemsize
+        log("timing a plain device copy of the same %d bytes (read and written)" % nx)
+        cgbs, cms = copy_reference(nx, args.steps, args.warmup)
+        log("  %.2f us/copy, %.1f GB/s" % (cms * 1e3, cgbs))
+        copy_ref = {"what": "torch copy_ of the step's X bytes into Y (N(0,1) fp16 data, same >= 1 GiB rotation)",
+                    "bytes_per_copy": 2 * nx, "us": round(cms * 1e3, 3), "gbs": round(cgbs, 1),
+                    "frac_of_peak": round(cgbs / PEAK_GBS, 4),
+                    "step_rate_over_copy_rate": round(head["gbs"] / cgbs, 4)}
     result = {
         "metric": METRIC,
         "value": round(head["gbs"], 3),
@@ -419,11 +453,13 @@ def main():
             "unit": "GB/s",
             "frac": round(head["gbs"] / PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "rope_vec_kernel (fp16, split halves, gathered table)",
+            "kernel": "%s, variant %s" % (KERNEL_FUNCTIONS.get(head["kernel_variant"].split("/")[0], "?"),
+                                          head["kernel_variant"]),
             "kernel_us_mean": round(head["ms_per_step"] * 1e3, 3),
             "algorithmic_bytes_per_launch": head["bytes_per_step"],
         },
         "cpu_baseline": cpu,
+        "copy_reference": copy_ref,
         "also": also,
     }
     print(json.dumps(result), flush=True)

@@ -166,7 +166,7 @@ def rope_apply_qkv_packed_launcher(qkv, cos_cache, sin_cache, position_ids, out,
                                    inv_freq=None, attention_scaling=1.0):
     dev = _device_of(qkv)
     ds = [_desc(t, dev) for t in (qkv, cos_cache, sin_cache, position_ids, out, inv_freq)]
-    rc, _ = rope_apply_qkv_packed_check(*ds[:5], interleaved=interleaved, num_heads=num_heads,
+    rc, variant = rope_apply_qkv_packed_check(*ds[:5], interleaved=interleaved, num_heads=num_heads,
                                         kv_num_heads=kv_num_heads,
                                         rotary_embedding_dim=rotary_embedding_dim,
                                         inv_freq=ds[5], attention_scaling=attention_scaling)
@@ -174,7 +174,7 @@ def rope_apply_qkv_packed_launcher(qkv, cos_cache, sin_cache, position_ids, out,
     args = [_lib.ref(d) for d in ds[:5]] + [interleaved, num_heads, kv_num_heads, rotary_embedding_dim,
                                             _lib.ref(ds[5]), attention_scaling, _stream(dev)]
     return Launcher(_lib.load().rope_apply_qkv_packed, args,
-                    (ds, qkv, cos_cache, sin_cache, position_ids, out, inv_freq))
+                    (ds, qkv, cos_cache, sin_cache, position_ids, out, inv_freq), variant)
 
 
 def rope_apply_qk_norm(q, k, q_weight, k_weight, cos_cache=None, sin_cache=None, position_ids=None, *,
@@ -213,7 +213,7 @@ def rope_apply_qk_norm_launcher(q, k, q_weight, k_weight, cos_cache, sin_cache, 
     dev = _device_of(q)
     ds = [_desc(t, dev) for t in (q, k, q_weight, k_weight, cos_cache, sin_cache, position_ids, out_q, out_k,
                                   inv_freq)]
-    rc, _ = rope_apply_qk_norm_check(*ds[:9], epsilon=epsilon, interleaved=interleaved, num_heads=num_heads,
+    rc, variant = rope_apply_qk_norm_check(*ds[:9], epsilon=epsilon, interleaved=interleaved, num_heads=num_heads,
                                      kv_num_heads=kv_num_heads, rotary_embedding_dim=rotary_embedding_dim,
                                      inv_freq=ds[9], attention_scaling=attention_scaling)
     _check(rc)
@@ -221,7 +221,8 @@ def rope_apply_qk_norm_launcher(q, k, q_weight, k_weight, cos_cache, sin_cache, 
         [_lib.ref(d) for d in ds[4:9]] + [interleaved, num_heads, kv_num_heads, rotary_embedding_dim,
                                           _lib.ref(ds[9]), attention_scaling, _stream(dev)]
     return Launcher(_lib.load().rope_apply_qk_norm, args,
-                    (ds, q, k, q_weight, k_weight, cos_cache, sin_cache, position_ids, out_q, out_k, inv_freq))
+                    (ds, q, k, q_weight, k_weight, cos_cache, sin_cache, position_ids, out_q, out_k, inv_freq),
+                    variant)
 
 
 def rope_kv_append(query, key, value, past_key, past_value, key_total_sequence_lengths,
@@ -263,14 +264,14 @@ def rope_kv_append_launcher(query, key, value, past_key, past_value, key_total_s
     dev = _device_of(query)
     ds = [_desc(t, dev) for t in (query, key, value, past_key, past_value, key_total_sequence_lengths,
                                   cos_cache, sin_cache, out)]
-    rc, _ = rope_kv_append_check(*ds[:6], total_sequence_length, *ds[6:], num_heads=num_heads,
+    rc, variant = rope_kv_append_check(*ds[:6], total_sequence_length, *ds[6:], num_heads=num_heads,
                                  kv_num_heads=kv_num_heads, rotary_interleaved=rotary_interleaved)
     _check(rc)
     args = [_lib.ref(d) for d in ds[:6]] + [int(total_sequence_length)] + [_lib.ref(d) for d in ds[6:]] + \
         [rotary_interleaved, num_heads, kv_num_heads, _stream(dev)]
     return Launcher(_lib.load().rope_kv_append, args,
                     (ds, query, key, value, past_key, past_value, key_total_sequence_lengths, cos_cache,
-                     sin_cache, out))
+                     sin_cache, out), variant)
 
 
 def _q_out_for(query, key, num_heads, kv_num_heads):
@@ -314,7 +315,7 @@ def rope_kv_append_qk_norm_launcher(query, key, value, past_key, past_value, key
     dev = _device_of(query)
     ds = [_desc(t, dev) for t in (query, key, value, past_key, past_value, key_total_sequence_lengths,
                                   cos_cache, sin_cache, out, q_weight, k_weight)]
-    rc, _ = rope_kv_append_qk_norm_check(*ds[:6], total_sequence_length, *ds[6:], epsilon=epsilon,
+    rc, variant = rope_kv_append_qk_norm_check(*ds[:6], total_sequence_length, *ds[6:], epsilon=epsilon,
                                          num_heads=num_heads, kv_num_heads=kv_num_heads,
                                          rotary_interleaved=rotary_interleaved)
     _check(rc)
@@ -322,7 +323,7 @@ def rope_kv_append_qk_norm_launcher(query, key, value, past_key, past_value, key
         [float(epsilon), rotary_interleaved, num_heads, kv_num_heads, _stream(dev)]
     return Launcher(_lib.load().rope_kv_append_qk_norm, args,
                     (ds, query, key, value, past_key, past_value, key_total_sequence_lengths, cos_cache,
-                     sin_cache, out, q_weight, k_weight))
+                     sin_cache, out, q_weight, k_weight), variant)
 
 
 def rope_inv_freq(rotary_dim, base, device="cuda", out=None):
@@ -416,12 +417,15 @@ def set_kernel_policy(policy):
 # in shape, address and stream)
 
 class Launcher:
-    """Zero-argument callable that re-issues one C-ABI call."""
+    """Zero-argument callable that re-issues one C-ABI call. `variant` names
+    the kernel the call runs (as the *_check functions report it, e.g.
+    "vec16/gather"), fixed when the launcher is made."""
 
-    def __init__(self, fn, args, keep):
+    def __init__(self, fn, args, keep, variant=None):
         self._fn = fn
         self._args = args
         self._keep = keep      # descriptors and tensors referenced by args
+        self.variant = variant
 
     def __call__(self):
         rc = self._fn(*self._args)
@@ -433,11 +437,11 @@ def rope_apply_launcher(x, cos_cache, sin_cache, position_ids, out, *, interleav
                         num_heads=0, rotary_embedding_dim=0):
     dev = _device_of(x)
     ds = [_desc(t, dev) for t in (x, cos_cache, sin_cache, position_ids, out)]
-    rc, _ = rope_apply_check(*ds, interleaved=interleaved, num_heads=num_heads,
+    rc, variant = rope_apply_check(*ds, interleaved=interleaved, num_heads=num_heads,
                              rotary_embedding_dim=rotary_embedding_dim)
     _check(rc)
     args = [_lib.ref(d) for d in ds] + [interleaved, num_heads, rotary_embedding_dim, _stream(dev)]
-    return Launcher(_lib.load().rope_apply, args, (ds, x, cos_cache, sin_cache, position_ids, out))
+    return Launcher(_lib.load().rope_apply, args, (ds, x, cos_cache, sin_cache, position_ids, out), variant)
 
 
 def mrope_apply_launcher(x, position_ids, cos_cache, sin_cache, out, *, mrope_section, interleaved=0,
@@ -446,14 +450,15 @@ def mrope_apply_launcher(x, position_ids, cos_cache, sin_cache, out, *, mrope_se
     dev = _device_of(x)
     ds = [_desc(t, dev) for t in (x, position_ids, cos_cache, sin_cache, out)]
     sec = (ctypes.c_int64 * 3)(*[int(v) for v in mrope_section])
-    rc, _ = mrope_apply_check(*ds, mrope_section=mrope_section, interleaved=interleaved,
+    rc, variant = mrope_apply_check(*ds, mrope_section=mrope_section, interleaved=interleaved,
                               is_packed_batching=is_packed_batching, mrope_layout=mrope_layout,
                               num_heads=num_heads, rotary_embedding_dim=rotary_embedding_dim,
                               scale=scale)
     _check(rc)
     args = [_lib.ref(d) for d in ds] + [interleaved, is_packed_batching, mrope_layout, sec, num_heads,
                                         rotary_embedding_dim, scale, _stream(dev)]
-    return Launcher(_lib.load().mrope_apply, args, (ds, sec, x, position_ids, cos_cache, sin_cache, out))
+    return Launcher(_lib.load().mrope_apply, args, (ds, sec, x, position_ids, cos_cache, sin_cache, out),
+                    variant)
 
 
 def rope_apply_qk_launcher(q, k, cos_cache, sin_cache, position_ids, out_q, out_k, *, interleaved=0,
@@ -461,11 +466,11 @@ def rope_apply_qk_launcher(q, k, cos_cache, sin_cache, position_ids, out_q, out_
                            attention_scaling=1.0):
     dev = _device_of(q)
     ds = [_desc(t, dev) for t in (q, k, cos_cache, sin_cache, position_ids, out_q, out_k, inv_freq)]
-    rc, _ = rope_apply_qk_check(*ds[:7], interleaved=interleaved, num_heads=num_heads,
+    rc, variant = rope_apply_qk_check(*ds[:7], interleaved=interleaved, num_heads=num_heads,
                                 kv_num_heads=kv_num_heads, rotary_embedding_dim=rotary_embedding_dim,
                                 inv_freq=ds[7], attention_scaling=attention_scaling)
     _check(rc)
     args = [_lib.ref(d) for d in ds[:7]] + [interleaved, num_heads, kv_num_heads, rotary_embedding_dim,
                                             _lib.ref(ds[7]), attention_scaling, _stream(dev)]
     return Launcher(_lib.load().rope_apply_qk, args,
-                    (ds, q, k, cos_cache, sin_cache, position_ids, out_q, out_k, inv_freq))
+                    (ds, q, k, cos_cache, sin_cache, position_ids, out_q, out_k, inv_freq), variant)
