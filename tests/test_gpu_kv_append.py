@@ -11,7 +11,7 @@ import rotary_position_embedding_amd as rpe
 from gpu_io import DEV, cuda, host, torch_dtype, POLICIES, POLICY_IDS
 from oracle_pins import angle_table, ids_in
 from parity import assert_bitwise, assert_parity, assert_parity_norm, bits
-from rope_inputs import BFLOAT16, normal_tensor
+from rope_inputs import BFLOAT16, get, normal_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -220,3 +220,36 @@ def test_kv_append_qk_norm(case, policy):
                 zmax_cache[b, :, r, :] = zk[b, s][:, None]
     assert_parity_norm(host(gk), ek, zmax_cache, "key cache")
     assert_bitwise(host(gv), ev, "value cache")
+
+
+def test_kv_append_qk_norm_decode_full_size():
+    """The decode step the benchmark times (qk_norm_kv_append_f16_decode) in
+    its launch configuration: 256 sequences, 32 query and 8 key heads of 128,
+    f16, QK-norm weights; a 512-row cache (the cache length does not change
+    the launch) holding a cheap bit pattern, lengths U[1, 512]."""
+    w = get("qk_norm_kv_append_f16_decode")
+    B, H, Hk, D, Smax = w.batch, w.num_heads, w.kv_num_heads, w.head_size, 512
+    lens = (ids_in(12300, (B,), Smax) + 1).astype(np.int32)
+    inv = oracle.inv_freq(w.cache_base, D)
+    cos, sin = oracle.cos_sin_cache(np.float16, w.cache_rows, inv)
+    q, k, v = w.make_x(), w.make_k(), w.make_v()
+    wq, wk = w.make_norm_weights()
+    n = B * Hk * Smax * D
+    pk = ((np.arange(n, dtype=np.uint64) * np.uint64(2654435761)) >> np.uint64(7) & np.uint64(0x3bff)) \
+        .astype(np.uint16).view(np.float16).reshape(B, Hk, Smax, D)
+    total = int(lens.max())
+    eq, ek, ev = oracle.rope_kv_append(q, k, v, pk, pk, lens, total, cos, sin, H, Hk,
+                                       q_weight=wq, k_weight=wk, epsilon=1e-6)
+    gk, gv = cuda(pk), cuda(pk)
+    gq = rpe.rope_kv_append_qk_norm(cuda(q), cuda(k), cuda(v), gk, gv, cuda(lens), total, cuda(cos), cuda(sin),
+                                    cuda(wq), cuda(wk), epsilon=1e-6, num_heads=H, kv_num_heads=Hk)
+    zq = zmax(q, wq, 1e-6, H).max(-1, keepdims=True)
+    zq = np.broadcast_to(zq, (B, 1, H, D)).reshape(B, 1, H * D)
+    r = assert_parity_norm(host(gq), eq, zq, "q_out")
+    zk = zmax(k, wk, 1e-6, Hk).max(-1)                   # (B, 1, Hk)
+    zc = np.zeros((B, Hk, Smax, D))
+    for b in range(B):
+        zc[b, :, lens[b] - 1, :] = zk[b, 0][:, None]
+    assert_parity_norm(host(gk), ek, zc, "key cache")
+    assert_bitwise(host(gv), ev, "value cache")
+    print("norm decode full size", r, flush=True)

@@ -9,7 +9,7 @@ import rotary_position_embedding_amd as rpe
 from gpu_io import cuda, host, POLICIES, POLICY_IDS
 from oracle_pins import angle_table, ids_in
 from parity import assert_parity_norm
-from rope_inputs import BFLOAT16, normal_tensor
+from rope_inputs import BFLOAT16, get, normal_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -137,3 +137,21 @@ def test_qk_norm_prefill_full_size(dt):
     rq = assert_parity_norm(host(gq), want_q, zmax_rows(q, wq, 1e-6, 3, H), "Q")
     rk = assert_parity_norm(host(gk), want_k, zmax_rows(k, wk, 1e-6, 3, Hk), "K")
     print("prefill", np.dtype(dt).name, rq, rk, flush=True)
+
+
+def test_qk_norm_decode_full_size():
+    """The decode step the benchmark times (qk_norm_f16_decode): 256 sequences
+    of one token, 32 query and 8 key heads of 128, f16, ids U[0, 32768),
+    coefficients on the fly, in the same launch configuration."""
+    w = get("qk_norm_f16_decode")
+    q, k, ids = w.make_x(), w.make_k(), w.make_ids()
+    wq, wk = w.make_norm_weights()
+    inv = oracle.inv_freq(w.cache_base, w.rotary_dim)
+    want_q, want_k = oracle.rope_apply_qk_norm(q, k, wq, wk, 1e-6, None, None, ids, num_heads=w.num_heads,
+                                               kv_num_heads=w.kv_num_heads, inv_freq=inv, attention_scaling=w.scaling)
+    gq, gk = rpe.rope_apply_qk_norm(cuda(q), cuda(k), cuda(wq), cuda(wk), None, None, cuda(ids), epsilon=1e-6,
+                                    num_heads=w.num_heads, kv_num_heads=w.kv_num_heads, inv_freq=cuda(inv),
+                                    attention_scaling=w.scaling)
+    rq = assert_parity_norm(host(gq), want_q, zmax_rows(q, wq, 1e-6, 3, w.num_heads), "Q")
+    rk = assert_parity_norm(host(gk), want_k, zmax_rows(k, wk, 1e-6, 3, w.kv_num_heads), "K")
+    print("decode full size", rq, rk, flush=True)
