@@ -730,18 +730,19 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row kernel, for head rows whose byte size is a power of two up to 1 KiB and
-// coefficient rows gathered by id or per token. The lanes of a wave hold
-// consecutive 16-byte chunks of consecutive head rows of one token: lane l
-// has chunk l % row_lanes of head l / row_lanes, and load u of the wave
-// covers the next 64 / row_lanes heads. With the token's heads adjacent in
-// memory (rank 3, packed, decode) every load and store instruction of the
-// wave covers 1 KiB of contiguous memory, a pattern that streams a few
-// percent faster on MI355X than the strided one of the vector kernel (an
-// 8-token by 128-byte tile per instruction): 5.90 vs 5.73 TB/s for a plain
-// 64 MiB copy in each pattern. A wave covers up to kRowLoads instructions
-// (hpw heads) of one token, so the position id, its bound check and the
-// coefficient slice of each lane are the same for all of them.
+// Row kernel, for head rows whose byte size is a power of two up to 1 KiB,
+// coefficients gathered by id, per token, on the fly or at the cache-append
+// position; the planner uses it for decode-sized launches. The lanes of a
+// wave hold consecutive 16-byte chunks of consecutive head rows of one
+// token: lane l has chunk l % row_lanes of head l / row_lanes, and load u of
+// the wave covers the next 64 / row_lanes heads (with a token's heads
+// adjacent, 1 KiB of contiguous memory per instruction). A wave covers up to
+// kRowLoads instructions (hpw heads) of one token, so the position, its bound
+// check and each lane's coefficient slice are the same for all of them: the
+// dependence chain of a wave is one scalar position load and one slice
+// gather, which is what makes small launches shorter than with the vector
+// kernel (whose lanes each hold another token). For large launches the
+// vector kernel streams faster.
 //   split halves: chunk c < half_lanes holds first elements, its partner
 //   (R/2 elements later) is chunk c + half_lanes of the same row, i.e. the
 //   lane half_lanes away (a power of two), fetched by a cross-lane move;
