@@ -310,8 +310,9 @@ __device__ inline int task_index_items(const KArgs& a, int64_t item) {
 //   wave -> (task, token group g, head chunk hc) in tiles of `tile` token
 //   groups x all chunks: g varies fastest inside a tile. tile = 1 (rank 3:
 //   a token's heads are contiguous) puts the chunks of one token group in one
-//   workgroup; tile = 4 (rank 4: a head's tokens are contiguous) gives each
-//   head chunk a run of 4 consecutive token groups per workgroup.
+//   workgroup; tile = 2 or 4 (rank 4: a head's tokens are contiguous) gives
+//   each head chunk a run of consecutive token groups (with 2, a workgroup
+//   holds two chunks of two groups).
 //   lane item q = lane + 64*m (m < IPL) -> token t = q / W, item w = q % W.
 //   item w < NP rotates: split halves -> elements [w*E, w*E+E) with partners
 //   R/2 later; interleaved -> elements [w*E, w*E+E) = E/2 pairs.
