@@ -370,14 +370,16 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + wave_in_block;
     const TaskView tk = task_of<COEF, NORM>(a, task_index(a, gw));
-    const int64_t local = gw - tk.wave_begin;
-    const int64_t per_tile = (int64_t)tk.tile * tk.chunks;
-    const int64_t tile = local / per_tile;
+    // 32-bit index arithmetic (the planner keeps a vector-kernel launch's
+    // waves and tokens below 2^31): a short scalar prologue before the loads
+    const uint32_t local = (uint32_t)(gw - tk.wave_begin);
+    const uint32_t per_tile = (uint32_t)tk.tile * (uint32_t)tk.chunks;
+    const uint32_t tile = local / per_tile;
     const int r = (int)(local - tile * per_tile);
     const int hc = r / tk.tile;
-    const int64_t g = tile * tk.tile + (r - hc * tk.tile);
-    const int64_t n0 = g * a.TG;
-    if (n0 >= a.ntok) return;
+    const uint32_t g = tile * (uint32_t)tk.tile + (uint32_t)(r - hc * tk.tile);
+    const uint32_t n0 = g * (uint32_t)a.TG;
+    if (n0 >= (uint64_t)a.ntok) return;
     const int h_begin = hc * tk.hpw;
     const int h_end = min(tk.heads, h_begin + tk.hpw);
     const int64_t sh_bytes = tk.sh * ES;
@@ -398,12 +400,14 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         const int q = lane + 64 * m;
         const int t = q / a.W;
         const int w = q - t * a.W;
-        const int64_t n = n0 + t;
-        act[m] = t < a.TG && n < a.ntok;
+        const uint32_t n = n0 + (uint32_t)t;
+        act[m] = t < a.TG && n < (uint64_t)a.ntok;
         rot[m] = act[m] && w < a.NP;
-        tok[m] = act[m] ? n : 0;
-        const int64_t b = tok[m] / a.S;
-        const int64_t s = tok[m] - b * a.S;
+        const uint32_t n32 = act[m] ? n : 0u;
+        const uint32_t b32 = n32 / (uint32_t)a.S;
+        tok[m] = n32;
+        const int64_t b = b32;
+        const int64_t s = (int64_t)(n32 - b32 * (uint32_t)a.S);
         const int64_t e0 = w < a.NP ? (int64_t)w * E : (int64_t)a.R + (int64_t)(w - a.NP) * E;
         off[m] = act[m] ? (b * tk.sb + s * tk.ss + e0) * ES : 0;
         slot0[m] = rot[m] ? w * CE : 0;  // non-rotation items read slot 0 (unused)
@@ -803,17 +807,21 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
     const TaskView tk = task_of<COEF, NORM>(a, task_index(a, gw));
-    const int64_t local = gw - tk.wave_begin;
-    const int64_t n = uniform64(local / tk.chunks);  // the token
-    const int part = (int)(local - n * tk.chunks);
-    if (n >= a.ntok) return;
+    // 32-bit index arithmetic: the planner keeps the waves and tokens of a
+    // row-kernel launch below 2^31
+    const uint32_t local = (uint32_t)(gw - tk.wave_begin);
+    const uint32_t n32 = local / (uint32_t)tk.chunks;  // the token
+    const int part = (int)(local - n32 * (uint32_t)tk.chunks);
+    if (n32 >= (uint64_t)a.ntok) return;
     const int rpi = 64 >> a.row_shift;  // head rows per instruction
     const int hi = lane >> a.row_shift;
     const int c = lane & (a.row_lanes - 1);
     const int h0 = part * tk.hpw;
     const int nh = min(tk.heads - h0, tk.hpw);
-    const int64_t b = n / a.S;
-    const int64_t s = n - b * a.S;
+    const uint32_t b32 = n32 / (uint32_t)a.S;
+    const int64_t n = n32;
+    const int64_t b = b32;
+    const int64_t s = (int64_t)(n32 - b32 * (uint32_t)a.S);
 
     // the position (wave-uniform: scalar loads through the scalar data cache,
     // read-only), then X, then the coefficient slice

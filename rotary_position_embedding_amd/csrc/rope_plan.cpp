@@ -222,6 +222,7 @@ static bool choose_row_geometry(Plan* pl) {
         if (waves >= 1024 || loads == 1) break;
         loads /= 2;
     }
+    int64_t total_waves = 0;
     for (int t = 0; t < p.ntask; ++t) {
         const int64_t H = p.task[t].heads;
         const int64_t hpw = H > 0 ? std::min<int64_t>(H, (int64_t)loads * rpi) : 1;
@@ -229,7 +230,10 @@ static bool choose_row_geometry(Plan* pl) {
         g.heads_per_wave[t] = (int32_t)hpw;
         g.chunks[t] = (int32_t)chunks;
         g.waves[t] = H > 0 ? ntok * chunks : 0;
+        total_waves += g.waves[t];
     }
+    // the kernel's index arithmetic is 32-bit
+    if (total_waves > INT32_MAX || ntok > INT32_MAX) return false;
     g.row_kernel = 1;
     g.row_lanes = RL;
     g.half_lanes = (int32_t)dl;
@@ -382,6 +386,15 @@ static void choose_geometry(Plan* pl) {
     // coefficients. When each workgroup's waves are chunks of one token group
     // of one task (a tile of one group, chunk counts divisible by the waves
     // per workgroup), they split that work and exchange it through LDS.
+    // the kernel's index arithmetic is 32-bit: larger launches take the
+    // scalar kernel
+    int64_t total_waves = 0;
+    for (int t = 0; t < p.ntask; ++t) total_waves += g.waves[t];
+    if (total_waves > INT32_MAX || ntok > INT32_MAX) {
+        g.vector = false;
+        g.variant = variant_name(false, p.coef, p.norm != 0);
+        return;
+    }
     g.share_coef = 0;
     if (p.coef == kCoefOnTheFly && g.tile == 1 && overrides().no_share == 0) {
         bool ok_share = true;
