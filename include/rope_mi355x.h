@@ -44,9 +44,9 @@
  *     stream) and returns. Results are ready when the stream reaches them.
  *   - Validation is complete before anything is enqueued: a non-zero return
  *     means nothing was launched. ROPE_ERR_LAUNCH means a launch was
- *     attempted and the HIP runtime refused it. ROPE_ERR_UNSUPPORTED is also
- *     returned, before any launch, for a problem whose grid would exceed
- *     2^31 - 1 workgroups (inputs of about 2^39 elements).
+ *     attempted and the HIP runtime refused it. Problems of 2^31 tokens or
+ *     more (or whose vector kernel would need 2^31 waves) run on the
+ *     grid-stride scalar kernel, whose grid is bounded.
  *   - A tensor with a zero dimension is valid; an op whose output is empty
  *     launches nothing and returns ROPE_OK. Data pointers of non-empty
  *     tensors must not be NULL.

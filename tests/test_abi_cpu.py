@@ -165,6 +165,14 @@ def test_row_kernel_selection_rules():
     assert check_rope(rope_case(D=64, dt=F32, R=32)) == (OK, "row16/gather")  # partial, 4 lanes apart
 
 
+def test_huge_launches_take_the_scalar_kernel():
+    """The vector and row kernels index in 32 bits: 2^31 tokens or more go to
+    the grid-stride scalar kernel (no memory is touched by a check)."""
+    assert check_rope(rope_case(B=1, S=(1 << 31) - 8, H=1, D=16)) == (OK, "vec16/gather")
+    assert check_rope(rope_case(B=1, S=1 << 31, H=1, D=16)) == (OK, "scalar/gather")
+    assert check_rope(rope_case(B=2, S=1 << 30, H=1, D=16)) == (OK, "scalar/gather")
+
+
 # Each clause of the manifest's contracts, negated -> its status.
 def _neg_cases():
     cases = []
