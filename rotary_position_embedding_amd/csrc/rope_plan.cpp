@@ -168,12 +168,13 @@ static int env_int(const char* name) {
 // Tuning overrides for measurement sweeps, read once per process (getenv
 // scans the environment: too slow for every call).
 struct TuningOverrides {
-    int heads_per_wave, items_per_lane, head_batch, xcd_remap, wave_tile, no_share;
+    int heads_per_wave, items_per_lane, head_batch, xcd_remap, wave_tile, no_share, row_loads;
 };
 static const TuningOverrides& overrides() {
     static const TuningOverrides o = {env_int("ROPE_HEADS_PER_WAVE"), env_int("ROPE_ITEMS_PER_LANE"),
                                       env_int("ROPE_HEAD_BATCH"),     env_int("ROPE_XCD_REMAP"),
-                                      env_int("ROPE_WAVE_TILE"),      env_int("ROPE_NO_SHARE")};
+                                      env_int("ROPE_WAVE_TILE"),      env_int("ROPE_NO_SHARE"),
+                                      env_int("ROPE_ROW_LOADS")};
     return o;
 }
 
@@ -189,8 +190,8 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // (fp16, 32 heads of 128: 2.7 vs 3.4 us at 64 tokens, 3.2 vs 3.7 at 256);
 // for large launches the vector kernel streams faster (23.6 vs 25.6 us at
 // 8192 tokens), both measured on MI355X in HIP-graph replay.
-// A wave takes up to kRowLoads instructions of one token; launches of fewer
-// than ~1024 waves take fewer per wave so that they still spread over the chip.
+// A wave takes up to kRowLoads instructions of one token; smaller launches
+// take fewer per wave so that they spread over the chip.
 static constexpr int64_t kRowMaxBytes = 4 << 20;
 
 static bool choose_row_geometry(Plan* pl) {
@@ -211,6 +212,15 @@ static bool choose_row_geometry(Plan* pl) {
     const int RL = (int)(row_bytes / 16);
     const int rpi = 64 / RL;
     const int64_t ntok = p.B * p.S;
+    // Fewer loads per wave (more waves) while a launch has fewer than ~4096
+    // waves: measured on MI355X in HIP-graph replay (fp16 decode steps, 256
+    // tokens, 32 + 8 heads of 128), one instruction per wave against the
+    // earlier rule of ~1024 waves: packed [Q|K|V] 3.33 vs 3.75 us, cache
+    // append 3.61 vs 4.05, QK-norm on the fly 4.19 vs 4.45, QK-norm + cache
+    // append 4.10 vs 4.93; Q+K with a table 3.31 vs 3.29. Plain on-the-fly
+    // launches keep ~1024 (each wave computes the token's slots once: 3.64
+    // us with two instructions per wave, 3.77 with one).
+    const int64_t target_waves = p.coef == kCoefOnTheFly && !p.norm ? 1024 : 4096;
     int loads = kRowLoads;
     for (;;) {
         int64_t waves = 0;
@@ -219,9 +229,11 @@ static bool choose_row_geometry(Plan* pl) {
             const int64_t hpw = std::min<int64_t>(H, (int64_t)loads * rpi);
             waves += H > 0 ? ntok * ((H + hpw - 1) / hpw) : 0;
         }
-        if (waves >= 1024 || loads == 1) break;
+        if (waves >= target_waves || loads == 1) break;
         loads /= 2;
     }
+    const int over_loads = overrides().row_loads;  // tuning override (sweeps)
+    if (over_loads == 1 || over_loads == 2 || over_loads == 4 || over_loads == 8) loads = over_loads;
     int64_t total_waves = 0;
     for (int t = 0; t < p.ntask; ++t) {
         const int64_t H = p.task[t].heads;
