@@ -18,7 +18,8 @@ prefill in both section layouts, the fp32 partial interleaved case, the fp16
 decode Q+K step (table and on the fly), the prefill and M-RoPE stored in
 bfloat16, the packed [Q|K|V] decode step, the decode step with the
 key/value cache append, QK-norm + RoPE (prefill with a table, decode on the
-fly), and the QK-norm decode step with the cache append.
+fly), the QK-norm decode step with the cache append, and an M-RoPE decode
+step.
 """
 import argparse
 import hashlib
@@ -392,7 +393,8 @@ def main():
                  (rope_inputs.get("kv_append_f16_decode"), False),
                  (rope_inputs.get("qk_norm_f16_prefill"), False),
                  (rope_inputs.get("qk_norm_f16_decode"), True),
-                 (rope_inputs.get("qk_norm_kv_append_f16_decode"), False)]
+                 (rope_inputs.get("qk_norm_kv_append_f16_decode"), False),
+                 (rope_inputs.get("mrope_f16_decode"), False)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
             decode = ew.tokens <= 4096

@@ -137,6 +137,10 @@ class Workload:
         return (uniform_ints(seed(self.index, 1), (self.batch,), cap) + 1).astype(np.int32)
 
     def make_ids(self) -> Optional[np.ndarray]:
+        if self.op == "mrope" and self.extra.get("ids") == "decode":
+            # a text token after the prompt: the three streams share its position
+            p = uniform_ints(seed(self.index, 1), (self.batch, self.seq), self.cache_rows)
+            return np.stack([p, p, p])
         if self.op == "mrope":
             return mrope_ids(self.index, self.batch, self.seq, self.cache_rows,
                              self.extra.get("oob_fraction", 0.01))
@@ -267,6 +271,13 @@ EXTRA_WORKLOADS.update({
         cache_rows=32768, cache_base=1e6, extra={"cache_seq": 4096},
         description="QK-norm model decode step: Q 32 + K, V 8 heads of 128 (batch 256), RMSNorm of Q and "
                     "K, RoPE, K and V appended to (256, 8, 4096, 128) caches, lengths U[1, 4096]"),
+    "mrope_f16_decode": Workload(
+        index=10, name="mrope_f16_decode", op="mrope", dtype=np.float16,
+        x_shape=(256, 1, 28 * 128), num_heads=28, cache_rows=32768, cache_base=1e6,
+        mrope_section=(16, 24, 24), mrope_layout=0, scale=1.0, extra={"ids": "decode"},
+        description="MRotaryEmbedding decode fp16 (Qwen2-VL-like): batch 256, seq 1, 28 heads of 128, "
+                    "rank 3, section [16,24,24], the three streams at the token's position U[0, 32768), "
+                    "table (32768, 64)"),
     "qk_norm_f16_decode": Workload(
         index=8, name="qk_norm_f16_decode", op="qk_norm", dtype=np.float16,
         x_shape=(256, 1, 4096), num_heads=32, k_shape=(256, 1, 1024), kv_num_heads=8,

@@ -736,8 +736,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 
 // ---------------------------------------------------------------------------
 // Row kernel, for head rows whose byte size is a power of two up to 1 KiB,
-// coefficients gathered by id, per token, on the fly or at the cache-append
-// position; the planner uses it for decode-sized launches. The lanes of a
+// coefficients gathered by id, per token, M-RoPE-assembled, on the fly or at
+// the cache-append position; the planner uses it for decode-sized launches. The lanes of a
 // wave hold consecutive 16-byte chunks of consecutive head rows of one
 // token: lane l has chunk l % row_lanes of head l / row_lanes, and load u of
 // the wave covers the next 64 / row_lanes heads (with a token's heads
@@ -837,6 +837,8 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
         row = valid ? pos : 0;
     } else if (COEF == kCoefPerToken) {
         row = n;
+    } else if (COEF == kCoefMrope) {
+        // the three streams' positions; bound checks per slot below
     } else if (COEF == kCoefAppend) {
         const int64_t past = a.prompt ? 0 : (int64_t)((const_i32)a.seqlens)[b] - a.S;
         pos = past + s;
@@ -846,6 +848,11 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
             if (pos < 0 || pos >= a.rows_out) return;  // no such cache row
             yrow = pos;
         }
+    }
+    int64_t mpos[COEF == kCoefMrope ? 3 : 1];
+    if (COEF == kCoefMrope) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) mpos[k] = ((const_i64)a.ids)[k * a.ntok + n];
     }
     const char* px = tk.x + (b * tk.sb + s * tk.ss + (int64_t)(h0 + hi) * tk.sh) * ES + c * 16;
     char* py = tk.y + (b * tk.ysb + yrow * tk.yss + (int64_t)(h0 + hi) * tk.ysh) * ES + c * 16;
@@ -867,7 +874,44 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     float cf[CE], sf[CE];  // split halves: sf carries the sign of the lane's half
 #pragma unroll
     for (int j = 0; j < CE; ++j) { cf[j] = 1.0f; sf[j] = 0.0f; }
-    if (COEF == kCoefOnTheFly && rotate) {
+    u32x4 keep = u32x4{0u, 0u, 0u, 0u};  // M-RoPE: chunk bits passed through
+    if (COEF == kCoefMrope && rotate) {
+        // slot i takes its stream's row (2-bit code per slot); the lane's
+        // slice of each of the three rows, then a per-slot select; a stream
+        // whose position is out of range passes its slots' pairs through
+        const uint32_t codes = a.sel[slot0 >> 4] >> (2 * (slot0 & 15));
+        cvec cs[3], sn[3];
+        bool ok[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            ok[k] = mpos[k] >= 0 && mpos[k] < a.M;
+            const int64_t e = ((ok[k] ? mpos[k] : 0) * a.P + slot0) * ES;  // row 0 if out of range
+            cs[k] = *reinterpret_cast<const cvec*>(a.cos + e);
+            sn[k] = *reinterpret_cast<const cvec*>(a.sin + e);
+        }
+#pragma unroll
+        for (int j = 0; j < CE; ++j) {
+            const uint32_t k = (codes >> (2 * j)) & 3u;
+            const T cv = k == 0 ? cs[0][j] : (k == 1 ? cs[1][j] : cs[2][j]);
+            const T sv = k == 0 ? sn[0][j] : (k == 1 ? sn[1][j] : sn[2][j]);
+            const bool okj = k == 0 ? ok[0] : (k == 1 ? ok[1] : ok[2]);
+            float c1 = to_f(cv), s1 = to_f(sv);
+            if (a.scale != 1.0f) {  // scaled coefficient: binary32 product rounded to T
+                c1 = round_to<T>(keep_f32(c1 * a.scale));
+                s1 = round_to<T>(keep_f32(s1 * a.scale));
+            }
+            cf[j] = c1;
+            sf[j] = lower ? -s1 : s1;  // y1 = x1*c + x2*(-s)
+            if (rotc && !okj) {
+                if (IL) {
+                    mask_elem<T>(keep, 2 * j);
+                    mask_elem<T>(keep, 2 * j + 1);
+                } else {
+                    mask_elem<T>(keep, j);
+                }
+            }
+        }
+    } else if (COEF == kCoefOnTheFly && rotate) {
         // every slot of the token once per wave (lane i computes slots i,
         // i + 64, ...), exchanged through the wave's own LDS rows
         __shared__ float lds_cs[kWavesPerBlock][2][kRowMaxSlots];
@@ -971,6 +1015,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
                 for (int e = 0; e < E; ++e) y[e] = fmaf(to_f(xv[e]), cf[e], to_f(pvv[e]) * sf[e]);
             }
             o = chunk_pack<T>(y);
+            if (COEF == kCoefMrope) o = select_bits(keep, in[u], o);
         }
         if (act) store_nt(py + u * ystep, o);
     }
@@ -1180,6 +1225,10 @@ inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream
         case kCoefPerToken: fn = ROPE_ROW(kCoefPerToken); break;
         case kCoefOnTheFly: fn = ROPE_ROW(kCoefOnTheFly); break;
         case kCoefAppend: fn = ROPE_ROW(kCoefAppend); break;
+        case kCoefMrope:
+            if (norm) return hipErrorInvalidValue;
+            fn = (const void*)rope_row_kernel<T, IL, kCoefMrope, false>;
+            break;
         default: return hipErrorInvalidValue;
     }
 #undef ROPE_ROW

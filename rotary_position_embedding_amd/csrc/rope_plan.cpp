@@ -154,7 +154,7 @@ static const char* variant_name(bool vec, CoefKind c, bool norm) {
 }
 
 static const char* row_variant_name(CoefKind c, bool norm) {
-    static const char* names[5] = {"row16/gather", "row16/per_token", "", "row16/on_the_fly", "row16/append"};
+    static const char* names[5] = {"row16/gather", "row16/per_token", "row16/mrope", "row16/on_the_fly", "row16/append"};
     static const char* norm_names[5] = {"row16/norm/gather", "row16/norm/per_token", "", "row16/norm/on_the_fly",
                                         "row16/norm/append"};
     return (norm ? norm_names : names)[(int)c];
@@ -183,7 +183,8 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // Row kernel (rope_device.hpp): lanes along the head rows of one token, for
 // head rows of a power-of-two byte size from 32 bytes to 1 KiB, split-half
 // partners a power of two of lanes apart, coefficients gathered, per token,
-// on the fly or at the cache-append position. Used for launches that read at
+// M-RoPE-assembled, on the fly or at the cache-append position. Used for
+// launches that read at
 // most kRowMaxBytes of activations (decode steps): there its short per-wave
 // dependence chain (one wave-uniform position, at most kRowLoads loads per
 // lane) makes the launch 0.5-0.7 us shorter than the vector kernel's
@@ -199,7 +200,6 @@ static bool choose_row_geometry(Plan* pl) {
     Geometry& g = pl->g;
     const int policy = kernel_policy();
     if (policy == 2) return false;
-    if (p.coef == kCoefMrope) return false;
     if (p.coef == kCoefOnTheFly && p.R / 2 > kRowMaxSlots) return false;
     const int es = elem_size(p.dtype);
     const int64_t row_bytes = p.D * es;

@@ -307,7 +307,9 @@ def test_mrope_accepted():
         for layout in (0, 1):
             for dt in (F16, F32):
                 rc, v = check_mrope(mrope_case(rank=rank, mrope_layout=layout, dt=dt))
-                assert rc == OK and v == "vec16/mrope", _lib.load().rope_last_error()
+                assert rc == OK and v == "row16/mrope", _lib.load().rope_last_error()
+                kw = mrope_case(rank=rank, mrope_layout=layout, dt=dt)
+                assert with_policy(2, check_mrope, kw) == (OK, "vec16/mrope")
     # odd head size with a smaller even rotary dim: allowed, scalar kernel
     rc, v = check_mrope(mrope_case(D=9, R=8, section=(2, 1, 1)))
     assert rc == OK and v == "scalar/mrope"

@@ -9,7 +9,7 @@ import rotary_position_embedding_amd as rpe
 from oracle_pins import angle_table, ids_in, pair_index
 from parity import assert_bitwise, assert_parity, assert_parity_binary32_range, bits, compare
 from gpu_io import DEV, cuda, host, one, torch_dtype, POLICIES, POLICY_IDS
-from rope_inputs import BFLOAT16, WORKLOADS, normal_tensor, with_dtype, with_layout
+from rope_inputs import BFLOAT16, EXTRA_WORKLOADS, WORKLOADS, normal_tensor, with_dtype, with_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -103,6 +103,14 @@ def test_c4_mrope_f16_prefill(layout):
     for j in (i, i + w.half):
         assert_bitwise(got[b, :, s, j], x[b, :, s, j], "out-of-range pairs")
     log("%s %s oob_pairs=%d" % (w.name, r, i.size))
+
+
+def test_mrope_decode_full_size():
+    """The M-RoPE decode step the benchmark times (mrope_f16_decode), in its
+    launch configuration."""
+    w = EXTRA_WORKLOADS["mrope_f16_decode"]
+    got, want, _inputs = run_workload(w)
+    log("%s %s" % (w.name, assert_parity(got, want, w.name)))
 
 
 @pytest.mark.parametrize("onthefly", [False, True])
@@ -343,11 +351,15 @@ MROPE = [
     (4, BFLOAT16, 2, 45, 3, 128, 0, (16, 24, 24), 0, 1.0),
     (3, BFLOAT16, 2, 33, 4, 128, 0, (24, 20, 20), 1, 1.25),
     (4, BFLOAT16, 2, 20, 2, 9, 8, (2, 1, 1), 0, 1.0),
+    (3, np.float16, 64, 1, 28, 128, 0, (16, 24, 24), 0, 1.0),   # decode-like
+    (3, np.float16, 3, 7, 4, 128, 64, (8, 12, 12), 1, 1.5),     # partial, tail chunks, scaled
+    (3, np.float32, 2, 9, 2, 256, 0, (40, 44, 44), 0, 1.0),     # 1 KiB rows
+    (3, np.float32, 2, 9, 3, 32, 0, (4, 6, 6), 1, 1.0),         # 128-byte rows, interleaved
 ]
 
 
 @pytest.mark.parametrize("layout", [0, 1])
-@pytest.mark.parametrize("policy", [0, 1], ids=["auto", "scalar"])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 @pytest.mark.parametrize("case", MROPE, ids=[str(i) for i in range(len(MROPE))])
 def test_mrope_sweep(case, policy, layout):
     rank, dt, B, S, H, D, R, sec, il, scale = case
@@ -360,7 +372,7 @@ def test_mrope_sweep(case, policy, layout):
     ids = ids_in(6002 + S, (3, B, S), M + 4) - 2
     ids[:, 0, 0] = (0, 1, 2)
     ids[1, -1, -1] = 2 ** 40
-    ids[2, -1, -2] = -(2 ** 40)
+    ids[2, -1, S - 2 if S > 1 else 0] = -(2 ** 40)
     want = oracle.mrope_apply(x, ids, cos, sin, sec, layout, interleaved=il, num_heads=H,
                               rotary_embedding_dim=R, scale=scale)
     got = host(rpe.mrope_apply(cuda(x), cuda(ids), cuda(cos), cuda(sin), mrope_section=sec,
