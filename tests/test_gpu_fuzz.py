@@ -1,8 +1,10 @@
 """Randomised GPU parity: seeded random configurations of every op (shapes,
 storage types, ranks, pairings, partial rotation, out-of-range ids, tables
-or on the fly, in place or not, both kernels), each against the oracle.
+or on the fly, in place or not, every kernel policy), each against the oracle.
 Configurations come from a fixed splitmix64 stream, so a failure names a
 reproducible case."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,7 +18,8 @@ from rope_inputs import BFLOAT16, SplitMix64, bfloat16_bits, normal_tensor
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 300
+# seeded configurations (ROPE_FUZZ_CASES overrides the count for longer runs)
+N_CASES = int(os.environ.get("ROPE_FUZZ_CASES", "1000"))
 
 
 @pytest.fixture(autouse=True)
