@@ -620,8 +620,8 @@ def test_kv_append_clauses():
 # ---------------------------------------------------------------------------
 # QK-norm then RoPE
 
-def norm_case(dt=F16, rank=3, D=128, table=True, **over):
-    kw = qk_case(dt=dt, rank=rank, D=D, table=table)
+def norm_case(dt=F16, rank=3, D=128, table=True, shape=None, **over):
+    kw = qk_case(dt=dt, rank=rank, D=D, table=table, **(shape or {}))
     a = Alloc()
     a.next = 1 << 40
     kw["q_weight"] = a(dt, (D,))
@@ -717,3 +717,26 @@ def test_kv_append_qk_norm_accepted_and_clauses():
         kw.update(over)
         rc, _ = check_kv_norm(kw)
         assert rc == code, (name, rc, lib.rope_last_error())
+
+
+def test_benchmark_workloads_kernel_choice():
+    """The kernel each benchmark workload runs (the planner's choice for its
+    shapes): the vector kernel for the prefill steps, the row kernel for the
+    decode steps."""
+    assert check_rope(rope_case(B=4, S=2048, H=32, D=128, M=8192)) == (OK, "vec16/gather")            # c2
+    assert check_rope(rope_case(B=4, S=2048, H=32, D=128, M=8192, dt=BF16)) == (OK, "vec16/gather")
+    assert check_rope(rope_case(rank=4, dt=F32, B=8, S=1024, H=32, D=96, R=64, interleaved=1,
+                                M=4096)) == (OK, "vec16/gather")                                     # c3
+    assert check_mrope(mrope_case(rank=4, B=2, S=4096, H=28, D=128, M=32768,
+                                  section=(16, 24, 24))) == (OK, "vec16/mrope")                      # c4
+    assert check_mrope(mrope_case(rank=3, B=256, S=1, H=28, D=128, M=32768,
+                                  section=(16, 24, 24))) == (OK, "row16/mrope")                      # decode
+    assert check_qk(qk_case(B=256, S=1, H=32, Hk=8, D=128, M=32768)) == (OK, "row16/gather")        # c5
+    assert check_qk(qk_case(B=256, S=1, H=32, Hk=8, D=128, table=False)) == (OK, "row16/on_the_fly")
+    assert check_packed(packed_case(B=256, S=1, H=32, Hk=8, D=128, M=32768)) == (OK, "row16/gather")
+    assert check_kv(kv_case(B=256, S=1, H=32, Hk=8, D=128, Smax=4096, M=32768, total=4096)) == (OK, "row16/append")
+    assert check_norm(norm_case(table=True, shape=dict(B=4, S=2048, H=32, Hk=8, M=8192))) == \
+        (OK, "vec16/norm/gather")
+    assert check_norm(norm_case(table=False, shape=dict(B=256, S=1, H=32, Hk=8))) == (OK, "row16/norm/on_the_fly")
+    assert check_kv_norm(kv_norm_case(B=256, S=1, H=32, Hk=8, Smax=4096, M=32768, total=4096)) == \
+        (OK, "row16/norm/append")
