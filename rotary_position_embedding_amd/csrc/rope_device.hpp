@@ -859,6 +859,17 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     const int64_t xstep = (int64_t)rpi * tk.sh * ES;
     const int64_t ystep = (int64_t)rpi * tk.ysh * ES;
 
+    // on the fly: this lane's inv_freq values (slots lane, lane + 64, ...)
+    // are requested before X, so that the slot computation can start while
+    // the X loads are in flight (loads complete in issue order)
+    constexpr int kOtf = COEF == kCoefOnTheFly ? kRowMaxSlots / 64 : 1;
+    float invf[kOtf];
+#pragma unroll
+    for (int k = 0; k < kOtf; ++k) {
+        invf[k] = 0.0f;
+        if (COEF == kCoefOnTheFly && lane + 64 * k < a.P) invf[k] = a.inv_freq[lane + 64 * k];
+    }
+
     u32x4 in[kRowLoads];
 #pragma unroll
     for (int u = 0; u < kRowLoads; ++u) {
@@ -912,14 +923,17 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
             }
         }
     } else if (COEF == kCoefOnTheFly && rotate) {
-        // every slot of the token once per wave (lane i computes slots i,
-        // i + 64, ...), exchanged through the wave's own LDS rows
+        // every slot of the token once per wave (lane l computes slots l,
+        // l + 64, ...), exchanged through the wave's own LDS rows
         __shared__ float lds_cs[kWavesPerBlock][2][kRowMaxSlots];
         float* wc = lds_cs[wave_in_block][0];
         float* ws = lds_cs[wave_in_block][1];
-        for (int i = lane; i < a.P; i += 64) {
+#pragma unroll
+        for (int k = 0; k < kOtf; ++k) {
+            const int i = lane + 64 * k;
+            if (i >= a.P) break;
             float cv, sv;
-            onthefly_coef<T>(a.inv_freq[i], pos, a.scaling, cv, sv);
+            onthefly_coef<T>(invf[k], pos, a.scaling, cv, sv);
             wc[i] = cv;
             ws[i] = sv;
         }
