@@ -296,9 +296,46 @@ __device__ inline TaskView task_of(const KArgs& a, int i) {
     return v;
 }
 
+// Task 0 of a single-task launch: its own fields only, no selection (the
+// selection costs measurable time in launches of many waves: fp16 prefill
+// 23.5 -> 23.2 us, fp32 partial interleaved 36.8 -> 36.2, M-RoPE decode
+// 3.86 -> 3.62).
+template <int COEF, bool NORM = false>
+__device__ inline TaskView task0_of(const KArgs& a) {
+    const KTask& t = a.t[0];
+    TaskView v;
+    v.x = t.x;
+    v.y = t.y;
+    v.sb = t.sb;
+    v.sh = t.sh;
+    v.ss = t.ss;
+    v.wave_begin = t.wave_begin;
+    v.item_begin = t.item_begin;
+    v.heads = t.heads;
+    v.hpw = t.hpw;
+    v.chunks = t.chunks;
+    v.tile = t.tile;
+    v.copy = t.copy;
+    v.yrow = COEF == kCoefAppend ? t.yrow : 0;
+    v.ysb = COEF == kCoefAppend ? t.ysb : t.sb;
+    v.ysh = COEF == kCoefAppend ? t.ysh : t.sh;
+    v.yss = COEF == kCoefAppend ? t.yss : t.ss;
+    v.wgt = NORM ? t.wgt : nullptr;
+    return v;
+}
+
 // Tasks occupy consecutive ranges; unused ones start at INT64_MAX.
 __device__ inline int task_index(const KArgs& a, int64_t wave) {
     return wave >= a.t[2].wave_begin ? 2 : (wave >= a.t[1].wave_begin ? 1 : 0);
+}
+
+// The task of wave gw. MT (compile time): the launch may hold several
+// tasks; a single-task instance reads task 0's fields only (a runtime branch
+// on the task count would put one more dependent scalar load before them).
+template <int COEF, bool NORM, bool MT>
+__device__ inline TaskView task_pick(const KArgs& a, int64_t gw) {
+    if (MT) return task_of<COEF, NORM>(a, task_index(a, gw));
+    return task0_of<COEF, NORM>(a);
 }
 
 __device__ inline int task_index_items(const KArgs& a, int64_t item) {
@@ -357,7 +394,7 @@ __device__ inline void load_batch(const char* x, const int64_t* off, const bool*
     }
 }
 
-template <typename T, int IL, int COEF, int IPL, int HU, bool NORM = false>
+template <typename T, int IL, int COEF, int IPL, int HU, bool NORM = false, bool MT = true>
 __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation item
@@ -369,7 +406,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     // task selection and its fields in scalar registers
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + wave_in_block;
-    const TaskView tk = task_of<COEF, NORM>(a, task_index(a, gw));
+    const TaskView tk = task_pick<COEF, NORM, MT>(a, gw);
     // 32-bit index arithmetic (the planner keeps a vector-kernel launch's
     // waves and tokens below 2^31): a short scalar prologue before the loads
     const uint32_t local = (uint32_t)(gw - tk.wave_begin);
@@ -796,7 +833,7 @@ __device__ inline int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <typename T, int IL, int COEF, bool NORM>
+template <typename T, int IL, int COEF, bool NORM, bool MT = true>
 __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation chunk
@@ -806,7 +843,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
-    const TaskView tk = task_of<COEF, NORM>(a, task_index(a, gw));
+    const TaskView tk = task_pick<COEF, NORM, MT>(a, gw);
     // 32-bit index arithmetic: the planner keeps the waves and tokens of a
     // row-kernel launch below 2^31
     const uint32_t local = (uint32_t)(gw - tk.wave_begin);
@@ -1171,11 +1208,11 @@ inline int launched(hipError_t e) {
 }
 
 // Instantiated (items per lane, head batch) pairs; the planner picks one.
-template <typename T, int IL, int COEF>
+template <typename T, int IL, int COEF, bool MT>
 inline hipError_t launch_vec_ipl(const KArgs& a, int ipl, int hu, dim3 grid, hipStream_t st) {
     void* args[] = {const_cast<KArgs*>(&a)};
     const void* fn;
-#define ROPE_VEC(I, H) (const void*)rope_vec_kernel<T, IL, COEF, I, H>
+#define ROPE_VEC(I, H) (const void*)rope_vec_kernel<T, IL, COEF, I, H, false, MT>
     switch (ipl * 16 + hu) {
         case 1 * 16 + 2: fn = ROPE_VEC(1, 2); break;
         case 1 * 16 + 4: fn = ROPE_VEC(1, 4); break;
@@ -1221,11 +1258,20 @@ inline hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, d
         }
     }
     switch (c) {
-        case kCoefGather: return launch_vec_ipl<T, IL, kCoefGather>(a, ipl, hu, grid, st);
-        case kCoefPerToken: return launch_vec_ipl<T, IL, kCoefPerToken>(a, ipl, hu, grid, st);
-        case kCoefMrope: return launch_vec_ipl<T, IL, kCoefMrope>(a, ipl, hu, grid, st);
-        case kCoefAppend: return launch_vec_ipl<T, IL, kCoefAppend>(a, ipl, hu, grid, st);
-        default: return launch_vec_ipl<T, IL, kCoefOnTheFly>(a, ipl, hu, grid, st);
+        // M-RoPE launches hold one task, the cache append three (Q, K, V)
+        case kCoefGather:
+            return a.ntask > 1 ? launch_vec_ipl<T, IL, kCoefGather, true>(a, ipl, hu, grid, st)
+                               : launch_vec_ipl<T, IL, kCoefGather, false>(a, ipl, hu, grid, st);
+        case kCoefPerToken:
+            return a.ntask > 1 ? launch_vec_ipl<T, IL, kCoefPerToken, true>(a, ipl, hu, grid, st)
+                               : launch_vec_ipl<T, IL, kCoefPerToken, false>(a, ipl, hu, grid, st);
+        case kCoefMrope:
+            if (a.ntask != 1) return hipErrorInvalidValue;
+            return launch_vec_ipl<T, IL, kCoefMrope, false>(a, ipl, hu, grid, st);
+        case kCoefAppend: return launch_vec_ipl<T, IL, kCoefAppend, true>(a, ipl, hu, grid, st);
+        default:
+            return a.ntask > 1 ? launch_vec_ipl<T, IL, kCoefOnTheFly, true>(a, ipl, hu, grid, st)
+                               : launch_vec_ipl<T, IL, kCoefOnTheFly, false>(a, ipl, hu, grid, st);
     }
 }
 
@@ -1233,15 +1279,22 @@ template <typename T, int IL>
 inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream_t st, bool norm) {
     void* args[] = {const_cast<KArgs*>(&a)};
     const void* fn;
-#define ROPE_ROW(K) (norm ? (const void*)rope_row_kernel<T, IL, K, true> : (const void*)rope_row_kernel<T, IL, K, false>)
+    // norm launches hold two or three tasks (Q and K, or Q, K and V)
+#define ROPE_ROW(K)                                                                      \
+    (norm ? (const void*)rope_row_kernel<T, IL, K, true, true>                           \
+          : (a.ntask > 1 ? (const void*)rope_row_kernel<T, IL, K, false, true>           \
+                         : (const void*)rope_row_kernel<T, IL, K, false, false>))
     switch (c) {
         case kCoefGather: fn = ROPE_ROW(kCoefGather); break;
         case kCoefPerToken: fn = ROPE_ROW(kCoefPerToken); break;
         case kCoefOnTheFly: fn = ROPE_ROW(kCoefOnTheFly); break;
-        case kCoefAppend: fn = ROPE_ROW(kCoefAppend); break;
+        case kCoefAppend:
+            fn = norm ? (const void*)rope_row_kernel<T, IL, kCoefAppend, true, true>
+                      : (const void*)rope_row_kernel<T, IL, kCoefAppend, false, true>;
+            break;
         case kCoefMrope:
-            if (norm) return hipErrorInvalidValue;
-            fn = (const void*)rope_row_kernel<T, IL, kCoefMrope, false>;
+            if (norm || a.ntask != 1) return hipErrorInvalidValue;
+            fn = (const void*)rope_row_kernel<T, IL, kCoefMrope, false, false>;
             break;
         default: return hipErrorInvalidValue;
     }
