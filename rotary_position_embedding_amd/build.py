@@ -19,9 +19,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["rope_plan.cpp", "rope_abi.cpp"]
-# the kernels of each storage type in a translation unit of their own, so that
-# they compile in parallel
-HIP_SOURCES = ["rope_kernels.hip", "rope_kernels_f32.hip", "rope_kernels_f16.hip", "rope_kernels_bf16.hip"]
+# the kernels of each storage type in translation units of their own (the
+# vector kernel; the row, scalar and table kernels), so that they compile in
+# parallel
+HIP_SOURCES = ["rope_kernels.hip",
+               "rope_kernels_f32.hip", "rope_kernels_f16.hip", "rope_kernels_bf16.hip",
+               "rope_kernels_f32_row.hip", "rope_kernels_f16_row.hip", "rope_kernels_bf16_row.hip"]
 
 
 def _run(cmd, verbose):

@@ -1,6 +1,7 @@
 // rope_device.hpp -- the kernels and their launch templates (device side),
-// included by rope_kernels.hip and by one translation unit per storage
-// type (rope_kernels_f32/f16/bf16.hip), which instantiate them in parallel
+// included by rope_kernels.hip and by two translation units per storage
+// type (rope_kernels_<type>.hip: the vector kernel; rope_kernels_<type>_row.hip:
+// the row, scalar and table kernels), which instantiate them in parallel
 // builds.
 //
 //
@@ -252,19 +253,24 @@ struct TaskView {
 // address (that costs the wave a second, dependent round of scalar loads).
 template <typename V>
 __device__ inline V opaque_s(V v) {
-    asm volatile("" : "+s"(v));
+    asm("" : "+s"(v));  // not volatile: dropped when the value is unused
     return v;
 }
 
 // Task i (0..2) of the launch: every task's fields are read in the first
 // batch of scalar loads and the values are selected. The output geometry is
 // the input's except for the append kind.
-template <int COEF, bool NORM = false>
+template <int COEF, bool NORM = false, int NT = kMaxTasks>
 __device__ inline TaskView task_of(const KArgs& a, int i) {
 #define ROPE_PICK(f)                                                                      \
     do {                                                                                  \
-        const auto f0 = opaque_s(a.t[0].f), f1 = opaque_s(a.t[1].f), f2 = opaque_s(a.t[2].f); \
-        v.f = i == 2 ? f2 : (i == 1 ? f1 : f0);                                           \
+        const auto f0 = opaque_s(a.t[0].f), f1 = opaque_s(a.t[1].f);                      \
+        if (NT == 2) {                                                                    \
+            v.f = i == 1 ? f1 : f0;                                                       \
+        } else {                                                                          \
+            const auto f2 = opaque_s(a.t[2].f);                                           \
+            v.f = i == 2 ? f2 : (i == 1 ? f1 : f0);                                       \
+        }                                                                                 \
     } while (0)
     TaskView v;
     ROPE_PICK(x);
@@ -329,13 +335,14 @@ __device__ inline int task_index(const KArgs& a, int64_t wave) {
     return wave >= a.t[2].wave_begin ? 2 : (wave >= a.t[1].wave_begin ? 1 : 0);
 }
 
-// The task of wave gw. MT (compile time): the launch may hold several
-// tasks; a single-task instance reads task 0's fields only (a runtime branch
-// on the task count would put one more dependent scalar load before them).
-template <int COEF, bool NORM, bool MT>
+// The task of wave gw in a launch of NT tasks (compile time: a runtime
+// branch on the count would put one more dependent scalar load before the
+// fields): one task reads task 0's fields only, two select between two.
+template <int COEF, bool NORM, int NT>
 __device__ inline TaskView task_pick(const KArgs& a, int64_t gw) {
-    if (MT) return task_of<COEF, NORM>(a, task_index(a, gw));
-    return task0_of<COEF, NORM>(a);
+    if (NT == 1) return task0_of<COEF, NORM>(a);
+    if (NT == 2) return task_of<COEF, NORM, 2>(a, gw >= a.t[1].wave_begin ? 1 : 0);
+    return task_of<COEF, NORM>(a, task_index(a, gw));
 }
 
 __device__ inline int task_index_items(const KArgs& a, int64_t item) {
@@ -394,7 +401,7 @@ __device__ inline void load_batch(const char* x, const int64_t* off, const bool*
     }
 }
 
-template <typename T, int IL, int COEF, int IPL, int HU, bool NORM = false, bool MT = true>
+template <typename T, int IL, int COEF, int IPL, int HU, bool NORM = false, int NT = kMaxTasks>
 __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation item
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     // task selection and its fields in scalar registers
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + wave_in_block;
-    const TaskView tk = task_pick<COEF, NORM, MT>(a, gw);
+    const TaskView tk = task_pick<COEF, NORM, NT>(a, gw);
     // 32-bit index arithmetic (the planner keeps a vector-kernel launch's
     // waves and tokens below 2^31): a short scalar prologue before the loads
     const uint32_t local = (uint32_t)(gw - tk.wave_begin);
@@ -833,7 +840,7 @@ __device__ inline int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <typename T, int IL, int COEF, bool NORM, bool MT = true>
+template <typename T, int IL, int COEF, bool NORM, int NT = kMaxTasks>
 __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     constexpr int E = Elem<T>::E;
     constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation chunk
@@ -843,7 +850,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     const int lane = threadIdx.x & 63;
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
-    const TaskView tk = task_pick<COEF, NORM, MT>(a, gw);
+    const TaskView tk = task_pick<COEF, NORM, NT>(a, gw);
     // 32-bit index arithmetic: the planner keeps the waves and tokens of a
     // row-kernel launch below 2^31
     const uint32_t local = (uint32_t)(gw - tk.wave_begin);
@@ -1208,11 +1215,11 @@ inline int launched(hipError_t e) {
 }
 
 // Instantiated (items per lane, head batch) pairs; the planner picks one.
-template <typename T, int IL, int COEF, bool MT>
+template <typename T, int IL, int COEF, int NT>
 inline hipError_t launch_vec_ipl(const KArgs& a, int ipl, int hu, dim3 grid, hipStream_t st) {
     void* args[] = {const_cast<KArgs*>(&a)};
     const void* fn;
-#define ROPE_VEC(I, H) (const void*)rope_vec_kernel<T, IL, COEF, I, H, false, MT>
+#define ROPE_VEC(I, H) (const void*)rope_vec_kernel<T, IL, COEF, I, H, false, NT>
     switch (ipl * 16 + hu) {
         case 1 * 16 + 2: fn = ROPE_VEC(1, 2); break;
         case 1 * 16 + 4: fn = ROPE_VEC(1, 4); break;
@@ -1230,15 +1237,28 @@ inline hipError_t launch_vec_ipl(const KArgs& a, int ipl, int hu, dim3 grid, hip
     return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
 }
 
+template <typename T, int IL, int COEF>
+inline hipError_t launch_vec_nt(const KArgs& a, int ipl, int hu, dim3 grid, hipStream_t st) {
+    switch (a.ntask) {
+        case 1: return launch_vec_ipl<T, IL, COEF, 1>(a, ipl, hu, grid, st);
+        case 2: return launch_vec_ipl<T, IL, COEF, 2>(a, ipl, hu, grid, st);
+        case 3: return launch_vec_ipl<T, IL, COEF, 3>(a, ipl, hu, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // QK-norm: one item per lane, any instantiated head batch.
 template <typename T, int IL, int COEF>
 inline hipError_t launch_vec_norm(const KArgs& a, int hu, dim3 grid, hipStream_t st) {
+    // QK-norm launches hold Q and K, the cache append Q, K and V
+    constexpr int NT = COEF == kCoefAppend ? 3 : 2;
+    if (a.ntask != NT) return hipErrorInvalidValue;
     void* args[] = {const_cast<KArgs*>(&a)};
     const void* fn;
     switch (hu) {
-        case 2: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 2, true>; break;
-        case 4: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 4, true>; break;
-        case 8: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 8, true>; break;
+        case 2: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 2, true, NT>; break;
+        case 4: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 4, true, NT>; break;
+        case 8: fn = (const void*)rope_vec_kernel<T, IL, COEF, 1, 8, true, NT>; break;
         default: return hipErrorInvalidValue;
     }
     return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
@@ -1258,20 +1278,17 @@ inline hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, d
         }
     }
     switch (c) {
-        // M-RoPE launches hold one task, the cache append three (Q, K, V)
-        case kCoefGather:
-            return a.ntask > 1 ? launch_vec_ipl<T, IL, kCoefGather, true>(a, ipl, hu, grid, st)
-                               : launch_vec_ipl<T, IL, kCoefGather, false>(a, ipl, hu, grid, st);
-        case kCoefPerToken:
-            return a.ntask > 1 ? launch_vec_ipl<T, IL, kCoefPerToken, true>(a, ipl, hu, grid, st)
-                               : launch_vec_ipl<T, IL, kCoefPerToken, false>(a, ipl, hu, grid, st);
+        // M-RoPE launches hold one task, the cache append three (Q, K, V);
+        // the others one (RotaryEmbedding), two (Q+K) or three (packed)
+        case kCoefGather: return launch_vec_nt<T, IL, kCoefGather>(a, ipl, hu, grid, st);
+        case kCoefPerToken: return launch_vec_nt<T, IL, kCoefPerToken>(a, ipl, hu, grid, st);
         case kCoefMrope:
             if (a.ntask != 1) return hipErrorInvalidValue;
-            return launch_vec_ipl<T, IL, kCoefMrope, false>(a, ipl, hu, grid, st);
-        case kCoefAppend: return launch_vec_ipl<T, IL, kCoefAppend, true>(a, ipl, hu, grid, st);
-        default:
-            return a.ntask > 1 ? launch_vec_ipl<T, IL, kCoefOnTheFly, true>(a, ipl, hu, grid, st)
-                               : launch_vec_ipl<T, IL, kCoefOnTheFly, false>(a, ipl, hu, grid, st);
+            return launch_vec_ipl<T, IL, kCoefMrope, 1>(a, ipl, hu, grid, st);
+        case kCoefAppend:
+            if (a.ntask != 3) return hipErrorInvalidValue;
+            return launch_vec_ipl<T, IL, kCoefAppend, 3>(a, ipl, hu, grid, st);
+        default: return launch_vec_nt<T, IL, kCoefOnTheFly>(a, ipl, hu, grid, st);
     }
 }
 
@@ -1279,25 +1296,30 @@ template <typename T, int IL>
 inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream_t st, bool norm) {
     void* args[] = {const_cast<KArgs*>(&a)};
     const void* fn;
-    // norm launches hold two or three tasks (Q and K, or Q, K and V)
+    // QK-norm launches hold Q and K; the cache append Q, K and V; M-RoPE one
+    // task; the others one (RotaryEmbedding), two (Q+K) or three (packed)
 #define ROPE_ROW(K)                                                                      \
-    (norm ? (const void*)rope_row_kernel<T, IL, K, true, true>                           \
-          : (a.ntask > 1 ? (const void*)rope_row_kernel<T, IL, K, false, true>           \
-                         : (const void*)rope_row_kernel<T, IL, K, false, false>))
+    (norm ? (a.ntask == 2 ? (const void*)rope_row_kernel<T, IL, K, true, 2> : nullptr)   \
+          : (a.ntask == 1   ? (const void*)rope_row_kernel<T, IL, K, false, 1>           \
+             : a.ntask == 2 ? (const void*)rope_row_kernel<T, IL, K, false, 2>           \
+             : a.ntask == 3 ? (const void*)rope_row_kernel<T, IL, K, false, 3>           \
+                            : nullptr))
     switch (c) {
         case kCoefGather: fn = ROPE_ROW(kCoefGather); break;
         case kCoefPerToken: fn = ROPE_ROW(kCoefPerToken); break;
         case kCoefOnTheFly: fn = ROPE_ROW(kCoefOnTheFly); break;
         case kCoefAppend:
-            fn = norm ? (const void*)rope_row_kernel<T, IL, kCoefAppend, true, true>
-                      : (const void*)rope_row_kernel<T, IL, kCoefAppend, false, true>;
+            if (a.ntask != 3) return hipErrorInvalidValue;
+            fn = norm ? (const void*)rope_row_kernel<T, IL, kCoefAppend, true, 3>
+                      : (const void*)rope_row_kernel<T, IL, kCoefAppend, false, 3>;
             break;
         case kCoefMrope:
             if (norm || a.ntask != 1) return hipErrorInvalidValue;
-            fn = (const void*)rope_row_kernel<T, IL, kCoefMrope, false, false>;
+            fn = (const void*)rope_row_kernel<T, IL, kCoefMrope, false, 1>;
             break;
         default: return hipErrorInvalidValue;
     }
+    if (!fn) return hipErrorInvalidValue;
 #undef ROPE_ROW
     return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
 }
@@ -1357,13 +1379,15 @@ hipError_t launch_table_for(const float* inv, void* cos, void* sin, int64_t rows
     return hipLaunchKernel((const void*)table_kernel<T>, grid, dim3(kBlock), args, 0, st);
 }
 
-#define ROPE_TYPE_ENTRY_POINTS(EXT, T)                                                             \
+#define ROPE_VEC_ENTRY_POINTS(EXT, T)                                                              \
     EXT template hipError_t launch_vector_for<T>(const KArgs&, CoefKind, int, int, int, dim3,      \
-                                                 hipStream_t, bool);                               \
+                                                 hipStream_t, bool);
+#define ROPE_ROW_ENTRY_POINTS(EXT, T)                                                              \
     EXT template hipError_t launch_row_for<T>(const KArgs&, CoefKind, int, dim3, hipStream_t, bool); \
     EXT template hipError_t launch_scalar_for<T>(const KArgs&, CoefKind, int64_t, hipStream_t, bool); \
     EXT template hipError_t launch_table_for<T>(const float*, void*, void*, int64_t, int64_t, float, \
                                                 dim3, hipStream_t);
+#define ROPE_TYPE_ENTRY_POINTS(EXT, T) ROPE_VEC_ENTRY_POINTS(EXT, T) ROPE_ROW_ENTRY_POINTS(EXT, T)
 // instantiated elsewhere: every translation unit but its own refers to them
 ROPE_TYPE_ENTRY_POINTS(extern, float)
 ROPE_TYPE_ENTRY_POINTS(extern, half_t)

@@ -1,6 +1,6 @@
-// rope_kernels_bf16.hip -- the kernels for bfloat16 storage (see rope_device.hpp).
+// rope_kernels_bf16.hip -- the vector kernel for bfloat16 storage (see rope_device.hpp).
 #include "rope_device.hpp"
 
 namespace rope {
-ROPE_TYPE_ENTRY_POINTS(, bf16_t)
+ROPE_VEC_ENTRY_POINTS(, bf16_t)
 }  // namespace rope
