@@ -64,6 +64,8 @@ struct KTask {
     int32_t yrow;          // append kind: y row is the token's position
     int64_t ysb, ysh, yss; // append kind: element strides of y (b, h, row)
     const char* wgt;       // QK-norm: (D,) weight of this projection
+    // division by chunks, tile and tile * chunks (multiply-high and shift)
+    uint32_t chunks_m, chunks_s, tile_m, tile_s, per_tile_m, per_tile_s;
 };
 
 struct KArgs {
@@ -82,6 +84,7 @@ struct KArgs {
     int32_t row_lanes;          // row kernel: lanes per head row (a power of two)
     int32_t row_shift;          // log2(row_lanes)
     int32_t half_lanes;         // row kernel, split halves: lanes between partner chunks
+    uint32_t w_m, w_s, s_m, s_s;  // division by W and by S (multiply-high and shift)
     const int32_t* seqlens;     // append kind: total key length per sequence
     int64_t rows_out;           // append kind: cache rows
     uint32_t sel[kSelWords];
@@ -246,7 +249,17 @@ struct TaskView {
     int32_t heads, hpw, chunks, tile, copy, yrow;
     int64_t ysb, ysh, yss;
     const char* wgt;
+    uint32_t chunks_m, chunks_s, tile_m, tile_s, per_tile_m, per_tile_s;
 };
+
+// n / d for n < 2^31 from the divisor's multiplier m and shift l, computed
+// on the host (ceil(log2 d) = l, m = floor(2^32 (2^l - d) / d) + 1): with
+// t = mulhi(m, n), n / d = (t + n) >> l (the round-up method of Granlund
+// and Montgomery, "Division by invariant integers using multiplication",
+// 1994; the sum stays below 2^32 because t <= n < 2^31).
+__device__ inline uint32_t fast_div(uint32_t n, uint32_t m, uint32_t l) {
+    return (__umulhi(m, n) + n) >> l;
+}
 
 // An SGPR value the compiler must treat as opaque: keeps a select of two
 // kernel-argument loads from being folded into one load from a selected
@@ -284,6 +297,12 @@ __device__ inline TaskView task_of(const KArgs& a, int i) {
     ROPE_PICK(hpw);
     ROPE_PICK(chunks);
     ROPE_PICK(tile);
+    ROPE_PICK(chunks_m);
+    ROPE_PICK(chunks_s);
+    ROPE_PICK(tile_m);
+    ROPE_PICK(tile_s);
+    ROPE_PICK(per_tile_m);
+    ROPE_PICK(per_tile_s);
     ROPE_PICK(copy);
     if (COEF == kCoefAppend) {
         ROPE_PICK(yrow);
@@ -321,6 +340,12 @@ __device__ inline TaskView task0_of(const KArgs& a) {
     v.hpw = t.hpw;
     v.chunks = t.chunks;
     v.tile = t.tile;
+    v.chunks_m = t.chunks_m;
+    v.chunks_s = t.chunks_s;
+    v.tile_m = t.tile_m;
+    v.tile_s = t.tile_s;
+    v.per_tile_m = t.per_tile_m;
+    v.per_tile_s = t.per_tile_s;
     v.copy = t.copy;
     v.yrow = COEF == kCoefAppend ? t.yrow : 0;
     v.ysb = COEF == kCoefAppend ? t.ysb : t.sb;
@@ -417,10 +442,14 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     // 32-bit index arithmetic (the planner keeps a vector-kernel launch's
     // waves and tokens below 2^31): a short scalar prologue before the loads
     const uint32_t local = (uint32_t)(gw - tk.wave_begin);
+    // The QK-norm instances keep the hardware-sequence divisions: measured on
+    // MI355X, a shorter prologue made their prefill slower (31.8 vs 30.9 us;
+    // at 160 VGPRs they run 3 waves per SIMD, so the launch comes in two
+    // rounds of waves, and earlier loads arrive in a sharper burst).
     const uint32_t per_tile = (uint32_t)tk.tile * (uint32_t)tk.chunks;
-    const uint32_t tile = local / per_tile;
+    const uint32_t tile = NORM ? local / per_tile : fast_div(local, tk.per_tile_m, tk.per_tile_s);
     const int r = (int)(local - tile * per_tile);
-    const int hc = r / tk.tile;
+    const int hc = NORM ? r / tk.tile : (int)fast_div((uint32_t)r, tk.tile_m, tk.tile_s);
     const uint32_t g = tile * (uint32_t)tk.tile + (uint32_t)(r - hc * tk.tile);
     const uint32_t n0 = g * (uint32_t)a.TG;
     if (n0 >= (uint64_t)a.ntok) return;
@@ -442,13 +471,13 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 #pragma unroll
     for (int m = 0; m < IPL; ++m) {
         const int q = lane + 64 * m;
-        const int t = q / a.W;
+        const int t = NORM ? q / a.W : (int)fast_div((uint32_t)q, a.w_m, a.w_s);
         const int w = q - t * a.W;
         const uint32_t n = n0 + (uint32_t)t;
         act[m] = t < a.TG && n < (uint64_t)a.ntok;
         rot[m] = act[m] && w < a.NP;
         const uint32_t n32 = act[m] ? n : 0u;
-        const uint32_t b32 = n32 / (uint32_t)a.S;
+        const uint32_t b32 = NORM ? n32 / (uint32_t)a.S : fast_div(n32, a.s_m, a.s_s);
         tok[m] = n32;
         const int64_t b = b32;
         const int64_t s = (int64_t)(n32 - b32 * (uint32_t)a.S);
@@ -854,7 +883,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     // 32-bit index arithmetic: the planner keeps the waves and tokens of a
     // row-kernel launch below 2^31
     const uint32_t local = (uint32_t)(gw - tk.wave_begin);
-    const uint32_t n32 = local / (uint32_t)tk.chunks;  // the token
+    const uint32_t n32 = fast_div(local, tk.chunks_m, tk.chunks_s);  // the token
     const int part = (int)(local - n32 * (uint32_t)tk.chunks);
     if (n32 >= (uint64_t)a.ntok) return;
     const int rpi = 64 >> a.row_shift;  // head rows per instruction
@@ -862,7 +891,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     const int c = lane & (a.row_lanes - 1);
     const int h0 = part * tk.hpw;
     const int nh = min(tk.heads - h0, tk.hpw);
-    const uint32_t b32 = n32 / (uint32_t)a.S;
+    const uint32_t b32 = fast_div(n32, a.s_m, a.s_s);
     const int64_t n = n32;
     const int64_t b = b32;
     const int64_t s = (int64_t)(n32 - b32 * (uint32_t)a.S);

@@ -14,6 +14,17 @@ __global__ __launch_bounds__(kBlock) void inv_freq_kernel(float* out, int64_t ha
     out[i] = (float)pow(base, -2.0 * (double)i / (double)(2 * half));
 }
 
+// Multiplier and shift for division by d (1 <= d < 2^31) of dividends below
+// 2^31, as fast_div in rope_device.hpp uses them.
+static void fast_div_magic(int64_t d, uint32_t* m, uint32_t* l) {
+    if (d < 1) d = 1;
+    uint32_t s = 0;
+    while (((int64_t)1 << s) < d) ++s;
+    const unsigned __int128 num = ((unsigned __int128)1 << 32) * (unsigned __int128)(((int64_t)1 << s) - d);
+    *m = (uint32_t)(num / (unsigned __int128)d + 1);
+    *l = s;
+}
+
 int launch_plan(const Plan& pl, void* stream) {
     if (pl.empty) return ROPE_OK;
     const Problem& p = pl.p;
@@ -53,6 +64,9 @@ int launch_plan(const Plan& pl, void* stream) {
             a.t[t].hpw = g.heads_per_wave[t];
             a.t[t].chunks = g.chunks[t] > 0 ? g.chunks[t] : 1;
             a.t[t].tile = g.tile > 0 ? g.tile : 1;
+            fast_div_magic(a.t[t].chunks, &a.t[t].chunks_m, &a.t[t].chunks_s);
+            fast_div_magic(a.t[t].tile, &a.t[t].tile_m, &a.t[t].tile_s);
+            fast_div_magic((int64_t)a.t[t].tile * a.t[t].chunks, &a.t[t].per_tile_m, &a.t[t].per_tile_s);
             if (g.waves[t] > 0) {
                 a.t[t].wave_begin = wave_begin;
                 wave_begin += g.waves[t];
@@ -90,6 +104,8 @@ int launch_plan(const Plan& pl, void* stream) {
     a.row_shift = 0;
     while ((1 << a.row_shift) < a.row_lanes) ++a.row_shift;
     a.half_lanes = g.row_kernel ? g.half_lanes : 0;
+    fast_div_magic(a.W > 0 ? a.W : 1, &a.w_m, &a.w_s);
+    fast_div_magic(a.S > 0 ? a.S : 1, &a.s_m, &a.s_s);
     a.inv_d = 1.0f / (float)p.D;
     a.seqlens = p.seqlens;
     a.prompt = p.prompt;
