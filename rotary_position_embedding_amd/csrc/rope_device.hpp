@@ -76,7 +76,7 @@ struct KArgs {
     const int64_t* ids;
     const float* inv_freq;
     int32_t ntask, W, NP, TG, P, R, D, interleaved;
-    int32_t xcd_remap, prompt;  // prompt: append kind, every sequence starts at 0
+    int32_t pad0, prompt;       // prompt: append kind, every sequence starts at 0
     float scaling, scale;
     float eps;                  // QK-norm epsilon
     float inv_d;                // QK-norm: 1/D rounded to binary32
@@ -395,17 +395,11 @@ __device__ inline int task_index_items(const KArgs& a, int64_t item) {
 // the predicated loads (versus clamped unconditional ones). X and Y are
 // touched once: nontemporal loads and stores.
 
-// Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i % 8),
-// each XCD with its own L2. With remapping, consecutive logical workgroups
-// run on the same XCD, so the waves that share a token group's ids and
-// coefficient rows fill one L2 instead of several. A bijection on
-// [0, gridDim.x) for any grid size.
-__device__ inline uint32_t logical_block(int remap) {
-    const uint32_t p = blockIdx.x;
-    if (!remap) return p;
-    const uint32_t n = gridDim.x, q = n / 8, r = n % 8, x = p % 8;
-    return x * q + min(x, r) + p / 8;
-}
+// Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i % 8).
+// A remapping that keeps consecutive logical workgroups on one XCD (so that
+// the waves sharing a token group's coefficient rows fill one L2) measured
+// slower on MI355X and is not used; the workgroup order is the dispatch
+// order, which also keeps the kernel-argument loads in one batch.
 
 // X chunks of one head batch (one or two 16-byte chunks per item and head).
 template <typename T, int IL, int IPL, int HU>
@@ -437,7 +431,7 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     // wave-uniform by construction; readfirstlane lets the compiler keep the
     // task selection and its fields in scalar registers
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t gw = (int64_t)logical_block(a.xcd_remap) * kWavesPerBlock + wave_in_block;
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
     const TaskView tk = task_pick<COEF, NORM, NT>(a, gw);
     // 32-bit index arithmetic (the planner keeps a vector-kernel launch's
     // waves and tokens below 2^31): a short scalar prologue before the loads

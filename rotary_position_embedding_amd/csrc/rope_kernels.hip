@@ -95,7 +95,6 @@ int launch_plan(const Plan& pl, void* stream) {
     a.R = (int32_t)p.R;
     a.D = (int32_t)p.D;
     a.interleaved = p.interleaved;
-    a.xcd_remap = g.xcd_remap;
     a.scaling = p.scaling;
     a.scale = p.scale;
     a.eps = p.eps;

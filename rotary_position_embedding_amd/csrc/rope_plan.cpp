@@ -168,12 +168,12 @@ static int env_int(const char* name) {
 // Tuning overrides for measurement sweeps, read once per process (getenv
 // scans the environment: too slow for every call).
 struct TuningOverrides {
-    int heads_per_wave, items_per_lane, head_batch, xcd_remap, wave_tile, no_share, row_loads;
+    int heads_per_wave, items_per_lane, head_batch, wave_tile, no_share, row_loads;
 };
 static const TuningOverrides& overrides() {
     static const TuningOverrides o = {env_int("ROPE_HEADS_PER_WAVE"), env_int("ROPE_ITEMS_PER_LANE"),
-                                      env_int("ROPE_HEAD_BATCH"),     env_int("ROPE_XCD_REMAP"),
-                                      env_int("ROPE_WAVE_TILE"),      env_int("ROPE_NO_SHARE"),
+                                      env_int("ROPE_HEAD_BATCH"),     env_int("ROPE_WAVE_TILE"),
+                                      env_int("ROPE_NO_SHARE"),
                                       env_int("ROPE_ROW_LOADS")};
     return o;
 }
@@ -256,7 +256,6 @@ static bool choose_row_geometry(Plan* pl) {
     g.items_per_lane = 1;
     g.head_batch = loads;
     g.share_coef = 0;
-    g.xcd_remap = 0;
     return true;
 }
 
@@ -382,7 +381,6 @@ static void choose_geometry(Plan* pl) {
     // 2 groups for 2-byte types, 4 for 4-byte ones (measured on MI355X: the
     // fp16 M-RoPE prefill 21.7 us with 2, 22.1 with 4, 22.6 with 3; the fp32
     // partial interleaved case 37.4 us with 4, 37.9 with 2).
-    g.xcd_remap = overrides().xcd_remap;
     const int over_tile = overrides().wave_tile;
     g.tile = over_tile > 0 ? over_tile : (g.rank == 4 ? (es == 2 ? 2 : 4) : 1);
     const int64_t tiles = (groups + g.tile - 1) / g.tile;

@@ -83,7 +83,6 @@ struct Geometry {
     int32_t NP;           // of which rotation items
     int32_t TG;           // tokens per wave
     int32_t tile;         // token groups per head chunk in a tile of waves
-    int32_t xcd_remap;    // 1: consecutive workgroups on one XCD
     int32_t share_coef;   // on the fly: the 4 waves of a workgroup share one token group
     int32_t row_kernel;   // 1: the row kernel (lanes along head rows of one token)
     int32_t row_lanes;    // row kernel: lanes per head row
