@@ -446,7 +446,10 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     const int hc = NORM ? r / tk.tile : (int)fast_div((uint32_t)r, tk.tile_m, tk.tile_s);
     const uint32_t g = tile * (uint32_t)tk.tile + (uint32_t)(r - hc * tk.tile);
     const uint32_t n0 = g * (uint32_t)a.TG;
-    if (n0 >= (uint64_t)a.ntok) return;
+    // No early exit for waves past the last token (the rest of a partial
+    // tile): their items are inactive, so they load and store nothing. An exit
+    // branch here made the compiler defer kernel-argument loads behind it, one
+    // more dependent round of scalar loads for every wave.
     const int h_begin = hc * tk.hpw;
     const int h_end = min(tk.heads, h_begin + tk.hpw);
     const int64_t sh_bytes = tk.sh * ES;
