@@ -880,9 +880,15 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     // 32-bit index arithmetic: the planner keeps the waves and tokens of a
     // row-kernel launch below 2^31
     const uint32_t local = (uint32_t)(gw - tk.wave_begin);
-    const uint32_t n32 = fast_div(local, tk.chunks_m, tk.chunks_s);  // the token
-    const int part = (int)(local - n32 * (uint32_t)tk.chunks);
-    if (n32 >= (uint64_t)a.ntok) return;
+    const uint32_t nw = fast_div(local, tk.chunks_m, tk.chunks_s);  // the token
+    const int part = (int)(local - nw * (uint32_t)tk.chunks);
+    // Waves past the last token (in the last workgroup) run on a valid token
+    // and store nothing: an early exit makes the compiler defer
+    // kernel-argument loads behind the branch (measured slower, except for
+    // the cache-append kind, which exits)
+    const bool live = nw < (uint64_t)a.ntok;
+    if (COEF == kCoefAppend && !live) return;
+    const uint32_t n32 = live ? nw : (uint32_t)(a.ntok - 1);
     const int rpi = 64 >> a.row_shift;  // head rows per instruction
     const int hi = lane >> a.row_shift;
     const int c = lane & (a.row_lanes - 1);
@@ -1101,7 +1107,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
             o = chunk_pack<T>(y);
             if (COEF == kCoefMrope) o = select_bits(keep, in[u], o);
         }
-        if (act) store_nt(py + u * ystep, o);
+        if (act && live) store_nt(py + u * ystep, o);
     }
 }
 
