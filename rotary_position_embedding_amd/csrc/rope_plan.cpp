@@ -304,8 +304,9 @@ static void choose_geometry(Plan* pl) {
     //    27.1 us for (1, 8); 12 items per row: (3, 4), 19.3 vs 20.8 us);
     //  * 4-byte types: the smallest ipl keeping 3/4 of the lanes busy and at
     //    most 4 heads per batch (fp32 prefill 44.2 vs 51.1 us with 8 heads;
-    //    the partial interleaved fp32 case, 24 items per row, 37.3 us with
-    //    one item per lane vs 39.8 with three);
+    //    the partial interleaved fp32 case, 24 items per row, 35.9 us with
+    //    one item per lane and 4 heads per batch, 36.9 with three items and
+    //    2 heads, 38.2 with two and 4, 39.4 with four and 4);
     //  * QK-norm: one item per lane (its only instantiation).
     static const int kPairs[][2] = {{1, 2}, {1, 4}, {1, 8}, {2, 2}, {2, 4}, {2, 8},
                                     {3, 2}, {3, 4}, {4, 2}, {4, 4}};
@@ -380,7 +381,7 @@ static void choose_geometry(Plan* pl) {
     // token groups per head chunk gives each workgroup longer runs per head:
     // 2 groups for 2-byte types, 4 for 4-byte ones (measured on MI355X: the
     // fp16 M-RoPE prefill 21.7 us with 2, 22.1 with 4, 22.6 with 3; the fp32
-    // partial interleaved case 37.4 us with 4, 37.9 with 2).
+    // partial interleaved case 35.9 us with 4, 36.3 with 8).
     const int over_tile = overrides().wave_tile;
     g.tile = over_tile > 0 ? over_tile : (g.rank == 4 ? (es == 2 ? 2 : 4) : 1);
     const int64_t tiles = (groups + g.tile - 1) / g.tile;
