@@ -43,7 +43,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_rope_f16_prefill.json"
 KERNEL_SOURCES = [os.path.join(ROOT, "rotary_position_embedding_amd", "csrc", f)
                   for f in ("rope_device.hpp", "rope_kernels.hip", "rope_kernels_f32.hip",
                             "rope_kernels_f16.hip", "rope_kernels_bf16.hip", "rope_kernels_f32_row.hip",
-                            "rope_kernels_f16_row.hip", "rope_kernels_bf16_row.hip")]
+                            "rope_kernels_f16_row.hip", "rope_kernels_bf16_row.hip",
+                            "rope_plan.hpp", "rope_plan.cpp")]  # the planner sets the launch geometry
 
 
 # kernel variant prefix (as the *_check functions report it) -> kernel function

@@ -198,7 +198,7 @@ int rope_apply_qk(const rope_tensor* q, const rope_tensor* k,
  * y:            same shape and type. Query and key heads rotated exactly as
  *               rope_apply_qk would; value heads copied bit for bit. y may be
  *               qkv itself (in place); then the value heads are not touched.
- * num_heads, kv_num_heads: required (>= 1); kv_num_heads divides num_heads.
+ * num_heads, kv_num_heads: required (>= 1, num_heads <= 2^31 - 1); kv_num_heads divides num_heads.
  * Tables, position_ids, inv_freq (on the fly when both tables are NULL),
  * interleaved, rotary_embedding_dim, attention_scaling: as rope_apply_qk.
  */
@@ -263,7 +263,7 @@ int rope_apply_qk_norm(const rope_tensor* q, const rope_tensor* k,
  *               packed (in place). The caches may not overlap any input,
  *               q_out or each other.
  * rotary_interleaved: 0 half-split pairs, 1 adjacent pairs.
- * num_heads, kv_num_heads: >= 1, kv_num_heads divides num_heads.
+ * num_heads, kv_num_heads: >= 1, num_heads <= 2^31 - 1, kv_num_heads divides num_heads.
  * Device data outside the README's bounds (a per-sequence length above
  * total_sequence_length or below S): a row outside [0, Smax) is not written
  * and a position outside [0, M) keeps its pairs; nothing is read or written

@@ -463,6 +463,14 @@ static int activation_dims(const rope_tensor* x, const char* name, int64_t heads
     return fail(ROPE_ERR_RANK, "%s must be rank 3 or 4, got %d", name, (int)x->rank);
 }
 
+// Head counts of the packed layouts (num_heads + 2 * kv_num_heads heads per
+// token, kv_num_heads dividing num_heads): bounded so that the sum fits.
+static int check_head_count(int64_t num_heads) {
+    if (num_heads > INT32_MAX)
+        return fail(ROPE_ERR_ATTRIBUTE, "num_heads %lld exceeds 2^31 - 1", (long long)num_heads);
+    return ROPE_OK;
+}
+
 #define TRY(expr)                          \
     do {                                   \
         int rc_ = (expr);                  \
@@ -478,7 +486,7 @@ static int check_tables(const rope_tensor* cos, const rope_tensor* sin, const ro
     if (ids) {
         if (cos->rank != 2)
             return fail(ROPE_ERR_RANK, "cos_cache must be rank 2 (max_sequence_length, rotary_dim/2) with position_ids");
-        if (cos->shape[1] * 2 != R)
+        if (cos->shape[1] != R / 2)
             return fail(ROPE_ERR_SHAPE, "cos_cache width %lld * 2 != rotary dim %lld",
                         (long long)cos->shape[1], (long long)R);
         if (ids->rank != 2)
@@ -494,7 +502,7 @@ static int check_tables(const rope_tensor* cos, const rope_tensor* sin, const ro
     if (cos->shape[0] != B || cos->shape[1] != S)
         return fail(ROPE_ERR_SHAPE, "cos_cache leading dims (%lld, %lld) != (batch %lld, sequence %lld)",
                     (long long)cos->shape[0], (long long)cos->shape[1], (long long)B, (long long)S);
-    if (cos->shape[2] * 2 != R)
+    if (cos->shape[2] != R / 2)
         return fail(ROPE_ERR_SHAPE, "cos_cache width %lld * 2 != rotary dim %lld",
                     (long long)cos->shape[2], (long long)R);
     *M = 0;
@@ -633,9 +641,10 @@ int plan_mrope(const rope_tensor* x, const rope_tensor* position_ids, const rope
     if (half > kMaxMropeHalf)
         return fail(ROPE_ERR_UNSUPPORTED, "rotary dim / 2 = %lld exceeds %d", (long long)half,
                     kMaxMropeHalf);
-    if (mrope_section[0] + mrope_section[1] + mrope_section[2] != half)
-        return fail(ROPE_ERR_ATTRIBUTE, "mrope_section sums to %lld, must be rotary dim / 2 = %lld",
-                    (long long)(mrope_section[0] + mrope_section[1] + mrope_section[2]),
+    if (mrope_section[0] > half || mrope_section[1] > half || mrope_section[2] > half ||
+        mrope_section[0] + mrope_section[1] + mrope_section[2] != half)  // no overflow: each <= half
+        return fail(ROPE_ERR_ATTRIBUTE, "mrope_section (%lld, %lld, %lld) must sum to rotary dim / 2 = %lld",
+                    (long long)mrope_section[0], (long long)mrope_section[1], (long long)mrope_section[2],
                     (long long)half);
     if (cos_cache->rank != 2)
         return fail(ROPE_ERR_RANK, "cos_cache must be rank 2 (max_sequence_length, rotary_dim/2)");
@@ -738,7 +747,7 @@ int plan_rope_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor* 
     if (!onthefly) {
         TRY(check_tables(cos_cache, sin_cache, position_ids, B, S, R, &M));
     } else {
-        if (inv_freq->rank != 1 || inv_freq->shape[0] * 2 != R)
+        if (inv_freq->rank != 1 || inv_freq->shape[0] != R / 2)
             return fail(ROPE_ERR_SHAPE, "inv_freq must be (rotary_dim/2,) = (%lld,)", (long long)(R / 2));
         if (position_ids->rank != 2)
             return fail(ROPE_ERR_RANK, "position_ids must be rank 2 (batch, sequence)");
@@ -857,6 +866,7 @@ int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
         return fail(ROPE_ERR_ATTRIBUTE, "interleaved must be 0 or 1");
     if (num_heads < 1 || kv_num_heads < 1)
         return fail(ROPE_ERR_ATTRIBUTE, "num_heads and kv_num_heads are required (>= 1) for packed QKV");
+    TRY(check_head_count(num_heads));
     if (num_heads % kv_num_heads != 0)
         return fail(ROPE_ERR_SHAPE, "kv_num_heads %lld must divide num_heads %lld",
                     (long long)kv_num_heads, (long long)num_heads);
@@ -885,7 +895,7 @@ int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
     if (!onthefly) {
         TRY(check_tables(cos_cache, sin_cache, position_ids, B, S, R, &M));
     } else {
-        if (inv_freq->rank != 1 || inv_freq->shape[0] * 2 != R)
+        if (inv_freq->rank != 1 || inv_freq->shape[0] != R / 2)
             return fail(ROPE_ERR_SHAPE, "inv_freq must be (rotary_dim/2,) = (%lld,)", (long long)(R / 2));
         if (position_ids->rank != 2)
             return fail(ROPE_ERR_RANK, "position_ids must be rank 2 (batch, sequence)");
@@ -982,6 +992,7 @@ int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
         return fail(ROPE_ERR_ATTRIBUTE, "rotary_interleaved must be 0 or 1");
     if (num_heads < 1 || kv_num_heads < 1)
         return fail(ROPE_ERR_ATTRIBUTE, "num_heads and kv_num_heads are required (>= 1)");
+    TRY(check_head_count(num_heads));
     if (num_heads % kv_num_heads != 0)
         return fail(ROPE_ERR_SHAPE, "kv_num_heads %lld must divide num_heads %lld",
                     (long long)kv_num_heads, (long long)num_heads);
@@ -1011,11 +1022,11 @@ int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
         return fail(ROPE_ERR_SHAPE, "key_total_sequence_lengths must be (batch,) = (%lld,)", (long long)B);
     if (cos_cache->rank != 2) return fail(ROPE_ERR_RANK, "cos_cache must be rank 2 (rows, rotary_dim/2)");
     if (!same_shape(cos_cache, sin_cache)) return fail(ROPE_ERR_SHAPE, "sin_cache must have the shape of cos_cache");
-    const int64_t R = 2 * cos_cache->shape[1];
-    const int64_t M = cos_cache->shape[0];
-    if (R < 2 || R > D)
+    if (cos_cache->shape[1] < 1 || cos_cache->shape[1] > D / 2)
         return fail(ROPE_ERR_SHAPE, "cos_cache width %lld must be in [1, head_size/2 = %lld]",
                     (long long)cos_cache->shape[1], (long long)(D / 2));
+    const int64_t R = 2 * cos_cache->shape[1];
+    const int64_t M = cos_cache->shape[0];
     if (q_out->rank != 3 || q_out->shape[0] != B || q_out->shape[1] != S || q_out->shape[2] != num_heads * D)
         return fail(ROPE_ERR_SHAPE, "q_out must be (%lld, %lld, %lld)", (long long)B, (long long)S,
                     (long long)(num_heads * D));

@@ -302,6 +302,45 @@ def check_mrope(kw):
     return rpe.mrope_apply_check(*args, **kw)
 
 
+def test_huge_dimension_beside_a_zero_one():
+    """A zero dimension admits any other dimension (the element count stays
+    0): table widths far beyond any rotary dim are still shape errors."""
+    lib = _lib.load()
+    huge = 2 ** 62
+    kw = rope_case()
+    kw["cos_cache"] = reshape(kw["cos_cache"], (0, huge))
+    kw["sin_cache"] = reshape(kw["sin_cache"], (0, huge))
+    assert check_rope(kw)[0] == SHAPE, lib.rope_last_error()
+    kw = rope_case(ids=False, B=0)
+    kw["cos_cache"] = reshape(kw["cos_cache"], (0, 5, huge))
+    kw["sin_cache"] = reshape(kw["sin_cache"], (0, 5, huge))
+    assert check_rope(kw)[0] == SHAPE, lib.rope_last_error()
+    kw = mrope_case()
+    kw["cos_cache"] = reshape(kw["cos_cache"], (0, huge))
+    kw["sin_cache"] = reshape(kw["sin_cache"], (0, huge))
+    assert check_mrope(kw)[0] == SHAPE, lib.rope_last_error()
+
+
+def test_head_counts_whose_packed_sum_overflows():
+    """Packed layouts hold num_heads + 2 * kv_num_heads heads per token: head
+    counts above 2^31 - 1 are attribute errors, not an overflowing sum."""
+    lib = _lib.load()
+    big = 2 ** 62
+    assert check_packed(packed_case(num_heads=big, kv_num_heads=big))[0] == ATTR, lib.rope_last_error()
+    assert check_kv(kv_case(num_heads=big, kv_num_heads=big))[0] == ATTR, lib.rope_last_error()
+    assert check_kv(kv_case(packed=True, num_heads=big, kv_num_heads=big))[0] == ATTR, lib.rope_last_error()
+    # the largest accepted count still plans (a rank-3 width of zero heads)
+    kw = packed_case(B=0, num_heads=2 ** 31 - 1, kv_num_heads=1)
+    kw["qkv"] = reshape(kw["qkv"], (0, 3, 0))
+    kw["y"] = reshape(kw["y"], (0, 3, 0))
+    assert check_packed(kw)[0] != ATTR, lib.rope_last_error()
+    # a cache-append table width far beyond the head size, beside zero rows
+    kw = kv_case()
+    kw["cos_cache"] = reshape(kw["cos_cache"], (0, 2 ** 62))
+    kw["sin_cache"] = reshape(kw["sin_cache"], (0, 2 ** 62))
+    assert check_kv(kw)[0] == SHAPE, lib.rope_last_error()
+
+
 def test_mrope_accepted():
     for rank in (3, 4):
         for layout in (0, 1):
@@ -326,6 +365,7 @@ def test_mrope_clauses():
         ("interleaved 2", ATTR, dict(interleaved=2)),
         ("negative section", ATTR, dict(mrope_section=(5, -1, 4))),
         ("section sum", ATTR, dict(mrope_section=(4, 2, 1))),
+        ("section entries whose sum overflows", ATTR, dict(mrope_section=(2 ** 63 - 1, 2 ** 63 - 1, 4))),
         ("rotary odd", ATTR, dict(rotary_embedding_dim=7)),
         ("rotary negative", ATTR, dict(rotary_embedding_dim=-2)),
         ("num_heads negative", ATTR, dict(num_heads=-1)),
