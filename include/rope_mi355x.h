@@ -46,7 +46,8 @@
  *     means nothing was launched. ROPE_ERR_LAUNCH means a launch was
  *     attempted and the HIP runtime refused it. Problems of 2^31 tokens or
  *     more (or whose vector kernel would need 2^31 waves) run on the
- *     grid-stride scalar kernel, whose grid is bounded.
+ *     grid-stride scalar kernel, whose grid is bounded. A head size or a
+ *     head count above 2^31 - 1 is ROPE_ERR_UNSUPPORTED.
  *   - A tensor with a zero dimension is valid; an op whose output is empty
  *     launches nothing and returns ROPE_OK. Data pointers of non-empty
  *     tensors must not be NULL.

@@ -415,6 +415,20 @@ static void choose_geometry(Plan* pl) {
     }
 }
 
+// The kernels take the head size and head counts as 32-bit values (every
+// other size is 64-bit): larger ones are refused before anything launches.
+// Then the kernel choice.
+static int finish_plan(Plan* pl) {
+    const Problem& p = pl->p;
+    if (p.D > INT32_MAX)
+        return fail(ROPE_ERR_UNSUPPORTED, "head_size %lld exceeds 2^31 - 1", (long long)p.D);
+    for (int t = 0; t < p.ntask; ++t)
+        if (p.task[t].heads > INT32_MAX)
+            return fail(ROPE_ERR_UNSUPPORTED, "head count %lld exceeds 2^31 - 1", (long long)p.task[t].heads);
+    choose_geometry(pl);
+    return ROPE_OK;
+}
+
 static void fill_strides(Task* t, int rank, int64_t S, int64_t H, int64_t D) {
     t->heads = H;
     if (rank == 4) {
@@ -578,8 +592,7 @@ int plan_rope(const rope_tensor* x, const rope_tensor* cos_cache, const rope_ten
     p.scaling = 1.0f;
     out->empty = numel(x) == 0;
     out->g.rank = x->rank;
-    choose_geometry(out);
-    return ROPE_OK;
+    return finish_plan(out);
 }
 
 int plan_mrope(const rope_tensor* x, const rope_tensor* position_ids, const rope_tensor* cos_cache,
@@ -683,8 +696,7 @@ int plan_mrope(const rope_tensor* x, const rope_tensor* position_ids, const rope
         p.sel[i / 16] |= (uint32_t)streams[i] << (2 * (i % 16));
     out->empty = numel(x) == 0;
     out->g.rank = x->rank;
-    choose_geometry(out);
-    return ROPE_OK;
+    return finish_plan(out);
 }
 
 int plan_rope_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor* cos_cache,
@@ -788,8 +800,7 @@ int plan_rope_qk(const rope_tensor* q, const rope_tensor* k, const rope_tensor* 
     }
     out->empty = numel(q) == 0 && numel(k) == 0;
     out->g.rank = q->rank;
-    choose_geometry(out);
-    return ROPE_OK;
+    return finish_plan(out);
 }
 
 // QK-norm then RoPE: onnxruntime PR #27590 review, Qwen3 architecture (RMSNorm
@@ -824,8 +835,7 @@ int plan_rope_qk_norm(const rope_tensor* q, const rope_tensor* k, const rope_ten
     p.eps = epsilon;
     p.task[0].weight = q_weight->data;
     p.task[1].weight = k_weight->data;
-    choose_geometry(out);
-    return ROPE_OK;
+    return finish_plan(out);
 }
 
 // Packed [Q|K|V]: the SparseAttention README's packed query input holds,
@@ -941,8 +951,7 @@ int plan_rope_qkv_packed(const rope_tensor* qkv, const rope_tensor* cos_cache,
     }
     out->empty = numel(qkv) == 0;
     out->g.rank = qkv->rank;
-    choose_geometry(out);
-    return ROPE_OK;
+    return finish_plan(out);
 }
 
 // RoPE on Q and K with the key/value cache append: the SparseAttention
@@ -1092,8 +1101,7 @@ int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
     p.scaling = 1.0f;
     out->empty = B * S == 0;
     out->g.rank = 3;
-    choose_geometry(out);
-    return ROPE_OK;
+    return finish_plan(out);
 }
 
 // The cache append with QK-norm: Q and K RMS-normalised before the rotation
@@ -1134,8 +1142,7 @@ int plan_rope_kv_append_qk_norm(const rope_tensor* query, const rope_tensor* key
     p.task[0].weight = q_weight->data;
     p.task[1].weight = k_weight->data;
     p.task[2].weight = nullptr;  // V: copied, never normalised
-    choose_geometry(out);
-    return ROPE_OK;
+    return finish_plan(out);
 }
 
 int plan_inv_freq(const rope_tensor* inv_freq, double base, float** out, int64_t* half) {

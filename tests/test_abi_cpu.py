@@ -341,6 +341,31 @@ def test_head_counts_whose_packed_sum_overflows():
     assert check_kv(kw)[0] == SHAPE, lib.rope_last_error()
 
 
+def test_head_size_and_head_count_limits():
+    """Head sizes and head counts reach the kernels as 32-bit values: above
+    2^31 - 1 they are refused before any launch (legal shapes of a few GiB)."""
+    lib = _lib.load()
+    a = Alloc()
+    x = a(F16, (1, 2 ** 31, 1, 2))  # 2^31 heads of 2 (8 GiB)
+    kw = dict(x=x, cos_cache=a(F16, (4, 1)), sin_cache=a(F16, (4, 1)), position_ids=a(I64, (1, 1)),
+              y=a(F16, (1, 2 ** 31, 1, 2)), interleaved=0, num_heads=0, rotary_embedding_dim=0)
+    assert check_rope(kw)[0] == UNSUP, lib.rope_last_error()
+    kw["x"] = a(F16, (1, 1, 2 ** 33)); kw["y"] = a(F16, (1, 1, 2 ** 33)); kw["num_heads"] = 2 ** 32
+    assert check_rope(kw)[0] == UNSUP, lib.rope_last_error()
+    D = 2 ** 31 + 2  # one head of 2^31 + 2 elements (4 GiB)
+    kw = dict(x=a(F16, (1, 1, 1, D)), cos_cache=a(F16, (4, D // 2)), sin_cache=a(F16, (4, D // 2)),
+              position_ids=a(I64, (1, 1)), y=a(F16, (1, 1, 1, D)), interleaved=0, num_heads=0,
+              rotary_embedding_dim=0)
+    assert check_rope(kw)[0] == UNSUP, lib.rope_last_error()
+    kw["rotary_embedding_dim"] = 2; kw["cos_cache"] = a(F16, (4, 1)); kw["sin_cache"] = a(F16, (4, 1))
+    assert check_rope(kw)[0] == UNSUP, lib.rope_last_error()
+    # just below the limits: accepted
+    x = a(F16, (1, 2 ** 31 - 1, 1, 2))
+    kw = dict(x=x, cos_cache=a(F16, (4, 1)), sin_cache=a(F16, (4, 1)), position_ids=a(I64, (1, 1)),
+              y=a(F16, (1, 2 ** 31 - 1, 1, 2)), interleaved=0, num_heads=0, rotary_embedding_dim=0)
+    assert check_rope(kw)[0] == OK, lib.rope_last_error()
+
+
 def test_mrope_accepted():
     for rank in (3, 4):
         for layout in (0, 1):
