@@ -233,11 +233,7 @@ def rope_kv_append(query, key, value, past_key, past_value, key_total_sequence_l
     [Q|K|V]. Returns q_out ((B, S, H*D): a new tensor, or `out`, which may be
     an unpacked query); past_key and past_value are updated in place."""
     dev = _device_of(query)
-    if out is None:
-        B, S = query.shape[0], query.shape[1]
-        width = query.shape[2]
-        groups = num_heads + (2 * kv_num_heads if key is None else 0)
-        out = torch.empty(B, S, width // groups * num_heads if groups else 0, dtype=query.dtype, device=dev)
+    out = _q_out_for(query, key, num_heads, kv_num_heads) if out is None else out
     ds = [_desc(t, dev) for t in (query, key, value, past_key, past_value, key_total_sequence_lengths,
                                   cos_cache, sin_cache, out)]
     with _on_device(dev):
@@ -275,10 +271,13 @@ def rope_kv_append_launcher(query, key, value, past_key, past_value, key_total_s
 
 
 def _q_out_for(query, key, num_heads, kv_num_heads):
-    B, S, width = query.shape
+    """q_out of (B, S, num_heads * head_size); shapes the library will refuse
+    get an empty placeholder, so that its status names the failing clause."""
     groups = num_heads + (2 * kv_num_heads if key is None else 0)
-    return torch.empty(B, S, width // groups * num_heads if groups else 0, dtype=query.dtype,
-                       device=query.device)
+    if query.dim() != 3 or groups < 1:
+        return torch.empty(0, dtype=query.dtype, device=query.device)
+    B, S, width = query.shape
+    return torch.empty(B, S, width // groups * num_heads, dtype=query.dtype, device=query.device)
 
 
 def rope_kv_append_qk_norm(query, key, value, past_key, past_value, key_total_sequence_lengths,

@@ -334,6 +334,18 @@ def test_errors_raise():
     assert e.value.status_name == "ROPE_ERR_SHAPE"
     with pytest.raises(rpe.RopeError):
         rpe.rope_apply(x, cos.float(), cos.float(), ids, num_heads=2)
+    # the cache append allocates q_out itself: a query of the wrong rank or a
+    # zero head count still reaches the library, whose status names the clause
+    pk = torch.zeros(2, 2, 8, 32, dtype=torch.float16, device=DEV)
+    lens = torch.full((2,), 4, dtype=torch.int32, device=DEV)
+    with pytest.raises(rpe.RopeError) as e:
+        rpe.rope_kv_append(x.view(6, 64), None, None, pk, pk.clone(), lens, 4, cos, cos,
+                           num_heads=2, kv_num_heads=2)
+    assert e.value.status_name == "ROPE_ERR_RANK"
+    with pytest.raises(rpe.RopeError) as e:
+        rpe.rope_kv_append_qk_norm(x, None, None, pk, pk.clone(), lens, 4, cos, cos, cos[0], cos[0],
+                                   epsilon=1e-6, num_heads=0, kv_num_heads=0)
+    assert e.value.status_name == "ROPE_ERR_ATTRIBUTE"
 
 
 # ---------------------------------------------------------------------------
