@@ -253,3 +253,57 @@ def test_kv_append_qk_norm_decode_full_size():
     assert_parity_norm(host(gk), ek, zc, "key cache")
     assert_bitwise(host(gv), ev, "value cache")
     print("norm decode full size", r, flush=True)
+
+
+@pytest.mark.parametrize("name", ["kv_append_f16_decode", "qk_norm_kv_append_f16_decode"])
+def test_kv_append_decode_bench_size(name):
+    """The decode steps the benchmark times, at their exact size and launch
+    configuration: 256 sequences of one new token, 32 query and 8 key heads of
+    128, f16, caches of (256, 8, 4096, 128) (2 GiB each), lengths U[1, 4096],
+    a (32768, 64) table. For one new token the cache append is RoPE (after
+    QK-norm for the norm variant) at position L[b] - 1, stored in that cache
+    row (the oracle pins tie the append to this); q_out and every written row
+    are compared with the oracle, and every other cache element must still
+    hold its fill value (checked on the device, the caches stay there)."""
+    w = get(name)
+    norm = name.startswith("qk_norm")
+    B, H, Hk, D, Smax = w.batch, w.num_heads, w.kv_num_heads, w.head_size, w.extra["cache_seq"]
+    q, k, v, lens = w.make_x(), w.make_k(), w.make_v(), w.make_lengths()
+    total = int(lens.max())
+    inv = oracle.inv_freq(w.cache_base, D)
+    cos, sin = oracle.cos_sin_cache(np.float16, w.cache_rows, inv)
+    pos = (lens.astype(np.int64) - 1).reshape(B, 1)
+    fill_k, fill_v = 0x3c00, 0xbc00  # 1.0 and -1.0
+    gk = torch.full((B, Hk, Smax, D), 1.0, dtype=torch.float16, device=DEV)
+    gv = torch.full((B, Hk, Smax, D), -1.0, dtype=torch.float16, device=DEV)
+    print("bench-size cache append", name, flush=True)
+    if norm:
+        wq, wk = w.make_norm_weights()
+        eq, ek = oracle.rope_apply_qk_norm(q, k, wq, wk, 1e-6, cos, sin, pos, num_heads=H, kv_num_heads=Hk)
+        gq = rpe.rope_kv_append_qk_norm(cuda(q), cuda(k), cuda(v), gk, gv, cuda(lens), total, cuda(cos),
+                                        cuda(sin), cuda(wq), cuda(wk), epsilon=1e-6, num_heads=H,
+                                        kv_num_heads=Hk)
+    else:
+        eq, ek = oracle.rope_apply_qk(q, k, cos, sin, pos, num_heads=H, kv_num_heads=Hk)
+        gq = rpe.rope_kv_append(cuda(q), cuda(k), cuda(v), gk, gv, cuda(lens), total, cuda(cos), cuda(sin),
+                                num_heads=H, kv_num_heads=Hk)
+    torch.cuda.synchronize()
+    bidx = torch.arange(B, device=DEV)
+    rows = torch.from_numpy(pos[:, 0]).to(DEV)
+    got_k = host(gk[bidx, :, rows, :].contiguous()).reshape(B, 1, Hk * D)
+    got_v = host(gv[bidx, :, rows, :].contiguous()).reshape(B, 1, Hk * D)
+    if norm:
+        zq = np.broadcast_to(zmax(q, wq, 1e-6, H).max(-1, keepdims=True), (B, 1, H, D)).reshape(B, 1, H * D)
+        zk = np.broadcast_to(zmax(k, wk, 1e-6, Hk).max(-1, keepdims=True), (B, 1, Hk, D)).reshape(B, 1, Hk * D)
+        r = assert_parity_norm(host(gq), eq, zq, "q_out")
+        assert_parity_norm(got_k, ek, zk, "written key rows")
+    else:
+        r = assert_parity(host(gq), eq, "q_out")
+        assert_parity(got_k, ek, "written key rows")
+    assert_bitwise(got_v, v, "written value rows")
+    # put the fill value back into the written rows: then nothing may differ
+    gk[bidx, :, rows, :] = 1.0
+    gv[bidx, :, rows, :] = -1.0
+    assert bool((gk.view(torch.int16) == fill_k).all()), "a key-cache row outside L[b] - 1 was written"
+    assert bool((gv.view(torch.int16) == fill_v - 0x10000).all()), "a value-cache row outside L[b] - 1 was written"
+    print(name, "bench size", r, flush=True)
