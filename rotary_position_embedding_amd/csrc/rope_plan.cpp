@@ -217,10 +217,10 @@ static bool choose_row_geometry(Plan* pl) {
     // tokens, 32 + 8 heads of 128), one instruction per wave against the
     // earlier rule of ~1024 waves: packed [Q|K|V] 3.33 vs 3.75 us, cache
     // append 3.61 vs 4.05, QK-norm on the fly 4.19 vs 4.45, QK-norm + cache
-    // append 4.10 vs 4.93; Q+K with a table 3.31 vs 3.29. Plain on-the-fly
-    // launches keep ~1024 (each wave computes the token's slots once: 3.64
-    // us with two instructions per wave, 3.77 with one).
-    const int64_t target_waves = p.coef == kCoefOnTheFly && !p.norm ? 1024 : 4096;
+    // append 4.10 vs 4.93; Q+K with a table 3.31 vs 3.29; Q+K on the fly
+    // (each wave computes its token's slots) 3.35 vs 3.47 with two
+    // instructions per wave.
+    const int64_t target_waves = 4096;
     int loads = kRowLoads;
     for (;;) {
         int64_t waves = 0;
