@@ -117,6 +117,22 @@ template <> __device__ inline bf16_t from_f<bf16_t>(float v) {
 }
 template <typename T> __device__ inline float round_to(float v) { return to_f(from_f<T>(v)); }
 
+// One output of a pair's rotation, a*b + c*d (the caller folds the sign into
+// d), as the binary32 value that is then converted to T.
+//   binary16 / bfloat16 storage: c*d is exact in binary32 (11 + 11 or 8 + 8
+//   significant bits), so one fma rounds the exact sum once to binary32.
+//   binary32 storage: c*d is not exact in binary32, and rounding it before
+//   the fma would make the error relative to the products rather than to the
+//   result when they cancel. Both products are exact in binary64 (24 + 24
+//   bits, exponents far inside its range), so the sum is formed there with
+//   one rounding and then rounded to binary32: the value the definition
+//   gives when evaluated in binary64, overflow included.
+template <typename T>
+__device__ inline float rot_out(float a, float b, float c, float d) {
+    if (sizeof(T) == 4) return (float)fma((double)a, (double)b, (double)c * (double)d);
+    return fmaf(a, b, c * d);
+}
+
 // Element e of a 16-byte chunk, as float. The whole chunk is reinterpreted
 // as a vector of T and then indexed (a bit_cast applied to a single vector
 // element is miscompiled to element 0 by this toolchain, so it is avoided).
@@ -769,8 +785,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         const float x1 = to_f(xv[2 * j]);
                         const float x2 = to_f(xv[2 * j + 1]);
                         const float c = to_f(cf[m][j]), s = to_f(sf[m][j]);
-                        r[2 * j] = fmaf(x1, c, -(x2 * s));
-                        r[2 * j + 1] = fmaf(x2, c, x1 * s);
+                        r[2 * j] = rot_out<T>(x1, c, x2, -s);
+                        r[2 * j + 1] = rot_out<T>(x2, c, x1, s);
                     }
                     u32x4 o = chunk_pack<T>(r);
                     if ((COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy) && kany)
@@ -785,8 +801,8 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                         const float x1 = to_f(xv1[j]);
                         const float x2 = to_f(xv2[j]);
                         const float c = to_f(cf[m][j]), s = to_f(sf[m][j]);
-                        r1[j] = fmaf(x1, c, -(x2 * s));
-                        r2[j] = fmaf(x2, c, x1 * s);
+                        r1[j] = rot_out<T>(x1, c, x2, -s);
+                        r2[j] = rot_out<T>(x2, c, x1, s);
                     }
                     u32x4 o1 = chunk_pack<T>(r1);
                     u32x4 o2 = chunk_pack<T>(r2);
@@ -1097,12 +1113,12 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
 #pragma unroll
                 for (int j = 0; j < CE; ++j) {
                     const float x1 = to_f(xv[2 * j]), x2 = to_f(xv[2 * j + 1]);
-                    y[2 * j] = fmaf(x1, cf[j], -(x2 * sf[j]));
-                    y[2 * j + 1] = fmaf(x2, cf[j], x1 * sf[j]);
+                    y[2 * j] = rot_out<T>(x1, cf[j], x2, -sf[j]);
+                    y[2 * j + 1] = rot_out<T>(x2, cf[j], x1, sf[j]);
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < E; ++e) y[e] = fmaf(to_f(xv[e]), cf[e], to_f(pvv[e]) * sf[e]);
+                for (int e = 0; e < E; ++e) y[e] = rot_out<T>(to_f(xv[e]), cf[e], to_f(pvv[e]), sf[e]);
             }
             o = chunk_pack<T>(y);
             if (COEF == kCoefMrope) o = select_bits(keep, in[u], o);
@@ -1155,8 +1171,8 @@ __global__ __launch_bounds__(kBlock) void rope_scalar_kernel(const KArgs a, int6
         }
         const float x1 = to_f(__builtin_bit_cast(T, xb[j1]));
         const float x2 = to_f(__builtin_bit_cast(T, xb[j2]));
-        yb[j1] = __builtin_bit_cast(B, from_f<T>(fmaf(x1, c, -(x2 * sn))));
-        yb[j2] = __builtin_bit_cast(B, from_f<T>(fmaf(x2, c, x1 * sn)));
+        yb[j1] = __builtin_bit_cast(B, from_f<T>(rot_out<T>(x1, c, x2, -sn)));
+        yb[j2] = __builtin_bit_cast(B, from_f<T>(rot_out<T>(x2, c, x1, sn)));
     }
 }
 

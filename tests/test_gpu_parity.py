@@ -7,7 +7,7 @@ import torch
 import oracle
 import rotary_position_embedding_amd as rpe
 from oracle_pins import angle_table, ids_in, pair_index
-from parity import assert_bitwise, assert_parity, assert_parity_binary32_range, bits, compare
+from parity import assert_bitwise, assert_parity, bits, compare
 from gpu_io import DEV, cuda, host, one, torch_dtype, POLICIES, POLICY_IDS
 from rope_inputs import BFLOAT16, EXTRA_WORKLOADS, WORKLOADS, normal_tensor, with_dtype, with_layout
 
@@ -623,19 +623,13 @@ def test_special_values(dt, il, policy):
     want = oracle.rope_apply(x, cos, sin, ids, interleaved=il, num_heads=H)
     got = host(rpe.rope_apply(cuda(x), cuda(cos), cuda(sin), cuda(ids), interleaved=il, num_heads=H))
     what = "special values dt=%s il=%d" % (np.dtype(dt).name, il)
+    r = assert_parity(got, want, what)
     if np.dtype(dt) == np.float32:
-        # magnitudes of each element's two products, for the binary32-range bound
-        xr = x.reshape(B, S, H, D).astype(np.float64)
-        j1, j2 = pair_index(il, D // 2)
-        c64 = cos[ids][:, :, None, :].astype(np.float64)
-        s64 = sin[ids][:, :, None, :].astype(np.float64)
-        with np.errstate(invalid="ignore"):
-            mag = np.zeros_like(xr)
-            mag[..., j1] = np.abs(xr[..., j1] * c64) + np.abs(xr[..., j2] * s64)
-            mag[..., j2] = np.abs(xr[..., j2] * c64) + np.abs(xr[..., j1] * s64)
-        r = assert_parity_binary32_range(got, want, mag.reshape(B, S, H * D), what)
-    else:
-        r = assert_parity(got, want, what)
+        # binary32: both products exact in binary64 and one rounding there, as
+        # in the oracle, so every non-NaN result (overflow to inf included)
+        # has the oracle's bits
+        keep = ~np.isnan(want)
+        assert_bitwise(got[keep], want[keep], what + " (bits)")
     log("special values %s il=%d policy=%d %s" % (np.dtype(dt).name, il, policy, r))
 
 
