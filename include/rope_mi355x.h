@@ -263,7 +263,8 @@ int rope_apply_qk_norm(const rope_tensor* q, const rope_tensor* k,
  * q_out:        (B, S, H*D), type T; may be `query` itself when it is not
  *               packed (in place). The caches may not overlap any input,
  *               q_out or each other.
- * rotary_interleaved: 0 half-split pairs, 1 adjacent pairs.
+ * rotary_interleaved: 1 adjacent pairs; any other value the half-split
+ *               (NeoX) pairs, as the README's Attributes table says.
  * num_heads, kv_num_heads: >= 1, num_heads <= 2^31 - 1, kv_num_heads divides num_heads.
  * Device data outside the README's bounds (a per-sequence length above
  * total_sequence_length or below S): a row outside [0, Smax) is not written

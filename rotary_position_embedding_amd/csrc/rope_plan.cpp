@@ -997,8 +997,9 @@ int plan_rope_kv_append(const rope_tensor* query, const rope_tensor* key,
         return fail(ROPE_ERR_DTYPE, "key, value, caches, tables and q_out must have the type of query");
     if (key_total_sequence_lengths->dtype != ROPE_INT32)
         return fail(ROPE_ERR_DTYPE, "key_total_sequence_lengths must be int32");
-    if (interleaved != 0 && interleaved != 1)
-        return fail(ROPE_ERR_ATTRIBUTE, "rotary_interleaved must be 0 or 1");
+    // SparseAttention README, Attributes: 1 rotates adjacent pairs and every
+    // other value selects the NeoX half-split
+    interleaved = interleaved == 1 ? 1 : 0;
     if (num_heads < 1 || kv_num_heads < 1)
         return fail(ROPE_ERR_ATTRIBUTE, "num_heads and kv_num_heads are required (>= 1)");
     TRY(check_head_count(num_heads));

@@ -630,6 +630,19 @@ def test_kv_append_accepted():
     assert rc == OK
 
 
+def test_kv_append_rotary_interleaved_any_value():
+    """SparseAttention README, Attributes: rotary_interleaved 1 rotates
+    adjacent pairs and every other value selects the NeoX half-split, so
+    2, -1 and large values are accepted (unlike RotaryEmbedding's
+    interleaved, which its manifest restricts to 0 and 1)."""
+    lib = _lib.load()
+    for value in (0, 1, 2, -1, 7, 2 ** 40):
+        rc, v = check_kv(kv_case(rotary_interleaved=value))
+        assert rc == OK and v == "row16/append", (value, rc, lib.rope_last_error())
+        rc, v = check_kv_norm(kv_norm_case(rotary_interleaved=value))
+        assert rc == OK, (value, rc, lib.rope_last_error())
+
+
 def test_kv_append_clauses():
     lib = _lib.load()
     base = kv_case()
@@ -642,7 +655,6 @@ def test_kv_append_clauses():
         ("lengths int64", DTYPE, dict(key_total_sequence_lengths=reshape(base["key_total_sequence_lengths"], (2,), I64))),
         ("cache float32", DTYPE, dict(past_key=reshape(base["past_key"], (2, 2, 40, 16), F32))),
         ("query int64", DTYPE, dict(query=reshape(base["query"], (2, 3, 128), I64))),
-        ("interleaved 2", ATTR, dict(rotary_interleaved=2)),
         ("no heads", ATTR, dict(num_heads=0)),
         ("kv does not divide", SHAPE, dict(kv_num_heads=3)),
         ("query rank 4", RANK, dict(query=reshape(base["query"], (2, 3, 8, 16)))),

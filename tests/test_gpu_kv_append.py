@@ -41,7 +41,10 @@ def check_guards(buf, what):
     assert (whole[:GUARD] == 0x7e11).all() and (whole[-GUARD:] == 0x7e11).all(), what + ": guard overwritten"
 
 
-def run_case(dt, B, S, H, Hk, D, width, Smax, M, lens, total, il=0, packed=False, inplace=False, seed=0):
+def run_case(dt, B, S, H, Hk, D, width, Smax, M, lens, total, il=0, packed=False, inplace=False, seed=0,
+             gpu_il=None):
+    """gpu_il: the rotary_interleaved value passed to the library, when it
+    differs from the pairing `il` the oracle is asked for."""
     if packed:
         query = normal_tensor(12000 + seed, (B, S, (H + 2 * Hk) * D), dt)
         key = value = None
@@ -61,9 +64,11 @@ def run_case(dt, B, S, H, Hk, D, width, Smax, M, lens, total, il=0, packed=False
     out = q_t if inplace else None
     got_q = rpe.rope_kv_append(q_t, None if packed else cuda(key), None if packed else cuda(value), gk, gv,
                                cuda(lens), total, cuda(cos), cuda(sin), num_heads=H, kv_num_heads=Hk,
-                               rotary_interleaved=il, out=out)
+                               rotary_interleaved=il if gpu_il is None else gpu_il, out=out)
     what = "dt=%s B=%d S=%d H=%d Hk=%d D=%d w=%d lens=%s total=%d il=%d packed=%s" % (
         np.dtype(dt).name, B, S, H, Hk, D, width, lens.tolist()[:4], total, il, packed)
+    if gpu_il is not None:
+        what += " rotary_interleaved=%d" % gpu_il
     assert_parity(host(got_q), wq, "q_out " + what)
     assert_parity(host(gk), wk, "present_key " + what)
     assert_bitwise(host(gv), wv, "present_value " + what)
@@ -111,6 +116,17 @@ def test_kv_append_sweep(case, policy, inplace):
         total = int(lens.max())
     print(run_case(dt, B, S, H, Hk, D, width, Smax, M, lens, total, il, packed, inplace, seed=B + S + D),
           flush=True)
+
+
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
+@pytest.mark.parametrize("value", [2, -1])
+def test_kv_append_rotary_interleaved_other_values(value, policy):
+    """SparseAttention README, Attributes: every rotary_interleaved value
+    other than 1 selects the NeoX half-split, so 2 and -1 give the oracle's
+    half-split result."""
+    rpe.set_kernel_policy(policy)
+    print(run_case(np.float16, 4, 3, 8, 2, 128, 64, 40, 50, (3, 9, 33, 40), 40, il=0, seed=91,
+                   gpu_il=value), flush=True)
 
 
 @pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
