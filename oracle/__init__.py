@@ -19,7 +19,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle_rope.so")
+# ROPE_ORACLE_LIBRARY selects another build of the same C file (the
+# sanitizer build of the CPU tests); by default the in-tree one
+LIB_PATH = os.path.abspath(os.environ.get("ROPE_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle_rope.so"))
 SOURCE_PATH = os.path.join(_HERE, "rope_oracle.c")
 
 F32 = 1
@@ -66,6 +68,11 @@ class Oracle:
     def __init__(self, lib_path=LIB_PATH):
         if not os.path.exists(lib_path):
             raise RuntimeError("oracle library not built: %s (run __graft_entry__.build())" % lib_path)
+        if os.path.abspath(lib_path) == LIB_PATH:
+            from . import build as _build
+            if not _build.is_current(lib_path):
+                raise RuntimeError("oracle library %s was built from other sources "
+                                   "(run __graft_entry__.build())" % lib_path)
         lib = ctypes.CDLL(lib_path)
         i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
         sig = {

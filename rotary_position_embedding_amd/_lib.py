@@ -1,13 +1,18 @@
 """ctypes view of librope_mi355x.so (declared in include/rope_mi355x.h).
 
-Loading fails loudly if the library has not been built: there is no other
-implementation behind these names.
+Loading fails loudly if the library has not been built, or was built from
+other sources than the ones beside it: there is no other implementation
+behind these names.
 """
 import ctypes
 import os
 
+from . import build as _build
+
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "librope_mi355x.so")
+# ROPE_MI355X_LIBRARY selects another build of the same sources (the
+# sanitizer build of the CPU tests); by default the in-tree library
+LIB_PATH = os.path.abspath(os.environ.get("ROPE_MI355X_LIBRARY") or os.path.join(HERE, "librope_mi355x.so"))
 
 ROPE_FLOAT = 1
 ROPE_INT32 = 6
@@ -68,6 +73,11 @@ def load():
         raise ImportError(
             "librope_mi355x.so is not built (%s); run __graft_entry__.build() -- "
             "there is no fallback implementation" % LIB_PATH)
+    if not _build.is_current(LIB_PATH):
+        raise ImportError(
+            "%s was built from other sources (recorded %s, sources now %s); "
+            "rebuild it with __graft_entry__.build()" % (LIB_PATH, _build.built_hash(LIB_PATH),
+                                                         _build.source_hash()))
     lib = ctypes.CDLL(LIB_PATH)
     for name, (args, res) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -17,10 +17,13 @@ def pytest_configure(config):
 
 
 def _ensure_built():
-    """Build only what is missing; a built tree is used as is."""
-    from oracle import LIB_PATH as ORACLE_LIB
-    product_lib = os.path.join(ROOT, "rotary_position_embedding_amd", "librope_mi355x.so")
-    if not os.path.exists(ORACLE_LIB) or not os.path.exists(product_lib):
+    """Build the oracle and the product library when either is missing or
+    was built from other sources than the ones in the tree (each build
+    records a hash of its sources beside the library); a current build is
+    used as is."""
+    from oracle import build as oracle_build
+    from rotary_position_embedding_amd import build as product_build
+    if not oracle_build.is_current() or not product_build.is_current():
         import __graft_entry__ as ge
         ge.build()
 

@@ -42,6 +42,55 @@ def test_library_exports_every_declared_function():
         assert name in _lib.SIGNATURES, "binding lacks %s" % name
 
 
+def test_library_matches_its_sources():
+    """The build records a hash of its sources beside the library; the tree
+    under test is the build of the sources in it."""
+    from rotary_position_embedding_amd import build
+    assert build.is_current(), (build.built_hash(), build.source_hash())
+    assert len(build.built_hash()) == 64
+
+
+def test_stale_library_is_refused(monkeypatch):
+    """A library whose recorded source hash differs from the sources is not
+    loaded: the loader raises instead of running an older build."""
+    from rotary_position_embedding_amd import build
+    monkeypatch.setattr(build, "source_hash", lambda: "0" * 64)   # the sources moved on
+    assert not build.is_current() and not build.is_current(_lib.LIB_PATH)
+    monkeypatch.setattr(_lib, "_lib", None)       # as in a fresh process
+    with pytest.raises(ImportError, match="other sources"):
+        _lib.load()
+
+
+def test_library_without_record_is_refused(tmp_path, monkeypatch):
+    """A copy of the library with no recorded source hash beside it."""
+    import shutil
+    copy = tmp_path / "librope_mi355x.so"
+    shutil.copyfile(_lib.LIB_PATH, copy)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(copy))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError, match="other sources"):
+        _lib.load()
+
+
+def test_source_edit_changes_the_hash(tmp_path, monkeypatch):
+    """Any edit to a source file changes the hash, so the recorded one no
+    longer matches and the suite's set-up rebuilds."""
+    from rotary_position_embedding_amd import build
+    extra = tmp_path / "extra.hpp"
+    extra.write_text("// a\n")
+    files = build.source_files() + [str(extra)]
+    monkeypatch.setattr(build, "source_files", lambda: files)
+    h1 = build.source_hash()
+    extra.write_text("// b\n")
+    assert build.source_hash() != h1
+    assert not build.is_current()
+
+
+def test_oracle_library_matches_its_sources():
+    from oracle import build as oracle_build
+    assert oracle_build.is_current()
+
+
 def test_status_strings():
     lib = _lib.load()
     for code, name in _lib.STATUS.items():
