@@ -13,6 +13,11 @@ Decode-sized workloads (a few MB per step) are bound by the host's per-call
 cost when launched one by one; for them the rates come from the same launches
 captured in one HIP graph and replayed (the eager time is reported too).
 
+Timing: the K launches run in batches (10 by default) with a pair of HIP
+events on the launch stream around each batch; ms_per_step is the median of
+the batches' per-launch times, and the line also gives the batches' minimum,
+maximum and the mean over all K launches.
+
 Prints ONE JSON line on stdout. Also reported (in "also"): the M-RoPE
 prefill in both section layouts, the fp32 partial interleaved case, the fp16
 decode Q+K step (table and on the fly), the prefill and M-RoPE stored in
@@ -22,7 +27,6 @@ fly), the QK-norm decode step with the cache append, and an M-RoPE decode
 step.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -39,12 +43,8 @@ PEAK_GBS = 8000.0            # MI355X HBM3E, published
 ROTATE_BYTES = 1 << 30       # >= 4x the 256 MB last-level cache
 HEADLINE = "c2_rope_f16_prefill"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_c2_rope_f16_prefill.json")
-# the kernel source files (device code and its per-type instantiations)
-KERNEL_SOURCES = [os.path.join(ROOT, "rotary_position_embedding_amd", "csrc", f)
-                  for f in ("rope_device.hpp", "rope_kernels.hip", "rope_kernels_f32.hip",
-                            "rope_kernels_f16.hip", "rope_kernels_bf16.hip", "rope_kernels_f32_row.hip",
-                            "rope_kernels_f16_row.hip", "rope_kernels_bf16_row.hip",
-                            "rope_plan.hpp", "rope_plan.cpp")]  # the planner sets the launch geometry
+BATCHES = 10                 # event-timed batches per measurement (median reported)
+CPU_THREADS_MAX = 16         # host cores one GPU's share of the machine offers
 
 
 # kernel variant prefix (as the *_check functions report it) -> kernel function
@@ -56,11 +56,10 @@ def log(*a):
 
 
 def kernel_source_sha():
-    h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+    """SHA-256 of every source the library is built from (the hash its build
+    records beside it)."""
+    from rotary_position_embedding_amd import build
+    return build.source_hash()
 
 
 # ---------------------------------------------------------------------------
@@ -178,32 +177,51 @@ def setup_kv_append(w, q0, dt, dev):
     return launchers, nsets * set_bytes
 
 
+def _batches(steps):
+    """Split K launches into at most BATCHES nearly equal batches."""
+    nb = max(1, min(BATCHES, steps))
+    return [steps // nb + (1 if i < steps % nb else 0) for i in range(nb)]
+
+
+def _summary(per_launch, counts):
+    """ms per launch: the median over batches, their spread and the mean over
+    all launches."""
+    total = sum(ms * n for ms, n in zip(per_launch, counts))
+    return {"median": float(np.median(per_launch)), "min": float(min(per_launch)),
+            "max": float(max(per_launch)), "mean": total / sum(counts), "batches": len(counts)}
+
+
 def time_steps(launchers, steps, warmup):
-    """Mean ms per launch over K back-to-back launches between two HIP events
-    on the launch stream, synchronised on both sides. Each step is one kernel,
-    so this is also the kernel's average launch duration (it agrees with the
-    rocprofv3 kernel trace; event pairs around every launch would add their
-    own overhead)."""
+    """K back-to-back launches in batches, a pair of HIP events around each
+    batch on the launch stream (the current stream, which the launchers were
+    bound to), synchronised on both sides of the K launches. Each step is
+    one kernel, so a batch's time over its launch count is the kernel's
+    average launch duration in that batch."""
     import torch
     n = len(launchers)
     for i in range(warmup):
         launchers[i % n]()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        launchers[i % n]()
-    t1.record()
+    counts = _batches(steps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in counts]
+    k = 0
+    for (e0, e1), c in zip(evs, counts):
+        e0.record()
+        for _ in range(c):
+            launchers[k % n]()
+            k += 1
+        e1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    return _summary([e0.elapsed_time(e1) / c for (e0, e1), c in zip(evs, counts)], counts)
 
 
 def time_steps_graph(launchers, steps, warmup):
-    """Mean ms per launch with the K launches captured in one HIP graph and
-    replayed: what the GPU takes per step once the host's per-call cost is
-    out of the way (decode steps are that small). The launchers were bound
-    to the capture stream when they were made."""
+    """The K launches captured in one HIP graph (rotating over the input
+    sets as the eager launches do) and the graph replayed once per batch,
+    each replay between a pair of events: what the GPU takes per step once
+    the host's per-call cost is out of the way (decode steps are that
+    small). The launchers were bound to the capture stream when they were
+    made."""
     import torch
     n = len(launchers)
     for i in range(warmup):
@@ -213,15 +231,16 @@ def time_steps_graph(launchers, steps, warmup):
     with torch.cuda.graph(g, stream=torch.cuda.current_stream()):
         for i in range(steps):
             launchers[i % n]()
-    g.replay()                       # first replay uploads the graph
+    g.replay()                       # the first replay uploads the graph
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    g.replay()
-    t1.record()
+    nb = max(5, min(BATCHES, 10))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nb)]
+    for e0, e1 in evs:
+        e0.record()
+        g.replay()
+        e1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps
+    return _summary([e0.elapsed_time(e1) / steps for e0, e1 in evs], [steps] * nb)
 
 
 def copy_reference(nbytes, steps, warmup):
@@ -236,7 +255,7 @@ def copy_reference(nbytes, steps, warmup):
         a = torch.empty(n, dtype=torch.float16, device="cuda:0").normal_()
         pairs.append((a, torch.empty_like(a)))
     launchers = [lambda a=a, b=b: b.copy_(a) for a, b in pairs]
-    ms = time_steps(launchers, steps, warmup)
+    ms = time_steps(launchers, steps, warmup)["median"]
     del pairs, launchers
     torch.cuda.empty_cache()
     return 2 * nbytes / (ms * 1e-3) / 1e9, ms
@@ -249,16 +268,21 @@ def measure(w, steps, warmup, onthefly=False, graph=False):
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):    # launchers bind the stream they are made on
         launchers, rot = setup(w, onthefly)
-        ms = time_steps(launchers, steps, warmup)
-        ms_graph = time_steps_graph(launchers, steps, warmup) if graph else None
+        eager = time_steps(launchers, steps, warmup)
+        in_graph = time_steps_graph(launchers, steps, warmup) if graph else None
     torch.cuda.synchronize()
     nbytes = w.algorithmic_bytes(onthefly)
-    ms_rate = ms_graph if graph else ms
+    t = in_graph if graph else eager
+    ms_rate = t["median"]
     gbs = nbytes / (ms_rate * 1e-3) / 1e9
     r = {
         "workload": w.name + ("_onthefly" if onthefly else ""),
         "bytes_per_step": nbytes,
         "ms_per_step": ms_rate,
+        "ms_per_step_min": t["min"],
+        "ms_per_step_max": t["max"],
+        "ms_per_step_mean": t["mean"],
+        "batches": t["batches"],
         "gbs": gbs,
         "frac_of_peak": gbs / PEAK_GBS,
         "tokens_heads_per_s": w.tokens_heads() / (ms_rate * 1e-3),
@@ -266,7 +290,7 @@ def measure(w, steps, warmup, onthefly=False, graph=False):
         "kernel_variant": launchers[0].variant,
     }
     if graph:
-        r["ms_per_step_eager"] = ms
+        r["ms_per_step_eager"] = eager["median"]
         r["rates_from"] = "hip_graph"
     return r
 
@@ -274,25 +298,78 @@ def measure(w, steps, warmup, onthefly=False, graph=False):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on the host cores of this machine
 
-def cpu_baseline(w, budget_s=10.0):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, reps=5):
+    """The oracle as it stands on the whole workload input: single-threaded,
+    and on all the host cores this GPU's share allows (up to 16) by running
+    the unmodified oracle on token slices in a thread pool (its C calls
+    release the interpreter lock; every slice is an independent
+    RotaryEmbedding call, so the result is the same, which is checked).
+    Median of `reps` runs each."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     x = w.make_x()
     ids = w.make_ids()
     cos, sin = oracle.table_for(w)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.rope_apply(x, cos, sin, ids, interleaved=w.interleaved,
-                          num_heads=w.num_heads if w.rank == 3 else 0,
-                          rotary_embedding_dim=w.rotary_embedding_dim)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    nbytes = w.algorithmic_bytes() * reps
-    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "the whole %s input (%d tokens x %d heads), %d repetitions, %.1f s, "
-                      "single-threaded scalar C oracle (binary64)" % (w.name, w.tokens, w.heads, reps, el)}
+    nh = w.num_heads if w.rank == 3 else 0
+    kw = dict(interleaved=w.interleaved, num_heads=nh, rotary_embedding_dim=w.rotary_embedding_dim)
+
+    def whole():
+        return oracle.rope_apply(x, cos, sin, ids, **kw)
+
+    # token slices: rank 3 (B, S, H*D) with ids (B, S) -> x[b, s0:s1], ids[b, s0:s1]
+    if w.rank != 3 or ids is None:
+        raise ValueError("the CPU baseline slices rank-3 inputs with position ids")
+    B, S = ids.shape
+    step = 128
+    slices = [(b, s0, min(S, s0 + step)) for b in range(B) for s0 in range(0, S, step)]
+
+    def one(sl):
+        b, s0, s1 = sl
+        return oracle.rope_apply(x[b:b + 1, s0:s1], cos, sin, ids[b:b + 1, s0:s1], **kw)
+
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    threads = max(1, min(CPU_THREADS_MAX, avail))
+    nbytes = w.algorithmic_bytes()
+    t_single = []
+    ref = None
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        ref = whole()
+        t_single.append(time.perf_counter() - t0)
+    t_par = []
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            parts = list(pool.map(one, slices))
+            t_par.append(time.perf_counter() - t0)
+    got = np.concatenate([np.concatenate([p for sl, p in zip(slices, parts) if sl[0] == b], axis=1)
+                          for b in range(B)], axis=0)
+    if not np.array_equal(got.view(np.uint8), ref.view(np.uint8)):
+        raise AssertionError("oracle on token slices differs from the whole-input oracle")
+    single = nbytes / float(np.median(t_single)) / 1e9
+    par = nbytes / float(np.median(t_par)) / 1e9
+    return {"value": round(par, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole %s input (%d tokens x %d heads, %d algorithmic bytes), median of %d runs; "
+                      "scalar C oracle in binary64 on %d token slices of %d in a pool of %d threads"
+                      % (w.name, w.tokens, w.heads, nbytes, reps, len(slices), step, threads),
+            "single_thread": {"value": round(single, 4), "unit": "GB/s", "cores": 1,
+                              "median_s": round(float(np.median(t_single)), 3)},
+            "all_cores_median_s": round(float(np.median(t_par)), 3),
+            "host": {"nproc": os.cpu_count(), "affinity_cpus": avail, "cpu_model": cpu_model()}}
 
 
 def traffic_for_headline():
@@ -322,6 +399,8 @@ def main():
                     help="time the workload stored in this type instead of its own")
     ap.add_argument("--interleaved", type=int, choices=[0, 1], default=None,
                     help="time the workload with this pairing instead of its own")
+    ap.add_argument("--mrope-layout", type=int, choices=[0, 1], default=None,
+                    help="time an M-RoPE workload with this mrope_layout instead of its own")
     ap.add_argument("--rotary-dim", type=int, default=None,
                     help="time the workload with this rotary_embedding_dim instead of its own")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
@@ -338,6 +417,10 @@ def main():
               "build runs on a single MI355X; --gpus %d is not supported" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+
+    # the library must be the build of the sources in this tree
+    from rotary_position_embedding_amd import build as product_build
+    product_build.ensure_current()
 
     import torch
     import rope_inputs
@@ -371,6 +454,8 @@ def main():
     if args.dtype:
         dt = {"bf16": rope_inputs.BFLOAT16, "f32": np.float32, "f16": np.float16}[args.dtype]
         w = rope_inputs.with_dtype(w, dt, args.dtype)
+    if args.mrope_layout is not None:
+        w = rope_inputs.with_layout(w, args.mrope_layout)
     if args.interleaved is not None or args.rotary_dim is not None:
         from dataclasses import replace
         w = replace(w, interleaved=w.interleaved if args.interleaved is None else args.interleaved,
@@ -378,8 +463,9 @@ def main():
                     name="%s_il%s_r%s" % (w.name, args.interleaved, args.rotary_dim))
     log("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
     head = measure(w, args.steps, args.warmup, args.onthefly, graph=w.tokens <= 4096)
-    log("  %.2f us/step, %.1f GB/s (%.1f%% of %g)" % (
-        head["ms_per_step"] * 1e3, head["gbs"], 100 * head["frac_of_peak"], PEAK_GBS))
+    log("  %.2f us/step (median of %d batches; %.2f-%.2f), %.1f GB/s (%.1f%% of %g)" % (
+        head["ms_per_step"] * 1e3, head["batches"], head["ms_per_step_min"] * 1e3,
+        head["ms_per_step_max"] * 1e3, head["gbs"], 100 * head["frac_of_peak"], PEAK_GBS))
 
     also = []
     if not only:
@@ -410,10 +496,11 @@ def main():
             also.append({k: (round(v, 6) if isinstance(v, float) else v) for k, v in r.items()})
 
     cpu = None
-    if not args.no_cpu_baseline and w.op == "rope":
+    if not args.no_cpu_baseline and w.op == "rope" and w.rank == 3 and w.has_ids:
         log("cpu baseline (oracle) on %s" % w.name)
         cpu = cpu_baseline(w)
-        log("  %.3f GB/s" % cpu["value"])
+        log("  %.3f GB/s on %d threads, %.3f GB/s single-threaded" % (
+            cpu["value"], cpu["cores"], cpu["single_thread"]["value"]))
 
     traffic = traffic_for_headline() if w.name == HEADLINE else None
     copy_ref = None
@@ -459,10 +546,19 @@ def main():
             "traffic": traffic,
             "kernel": "%s, variant %s" % (KERNEL_FUNCTIONS.get(head["kernel_variant"].split("/")[0], "?"),
                                           head["kernel_variant"]),
-            "kernel_us_mean": round(head["ms_per_step"] * 1e3, 3),
             "algorithmic_bytes_per_launch": head["bytes_per_step"],
+            # HIP events on the launch stream: the median over batches of the
+            # batch time per launch (one kernel per launch), and the spread
+            "event_us_per_launch": round(head["ms_per_step"] * 1e3, 3),
+            "event_us_batches": {"min": round(head["ms_per_step_min"] * 1e3, 3),
+                                 "max": round(head["ms_per_step_max"] * 1e3, 3),
+                                 "mean_all_launches": round(head["ms_per_step_mean"] * 1e3, 3),
+                                 "batches": head["batches"]},
+            "frac_range": [round(head["bytes_per_step"] / (head["ms_per_step_max"] * 1e-3) / 1e9 / PEAK_GBS, 4),
+                           round(head["bytes_per_step"] / (head["ms_per_step_min"] * 1e-3) / 1e9 / PEAK_GBS, 4)],
         },
         "cpu_baseline": cpu,
+        "source_sha256": kernel_source_sha(),
         "copy_reference": copy_ref,
         "also": also,
     }
