@@ -9,7 +9,7 @@ import rotary_position_embedding_amd as rpe
 from oracle_pins import angle_table, ids_in, pair_index
 from parity import assert_bitwise, assert_parity, bits, compare
 from gpu_io import DEV, cuda, host, one, torch_dtype, POLICIES, POLICY_IDS
-from rope_inputs import BFLOAT16, EXTRA_WORKLOADS, WORKLOADS, normal_tensor, with_dtype, with_layout
+from rope_inputs import BFLOAT16, EXTRA_WORKLOADS, WORKLOADS, SplitMix64, normal_tensor, with_dtype, with_layout
 
 pytestmark = pytest.mark.gpu
 
@@ -402,6 +402,45 @@ def test_mrope_sweep(case, policy, layout):
     j1, j2 = pair_index(il, Rf // 2)
     for j in (j1[i], j2[i]):
         assert_bitwise(gd[b, :, s, j], xd[b, :, s, j], "out-of-range pairs")
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
+@pytest.mark.parametrize("case", [(3, np.float16, 48, 1, 28, 128), (3, BFLOAT16, 8, 5, 4, 128),
+                                  (4, np.float16, 2, 33, 3, 64), (3, np.float32, 16, 1, 4, 64)],
+                         ids=["decode_f16", "bf16", "rank4", "decode_f32"])
+def test_mrope_text_and_image_tokens(case, policy, layout):
+    """Tokens whose three stream positions are equal (text) mixed with tokens
+    whose streams differ (image patches), including equal positions outside
+    the table (every pair kept) and a single stream out of range: the
+    kernels' one-row path for equal positions against the oracle."""
+    rank, dt, B, S, H, D = case
+    rpe.set_kernel_policy(policy)
+    M = 211
+    shape = (B, S, H * D) if rank == 3 else (B, H, S, D)
+    x = normal_tensor(6500 + B + S, shape, dt)
+    cos, sin = angle_table(6501 + D, M, D // 2, dt)
+    g = SplitMix64(6502 + B * S)
+    ids = ids_in(6503 + S, (3, B, S), M)
+    text = g.below(B * S, 3).reshape(B, S) != 0            # about 2/3 text tokens
+    ids[1][text] = ids[0][text]
+    ids[2][text] = ids[0][text]
+    flat = ids.reshape(3, -1)
+    flat[:, 0] = -3                                          # equal and below the table
+    flat[:, -1] = M + 7                                      # equal and past the table
+    if flat.shape[1] > 2:
+        flat[1, 1] = 2 ** 40                                 # one stream out of range
+    sec = (16, 24, 24) if D == 128 else (8, 12, 12)
+    want = oracle.mrope_apply(x, ids, cos, sin, sec, layout, num_heads=H)
+    got = host(rpe.mrope_apply(cuda(x), cuda(ids), cuda(cos), cuda(sin), mrope_section=sec,
+                               mrope_layout=layout, num_heads=H))
+    assert_parity(got, want, "%s policy %d layout %d" % (case, policy, layout))
+    xd = x if rank == 4 else x.reshape(B, S, H, D).transpose(0, 2, 1, 3)
+    gd = got if rank == 4 else got.reshape(B, S, H, D).transpose(0, 2, 1, 3)
+    b0, s0 = np.unravel_index(0, (B, S))
+    b1, s1 = np.unravel_index(B * S - 1, (B, S))
+    assert_bitwise(gd[b0, :, s0], xd[b0, :, s0], "equal positions below the table")
+    assert_bitwise(gd[b1, :, s1], xd[b1, :, s1], "equal positions past the table")
 
 
 def test_mrope_equal_streams_equal_rope_on_gpu():
