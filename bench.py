@@ -309,13 +309,14 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(w, reps=5):
+def cpu_baseline(w, min_reps=5, single_s=8.0, pool_s=2.0):
     """The oracle as it stands on the whole workload input: single-threaded,
     and on all the host cores this GPU's share allows (up to 16) by running
     the unmodified oracle on token slices in a thread pool (its C calls
     release the interpreter lock; every slice is an independent
     RotaryEmbedding call, so the result is the same, which is checked).
-    Median of `reps` runs each."""
+    Median of at least `min_reps` runs each, repeated until the leg has run
+    `single_s` / `pool_s` seconds (a bounded sample of about 10 s)."""
     from concurrent.futures import ThreadPoolExecutor
     import oracle
     x = w.make_x()
@@ -346,13 +347,13 @@ def cpu_baseline(w, reps=5):
     nbytes = w.algorithmic_bytes()
     t_single = []
     ref = None
-    for _ in range(reps):
+    while len(t_single) < min_reps or sum(t_single) < single_s:
         t0 = time.perf_counter()
         ref = whole()
         t_single.append(time.perf_counter() - t0)
     t_par = []
     with ThreadPoolExecutor(max_workers=threads) as pool:
-        for _ in range(reps):
+        while len(t_par) < min_reps or sum(t_par) < pool_s:
             t0 = time.perf_counter()
             parts = list(pool.map(one, slices))
             t_par.append(time.perf_counter() - t0)
@@ -363,11 +364,12 @@ def cpu_baseline(w, reps=5):
     single = nbytes / float(np.median(t_single)) / 1e9
     par = nbytes / float(np.median(t_par)) / 1e9
     return {"value": round(par, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "the whole %s input (%d tokens x %d heads, %d algorithmic bytes), median of %d runs; "
-                      "scalar C oracle in binary64 on %d token slices of %d in a pool of %d threads"
-                      % (w.name, w.tokens, w.heads, nbytes, reps, len(slices), step, threads),
+            "sample": "the whole %s input (%d tokens x %d heads, %d algorithmic bytes); scalar C oracle in "
+                      "binary64 on %d token slices of %d in a pool of %d threads, median of %d runs (%.1f s)"
+                      % (w.name, w.tokens, w.heads, nbytes, len(slices), step, threads, len(t_par), sum(t_par)),
             "single_thread": {"value": round(single, 4), "unit": "GB/s", "cores": 1,
-                              "median_s": round(float(np.median(t_single)), 3)},
+                              "median_s": round(float(np.median(t_single)), 3),
+                              "runs": len(t_single), "total_s": round(sum(t_single), 1)},
             "all_cores_median_s": round(float(np.median(t_par)), 3),
             "host": {"nproc": os.cpu_count(), "affinity_cpus": avail, "cpu_model": cpu_model()}}
 
@@ -380,7 +382,7 @@ def traffic_for_headline():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256") != kernel_source_sha():
+    if t.get("source_sha256") != kernel_source_sha():
         return None
     return t.get("traffic_bytes_per_launch")
 
