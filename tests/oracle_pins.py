@@ -487,6 +487,55 @@ def pin_c1_against_real_math(orc):
                 assert abs(float(r2) - float(y[0, h, s, i + 4])) <= 1e-5 * max(1.0, abs(float(r2)))
 
 
+def _rne_f32_of_fraction(q):
+    """The binary32 value nearest to the rational q (ties to the even
+    significand): one rounding, from the exact value."""
+    from fractions import Fraction
+    f = np.float32(float(q))                      # within one binary32 step of the answer
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    return min(cands, key=lambda v: (abs(Fraction(float(v)) - q), int(np.float32(v).view(np.uint32)) & 1))
+
+
+def pin_f32_cancellation_exact(orc):
+    """binary32 data where the two products of a pair nearly cancel
+    (x1 = rnd(x2*s/c) or x1 = rnd(-x2*c/s), magnitudes up to 1e4): every
+    output equals the exact x1*c - x2*s (x2*c + x1*s), formed in rational
+    arithmetic and rounded once to binary32. A product rounded to binary32
+    before the difference misses it in many of these outputs (checked, so
+    the pin is known to see that mistake)."""
+    from fractions import Fraction
+    B, H, S, D = 1, 3, 12, 8
+    half = D // 2
+    cos, sin = angle_table(4243, S, half, np.float32)
+    g = SplitMix64(4244)
+    n = B * H * S * half
+    mag = 10.0 ** (g.uniform(n) * 6.0 - 2.0)
+    x2 = (g.normal(n) * mag).astype(np.float32).astype(np.float64).reshape(B, H, S, half)
+    x1 = (g.normal(n) * mag).reshape(B, H, S, half)
+    kind = g.below(n, 3).reshape(B, H, S, half)
+    c = cos.astype(np.float64)[None, None]
+    sn = sin.astype(np.float64)[None, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        x1 = np.where((kind == 0) & (np.abs(c) > 0.05), x2 * sn / c, x1)
+        x1 = np.where((kind == 1) & (np.abs(sn) > 0.05), -x2 * c / sn, x1)
+    x = np.zeros((B, H, S, D), np.float32)
+    x[..., :half] = x1.astype(np.float32)
+    x[..., half:] = x2.astype(np.float32)
+    y = orc.rope_apply(x, cos.reshape(1, S, half), sin.reshape(1, S, half))
+    misses = 0
+    for h in range(H):
+        for si in range(S):
+            for i in range(half):
+                a1, a2 = Fraction(float(x[0, h, si, i])), Fraction(float(x[0, h, si, i + half]))
+                cc, ss = Fraction(float(cos[si, i])), Fraction(float(sin[si, i]))
+                for j, exact, rounded in ((i, a1 * cc - a2 * ss, float(a1 * cc) - float(np.float32(float(a2 * ss)))),
+                                          (i + half, a2 * cc + a1 * ss, float(a2 * cc) + float(np.float32(float(a1 * ss))))):
+                    want = _rne_f32_of_fraction(exact)
+                    assert bits(np.float32(y[0, h, si, j])) == bits(want), (h, si, j, y[0, h, si, j], want)
+                    misses += np.float32(rounded) != want
+    assert misses >= n // 10, "the inputs do not separate the two arithmetics (%d)" % misses
+
+
 # --------------------------------------------------------------------------
 # M-RoPE
 

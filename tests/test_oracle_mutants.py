@@ -13,6 +13,8 @@ from oracle_pins import ALL_PINS
 MUTANTS = {
     "sign_of_first_output": [("x1 * c[i] - x2 * s[i]", "x1 * c[i] + x2 * s[i]")],
     "dropped_term_second_output": [("x2 * c[i] + x1 * s[i]", "x2 * c[i]")],
+    "f32_second_product_rounded_first": [("x1 * c[i] - x2 * s[i]",
+                                          "x1 * c[i] - (dtype == ORACLE_F32 ? (double)(float)(x2 * s[i]) : x2 * s[i])")],
     "cos_sin_transposed": [("x1 * c[i] - x2 * s[i]", "x1 * s[i] - x2 * c[i]")],
     "operands_swapped_second_output": [("x2 * c[i] + x1 * s[i]", "x1 * c[i] + x2 * s[i]")],
     "half_split_partner": [("int64_t j2 = interleaved ? 2 * i + 1 : i + half;",
