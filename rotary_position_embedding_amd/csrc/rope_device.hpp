@@ -436,6 +436,26 @@ __device__ inline void load_batch(const char* x, const int64_t* off, const bool*
     }
 }
 
+// The same with every load issued, so that the compiler can count them: it
+// then waits for one head batch while the next is in flight. Inactive items
+// read their task's first row (offset 0) and heads past the chunk's end
+// repeat its last head; the values of such loads are never used.
+template <typename T, int IL, int IPL, int HU>
+__device__ inline void load_batch_all(const char* x, const int64_t* off, const bool* rot,
+                                      int h, int h_end, int64_t sh_bytes, int64_t half_bytes,
+                                      u32x4 (*in1)[IPL], u32x4 (*in2)[IPL]) {
+#pragma unroll
+    for (int u = 0; u < HU; ++u) {
+        const int hh = min(h + u, h_end - 1);
+#pragma unroll
+        for (int m = 0; m < IPL; ++m) {
+            const char* px = x + off[m] + (int64_t)hh * sh_bytes;
+            in1[u][m] = load_nt(px);
+            if (!IL) in2[u][m] = load_nt(px + (rot[m] ? half_bytes : 0));
+        }
+    }
+}
+
 template <typename T, int IL, int COEF, int IPL, int HU, bool NORM = false, int NT = kMaxTasks>
 __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     constexpr int E = Elem<T>::E;
@@ -535,8 +555,21 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
         for (int m = 0; m < IPL; ++m) codes[m] = a.sel[slot0[m] >> 4] >> (2 * (slot0[m] & 15));
     }
 
+    // Interleaved binary32 data (rotation in binary64, longer per-pair
+    // latency): every load issued and two or more head batches per wave
+    // pipelined, the next batch's loads before this batch's stores (measured
+    // on MI355X: fp32 partial interleaved prefill 36.2 -> 35.7 us). Other
+    // instances: predicated loads, one batch at a time, the compiler waiting
+    // for all of a batch's loads and placing a full wait before each head's
+    // stores, which measured faster for them (with the pipelining: fp16
+    // prefill 23.0 -> 24.3 us, M-RoPE 20.6 -> 24.4, split-half fp32 44.9 ->
+    // 50.5).
+    constexpr bool kPipe = sizeof(T) == 4 && IL && !NORM;
     u32x4 in1[HU][IPL], in2[HU][IPL];
-    load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h_begin, h_end, sh_bytes, half_bytes, in1, in2);
+    if (kPipe)
+        load_batch_all<T, IL, IPL, HU>(tk.x, off, rot, h_begin, h_end, sh_bytes, half_bytes, in1, in2);
+    else
+        load_batch<T, IL, IPL, HU>(tk.x, off, act, rot, h_begin, h_end, sh_bytes, half_bytes, in1, in2);
 
     T cf[IPL][CE], sf[IPL][CE];
     u32x4 keep[IPL];  // input bits copied to the output as they are
@@ -686,6 +719,68 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     }
 
     // -- rotate and store, one head batch at a time --------------------------
+    if (kPipe) {
+        // interleaved pairs only: whole pairs inside each item, no partner chunk
+        auto store_batch = [&](int h, u32x4 (&b1)[HU][IPL]) {
+#pragma unroll
+            for (int u = 0; u < HU; ++u) {
+#pragma unroll
+                for (int m = 0; m < IPL; ++m) {
+                    if (!(wr[m] && h + u < h_end)) continue;
+                    char* py = tk.y + yoff[m] + (int64_t)(h + u) * ysh_bytes;
+                    if (!rot[m]) {
+                        store_nt(py, b1[u][m]);
+                        continue;
+                    }
+                    const auto xv = chunk_values<T>(b1[u][m]);
+                    float r[E];
+#pragma unroll
+                    for (int j = 0; j < CE; ++j) {
+                        const float x1 = to_f(xv[2 * j]);
+                        const float x2 = to_f(xv[2 * j + 1]);
+                        const float c = to_f(cf[m][j]), s = to_f(sf[m][j]);
+                        r[2 * j] = rot_out<T>(x1, c, x2, -s);
+                        r[2 * j + 1] = rot_out<T>(x2, c, x1, s);
+                    }
+                    u32x4 o = chunk_pack<T>(r);
+                    if ((COEF == kCoefGather || COEF == kCoefMrope || COEF == kCoefAppend || tk.copy) && kany)
+                        o = select_bits(keep[m], b1[u][m], o);
+                    store_nt(py, o);
+                }
+            }
+        };
+        // At most kVecMaxHeads / HU batches per wave (the planner keeps these
+        // instances' head chunks within kVecMaxHeads heads), written out step
+        // by step: buffers in1 and nx1 hold batches in turn (a copy between
+        // them would wait for the loads), and each step's stores appear on
+        // both sides of the test for a next batch, so that no branch merges
+        // between a prefetch and the stores it overlaps.
+        constexpr int kMaxBatches = kVecMaxHeads / HU;
+        static_assert(kMaxBatches >= 1 && kMaxBatches <= 8, "head batches per wave");
+        u32x4 nx1[HU][IPL], nx2[HU][IPL];
+        int h = h_begin;
+#define ROPE_PIPE_STEP(K, C1, N1, N2)                                                                   \
+        if ((K) < kMaxBatches) {                                                                        \
+            if ((K) + 1 < kMaxBatches && h + HU < h_end) {                                              \
+                load_batch_all<T, IL, IPL, HU>(tk.x, off, rot, h + HU, h_end, sh_bytes, half_bytes, N1, N2); \
+                store_batch(h, C1);                                                                     \
+                h += HU;                                                                                \
+            } else {                                                                                    \
+                store_batch(h, C1);                                                                     \
+                return;                                                                                 \
+            }                                                                                           \
+        }
+        ROPE_PIPE_STEP(0, in1, nx1, nx2)
+        ROPE_PIPE_STEP(1, nx1, in1, in2)
+        ROPE_PIPE_STEP(2, in1, nx1, nx2)
+        ROPE_PIPE_STEP(3, nx1, in1, in2)
+        ROPE_PIPE_STEP(4, in1, nx1, nx2)
+        ROPE_PIPE_STEP(5, nx1, in1, in2)
+        ROPE_PIPE_STEP(6, in1, nx1, nx2)
+        ROPE_PIPE_STEP(7, nx1, in1, in2)
+#undef ROPE_PIPE_STEP
+        return;
+    }
     for (int h = h_begin; h < h_end; h += HU) {
         if (norm) {
             // RMSNorm of each head row first: the lane's sum of squares, summed

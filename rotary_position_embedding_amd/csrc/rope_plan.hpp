@@ -44,6 +44,9 @@ constexpr int kMaxPlanTasks = 3;
 // Waves per workgroup of the vector kernel (the planner's grouping rules
 // depend on it).
 constexpr int kWavesPerBlock = 4;
+// vector kernel, interleaved binary32 data: at most this many heads per wave
+// (the head loop of those instances is unrolled)
+constexpr int kVecMaxHeads = 16;
 // row kernel: 16-byte load instructions per wave (each covering 64 / row_lanes head rows)
 constexpr int kRowLoads = 8;
 // row kernel, on the fly: slots per token computed once per wave (LDS rows)

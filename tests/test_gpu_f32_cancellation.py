@@ -14,6 +14,7 @@ kernel policies (automatic, scalar, vector only, row wherever it applies).
 """
 import numpy as np
 import pytest
+import torch
 
 import oracle
 import rotary_position_embedding_amd as rpe
@@ -187,3 +188,34 @@ def test_kv_append_f32_cancellation(policy):
     check(host(gq), wq, what + " q_out")
     check(host(pk), wk, what + " key cache")
     assert_bitwise(host(pv), wv, what + " value cache")
+
+
+# (rank, B, S, H, D, R): launches large enough that interleaved binary32 data
+# runs two head batches per wave (the second loaded while the first stores),
+# with head counts that leave the last batch partial
+PIPELINED = [(3, 4, 1024, 7, 96, 64), (4, 2, 2048, 13, 128, 0), (3, 2, 1500, 11, 64, 32)]
+
+
+@pytest.mark.parametrize("case", PIPELINED, ids=[str(i) for i in range(len(PIPELINED))])
+def test_f32_interleaved_two_batches_per_wave(case):
+    rank, B, S, H, D, R = case
+    half = (R or D) // 2
+    M = 509
+    cos, sin = angle_table(25000 + D, M, half, np.float32)
+    ids = ids_in(25100 + S, (B, S), M + 5) - 2              # a few ids outside the table
+    ok = (ids >= 0) & (ids < M)
+    c = np.where(ok[..., None], cos[np.clip(ids, 0, M - 1)], 1.0).astype(np.float32)
+    s = np.where(ok[..., None], sin[np.clip(ids, 0, M - 1)], 0.0).astype(np.float32)
+    rows = cancelling_rows(25200 + H, np.broadcast_to(c[:, :, None], (B, S, H, half)),
+                           np.broadcast_to(s[:, :, None], (B, S, H, half)), D, 1)
+    x = rows.reshape(B, S, H * D) if rank == 3 else np.ascontiguousarray(rows.transpose(0, 2, 1, 3))
+    nh = H if rank == 3 else 0
+    xt = cuda(x)
+    yt = torch.empty_like(xt)
+    launch = rpe.rope_apply_launcher(xt, cuda(cos), cuda(sin), cuda(ids), yt, interleaved=1, num_heads=nh,
+                                     rotary_embedding_dim=R)
+    assert launch.variant.startswith("vec16"), launch.variant       # the vector kernel at these sizes
+    launch()
+    want = oracle.rope_apply(x, cos, sin, ids, interleaved=1, num_heads=nh, rotary_embedding_dim=R)
+    got = host(yt)
+    check(got, want, "f32 interleaved, two batches per wave %s" % (case,))
