@@ -261,6 +261,53 @@ def copy_reference(nbytes, steps, warmup):
     return 2 * nbytes / (ms * 1e-3) / 1e9, ms
 
 
+# hand-written plain copies (libstream_copy.so): pattern, workgroups of the
+# persistent patterns, description
+STREAM_COPY_PATTERNS = [(1, 0, "one 1 KiB run per wave"), (2, 0, "one 16 KiB run per wave"),
+                        (3, 1024, "persistent, 4 KiB chunks, 1024 workgroups"),
+                        (4, 1024, "persistent, 8 KiB chunks, 1024 workgroups")]
+
+
+def stream_copy_ceiling(nbytes, steps, warmup):
+    """The best of the hand-written plain copies of `nbytes` read and the same
+    written (no rotation), timed like the steps (same >= 1 GiB rotation over
+    independent buffers, event-timed batches, median): the rate this GPU
+    reaches for a pure stream of this size in this run."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "rotary_position_embedding_amd", "libstream_copy.so"))
+    fn = lib.stream_copy
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    nsets = max(2, -(-ROTATE_BYTES // (2 * nbytes)))
+    side = torch.cuda.Stream()
+    out = []
+    with torch.cuda.stream(side):
+        pairs = []
+        for _ in range(nsets):
+            a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda:0").normal_()
+            pairs.append((a, torch.empty_like(a)))
+        st = side.cuda_stream
+        for pattern, blocks, what in STREAM_COPY_PATTERNS:
+            def make(a, b, pattern=pattern, blocks=blocks):
+                args = (a.data_ptr(), b.data_ptr(), nbytes, pattern, blocks, st)
+
+                def launch():
+                    rc = fn(*args)
+                    if rc != 0:
+                        raise RuntimeError("stream_copy failed: %d" % rc)
+                return launch
+            t = time_steps([make(a, b) for a, b in pairs], steps, warmup)
+            out.append({"pattern": what, "us": round(t["median"] * 1e3, 3),
+                        "gbs": round(2 * nbytes / (t["median"] * 1e-3) / 1e9, 1)})
+    torch.cuda.synchronize()
+    del pairs
+    torch.cuda.empty_cache()
+    best = min(out, key=lambda r: r["us"])
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "patterns": out, "best_us": best["us"],
+            "best_gbs": best["gbs"], "best_frac_of_peak": round(best["gbs"] / PEAK_GBS, 4)}
+
+
 def measure(w, steps, warmup, onthefly=False, graph=False):
     """Eager timing; with graph=True also the HIP-graph replay timing, which
     then gives the rates (the launch-bound decode steps)."""
@@ -412,6 +459,8 @@ def main():
                          "3 row kernel wherever its shape rules allow (kernel comparisons)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time plain 128 MiB device copies instead (counter calibration)")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="time only the hand-written plain copies of the prefill workloads' X/Y sizes")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -449,6 +498,19 @@ def main():
         el = time.perf_counter() - t0
         log("copy %d bytes x %d: %.1f GB/s" % (2 * n, args.steps, 2 * 2 * n * args.steps / el / 1e9))
         print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "steps": args.steps}))
+        return
+
+    if args.copy_ceiling:
+        res = []
+        for name in (HEADLINE, "c4_mrope_f16_prefill", "c3_rope_f32_partial_interleaved"):
+            cw = rope_inputs.get(name)
+            nx = int(np.prod(cw.x_shape)) * np.dtype(cw.dtype).itemsize
+            log("plain copies of %s's X bytes (%d read, %d written)" % (name, nx, nx))
+            c = stream_copy_ceiling(nx, args.steps, args.warmup)
+            for r in c["patterns"]:
+                log("  %-45s %8.2f us  %7.1f GB/s" % (r["pattern"], r["us"], r["gbs"]))
+            res.append(dict(c, workload=name))
+        print(json.dumps({"copy_ceiling": res}), flush=True)
         return
 
     only = args.workload != HEADLINE or args.no_extra
@@ -506,6 +568,7 @@ def main():
 
     traffic = traffic_for_headline() if w.name == HEADLINE else None
     copy_ref = None
+    ceiling = None
     if not only and w.op == "rope":
         # the activation bytes of the step (X read, Y written) as a plain copy
         nx = int(np.prod(w.x_shape)) * np.dtype(w.dtype).itemsize
@@ -516,6 +579,12 @@ def main():
                     "bytes_per_copy": 2 * nx, "us": round(cms * 1e3, 3), "gbs": round(cgbs, 1),
                     "frac_of_peak": round(cgbs / PEAK_GBS, 4),
                     "step_rate_over_copy_rate": round(head["gbs"] / cgbs, 4)}
+        log("timing hand-written plain copies of the same %d bytes (read and written)" % nx)
+        ceiling = stream_copy_ceiling(nx, args.steps, args.warmup)
+        for r in ceiling["patterns"]:
+            log("  %-45s %8.2f us  %7.1f GB/s" % (r["pattern"], r["us"], r["gbs"]))
+        # the step moves X, Y and the coefficient rows and ids; the copy X and Y only
+        ceiling["step_us_over_best_copy_us"] = round(head["ms_per_step"] * 1e3 / ceiling["best_us"], 4)
     result = {
         "metric": METRIC,
         "value": round(head["gbs"], 3),
@@ -562,6 +631,7 @@ def main():
         "cpu_baseline": cpu,
         "source_sha256": kernel_source_sha(),
         "copy_reference": copy_ref,
+        "copy_ceiling": ceiling,
         "also": also,
     }
     print(json.dumps(result), flush=True)

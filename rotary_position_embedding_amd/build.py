@@ -30,6 +30,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "librope_mi355x.so")
 STAMP = LIB + ".srchash"
+# plain streaming copies, the measuring stick bench.py sets beside the rotary
+# kernels' rates (its own library: not part of the rotary C ABI)
+STREAM_COPY_LIB = os.path.join(HERE, "libstream_copy.so")
+STREAM_COPY_SOURCE = "stream_copy.hip"
 SANITIZE_DIR = os.path.join(BUILD, "sanitize")
 SANITIZED_LIB = os.path.join(SANITIZE_DIR, "librope_mi355x.so")
 SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
@@ -81,6 +85,8 @@ def built_hash(lib=None):
 
 
 def is_current(lib=None) -> bool:
+    if lib is None and not os.path.exists(STREAM_COPY_LIB):
+        return False
     return os.path.exists(lib or LIB) and built_hash(lib) == source_hash()
 
 
@@ -123,9 +129,13 @@ def build(verbose: bool = False) -> str:
               "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         return obj
 
-    jobs = max(1, min(len(HIP_SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    jobs = max(1, min(len(HIP_SOURCES) + 1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
     with ThreadPoolExecutor(max_workers=jobs) as pool:
-        objs += list(pool.map(hip_obj, HIP_SOURCES))
+        hip_objs = list(pool.map(hip_obj, HIP_SOURCES + [STREAM_COPY_SOURCE]))
+    objs += hip_objs[:-1]
+    tmp = STREAM_COPY_LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, hip_objs[-1]], verbose)
+    os.replace(tmp, STREAM_COPY_LIB)
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
