@@ -55,7 +55,10 @@
  *     any other overlap between an output and an input or another output is
  *     ROPE_ERR_ALIAS.
  *   - Arithmetic: products and sums in binary32 with fused multiply-add,
- *     one rounding to the storage type at the end; subnormals kept.
+ *     one rounding to the storage type at the end; subnormals kept. For
+ *     binary32 storage the rotation's two products and their sum are formed
+ *     in binary64 (both products exact there) and rounded to binary32 once,
+ *     so a pair whose products nearly cancel keeps full relative accuracy.
  *     Pass-through elements (the tail beyond the rotary dimension, pairs
  *     with an out-of-range position) are bit copies.
  *   - Stateless and thread-safe; rope_last_error() is per thread.

@@ -149,35 +149,6 @@ __device__ inline typename ChunkVec<T>::type chunk_values(const u32x4& v) {
     return __builtin_bit_cast(typename ChunkVec<T>::type, v);
 }
 
-// acc + the sum of squares of a 16-byte chunk's elements, in binary32. For
-// 16-bit data each pair of elements goes through one v_dot2_f32_{f16,bf16}
-// in half the issue slots of two fmas: the squares are exact in binary32
-// (bf16 ones barring overflow and underflow, where fmas fare no better) and
-// the instruction rounds the sum of the two with acc to nearest.
-typedef half_t h2 __attribute__((ext_vector_type(2)));
-typedef bf16_t b2 __attribute__((ext_vector_type(2)));
-template <typename T>
-__device__ inline float sum_squares(const u32x4& v, float acc) {
-    const auto f = chunk_values<T>(v);
-    if constexpr (sizeof(T) == 4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = fmaf(f[e], f[e], acc);
-    } else if constexpr (__is_same(T, half_t)) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const h2 p = {f[2 * k], f[2 * k + 1]};
-            acc = __builtin_amdgcn_fdot2(p, p, acc, false);
-        }
-    } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const b2 p = {f[2 * k], f[2 * k + 1]};
-            acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
-        }
-    }
-    return acc;
-}
-
 template <typename T>
 __device__ inline u32x4 chunk_pack(const float* f) {
     typename ChunkVec<T>::type r;
@@ -821,8 +792,14 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
             for (int u = 0; u < HU; ++u) {
                 float ss = 0.0f;
                 if (act[0] && h + u < h_end) {
-                    ss = sum_squares<T>(in1[u][0], ss);
-                    if (!IL && rot[0]) ss = sum_squares<T>(in2[u][0], ss);
+                    const auto v1 = chunk_values<T>(in1[u][0]);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) ss = fmaf(to_f(v1[e]), to_f(v1[e]), ss);
+                    if (!IL && rot[0]) {
+                        const auto v2 = chunk_values<T>(in2[u][0]);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) ss = fmaf(to_f(v2[e]), to_f(v2[e]), ss);
+                    }
                 }
                 ss = group_sum(ss, a.W);
                 rn[u] = rsqrtf(ss * a.inv_d + a.eps);  // v_rsq_f32: about 1 ulp
@@ -1214,7 +1191,9 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
         const auto xv = chunk_values<T>(in[u]);
         const auto pvv = chunk_values<T>(pv);
         if (norm) {
-            float ss = sum_squares<T>(in[u], 0.0f);
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; ++e) ss = fmaf(to_f(xv[e]), to_f(xv[e]), ss);
             ss = group_sum(ss, a.row_lanes);
             const float r = rsqrtf(ss * a.inv_d + a.eps);  // v_rsq_f32: about 1 ulp
             float z[E];
