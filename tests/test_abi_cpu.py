@@ -19,7 +19,8 @@ OK, NULL, DTYPE, RANK, SHAPE, ATTR, UNSUP, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
 
 
 def header_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
