@@ -464,9 +464,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: the rotary apply has no cross-GPU step and this "
-              "build runs on a single MI355X; --gpus %d is not supported" % args.gpus,
-              file=sys.stderr)
+        print("bench.py measures one GPU (the rotary apply has no cross-GPU step); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     # the library must be the build of the sources in this tree
@@ -596,7 +595,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # the arithmetic type: binary32 for 16-bit storage, binary64 products
+        # and sums for float32 storage
+        "dtype": "f64" if np.dtype(w.dtype) == np.float32 else "f32",
         "data": "synthetic",
         "config": {
             "workload": w.name,

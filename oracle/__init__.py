@@ -67,12 +67,12 @@ def _dims(x, num_heads):
 class Oracle:
     def __init__(self, lib_path=LIB_PATH):
         if not os.path.exists(lib_path):
-            raise RuntimeError("oracle library not built: %s (run __graft_entry__.build())" % lib_path)
+            raise RuntimeError("oracle library not built: %s (run python -m oracle.build)" % lib_path)
         if os.path.abspath(lib_path) == LIB_PATH:
             from . import build as _build
             if not _build.is_current(lib_path):
                 raise RuntimeError("oracle library %s was built from other sources "
-                                   "(run __graft_entry__.build())" % lib_path)
+                                   "(run python -m oracle.build)" % lib_path)
         lib = ctypes.CDLL(lib_path)
         i64, vp, f32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_int
         sig = {

@@ -71,12 +71,12 @@ def load():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            "librope_mi355x.so is not built (%s); run __graft_entry__.build() -- "
+            "librope_mi355x.so is not built (%s); run python -m rotary_position_embedding_amd.build -- "
             "there is no fallback implementation" % LIB_PATH)
     if not _build.is_current(LIB_PATH):
         raise ImportError(
             "%s was built from other sources (recorded %s, sources now %s); "
-            "rebuild it with __graft_entry__.build()" % (LIB_PATH, _build.built_hash(LIB_PATH),
+            "rebuild it with python -m rotary_position_embedding_amd.build" % (LIB_PATH, _build.built_hash(LIB_PATH),
                                                          _build.source_hash()))
     lib = ctypes.CDLL(LIB_PATH)
     for name, (args, res) in SIGNATURES.items():
