@@ -14,7 +14,7 @@ POLICY_IDS = ["auto", "scalar", "vector", "row"]
 
 def cuda(a):
     """numpy -> device tensor; uint16 arrays are bfloat16 bit patterns."""
-    a = np.ascontiguousarray(a)
+    a = np.require(a, requirements=["C", "W"])  # a writable contiguous copy only when needed
     if a.dtype == BFLOAT16:
         return torch.from_numpy(a.view(np.int16)).to(DEV).view(torch.bfloat16)
     return torch.from_numpy(a).to(DEV)

@@ -52,7 +52,8 @@ def compare(got, want):
     nan_bad = int(np.count_nonzero(nan_w != np.isnan(g)))
     finite = ~nan_w & ~np.isnan(g)
     diff = np.zeros_like(w)
-    diff[finite] = np.abs(g[finite] - w[finite])
+    with np.errstate(invalid="ignore"):  # inf - inf of equal infinities; cleared below
+        diff[finite] = np.abs(g[finite] - w[finite])
     diff[~np.isfinite(diff)] = np.inf
     same_inf = np.isinf(w) & (g == w)
     diff[same_inf] = 0.0
