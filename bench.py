@@ -9,9 +9,10 @@ seeded synthetic tensors resident in HBM before the timed region; launches
 rotate over independent (X, Y, ids) sets totalling >= 1 GiB so that the 256 MB
 last-level cache cannot hold them and the rate measured is HBM's.
 
-Decode-sized workloads (a few MB per step) are bound by the host's per-call
-cost when launched one by one; for them the rates come from the same launches
-captured in one HIP graph and replayed (the eager time is reported too).
+Workloads under 64 MiB per step (decode steps, a tensor-parallel share) are
+bound by the host's per-call cost when launched one by one; for them the
+rates come from the same launches captured in one HIP graph and replayed (the
+eager time is reported too).
 
 Timing: the K launches run in batches (10 by default) with a pair of HIP
 events on the launch stream around each batch; ms_per_step is the median of
@@ -23,8 +24,9 @@ prefill in both section layouts, the fp32 partial interleaved case, the fp16
 decode Q+K step (table and on the fly), the prefill and M-RoPE stored in
 bfloat16, the packed [Q|K|V] decode step, the decode step with the
 key/value cache append, QK-norm + RoPE (prefill with a table, decode on the
-fly), the QK-norm decode step with the cache append, and an M-RoPE decode
-step.
+fly), the QK-norm decode step with the cache append, an M-RoPE decode step,
+and one GPU's share of the fp16 prefill and of the decode Q+K step under
+8-way tensor parallelism (4 of the 32 query heads, 1 of the 8 key heads).
 """
 import argparse
 import json
@@ -308,6 +310,15 @@ def stream_copy_ceiling(nbytes, steps, warmup):
             "best_gbs": best["gbs"], "best_frac_of_peak": round(best["gbs"] / PEAK_GBS, 4)}
 
 
+# Launches moving less than this are timed in a HIP graph replay: eager, the
+# host's per-call cost (several µs) would set their rate.
+GRAPH_BELOW_BYTES = 64 << 20
+
+
+def small(w):
+    return w.algorithmic_bytes() < GRAPH_BELOW_BYTES
+
+
 def measure(w, steps, warmup, onthefly=False, graph=False):
     """Eager timing; with graph=True also the HIP-graph replay timing, which
     then gives the rates (the launch-bound decode steps)."""
@@ -525,7 +536,7 @@ def main():
                     rotary_embedding_dim=w.rotary_embedding_dim if args.rotary_dim is None else args.rotary_dim,
                     name="%s_il%s_r%s" % (w.name, args.interleaved, args.rotary_dim))
     log("timing %s: %d warmup + %d steps" % (w.name, args.warmup, args.steps))
-    head = measure(w, args.steps, args.warmup, args.onthefly, graph=w.tokens <= 4096)
+    head = measure(w, args.steps, args.warmup, args.onthefly, graph=small(w))
     log("  %.2f us/step (median of %d batches; %.2f-%.2f), %.1f GB/s (%.1f%% of %g)" % (
         head["ms_per_step"] * 1e3, head["batches"], head["ms_per_step_min"] * 1e3,
         head["ms_per_step_max"] * 1e3, head["gbs"], 100 * head["frac_of_peak"], PEAK_GBS))
@@ -545,10 +556,12 @@ def main():
                  (rope_inputs.get("qk_norm_f16_prefill"), False),
                  (rope_inputs.get("qk_norm_f16_decode"), True),
                  (rope_inputs.get("qk_norm_kv_append_f16_decode"), False),
-                 (rope_inputs.get("mrope_f16_decode"), False)]
+                 (rope_inputs.get("mrope_f16_decode"), False),
+                 (rope_inputs.get("c2_rope_f16_prefill_tp8"), False),
+                 (rope_inputs.get("c5_rope_qk_f16_decode_tp8"), False)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
-            decode = ew.tokens <= 4096
+            decode = small(ew)
             r = measure(ew, min(args.steps, 100), min(args.warmup, 10), otf, graph=decode)
             if decode:
                 log("  %.2f us/step in a HIP graph (%.2f eager): %.1f GB/s (%.1f%% of peak)" % (

@@ -287,6 +287,25 @@ EXTRA_WORKLOADS.update({
 })
 
 
+# One GPU's share of c2 and c5 under 8-way tensor parallelism (heads split
+# over the GPUs, every token on every GPU): the same kernels at the shard's
+# real shape, shorter head rows per token.
+EXTRA_WORKLOADS.update({
+    "c2_rope_f16_prefill_tp8": Workload(
+        index=11, name="c2_rope_f16_prefill_tp8", op="rope", dtype=np.float16,
+        x_shape=(4, 2048, 512), num_heads=4, cache_rows=8192, cache_base=1e6,
+        extra={"ids": "offset_arange", "offset_bound": 4096},
+        description="c2's share on one of 8 GPUs (heads split 8 ways): RotaryEmbedding rank-3 fp16 "
+                    "(4,2048,512), 4 heads of 128, ids = per-batch offset + arange, table (8192,64) base 1e6"),
+    "c5_rope_qk_f16_decode_tp8": Workload(
+        index=12, name="c5_rope_qk_f16_decode_tp8", op="rope_qk", dtype=np.float16,
+        x_shape=(256, 1, 512), num_heads=4, k_shape=(256, 1, 128), kv_num_heads=1,
+        cache_rows=32768, cache_base=1e6, extra={"ids": "uniform", "id_bound": 32768},
+        description="c5's share on one of 8 GPUs (heads split 8 ways): decode Q+K fp16, batch 256, "
+                    "Q 4 heads + K 1 head of 128, positions U[0,32768), table (32768,64) or on the fly"),
+})
+
+
 def get(name: str) -> Workload:
     return WORKLOADS[name] if name in WORKLOADS else EXTRA_WORKLOADS[name]
 

@@ -265,6 +265,9 @@ static bool choose_row_geometry(Plan* pl) {
 // (interleaved); tail items are copied. A wave owns TG consecutive tokens
 // times W items (items_per_lane items per lane) and loops over a chunk of
 // heads, keeping each lane's coefficients in registers.
+// Vector-kernel launches with fewer waves take fewer heads per wave.
+static constexpr int64_t kVecMinWaves = 2048;
+
 static void choose_geometry(Plan* pl) {
     Problem& p = pl->p;
     Geometry& g = pl->g;
@@ -370,8 +373,11 @@ static void choose_geometry(Plan* pl) {
     const int over = overrides().heads_per_wave;
     g.head_batch = hb;
     // Heads per wave: one batch, split evenly over the head count (28 heads
-    // with batch 8 -> 4 waves of 7); halved for small launches so that they
-    // still spread over the chip.
+    // with batch 8 -> 4 waves of 7); halved while a launch has fewer than
+    // kVecMinWaves waves so that small launches still spread over the chip,
+    // and the batch then no wider than a wave's heads (fp16, 8192 tokens of
+    // 4 heads of 128, one GPU's share of an 8-way head split: 1024 waves of 4
+    // heads 4.75 us, 2048 waves of 2 heads in batches of 2 4.32 us).
     int64_t total_heads = 0;
     for (int t = 0; t < p.ntask; ++t) total_heads += p.task[t].heads;
     // Interleaved binary32 data runs two batches per wave, the second one's
@@ -380,7 +386,8 @@ static void choose_geometry(Plan* pl) {
     // kVecMaxHeads heads.
     const bool pipelined = es == 4 && p.interleaved && !p.norm;
     int64_t hpw_cap = pipelined ? 2 * hb : hb;
-    while (hpw_cap > 2 && groups * ((total_heads + hpw_cap - 1) / hpw_cap) < 1024) hpw_cap /= 2;
+    while (hpw_cap > 2 && groups * ((total_heads + hpw_cap - 1) / hpw_cap) < kVecMinWaves) hpw_cap /= 2;
+    if (!pipelined && over <= 0 && over_batch == 0 && hb > hpw_cap) g.head_batch = hb = (int)hpw_cap;
     if (over > 0) hpw_cap = over;  // tuning override (a wave loops over its batches)
     if (pipelined && hpw_cap > kVecMaxHeads) hpw_cap = kVecMaxHeads;
     // Wave order: rank 4 keeps a head's tokens contiguous, so a tile of

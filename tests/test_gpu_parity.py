@@ -133,6 +133,19 @@ def test_c5_onthefly_equals_table_on_gpu():
     assert_bitwise(host(a[1]), host(b[1]), "K")
 
 
+@pytest.mark.parametrize("name", ["c2_rope_f16_prefill_tp8", "c5_rope_qk_f16_decode_tp8"])
+def test_tensor_parallel_shares_full_size(name):
+    """One GPU's share of c2 and c5 under 8-way tensor parallelism (4 query
+    heads, 1 key head), in the launch configuration the benchmark times."""
+    w = EXTRA_WORKLOADS[name]
+    got, want, _ = run_workload(w)
+    if w.op == "rope_qk":
+        log("%s Q %s K %s" % (w.name, assert_parity(got[0], want[0], w.name + " Q"),
+                              assert_parity(got[1], want[1], w.name + " K")))
+    else:
+        log("%s %s" % (w.name, assert_parity(got, want, w.name)))
+
+
 # the same workloads stored in bfloat16 (same seeds and shapes)
 
 @pytest.mark.parametrize("name,variant", [
