@@ -25,8 +25,10 @@ decode Q+K step (table and on the fly), the prefill and M-RoPE stored in
 bfloat16, the packed [Q|K|V] decode step, the decode step with the
 key/value cache append, QK-norm + RoPE (prefill with a table, decode on the
 fly), the QK-norm decode step with the cache append, an M-RoPE decode step,
-and one GPU's share of the fp16 prefill and of the decode Q+K step under
-8-way tensor parallelism (4 of the 32 query heads, 1 of the 8 key heads).
+one GPU's share of the fp16 prefill and of the decode Q+K step under 8-way
+tensor parallelism (4 of the 32 query heads, 1 of the 8 key heads), and its
+share of the fp16 prefill under 8-way sequence parallelism (256 of the 2048
+tokens of each sequence).
 """
 import argparse
 import json
@@ -558,7 +560,8 @@ def main():
                  (rope_inputs.get("qk_norm_kv_append_f16_decode"), False),
                  (rope_inputs.get("mrope_f16_decode"), False),
                  (rope_inputs.get("c2_rope_f16_prefill_tp8"), False),
-                 (rope_inputs.get("c5_rope_qk_f16_decode_tp8"), False)]
+                 (rope_inputs.get("c5_rope_qk_f16_decode_tp8"), False),
+                 (rope_inputs.get("c2_rope_f16_prefill_sp8"), False)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
             decode = small(ew)

@@ -288,8 +288,9 @@ EXTRA_WORKLOADS.update({
 
 
 # One GPU's share of c2 and c5 under 8-way tensor parallelism (heads split
-# over the GPUs, every token on every GPU): the same kernels at the shard's
-# real shape, shorter head rows per token.
+# over the GPUs, every token on every GPU), and of c2 under 8-way sequence
+# parallelism (tokens split, whole rows): the same kernels at the shard's
+# real shape.
 EXTRA_WORKLOADS.update({
     "c2_rope_f16_prefill_tp8": Workload(
         index=11, name="c2_rope_f16_prefill_tp8", op="rope", dtype=np.float16,
@@ -303,6 +304,12 @@ EXTRA_WORKLOADS.update({
         cache_rows=32768, cache_base=1e6, extra={"ids": "uniform", "id_bound": 32768},
         description="c5's share on one of 8 GPUs (heads split 8 ways): decode Q+K fp16, batch 256, "
                     "Q 4 heads + K 1 head of 128, positions U[0,32768), table (32768,64) or on the fly"),
+    "c2_rope_f16_prefill_sp8": Workload(
+        index=13, name="c2_rope_f16_prefill_sp8", op="rope", dtype=np.float16,
+        x_shape=(4, 256, 4096), num_heads=32, cache_rows=8192, cache_base=1e6,
+        extra={"ids": "offset_arange", "offset_bound": 7936},
+        description="c2's share on one of 8 GPUs (sequence split 8 ways): RotaryEmbedding rank-3 fp16 "
+                    "(4,256,4096), 32 heads of 128, ids = per-batch offset U[0,7936) + arange, table (8192,64)"),
 })
 
 

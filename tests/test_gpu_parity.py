@@ -133,10 +133,12 @@ def test_c5_onthefly_equals_table_on_gpu():
     assert_bitwise(host(a[1]), host(b[1]), "K")
 
 
-@pytest.mark.parametrize("name", ["c2_rope_f16_prefill_tp8", "c5_rope_qk_f16_decode_tp8"])
-def test_tensor_parallel_shares_full_size(name):
+@pytest.mark.parametrize("name", ["c2_rope_f16_prefill_tp8", "c5_rope_qk_f16_decode_tp8",
+                                  "c2_rope_f16_prefill_sp8"])
+def test_parallel_shares_full_size(name):
     """One GPU's share of c2 and c5 under 8-way tensor parallelism (4 query
-    heads, 1 key head), in the launch configuration the benchmark times."""
+    heads, 1 key head) and of c2 under 8-way sequence parallelism (256
+    tokens per sequence), in the launch configuration the benchmark times."""
     w = EXTRA_WORKLOADS[name]
     got, want, _ = run_workload(w)
     if w.op == "rope_qk":
