@@ -324,7 +324,10 @@ int rope_cos_sin_cache(const rope_tensor* inv_freq, float scaling,
 
 /*
  * Validation without launching: the same checks as the op, and the kernel
- * variant it would run (static string, e.g. "rope/vec16/ids"), written to
+ * variant it would run (static string: the kernel, "vec16", "row16" or
+ * "scalar", then "/norm" for the QK-norm ops, then the coefficient source,
+ * "gather", "per_token", "mrope", "on_the_fly" or "append"; e.g.
+ * "vec16/gather"), written to
  * *variant when variant != NULL and the status is ROPE_OK. Never touches
  * the GPU, so it can be called on a machine without one.
  */
