@@ -265,8 +265,10 @@ static bool choose_row_geometry(Plan* pl) {
 // (interleaved); tail items are copied. A wave owns TG consecutive tokens
 // times W items (items_per_lane items per lane) and loops over a chunk of
 // heads, keeping each lane's coefficients in registers.
-// Vector-kernel launches with fewer waves take fewer heads per wave.
-static constexpr int64_t kVecMinWaves = 2048;
+// Vector-kernel launches: heads per wave are halved while the launch then
+// stays within this many waves (about one round of resident waves of the
+// 16-bit instances).
+static constexpr int64_t kVecTargetWaves = 4096;
 
 static void choose_geometry(Plan* pl) {
     Problem& p = pl->p;
@@ -373,20 +375,30 @@ static void choose_geometry(Plan* pl) {
     const int over = overrides().heads_per_wave;
     g.head_batch = hb;
     // Heads per wave: one batch, split evenly over the head count (28 heads
-    // with batch 8 -> 4 waves of 7); halved while a launch has fewer than
-    // kVecMinWaves waves so that small launches still spread over the chip,
-    // and the batch then no wider than a wave's heads (fp16, 8192 tokens of
-    // 4 heads of 128, one GPU's share of an 8-way head split: 1024 waves of 4
-    // heads 4.75 us, 2048 waves of 2 heads in batches of 2 4.32 us).
-    int64_t total_heads = 0;
-    for (int t = 0; t < p.ntask; ++t) total_heads += p.task[t].heads;
+    // with batch 8 -> 4 waves of 7); halved while the launch then keeps
+    // within kVecTargetWaves waves, so that smaller launches still fill the
+    // chip, down to 2 heads per wave (4 for M-RoPE, whose per-wave
+    // coefficient assembly would otherwise serve too few heads); the batch
+    // then no wider than a wave's heads. Measured on MI355X (fp16, heads of
+    // 128): 8192 tokens of 16 heads 12.1 us with 2048 waves of 8 heads, 11.7
+    // with 4096 of 4, 13.1 with 8192 of 2; 8192 tokens of 4 heads (one GPU's
+    // share of an 8-way head split) 4.75 us with 1024 waves of 4 heads, 4.32
+    // with 2048 of 2; M-RoPE with 28 heads and 4096 tokens 12.2 us with 2048
+    // waves of 7 heads, 11.2 with 3584 of 4, 13.8 with 7168 of 2; c2 and c4
+    // (4096 waves) lose 14-16% with 4 heads per wave.
     // Interleaved binary32 data runs two batches per wave, the second one's
     // loads in flight while the first stores (fp32 partial interleaved
     // prefill 36.2 -> 35.7 us); its head loop is unrolled over at most
     // kVecMaxHeads heads.
     const bool pipelined = es == 4 && p.interleaved && !p.norm;
     int64_t hpw_cap = pipelined ? 2 * hb : hb;
-    while (hpw_cap > 2 && groups * ((total_heads + hpw_cap - 1) / hpw_cap) < kVecMinWaves) hpw_cap /= 2;
+    auto waves_at = [&](int64_t cap) {
+        int64_t w = 0;
+        for (int t = 0; t < p.ntask; ++t) w += groups * ((p.task[t].heads + cap - 1) / cap);
+        return w;
+    };
+    const int64_t min_hpw = p.coef == kCoefMrope ? 4 : 2;
+    while (hpw_cap / 2 >= min_hpw && waves_at(hpw_cap / 2) <= kVecTargetWaves) hpw_cap /= 2;
     if (!pipelined && over <= 0 && over_batch == 0 && hb > hpw_cap) g.head_batch = hb = (int)hpw_cap;
     if (over > 0) hpw_cap = over;  // tuning override (a wave loops over its batches)
     if (pipelined && hpw_cap > kVecMaxHeads) hpw_cap = kVecMaxHeads;
