@@ -193,7 +193,15 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // 8192 tokens), both measured on MI355X in HIP-graph replay.
 // A wave takes up to kRowLoads instructions of one token; smaller launches
 // take fewer per wave so that they spread over the chip.
-static constexpr int64_t kRowMaxBytes = 4 << 20;
+// Between 4 and 8 MiB (fp16, heads of 128, µs row / vector kernel): Q+K of
+// 512 tokens (5 MiB) 3.64 / 3.99 with a table and 3.99 / 5.16 on the fly,
+// QK-norm on the fly 4.63 / 5.65; 1536 tokens of 4 heads (6 MiB) 3.72 /
+// 3.95; 4 x 192 tokens of 32 heads (6 MiB) 3.70 / 3.93; Q+K of 768 tokens
+// (7.5 MiB) 4.32 / 4.37; at 8 MiB 4.78 / 4.32 (4 heads) and 4.39 / 4.27 (32
+// heads). M-RoPE (rank 4, 28 heads) turns earlier: 4.37 / 4.53 at 3.5 MiB,
+// 5.04 / 4.67 at 5.25 MiB.
+static constexpr int64_t kRowMaxBytes = 6 << 20;
+static constexpr int64_t kRowMaxBytesMrope = 4 << 20;
 
 static bool choose_row_geometry(Plan* pl) {
     Problem& p = pl->p;
@@ -208,7 +216,8 @@ static bool choose_row_geometry(Plan* pl) {
     if (!p.interleaved && !pow2(dl)) return false;
     int64_t xbytes = 0;
     for (int t = 0; t < p.ntask; ++t) xbytes += p.B * p.S * p.task[t].heads * row_bytes;
-    if (xbytes > kRowMaxBytes && policy != 3) return false;
+    const int64_t max_bytes = p.coef == kCoefMrope ? kRowMaxBytesMrope : kRowMaxBytes;
+    if (xbytes > max_bytes && policy != 3) return false;
     const int RL = (int)(row_bytes / 16);
     const int rpi = 64 / RL;
     const int64_t ntok = p.B * p.S;
@@ -269,6 +278,8 @@ static bool choose_row_geometry(Plan* pl) {
 // stays within this many waves (about one round of resident waves of the
 // 16-bit instances).
 static constexpr int64_t kVecTargetWaves = 4096;
+// M-RoPE keeps 4 heads per wave while that still gives this many waves.
+static constexpr int64_t kVecMropeMinWaves = 1536;
 
 static void choose_geometry(Plan* pl) {
     Problem& p = pl->p;
@@ -378,7 +389,11 @@ static void choose_geometry(Plan* pl) {
     // with batch 8 -> 4 waves of 7); halved while the launch then keeps
     // within kVecTargetWaves waves, so that smaller launches still fill the
     // chip, down to 2 heads per wave (4 for M-RoPE, whose per-wave
-    // coefficient assembly would otherwise serve too few heads); the batch
+    // coefficient assembly would otherwise serve too few heads, unless that
+    // leaves fewer than kVecMropeMinWaves waves: 2 x 28 heads x 768 tokens
+    // 5.85 us with 2688 waves of 2, 6.05 with 1344 of 4; x 384 tokens 4.46
+    // with 1344 of 2, 4.69 with 672 of 4; x 1024 tokens 7.78 with 3584 of 2,
+    // 6.50 with 1792 of 4); the batch
     // then no wider than a wave's heads. Measured on MI355X (fp16, heads of
     // 128): 8192 tokens of 16 heads 12.1 us with 2048 waves of 8 heads, 11.7
     // with 4096 of 4, 13.1 with 8192 of 2; 8192 tokens of 4 heads (one GPU's
@@ -397,7 +412,7 @@ static void choose_geometry(Plan* pl) {
         for (int t = 0; t < p.ntask; ++t) w += groups * ((p.task[t].heads + cap - 1) / cap);
         return w;
     };
-    const int64_t min_hpw = p.coef == kCoefMrope ? 4 : 2;
+    const int64_t min_hpw = p.coef == kCoefMrope && waves_at(4) >= kVecMropeMinWaves ? 4 : 2;
     while (hpw_cap / 2 >= min_hpw && waves_at(hpw_cap / 2) <= kVecTargetWaves) hpw_cap /= 2;
     if (!pipelined && over <= 0 && over_batch == 0 && hb > hpw_cap) g.head_batch = hb = (int)hpw_cap;
     if (over > 0) hpw_cap = over;  // tuning override (a wave loops over its batches)

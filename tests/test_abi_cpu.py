@@ -198,14 +198,18 @@ def test_kernel_policy_forces_scalar():
 
 
 def test_row_kernel_selection_rules():
-    """The row kernel: decode-sized launches (<= 4 MiB of activations read), head
-    rows of a power-of-two size from 32 B to 1 KiB, split-half partners a power
-    of two of lanes apart; never M-RoPE. Policy 3 lifts the size rule."""
+    """The row kernel: decode-sized launches (<= 6 MiB of activations read,
+    <= 4 MiB for M-RoPE), head rows of a power-of-two size from 32 B to 1 KiB,
+    split-half partners a power of two of lanes apart. Policy 3 lifts the size
+    rule."""
     big = dict(B=1, S=8192, H=32, D=128)                        # 64 MiB of fp16 X
     assert check_rope(rope_case(**big)) == (OK, "vec16/gather")
     assert with_policy(3, check_rope, rope_case(**big)) == (OK, "row16/gather")
-    assert check_rope(rope_case(B=1, S=512, H=32, D=128)) == (OK, "row16/gather")    # 4 MiB
-    assert check_rope(rope_case(B=1, S=513, H=32, D=128)) == (OK, "vec16/gather")
+    assert check_rope(rope_case(B=1, S=768, H=32, D=128)) == (OK, "row16/gather")    # 6 MiB
+    assert check_rope(rope_case(B=1, S=769, H=32, D=128)) == (OK, "vec16/gather")
+    m = dict(rank=4, B=1, H=32, D=128, M=64, section=(16, 24, 24))
+    assert check_mrope(mrope_case(S=512, **m)) == (OK, "row16/mrope")               # 4 MiB
+    assert check_mrope(mrope_case(S=513, **m)) == (OK, "vec16/mrope")
     assert check_rope(rope_case(D=96)) == (OK, "vec16/gather")            # 192-byte rows
     assert check_rope(rope_case(D=128, R=96)) == (OK, "vec16/gather")     # partners 6 lanes apart
     assert check_rope(rope_case(D=128, R=96, interleaved=1)) == (OK, "row16/gather")
