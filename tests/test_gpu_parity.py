@@ -10,6 +10,7 @@ from oracle_pins import angle_table, ids_in, pair_index
 from parity import assert_bitwise, assert_parity, bits, compare
 from gpu_io import DEV, cuda, host, one, torch_dtype, POLICIES, POLICY_IDS
 from rope_inputs import BFLOAT16, EXTRA_WORKLOADS, WORKLOADS, SplitMix64, normal_tensor, with_dtype, with_layout
+from rope_inputs import get as get_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -146,6 +147,52 @@ def test_parallel_shares_full_size(name):
                               assert_parity(got[1], want[1], w.name + " K")))
     else:
         log("%s %s" % (w.name, assert_parity(got, want, w.name)))
+
+
+def _resized(name, seq=None, heads=None):
+    """A workload at another sequence length or head count (same seeds and
+    recipe), for the launch geometries between the decode steps and the
+    benchmark prefills."""
+    from dataclasses import replace
+    w = get_workload(name)
+    xs = list(w.x_shape)
+    ks = None if w.k_shape is None else list(w.k_shape)
+    if seq is not None:
+        xs[2 if len(xs) == 4 else 1] = seq
+        if ks is not None:
+            ks[2 if len(ks) == 4 else 1] = seq
+    if heads is not None:
+        xs[2] = heads * w.head_size
+    return replace(w, x_shape=tuple(xs), k_shape=None if ks is None else tuple(ks),
+                   num_heads=heads or w.num_heads, name="%s_s%s_h%s" % (name, seq, heads))
+
+
+@pytest.mark.parametrize("name,seq,heads,layout,onthefly", [
+    ("c4_mrope_f16_prefill", 1024, None, 0, False),    # M-RoPE, 4 heads per wave
+    ("c4_mrope_f16_prefill", 1024, None, 1, False),
+    ("c4_mrope_f16_prefill", 768, None, 0, False),     # M-RoPE, 2 heads per wave
+    ("c2_rope_f16_prefill", None, 16, None, False),    # 4 heads per wave in batches of 4
+    ("c2_rope_f16_prefill", 512, None, None, False),
+    ("c3_rope_f32_partial_interleaved", 128, None, None, False),
+    ("c5_rope_qk_f16_decode", 2, None, None, False),   # 5 MiB: the row kernel
+    ("c5_rope_qk_f16_decode", 2, None, None, True),
+])
+def test_mid_size_launches(name, seq, heads, layout, onthefly):
+    """Launches between the decode steps and the benchmark prefills, in the
+    geometries the planner gives them (fewer heads per wave, the row kernel
+    up to 6 MiB), against the oracle at full size."""
+    w = _resized(name, seq, heads)
+    if layout is not None:
+        w = with_layout(w, layout)
+    log("mid-size %s layout=%s onthefly=%s" % (w.name, layout, onthefly))
+    got, want, inputs = run_workload(w, onthefly)
+    if w.op == "rope_qk":
+        log("%s Q %s K %s" % (w.name, assert_parity(got[0], want[0], w.name + " Q"),
+                              assert_parity(got[1], want[1], w.name + " K")))
+        return
+    log("%s %s" % (w.name, assert_parity(got, want, w.name)))
+    if w.rotary_embedding_dim:
+        assert_bitwise(got[..., w.rotary_embedding_dim:], inputs[0][..., w.rotary_embedding_dim:], "tail")
 
 
 # the same workloads stored in bfloat16 (same seeds and shapes)
