@@ -408,8 +408,9 @@ __device__ inline int task_index_items(const KArgs& a, int64_t item) {
 // stores, so a lane has at most two 16-byte stores in flight; measured on
 // MI355X this metering is faster than letting a wave's stores pile up (a
 // batch of 16 unmetered stores per lane doubled the kernel time), and so are
-// the predicated loads (versus clamped unconditional ones). X and Y are
-// touched once: nontemporal loads and stores.
+// the predicated loads (versus clamped unconditional ones), except for
+// interleaved binary32 data, whose head batches are pipelined (in the
+// kernel). X and Y are touched once: nontemporal loads and stores.
 
 // Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i % 8).
 // A remapping that keeps consecutive logical workgroups on one XCD (so that
