@@ -28,7 +28,8 @@ fly), the QK-norm decode step with the cache append, an M-RoPE decode step,
 one GPU's share of the fp16 prefill and of the decode Q+K step under 8-way
 tensor parallelism (4 of the 32 query heads, 1 of the 8 key heads), and its
 share of the fp16 prefill under 8-way sequence parallelism (256 of the 2048
-tokens of each sequence).
+tokens of each sequence), and a prompt of 4 x 2048 tokens written to the
+key/value caches.
 """
 import argparse
 import json
@@ -149,7 +150,8 @@ def setup_kv_append(w, q0, dt, dev):
     """Decode with cache append: sets of (Q, K, V, q_out, lengths) rotate;
     the two caches are shared, and each set's lengths are the base lengths
     shifted by a set-dependent offset (mod the cache length) so that the
-    rows written differ from set to set."""
+    rows written differ from set to set. A prompt (every sequence starts at
+    0, rows 0..S-1 written): each set has caches of its own."""
     import torch
     import rotary_position_embedding_amd as rpe
     smax = w.extra["cache_seq"]
@@ -159,6 +161,7 @@ def setup_kv_append(w, q0, dt, dev):
     lens0 = w.make_lengths()
     inv = rpe.rope_inv_freq(w.rotary_dim, w.cache_base, device=dev)
     cos, sin = rpe.rope_cos_sin_cache(inv, w.cache_rows, dt, w.scaling)
+    prompt = bool(w.extra.get("prompt"))
     pk = torch.zeros(B, Hk, smax, D, dtype=dt, device=dev)
     pv = torch.zeros_like(pk)
     set_bytes = 2 * (q0.numel() + 2 * k0.numel()) * q0.element_size()
@@ -166,7 +169,11 @@ def setup_kv_append(w, q0, dt, dev):
     launchers = []
     wts = [to_device(a, dev) for a in w.make_norm_weights()] if w.op == "kv_append_norm" else None
     for i in range(nsets):
-        lens_h = ((lens0.astype(np.int64) - 1 + 997 * i) % smax + 1).astype(np.int32)
+        if prompt:
+            lens_h = lens0.copy()
+            pk, pv = torch.zeros_like(pk), torch.zeros_like(pv)
+        else:
+            lens_h = ((lens0.astype(np.int64) - 1 + 997 * i) % smax + 1).astype(np.int32)
         q, k, v = q0.clone(), k0.clone(), v0.clone()
         lens = torch.from_numpy(lens_h).to(dev)
         if wts is None:
@@ -561,7 +568,8 @@ def main():
                  (rope_inputs.get("mrope_f16_decode"), False),
                  (rope_inputs.get("c2_rope_f16_prefill_tp8"), False),
                  (rope_inputs.get("c5_rope_qk_f16_decode_tp8"), False),
-                 (rope_inputs.get("c2_rope_f16_prefill_sp8"), False)]
+                 (rope_inputs.get("c2_rope_f16_prefill_sp8"), False),
+                 (rope_inputs.get("kv_append_f16_prompt"), False)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
             decode = small(ew)

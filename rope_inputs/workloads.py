@@ -132,7 +132,10 @@ class Workload:
         return normal_tensor(seed(self.index, 4), self.k_shape, self.dtype)
 
     def make_lengths(self) -> np.ndarray:
-        """kv_append: per-sequence total key lengths U[1, cache_seq] (int32)."""
+        """kv_append: per-sequence total key lengths U[1, cache_seq] (int32);
+        a prompt: every sequence holds its S new tokens only."""
+        if self.extra.get("prompt"):
+            return np.full((self.batch,), self.seq, np.int32)
         cap = self.extra["cache_seq"]
         return (uniform_ints(seed(self.index, 1), (self.batch,), cap) + 1).astype(np.int32)
 
@@ -304,6 +307,12 @@ EXTRA_WORKLOADS.update({
         cache_rows=32768, cache_base=1e6, extra={"ids": "uniform", "id_bound": 32768},
         description="c5's share on one of 8 GPUs (heads split 8 ways): decode Q+K fp16, batch 256, "
                     "Q 4 heads + K 1 head of 128, positions U[0,32768), table (32768,64) or on the fly"),
+    "kv_append_f16_prompt": Workload(
+        index=14, name="kv_append_f16_prompt", op="kv_append", dtype=np.float16,
+        x_shape=(4, 2048, 4096), num_heads=32, k_shape=(4, 2048, 1024), kv_num_heads=8,
+        cache_rows=8192, cache_base=1e6, extra={"cache_seq": 4096, "prompt": True},
+        description="Prompt with cache append fp16: 4 sequences of 2048 new tokens, Q 32 heads + K, V "
+                    "8 heads of 128, written to rows 0..2047 of (4, 8, 4096, 128) caches, table (8192, 64)"),
     "c2_rope_f16_prefill_sp8": Workload(
         index=13, name="c2_rope_f16_prefill_sp8", op="rope", dtype=np.float16,
         x_shape=(4, 256, 4096), num_heads=32, cache_rows=8192, cache_base=1e6,

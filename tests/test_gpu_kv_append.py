@@ -323,3 +323,38 @@ def test_kv_append_decode_bench_size(name):
     assert bool((gk.view(torch.int16) == fill_k).all()), "a key-cache row outside L[b] - 1 was written"
     assert bool((gv.view(torch.int16) == fill_v - 0x10000).all()), "a value-cache row outside L[b] - 1 was written"
     print(name, "bench size", r, flush=True)
+
+
+def test_kv_append_prompt_bench_size():
+    """The prompt with cache append the benchmark times, at its size and in
+    its launch configuration: 4 sequences of 2048 new tokens (a prompt: each
+    starts at position 0), 32 query and 8 key heads of 128, f16, caches of
+    (4, 8, 4096, 128), an (8192, 64) table. q_out and the written rows 0..2047
+    against the oracle (RoPE at positions 0..2047, as the pins tie the append
+    to it), V rows bit for bit, and every other cache element must still hold
+    its fill value."""
+    w = get("kv_append_f16_prompt")
+    B, S, H, Hk, D, Smax = w.batch, w.seq, w.num_heads, w.kv_num_heads, w.head_size, w.extra["cache_seq"]
+    q, k, v, lens = w.make_x(), w.make_k(), w.make_v(), w.make_lengths()
+    assert (lens == S).all()
+    inv = oracle.inv_freq(w.cache_base, D)
+    cos, sin = oracle.cos_sin_cache(np.float16, w.cache_rows, inv)
+    pos = np.broadcast_to(np.arange(S, dtype=np.int64), (B, S)).copy()
+    eq, ek = oracle.rope_apply_qk(q, k, cos, sin, pos, num_heads=H, kv_num_heads=Hk)
+    fill_k, fill_v = 0x3c00, 0xbc00  # 1.0 and -1.0
+    gk = torch.full((B, Hk, Smax, D), 1.0, dtype=torch.float16, device=DEV)
+    gv = torch.full((B, Hk, Smax, D), -1.0, dtype=torch.float16, device=DEV)
+    print("bench-size prompt cache append", flush=True)
+    gq = rpe.rope_kv_append(cuda(q), cuda(k), cuda(v), gk, gv, cuda(lens), S, cuda(cos), cuda(sin),
+                            num_heads=H, kv_num_heads=Hk)
+    torch.cuda.synchronize()
+    got_k = host(gk[:, :, :S, :].permute(0, 2, 1, 3).contiguous()).reshape(B, S, Hk * D)
+    got_v = host(gv[:, :, :S, :].permute(0, 2, 1, 3).contiguous()).reshape(B, S, Hk * D)
+    r = assert_parity(host(gq), eq, "q_out")
+    assert_parity(got_k, ek, "written key rows")
+    assert_bitwise(got_v, v, "written value rows")
+    gk[:, :, :S, :] = 1.0
+    gv[:, :, :S, :] = -1.0
+    assert bool((gk.view(torch.int16) == fill_k).all()), "a key-cache row past the prompt was written"
+    assert bool((gv.view(torch.int16) == fill_v - 0x10000).all()), "a value-cache row past the prompt was written"
+    print("prompt bench size", r, flush=True)

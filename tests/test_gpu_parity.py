@@ -176,11 +176,14 @@ def _resized(name, seq=None, heads=None):
     ("c3_rope_f32_partial_interleaved", 128, None, None, False),
     ("c5_rope_qk_f16_decode", 2, None, None, False),   # 5 MiB: the row kernel
     ("c5_rope_qk_f16_decode", 2, None, None, True),
+    ("c2_rope_f16_prefill", None, 40, None, False),    # over one round: many waves of 2 heads
+    ("c5_rope_qk_f16_decode", 32, None, None, False),
 ])
 def test_mid_size_launches(name, seq, heads, layout, onthefly):
-    """Launches between the decode steps and the benchmark prefills, in the
-    geometries the planner gives them (fewer heads per wave, the row kernel
-    up to 6 MiB), against the oracle at full size."""
+    """Launches between the decode steps and the benchmark prefills, and
+    larger ones, in the geometries the planner gives them (fewer heads per
+    wave, the row kernel up to 6 MiB, batches of 2 heads past one round of
+    waves), against the oracle at full size."""
     w = _resized(name, seq, heads)
     if layout is not None:
         w = with_layout(w, layout)
