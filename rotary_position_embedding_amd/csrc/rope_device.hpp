@@ -873,6 +873,11 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
                     store_nt(py, in1[u][m]);
                     continue;
                 }
+                if (NT == 3 && tk.copy) {  // a pass-through task (V): its chunks as loaded
+                    store_nt(py, in1[u][m]);
+                    if (!IL) store_nt(py + half_bytes, in2[u][m]);
+                    continue;
+                }
                 if (IL) {
                     const auto xv = chunk_values<T>(in1[u][m]);
                     float r[E];
