@@ -76,7 +76,8 @@ struct KArgs {
     const int64_t* ids;
     const float* inv_freq;
     int32_t ntask, W, NP, TG, P, R, D, interleaved;
-    int32_t pad0, prompt;       // prompt: append kind, every sequence starts at 0
+    int32_t group_major;        // three-task vector launch: waves in token-group order
+    int32_t prompt;             // prompt: append kind, every sequence starts at 0
     float scaling, scale;
     float eps;                  // QK-norm epsilon
     float inv_d;                // QK-norm: 1/D rounded to binary32
@@ -85,6 +86,10 @@ struct KArgs {
     int32_t row_shift;          // log2(row_lanes)
     int32_t half_lanes;         // row kernel, split halves: lanes between partner chunks
     uint32_t w_m, w_s, s_m, s_s;  // division by W and by S (multiply-high and shift)
+    // group_major: per token group the chunks of task 0, then 1, then 2
+    // (c0, c0 + c1 and c0 + c1 + c2 chunks), and the division by the last
+    int32_t gm_c0, gm_c01, gm_c;
+    uint32_t gm_m, gm_s;
     const int32_t* seqlens;     // append kind: total key length per sequence
     int64_t rows_out;           // append kind: cache rows
     uint32_t sel[kSelWords];
@@ -468,8 +473,22 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
     // wave-uniform by construction; readfirstlane lets the compiler keep the
     // task selection and its fields in scalar registers
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
-    const TaskView tk = task_pick<COEF, NORM, NT>(a, gw);
+    int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
+    TaskView tk;
+    if (NT == 3 && a.group_major) {
+        // token-group order: the chunks of all three tasks of one token group
+        // are consecutive waves (a packed [Q|K|V] row is read in one visit);
+        // gw becomes the wave's index in its task's own order
+        const uint32_t g = fast_div((uint32_t)gw, a.gm_m, a.gm_s);
+        const int r = (int)((uint32_t)gw - g * (uint32_t)a.gm_c);
+        const int ti = r < a.gm_c0 ? 0 : (r < a.gm_c01 ? 1 : 2);
+        const int first = ti == 0 ? 0 : (ti == 1 ? a.gm_c0 : a.gm_c01);
+        const int next = ti == 0 ? a.gm_c0 : (ti == 1 ? a.gm_c01 : a.gm_c);
+        tk = task_of<COEF, NORM>(a, ti);
+        gw = tk.wave_begin + (int64_t)g * (next - first) + (r - first);
+    } else {
+        tk = task_pick<COEF, NORM, NT>(a, gw);
+    }
     // 32-bit index arithmetic (the planner keeps a vector-kernel launch's
     // waves and tokens below 2^31): a short scalar prologue before the loads
     const uint32_t local = (uint32_t)(gw - tk.wave_begin);

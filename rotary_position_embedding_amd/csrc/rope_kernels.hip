@@ -73,6 +73,14 @@ int launch_plan(const Plan& pl, void* stream) {
             }
         }
     }
+    a.group_major = 0;
+    if (g.vector && !g.row_kernel && g.group_major && p.ntask == 3) {
+        a.group_major = 1;
+        a.gm_c0 = a.t[0].chunks;
+        a.gm_c01 = a.t[0].chunks + a.t[1].chunks;
+        a.gm_c = a.gm_c01 + a.t[2].chunks;
+        fast_div_magic(a.gm_c, &a.gm_m, &a.gm_s);
+    }
     a.ntok = p.B * p.S;
     a.S = p.S;
     a.M = p.M;

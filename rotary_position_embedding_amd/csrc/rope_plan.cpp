@@ -168,13 +168,13 @@ static int env_int(const char* name) {
 // Tuning overrides for measurement sweeps, read once per process (getenv
 // scans the environment: too slow for every call).
 struct TuningOverrides {
-    int heads_per_wave, items_per_lane, head_batch, wave_tile, no_share, row_loads;
+    int heads_per_wave, items_per_lane, head_batch, wave_tile, no_share, row_loads, task_order;
 };
 static const TuningOverrides& overrides() {
     static const TuningOverrides o = {env_int("ROPE_HEADS_PER_WAVE"), env_int("ROPE_ITEMS_PER_LANE"),
                                       env_int("ROPE_HEAD_BATCH"),     env_int("ROPE_WAVE_TILE"),
                                       env_int("ROPE_NO_SHARE"),
-                                      env_int("ROPE_ROW_LOADS")};
+                                      env_int("ROPE_ROW_LOADS"),      env_int("ROPE_TASK_ORDER")};
     return o;
 }
 
@@ -305,6 +305,7 @@ static void choose_geometry(Plan* pl) {
     g.vector = ok;
     g.variant = variant_name(ok, p.coef, p.norm != 0);
     g.row_kernel = 0;
+    g.group_major = 0;
     if (!ok) return;
     if (choose_row_geometry(pl)) {
         g.variant = row_variant_name(p.coef, p.norm != 0);
@@ -465,6 +466,33 @@ static void choose_geometry(Plan* pl) {
         for (int t = 0; t < p.ntask; ++t)
             if (p.task[t].heads > 0 && g.chunks[t] % kWavesPerBlock != 0) ok_share = false;
         g.share_coef = ok_share ? 1 : 0;
+    }
+    // Three tasks read from one packed rank-3 tensor ([Q|K|V] in each token's
+    // row: the packed op, or the cache append's packed query), in a launch of
+    // more than one round of waves: waves in token-group order, so that the
+    // three tasks' chunks of one token group run together and a token's row
+    // is read in one visit instead of its Q part in the first waves and its
+    // K and V parts in the last. Measured on MI355X (fp16, µs, token-group /
+    // task order): packed [Q|K|V] of 8192 tokens 38.3 / 40.8 (on the fly
+    // 38.4 / 40.8), of 2048 tokens (one round) 9.63 / 9.36; with separate Q,
+    // K and V tensors the task order is faster (the cache append of a 4 x
+    // 2048-token prompt 36.3 / 35.3, its QK-norm form 40.3 / 38.3). With
+    // coefficients shared through LDS every chunk count is a multiple of the
+    // waves per workgroup, so a workgroup still holds chunks of one task and
+    // one token group.
+    g.group_major = 0;
+    const int order = overrides().task_order;  // 1: token-group order, 2: task order (sweeps)
+    if (p.ntask == 3 && g.tile == 1 && order != 2) {
+        const uintptr_t x0 = (uintptr_t)p.task[0].x;
+        const uintptr_t row = (uintptr_t)(p.task[0].stride_s * es);  // bytes of a token's row
+        bool packed = true, ok_order = true;
+        for (int t = 0; t < p.ntask; ++t) {
+            const uintptr_t xt = (uintptr_t)p.task[t].x;
+            packed = packed && p.task[t].stride_s == p.task[0].stride_s &&
+                     p.task[t].stride_b == p.task[0].stride_b && xt >= x0 && xt - x0 < row;
+            if (p.task[t].heads <= 0 || g.waves[t] != groups * g.chunks[t]) ok_order = false;
+        }
+        g.group_major = ok_order && (order == 1 || (packed && total_waves > kVecTargetWaves)) ? 1 : 0;
     }
 }
 

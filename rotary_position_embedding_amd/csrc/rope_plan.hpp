@@ -87,6 +87,7 @@ struct Geometry {
     int32_t TG;           // tokens per wave
     int32_t tile;         // token groups per head chunk in a tile of waves
     int32_t share_coef;   // on the fly: the 4 waves of a workgroup share one token group
+    int32_t group_major;  // three tasks: waves in token-group order (see KArgs)
     int32_t row_kernel;   // 1: the row kernel (lanes along head rows of one token)
     int32_t row_lanes;    // row kernel: lanes per head row
     int32_t half_lanes;   // row kernel, split halves: lanes between partner chunks

@@ -637,6 +637,29 @@ def test_qkv_packed(case, policy, onthefly, inplace):
     assert_bitwise(gv, v, "V")
 
 
+@pytest.mark.parametrize("onthefly", [False, True])
+def test_qkv_packed_prefill_size(onthefly):
+    """A packed [Q|K|V] prefill of 4 x 2048 tokens (32 + 8 + 8 heads of 128,
+    fp16) in the default launch configuration: more than one round of waves,
+    so the three tasks' waves run in token-group order."""
+    B, S, H, Hk, D, M = 4, 2048, 32, 8, 128, 8192
+    qkv = normal_tensor(9150, (B, S, (H + 2 * Hk) * D), np.float16)
+    ids = ids_in(9151, (B, 1), 4096) + np.arange(S, dtype=np.int64)[None, :]
+    inv = oracle.inv_freq(1e6, D)
+    q, k, v = split_packed(qkv, 3, H, Hk)
+    if onthefly:
+        wq, wk = oracle.rope_apply_qk(q, k, None, None, ids, num_heads=H, kv_num_heads=Hk, inv_freq=inv)
+        tabs = dict(cos_cache=None, sin_cache=None, inv_freq=cuda(inv))
+    else:
+        cos, sin = oracle.cos_sin_cache(np.float16, M, inv)
+        wq, wk = oracle.rope_apply_qk(q, k, cos, sin, ids, num_heads=H, kv_num_heads=Hk)
+        tabs = dict(cos_cache=cuda(cos), sin_cache=cuda(sin))
+    y = rpe.rope_apply_qkv_packed(cuda(qkv), position_ids=cuda(ids), num_heads=H, kv_num_heads=Hk, **tabs)
+    gq, gk, gv = split_packed(host(y), 3, H, Hk)
+    log("packed prefill onthefly=%s Q %s K %s" % (onthefly, assert_parity(gq, wq, "Q"), assert_parity(gk, wk, "K")))
+    assert_bitwise(gv, v, "V")
+
+
 @pytest.mark.parametrize("policy", POLICIES, ids=POLICY_IDS)
 def test_empty_table_copies_everything(policy):
     """M = 0 rows: every id is out of range, so Y == X bit for bit (the vector
