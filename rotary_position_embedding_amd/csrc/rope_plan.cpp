@@ -413,17 +413,20 @@ static void choose_geometry(Plan* pl) {
         for (int t = 0; t < p.ntask; ++t) w += groups * ((p.task[t].heads + cap - 1) / cap);
         return w;
     };
-    // Launches whose full-batch waves need more than one round (16-bit data,
-    // one item per lane): many small waves, batches of 2, which measured
-    // faster (fp16, µs, batch 8 / 2): 8192 tokens of 40 heads 33.2 / 29.7,
+    // Launches whose full-batch waves need more than one round (one or two
+    // items per lane, not the pipelined binary32 instances): many small
+    // waves, batches of 2, which measured faster (fp16, µs, batch 8 / 2):
+    // 8192 tokens of 40 heads 33.2 / 29.7,
     // of 36 heads 30.7 / 26.8, of 64 heads 50.8 / 45.7; 16384 tokens of 32
     // heads 49.9 / 45.5; Q+K of 8192 tokens 33.4 / 30.0, of 16384 62.9 /
     // 56.5; a 4 x 2048-token prompt with cache append 40.2 / 35.2; M-RoPE of
     // 2 x 28 heads x 8192 tokens 43.3 / 41.5; packed [Q|K|V] of 8192 tokens
-    // 41.9 / 40.4. Launches of one round keep their batch (c2 23.0 / 24.5, c4
-    // 20.6 / 23.4); QK-norm (29.7 / 33.8) and coefficients on the fly (32.1 /
-    // 32.4) keep it too.
-    const bool many_small = es == 2 && !p.norm && p.coef != kCoefOnTheFly && best == 1 && !pipelined &&
+    // 41.9 / 40.4; interleaved pairs (two items per lane), 16384 tokens of 32
+    // heads 53.0 / 48.0; fp32 (batch 4 / 2) 8192 tokens of 32 heads 45.0 /
+    // 44.0, 16384 tokens 86.4 / 83.9. Launches of one round keep their batch
+    // (c2 23.0 / 24.5, c4 20.6 / 23.4, interleaved c2 23.5 / 25.8); QK-norm
+    // (29.7 / 33.8) and coefficients on the fly (32.1 / 32.4) keep it too.
+    const bool many_small = !p.norm && p.coef != kCoefOnTheFly && best <= 2 && !pipelined &&
                             over <= 0 && over_batch == 0 && hb > 2 && waves_at(hpw_cap) > kVecTargetWaves;
     if (many_small) g.head_batch = hb = hpw_cap = 2;
     const int64_t min_hpw = p.coef == kCoefMrope && waves_at(4) >= kVecMropeMinWaves ? 4 : 2;
