@@ -200,8 +200,35 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // (7.5 MiB) 4.32 / 4.37; at 8 MiB 4.78 / 4.32 (4 heads) and 4.39 / 4.27 (32
 // heads). M-RoPE (rank 4, 28 heads) turns earlier: 4.37 / 4.53 at 3.5 MiB,
 // 5.04 / 4.67 at 5.25 MiB.
+// Larger launches take the row kernel too where the vector kernel's items
+// fit the rows poorly: 2-byte types with a token's head rows adjacent and
+// together at least 1 KiB, not QK-norm and not M-RoPE, whose pairs are
+// interleaved, whose split halves are
+// shorter than 128 bytes, or that hold two tasks (Q+K) or the cache append.
+// Measured on MI355X (fp16, 8192 tokens, µs row / vector kernel, the vector
+// kernel in its best geometry of 2, 4 or 8 heads per wave): heads of 64, 64
+// heads 23.9 / 27.4; rotary_embedding_dim 64 of 128 24.0 / 27.2, 32 of 128
+// 23.8 / 31.7; interleaved pairs 22.5 / 23.4, heads of 64 22.5 / 25.3, of
+// 256 22.5 / 27.4; Q+K with a table 29.4 / 29.9, on the fly 29.7 / 32.0; a 4
+// x 2048-token prompt with the cache append 34.2 / 35.4; at 2048 tokens
+// heads of 64 6.66 / 7.19, rotary_embedding_dim 64 6.65 / 8.91, interleaved
+// 6.48 / 7.04. The vector kernel stays faster for split halves of 128 bytes
+// or more in one task (32 heads of 128: 22.8 / 23.9; 16 heads 11.6 / 13.3;
+// 32 heads of 256: 44.8 / 46.5), float32 data (44.2 / 46.5), M-RoPE (20.7 /
+// 24.5), packed [Q|K|V] (38.6 / 40.0) and QK-norm (30.1 / 30.6).
 static constexpr int64_t kRowMaxBytes = 6 << 20;
 static constexpr int64_t kRowMaxBytesMrope = 4 << 20;
+
+static bool row_kernel_fits_better(const Problem& p, int es) {
+    if (es != 2 || p.norm || p.coef == kCoefMrope) return false;
+    for (int t = 0; t < p.ntask; ++t) {
+        if (p.task[t].heads > 1 && p.task[t].stride_h != p.D) return false;  // head rows apart
+        // a token's rows fill at least one 1 KiB instruction of a wave
+        if (p.task[t].heads > 0 && p.task[t].heads * p.D * es < 1024) return false;
+    }
+    const int64_t half_bytes = (p.R / 2) * es;
+    return p.interleaved || half_bytes < 128 || p.ntask == 2 || p.coef == kCoefAppend;
+}
 
 static bool choose_row_geometry(Plan* pl) {
     Problem& p = pl->p;
@@ -217,7 +244,7 @@ static bool choose_row_geometry(Plan* pl) {
     int64_t xbytes = 0;
     for (int t = 0; t < p.ntask; ++t) xbytes += p.B * p.S * p.task[t].heads * row_bytes;
     const int64_t max_bytes = p.coef == kCoefMrope ? kRowMaxBytesMrope : kRowMaxBytes;
-    if (xbytes > max_bytes && policy != 3) return false;
+    if (xbytes > max_bytes && policy != 3 && !row_kernel_fits_better(p, es)) return false;
     const int RL = (int)(row_bytes / 16);
     const int rpi = 64 / RL;
     const int64_t ntok = p.B * p.S;
@@ -426,8 +453,13 @@ static void choose_geometry(Plan* pl) {
     // 44.0, 16384 tokens 86.4 / 83.9. Launches of one round keep their batch
     // (c2 23.0 / 24.5, c4 20.6 / 23.4, interleaved c2 23.5 / 25.8); QK-norm
     // (29.7 / 33.8) and coefficients on the fly (32.1 / 32.4) keep it too.
+    // 2-byte split halves longer than 128 bytes take batches of 2 at any
+    // size (heads of 256, 16 heads, 8192 tokens: 27.4 us in one round of 8
+    // heads per wave, 25.5 with 4, 24.2 with 2).
+    const bool wide_halves = es == 2 && !p.interleaved && p.coef != kCoefMrope && half * es > 128;
     const bool many_small = !p.norm && p.coef != kCoefOnTheFly && best <= 2 && !pipelined &&
-                            over <= 0 && over_batch == 0 && hb > 2 && waves_at(hpw_cap) > kVecTargetWaves;
+                            over <= 0 && over_batch == 0 && hb > 2 &&
+                            (waves_at(hpw_cap) > kVecTargetWaves || wide_halves);
     if (many_small) g.head_batch = hb = hpw_cap = 2;
     const int64_t min_hpw = p.coef == kCoefMrope && waves_at(4) >= kVecMropeMinWaves ? 4 : 2;
     while (hpw_cap / 2 >= min_hpw && waves_at(hpw_cap / 2) <= kVecTargetWaves) hpw_cap /= 2;

@@ -219,6 +219,33 @@ def test_row_kernel_selection_rules():
     assert check_rope(rope_case(D=64, dt=F32, R=32)) == (OK, "row16/gather")  # partial, 4 lanes apart
 
 
+def test_row_kernel_at_prefill_sizes():
+    """Above 6 MiB the row kernel still takes 2-byte launches whose rows the
+    vector kernel's items fit poorly (interleaved pairs, split halves under
+    128 bytes, Q+K, the cache append), when a token's head rows are adjacent
+    and fill at least 1 KiB; the vector kernel keeps the others."""
+    big = dict(B=1, S=8192, H=32, D=128)
+    assert check_rope(rope_case(**big)) == (OK, "vec16/gather")                         # halves of 128 B
+    assert check_rope(rope_case(interleaved=1, **big)) == (OK, "row16/gather")
+    assert check_rope(rope_case(dt=BF16, interleaved=1, **big)) == (OK, "row16/gather")
+    assert check_rope(rope_case(R=64, **big)) == (OK, "row16/gather")                    # halves of 64 B
+    assert check_rope(rope_case(B=1, S=8192, H=64, D=64)) == (OK, "row16/gather")
+    assert check_rope(rope_case(ids=False, interleaved=1, **big)) == (OK, "row16/per_token")
+    assert check_rope(rope_case(B=1, S=8192, H=16, D=256)) == (OK, "vec16/gather")       # halves of 256 B
+    assert check_rope(rope_case(dt=F32, interleaved=1, **big)) == (OK, "vec16/gather")   # 4-byte type
+    assert check_rope(rope_case(rank=4, interleaved=1, **big)) == (OK, "vec16/gather")   # head rows apart
+    assert check_rope(rope_case(B=1, S=1 << 16, H=2, D=64, interleaved=1)) == (OK, "vec16/gather")  # 256 B a token
+    assert check_rope(rope_case(B=1, S=8192, H=32, D=96)) == (OK, "vec16/gather")        # 192-byte rows
+    qk = dict(B=1, S=8192, H=32, Hk=8, M=8192)
+    assert check_qk(qk_case(D=128, **qk)) == (OK, "row16/gather")
+    assert check_qk(qk_case(D=128, table=False, **qk)) == (OK, "row16/on_the_fly")
+    assert check_norm(norm_case(shape=qk)) == (OK, "vec16/norm/gather")
+    assert check_packed(packed_case(D=128, **qk)) == (OK, "vec16/gather")
+    assert check_kv(kv_case(B=4, S=2048, Smax=4096, total=2048, H=32, Hk=8, D=128, M=8192)) == (OK, "row16/append")
+    m = dict(rank=4, B=1, H=32, D=128, M=64, section=(16, 24, 24))
+    assert check_mrope(mrope_case(S=8192, **m)) == (OK, "vec16/mrope")
+
+
 def test_huge_launches_take_the_scalar_kernel():
     """The vector and row kernels index in 32 bits: 2^31 tokens or more go to
     the grid-stride scalar kernel (no memory is touched by a check)."""

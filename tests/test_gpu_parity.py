@@ -198,6 +198,54 @@ def test_mid_size_launches(name, seq, heads, layout, onthefly):
         assert_bitwise(got[..., w.rotary_embedding_dim:], inputs[0][..., w.rotary_embedding_dim:], "tail")
 
 
+def _reshaped(name, head_size=None, heads=None, interleaved=None, rotary_dim=None):
+    """A rank-3 workload with another head size, head count, pairing or
+    rotary_embedding_dim (same seeds and recipe)."""
+    from dataclasses import replace
+    w = get_workload(name)
+    D = head_size or w.head_size
+    H = heads or w.num_heads
+    return replace(w, x_shape=(w.x_shape[0], w.x_shape[1], H * D), num_heads=H,
+                   interleaved=w.interleaved if interleaved is None else interleaved,
+                   rotary_embedding_dim=w.rotary_embedding_dim if rotary_dim is None else rotary_dim,
+                   name="%s_d%d_h%d_il%s_r%s" % (name, D, H, interleaved, rotary_dim))
+
+
+@pytest.mark.parametrize("head_size,heads,interleaved,rotary_dim,dtype", [
+    (64, 64, 0, None, None),        # split halves of 64 bytes: the row kernel
+    (64, 64, 1, None, None),        # interleaved pairs: the row kernel
+    (128, 32, 1, None, None),
+    (128, 32, 1, None, "bf16"),
+    (128, 32, 0, 64, None),         # partial rotation: the row kernel, tail copied
+    (128, 32, 0, 32, None),
+    (256, 16, 0, None, None),       # split halves of 256 bytes: the vector kernel, batches of 2
+])
+def test_prefill_head_shapes(head_size, heads, interleaved, rotary_dim, dtype):
+    """8192-token fp16/bf16 prefills with other head sizes, pairings and
+    rotary dims, each in the kernel and geometry the planner gives it,
+    against the oracle at full size."""
+    w = _reshaped("c2_rope_f16_prefill", head_size, heads, interleaved, rotary_dim)
+    if dtype == "bf16":
+        w = with_dtype(w, BFLOAT16, "bf16")
+    log("prefill head shape %s" % w.name)
+    got, want, inputs = run_workload(w)
+    log("%s %s" % (w.name, assert_parity(got, want, w.name)))
+    if w.rotary_embedding_dim:
+        rows = (w.batch, w.seq, w.num_heads, w.head_size)   # rank 3: heads side by side
+        R = w.rotary_embedding_dim
+        assert_bitwise(got.reshape(rows)[..., R:], inputs[0].reshape(rows)[..., R:], "tail")
+
+
+def test_qk_on_the_fly_prefill_size():
+    """Q+K with coefficients on the fly over 8192 tokens (the row kernel at
+    prefill size), against the oracle."""
+    w = _resized("c5_rope_qk_f16_decode", 32, None)
+    log("Q+K on the fly %s" % w.name)
+    got, want, _ = run_workload(w, onthefly=True)
+    log("%s Q %s K %s" % (w.name, assert_parity(got[0], want[0], w.name + " Q"),
+                          assert_parity(got[1], want[1], w.name + " K")))
+
+
 # the same workloads stored in bfloat16 (same seeds and shapes)
 
 @pytest.mark.parametrize("name,variant", [
