@@ -82,9 +82,11 @@ struct KArgs {
     float eps;                  // QK-norm epsilon
     float inv_d;                // QK-norm: 1/D rounded to binary32
     int32_t share_coef;         // on the fly: the waves of a workgroup split the slots
-    int32_t row_lanes;          // row kernel: lanes per head row (a power of two)
-    int32_t row_shift;          // log2(row_lanes)
+    int32_t row_lanes;          // row kernel: lanes per head row
+    int32_t row_shift;          // log2(row_lanes) (rows of a power-of-two size)
     int32_t half_lanes;         // row kernel, split halves: lanes between partner chunks
+    int32_t row_rpi;            // row kernel, other row sizes: head rows per instruction
+    uint32_t row_m;             // ... and ceil(2^16 / row_lanes): lane / row_lanes as a multiply-shift
     uint32_t w_m, w_s, s_m, s_s;  // division by W and by S (multiply-high and shift)
     // group_major: per token group the chunks of task 0, then 1, then 2
     // (c0, c0 + c1 and c0 + c1 + c2 chunks), and the division by the last
@@ -941,9 +943,10 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Row kernel, for head rows whose byte size is a power of two up to 1 KiB,
-// coefficients gathered by id, per token, M-RoPE-assembled, on the fly or at
-// the cache-append position; the planner uses it for decode-sized launches. The lanes of a
+// Row kernel, for head rows of 32 bytes to 1 KiB, coefficients gathered by
+// id, per token, M-RoPE-assembled, on the fly or at the cache-append
+// position; the planner uses it for decode-sized launches and for larger ones
+// whose rows the vector kernel's items fit poorly. The lanes of a
 // wave hold consecutive 16-byte chunks of consecutive head rows of one
 // token: lane l has chunk l % row_lanes of head l / row_lanes, and load u of
 // the wave covers the next 64 / row_lanes heads (with a token's heads
@@ -956,9 +959,15 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 // vector kernel streams faster.
 //   split halves: chunk c < half_lanes holds first elements, its partner
 //   (R/2 elements later) is chunk c + half_lanes of the same row, i.e. the
-//   lane half_lanes away (a power of two), fetched by a cross-lane move;
+//   lane half_lanes away, fetched by a cross-lane move;
 //   interleaved: whole pairs inside the chunk; chunks from the rotated
 //   prefix on are copied (or, with the QK-norm, store z).
+// Rows of a power-of-two size (GEN = 0) take lane l as chunk l % row_lanes
+// of row l / row_lanes by shift and mask, and partners a power of two of
+// lanes apart by DPP or an XOR permute. Other rows (GEN = 1: 16-byte chunks,
+// row_lanes up to 64; not the QK-norm, not M-RoPE) take 64 / row_lanes rows
+// per instruction, the remaining lanes idle, the row and chunk by a
+// multiply-shift, and each lane's partner by a permute from lane l +- half_lanes.
 // The chunk of lane (lane ^ d), d a power of two < 64 (uniform): DPP row
 // permutes for d = 1, 2, 4, 8 (4: a quad reverse, i -> i ^ 3, then the
 // half-row mirror, i -> i ^ 7), a permute through the LDS crossbar for 16 and
@@ -995,6 +1004,14 @@ __device__ inline u32x4 chunk_xor(const u32x4& v, int d) {
     return r;
 }
 
+// The chunk of lane src (any lane of the wave; every lane takes part).
+__device__ inline u32x4 chunk_from(const u32x4& v, int src) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = (uint32_t)__shfl((int)v[k], src);
+    return r;
+}
+
 // A wave-uniform 64-bit value placed in scalar registers.
 __device__ inline int64_t uniform64(int64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -1002,8 +1019,9 @@ __device__ inline int64_t uniform64(int64_t v) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-template <typename T, int IL, int COEF, bool NORM, int NT = kMaxTasks>
+template <typename T, int IL, int COEF, bool NORM, int NT = kMaxTasks, int GEN = 0>
 __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
+    static_assert(!GEN || (!NORM && COEF != kCoefMrope), "rows of other sizes: no QK-norm, no M-RoPE");
     constexpr int E = Elem<T>::E;
     constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation chunk
     constexpr int ES = (int)sizeof(T);
@@ -1025,9 +1043,12 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
     const bool live = nw < (uint64_t)a.ntok;
     if (COEF == kCoefAppend && !live) return;
     const uint32_t n32 = live ? nw : (uint32_t)(a.ntok - 1);
-    const int rpi = 64 >> a.row_shift;  // head rows per instruction
-    const int hi = lane >> a.row_shift;
-    const int c = lane & (a.row_lanes - 1);
+    // head rows per instruction; the lane's row and chunk (GEN: lanes past
+    // the last whole row idle)
+    const int rpi = GEN ? a.row_rpi : 64 >> a.row_shift;
+    const int hi = GEN ? (int)(((uint32_t)lane * a.row_m) >> 16) : lane >> a.row_shift;
+    const int c = GEN ? lane - hi * a.row_lanes : lane & (a.row_lanes - 1);
+    const bool lane_ok = !GEN || hi < rpi;
     const int h0 = part * tk.hpw;
     const int nh = min(tk.heads - h0, tk.hpw);
     const uint32_t b32 = fast_div(n32, a.s_m, a.s_s);
@@ -1086,14 +1107,14 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
 #pragma unroll
     for (int u = 0; u < kRowLoads; ++u) {
         in[u] = u32x4{0u, 0u, 0u, 0u};
-        if (u * rpi + hi < nh) in[u] = load_nt(px + u * xstep);
+        if (lane_ok && u * rpi + hi < nh) in[u] = load_nt(px + u * xstep);
     }
 
     const bool rotate = valid && !tk.copy;  // wave-uniform
     const bool rotc = c < a.NP;            // a chunk of the rotated prefix
     const int dl = a.half_lanes;
     const bool lower = !IL && c < dl;      // split halves: the first element of its pairs
-    const int slot0 = !rotc ? 0 : (IL ? c * CE : (c & (dl - 1)) * E);
+    const int slot0 = !rotc ? 0 : (IL ? c * CE : (GEN ? (lower ? c : c - dl) : (c & (dl - 1))) * E);
     float cf[CE], sf[CE];  // split halves: sf carries the sign of the lane's half
 #pragma unroll
     for (int j = 0; j < CE; ++j) { cf[j] = 1.0f; sf[j] = 0.0f; }
@@ -1210,8 +1231,11 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
 #pragma unroll
     for (int u = 0; u < kRowLoads; ++u) {
         if (u * rpi >= nh) break;
-        const bool act = u * rpi + hi < nh;
-        const u32x4 pv = !IL && rotate ? chunk_xor(in[u], dl) : in[u];  // split halves: the partner chunk
+        const bool act = lane_ok && u * rpi + hi < nh;
+        // split halves: the partner chunk
+        u32x4 pv = in[u];
+        if (!IL && rotate)
+            pv = GEN ? chunk_from(in[u], rotc && lane_ok ? (lower ? lane + dl : lane - dl) : lane) : chunk_xor(in[u], dl);
         u32x4 o = in[u];
         const auto xv = chunk_values<T>(in[u]);
         const auto pvv = chunk_values<T>(pv);
@@ -1473,34 +1497,39 @@ inline hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, d
 }
 
 template <typename T, int IL>
-inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream_t st, bool norm) {
+inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream_t st, bool norm, bool gen) {
     void* args[] = {const_cast<KArgs*>(&a)};
     const void* fn;
     // QK-norm launches hold Q and K; the cache append Q, K and V; M-RoPE one
-    // task; the others one (RotaryEmbedding), two (Q+K) or three (packed)
-#define ROPE_ROW(K)                                                                      \
-    (norm ? (a.ntask == 2 ? (const void*)rope_row_kernel<T, IL, K, true, 2> : nullptr)   \
-          : (a.ntask == 1   ? (const void*)rope_row_kernel<T, IL, K, false, 1>           \
-             : a.ntask == 2 ? (const void*)rope_row_kernel<T, IL, K, false, 2>           \
-             : a.ntask == 3 ? (const void*)rope_row_kernel<T, IL, K, false, 3>           \
-                            : nullptr))
+    // task; the others one (RotaryEmbedding), two (Q+K) or three (packed).
+    // Rows of other sizes (gen): no QK-norm, no M-RoPE.
+#define ROPE_ROW_NT(K, G)                                                          \
+    (a.ntask == 1   ? (const void*)rope_row_kernel<T, IL, K, false, 1, G>          \
+     : a.ntask == 2 ? (const void*)rope_row_kernel<T, IL, K, false, 2, G>          \
+     : a.ntask == 3 ? (const void*)rope_row_kernel<T, IL, K, false, 3, G>          \
+                    : nullptr)
+#define ROPE_ROW(K)                                                                            \
+    (norm ? (gen || a.ntask != 2 ? nullptr : (const void*)rope_row_kernel<T, IL, K, true, 2>) \
+          : (gen ? ROPE_ROW_NT(K, 1) : ROPE_ROW_NT(K, 0)))
     switch (c) {
         case kCoefGather: fn = ROPE_ROW(kCoefGather); break;
         case kCoefPerToken: fn = ROPE_ROW(kCoefPerToken); break;
         case kCoefOnTheFly: fn = ROPE_ROW(kCoefOnTheFly); break;
         case kCoefAppend:
-            if (a.ntask != 3) return hipErrorInvalidValue;
-            fn = norm ? (const void*)rope_row_kernel<T, IL, kCoefAppend, true, 3>
-                      : (const void*)rope_row_kernel<T, IL, kCoefAppend, false, 3>;
+            if (a.ntask != 3 || (gen && norm)) return hipErrorInvalidValue;
+            fn = norm  ? (const void*)rope_row_kernel<T, IL, kCoefAppend, true, 3>
+                 : gen ? (const void*)rope_row_kernel<T, IL, kCoefAppend, false, 3, 1>
+                       : (const void*)rope_row_kernel<T, IL, kCoefAppend, false, 3>;
             break;
         case kCoefMrope:
-            if (norm || a.ntask != 1) return hipErrorInvalidValue;
+            if (norm || gen || a.ntask != 1) return hipErrorInvalidValue;
             fn = (const void*)rope_row_kernel<T, IL, kCoefMrope, false, 1>;
             break;
         default: return hipErrorInvalidValue;
     }
     if (!fn) return hipErrorInvalidValue;
 #undef ROPE_ROW
+#undef ROPE_ROW_NT
     return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
 }
 
@@ -1541,8 +1570,10 @@ hipError_t launch_vector_for(const KArgs& a, CoefKind c, int interleaved, int ip
 }
 
 template <typename T>
-hipError_t launch_row_for(const KArgs& a, CoefKind c, int interleaved, dim3 grid, hipStream_t st, bool norm) {
-    return interleaved ? launch_row_il<T, 1>(a, c, grid, st, norm) : launch_row_il<T, 0>(a, c, grid, st, norm);
+hipError_t launch_row_for(const KArgs& a, CoefKind c, int interleaved, dim3 grid, hipStream_t st, bool norm,
+                          bool gen) {
+    return interleaved ? launch_row_il<T, 1>(a, c, grid, st, norm, gen)
+                       : launch_row_il<T, 0>(a, c, grid, st, norm, gen);
 }
 
 template <typename T>
@@ -1563,7 +1594,7 @@ hipError_t launch_table_for(const float* inv, void* cos, void* sin, int64_t rows
     EXT template hipError_t launch_vector_for<T>(const KArgs&, CoefKind, int, int, int, dim3,      \
                                                  hipStream_t, bool);
 #define ROPE_ROW_ENTRY_POINTS(EXT, T)                                                              \
-    EXT template hipError_t launch_row_for<T>(const KArgs&, CoefKind, int, dim3, hipStream_t, bool); \
+    EXT template hipError_t launch_row_for<T>(const KArgs&, CoefKind, int, dim3, hipStream_t, bool, bool); \
     EXT template hipError_t launch_scalar_for<T>(const KArgs&, CoefKind, int64_t, hipStream_t, bool); \
     EXT template hipError_t launch_table_for<T>(const float*, void*, void*, int64_t, int64_t, float, \
                                                 dim3, hipStream_t);

@@ -111,6 +111,8 @@ int launch_plan(const Plan& pl, void* stream) {
     a.row_shift = 0;
     while ((1 << a.row_shift) < a.row_lanes) ++a.row_shift;
     a.half_lanes = g.row_kernel ? g.half_lanes : 0;
+    a.row_rpi = 64 / a.row_lanes;
+    a.row_m = (uint32_t)((65536 + a.row_lanes - 1) / a.row_lanes);
     fast_div_magic(a.W > 0 ? a.W : 1, &a.w_m, &a.w_s);
     fast_div_magic(a.S > 0 ? a.S : 1, &a.s_m, &a.s_s);
     a.inv_d = 1.0f / (float)p.D;
@@ -129,10 +131,12 @@ int launch_plan(const Plan& pl, void* stream) {
         const dim3 grid((unsigned)blocks);
         const int ipl = g.items_per_lane;
         const int hu = g.head_batch;
-        if (g.row_kernel)
-            e = p.dtype == ROPE_FLOAT16    ? launch_row_for<half_t>(a, p.coef, p.interleaved, grid, st, p.norm)
-                : p.dtype == ROPE_BFLOAT16 ? launch_row_for<bf16_t>(a, p.coef, p.interleaved, grid, st, p.norm)
-                                           : launch_row_for<float>(a, p.coef, p.interleaved, grid, st, p.norm);
+        if (g.row_kernel) {
+            const bool gen = g.row_general != 0;
+            e = p.dtype == ROPE_FLOAT16    ? launch_row_for<half_t>(a, p.coef, p.interleaved, grid, st, p.norm, gen)
+                : p.dtype == ROPE_BFLOAT16 ? launch_row_for<bf16_t>(a, p.coef, p.interleaved, grid, st, p.norm, gen)
+                                           : launch_row_for<float>(a, p.coef, p.interleaved, grid, st, p.norm, gen);
+        }
         else if (p.dtype == ROPE_FLOAT16)
             e = launch_vector_for<half_t>(a, p.coef, p.interleaved, ipl, hu, grid, st, p.norm);
         else if (p.dtype == ROPE_BFLOAT16)

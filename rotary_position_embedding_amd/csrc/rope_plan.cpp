@@ -181,10 +181,11 @@ static const TuningOverrides& overrides() {
 static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 // Row kernel (rope_device.hpp): lanes along the head rows of one token, for
-// head rows of a power-of-two byte size from 32 bytes to 1 KiB, split-half
-// partners a power of two of lanes apart, coefficients gathered, per token,
-// M-RoPE-assembled, on the fly or at the cache-append position. Used for
-// launches that read at
+// head rows of 32 bytes to 1 KiB (rows of other than a power-of-two size, or
+// split-half partners other than a power of two of lanes apart, in its
+// general instances: not QK-norm, not M-RoPE), coefficients gathered, per
+// token, M-RoPE-assembled, on the fly or at the cache-append position. Used
+// for launches that read at
 // most kRowMaxBytes of activations (decode steps): there its short per-wave
 // dependence chain (one wave-uniform position, at most kRowLoads loads per
 // lane) makes the launch 0.5-0.7 us shorter than the vector kernel's
@@ -202,9 +203,10 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // 5.04 / 4.67 at 5.25 MiB.
 // Larger launches take the row kernel too where the vector kernel's items
 // fit the rows poorly: 2-byte types with a token's head rows adjacent and
-// together at least 1 KiB, not QK-norm and not M-RoPE, whose pairs are
-// interleaved, whose split halves are
-// shorter than 128 bytes, or that hold two tasks (Q+K) or the cache append.
+// together at least 1 KiB, not QK-norm and not M-RoPE, whose rows are not a
+// power of two in size (or partners not a power of two of lanes apart),
+// whose pairs are interleaved, whose split halves are shorter than 128
+// bytes, or that hold two tasks (Q+K) or the cache append.
 // Measured on MI355X (fp16, 8192 tokens, µs row / vector kernel, the vector
 // kernel in its best geometry of 2, 4 or 8 heads per wave): heads of 64, 64
 // heads 23.9 / 27.4; rotary_embedding_dim 64 of 128 24.0 / 27.2, 32 of 128
@@ -212,14 +214,16 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // 256 22.5 / 27.4; Q+K with a table 29.4 / 29.9, on the fly 29.7 / 32.0; a 4
 // x 2048-token prompt with the cache append 34.2 / 35.4; at 2048 tokens
 // heads of 64 6.66 / 7.19, rotary_embedding_dim 64 6.65 / 8.91, interleaved
-// 6.48 / 7.04. The vector kernel stays faster for split halves of 128 bytes
+// 6.48 / 7.04; rows of 160 bytes (rotary_embedding_dim 32) 16.5 / 31.4,
+// of 192 bytes 19.1 / 24.7, interleaved 19.0 / 20.1, of 384 bytes 18.5 /
+// 20.1 (16 heads). The vector kernel stays faster for split halves of 128 bytes
 // or more in one task (32 heads of 128: 22.8 / 23.9; 16 heads 11.6 / 13.3;
 // 32 heads of 256: 44.8 / 46.5), float32 data (44.2 / 46.5), M-RoPE (20.7 /
 // 24.5), packed [Q|K|V] (38.6 / 40.0) and QK-norm (30.1 / 30.6).
 static constexpr int64_t kRowMaxBytes = 6 << 20;
 static constexpr int64_t kRowMaxBytesMrope = 4 << 20;
 
-static bool row_kernel_fits_better(const Problem& p, int es) {
+static bool row_kernel_fits_better(const Problem& p, int es, bool general) {
     if (es != 2 || p.norm || p.coef == kCoefMrope) return false;
     for (int t = 0; t < p.ntask; ++t) {
         if (p.task[t].heads > 1 && p.task[t].stride_h != p.D) return false;  // head rows apart
@@ -227,7 +231,7 @@ static bool row_kernel_fits_better(const Problem& p, int es) {
         if (p.task[t].heads > 0 && p.task[t].heads * p.D * es < 1024) return false;
     }
     const int64_t half_bytes = (p.R / 2) * es;
-    return p.interleaved || half_bytes < 128 || p.ntask == 2 || p.coef == kCoefAppend;
+    return general || p.interleaved || half_bytes < 128 || p.ntask == 2 || p.coef == kCoefAppend;
 }
 
 static bool choose_row_geometry(Plan* pl) {
@@ -238,13 +242,16 @@ static bool choose_row_geometry(Plan* pl) {
     if (p.coef == kCoefOnTheFly && p.R / 2 > kRowMaxSlots) return false;
     const int es = elem_size(p.dtype);
     const int64_t row_bytes = p.D * es;
-    if (!pow2(row_bytes) || row_bytes < 32 || row_bytes > 1024) return false;
+    if (row_bytes % 16 != 0 || row_bytes < 32 || row_bytes > 1024) return false;
     const int64_t dl = p.interleaved ? 0 : (p.R / 2) * es / 16;
-    if (!p.interleaved && !pow2(dl)) return false;
+    // rows of other sizes, or partners a number of lanes apart other than a
+    // power of two: the kernel's general instances (no QK-norm, no M-RoPE)
+    const bool general = !pow2(row_bytes) || (!p.interleaved && !pow2(dl));
+    if (general && (p.norm || p.coef == kCoefMrope)) return false;
     int64_t xbytes = 0;
     for (int t = 0; t < p.ntask; ++t) xbytes += p.B * p.S * p.task[t].heads * row_bytes;
     const int64_t max_bytes = p.coef == kCoefMrope ? kRowMaxBytesMrope : kRowMaxBytes;
-    if (xbytes > max_bytes && policy != 3 && !row_kernel_fits_better(p, es)) return false;
+    if (xbytes > max_bytes && policy != 3 && !row_kernel_fits_better(p, es, general)) return false;
     const int RL = (int)(row_bytes / 16);
     const int rpi = 64 / RL;
     const int64_t ntok = p.B * p.S;
@@ -283,6 +290,7 @@ static bool choose_row_geometry(Plan* pl) {
     // the kernel's index arithmetic is 32-bit
     if (total_waves > INT32_MAX || ntok > INT32_MAX) return false;
     g.row_kernel = 1;
+    g.row_general = general ? 1 : 0;
     g.row_lanes = RL;
     g.half_lanes = (int32_t)dl;
     g.NP = (int32_t)(p.R * es / 16);  // chunks of the rotated prefix
@@ -332,6 +340,7 @@ static void choose_geometry(Plan* pl) {
     g.vector = ok;
     g.variant = variant_name(ok, p.coef, p.norm != 0);
     g.row_kernel = 0;
+    g.row_general = 0;
     g.group_major = 0;
     if (!ok) return;
     if (choose_row_geometry(pl)) {

@@ -90,6 +90,8 @@ struct Geometry {
     int32_t group_major;  // three tasks: waves in token-group order (see KArgs)
     int32_t row_kernel;   // 1: the row kernel (lanes along head rows of one token)
     int32_t row_lanes;    // row kernel: lanes per head row
+    int32_t row_general;  // row kernel: rows of a size other than a power of two, or partners
+                          // a number of lanes apart other than a power of two
     int32_t half_lanes;   // row kernel, split halves: lanes between partner chunks
     int32_t heads_per_wave[kMaxPlanTasks];
     int32_t chunks[kMaxPlanTasks];  // head chunks per token group

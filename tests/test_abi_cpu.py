@@ -170,7 +170,9 @@ def test_rope_variants_accepted(rank, ids, dt):
 def test_rope_partial_interleaved_accepted():
     for il in (0, 1):
         rc, v = check_rope(rope_case(rank=4, dt=F32, D=96, R=64, interleaved=il))
-        assert rc == OK and v == "vec16/gather"
+        assert rc == OK and v == "row16/gather"        # 384-byte rows: the row kernel's general rows
+        assert with_policy(2, check_rope, rope_case(rank=4, dt=F32, D=96, R=64, interleaved=il)) == (
+            OK, "vec16/gather")
 
 
 def test_rope_scalar_path_for_unaligned_shapes():
@@ -199,9 +201,10 @@ def test_kernel_policy_forces_scalar():
 
 def test_row_kernel_selection_rules():
     """The row kernel: decode-sized launches (<= 6 MiB of activations read,
-    <= 4 MiB for M-RoPE), head rows of a power-of-two size from 32 B to 1 KiB,
-    split-half partners a power of two of lanes apart. Policy 3 lifts the size
-    rule."""
+    <= 4 MiB for M-RoPE), head rows of 16-byte chunks from 32 B to 1 KiB (rows
+    of other than a power-of-two size, or split-half partners other than a
+    power of two of lanes apart, not with QK-norm or M-RoPE). Policy 3 lifts
+    the size rule."""
     big = dict(B=1, S=8192, H=32, D=128)                        # 64 MiB of fp16 X
     assert check_rope(rope_case(**big)) == (OK, "vec16/gather")
     assert with_policy(3, check_rope, rope_case(**big)) == (OK, "row16/gather")
@@ -210,8 +213,10 @@ def test_row_kernel_selection_rules():
     m = dict(rank=4, B=1, H=32, D=128, M=64, section=(16, 24, 24))
     assert check_mrope(mrope_case(S=512, **m)) == (OK, "row16/mrope")               # 4 MiB
     assert check_mrope(mrope_case(S=513, **m)) == (OK, "vec16/mrope")
-    assert check_rope(rope_case(D=96)) == (OK, "vec16/gather")            # 192-byte rows
-    assert check_rope(rope_case(D=128, R=96)) == (OK, "vec16/gather")     # partners 6 lanes apart
+    assert check_rope(rope_case(D=96)) == (OK, "row16/gather")            # 192-byte rows
+    assert check_rope(rope_case(D=128, R=96)) == (OK, "row16/gather")     # partners 6 lanes apart
+    assert check_mrope(mrope_case(S=4, rank=4, B=1, H=4, D=96, M=64, section=(16, 16, 16))) == (
+        OK, "vec16/mrope")                                                # no M-RoPE on general rows
     assert check_rope(rope_case(D=128, R=96, interleaved=1)) == (OK, "row16/gather")
     assert check_rope(rope_case(D=1024)) == (OK, "vec16/gather")          # 2 KiB rows
     assert check_rope(rope_case(D=8, dt=F16, interleaved=1)) == (OK, "vec16/gather")  # 16-byte rows
@@ -235,7 +240,9 @@ def test_row_kernel_at_prefill_sizes():
     assert check_rope(rope_case(dt=F32, interleaved=1, **big)) == (OK, "vec16/gather")   # 4-byte type
     assert check_rope(rope_case(rank=4, interleaved=1, **big)) == (OK, "vec16/gather")   # head rows apart
     assert check_rope(rope_case(B=1, S=1 << 16, H=2, D=64, interleaved=1)) == (OK, "vec16/gather")  # 256 B a token
-    assert check_rope(rope_case(B=1, S=8192, H=32, D=96)) == (OK, "vec16/gather")        # 192-byte rows
+    assert check_rope(rope_case(B=1, S=8192, H=32, D=96)) == (OK, "row16/gather")        # 192-byte rows
+    assert check_rope(rope_case(B=1, S=8192, H=16, D=192)) == (OK, "row16/gather")       # 384-byte rows
+    assert check_rope(rope_case(B=1, S=8192, H=32, D=96, dt=F32)) == (OK, "vec16/gather")
     qk = dict(B=1, S=8192, H=32, Hk=8, M=8192)
     assert check_qk(qk_case(D=128, **qk)) == (OK, "row16/gather")
     assert check_qk(qk_case(D=128, table=False, **qk)) == (OK, "row16/on_the_fly")

@@ -219,6 +219,9 @@ def _reshaped(name, head_size=None, heads=None, interleaved=None, rotary_dim=Non
     (128, 32, 0, 64, None),         # partial rotation: the row kernel, tail copied
     (128, 32, 0, 32, None),
     (256, 16, 0, None, None),       # split halves of 256 bytes: the vector kernel, batches of 2
+    (96, 32, 0, None, None),        # 192-byte rows, partners 6 lanes apart: the row kernel's general rows
+    (96, 32, 1, None, None),
+    (80, 32, 0, 32, None),          # 160-byte rows, rotary dim 32
 ])
 def test_prefill_head_shapes(head_size, heads, interleaved, rotary_dim, dtype):
     """8192-token fp16/bf16 prefills with other head sizes, pairings and
