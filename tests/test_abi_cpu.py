@@ -226,9 +226,11 @@ def test_row_kernel_selection_rules():
 
 def test_row_kernel_at_prefill_sizes():
     """Above 6 MiB the row kernel still takes 2-byte launches whose rows the
-    vector kernel's items fit poorly (interleaved pairs, split halves under
-    128 bytes, Q+K, the cache append), when a token's head rows are adjacent
-    and fill at least 1 KiB; the vector kernel keeps the others."""
+    vector kernel's items fit poorly (a token's head rows filling at least
+    1 KiB): with the rows adjacent, rows of other than a power-of-two size,
+    interleaved pairs, split halves under 128 bytes, Q+K and the cache
+    append; with the rows apart (rank 4), power-of-two rows with interleaved
+    pairs or short halves. The vector kernel keeps the others."""
     big = dict(B=1, S=8192, H=32, D=128)
     assert check_rope(rope_case(**big)) == (OK, "vec16/gather")                         # halves of 128 B
     assert check_rope(rope_case(interleaved=1, **big)) == (OK, "row16/gather")
@@ -238,7 +240,11 @@ def test_row_kernel_at_prefill_sizes():
     assert check_rope(rope_case(ids=False, interleaved=1, **big)) == (OK, "row16/per_token")
     assert check_rope(rope_case(B=1, S=8192, H=16, D=256)) == (OK, "vec16/gather")       # halves of 256 B
     assert check_rope(rope_case(dt=F32, interleaved=1, **big)) == (OK, "vec16/gather")   # 4-byte type
-    assert check_rope(rope_case(rank=4, interleaved=1, **big)) == (OK, "vec16/gather")   # head rows apart
+    assert check_rope(rope_case(rank=4, **big)) == (OK, "vec16/gather")                 # rank 4: halves of 128 B
+    assert check_rope(rope_case(rank=4, interleaved=1, **big)) == (OK, "row16/gather")   # rank 4, pow2 rows
+    assert check_rope(rope_case(rank=4, B=8, S=1024, H=32, D=64)) == (OK, "row16/gather")
+    assert check_rope(rope_case(rank=4, B=8, S=1024, H=32, D=96, R=64, interleaved=1)) == (
+        OK, "vec16/gather")                                                              # rank 4, 192-byte rows
     assert check_rope(rope_case(B=1, S=1 << 16, H=2, D=64, interleaved=1)) == (OK, "vec16/gather")  # 256 B a token
     assert check_rope(rope_case(B=1, S=8192, H=32, D=96)) == (OK, "row16/gather")        # 192-byte rows
     assert check_rope(rope_case(B=1, S=8192, H=16, D=192)) == (OK, "row16/gather")       # 384-byte rows

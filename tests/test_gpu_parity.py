@@ -239,6 +239,28 @@ def test_prefill_head_shapes(head_size, heads, interleaved, rotary_dim, dtype):
         assert_bitwise(got.reshape(rows)[..., R:], inputs[0].reshape(rows)[..., R:], "tail")
 
 
+@pytest.mark.parametrize("head_size,interleaved,rotary_dim", [
+    (64, 0, 0),       # rank 4, split halves of 64 bytes: the row kernel
+    (64, 1, 0),
+    (128, 1, 0),      # rank 4, interleaved: the row kernel
+    (128, 0, 64),
+    (96, 1, 64),      # rank 4, 192-byte rows: the vector kernel
+])
+def test_prefill_rank4_head_shapes(head_size, interleaved, rotary_dim):
+    """Rank-4 (8, 32, 1024, D) fp16 inputs in the kernel the planner gives
+    them, against the oracle at full size, tail bitwise."""
+    from dataclasses import replace
+    w = with_dtype(get_workload("c3_rope_f32_partial_interleaved"), np.float16, "f16")
+    xs = w.x_shape[:3] + (head_size,)
+    w = replace(w, x_shape=xs, interleaved=interleaved, rotary_embedding_dim=rotary_dim,
+                name="%s_d%d_il%d_r%d" % (w.name, head_size, interleaved, rotary_dim))
+    log("rank-4 prefill %s" % w.name)
+    got, want, inputs = run_workload(w)
+    log("%s %s" % (w.name, assert_parity(got, want, w.name)))
+    if rotary_dim:
+        assert_bitwise(got[..., rotary_dim:], inputs[0][..., rotary_dim:], "tail")
+
+
 def test_qk_on_the_fly_prefill_size():
     """Q+K with coefficients on the fly over 8192 tokens (the row kernel at
     prefill size), against the oracle."""
