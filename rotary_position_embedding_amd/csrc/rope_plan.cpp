@@ -202,13 +202,15 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // heads). M-RoPE (rank 4, 28 heads) turns earlier: 4.37 / 4.53 at 3.5 MiB,
 // 5.04 / 4.67 at 5.25 MiB.
 // Larger launches take the row kernel too where the vector kernel's items
-// fit the rows poorly: 2-byte types whose head rows make at least 1 KiB a
-// token, not QK-norm and not M-RoPE, with a token's head rows adjacent
-// (rank 3) and rows not a power of two in size (or partners not a power of
-// two of lanes apart), interleaved pairs, split halves shorter than 128
-// bytes, two tasks (Q+K) or the cache append; with head rows apart (rank 4),
-// rows of a power-of-two size with interleaved pairs or split halves
-// shorter than 128 bytes.
+// fit the rows poorly, for head rows making at least 1 KiB a token, not
+// M-RoPE: 2-byte types with a token's head rows adjacent (rank 3) and rows
+// not a power of two in size (or partners not a power of two of lanes
+// apart), interleaved pairs, split halves shorter than 128 bytes, two tasks
+// (Q+K) or the cache append; with head rows apart (rank 4), rows of a
+// power-of-two size with interleaved pairs or split halves shorter than 128
+// bytes; float32 rank 3 with rows of other sizes or a partial rotation of
+// split halves; QK-norm rank 3 in float32 or with 2-byte split halves longer
+// than 128 bytes.
 // Measured on MI355X (fp16, 8192 tokens, µs row / vector kernel, the vector
 // kernel in its best geometry of 2, 4 or 8 heads per wave): heads of 64, 64
 // heads 23.9 / 27.4; rotary_embedding_dim 64 of 128 24.0 / 27.2, 32 of 128
@@ -221,15 +223,23 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // 20.1 (16 heads); rank 4 (8 x 32 heads x 1024 tokens): heads of 128
 // interleaved 22.8 / 24.3, heads of 64 13.8 / 17.1 (interleaved 11.5 /
 // 14.1), rotary_embedding_dim 64 of 128 24.6 / 31.2, but rows of 192 bytes
-// (rotary_embedding_dim 64, interleaved) 21.2 / 18.3. The vector kernel stays faster for split halves of 128 bytes
+// (rotary_embedding_dim 64, interleaved) 21.2 / 18.3; float32: heads of 96
+// 35.3 / 36.4 (rotary_embedding_dim 64 interleaved 34.7 / 36.8), of 80 with
+// rotary_embedding_dim 32 31.2 / 34.9, rotary_embedding_dim 64 of 128 46.1 /
+// 52.6 (at 2048 tokens 12.5 / 15.9), 32 of 64 46.4 / 48.8; QK-norm with
+// heads of 256 58.0 / 63.2 (bf16 58.2 / 63.8), in float32 57.1 / 58.2 (heads
+// of 64: 29.3 / 30.0). The vector kernel stays faster for split halves of 128 bytes
 // or more in one task (32 heads of 128: 22.8 / 23.9; 16 heads 11.6 / 13.3;
-// 32 heads of 256: 44.8 / 46.5), float32 data (44.2 / 46.5), M-RoPE (20.7 /
-// 24.5), packed [Q|K|V] (38.6 / 40.0) and QK-norm (30.1 / 30.6).
+// 32 heads of 256: 44.8 / 46.5), float32 heads of 128 (44.2 / 46.5), M-RoPE (20.7 /
+// 24.5), packed [Q|K|V] (38.6 / 40.0), 2-byte QK-norm with heads of 128
+// (30.1 / 30.6), float32 rows of 256 or 512 bytes with full or interleaved
+// rotations (heads of 64 45.2 / 46.0, of 256 46.1 / 46.5, rotary_embedding_dim 64 of
+// 128 interleaved 46.5 / 47.5).
 static constexpr int64_t kRowMaxBytes = 6 << 20;
 static constexpr int64_t kRowMaxBytesMrope = 4 << 20;
 
 static bool row_kernel_fits_better(const Problem& p, int es, bool general) {
-    if (es != 2 || p.norm || p.coef == kCoefMrope) return false;
+    if (p.coef == kCoefMrope) return false;
     bool adjacent = true;
     for (int t = 0; t < p.ntask; ++t) {
         if (p.task[t].heads > 1 && p.task[t].stride_h != p.D) adjacent = false;  // rank 4
@@ -237,6 +247,11 @@ static bool row_kernel_fits_better(const Problem& p, int es, bool general) {
         if (p.task[t].heads > 0 && p.task[t].heads * p.D * es < 1024) return false;
     }
     const int64_t half_bytes = (p.R / 2) * es;
+    // QK-norm (rows of a power-of-two size): float32 data, or 2-byte split
+    // halves longer than 128 bytes
+    if (p.norm) return adjacent && (es == 4 || (!p.interleaved && half_bytes > 128));
+    // float32: rows of other sizes, or a partial rotation of split halves
+    if (es == 4) return adjacent && (general || (!p.interleaved && p.R < p.D));
     // head rows apart (rank 4): rows of a power-of-two size only
     if (!adjacent) return !general && (p.interleaved || half_bytes < 128);
     return general || p.interleaved || half_bytes < 128 || p.ntask == 2 || p.coef == kCoefAppend;

@@ -230,7 +230,9 @@ def test_row_kernel_at_prefill_sizes():
     1 KiB): with the rows adjacent, rows of other than a power-of-two size,
     interleaved pairs, split halves under 128 bytes, Q+K and the cache
     append; with the rows apart (rank 4), power-of-two rows with interleaved
-    pairs or short halves. The vector kernel keeps the others."""
+    pairs or short halves; float32 rows of other sizes or partial split
+    rotations; QK-norm in float32 or with halves over 128 bytes. The vector
+    kernel keeps the others."""
     big = dict(B=1, S=8192, H=32, D=128)
     assert check_rope(rope_case(**big)) == (OK, "vec16/gather")                         # halves of 128 B
     assert check_rope(rope_case(interleaved=1, **big)) == (OK, "row16/gather")
@@ -248,11 +250,16 @@ def test_row_kernel_at_prefill_sizes():
     assert check_rope(rope_case(B=1, S=1 << 16, H=2, D=64, interleaved=1)) == (OK, "vec16/gather")  # 256 B a token
     assert check_rope(rope_case(B=1, S=8192, H=32, D=96)) == (OK, "row16/gather")        # 192-byte rows
     assert check_rope(rope_case(B=1, S=8192, H=16, D=192)) == (OK, "row16/gather")       # 384-byte rows
-    assert check_rope(rope_case(B=1, S=8192, H=32, D=96, dt=F32)) == (OK, "vec16/gather")
+    assert check_rope(rope_case(B=1, S=8192, H=32, D=96, dt=F32)) == (OK, "row16/gather")  # float32
+    assert check_rope(rope_case(dt=F32, **big)) == (OK, "vec16/gather")
+    assert check_rope(rope_case(dt=F32, R=64, **big)) == (OK, "row16/gather")           # partial rotation
+    assert check_rope(rope_case(dt=F32, R=64, interleaved=1, **big)) == (OK, "vec16/gather")
     qk = dict(B=1, S=8192, H=32, Hk=8, M=8192)
     assert check_qk(qk_case(D=128, **qk)) == (OK, "row16/gather")
     assert check_qk(qk_case(D=128, table=False, **qk)) == (OK, "row16/on_the_fly")
     assert check_norm(norm_case(shape=qk)) == (OK, "vec16/norm/gather")
+    assert check_norm(norm_case(D=256, shape=qk)) == (OK, "row16/norm/gather")          # halves of 256 B
+    assert check_norm(norm_case(dt=F32, shape=qk)) == (OK, "row16/norm/gather")
     assert check_packed(packed_case(D=128, **qk)) == (OK, "vec16/gather")
     assert check_kv(kv_case(B=4, S=2048, Smax=4096, total=2048, H=32, Hk=8, D=128, M=8192)) == (OK, "row16/append")
     m = dict(rank=4, B=1, H=32, D=128, M=64, section=(16, 24, 24))

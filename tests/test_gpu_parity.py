@@ -222,6 +222,8 @@ def _reshaped(name, head_size=None, heads=None, interleaved=None, rotary_dim=Non
     (96, 32, 0, None, None),        # 192-byte rows, partners 6 lanes apart: the row kernel's general rows
     (96, 32, 1, None, None),
     (80, 32, 0, 32, None),          # 160-byte rows, rotary dim 32
+    (128, 32, 0, 64, "f32"),        # float32 partial rotation: the row kernel
+    (96, 32, 1, 64, "f32"),         # float32 384-byte rows
 ])
 def test_prefill_head_shapes(head_size, heads, interleaved, rotary_dim, dtype):
     """8192-token fp16/bf16 prefills with other head sizes, pairings and
@@ -230,6 +232,8 @@ def test_prefill_head_shapes(head_size, heads, interleaved, rotary_dim, dtype):
     w = _reshaped("c2_rope_f16_prefill", head_size, heads, interleaved, rotary_dim)
     if dtype == "bf16":
         w = with_dtype(w, BFLOAT16, "bf16")
+    elif dtype == "f32":
+        w = with_dtype(w, np.float32, "f32")
     log("prefill head shape %s" % w.name)
     got, want, inputs = run_workload(w)
     log("%s %s" % (w.name, assert_parity(got, want, w.name)))

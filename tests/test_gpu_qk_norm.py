@@ -120,11 +120,14 @@ def test_qk_norm_in_place():
     assert_parity_norm(host(kt), want[1], zmax_rows(k, wk, 1e-6, 3, Hk), "K in place")
 
 
-@pytest.mark.parametrize("dt", [np.float16, BFLOAT16])
-def test_qk_norm_prefill_full_size(dt):
-    """A Qwen3-like prefill: 4 x 2048 tokens, 32 query and 8 key heads of 128,
-    positions per-sequence offset + arange into a (8192, 64) table."""
-    B, S, H, Hk, D, M = 4, 2048, 32, 8, 128, 8192
+@pytest.mark.parametrize("dt,D,H,Hk", [(np.float16, 128, 32, 8), (BFLOAT16, 128, 32, 8),
+                                       (np.float16, 256, 16, 8),   # halves of 256 B: the row kernel
+                                       (np.float32, 128, 32, 8)])  # float32: the row kernel
+def test_qk_norm_prefill_full_size(dt, D, H, Hk):
+    """A Qwen3-like prefill: 4 x 2048 tokens, 32 query and 8 key heads of 128
+    (or 16 and 8 of 256), positions per-sequence offset + arange into a
+    (8192, D/2) table."""
+    B, S, M = 4, 2048, 8192
     q = normal_tensor(13200, (B, S, H * D), dt)
     k = normal_tensor(13201, (B, S, Hk * D), dt)
     wq, wk = weights(13202, D, dt), weights(13203, D, dt)
@@ -136,7 +139,7 @@ def test_qk_norm_prefill_full_size(dt):
                                     epsilon=1e-6, num_heads=H, kv_num_heads=Hk)
     rq = assert_parity_norm(host(gq), want_q, zmax_rows(q, wq, 1e-6, 3, H), "Q")
     rk = assert_parity_norm(host(gk), want_k, zmax_rows(k, wk, 1e-6, 3, Hk), "K")
-    print("prefill", np.dtype(dt).name, rq, rk, flush=True)
+    print("prefill", np.dtype(dt).name, D, rq, rk, flush=True)
 
 
 def test_qk_norm_decode_full_size():
