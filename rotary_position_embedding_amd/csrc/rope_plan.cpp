@@ -287,7 +287,13 @@ static bool choose_row_geometry(Plan* pl) {
     // (each wave computes its token's slots) 3.35 vs 3.47 with two
     // instructions per wave.
     const int64_t target_waves = 4096;
-    int loads = kRowLoads;
+    // Q+K past the decode sizes: 4 instructions per wave (fp16, heads of
+    // 128, µs with 8 / 4: 2048 tokens 7.96 / 7.51, 8192 tokens 29.4 / 28.5,
+    // on the fly 29.7 / 28.6, 16384 tokens 55.4 / 53.7; heads of 64 15.6 /
+    // 15.6); one-task launches keep 8 (interleaved heads of 128 22.5 / 24.2)
+    // and so does the prompt with the cache append (at 4 x 512 tokens 9.23 /
+    // 10.12)
+    int loads = p.ntask == 2 && !p.norm && xbytes > max_bytes ? 4 : kRowLoads;
     for (;;) {
         int64_t waves = 0;
         for (int t = 0; t < p.ntask; ++t) {
