@@ -220,7 +220,9 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // heads of 64 6.66 / 7.19, rotary_embedding_dim 64 6.65 / 8.91, interleaved
 // 6.48 / 7.04; rows of 160 bytes (rotary_embedding_dim 32) 16.5 / 31.4,
 // of 192 bytes 19.1 / 24.7, interleaved 19.0 / 20.1, of 384 bytes 18.5 /
-// 20.1 (16 heads); rank 4 (8 x 32 heads x 1024 tokens): heads of 128
+// 20.1 (16 heads), of 224, 320, 640 and 768 bytes (heads of 112, 160,
+// 320 and 384; the one of 640 bytes leaves 24 lanes idle) 21.2 / 33.0,
+// 16.6 / 23.0, 16.5 / 17.3, 18.6 / 21.7; rank 4 (8 x 32 heads x 1024 tokens): heads of 128
 // interleaved 22.8 / 24.3, heads of 64 13.8 / 17.1 (interleaved 11.5 /
 // 14.1), rotary_embedding_dim 64 of 128 24.6 / 31.2, but rows of 192 bytes
 // (rotary_embedding_dim 64, interleaved) 21.2 / 18.3; float32: heads of 96

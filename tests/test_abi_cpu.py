@@ -250,6 +250,7 @@ def test_row_kernel_at_prefill_sizes():
     assert check_rope(rope_case(B=1, S=1 << 16, H=2, D=64, interleaved=1)) == (OK, "vec16/gather")  # 256 B a token
     assert check_rope(rope_case(B=1, S=8192, H=32, D=96)) == (OK, "row16/gather")        # 192-byte rows
     assert check_rope(rope_case(B=1, S=8192, H=16, D=192)) == (OK, "row16/gather")       # 384-byte rows
+    assert check_rope(rope_case(B=1, S=8192, H=8, D=320)) == (OK, "row16/gather")        # 40 of 64 lanes busy
     assert check_rope(rope_case(B=1, S=8192, H=32, D=96, dt=F32)) == (OK, "row16/gather")  # float32
     assert check_rope(rope_case(dt=F32, **big)) == (OK, "vec16/gather")
     assert check_rope(rope_case(dt=F32, R=64, **big)) == (OK, "row16/gather")           # partial rotation
