@@ -209,8 +209,8 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // (Q+K) or the cache append; with head rows apart (rank 4), rows of a
 // power-of-two size with interleaved pairs or split halves shorter than 128
 // bytes; float32 rank 3 with rows of other sizes or a partial rotation of
-// split halves; QK-norm rank 3 in float32 or with 2-byte split halves longer
-// than 128 bytes.
+// split halves; QK-norm rank 3 in float32 or with 2-byte split halves of
+// other than 128 bytes.
 // Measured on MI355X (fp16, 8192 tokens, µs row / vector kernel, the vector
 // kernel in its best geometry of 2, 4 or 8 heads per wave): heads of 64, 64
 // heads 23.9 / 27.4; rotary_embedding_dim 64 of 128 24.0 / 27.2, 32 of 128
@@ -229,8 +229,9 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // 35.3 / 36.4 (rotary_embedding_dim 64 interleaved 34.7 / 36.8), of 80 with
 // rotary_embedding_dim 32 31.2 / 34.9, rotary_embedding_dim 64 of 128 46.1 /
 // 52.6 (at 2048 tokens 12.5 / 15.9), 32 of 64 46.4 / 48.8; QK-norm with
-// heads of 256 58.0 / 63.2 (bf16 58.2 / 63.8), in float32 57.1 / 58.2 (heads
-// of 64: 29.3 / 30.0). The vector kernel stays faster for split halves of 128 bytes
+// heads of 256 58.0 / 63.2 (bf16 58.2 / 63.8), with heads of 64 17.8 / 18.5
+// (8 or 2 heads per batch; 4: 21.2), in float32 57.1 / 58.2 (heads of 64:
+// 29.3 / 30.0). The vector kernel stays faster for split halves of 128 bytes
 // or more in one task (32 heads of 128: 22.8 / 23.9; 16 heads 11.6 / 13.3;
 // 32 heads of 256: 44.8 / 46.5), float32 heads of 128 (44.2 / 46.5), M-RoPE (20.7 /
 // 24.5), packed [Q|K|V] (38.6 / 40.0), 2-byte QK-norm with heads of 128
@@ -250,8 +251,8 @@ static bool row_kernel_fits_better(const Problem& p, int es, bool general) {
     }
     const int64_t half_bytes = (p.R / 2) * es;
     // QK-norm (rows of a power-of-two size): float32 data, or 2-byte split
-    // halves longer than 128 bytes
-    if (p.norm) return adjacent && (es == 4 || (!p.interleaved && half_bytes > 128));
+    // halves other than 128 bytes long
+    if (p.norm) return adjacent && (es == 4 || (!p.interleaved && half_bytes != 128));
     // float32: rows of other sizes, or a partial rotation of split halves
     if (es == 4) return adjacent && (general || (!p.interleaved && p.R < p.D));
     // head rows apart (rank 4): rows of a power-of-two size only

@@ -231,8 +231,8 @@ def test_row_kernel_at_prefill_sizes():
     interleaved pairs, split halves under 128 bytes, Q+K and the cache
     append; with the rows apart (rank 4), power-of-two rows with interleaved
     pairs or short halves; float32 rows of other sizes or partial split
-    rotations; QK-norm in float32 or with halves over 128 bytes. The vector
-    kernel keeps the others."""
+    rotations; QK-norm in float32 or with halves other than 128 bytes. The
+    vector kernel keeps the others."""
     big = dict(B=1, S=8192, H=32, D=128)
     assert check_rope(rope_case(**big)) == (OK, "vec16/gather")                         # halves of 128 B
     assert check_rope(rope_case(interleaved=1, **big)) == (OK, "row16/gather")
@@ -260,6 +260,7 @@ def test_row_kernel_at_prefill_sizes():
     assert check_qk(qk_case(D=128, table=False, **qk)) == (OK, "row16/on_the_fly")
     assert check_norm(norm_case(shape=qk)) == (OK, "vec16/norm/gather")
     assert check_norm(norm_case(D=256, shape=qk)) == (OK, "row16/norm/gather")          # halves of 256 B
+    assert check_norm(norm_case(D=64, shape=qk)) == (OK, "row16/norm/gather")           # halves of 64 B
     assert check_norm(norm_case(dt=F32, shape=qk)) == (OK, "row16/norm/gather")
     assert check_packed(packed_case(D=128, **qk)) == (OK, "vec16/gather")
     assert check_kv(kv_case(B=4, S=2048, Smax=4096, total=2048, H=32, Hk=8, D=128, M=8192)) == (OK, "row16/append")
