@@ -406,8 +406,10 @@ int rope_kv_append_qk_norm_check(const rope_tensor* query,
 
 /*
  * Kernel choice for all ops: 0 = automatic (the row kernel for decode-sized
- * launches, the vector kernel for larger ones, where shapes and alignment
- * allow; the scalar kernel otherwise), 1 = always the scalar kernel, 2 = the
+ * launches and for larger ones whose head rows the vector kernel's 16-byte
+ * items fit poorly, the vector kernel for the other larger ones, where shapes
+ * and alignment allow; the scalar kernel otherwise), 1 = always the scalar
+ * kernel, 2 = the
  * vector kernel wherever it applies (never the row kernel), 3 = the row
  * kernel wherever its shape rules allow, at any size. Any other value is
  * taken as 0. Process-wide; returns the previous value. Used to test every

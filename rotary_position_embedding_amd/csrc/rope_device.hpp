@@ -955,8 +955,11 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 // check and each lane's coefficient slice are the same for all of them: the
 // dependence chain of a wave is one scalar position load and one slice
 // gather, which is what makes small launches shorter than with the vector
-// kernel (whose lanes each hold another token). For large launches the
-// vector kernel streams faster.
+// kernel (whose lanes each hold another token). For large launches it reads
+// each token's rows whole, where the vector kernel's items would load
+// half-used lines or sparse partner instructions (short, interleaved or
+// odd-sized rows); for full split halves of 128 bytes or more the vector
+// kernel streams faster.
 //   split halves: chunk c < half_lanes holds first elements, its partner
 //   (R/2 elements later) is chunk c + half_lanes of the same row, i.e. the
 //   lane half_lanes away, fetched by a cross-lane move;

@@ -190,8 +190,9 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // dependence chain (one wave-uniform position, at most kRowLoads loads per
 // lane) makes the launch 0.5-0.7 us shorter than the vector kernel's
 // (fp16, 32 heads of 128: 2.7 vs 3.4 us at 64 tokens, 3.2 vs 3.7 at 256);
-// for large launches the vector kernel streams faster (23.6 vs 25.6 us at
-// 8192 tokens), both measured on MI355X in HIP-graph replay.
+// for large launches of heads of 128 with full split-half rotations the
+// vector kernel streams faster (22.8 vs 23.9 us at 8192 tokens), both
+// measured on MI355X.
 // A wave takes up to kRowLoads instructions of one token; smaller launches
 // take fewer per wave so that they spread over the chip.
 // Between 4 and 8 MiB (fp16, heads of 128, µs row / vector kernel): Q+K of
@@ -208,9 +209,9 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // apart), interleaved pairs, split halves shorter than 128 bytes, two tasks
 // (Q+K) or the cache append; with head rows apart (rank 4), rows of a
 // power-of-two size with interleaved pairs or split halves shorter than 128
-// bytes; float32 rank 3 with rows of other sizes or a partial rotation of
-// split halves; QK-norm rank 3 in float32 or with 2-byte split halves of
-// other than 128 bytes.
+// bytes; float32 rank 3 with rows of other sizes, a partial rotation of
+// split halves or coefficients on the fly; QK-norm rank 3 in float32 or with
+// 2-byte split halves of other than 128 bytes.
 // Measured on MI355X (fp16, 8192 tokens, µs row / vector kernel, the vector
 // kernel in its best geometry of 2, 4 or 8 heads per wave): heads of 64, 64
 // heads 23.9 / 27.4; rotary_embedding_dim 64 of 128 24.0 / 27.2, 32 of 128
@@ -228,7 +229,8 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // (rotary_embedding_dim 64, interleaved) 21.2 / 18.3; float32: heads of 96
 // 35.3 / 36.4 (rotary_embedding_dim 64 interleaved 34.7 / 36.8), of 80 with
 // rotary_embedding_dim 32 31.2 / 34.9, rotary_embedding_dim 64 of 128 46.1 /
-// 52.6 (at 2048 tokens 12.5 / 15.9), 32 of 64 46.4 / 48.8; QK-norm with
+// 52.6 (at 2048 tokens 12.5 / 15.9), 32 of 64 46.4 / 48.8, Q+K on the fly
+// 54.5 / 58.6 (with the table 54.3 / 54.9: kept); QK-norm with
 // heads of 256 58.0 / 63.2 (bf16 58.2 / 63.8), with heads of 64 17.8 / 18.5
 // (8 or 2 heads per batch; 4: 21.2), in float32 57.1 / 58.2 (heads of 64:
 // 29.3 / 30.0). The vector kernel stays faster for split halves of 128 bytes
@@ -237,7 +239,8 @@ static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 // 24.5), packed [Q|K|V] (38.6 / 40.0), 2-byte QK-norm with heads of 128
 // (30.1 / 30.6), float32 rows of 256 or 512 bytes with full or interleaved
 // rotations (heads of 64 45.2 / 46.0, of 256 46.1 / 46.5, rotary_embedding_dim 64 of
-// 128 interleaved 46.5 / 47.5).
+// 128 interleaved 46.5 / 47.5), float32 packed [Q|K|V] (69.2 / 67.5) and
+// the float32 prompt with the cache append (66.3 / 65.2).
 static constexpr int64_t kRowMaxBytes = 6 << 20;
 static constexpr int64_t kRowMaxBytesMrope = 4 << 20;
 
@@ -253,8 +256,9 @@ static bool row_kernel_fits_better(const Problem& p, int es, bool general) {
     // QK-norm (rows of a power-of-two size): float32 data, or 2-byte split
     // halves other than 128 bytes long
     if (p.norm) return adjacent && (es == 4 || (!p.interleaved && half_bytes != 128));
-    // float32: rows of other sizes, or a partial rotation of split halves
-    if (es == 4) return adjacent && (general || (!p.interleaved && p.R < p.D));
+    // float32: rows of other sizes, a partial rotation of split halves, or
+    // coefficients on the fly
+    if (es == 4) return adjacent && (general || (!p.interleaved && p.R < p.D) || p.coef == kCoefOnTheFly);
     // head rows apart (rank 4): rows of a power-of-two size only
     if (!adjacent) return !general && (p.interleaved || half_bytes < 128);
     return general || p.interleaved || half_bytes < 128 || p.ntask == 2 || p.coef == kCoefAppend;

@@ -258,6 +258,8 @@ def test_row_kernel_at_prefill_sizes():
     qk = dict(B=1, S=8192, H=32, Hk=8, M=8192)
     assert check_qk(qk_case(D=128, **qk)) == (OK, "row16/gather")
     assert check_qk(qk_case(D=128, table=False, **qk)) == (OK, "row16/on_the_fly")
+    assert check_qk(qk_case(D=128, dt=F32, **qk)) == (OK, "vec16/gather")
+    assert check_qk(qk_case(D=128, dt=F32, table=False, **qk)) == (OK, "row16/on_the_fly")
     assert check_norm(norm_case(shape=qk)) == (OK, "vec16/norm/gather")
     assert check_norm(norm_case(D=256, shape=qk)) == (OK, "row16/norm/gather")          # halves of 256 B
     assert check_norm(norm_case(D=64, shape=qk)) == (OK, "row16/norm/gather")           # halves of 64 B
