@@ -204,6 +204,21 @@ __device__ inline float group_sum(float v, int W) {
     return v;
 }
 
+// The sum of v over a row of W consecutive lanes starting at lane `first`
+// (any W up to 64; c = lane - first): at step d each lane adds the partial
+// sum of the lane d above it when that lane is in the same row, so that
+// after the steps 1, 2, ..., 32 the row's first lane holds the sum of the
+// whole row (only values of the row are ever added), which every lane of the
+// row then reads. Every lane of the wave takes part.
+__device__ inline float row_sum(float v, int c, int W, int first) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float t = __shfl_down(v, d);
+        if (c + d < W) v += t;
+    }
+    return __shfl(v, first);
+}
+
 // Coefficient of slot i at position p computed on the fly (PR #27590
 // Motivation): theta = rnd_f32(rnd_f32(p) * inv_freq[i]); cos and sin of the
 // exact binary32 theta in binary64, rounded to binary32, times the scaling in
@@ -968,9 +983,10 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 // Rows of a power-of-two size (GEN = 0) take lane l as chunk l % row_lanes
 // of row l / row_lanes by shift and mask, and partners a power of two of
 // lanes apart by DPP or an XOR permute. Other rows (GEN = 1: 16-byte chunks,
-// row_lanes up to 64; not the QK-norm, not M-RoPE) take 64 / row_lanes rows
-// per instruction, the remaining lanes idle, the row and chunk by a
-// multiply-shift, and each lane's partner by a permute from lane l +- half_lanes.
+// row_lanes up to 64; not M-RoPE) take 64 / row_lanes rows per instruction,
+// the remaining lanes idle, the row and chunk by a multiply-shift, each
+// lane's partner by a permute from lane l +- half_lanes, and the QK-norm's
+// sum of squares by a segmented reduction over the row's lanes.
 // The chunk of lane (lane ^ d), d a power of two < 64 (uniform): DPP row
 // permutes for d = 1, 2, 4, 8 (4: a quad reverse, i -> i ^ 3, then the
 // half-row mirror, i -> i ^ 7), a permute through the LDS crossbar for 16 and
@@ -1024,7 +1040,7 @@ __device__ inline int64_t uniform64(int64_t v) {
 
 template <typename T, int IL, int COEF, bool NORM, int NT = kMaxTasks, int GEN = 0>
 __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
-    static_assert(!GEN || (!NORM && COEF != kCoefMrope), "rows of other sizes: no QK-norm, no M-RoPE");
+    static_assert(!GEN || COEF != kCoefMrope, "rows of other sizes: no M-RoPE");
     constexpr int E = Elem<T>::E;
     constexpr int CE = IL ? E / 2 : E;  // coefficient slots per rotation chunk
     constexpr int ES = (int)sizeof(T);
@@ -1221,7 +1237,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
                 fb[2 * j + 1] = wo[2 * j] * sf[j];      // w1 s
             }
         } else {
-            const int cp = rotc ? (c ^ dl) : c;
+            const int cp = rotc ? (GEN ? (lower ? c + dl : c - dl) : (c ^ dl)) : c;
             const auto w2 = chunk_values<T>(load16_global(tk.wgt + cp * 16));
 #pragma unroll
             for (int e = 0; e < E; ++e) {
@@ -1246,7 +1262,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
             float ss = 0.0f;
 #pragma unroll
             for (int e = 0; e < E; ++e) ss = fmaf(to_f(xv[e]), to_f(xv[e]), ss);
-            ss = group_sum(ss, a.row_lanes);
+            ss = GEN ? row_sum(ss, c, a.row_lanes, hi * a.row_lanes) : group_sum(ss, a.row_lanes);
             const float r = rsqrtf(ss * a.inv_d + a.eps);  // v_rsq_f32: about 1 ulp
             float z[E];
             if (rotate && rotc) {
@@ -1505,24 +1521,27 @@ inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream
     const void* fn;
     // QK-norm launches hold Q and K; the cache append Q, K and V; M-RoPE one
     // task; the others one (RotaryEmbedding), two (Q+K) or three (packed).
-    // Rows of other sizes (gen): no QK-norm, no M-RoPE.
+    // Rows of other sizes (gen): no M-RoPE.
 #define ROPE_ROW_NT(K, G)                                                          \
     (a.ntask == 1   ? (const void*)rope_row_kernel<T, IL, K, false, 1, G>          \
      : a.ntask == 2 ? (const void*)rope_row_kernel<T, IL, K, false, 2, G>          \
      : a.ntask == 3 ? (const void*)rope_row_kernel<T, IL, K, false, 3, G>          \
                     : nullptr)
-#define ROPE_ROW(K)                                                                            \
-    (norm ? (gen || a.ntask != 2 ? nullptr : (const void*)rope_row_kernel<T, IL, K, true, 2>) \
+#define ROPE_ROW(K)                                                                         \
+    (norm ? (a.ntask != 2 ? nullptr                                                         \
+             : gen        ? (const void*)rope_row_kernel<T, IL, K, true, 2, 1>              \
+                          : (const void*)rope_row_kernel<T, IL, K, true, 2>)                 \
           : (gen ? ROPE_ROW_NT(K, 1) : ROPE_ROW_NT(K, 0)))
     switch (c) {
         case kCoefGather: fn = ROPE_ROW(kCoefGather); break;
         case kCoefPerToken: fn = ROPE_ROW(kCoefPerToken); break;
         case kCoefOnTheFly: fn = ROPE_ROW(kCoefOnTheFly); break;
         case kCoefAppend:
-            if (a.ntask != 3 || (gen && norm)) return hipErrorInvalidValue;
-            fn = norm  ? (const void*)rope_row_kernel<T, IL, kCoefAppend, true, 3>
-                 : gen ? (const void*)rope_row_kernel<T, IL, kCoefAppend, false, 3, 1>
-                       : (const void*)rope_row_kernel<T, IL, kCoefAppend, false, 3>;
+            if (a.ntask != 3) return hipErrorInvalidValue;
+            fn = norm ? (gen ? (const void*)rope_row_kernel<T, IL, kCoefAppend, true, 3, 1>
+                             : (const void*)rope_row_kernel<T, IL, kCoefAppend, true, 3>)
+                      : (gen ? (const void*)rope_row_kernel<T, IL, kCoefAppend, false, 3, 1>
+                             : (const void*)rope_row_kernel<T, IL, kCoefAppend, false, 3>);
             break;
         case kCoefMrope:
             if (norm || gen || a.ntask != 1) return hipErrorInvalidValue;

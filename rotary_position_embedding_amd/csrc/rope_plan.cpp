@@ -264,7 +264,9 @@ static bool row_kernel_fits_better(const Problem& p, int es, bool general) {
     return general || p.interleaved || half_bytes < 128 || p.ntask == 2 || p.coef == kCoefAppend;
 }
 
-static bool choose_row_geometry(Plan* pl) {
+// vec_can: the vector kernel could take the launch (else the row kernel takes
+// it at any size when its rules allow, before the scalar kernel)
+static bool choose_row_geometry(Plan* pl, bool vec_can) {
     Problem& p = pl->p;
     Geometry& g = pl->g;
     const int policy = kernel_policy();
@@ -275,13 +277,13 @@ static bool choose_row_geometry(Plan* pl) {
     if (row_bytes % 16 != 0 || row_bytes < 32 || row_bytes > 1024) return false;
     const int64_t dl = p.interleaved ? 0 : (p.R / 2) * es / 16;
     // rows of other sizes, or partners a number of lanes apart other than a
-    // power of two: the kernel's general instances (no QK-norm, no M-RoPE)
+    // power of two: the kernel's general instances (no M-RoPE)
     const bool general = !pow2(row_bytes) || (!p.interleaved && !pow2(dl));
-    if (general && (p.norm || p.coef == kCoefMrope)) return false;
+    if (general && p.coef == kCoefMrope) return false;
     int64_t xbytes = 0;
     for (int t = 0; t < p.ntask; ++t) xbytes += p.B * p.S * p.task[t].heads * row_bytes;
     const int64_t max_bytes = p.coef == kCoefMrope ? kRowMaxBytesMrope : kRowMaxBytes;
-    if (xbytes > max_bytes && policy != 3 && !row_kernel_fits_better(p, es, general)) return false;
+    if (xbytes > max_bytes && policy != 3 && vec_can && !row_kernel_fits_better(p, es, general)) return false;
     const int RL = (int)(row_bytes / 16);
     const int rpi = 64 / RL;
     const int64_t ntok = p.B * p.S;
@@ -370,17 +372,23 @@ static void choose_geometry(Plan* pl) {
     const int64_t NT = (p.D - p.R) / E;
     const int64_t W = NP + NT;
     ok = ok && W >= 1 && W <= 256;
-    // QK-norm: a row's items must sit in one aligned group of W lanes (W a
-    // power of two dividing the wave) for the in-wave sum of squares
-    if (p.norm) ok = ok && W <= 64 && (W & (W - 1)) == 0;
+    // QK-norm in the vector kernel: a row's items must sit in one aligned
+    // group of W lanes (W a power of two dividing the wave) for the in-wave
+    // sum of squares; the row kernel sums any row of up to 64 lanes
+    const bool vec_can = !p.norm || (W <= 64 && (W & (W - 1)) == 0);
     g.vector = ok;
     g.variant = variant_name(ok, p.coef, p.norm != 0);
     g.row_kernel = 0;
     g.row_general = 0;
     g.group_major = 0;
     if (!ok) return;
-    if (choose_row_geometry(pl)) {
+    if (choose_row_geometry(pl, vec_can)) {
         g.variant = row_variant_name(p.coef, p.norm != 0);
+        return;
+    }
+    if (!vec_can) {
+        g.vector = false;
+        g.variant = variant_name(false, p.coef, p.norm != 0);
         return;
     }
 

@@ -828,7 +828,14 @@ def test_qk_norm_accepted():
             assert v == ("row16/norm/gather" if table else "row16/norm/on_the_fly")
             rc, v = with_policy(2, check_norm, norm_case(dt=dt, table=table))
             assert v == ("vec16/norm/gather" if table else "vec16/norm/on_the_fly")
-    rc, v = check_norm(norm_case(dt=F32, D=96))      # 12 items per row: not a power of two
+    rc, v = check_norm(norm_case(dt=F32, D=96))      # 24 chunks per row: the row kernel's general rows
+    assert rc == OK and v == "row16/norm/gather"
+    assert with_policy(2, check_norm, norm_case(dt=F32, D=96)) == (OK, "scalar/norm/gather")  # no vector kernel
+    rc, v = check_norm(norm_case(D=96, shape=dict(B=1, S=8192, H=32, Hk=8, M=8192)))  # any size
+    assert rc == OK and v == "row16/norm/gather"
+    rc, v = check_norm(norm_case(D=80, rank=4, shape=dict(B=1, S=8192, H=32, Hk=8, M=8192)))
+    assert rc == OK and v == "row16/norm/gather"
+    rc, v = check_norm(norm_case(dt=F32, D=1040 // 4 * 2, table=True))  # 2080-byte rows: neither
     assert rc == OK and v == "scalar/norm/gather"
     rc, v = check_norm(norm_case(rank=4))
     assert rc == OK and v == "row16/norm/gather"

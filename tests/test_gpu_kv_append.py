@@ -192,7 +192,9 @@ def zmax(x, w, eps, heads):
     (BFLOAT16, 3, 9, 8, 2, 128, 32, 40, 64, 40, 1, False),
     (np.float32, 2, 5, 4, 2, 64, 32, 16, 20, 5, 0, True),
     (np.float16, 2, 3, 4, 1, 10, 3, 12, 12, 11, 0, False),    # scalar kernel
-], ids=["decode_f16", "chunk_bf16", "prompt_f32_packed", "odd_rows"])
+    (np.float16, 5, 2, 6, 3, 96, 48, 24, 40, 9, 0, False),    # 192-byte rows: the row kernel's general rows
+    (BFLOAT16, 3, 4, 6, 2, 80, 16, 20, 30, 10, 1, True),      # 160-byte rows, interleaved, packed
+], ids=["decode_f16", "chunk_bf16", "prompt_f32_packed", "odd_rows", "rows96_f16", "rows80_bf16_packed"])
 def test_kv_append_qk_norm(case, policy):
     dt, B, S, H, Hk, D, width, Smax, M, total, il, packed = case
     rpe.set_kernel_policy(policy)

@@ -58,7 +58,11 @@ NORM = [
     (3, np.float32, 2, 11, 4, 2, 64, 32, 1, "gather"),
     (3, np.float16, 2, 9, 4, 2, 128, 64, 0, "per_token"),
     (4, BFLOAT16, 1, 33, 2, 1, 256, 0, 0, "gather"),
-    (3, np.float32, 2, 7, 4, 2, 96, 0, 0, "gather"),       # scalar kernel (12 items per row)
+    (3, np.float32, 2, 7, 4, 2, 96, 0, 0, "gather"),       # 384-byte rows: the row kernel's general rows
+    (3, np.float16, 3, 11, 6, 3, 96, 0, 0, "gather"),      # 192-byte rows, 5 per instruction
+    (3, BFLOAT16, 2, 9, 6, 2, 80, 32, 1, "onthefly"),      # 160-byte rows, partial, interleaved
+    (4, np.float16, 2, 13, 4, 2, 96, 64, 0, "per_token"),  # rank 4, partners 4 lanes apart
+    (3, np.float16, 2, 6, 3, 1, 192, 0, 0, "gather"),      # 384-byte rows, partners 12 lanes apart
     (3, np.float16, 2, 5, 2, 1, 10, 6, 0, "onthefly"),     # scalar kernel
     (3, np.float16, 64, 1, 32, 8, 128, 0, 0, "onthefly"),  # decode
     (3, np.float32, 2, 5, 2, 1, 256, 0, 0, "gather"),      # 1 KiB rows: the sum over 64 lanes
@@ -122,7 +126,8 @@ def test_qk_norm_in_place():
 
 @pytest.mark.parametrize("dt,D,H,Hk", [(np.float16, 128, 32, 8), (BFLOAT16, 128, 32, 8),
                                        (np.float16, 256, 16, 8),   # halves of 256 B: the row kernel
-                                       (np.float32, 128, 32, 8)])  # float32: the row kernel
+                                       (np.float32, 128, 32, 8),   # float32: the row kernel
+                                       (np.float16, 96, 32, 8)])   # 192-byte rows: general rows
 def test_qk_norm_prefill_full_size(dt, D, H, Hk):
     """A Qwen3-like prefill: 4 x 2048 tokens, 32 query and 8 key heads of 128
     (or 16 and 8 of 256), positions per-sequence offset + arange into a
