@@ -1303,6 +1303,147 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Row kernel, element-wise pairs: rows of 16-byte chunks (32 bytes to 1 KiB)
+// whose pairs do not fall on chunk boundaries, i.e. a rotary_embedding_dim
+// whose half (split halves) or whole (interleaved pairs) is not a multiple of
+// the elements of a chunk (GPT-NeoX-style partial rotations such as 24 of 96
+// or 20 of 80 dimensions). Lanes, waves and memory order as in the row
+// kernel's general rows (lane l: chunk l % row_lanes of row l / row_lanes,
+// 64 / row_lanes rows per instruction, whole chunks loaded and stored); each
+// wave puts its token's coefficient slots and, per instruction, its chunks in
+// its own LDS, and every element reads its partner element and its slot's
+// coefficients there. Binary32 (binary64 for float32 data) arithmetic as in
+// the other kernels; copied elements keep their bits. No QK-norm, no M-RoPE.
+template <typename T, int IL, int COEF, int NT>
+__global__ __launch_bounds__(kBlock) void rope_row_elem_kernel(const KArgs a) {
+    static_assert(COEF != kCoefMrope, "element-wise pairs: no M-RoPE");
+    constexpr int E = Elem<T>::E;
+    constexpr int ES = (int)sizeof(T);
+
+    const int lane = threadIdx.x & 63;
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t gw = (int64_t)blockIdx.x * kWavesPerBlock + wave_in_block;
+    const TaskView tk = task_pick<COEF, false, NT>(a, gw);
+    const uint32_t local = (uint32_t)(gw - tk.wave_begin);
+    const uint32_t nw = fast_div(local, tk.chunks_m, tk.chunks_s);  // the token
+    const int part = (int)(local - nw * (uint32_t)tk.chunks);
+    const bool live = nw < (uint64_t)a.ntok;
+    if (COEF == kCoefAppend && !live) return;
+    const uint32_t n32 = live ? nw : (uint32_t)(a.ntok - 1);
+    const int RL = a.row_lanes;
+    const int rpi = a.row_rpi;
+    const int hi = (int)(((uint32_t)lane * a.row_m) >> 16);
+    const int c = lane - hi * RL;
+    const bool lane_ok = hi < rpi;  // lanes past the last whole row idle
+    const int h0 = part * tk.hpw;
+    const int nh = min(tk.heads - h0, tk.hpw);
+    const uint32_t b32 = fast_div(n32, a.s_m, a.s_s);
+    const int64_t n = n32;
+    const int64_t b = b32;
+    const int64_t s = (int64_t)(n32 - b32 * (uint32_t)a.S);
+
+    typedef const __attribute__((address_space(4))) int64_t* const_i64;
+    typedef const __attribute__((address_space(4))) int32_t* const_i32;
+    bool valid = true;   // the coefficient row exists (else the pairs are copied)
+    int64_t row = 0;     // coefficient row
+    int64_t pos = 0;     // on the fly: the position
+    int64_t yrow = s;    // output row: the cache row of the append kind's K and V
+    if (COEF == kCoefGather || COEF == kCoefOnTheFly) {
+        pos = ((const_i64)a.ids)[n];
+        valid = COEF == kCoefOnTheFly || (pos >= 0 && pos < a.M);
+        row = valid ? pos : 0;
+    } else if (COEF == kCoefPerToken) {
+        row = n;
+    } else if (COEF == kCoefAppend) {
+        const int64_t past = a.prompt ? 0 : (int64_t)((const_i32)a.seqlens)[b] - a.S;
+        pos = past + s;
+        valid = pos >= 0 && pos < a.M;
+        row = valid ? pos : 0;
+        if (tk.yrow) {
+            if (pos < 0 || pos >= a.rows_out) return;  // no such cache row
+            yrow = pos;
+        }
+    }
+    const char* px = tk.x + (b * tk.sb + s * tk.ss + (int64_t)(h0 + hi) * tk.sh) * ES + c * 16;
+    char* py = tk.y + (b * tk.ysb + yrow * tk.yss + (int64_t)(h0 + hi) * tk.ysh) * ES + c * 16;
+    const int64_t xstep = (int64_t)rpi * tk.sh * ES;
+    const int64_t ystep = (int64_t)rpi * tk.ysh * ES;
+
+    u32x4 in[kRowLoads];
+#pragma unroll
+    for (int u = 0; u < kRowLoads; ++u) {
+        in[u] = u32x4{0u, 0u, 0u, 0u};
+        if (lane_ok && u * rpi + hi < nh) in[u] = load_nt(px + u * xstep);
+    }
+
+    // the token's coefficient slots (binary32 values of T), slot i in lane
+    // i % 64; the wave's own LDS rows, a wave barrier, no workgroup barrier
+    __shared__ float lds_cs[kWavesPerBlock][2][kRowMaxSlots];
+    __shared__ u32x4 lds_x[kWavesPerBlock][64];
+    float* wc = lds_cs[wave_in_block][0];
+    float* ws = lds_cs[wave_in_block][1];
+    const int P = a.P;
+    const bool rotate = valid && !tk.copy;  // wave-uniform
+    if (rotate) {
+        for (int i = lane; i < P; i += 64) {
+            float cv, sv;
+            if (COEF == kCoefOnTheFly) {
+                onthefly_coef<T>(a.inv_freq[i], pos, a.scaling, cv, sv);
+            } else {
+                const int64_t e = row * P + i;
+                cv = to_f(reinterpret_cast<const T*>(a.cos)[e]);
+                sv = to_f(reinterpret_cast<const T*>(a.sin)[e]);
+            }
+            wc[i] = cv;
+            ws[i] = sv;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const T* xrow = reinterpret_cast<const T*>(&lds_x[wave_in_block][lane_ok ? hi * RL : 0]);
+#pragma unroll
+    for (int u = 0; u < kRowLoads; ++u) {
+        if (u * rpi >= nh) break;
+        const bool act = lane_ok && u * rpi + hi < nh;
+        u32x4 o = in[u];
+        if (rotate) {
+            lds_x[wave_in_block][lane] = in[u];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            if (lane_ok) {
+                const auto xv = chunk_values<T>(in[u]);
+                float y[E];
+                u32x4 keep = u32x4{0u, 0u, 0u, 0u};  // elements copied as they are
+#pragma unroll
+                for (int j = 0; j < E; ++j) {
+                    const int d = c * E + j;  // element of the head row
+                    y[j] = 0.0f;
+                    if (d >= a.R) {
+                        mask_elem<T>(keep, j);
+                        continue;
+                    }
+                    // interleaved: (2i, 2i+1) take slot i; split halves: (i, i+P)
+                    const bool first = IL ? (d & 1) == 0 : d < P;
+                    const int pd = IL ? (d ^ 1) : (first ? d + P : d - P);
+                    const int slot = IL ? (d >> 1) : (first ? d : d - P);
+                    const float sv = ws[slot];
+                    y[j] = rot_out<T>(to_f(xv[j]), wc[slot], to_f(xrow[pd]), first ? -sv : sv);
+                }
+                o = select_bits(keep, in[u], chunk_pack<T>(y));
+            }
+            // the next instruction's chunks reuse the wave's LDS row
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        if (act && live) store_nt(py + u * ystep, o);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Scalar kernel: one thread per (token, head, k), k < R/2 a pair, k >= R/2 a
 // tail element R + k - R/2. Any head size, rotary dim and alignment.
 template <typename T, int COEF>
@@ -1516,7 +1657,7 @@ inline hipError_t launch_vec_coef(const KArgs& a, CoefKind c, int ipl, int hu, d
 }
 
 template <typename T, int IL>
-inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream_t st, bool norm, bool gen) {
+inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream_t st, bool norm, int gen) {
     void* args[] = {const_cast<KArgs*>(&a)};
     const void* fn;
     // QK-norm launches hold Q and K; the cache append Q, K and V; M-RoPE one
@@ -1532,6 +1673,27 @@ inline hipError_t launch_row_il(const KArgs& a, CoefKind c, dim3 grid, hipStream
              : gen        ? (const void*)rope_row_kernel<T, IL, K, true, 2, 1>              \
                           : (const void*)rope_row_kernel<T, IL, K, true, 2>)                 \
           : (gen ? ROPE_ROW_NT(K, 1) : ROPE_ROW_NT(K, 0)))
+    if (gen == 2) {  // element-wise pairs: no QK-norm, no M-RoPE
+        if (norm) return hipErrorInvalidValue;
+#define ROPE_ELEM(K)                                                                \
+    (a.ntask == 1   ? (const void*)rope_row_elem_kernel<T, IL, K, 1>                \
+     : a.ntask == 2 ? (const void*)rope_row_elem_kernel<T, IL, K, 2>                \
+     : a.ntask == 3 ? (const void*)rope_row_elem_kernel<T, IL, K, 3>                \
+                    : nullptr)
+        switch (c) {
+            case kCoefGather: fn = ROPE_ELEM(kCoefGather); break;
+            case kCoefPerToken: fn = ROPE_ELEM(kCoefPerToken); break;
+            case kCoefOnTheFly: fn = ROPE_ELEM(kCoefOnTheFly); break;
+            case kCoefAppend:
+                if (a.ntask != 3) return hipErrorInvalidValue;
+                fn = (const void*)rope_row_elem_kernel<T, IL, kCoefAppend, 3>;
+                break;
+            default: return hipErrorInvalidValue;
+        }
+#undef ROPE_ELEM
+        if (!fn) return hipErrorInvalidValue;
+        return hipLaunchKernel(fn, grid, dim3(kBlock), args, 0, st);
+    }
     switch (c) {
         case kCoefGather: fn = ROPE_ROW(kCoefGather); break;
         case kCoefPerToken: fn = ROPE_ROW(kCoefPerToken); break;
@@ -1593,7 +1755,7 @@ hipError_t launch_vector_for(const KArgs& a, CoefKind c, int interleaved, int ip
 
 template <typename T>
 hipError_t launch_row_for(const KArgs& a, CoefKind c, int interleaved, dim3 grid, hipStream_t st, bool norm,
-                          bool gen) {
+                          int gen) {
     return interleaved ? launch_row_il<T, 1>(a, c, grid, st, norm, gen)
                        : launch_row_il<T, 0>(a, c, grid, st, norm, gen);
 }
@@ -1616,7 +1778,7 @@ hipError_t launch_table_for(const float* inv, void* cos, void* sin, int64_t rows
     EXT template hipError_t launch_vector_for<T>(const KArgs&, CoefKind, int, int, int, dim3,      \
                                                  hipStream_t, bool);
 #define ROPE_ROW_ENTRY_POINTS(EXT, T)                                                              \
-    EXT template hipError_t launch_row_for<T>(const KArgs&, CoefKind, int, dim3, hipStream_t, bool, bool); \
+    EXT template hipError_t launch_row_for<T>(const KArgs&, CoefKind, int, dim3, hipStream_t, bool, int); \
     EXT template hipError_t launch_scalar_for<T>(const KArgs&, CoefKind, int64_t, hipStream_t, bool); \
     EXT template hipError_t launch_table_for<T>(const float*, void*, void*, int64_t, int64_t, float, \
                                                 dim3, hipStream_t);

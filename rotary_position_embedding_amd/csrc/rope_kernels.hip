@@ -132,7 +132,7 @@ int launch_plan(const Plan& pl, void* stream) {
         const int ipl = g.items_per_lane;
         const int hu = g.head_batch;
         if (g.row_kernel) {
-            const bool gen = g.row_general != 0;
+            const int gen = g.row_general;  // 0, 1 general rows, 2 element-wise pairs
             e = p.dtype == ROPE_FLOAT16    ? launch_row_for<half_t>(a, p.coef, p.interleaved, grid, st, p.norm, gen)
                 : p.dtype == ROPE_BFLOAT16 ? launch_row_for<bf16_t>(a, p.coef, p.interleaved, grid, st, p.norm, gen)
                                            : launch_row_for<float>(a, p.coef, p.interleaved, grid, st, p.norm, gen);

@@ -265,20 +265,22 @@ static bool row_kernel_fits_better(const Problem& p, int es, bool general) {
 }
 
 // vec_can: the vector kernel could take the launch (else the row kernel takes
-// it at any size when its rules allow, before the scalar kernel)
-static bool choose_row_geometry(Plan* pl, bool vec_can) {
+// it at any size when its rules allow, before the scalar kernel); elementwise:
+// pairs that do not fall on 16-byte chunks (the element-wise instances)
+static bool choose_row_geometry(Plan* pl, bool vec_can, bool elementwise = false) {
     Problem& p = pl->p;
     Geometry& g = pl->g;
     const int policy = kernel_policy();
     if (policy == 2) return false;
-    if (p.coef == kCoefOnTheFly && p.R / 2 > kRowMaxSlots) return false;
+    if ((p.coef == kCoefOnTheFly || elementwise) && p.R / 2 > kRowMaxSlots) return false;
+    if (elementwise && (p.norm || p.coef == kCoefMrope)) return false;
     const int es = elem_size(p.dtype);
     const int64_t row_bytes = p.D * es;
     if (row_bytes % 16 != 0 || row_bytes < 32 || row_bytes > 1024) return false;
-    const int64_t dl = p.interleaved ? 0 : (p.R / 2) * es / 16;
+    const int64_t dl = p.interleaved || elementwise ? 0 : (p.R / 2) * es / 16;
     // rows of other sizes, or partners a number of lanes apart other than a
     // power of two: the kernel's general instances (no M-RoPE)
-    const bool general = !pow2(row_bytes) || (!p.interleaved && !pow2(dl));
+    const bool general = elementwise || !pow2(row_bytes) || (!p.interleaved && !pow2(dl));
     if (general && p.coef == kCoefMrope) return false;
     int64_t xbytes = 0;
     for (int t = 0; t < p.ntask; ++t) xbytes += p.B * p.S * p.task[t].heads * row_bytes;
@@ -328,10 +330,10 @@ static bool choose_row_geometry(Plan* pl, bool vec_can) {
     // the kernel's index arithmetic is 32-bit
     if (total_waves > INT32_MAX || ntok > INT32_MAX) return false;
     g.row_kernel = 1;
-    g.row_general = general ? 1 : 0;
+    g.row_general = elementwise ? 2 : (general ? 1 : 0);
     g.row_lanes = RL;
     g.half_lanes = (int32_t)dl;
-    g.NP = (int32_t)(p.R * es / 16);  // chunks of the rotated prefix
+    g.NP = (int32_t)(p.R * es / 16);  // chunks of the rotated prefix (unused element-wise)
     g.W = RL;
     g.TG = 1;
     g.tile = 1;
@@ -361,17 +363,33 @@ static void choose_geometry(Plan* pl) {
     const int E = 16 / es;
     const int64_t half = p.R / 2;
     bool ok = kernel_policy() != 1;
-    ok = ok && p.D % E == 0 && p.R % E == 0 && (p.interleaved || half % E == 0);
+    // rows in 16-byte chunks; pairs within chunk boundaries (else only the
+    // row kernel's element-wise instances, or the scalar kernel)
+    ok = ok && p.D % E == 0;
+    const bool pairs_ok = p.R % E == 0 && (p.interleaved || half % E == 0);
     for (int t = 0; t < p.ntask; ++t)
         ok = ok && aligned16(p.task[t].x) && aligned16(p.task[t].y);
     if (p.norm)
         for (int t = 0; t < p.ntask; ++t) ok = ok && aligned16(p.task[t].weight);
     if (p.coef != kCoefOnTheFly)
         ok = ok && aligned16(p.cos) && aligned16(p.sin);
+    if (ok && !pairs_ok) {
+        g.row_kernel = 0;
+        g.row_general = 0;
+        g.group_major = 0;
+        g.vector = true;
+        if (choose_row_geometry(pl, false, true)) {
+            g.variant = row_variant_name(p.coef, p.norm != 0);
+            return;
+        }
+        g.vector = false;
+        g.variant = variant_name(false, p.coef, p.norm != 0);
+        return;
+    }
     const int64_t NP = p.interleaved ? p.R / E : half / E;
     const int64_t NT = (p.D - p.R) / E;
     const int64_t W = NP + NT;
-    ok = ok && W >= 1 && W <= 256;
+    ok = ok && pairs_ok && W >= 1 && W <= 256;
     // QK-norm in the vector kernel: a row's items must sit in one aligned
     // group of W lanes (W a power of two dividing the wave) for the in-wave
     // sum of squares; the row kernel sums any row of up to 64 lanes

@@ -100,6 +100,8 @@ KV = [
     (np.float32, 2, 3, 2, 2, 96, 32, 24, 30, (3, 24), 24, 1, True),
     (np.float16, 2, 3, 4, 2, 64, 16, 20, 30, (3, 11), 11, 0, False),       # partners 2 lanes apart, tail
     (np.float32, 1, 2, 2, 1, 256, 128, 8, 10, (2,), 2, 0, False),          # 1 KiB rows, prompt
+    (np.float16, 3, 4, 8, 2, 80, 10, 24, 30, (4, 9, 24), 24, 0, False),     # 20 of 80 rotated: element-wise
+    (BFLOAT16, 2, 3, 6, 3, 96, 10, 20, 30, (3, 11), 11, 1, True),          # interleaved 20 of 96, packed
 ]
 
 

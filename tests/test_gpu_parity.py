@@ -220,6 +220,9 @@ def _reshaped(name, head_size=None, heads=None, interleaved=None, rotary_dim=Non
     (128, 32, 0, 32, None),
     (256, 16, 0, None, None),       # split halves of 256 bytes: the vector kernel, batches of 2
     (96, 32, 0, None, None),        # 192-byte rows, partners 6 lanes apart: the row kernel's general rows
+    (96, 32, 0, 24, None),          # 24 of 96 rotated: element-wise pairs
+    (80, 32, 0, 20, "bf16"),        # 20 of 80 rotated
+    (128, 32, 1, 20, None),         # interleaved, 20 rotated
     (96, 32, 1, None, None),
     (80, 32, 0, 32, None),          # 160-byte rows, rotary dim 32
     (128, 32, 0, 64, "f32"),        # float32 partial rotation: the row kernel
@@ -353,6 +356,13 @@ SHAPES = [
     (3, np.float16, 2, 7, 3, 128, 64, 0, True, 50),      # partial: 4 lanes apart, tail chunks
     (3, np.float16, 2, 7, 3, 128, 96, 1, True, 50),      # interleaved partial, 12 rotated chunks
     (3, BFLOAT16, 2, 11, 6, 32, 0, 0, False, 0),         # 64-byte rows, per-token table
+    # pairs off the 16-byte chunks (the row kernel's element-wise instances)
+    (3, np.float16, 3, 29, 7, 96, 24, 0, True, 200),     # 24 of 96 rotated: halves of 12
+    (3, np.float16, 2, 17, 5, 80, 20, 0, False, 0),      # 20 of 80, per-token table
+    (4, BFLOAT16, 2, 15, 3, 64, 12, 0, True, 60),        # rank 4, halves of 6
+    (3, np.float16, 2, 9, 4, 128, 20, 1, True, 40),      # interleaved, 20 rotated
+    (3, np.float32, 2, 11, 3, 64, 20, 0, True, 50),      # float32, halves of 10
+    (3, np.float16, 2, 6, 2, 512, 40, 0, True, 60),      # 1 KiB rows, 40 rotated
 ]
 
 
@@ -609,6 +619,8 @@ QK = [
     (3, np.float16, 3, 4, 4, 2, 10, 0, 0),   # scalar kernel
     (3, BFLOAT16, 7, 1, 8, 2, 128, 0, 0),
     (4, BFLOAT16, 3, 17, 4, 4, 64, 0, 1),
+    (3, np.float16, 5, 3, 8, 2, 96, 24, 0),  # pairs off the 16-byte chunks
+    (3, BFLOAT16, 3, 6, 4, 2, 80, 20, 1),
 ]
 
 
