@@ -1316,6 +1316,7 @@ __global__ __launch_bounds__(kBlock) void rope_row_kernel(const KArgs a) {
 // the other kernels; copied elements keep their bits. No QK-norm, no M-RoPE.
 template <typename T, int IL, int COEF, int NT>
 __global__ __launch_bounds__(kBlock) void rope_row_elem_kernel(const KArgs a) {
+    constexpr int kElemLoads = kRowElemLoads;  // instructions per wave (their chunks all in LDS)
     static_assert(COEF != kCoefMrope, "element-wise pairs: no M-RoPE");
     constexpr int E = Elem<T>::E;
     constexpr int ES = (int)sizeof(T);
@@ -1369,17 +1370,18 @@ __global__ __launch_bounds__(kBlock) void rope_row_elem_kernel(const KArgs a) {
     const int64_t xstep = (int64_t)rpi * tk.sh * ES;
     const int64_t ystep = (int64_t)rpi * tk.ysh * ES;
 
-    u32x4 in[kRowLoads];
+    u32x4 in[kElemLoads];
 #pragma unroll
-    for (int u = 0; u < kRowLoads; ++u) {
+    for (int u = 0; u < kElemLoads; ++u) {
         in[u] = u32x4{0u, 0u, 0u, 0u};
         if (lane_ok && u * rpi + hi < nh) in[u] = load_nt(px + u * xstep);
     }
 
     // the token's coefficient slots (binary32 values of T), slot i in lane
-    // i % 64; the wave's own LDS rows, a wave barrier, no workgroup barrier
+    // i % 64, and the wave's chunks, all in the wave's own LDS rows; one wave
+    // barrier (no workgroup barrier) before any element reads them
     __shared__ float lds_cs[kWavesPerBlock][2][kRowMaxSlots];
-    __shared__ u32x4 lds_x[kWavesPerBlock][64];
+    __shared__ u32x4 lds_x[kWavesPerBlock][kElemLoads][64];
     float* wc = lds_cs[wave_in_block][0];
     float* ws = lds_cs[wave_in_block][1];
     const int P = a.P;
@@ -1397,47 +1399,51 @@ __global__ __launch_bounds__(kBlock) void rope_row_elem_kernel(const KArgs a) {
             wc[i] = cv;
             ws[i] = sv;
         }
+#pragma unroll
+        for (int u = 0; u < kElemLoads; ++u)
+            if (u * rpi < nh) lds_x[wave_in_block][u][lane] = in[u];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    const T* xrow = reinterpret_cast<const T*>(&lds_x[wave_in_block][lane_ok ? hi * RL : 0]);
+    // lanes holding rotated elements (the rest copy their chunks); a lane's
+    // coefficients, signs and partner offsets are the same for every row of
+    // the token, so they are read once
+    const bool rot_lane = rotate && lane_ok && c * E < a.R;
+    float cf[E], sf[E];
+    int pd[E];
+    u32x4 keep = u32x4{0u, 0u, 0u, 0u};  // elements copied as they are
 #pragma unroll
-    for (int u = 0; u < kRowLoads; ++u) {
+    for (int j = 0; j < E; ++j) {
+        const int d = c * E + j;  // element of the head row
+        cf[j] = 1.0f;
+        sf[j] = 0.0f;
+        pd[j] = 0;
+        if (d >= a.R) {
+            mask_elem<T>(keep, j);
+            continue;
+        }
+        if (!rot_lane) continue;
+        // interleaved: (2i, 2i+1) take slot i; split halves: (i, i+P)
+        const bool first = IL ? (d & 1) == 0 : d < P;
+        const int slot = IL ? (d >> 1) : (first ? d : d - P);
+        pd[j] = IL ? (d ^ 1) : (first ? d + P : d - P);
+        cf[j] = wc[slot];
+        sf[j] = first ? -ws[slot] : ws[slot];
+    }
+#pragma unroll
+    for (int u = 0; u < kElemLoads; ++u) {
         if (u * rpi >= nh) break;
         const bool act = lane_ok && u * rpi + hi < nh;
         u32x4 o = in[u];
-        if (rotate) {
-            lds_x[wave_in_block][lane] = in[u];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            if (lane_ok) {
-                const auto xv = chunk_values<T>(in[u]);
-                float y[E];
-                u32x4 keep = u32x4{0u, 0u, 0u, 0u};  // elements copied as they are
+        if (rot_lane) {
+            const T* xrow = reinterpret_cast<const T*>(&lds_x[wave_in_block][u][hi * RL]);
+            const auto xv = chunk_values<T>(in[u]);
+            float y[E];
 #pragma unroll
-                for (int j = 0; j < E; ++j) {
-                    const int d = c * E + j;  // element of the head row
-                    y[j] = 0.0f;
-                    if (d >= a.R) {
-                        mask_elem<T>(keep, j);
-                        continue;
-                    }
-                    // interleaved: (2i, 2i+1) take slot i; split halves: (i, i+P)
-                    const bool first = IL ? (d & 1) == 0 : d < P;
-                    const int pd = IL ? (d ^ 1) : (first ? d + P : d - P);
-                    const int slot = IL ? (d >> 1) : (first ? d : d - P);
-                    const float sv = ws[slot];
-                    y[j] = rot_out<T>(to_f(xv[j]), wc[slot], to_f(xrow[pd]), first ? -sv : sv);
-                }
-                o = select_bits(keep, in[u], chunk_pack<T>(y));
-            }
-            // the next instruction's chunks reuse the wave's LDS row
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            for (int j = 0; j < E; ++j) y[j] = rot_out<T>(to_f(xv[j]), cf[j], to_f(xrow[pd[j]]), sf[j]);
+            o = select_bits(keep, in[u], chunk_pack<T>(y));
         }
         if (act && live) store_nt(py + u * ystep, o);
     }

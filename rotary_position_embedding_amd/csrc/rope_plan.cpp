@@ -317,6 +317,7 @@ static bool choose_row_geometry(Plan* pl, bool vec_can, bool elementwise = false
     }
     const int over_loads = overrides().row_loads;  // tuning override (sweeps)
     if (over_loads == 1 || over_loads == 2 || over_loads == 4 || over_loads == 8) loads = over_loads;
+    if (elementwise && loads > kRowElemLoads) loads = kRowElemLoads;
     int64_t total_waves = 0;
     for (int t = 0; t < p.ntask; ++t) {
         const int64_t H = p.task[t].heads;

@@ -51,6 +51,11 @@ constexpr int kVecMaxHeads = 16;
 constexpr int kRowLoads = 8;
 // row kernel, on the fly: slots per token computed once per wave (LDS rows)
 constexpr int kRowMaxSlots = 256;
+// row kernel, element-wise pairs: at most this many instructions per wave
+#ifndef ROPE_ROW_ELEM_LOADS
+#define ROPE_ROW_ELEM_LOADS 4
+#endif
+constexpr int kRowElemLoads = ROPE_ROW_ELEM_LOADS;
 
 struct Problem {
     int32_t dtype;        // ROPE_FLOAT, ROPE_FLOAT16 or ROPE_BFLOAT16
