@@ -28,8 +28,10 @@ fly), the QK-norm decode step with the cache append, an M-RoPE decode step,
 one GPU's share of the fp16 prefill and of the decode Q+K step under 8-way
 tensor parallelism (4 of the 32 query heads, 1 of the 8 key heads), and its
 share of the fp16 prefill under 8-way sequence parallelism (256 of the 2048
-tokens of each sequence), and a prompt of 4 x 2048 tokens written to the
-key/value caches.
+tokens of each sequence), a prompt of 4 x 2048 tokens written to the
+key/value caches, and prefills of other model shapes: 64 heads of 64, 64
+heads of 96 with 24 dimensions rotated (GPT-NeoX-20B), QK-norm with heads of
+256.
 """
 import argparse
 import json
@@ -569,7 +571,10 @@ def main():
                  (rope_inputs.get("c2_rope_f16_prefill_tp8"), False),
                  (rope_inputs.get("c5_rope_qk_f16_decode_tp8"), False),
                  (rope_inputs.get("c2_rope_f16_prefill_sp8"), False),
-                 (rope_inputs.get("kv_append_f16_prompt"), False)]
+                 (rope_inputs.get("kv_append_f16_prompt"), False),
+                 (rope_inputs.get("rope_f16_prefill_heads64"), False),
+                 (rope_inputs.get("rope_f16_prefill_neox_partial"), False),
+                 (rope_inputs.get("qk_norm_f16_prefill_heads256"), False)]
         for ew, otf in extra:
             log("timing %s%s" % (ew.name, " on the fly" if otf else ""))
             decode = small(ew)

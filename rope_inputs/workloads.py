@@ -322,6 +322,31 @@ EXTRA_WORKLOADS.update({
 })
 
 
+# Prefills of other model shapes (fp16, 4 x 2048 tokens): small heads, a
+# GPT-NeoX-style partial rotation whose pairs do not fall on 16-byte chunks,
+# and QK-norm with heads of 256 (Gemma-3-like).
+EXTRA_WORKLOADS.update({
+    "rope_f16_prefill_heads64": Workload(
+        index=15, name="rope_f16_prefill_heads64", op="rope", dtype=np.float16,
+        x_shape=(4, 2048, 64 * 64), num_heads=64, cache_rows=8192, cache_base=1e4,
+        extra={"ids": "offset_arange", "offset_bound": 4096},
+        description="RotaryEmbedding rank-3 fp16 (4,2048,4096), 64 heads of 64, ids = per-batch offset + "
+                    "arange, table (8192,32) base 1e4"),
+    "rope_f16_prefill_neox_partial": Workload(
+        index=16, name="rope_f16_prefill_neox_partial", op="rope", dtype=np.float16,
+        x_shape=(4, 2048, 64 * 96), num_heads=64, rotary_embedding_dim=24, cache_rows=8192,
+        cache_base=1e4, extra={"ids": "offset_arange", "offset_bound": 4096},
+        description="RotaryEmbedding rank-3 fp16 (4,2048,6144), 64 heads of 96 with the first 24 "
+                    "dimensions rotated (GPT-NeoX-20B's shape), ids = per-batch offset + arange, table (8192,12)"),
+    "qk_norm_f16_prefill_heads256": Workload(
+        index=17, name="qk_norm_f16_prefill_heads256", op="qk_norm", dtype=np.float16,
+        x_shape=(4, 2048, 8 * 256), num_heads=8, k_shape=(4, 2048, 4 * 256), kv_num_heads=4,
+        cache_rows=8192, cache_base=1e6, extra={"ids": "offset_arange", "offset_bound": 4096},
+        description="QK-norm + RoPE prefill fp16 with heads of 256 (Gemma-3-like): Q (4,2048,8x256), "
+                    "K (4,2048,4x256), ids = per-batch offset + arange, table (8192,128) base 1e6"),
+})
+
+
 def get(name: str) -> Workload:
     return WORKLOADS[name] if name in WORKLOADS else EXTRA_WORKLOADS[name]
 

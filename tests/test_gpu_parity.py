@@ -268,6 +268,21 @@ def test_prefill_rank4_head_shapes(head_size, interleaved, rotary_dim):
         assert_bitwise(got[..., rotary_dim:], inputs[0][..., rotary_dim:], "tail")
 
 
+@pytest.mark.parametrize("name", ["rope_f16_prefill_heads64", "rope_f16_prefill_neox_partial"])
+def test_other_model_shapes_full_size(name):
+    """The benchmark's prefills of other model shapes (64 heads of 64; 64
+    heads of 96 with 24 dimensions rotated), in the launch configuration the
+    benchmark times, against the oracle at full size, tails bitwise."""
+    w = EXTRA_WORKLOADS[name]
+    log("other model shape %s" % w.name)
+    got, want, inputs = run_workload(w)
+    log("%s %s" % (w.name, assert_parity(got, want, w.name)))
+    if w.rotary_embedding_dim:
+        rows = (w.batch, w.seq, w.num_heads, w.head_size)
+        R = w.rotary_embedding_dim
+        assert_bitwise(got.reshape(rows)[..., R:], inputs[0].reshape(rows)[..., R:], "tail")
+
+
 def test_qk_on_the_fly_prefill_size():
     """Q+K with coefficients on the fly over 8192 tokens (the row kernel at
     prefill size), against the oracle."""

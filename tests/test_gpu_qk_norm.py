@@ -147,6 +147,22 @@ def test_qk_norm_prefill_full_size(dt, D, H, Hk):
     print("prefill", np.dtype(dt).name, D, rq, rk, flush=True)
 
 
+def test_qk_norm_prefill_heads256_bench_size():
+    """The benchmark's QK-norm prefill with heads of 256 (qk_norm_f16_prefill_heads256:
+    4 x 2048 tokens, 8 query and 4 key heads) in its launch configuration."""
+    w = get("qk_norm_f16_prefill_heads256")
+    q, k, ids = w.make_x(), w.make_k(), w.make_ids()
+    wq, wk = w.make_norm_weights()
+    cos, sin = oracle.table_for(w)
+    want_q, want_k = oracle.rope_apply_qk_norm(q, k, wq, wk, 1e-6, cos, sin, ids, num_heads=w.num_heads,
+                                               kv_num_heads=w.kv_num_heads)
+    gq, gk = rpe.rope_apply_qk_norm(cuda(q), cuda(k), cuda(wq), cuda(wk), cuda(cos), cuda(sin), cuda(ids),
+                                    epsilon=1e-6, num_heads=w.num_heads, kv_num_heads=w.kv_num_heads)
+    rq = assert_parity_norm(host(gq), want_q, zmax_rows(q, wq, 1e-6, 3, w.num_heads), "Q")
+    rk = assert_parity_norm(host(gk), want_k, zmax_rows(k, wk, 1e-6, 3, w.kv_num_heads), "K")
+    print("prefill heads of 256", rq, rk, flush=True)
+
+
 def test_qk_norm_decode_full_size():
     """The decode step the benchmark times (qk_norm_f16_decode): 256 sequences
     of one token, 32 query and 8 key heads of 128, f16, ids U[0, 32768),
