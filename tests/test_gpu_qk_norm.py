@@ -127,7 +127,10 @@ def test_qk_norm_in_place():
 @pytest.mark.parametrize("dt,D,H,Hk", [(np.float16, 128, 32, 8), (BFLOAT16, 128, 32, 8),
                                        (np.float16, 256, 16, 8),   # halves of 256 B: the row kernel
                                        (np.float32, 128, 32, 8),   # float32: the row kernel
-                                       (np.float16, 96, 32, 8)])   # 192-byte rows: general rows
+                                       (np.float16, 96, 32, 8),    # 192-byte rows: general rows
+                                       (np.float16, 64, 32, 8),    # 128-byte rows: the row kernel
+                                       (BFLOAT16, 256, 8, 4),      # 8 + 4 heads of 256
+                                       (np.float16, 96, 16, 8)])   # general rows, 16 + 8 heads
 def test_qk_norm_prefill_full_size(dt, D, H, Hk):
     """A Qwen3-like prefill: 4 x 2048 tokens, 32 query and 8 key heads of 128
     (or 16 and 8 of 256), positions per-sequence offset + arange into a
