@@ -92,6 +92,7 @@ struct KArgs {
     // (c0, c0 + c1 and c0 + c1 + c2 chunks), and the division by the last
     int32_t gm_c0, gm_c01, gm_c;
     uint32_t gm_m, gm_s;
+    int32_t mrope_single;       // M-RoPE: every rotation item's slots take one stream
     const int32_t* seqlens;     // append kind: total key length per sequence
     int64_t rows_out;           // append kind: cache rows
     uint32_t sel[kSelWords];
@@ -631,6 +632,28 @@ __global__ __launch_bounds__(kBlock) void rope_vec_kernel(const KArgs a) {
 #pragma unroll
             for (int j = 0; j < CE; ++j) { cf[m][j] = cv[j]; sf[m][j] = sv[j]; }
             if (!valid) keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
+        } else if (COEF == kCoefMrope && a.mrope_single) {
+            // every slot of the item takes the stream of its first slot: that
+            // stream's row alone, the whole item copied when its id is out of
+            // range
+            const uint32_t k0 = codes[m] & 3u;
+            const int64_t p = k0 == 0 ? pos[m][0] : (k0 == 1 ? pos[m][1] : pos[m][2]);
+            const bool ok = p >= 0 && p < a.M;
+            const int64_t e = ((ok ? p : 0) * a.P + slot0[m]) * ES;  // row 0 if out of range
+            const cvec cv = *reinterpret_cast<const cvec*>(a.cos + e);
+            const cvec sv = *reinterpret_cast<const cvec*>(a.sin + e);
+            if (a.scale == 1.0f) {
+#pragma unroll
+                for (int j = 0; j < CE; ++j) { cf[m][j] = cv[j]; sf[m][j] = sv[j]; }
+            } else {
+                // scaled coefficient: binary32 product rounded to T
+#pragma unroll
+                for (int j = 0; j < CE; ++j) {
+                    cf[m][j] = from_f<T>(keep_f32(to_f(cv[j]) * a.scale));
+                    sf[m][j] = from_f<T>(keep_f32(to_f(sv[j]) * a.scale));
+                }
+            }
+            if (!ok) keep[m] = u32x4{0xffffffffu, 0xffffffffu, 0xffffffffu, 0xffffffffu};
         } else if (COEF == kCoefMrope) {
             // Slots [slot0, slot0 + CE) of the three stream rows; slot i takes
             // its stream's value. Per-stream element masks over the slice are

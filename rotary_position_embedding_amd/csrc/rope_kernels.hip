@@ -120,6 +120,7 @@ int launch_plan(const Plan& pl, void* stream) {
     a.prompt = p.prompt;
     a.rows_out = p.rows_out;
     for (int i = 0; i < kSelWords; ++i) a.sel[i] = p.sel[i];
+    a.mrope_single = p.mrope_single;
 
     hipError_t e;
     if (g.vector) {

@@ -882,6 +882,13 @@ int plan_mrope(const rope_tensor* x, const rope_tensor* position_ids, const rope
     mrope_streams(half, mrope_section, mrope_layout, streams);
     for (int64_t i = 0; i < half; ++i)
         p.sel[i / 16] |= (uint32_t)streams[i] << (2 * (i % 16));
+    // the slots a 16-byte chunk of X rotates with (8 / 4 of them for 2- /
+    // 4-byte split halves, half that interleaved) all from one stream, as
+    // sectioned layouts with sections in multiples of that give
+    const int64_t chunk_slots = (16 / elem_size(p.dtype)) / (p.interleaved ? 2 : 1);
+    p.mrope_single = 1;
+    for (int64_t i = 0; i < half; ++i)
+        if (streams[i] != streams[i - i % chunk_slots]) p.mrope_single = 0;
     out->empty = numel(x) == 0;
     out->g.rank = x->rank;
     return finish_plan(out);

@@ -72,6 +72,7 @@ struct Problem {
     float scaling;        // on-the-fly attention scaling
     float scale;          // M-RoPE coefficient scale
     uint32_t sel[kSelWords];  // M-RoPE stream of slot i in bits 2*(i%16) of word i/16
+    int32_t mrope_single;     // M-RoPE: every 16-byte chunk's slots take one stream
     // cache append: per-sequence total lengths, prompt flag, cache rows
     const int32_t* seqlens;
     int32_t prompt;
